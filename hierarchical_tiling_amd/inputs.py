@@ -1,0 +1,104 @@
+"""Seeded synthetic inputs, shared by the GPU path, the tests and the benchmark.
+
+This module holds none of the GEMM's arithmetic: it draws seeded random values, rounds them once
+to an operand type, and lays them out with given element strides.  Everything that needs the
+same input (the GPU library and the CPU oracle) receives the bits produced here.
+
+Recipe (the pages measure on no dataset; every input is synthetic):
+* values are drawn in float64 from numpy's PCG64 generator seeded with the given seed, in
+  logical row-major order, so the same seed gives the same logical matrix in any storage order;
+* they are rounded to float32, then to the operand type with round-to-nearest-even by torch's CPU
+  cast (float8 is OCP e4m3 "fn");
+* storage is a flat array; element (r, c) sits at r * strides[0] + c * strides[1].
+"""
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+import torch
+
+STORAGE = {"f32": np.uint32, "f16": np.uint16, "bf16": np.uint16, "e4m3": np.uint8}
+_TORCH = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16,
+          "e4m3": torch.float8_e4m3fn}
+_TORCH_BITS = {"f32": torch.int32, "f16": torch.int16, "bf16": torch.int16, "e4m3": torch.uint8}
+ESIZE = {"f32": 4, "f16": 2, "bf16": 2, "e4m3": 1}
+
+
+def draw(seed: int, count: int, dist: str = "normal", *, std: float = 1.0, lo: float = -1.0,
+         hi: float = 1.0) -> np.ndarray:
+    """`count` float64 values: "normal" N(0, std^2), "uniform" U[lo, hi], or "dyadic" (multiples
+    of 1/4 in [-1, 1], exactly representable in every operand type)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    if dist == "normal":
+        return rng.standard_normal(count) * std
+    if dist == "uniform":
+        return rng.uniform(lo, hi, count)
+    if dist == "dyadic":
+        return rng.integers(-4, 5, count).astype(np.float64) / 4.0
+    raise ValueError(f"unknown distribution {dist!r}")
+
+
+def quantize(values: np.ndarray, dtype: str) -> np.ndarray:
+    """Round float64 values to `dtype`; returns the stored bits as a numpy array."""
+    t = torch.from_numpy(np.ascontiguousarray(values, dtype=np.float64).astype(np.float32))
+    bits = t.to(_TORCH[dtype]).view(_TORCH_BITS[dtype]).numpy()
+    return bits.view(STORAGE[dtype]).copy()
+
+
+@dataclasses.dataclass
+class HostMatrix:
+    storage: np.ndarray      # flat bits
+    dtype: str
+    shape: tuple             # (rows, cols)
+    strides: tuple           # element strides (row, col)
+
+    @property
+    def nbytes(self) -> int:
+        return self.storage.size * ESIZE[self.dtype]
+
+
+def layout_strides(rows: int, cols: int, order: str, ld: int | None = None):
+    """Strides of a row-major ("row", ld >= cols) or column-major ("col", ld >= rows) matrix."""
+    if order == "row":
+        ld = cols if ld is None else ld
+        if ld < cols:
+            raise ValueError("leading dimension below the row length")
+        return (ld, 1), (rows - 1) * ld + cols if rows and cols else 0
+    if order == "col":
+        ld = rows if ld is None else ld
+        if ld < rows:
+            raise ValueError("leading dimension below the column length")
+        return (1, ld), (cols - 1) * ld + rows if rows and cols else 0
+    raise ValueError(f"unknown order {order!r}")
+
+
+def place(bits_rowmajor: np.ndarray, rows: int, cols: int, dtype: str, order: str = "row",
+          ld: int | None = None, fill: int = 0) -> HostMatrix:
+    """Lay out logical row-major bits in the requested storage order."""
+    strides, n = layout_strides(rows, cols, order, ld)
+    storage = np.full(max(n, 1) if rows and cols else 0, fill, dtype=STORAGE[dtype])
+    if rows and cols:
+        logical = bits_rowmajor.reshape(rows, cols)
+        r = np.arange(rows, dtype=np.int64)[:, None]
+        c = np.arange(cols, dtype=np.int64)[None, :]
+        storage[(r * strides[0] + c * strides[1]).ravel()] = logical.ravel()
+    return HostMatrix(storage, dtype, (rows, cols), strides)
+
+
+def matrix(seed: int, rows: int, cols: int, dtype: str, dist: str = "normal", *,
+           order: str = "row", ld: int | None = None, **params) -> HostMatrix:
+    vals = draw(seed, rows * cols, dist, **params)
+    return place(quantize(vals, dtype), rows, cols, dtype, order, ld)
+
+
+def vector(seed: int, n: int, dtype: str, dist: str = "normal", **params) -> HostMatrix:
+    bits = quantize(draw(seed, n, dist, **params), dtype)
+    return HostMatrix(bits, dtype, (1, n), (n, 1))
+
+
+def to_device(m: HostMatrix, device="cuda") -> torch.Tensor:
+    """Upload the flat storage; the tensor is only a device buffer (its torch dtype is the
+    storage integer type)."""
+    t = torch.from_numpy(m.storage.view({1: np.uint8, 2: np.int16, 4: np.int32}[ESIZE[m.dtype]]))
+    return t.to(device)
