@@ -1,0 +1,60 @@
+"""Build libhtgemm.so (gfx950 HIP kernels + host API + layout helper) in the package directory.
+
+    python -m hierarchical_tiling_amd.build
+
+Objects go to _build/ at the repository root; the shared library lands next to this file so the
+binding loads it in-tree.
+"""
+from __future__ import annotations
+
+import concurrent.futures as cf
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+OUT = os.path.join(PKG, "libhtgemm.so")
+BUILD = os.path.join(ROOT, "_build")
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+ARCH = "gfx950"
+# Packed fp32 VALU instructions are kept out of every kernel.
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-command-line-argument"]
+
+SOURCES = [
+    ("kernels.hip", [HIPCC, f"--offload-arch={ARCH}"] + COMMON + DEVICE_FLAGS),
+    ("api.cpp", [HIPCC, f"--offload-arch={ARCH}"] + COMMON + DEVICE_FLAGS),
+    ("layout.cpp", ["g++"] + COMMON),
+]
+
+
+def _compile(src, cmd):
+    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+    full = cmd + ["-c", os.path.join(CSRC, src), "-o", obj]
+    res = subprocess.run(full, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"compile failed: {' '.join(full)}\n{res.stdout}\n{res.stderr}")
+    return obj
+
+
+def build(verbose: bool = True) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    with cf.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+        objs = list(ex.map(lambda sc: _compile(*sc), SOURCES))
+    tmp = OUT + ".tmp"
+    link = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
+    res = subprocess.run(link, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"link failed: {' '.join(link)}\n{res.stdout}\n{res.stderr}")
+    os.replace(tmp, OUT)
+    if verbose:
+        print(f"built {OUT}")
+    return OUT
+
+
+if __name__ == "__main__":
+    build()
+    sys.exit(0)

@@ -1,0 +1,276 @@
+// api.cpp -- host side of the C ABI in htgemm.h: validation ("can_implement"), the tile-table
+// choice, and the launch on the caller's stream.
+//
+// The life cycle mirrors the pages' device layer ("CUTLASS", stanleyjacob.dev, Part IV Stage 1:
+// get_workspace_size, can_implement, initialize, run; "CUTLASS, CuTe, and CUDA Tile", section
+// "Assembling a CUTLASS kernel": a stateful reusable handle; the kernel, not the caller, fixes
+// the grid).  The tile table plays the part of the pages' builder that picks a configuration
+// from the problem ("CUTLASS", Part IX: the best tile depends on the problem shape, which is why
+// the measurement tool ships with the library).
+#include <hip/hip_runtime.h>
+
+#include <cstdlib>
+#include <cstring>
+#include <new>
+
+#include "../../include/htgemm.h"
+#include "../../include/htlayout.h"
+#include "gemm_internal.h"
+
+using namespace htk;
+
+namespace {
+
+constexpr uint32_t kMagic = 0x47454d4du;   // live handle
+constexpr uint32_t kDead = 0xdeadbeefu;    // destroyed handle
+constexpr int64_t kLdsBudget = 160 * 1024;  // LDS per CU on gfx950
+
+struct Operand {
+  bool kmajor;  // unit stride along K
+  int64_t ld;   // the other stride
+};
+
+}  // namespace
+
+struct gemm_handle_s {
+  uint32_t magic;
+  gemm_desc d;
+  Operand a, b;
+  int cfg;       // entry used when A and B are 16-byte aligned
+  int fallback;  // narrow-load entry
+  int group_m;
+};
+
+namespace {
+
+bool valid_type(int t) { return t >= GEMM_F32 && t <= GEMM_F8E4M3; }
+
+// Unit-stride analysis of one input operand: rows x K with strides (s_row, s_k).
+int classify(int64_t s_row, int64_t s_k, Operand* op) {
+  if (s_row < 0 || s_k < 0) return GEMM_ERR_LAYOUT;
+  if (s_k == 1) { op->kmajor = true; op->ld = s_row; return GEMM_OK; }
+  if (s_row == 1) { op->kmajor = false; op->ld = s_k; return GEMM_OK; }
+  return GEMM_ERR_LAYOUT;
+}
+
+// Can the 16-byte-load path read this operand (given 16-byte aligned base pointers)?
+bool vec_ok(const Operand& op, int64_t rows, int64_t K, int dt) {
+  const int sz = dtype_size(dt), ve = 16 / sz;
+  if ((op.ld * sz) % 16 != 0) return false;
+  if (op.kmajor) return K % ve == 0;
+  if (dt == DT_F8) return false;  // no transposing vector loader for 1-byte elements
+  return rows % ve == 0;
+}
+
+bool entry_fits(const KernelEntry& e, const gemm_handle_s& h, bool vec_a, bool vec_b) {
+  const gemm_desc& d = h.d;
+  if (e.dtype != d.a_type) return false;
+  if ((e.a_kmajor != 0) != h.a.kmajor || (e.b_kmajor != 0) != h.b.kmajor) return false;
+  if (e.vec && !(vec_a && vec_b)) return false;
+  ht_tile_stats st;
+  ht_tile_plan(e.bm, e.bn, e.bk, dtype_size(e.dtype), kLdsBudget, &st);
+  if (!st.fits) return false;  // double-buffered A and B tiles must fit the LDS budget
+  return true;
+}
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Heuristic choice among fitting entries: the largest tile that still gives at least one
+// workgroup per CU (256 CUs), else the tile with the most workgroups.
+int choose(const gemm_handle_s& h, bool vec_a, bool vec_b, bool want_vec) {
+  const KernelEntry* t = table();
+  int best = -1;
+  int64_t best_area = -1;
+  int best_small = -1;
+  int64_t best_small_wg = -1;
+  for (int i = 0; i < table_size(); ++i) {
+    const KernelEntry& e = t[i];
+    if ((e.vec != 0) != want_vec) continue;
+    if (!entry_fits(e, h, vec_a, vec_b)) continue;
+    const int64_t wg = cdiv(h.d.M, e.bm) * cdiv(h.d.N, e.bn);
+    const int64_t area = int64_t(e.bm) * e.bn;
+    if (wg >= 256 && area > best_area) { best = i; best_area = area; }
+    if (wg > best_small_wg || (wg == best_small_wg && area > int64_t(t[best_small].bm) * t[best_small].bn)) {
+      best_small = i;
+      best_small_wg = wg;
+    }
+  }
+  return best >= 0 ? best : best_small;
+}
+
+int check_arch() {
+  const char* fake = std::getenv("HTGEMM_FAKE_ARCH");
+  if (fake && *fake) return std::strncmp(fake, "gfx950", 6) == 0 ? GEMM_OK : GEMM_ERR_ARCH;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return GEMM_ERR_HIP;
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return GEMM_ERR_HIP;
+  return std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? GEMM_OK : GEMM_ERR_ARCH;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+int gemm_create(const gemm_desc* desc, gemm_t* out) {
+  if (!desc || !out) return GEMM_ERR_INVALID_ARG;
+  *out = nullptr;
+  const gemm_desc& d = *desc;
+  if (d.reserved != 0) return GEMM_ERR_INVALID_ARG;
+  if (d.M < 0 || d.N < 0 || d.K < 0) return GEMM_ERR_INVALID_ARG;
+  if (d.M > INT32_MAX / 2 || d.N > INT32_MAX / 2 || d.K > INT32_MAX / 2) return GEMM_ERR_INVALID_ARG;
+  if (d.act < GEMM_ACT_NONE || d.act > GEMM_ACT_GELU) return GEMM_ERR_INVALID_ARG;
+  if ((d.has_c != 0 && d.has_c != 1) || (d.has_bias != 0 && d.has_bias != 1)) return GEMM_ERR_INVALID_ARG;
+  if (!valid_type(d.a_type) || !valid_type(d.b_type) || !valid_type(d.d_type)) return GEMM_ERR_DTYPE_COMBO;
+  if (d.a_type != d.b_type || d.d_type != out_dtype(d.a_type)) return GEMM_ERR_DTYPE_COMBO;
+  if (d.has_c && d.c_type != d.d_type) return GEMM_ERR_DTYPE_COMBO;
+  if (d.has_bias && d.bias_type != d.d_type) return GEMM_ERR_DTYPE_COMBO;
+  if (d.d_stride_m < 0 || d.d_stride_n < 0) return GEMM_ERR_LAYOUT;
+  if (d.has_c && (d.c_stride_m < 0 || d.c_stride_n < 0)) return GEMM_ERR_LAYOUT;
+
+  gemm_handle_s h;
+  std::memset(&h, 0, sizeof(h));
+  h.d = d;
+  int rc = classify(d.a_stride_m, d.a_stride_k, &h.a);
+  if (rc) return rc;
+  rc = classify(d.b_stride_n, d.b_stride_k, &h.b);
+  if (rc) return rc;
+  rc = check_arch();
+  if (rc) return rc;
+
+  const bool va = vec_ok(h.a, d.M, d.K, d.a_type), vb = vec_ok(h.b, d.N, d.K, d.b_type);
+  h.fallback = choose(h, va, vb, false);
+  if (h.fallback < 0) return GEMM_ERR_NO_CONFIG;
+  if (d.force_config >= 0) {
+    if (d.force_config >= table_size() || !entry_fits(table()[d.force_config], h, va, vb))
+      return GEMM_ERR_NO_CONFIG;
+    h.cfg = d.force_config;
+  } else {
+    h.cfg = (va && vb) ? choose(h, va, vb, true) : -1;
+    if (h.cfg < 0) h.cfg = h.fallback;
+  }
+  h.group_m = 4;
+
+  gemm_handle_s* p = new (std::nothrow) gemm_handle_s(h);
+  if (!p) return GEMM_ERR_INVALID_ARG;
+  p->magic = kMagic;
+  *out = p;
+  return GEMM_OK;
+}
+
+int gemm_workspace_size(gemm_t h, size_t* bytes) {
+  if (!h || h->magic != kMagic) return GEMM_ERR_BAD_HANDLE;
+  if (!bytes) return GEMM_ERR_INVALID_ARG;
+  *bytes = 0;
+  return GEMM_OK;
+}
+
+int gemm_get_info(gemm_t h, gemm_info* info) {
+  if (!h || h->magic != kMagic) return GEMM_ERR_BAD_HANDLE;
+  if (!info) return GEMM_ERR_INVALID_ARG;
+  const KernelEntry& e = table()[h->cfg];
+  std::memset(info, 0, sizeof(*info));
+  info->config = h->cfg;
+  info->fallback = h->fallback;
+  info->bm = e.bm;
+  info->bn = e.bn;
+  info->bk = e.bk;
+  info->waves = e.waves;
+  info->stages = e.stages;
+  info->lds_bytes = e.lds_bytes;
+  info->split_k = 1;
+  info->grid = cdiv(h->d.M, e.bm) * cdiv(h->d.N, e.bn);
+  std::strncpy(info->name, e.name, sizeof(info->name) - 1);
+  return GEMM_OK;
+}
+
+int gemm_run(gemm_t h, const void* A, const void* B, const void* C, void* D, const void* bias,
+             float alpha, float beta, float scale_a, float scale_b, void* workspace,
+             void* stream) {
+  (void)workspace;
+  if (!h || h->magic != kMagic) return GEMM_ERR_BAD_HANDLE;
+  const gemm_desc& d = h->d;
+  const bool read_c = d.has_c && beta != 0.0f;
+  if (!d.has_c && beta != 0.0f) return GEMM_ERR_INVALID_ARG;
+  if (d.M == 0 || d.N == 0) return GEMM_OK;
+  if (!D || (d.K > 0 && (!A || !B)) || (read_c && !C) || (d.has_bias && !bias))
+    return GEMM_ERR_INVALID_ARG;
+  const size_t in_sz = dtype_size(d.a_type), out_sz = dtype_size(d.d_type);
+  if (!aligned(A, in_sz) || !aligned(B, in_sz) || !aligned(D, out_sz) ||
+      (read_c && !aligned(C, out_sz)) || (d.has_bias && !aligned(bias, out_sz)))
+    return GEMM_ERR_MISALIGNED;
+
+  int idx = h->cfg;
+  if (table()[idx].vec && (!aligned(A, 16) || !aligned(B, 16))) idx = h->fallback;
+  const KernelEntry& e = table()[idx];
+
+  KParams p;
+  std::memset(&p, 0, sizeof(p));
+  p.A = A;
+  p.B = B;
+  p.C = read_c ? C : nullptr;
+  p.D = D;
+  p.bias = d.has_bias ? bias : nullptr;
+  p.M = d.M;
+  p.N = d.N;
+  p.K = d.K;
+  p.lda = h->a.ld;
+  p.ldb = h->b.ld;
+  p.c_sm = d.c_stride_m;
+  p.c_sn = d.c_stride_n;
+  p.d_sm = d.d_stride_m;
+  p.d_sn = d.d_stride_n;
+  p.alpha = alpha * scale_a * scale_b;
+  p.beta = beta;
+  p.has_c = read_c ? 1 : 0;
+  p.has_bias = d.has_bias;
+  p.act = d.act;
+  p.tiles_m = (int)cdiv(d.M, e.bm);
+  p.tiles_n = (int)cdiv(d.N, e.bn);
+  p.group_m = h->group_m;
+  p.split_k = 1;
+  p.k_per_split = (int)d.K;
+  const int64_t grid = int64_t(p.tiles_m) * p.tiles_n;
+  if (grid <= 0 || grid > INT32_MAX) return GEMM_ERR_INVALID_ARG;
+  hipError_t err = e.launch(p, (hipStream_t)stream, dim3((unsigned)grid));
+  return err == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
+}
+
+int gemm_destroy(gemm_t h) {
+  if (!h) return GEMM_OK;
+  if (h->magic != kMagic) return GEMM_ERR_BAD_HANDLE;
+  h->magic = kDead;
+  delete h;
+  return GEMM_OK;
+}
+
+const char* gemm_status_string(int status) {
+  switch (status) {
+    case GEMM_OK: return "success";
+    case GEMM_ERR_INVALID_ARG: return "invalid argument";
+    case GEMM_ERR_DTYPE_COMBO: return "unsupported type combination";
+    case GEMM_ERR_LAYOUT: return "operand has no unit stride";
+    case GEMM_ERR_MISALIGNED: return "pointer not aligned to its element size";
+    case GEMM_ERR_ARCH: return "device is not gfx950";
+    case GEMM_ERR_LAUNCH: return "kernel launch failed";
+    case GEMM_ERR_BAD_HANDLE: return "invalid or destroyed handle";
+    case GEMM_ERR_NO_CONFIG: return "no tile-table entry can run this problem";
+    case GEMM_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int gemm_num_configs(void) { return table_size(); }
+
+int gemm_config_name(int idx, char* out, size_t cap) {
+  if (idx < 0 || idx >= table_size() || !out) return GEMM_ERR_INVALID_ARG;
+  const char* n = table()[idx].name;
+  size_t len = std::strlen(n);
+  if (len + 1 > cap) return GEMM_ERR_INVALID_ARG;
+  std::memcpy(out, n, len + 1);
+  return GEMM_OK;
+}
+
+}  // extern "C"

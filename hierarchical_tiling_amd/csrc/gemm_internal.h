@@ -1,0 +1,56 @@
+// gemm_internal.h -- declarations shared by the host API (api.cpp) and the kernels (kernels.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace htk {
+
+// Operand element types; the numbering matches gemm_dtype in htgemm.h.
+enum : int { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2, DT_F8 = 3 };
+
+// Arguments of one launch.  The operand of A or B with unit stride is implied by the kernel
+// variant; lda / ldb is the other stride.  alpha already includes scale_a * scale_b.
+struct KParams {
+  const void* A;
+  const void* B;
+  const void* C;      // read only when has_c != 0
+  void* D;
+  const void* bias;   // read only when has_bias != 0
+  int64_t M, N, K;
+  int64_t lda, ldb;
+  int64_t c_sm, c_sn, d_sm, d_sn;
+  float alpha, beta;
+  int has_c, has_bias, act;
+  int tiles_m, tiles_n, group_m;
+  int split_k;        // workgroups per output tile along K (1: none)
+  int k_per_split;    // K elements per split (a multiple of the tile's K step)
+  float* workspace;   // fp32 partials when split_k > 1
+};
+
+typedef hipError_t (*launch_fn)(const KParams&, hipStream_t, dim3 grid);
+
+// One entry of the tile table.
+struct KernelEntry {
+  const char* name;
+  int dtype;          // operand type of A and B
+  int a_kmajor;       // 1: A has unit stride along K (row-major A); 0: along M
+  int b_kmajor;       // 1: B has unit stride along K (column-major B); 0: along N
+  int vec;            // 1: 16-byte loads (needs aligned pointers / leading dims); 0: any alignment
+  int skinny;         // 1: streaming kernel for small M
+  int bm, bn, bk;     // workgroup tile
+  int waves;          // waves per workgroup
+  int stages;         // LDS stages
+  int lds_bytes;      // LDS per workgroup
+  int max_split_k;    // largest split along K the kernel supports (1: none)
+  launch_fn launch;
+};
+
+const KernelEntry* table();
+int table_size();
+
+// Output type of a given operand type (htgemm.h type table).
+constexpr int out_dtype(int dt) { return dt == DT_F8 ? DT_BF16 : dt; }
+constexpr int dtype_size(int dt) { return dt == DT_F32 ? 4 : (dt == DT_F8 ? 1 : 2); }
+
+}  // namespace htk

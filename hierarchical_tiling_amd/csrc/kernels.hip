@@ -1,0 +1,521 @@
+// kernels.hip -- gfx950 (MI355X, CDNA4) kernels of the hierarchically tiled GEMM.
+//
+//   D = act(alpha * (A @ B) + beta * C + bias),  fp32 accumulation.
+//
+// The decomposition follows the pages' tile hierarchy ("CUTLASS", stanleyjacob.dev, Part I
+// "The mental model" and Part IV "The full life of one GEMM"; "A10 - CuTe, CUTLASS & CuTile",
+// section 3.2): the output is cut into workgroup tiles (BM x BN) that stream K in BK steps
+// through LDS; each wave owns a wave tile held in accumulator registers; each wave tile is a
+// grid of MFMA atoms.  What is MI355X-specific here:
+//
+//  * Atoms are CDNA4 MFMA instructions on 64-lane waves: v_mfma_f32_32x32x16_{bf16,f16},
+//    v_mfma_f32_32x32x64_f8f6f4 (OCP e4m3), v_mfma_f32_32x32x2_f32 and their 16x16 forms.
+//    For each atom, lane l holds row (l % MI) of the A tile and column (l % MI) of the B tile,
+//    and a contiguous run of k; A and B place the same k in the same lane slot, so the k order
+//    inside an atom never matters.  The 32x32 accumulator holds, in register r of lane l,
+//    row 8*(r/4) + 4*(l/32) + r%4 and column l % 32; the 16x16 one row 4*(l/16) + r.
+//  * LDS tiles are stored K-contiguous: one row per m (for A) or n (for B), BK*esize = 128
+//    bytes, i.e. eight 16-byte chunks.  Chunk c of row r lives at chunk slot c ^ (r & 7): the
+//    XOR swizzle of "A10", section 3.4 (Swizzle<3,4,3> in byte addressing), which puts the
+//    eight rows that one ds_read_b128 phase reads at the same logical chunk into eight
+//    different 16-byte bank groups, and also makes the row-wise 16-byte stores conflict free.
+//  * The K mainloop is double buffered ("CUTLASS", Part IV Stage 4): the global loads of
+//    k-tile t+1 are issued into registers before the MFMAs of tile t, and written into the other
+//    LDS stage after them, with one barrier per k-tile ("CuTe DSL / CUDA Tile" post, "Pipelining
+//    hides a wait": the slower of load and compute sets the interval).
+//  * Workgroup ids are remapped so that each of the 8 XCDs (each with its own L2) gets a
+//    contiguous range of tiles, walked in groups of GROUP_M tile rows ("CUTLASS", Part IV
+//    Stage 2: the tile scheduler swizzles the grid for L2 reuse).
+//  * Edges: rows past M or N are clamped to the last valid row on load (their results are never
+//    stored), the K tail is zero-filled, and stores are predicated.  MFMA issue is never
+//    predicated: it is wave-wide, so every lane always executes it ("A10", section 6,
+//    Pitfall 1: guards around a collective matrix instruction must be uniform).
+//  * A narrow-load variant reads element by element with full predication, for leading
+//    dimensions or pointers that are not 16-byte aligned ("CUTLASS", Part II: misaligned
+//    operands fall back to a slow path).
+//  * The epilogue applies alpha, beta*C, bias[n] and the activation in fp32 on the accumulator
+//    registers and rounds to the output type once ("CUTLASS", Part IV Stage 5).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gemm_internal.h"
+
+namespace htk {
+
+typedef uint8_t u8;
+typedef uint16_t u16;
+typedef uint32_t u32;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef u32 u32x4 __attribute__((ext_vector_type(4)));
+
+// ------------------------------------------------------------------------------------------
+// Element types
+// ------------------------------------------------------------------------------------------
+template <int DT> struct Ty;
+template <> struct Ty<DT_F32> { typedef u32 T; static constexpr int SZ = 4; typedef float O; };
+template <> struct Ty<DT_F16> { typedef u16 T; static constexpr int SZ = 2; typedef u16 O; };
+template <> struct Ty<DT_BF16> { typedef u16 T; static constexpr int SZ = 2; typedef u16 O; };
+template <> struct Ty<DT_F8> { typedef u8 T; static constexpr int SZ = 1; typedef u16 O; };
+
+__device__ __forceinline__ float bf16_to_f32(u16 b) { return __builtin_bit_cast(float, u32(b) << 16); }
+__device__ __forceinline__ float f16_to_f32(u16 h) { return (float)__builtin_bit_cast(_Float16, h); }
+__device__ __forceinline__ u16 f32_to_bf16(float x) { return __builtin_bit_cast(u16, (__bf16)x); }
+__device__ __forceinline__ u16 f32_to_f16(float x) { return __builtin_bit_cast(u16, (_Float16)x); }
+
+// Output (C, D, bias) element access by output dtype.
+template <int ODT> struct Out;
+template <> struct Out<DT_F32> {
+  __device__ static float load(const void* p, int64_t i) { return ((const float*)p)[i]; }
+  __device__ static void store(void* p, int64_t i, float v) { ((float*)p)[i] = v; }
+};
+template <> struct Out<DT_F16> {
+  __device__ static float load(const void* p, int64_t i) { return f16_to_f32(((const u16*)p)[i]); }
+  __device__ static void store(void* p, int64_t i, float v) { ((u16*)p)[i] = f32_to_f16(v); }
+};
+template <> struct Out<DT_BF16> {
+  __device__ static float load(const void* p, int64_t i) { return bf16_to_f32(((const u16*)p)[i]); }
+  __device__ static void store(void* p, int64_t i, float v) { ((u16*)p)[i] = f32_to_bf16(v); }
+};
+
+// ------------------------------------------------------------------------------------------
+// MFMA atoms.  G: lane groups along k (64 / MI); UNITS: 16-byte chunks per lane per operand per
+// instruction; PER_UNIT: instructions fed by one chunk; NACC: accumulator floats per lane.
+// ------------------------------------------------------------------------------------------
+template <int DT, int MI> struct Atom;
+
+template <> struct Atom<DT_BF16, 32> {
+  static constexpr int G = 2, UNITS = 1, PER_UNIT = 1, NACC = 16;
+  typedef f32x16 acc_t;
+  __device__ static void mma(acc_t& c, const u32x4* a, const u32x4* b, int) {
+    c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[0]),
+                                                __builtin_bit_cast(bf16x8, b[0]), c, 0, 0, 0);
+  }
+};
+template <> struct Atom<DT_BF16, 16> {
+  static constexpr int G = 4, UNITS = 1, PER_UNIT = 1, NACC = 4;
+  typedef f32x4 acc_t;
+  __device__ static void mma(acc_t& c, const u32x4* a, const u32x4* b, int) {
+    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[0]),
+                                                __builtin_bit_cast(bf16x8, b[0]), c, 0, 0, 0);
+  }
+};
+template <> struct Atom<DT_F16, 32> {
+  static constexpr int G = 2, UNITS = 1, PER_UNIT = 1, NACC = 16;
+  typedef f32x16 acc_t;
+  __device__ static void mma(acc_t& c, const u32x4* a, const u32x4* b, int) {
+    c = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a[0]),
+                                               __builtin_bit_cast(f16x8, b[0]), c, 0, 0, 0);
+  }
+};
+template <> struct Atom<DT_F16, 16> {
+  static constexpr int G = 4, UNITS = 1, PER_UNIT = 1, NACC = 4;
+  typedef f32x4 acc_t;
+  __device__ static void mma(acc_t& c, const u32x4* a, const u32x4* b, int) {
+    c = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a[0]),
+                                               __builtin_bit_cast(f16x8, b[0]), c, 0, 0, 0);
+  }
+};
+// fp8: format code 0 selects OCP E4M3 for both operands; scale operands left neutral (0).
+template <> struct Atom<DT_F8, 32> {
+  static constexpr int G = 2, UNITS = 2, PER_UNIT = 1, NACC = 16;
+  typedef f32x16 acc_t;
+  __device__ static void mma(acc_t& c, const u32x4* a, const u32x4* b, int) {
+    i32x8 av = {(int)a[0][0], (int)a[0][1], (int)a[0][2], (int)a[0][3],
+                (int)a[1][0], (int)a[1][1], (int)a[1][2], (int)a[1][3]};
+    i32x8 bv = {(int)b[0][0], (int)b[0][1], (int)b[0][2], (int)b[0][3],
+                (int)b[1][0], (int)b[1][1], (int)b[1][2], (int)b[1][3]};
+    c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, c, 0, 0, 0, 0, 0, 0);
+  }
+};
+template <> struct Atom<DT_F8, 16> {
+  static constexpr int G = 4, UNITS = 2, PER_UNIT = 1, NACC = 4;
+  typedef f32x4 acc_t;
+  __device__ static void mma(acc_t& c, const u32x4* a, const u32x4* b, int) {
+    i32x8 av = {(int)a[0][0], (int)a[0][1], (int)a[0][2], (int)a[0][3],
+                (int)a[1][0], (int)a[1][1], (int)a[1][2], (int)a[1][3]};
+    i32x8 bv = {(int)b[0][0], (int)b[0][1], (int)b[0][2], (int)b[0][3],
+                (int)b[1][0], (int)b[1][1], (int)b[1][2], (int)b[1][3]};
+    c = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 0, 0, 0, 0, 0, 0);
+  }
+};
+template <> struct Atom<DT_F32, 32> {
+  static constexpr int G = 2, UNITS = 1, PER_UNIT = 4, NACC = 16;
+  typedef f32x16 acc_t;
+  __device__ static void mma(acc_t& c, const u32x4* a, const u32x4* b, int sub) {
+    c = __builtin_amdgcn_mfma_f32_32x32x2f32(__builtin_bit_cast(float, a[0][sub]),
+                                             __builtin_bit_cast(float, b[0][sub]), c, 0, 0, 0);
+  }
+};
+template <> struct Atom<DT_F32, 16> {
+  static constexpr int G = 4, UNITS = 1, PER_UNIT = 4, NACC = 4;
+  typedef f32x4 acc_t;
+  __device__ static void mma(acc_t& c, const u32x4* a, const u32x4* b, int sub) {
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(__builtin_bit_cast(float, a[0][sub]),
+                                             __builtin_bit_cast(float, b[0][sub]), c, 0, 0, 0);
+  }
+};
+
+// Row (within the MI x MI block) of accumulator register r of lane l.
+template <int MI> __device__ __forceinline__ int acc_row(int l, int r) {
+  if constexpr (MI == 32) return 8 * (r >> 2) + 4 * (l >> 5) + (r & 3);
+  else return 4 * (l >> 4) + r;
+}
+
+// ------------------------------------------------------------------------------------------
+// Workgroup -> output tile.  Dispatch hands consecutive workgroup ids to the 8 XCDs in turn;
+// the remap gives XCD x the contiguous tile range [start(x), start(x) + count(x)), and tiles
+// are walked GROUP_M tile rows at a time so concurrently resident neighbours share A and B.
+// ------------------------------------------------------------------------------------------
+__device__ __forceinline__ void tile_of(const KParams& p, int pid, int nwg, int& tm, int& tn) {
+  const int per = nwg >> 3, extra = nwg & 7;
+  const int xcd = pid & 7, local = pid >> 3;
+  const int t = xcd * per + min(xcd, extra) + local;
+  const int width = p.group_m * p.tiles_n;
+  const int group = t / width;
+  const int first = group * p.group_m;
+  const int gsz = min(p.tiles_m - first, p.group_m);
+  const int within = t - group * width;
+  tm = first + within % gsz;
+  tn = within / gsz;
+}
+
+__device__ __forceinline__ float activate(int act, float v) {
+  if (act == 1) return v > 0.f ? v : (v == v ? 0.f : v);
+  if (act == 2) return 0.5f * v * (1.0f + erff(v * 0.7071067811865475f));
+  return v;
+}
+
+// ------------------------------------------------------------------------------------------
+// Tile loaders: global -> registers -> swizzled LDS.
+// LDS row r (an m of A or an n of B) holds BK elements as CH = BK*SZ/16 chunks.
+// ------------------------------------------------------------------------------------------
+template <int CH> __device__ __forceinline__ int lds_slot(int row, int chunk) {
+  static_assert(CH % 8 == 0, "rows must be a multiple of 128 bytes");
+  return row * CH + (chunk ^ (row & 7));
+}
+
+// K-contiguous operand, 16-byte loads.  `rows` valid rows starting at row0 (clamped).
+template <int DT, int R, int BKE, int NT>
+struct LoadKMajorVec {
+  static constexpr int SZ = Ty<DT>::SZ, VE = 16 / SZ, CH = BKE * SZ / 16;
+  static constexpr int N = R * CH / NT;
+  static_assert(R * CH % NT == 0, "tile chunks must divide over the threads");
+  u32x4 r[N];
+  template <bool PRED>
+  __device__ __forceinline__ void load(const void* base, int64_t ld, int64_t row0, int64_t rows,
+                                       int64_t k0, int64_t K, int tid) {
+    const typename Ty<DT>::T* src = (const typename Ty<DT>::T*)base;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int q = tid + i * NT, row = q / CH, c = q % CH;
+      const int64_t gr = min(row0 + row, rows - 1);
+      const int64_t k = k0 + (int64_t)c * VE;
+      if (!PRED || k < K)
+        r[i] = *(const u32x4*)(src + gr * ld + k);
+      else
+        r[i] = u32x4{0, 0, 0, 0};
+    }
+  }
+  __device__ __forceinline__ void store(u32x4* lds, int tid) const {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int q = tid + i * NT, row = q / CH, c = q % CH;
+      lds[lds_slot<CH>(row, c)] = r[i];
+    }
+  }
+};
+
+// Row-contiguous (M- or N-contiguous) operand, 16-byte loads of VE rows at one k, transposed
+// in registers into VE K-contiguous chunks.  Needs rows % VE == 0.
+template <int DT, int R, int BKE, int NT>
+struct LoadMNMajorVec {
+  static constexpr int SZ = Ty<DT>::SZ, VE = 16 / SZ, CH = BKE * SZ / 16;
+  static constexpr int BLOCKS = (BKE / VE) * (R / VE);
+  static constexpr int N = (BLOCKS + NT - 1) / NT;  // threads past BLOCKS idle (whole waves)
+  static_assert(BLOCKS % NT == 0 || (BLOCKS < NT && BLOCKS % 64 == 0),
+                "transpose blocks must cover whole waves");
+  static_assert(SZ == 2 || SZ == 4, "register transpose supports 2- and 4-byte elements");
+  u32x4 r[N][VE];
+  template <bool PRED>
+  __device__ __forceinline__ void load(const void* base, int64_t ld, int64_t row0, int64_t rows,
+                                       int64_t k0, int64_t K, int tid) {
+    const typename Ty<DT>::T* src = (const typename Ty<DT>::T*)base;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int q = tid + i * NT, rb = q % (R / VE), kb = q / (R / VE);
+      if (BLOCKS % NT != 0 && q >= BLOCKS) continue;
+      const int64_t gr = min(row0 + (int64_t)rb * VE, rows - VE);
+#pragma unroll
+      for (int kk = 0; kk < VE; ++kk) {
+        const int64_t k = k0 + (int64_t)kb * VE + kk;
+        if (!PRED || k < K)
+          r[i][kk] = *(const u32x4*)(src + k * ld + gr);
+        else
+          r[i][kk] = u32x4{0, 0, 0, 0};
+      }
+    }
+  }
+  __device__ __forceinline__ void store(u32x4* lds, int tid) const {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int q = tid + i * NT, rb = q % (R / VE), kb = q / (R / VE);
+      if (BLOCKS % NT != 0 && q >= BLOCKS) continue;
+#pragma unroll
+      for (int rr = 0; rr < VE; ++rr) {
+        u32x4 o;
+        if constexpr (SZ == 4) {
+          o = u32x4{r[i][0][rr], r[i][1][rr], r[i][2][rr], r[i][3][rr]};
+        } else {
+          const int w = rr >> 1, sh = (rr & 1) * 16;
+#pragma unroll
+          for (int d = 0; d < 4; ++d) {
+            const u32 lo = (r[i][2 * d][w] >> sh) & 0xffffu;
+            const u32 hi = (r[i][2 * d + 1][w] >> sh) & 0xffffu;
+            o[d] = lo | (hi << 16);
+          }
+        }
+        lds[lds_slot<CH>(rb * VE + rr, kb)] = o;
+      }
+    }
+  }
+};
+
+// Any alignment: element loads with full predication.  KMAJ selects which index is contiguous;
+// threads walk the contiguous direction so neighbouring lanes read neighbouring elements.
+template <int DT, bool KMAJ, int R, int BKE, int NT>
+struct LoadNarrow {
+  typedef typename Ty<DT>::T T;
+  static constexpr int SZ = Ty<DT>::SZ, VE = 16 / SZ, CH = BKE * SZ / 16;
+  static constexpr int N = R * CH / NT;
+  static_assert(R * CH % NT == 0, "tile chunks must divide over the threads");
+  T e[N][VE];
+  template <bool PRED>
+  __device__ __forceinline__ void load(const void* base, int64_t ld, int64_t row0, int64_t rows,
+                                       int64_t k0, int64_t K, int tid) {
+    const T* src = (const T*)base;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int q = tid + i * NT;
+      const int row = KMAJ ? q / CH : q % R;
+      const int c = KMAJ ? q % CH : q / R;
+      const int64_t gr = row0 + row;
+#pragma unroll
+      for (int j = 0; j < VE; ++j) {
+        const int64_t k = k0 + (int64_t)c * VE + j;
+        const bool ok = gr < rows && k < K;
+        const int64_t off = KMAJ ? gr * ld + k : k * ld + gr;
+        e[i][j] = ok ? src[off] : T(0);
+      }
+    }
+  }
+  __device__ __forceinline__ void store(u32x4* lds, int tid) const {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int q = tid + i * NT;
+      const int row = KMAJ ? q / CH : q % R;
+      const int c = KMAJ ? q % CH : q / R;
+      u32x4 o;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        u32 w = 0;
+#pragma unroll
+        for (int b = 0; b < 4 / SZ; ++b) w |= u32(e[i][d * (4 / SZ) + b]) << (8 * SZ * b);
+        o[d] = w;
+      }
+      lds[lds_slot<CH>(row, c)] = o;
+    }
+  }
+};
+
+template <int DT, bool KMAJ, bool VEC, int R, int BKE, int NT>
+struct PickLoader {
+  typedef LoadNarrow<DT, KMAJ, R, BKE, NT> type;
+};
+template <int DT, int R, int BKE, int NT>
+struct PickLoader<DT, true, true, R, BKE, NT> {
+  typedef LoadKMajorVec<DT, R, BKE, NT> type;
+};
+template <int DT, int R, int BKE, int NT>
+struct PickLoader<DT, false, true, R, BKE, NT> {
+  typedef LoadMNMajorVec<DT, R, BKE, NT> type;
+};
+
+// ------------------------------------------------------------------------------------------
+// The tiled kernel.
+// ------------------------------------------------------------------------------------------
+template <int DT, bool AK, bool BKM, bool VEC, int BM, int BN, int BKE, int WM, int WN, int MI>
+__global__ __launch_bounds__(WM * WN * 64) void gemm_tiled(const KParams p) {
+  typedef Atom<DT, MI> At;
+  typedef typename At::acc_t acc_t;
+  constexpr int NT = WM * WN * 64;
+  constexpr int SZ = Ty<DT>::SZ;
+  constexpr int CH = BKE * SZ / 16;          // 16-byte chunks per LDS row
+  constexpr int WTM = BM / WM, WTN = BN / WN; // wave tile
+  constexpr int RM = WTM / MI, RN = WTN / MI; // atoms per wave tile
+  constexpr int UPL = CH / At::G;             // chunks per lane per row per k-tile
+  static_assert(UPL % At::UNITS == 0, "k-tile must hold whole atoms");
+  static_assert(WTM % MI == 0 && WTN % MI == 0, "wave tile must hold whole atoms");
+
+  __shared__ u32x4 lds[2][(BM + BN) * CH];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int tm, tn;
+  tile_of(p, blockIdx.x, gridDim.x, tm, tn);
+  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+  const int wm = wave % WM, wn = wave / WM;
+
+  acc_t acc[RM][RN];
+#pragma unroll
+  for (int i = 0; i < RM; ++i)
+#pragma unroll
+    for (int j = 0; j < RN; ++j) acc[i][j] = acc_t{};
+
+  typename PickLoader<DT, AK, VEC, BM, BKE, NT>::type la;
+  typename PickLoader<DT, BKM, VEC, BN, BKE, NT>::type lb;
+
+  const int nk = (int)((p.K + BKE - 1) / BKE);
+  const int nfull = (int)(p.K / BKE);
+
+  // fragment addressing (chunk slots) for this lane
+  const int frow = lane % MI, fgrp = lane / MI;
+
+  if (nk > 0) {
+    if (nfull > 0) {
+      la.template load<false>(p.A, p.lda, m0, p.M, 0, p.K, tid);
+      lb.template load<false>(p.B, p.ldb, n0, p.N, 0, p.K, tid);
+    } else {
+      la.template load<true>(p.A, p.lda, m0, p.M, 0, p.K, tid);
+      lb.template load<true>(p.B, p.ldb, n0, p.N, 0, p.K, tid);
+    }
+    la.store(lds[0], tid);
+    lb.store(lds[0] + BM * CH, tid);
+    __syncthreads();
+
+    for (int kt = 0; kt < nk; ++kt) {
+      const int cur = kt & 1;
+      if (kt + 1 < nk) {
+        const int64_t k0 = (int64_t)(kt + 1) * BKE;
+        if (kt + 1 < nfull) {
+          la.template load<false>(p.A, p.lda, m0, p.M, k0, p.K, tid);
+          lb.template load<false>(p.B, p.ldb, n0, p.N, k0, p.K, tid);
+        } else {
+          la.template load<true>(p.A, p.lda, m0, p.M, k0, p.K, tid);
+          lb.template load<true>(p.B, p.ldb, n0, p.N, k0, p.K, tid);
+        }
+      }
+      const u32x4* As = lds[cur];
+      const u32x4* Bs = lds[cur] + BM * CH;
+#pragma unroll
+      for (int u = 0; u < UPL; u += At::UNITS) {
+        u32x4 fa[RM][At::UNITS], fb[RN][At::UNITS];
+#pragma unroll
+        for (int x = 0; x < At::UNITS; ++x) {
+          const int c = fgrp + At::G * (u + x);
+#pragma unroll
+          for (int i = 0; i < RM; ++i) fa[i][x] = As[lds_slot<CH>(wm * WTM + i * MI + frow, c)];
+#pragma unroll
+          for (int j = 0; j < RN; ++j) fb[j][x] = Bs[lds_slot<CH>(wn * WTN + j * MI + frow, c)];
+        }
+#pragma unroll
+        for (int s = 0; s < At::PER_UNIT; ++s)
+#pragma unroll
+          for (int i = 0; i < RM; ++i)
+#pragma unroll
+            for (int j = 0; j < RN; ++j) At::mma(acc[i][j], fa[i], fb[j], s);
+      }
+      if (kt + 1 < nk) {
+        la.store(lds[cur ^ 1], tid);
+        lb.store(lds[cur ^ 1] + BM * CH, tid);
+      }
+      __syncthreads();
+    }
+  }
+
+  // ---- epilogue: alpha, beta*C, bias[n], activation, one rounding, predicated store ----
+  constexpr int ODT = out_dtype(DT);
+  typedef Out<ODT> O;
+  const bool has_c = p.has_c != 0, has_bias = p.has_bias != 0;
+#pragma unroll
+  for (int i = 0; i < RM; ++i)
+#pragma unroll
+    for (int j = 0; j < RN; ++j) {
+      const int64_t col = n0 + wn * WTN + j * MI + (lane % MI);
+      const bool col_ok = col < p.N;
+      const float bv = (has_bias && col_ok) ? O::load(p.bias, col) : 0.f;
+#pragma unroll
+      for (int r = 0; r < At::NACC; ++r) {
+        const int64_t row = m0 + wm * WTM + i * MI + acc_row<MI>(lane, r);
+        if (col_ok && row < p.M) {
+          float v = p.alpha * acc[i][j][r];
+          if (has_c) v += p.beta * O::load(p.C, row * p.c_sm + col * p.c_sn);
+          if (has_bias) v += bv;
+          v = activate(p.act, v);
+          O::store(p.D, row * p.d_sm + col * p.d_sn, v);
+        }
+      }
+    }
+}
+
+// ------------------------------------------------------------------------------------------
+// Launchers and the tile table.
+// ------------------------------------------------------------------------------------------
+template <int DT, bool AK, bool BKM, bool VEC, int BM, int BN, int BKE, int WM, int WN, int MI>
+static hipError_t launch_tiled(const KParams& p, hipStream_t s, dim3 grid) {
+  hipLaunchKernelGGL((gemm_tiled<DT, AK, BKM, VEC, BM, BN, BKE, WM, WN, MI>), grid,
+                     dim3(WM * WN * 64), 0, s, p);
+  return hipGetLastError();
+}
+
+#define HT_TILED(NAME, DT, AK, BKM, VEC, BM, BN, BKE, WM, WN, MI)                        \
+  {NAME, DT, AK, BKM, VEC, 0, BM, BN, BKE, WM * WN, 2, 2 * (BM + BN) * BKE * Ty<DT>::SZ, 1, \
+   &launch_tiled<DT, AK, BKM, VEC, BM, BN, BKE, WM, WN, MI>}
+
+static const KernelEntry g_table[] = {
+    // bf16, BK = 64 (128-byte LDS rows)
+    HT_TILED("bf16_ak_bk_256x256x64_w2x2_m32_vec", DT_BF16, 1, 1, 1, 256, 256, 64, 2, 2, 32),
+    HT_TILED("bf16_ak_bk_128x128x64_w2x2_m32_vec", DT_BF16, 1, 1, 1, 128, 128, 64, 2, 2, 32),
+    HT_TILED("bf16_ak_bn_256x256x64_w2x2_m32_vec", DT_BF16, 1, 0, 1, 256, 256, 64, 2, 2, 32),
+    HT_TILED("bf16_ak_bn_128x128x64_w2x2_m32_vec", DT_BF16, 1, 0, 1, 128, 128, 64, 2, 2, 32),
+    HT_TILED("bf16_am_bk_128x128x64_w2x2_m32_vec", DT_BF16, 0, 1, 1, 128, 128, 64, 2, 2, 32),
+    HT_TILED("bf16_am_bn_128x128x64_w2x2_m32_vec", DT_BF16, 0, 0, 1, 128, 128, 64, 2, 2, 32),
+    HT_TILED("bf16_ak_bk_128x128x64_w2x2_m32_narrow", DT_BF16, 1, 1, 0, 128, 128, 64, 2, 2, 32),
+    HT_TILED("bf16_ak_bn_128x128x64_w2x2_m32_narrow", DT_BF16, 1, 0, 0, 128, 128, 64, 2, 2, 32),
+    HT_TILED("bf16_am_bk_128x128x64_w2x2_m32_narrow", DT_BF16, 0, 1, 0, 128, 128, 64, 2, 2, 32),
+    HT_TILED("bf16_am_bn_128x128x64_w2x2_m32_narrow", DT_BF16, 0, 0, 0, 128, 128, 64, 2, 2, 32),
+    // fp16
+    HT_TILED("f16_ak_bk_256x256x64_w2x2_m32_vec", DT_F16, 1, 1, 1, 256, 256, 64, 2, 2, 32),
+    HT_TILED("f16_ak_bk_128x128x64_w2x2_m32_vec", DT_F16, 1, 1, 1, 128, 128, 64, 2, 2, 32),
+    HT_TILED("f16_ak_bn_256x256x64_w2x2_m32_vec", DT_F16, 1, 0, 1, 256, 256, 64, 2, 2, 32),
+    HT_TILED("f16_ak_bn_128x128x64_w2x2_m32_vec", DT_F16, 1, 0, 1, 128, 128, 64, 2, 2, 32),
+    HT_TILED("f16_am_bk_128x128x64_w2x2_m32_vec", DT_F16, 0, 1, 1, 128, 128, 64, 2, 2, 32),
+    HT_TILED("f16_am_bn_128x128x64_w2x2_m32_vec", DT_F16, 0, 0, 1, 128, 128, 64, 2, 2, 32),
+    HT_TILED("f16_ak_bk_128x128x64_w2x2_m32_narrow", DT_F16, 1, 1, 0, 128, 128, 64, 2, 2, 32),
+    HT_TILED("f16_ak_bn_128x128x64_w2x2_m32_narrow", DT_F16, 1, 0, 0, 128, 128, 64, 2, 2, 32),
+    HT_TILED("f16_am_bk_128x128x64_w2x2_m32_narrow", DT_F16, 0, 1, 0, 128, 128, 64, 2, 2, 32),
+    HT_TILED("f16_am_bn_128x128x64_w2x2_m32_narrow", DT_F16, 0, 0, 0, 128, 128, 64, 2, 2, 32),
+    // fp32, BK = 32
+    HT_TILED("f32_ak_bk_128x128x32_w2x2_m32_vec", DT_F32, 1, 1, 1, 128, 128, 32, 2, 2, 32),
+    HT_TILED("f32_ak_bn_128x128x32_w2x2_m32_vec", DT_F32, 1, 0, 1, 128, 128, 32, 2, 2, 32),
+    HT_TILED("f32_am_bk_128x128x32_w2x2_m32_vec", DT_F32, 0, 1, 1, 128, 128, 32, 2, 2, 32),
+    HT_TILED("f32_am_bn_128x128x32_w2x2_m32_vec", DT_F32, 0, 0, 1, 128, 128, 32, 2, 2, 32),
+    HT_TILED("f32_ak_bk_64x64x32_w2x2_m16_narrow", DT_F32, 1, 1, 0, 64, 64, 32, 2, 2, 16),
+    HT_TILED("f32_ak_bn_64x64x32_w2x2_m16_narrow", DT_F32, 1, 0, 0, 64, 64, 32, 2, 2, 16),
+    HT_TILED("f32_am_bk_64x64x32_w2x2_m16_narrow", DT_F32, 0, 1, 0, 64, 64, 32, 2, 2, 16),
+    HT_TILED("f32_am_bn_64x64x32_w2x2_m16_narrow", DT_F32, 0, 0, 0, 64, 64, 32, 2, 2, 16),
+    // fp8 e4m3, BK = 128
+    HT_TILED("e4m3_ak_bk_256x256x128_w2x2_m32_vec", DT_F8, 1, 1, 1, 256, 256, 128, 2, 2, 32),
+    HT_TILED("e4m3_ak_bk_128x128x128_w2x2_m32_vec", DT_F8, 1, 1, 1, 128, 128, 128, 2, 2, 32),
+    HT_TILED("e4m3_ak_bk_128x128x128_w2x2_m32_narrow", DT_F8, 1, 1, 0, 128, 128, 128, 2, 2, 32),
+    HT_TILED("e4m3_ak_bn_128x128x128_w2x2_m32_narrow", DT_F8, 1, 0, 0, 128, 128, 128, 2, 2, 32),
+    HT_TILED("e4m3_am_bk_128x128x128_w2x2_m32_narrow", DT_F8, 0, 1, 0, 128, 128, 128, 2, 2, 32),
+    HT_TILED("e4m3_am_bn_128x128x128_w2x2_m32_narrow", DT_F8, 0, 0, 0, 128, 128, 128, 2, 2, 32),
+};
+
+const KernelEntry* table() { return g_table; }
+int table_size() { return (int)(sizeof(g_table) / sizeof(g_table[0])); }
+
+}  // namespace htk

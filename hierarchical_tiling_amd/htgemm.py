@@ -1,0 +1,302 @@
+"""ctypes binding of libhtgemm.so: the same entry points as include/htgemm.h and
+include/htlayout.h, with argument marshalling only.  Every step of the GEMM runs in the HIP
+library; nothing here computes.  If the library has not been built, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libhtgemm.so")
+
+# status codes (htgemm.h)
+GEMM_OK = 0
+STATUS_NAMES = {0: "GEMM_OK", 1: "GEMM_ERR_INVALID_ARG", 2: "GEMM_ERR_DTYPE_COMBO",
+                3: "GEMM_ERR_LAYOUT", 4: "GEMM_ERR_MISALIGNED", 5: "GEMM_ERR_ARCH",
+                6: "GEMM_ERR_LAUNCH", 7: "GEMM_ERR_BAD_HANDLE", 8: "GEMM_ERR_NO_CONFIG",
+                9: "GEMM_ERR_HIP"}
+DTYPES = {"f32": 0, "f16": 1, "bf16": 2, "e4m3": 3}
+ACTS = {"none": 0, "relu": 1, "gelu": 2}
+# layout status codes (htlayout.h)
+HT_STATUS_NAMES = {0: "HT_OK", 1: "HT_ERR_PARSE", 2: "HT_ERR_RANGE", 3: "HT_ERR_NOT_COMPOSABLE",
+                   4: "HT_ERR_CAPACITY", 5: "HT_ERR_NO_COMPLEMENT"}
+
+
+class GemmError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS_NAMES.get(status, status)}")
+
+
+class LayoutError(ValueError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {HT_STATUS_NAMES.get(status, status)}")
+
+
+class gemm_desc(ctypes.Structure):
+    _fields_ = [("M", ctypes.c_int64), ("N", ctypes.c_int64), ("K", ctypes.c_int64),
+                ("a_type", ctypes.c_int32), ("b_type", ctypes.c_int32),
+                ("c_type", ctypes.c_int32), ("d_type", ctypes.c_int32),
+                ("bias_type", ctypes.c_int32), ("has_c", ctypes.c_int32),
+                ("has_bias", ctypes.c_int32), ("act", ctypes.c_int32),
+                ("a_stride_m", ctypes.c_int64), ("a_stride_k", ctypes.c_int64),
+                ("b_stride_k", ctypes.c_int64), ("b_stride_n", ctypes.c_int64),
+                ("c_stride_m", ctypes.c_int64), ("c_stride_n", ctypes.c_int64),
+                ("d_stride_m", ctypes.c_int64), ("d_stride_n", ctypes.c_int64),
+                ("force_config", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+class gemm_info(ctypes.Structure):
+    _fields_ = [("config", ctypes.c_int32), ("fallback", ctypes.c_int32),
+                ("bm", ctypes.c_int32), ("bn", ctypes.c_int32), ("bk", ctypes.c_int32),
+                ("waves", ctypes.c_int32), ("stages", ctypes.c_int32),
+                ("lds_bytes", ctypes.c_int32), ("split_k", ctypes.c_int32),
+                ("grid", ctypes.c_int64), ("name", ctypes.c_char * 96)]
+
+
+class ht_tile_stats(ctypes.Structure):
+    _fields_ = [("flops", ctypes.c_int64), ("bytes", ctypes.c_int64),
+                ("intensity", ctypes.c_double), ("double_buffer_bytes", ctypes.c_int64),
+                ("fits", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded library; raises if it has not been built (no fallback path exists)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m hierarchical_tiling_amd.build`"
+                           " (or __graft_entry__.build()); there is no CPU fallback")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+    cp = ctypes.c_char_p
+    sig = {
+        "gemm_create": ([ctypes.POINTER(gemm_desc), ctypes.POINTER(vp)], i32),
+        "gemm_workspace_size": ([vp, ctypes.POINTER(sz)], i32),
+        "gemm_run": ([vp, vp, vp, vp, vp, vp, ctypes.c_float, ctypes.c_float, ctypes.c_float,
+                      ctypes.c_float, vp, vp], i32),
+        "gemm_destroy": ([vp], i32),
+        "gemm_status_string": ([i32], cp),
+        "gemm_get_info": ([vp, ctypes.POINTER(gemm_info)], i32),
+        "gemm_num_configs": ([], i32),
+        "gemm_config_name": ([i32, ctypes.c_char_p, sz], i32),
+        "ht_layout_eval": ([cp, cp, ctypes.POINTER(i64)], i32),
+        "ht_layout_size": ([cp, ctypes.POINTER(i64)], i32),
+        "ht_layout_table": ([cp, ctypes.POINTER(i64), i64], i32),
+        "ht_layout_coalesce": ([cp, ctypes.c_char_p, sz], i32),
+        "ht_layout_compose": ([cp, cp, ctypes.c_char_p, sz], i32),
+        "ht_layout_complement": ([cp, i64, ctypes.c_char_p, sz], i32),
+        "ht_layout_logical_divide": ([cp, cp, ctypes.c_char_p, sz], i32),
+        "ht_layout_zipped_divide": ([cp, cp, cp, ctypes.c_char_p, sz], i32),
+        "ht_swizzle": ([i64, i32, i32, i32], i64),
+        "ht_tile_plan": ([i64, i64, i64, i32, i64, ctypes.POINTER(ht_tile_stats)], i32),
+        "ht_pipeline_time": ([i64, ctypes.c_double, ctypes.c_double], ctypes.c_double),
+    }
+    for name, (args, res) in sig.items():
+        f = getattr(L, name)
+        f.argtypes = args
+        f.restype = res
+    _lib = L
+    return L
+
+
+EXPORTED = ["gemm_create", "gemm_workspace_size", "gemm_run", "gemm_destroy", "gemm_status_string",
+            "gemm_get_info", "gemm_num_configs", "gemm_config_name", "ht_layout_eval",
+            "ht_layout_size", "ht_layout_table", "ht_layout_coalesce", "ht_layout_compose",
+            "ht_layout_complement", "ht_layout_logical_divide", "ht_layout_zipped_divide",
+            "ht_swizzle", "ht_tile_plan", "ht_pipeline_time"]
+
+
+def _check(rc, where):
+    if rc != GEMM_OK:
+        raise GemmError(rc, where)
+
+
+# ---- GEMM entry points --------------------------------------------------------------------
+
+def gemm_create(desc: gemm_desc) -> int:
+    h = ctypes.c_void_p()
+    _check(lib().gemm_create(ctypes.byref(desc), ctypes.byref(h)), "gemm_create")
+    return h.value
+
+
+def gemm_workspace_size(h) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().gemm_workspace_size(h, ctypes.byref(n)), "gemm_workspace_size")
+    return n.value
+
+
+def gemm_run(h, A, B, C, D, bias, alpha, beta, scale_a=1.0, scale_b=1.0, workspace=None,
+             stream=None):
+    """Pointers are integers (device addresses) or None; stream is a hipStream_t as an integer."""
+    _check(lib().gemm_run(h, A, B, C, D, bias, alpha, beta, scale_a, scale_b, workspace, stream),
+           "gemm_run")
+
+
+def gemm_destroy(h):
+    _check(lib().gemm_destroy(h), "gemm_destroy")
+
+
+def gemm_status_string(status: int) -> str:
+    return lib().gemm_status_string(status).decode()
+
+
+def gemm_get_info(h) -> gemm_info:
+    info = gemm_info()
+    _check(lib().gemm_get_info(h, ctypes.byref(info)), "gemm_get_info")
+    return info
+
+
+def gemm_num_configs() -> int:
+    return lib().gemm_num_configs()
+
+
+def gemm_config_name(i: int) -> str:
+    buf = ctypes.create_string_buffer(128)
+    _check(lib().gemm_config_name(i, buf, 128), "gemm_config_name")
+    return buf.value.decode()
+
+
+def make_desc(M, N, K, dtype, a_strides, b_strides, d_strides, c_strides=None, has_bias=False,
+              act="none", force_config=-1) -> gemm_desc:
+    """a_strides = (stride_m, stride_k); b_strides = (stride_k, stride_n); c/d = (m, n)."""
+    out_t = "bf16" if dtype == "e4m3" else dtype
+    d = gemm_desc()
+    d.M, d.N, d.K = M, N, K
+    d.a_type = d.b_type = DTYPES[dtype]
+    d.c_type = d.d_type = d.bias_type = DTYPES[out_t]
+    d.has_c = 1 if c_strides is not None else 0
+    d.has_bias = 1 if has_bias else 0
+    d.act = ACTS[act]
+    d.a_stride_m, d.a_stride_k = a_strides
+    d.b_stride_k, d.b_stride_n = b_strides
+    d.c_stride_m, d.c_stride_n = c_strides if c_strides is not None else (0, 0)
+    d.d_stride_m, d.d_stride_n = d_strides
+    d.force_config = force_config
+    d.reserved = 0
+    return d
+
+
+class Gemm:
+    """RAII wrapper: a handle for one problem description."""
+
+    def __init__(self, desc: gemm_desc):
+        self.desc = desc
+        self.handle = gemm_create(desc)
+
+    @property
+    def info(self) -> gemm_info:
+        return gemm_get_info(self.handle)
+
+    def run(self, A, B, C, D, bias=None, alpha=1.0, beta=0.0, scale_a=1.0, scale_b=1.0,
+            stream=None):
+        gemm_run(self.handle, _addr(A), _addr(B), _addr(C), _addr(D), _addr(bias), alpha, beta,
+                 scale_a, scale_b, None, _stream(stream))
+
+    def close(self):
+        if self.handle:
+            gemm_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def _addr(x):
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(s):
+    if s is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(s, int):
+        return s
+    return s.cuda_stream
+
+
+# ---- layout helper ------------------------------------------------------------------------
+
+def _lcheck(rc, where):
+    if rc != 0:
+        raise LayoutError(rc, where)
+
+
+def _out_str(fn, *args):
+    buf = ctypes.create_string_buffer(4096)
+    _lcheck(fn(*args, buf, 4096), fn.__name__)
+    return buf.value.decode()
+
+
+def ht_layout_eval(layout: str, coord) -> int:
+    if not isinstance(coord, str):
+        coord = _coord_str(coord)
+    out = ctypes.c_int64()
+    _lcheck(lib().ht_layout_eval(layout.encode(), coord.encode(), ctypes.byref(out)), "ht_layout_eval")
+    return out.value
+
+
+def _coord_str(c):
+    if isinstance(c, (tuple, list)):
+        return "(" + ",".join(_coord_str(x) for x in c) + ")"
+    return str(int(c))
+
+
+def ht_layout_size(layout: str) -> int:
+    out = ctypes.c_int64()
+    _lcheck(lib().ht_layout_size(layout.encode(), ctypes.byref(out)), "ht_layout_size")
+    return out.value
+
+
+def ht_layout_table(layout: str):
+    n = ht_layout_size(layout)
+    arr = (ctypes.c_int64 * max(n, 1))()
+    _lcheck(lib().ht_layout_table(layout.encode(), arr, n), "ht_layout_table")
+    return list(arr[:n])
+
+
+def ht_layout_coalesce(layout: str) -> str:
+    return _out_str(lib().ht_layout_coalesce, layout.encode())
+
+
+def ht_layout_compose(a: str, b: str) -> str:
+    return _out_str(lib().ht_layout_compose, a.encode(), b.encode())
+
+
+def ht_layout_complement(a: str, m: int) -> str:
+    return _out_str(lib().ht_layout_complement, a.encode(), int(m))
+
+
+def ht_layout_logical_divide(a: str, b: str) -> str:
+    return _out_str(lib().ht_layout_logical_divide, a.encode(), b.encode())
+
+
+def ht_layout_zipped_divide(a: str, t0: str, t1: str) -> str:
+    return _out_str(lib().ht_layout_zipped_divide, a.encode(), t0.encode(), t1.encode())
+
+
+def ht_swizzle(offset: int, bbits: int, mbase: int, sshift: int) -> int:
+    return lib().ht_swizzle(offset, bbits, mbase, sshift)
+
+
+def ht_tile_plan(m, n, k, bytes_per_elem, budget_bytes) -> ht_tile_stats:
+    st = ht_tile_stats()
+    _lcheck(lib().ht_tile_plan(m, n, k, bytes_per_elem, budget_bytes, ctypes.byref(st)), "ht_tile_plan")
+    return st
+
+
+def ht_pipeline_time(n, load, compute) -> float:
+    return lib().ht_pipeline_time(n, load, compute)

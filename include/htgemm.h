@@ -1,0 +1,145 @@
+/*
+ * htgemm.h -- C ABI of the MI355X (gfx950) hierarchically tiled GEMM library.
+ *
+ * Operation (all entry points below compute or describe this one operation):
+ *
+ *     D = act( alpha * scale_a * scale_b * (A @ B)  +  beta * C  +  bias )
+ *
+ * with A an M x K matrix, B a K x N matrix, C and D M x N matrices and bias a length-N vector
+ * added to every row.  This is the GEMM the reference pages are built around ("CUTLASS",
+ * stanleyjacob.dev, Part I "The mental model": D = alpha * (A @ B) + beta * C; Part II "Using
+ * it": the problem shape, a {pointer, leading dimension} per operand and {alpha, beta}, checked
+ * against a success status).  The epilogue order -- alpha/beta, then bias, then activation --
+ * follows the same page's Part I diagram and Part IV Stage 5 ("The epilogue and fusion"); the
+ * per-tensor dequantisation scales of a narrow-type GEMM are folded into the epilogue as the
+ * page's Part V "Data types and quantization" describes.  Products accumulate in fp32 whatever
+ * the operand type.
+ *
+ * Handle life cycle ("CUTLASS", Part IV Stage 1: get_workspace_size, can_implement, initialize,
+ * run; and "CUTLASS, CuTe, and CUDA Tile", section "Assembling a CUTLASS kernel": a stateful,
+ * reusable handle whose kernel chooses its own grid):
+ *   gemm_create         validates the problem ("can_implement") and picks a kernel from the
+ *                       tile table; it allocates host memory only.
+ *   gemm_workspace_size reports the device scratch the caller must pass to gemm_run (0 here).
+ *   gemm_run            enqueues the kernel on the caller's HIP stream; asynchronous.
+ *   gemm_destroy        frees the handle.
+ *
+ * Ownership: the caller owns every device buffer (A, B, C, D, bias, workspace) and the stream.
+ * A handle holds host memory only and is immutable after gemm_create, so one handle may be run
+ * concurrently on several streams.  Nothing throws across this interface; every function returns
+ * a status code (GEMM_OK == 0) that gemm_status_string() describes.
+ *
+ * Element addressing: element (i, j) of an operand with strides (s0, s1) is at element offset
+ * i * s0 + j * s1 from its base pointer.  Each of A and B must have one unit stride (row-major A
+ * has a_stride_k == 1; column-major B has b_stride_k == 1).  C and D may have any strides.
+ * D may alias C only when their strides are identical; any other overlap is undefined.
+ *
+ * Conventions where the pages are silent:
+ *   - beta == 0 means C is not read at all (C may be NULL; NaNs in C do not propagate).
+ *   - alpha == 0 is not special-cased: NaN or Inf in A or B still propagate through 0 * x.
+ *   - GELU is the exact form x * Phi(x) = 0.5 * x * (1 + erf(x / sqrt(2))).
+ *   - fp8 is OCP E4M3 ("fn": bias 7, max 448, no infinities); outputs round to nearest even.
+ *   - M == 0 or N == 0 is a valid empty problem; K == 0 gives D = act(beta*C + bias).
+ *
+ * Supported type combinations (A and B share a type; C, D and bias share the output type):
+ *     A/B      C/D/bias
+ *     f32      f32
+ *     f16      f16
+ *     bf16     bf16
+ *     e4m3     bf16
+ */
+#ifndef HTGEMM_H
+#define HTGEMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ---------------------------------------------------------------------- */
+enum {
+  GEMM_OK = 0,
+  GEMM_ERR_INVALID_ARG = 1,  /* NULL pointer, negative size, missing C with beta != 0, ...   */
+  GEMM_ERR_DTYPE_COMBO = 2,  /* type combination not in the table above                       */
+  GEMM_ERR_LAYOUT = 3,       /* an operand of A or B has no unit stride                         */
+  GEMM_ERR_MISALIGNED = 4,   /* a pointer is not aligned to its element size                    */
+  GEMM_ERR_ARCH = 5,         /* the current device is not gfx950                                 */
+  GEMM_ERR_LAUNCH = 6,       /* the kernel launch failed (hipGetLastError)                       */
+  GEMM_ERR_BAD_HANDLE = 7,   /* NULL or destroyed handle                                         */
+  GEMM_ERR_NO_CONFIG = 8,    /* the forced tile-table entry cannot run this problem              */
+  GEMM_ERR_HIP = 9           /* another HIP runtime error (device query failed, ...)            */
+};
+
+/* ---- element types and activations ----------------------------------------------------- */
+typedef enum { GEMM_F32 = 0, GEMM_F16 = 1, GEMM_BF16 = 2, GEMM_F8E4M3 = 3 } gemm_dtype;
+typedef enum { GEMM_ACT_NONE = 0, GEMM_ACT_RELU = 1, GEMM_ACT_GELU = 2 } gemm_act;
+
+/* ---- problem descriptor ------------------------------------------------------------------ */
+typedef struct gemm_desc {
+  int64_t M, N, K;            /* problem shape; each >= 0                                       */
+  int32_t a_type, b_type;     /* gemm_dtype of A and B                                           */
+  int32_t c_type, d_type;     /* gemm_dtype of C (ignored if has_c == 0) and D                   */
+  int32_t bias_type;          /* gemm_dtype of bias (ignored if has_bias == 0)                   */
+  int32_t has_c;              /* 1: gemm_run reads C whenever beta != 0                          */
+  int32_t has_bias;           /* 1: add bias[n] to every row                                     */
+  int32_t act;                /* gemm_act, applied last                                          */
+  int64_t a_stride_m, a_stride_k;   /* A(m, k) at A[m * a_stride_m + k * a_stride_k]            */
+  int64_t b_stride_k, b_stride_n;   /* B(k, n) at B[k * b_stride_k + n * b_stride_n]            */
+  int64_t c_stride_m, c_stride_n;   /* C(m, n); ignored if has_c == 0                            */
+  int64_t d_stride_m, d_stride_n;   /* D(m, n)                                                    */
+  int32_t force_config;       /* -1: choose from the tile table; else a table index (tuning)     */
+  int32_t reserved;           /* must be 0                                                       */
+} gemm_desc;
+
+typedef struct gemm_handle_s* gemm_t;
+
+/* Validate `desc` and pick a kernel.  On success *out is a new handle.  Host-only: allocates
+ * no device memory and launches nothing.  Errors: GEMM_ERR_INVALID_ARG, GEMM_ERR_DTYPE_COMBO,
+ * GEMM_ERR_LAYOUT, GEMM_ERR_ARCH, GEMM_ERR_NO_CONFIG, GEMM_ERR_HIP. */
+int gemm_create(const gemm_desc* desc, gemm_t* out);
+
+/* Bytes of device workspace gemm_run needs for this handle (currently always 0). */
+int gemm_workspace_size(gemm_t h, size_t* bytes);
+
+/* Enqueue D = act(alpha*scale_a*scale_b*(A@B) + beta*C + bias) on `stream` (a hipStream_t;
+ * NULL is the default stream).  A, B, D are device pointers; C may be NULL when beta == 0 or the
+ * handle was created with has_c == 0 (then beta must be 0); bias must be non-NULL iff the handle
+ * has has_bias == 1.  scale_a and scale_b are the per-tensor dequantisation scales (pass 1.0f for
+ * non-fp8 operands).  Pointers only need element alignment: the library falls back to a
+ * narrow-load kernel when a pointer is not 16-byte aligned.  Returns after the launch is queued;
+ * launch failures return GEMM_ERR_LAUNCH. */
+int gemm_run(gemm_t h, const void* A, const void* B, const void* C, void* D, const void* bias,
+             float alpha, float beta, float scale_a, float scale_b, void* workspace,
+             void* stream);
+
+/* Free a handle.  NULL is accepted. */
+int gemm_destroy(gemm_t h);
+
+/* Static text for a status code. */
+const char* gemm_status_string(int status);
+
+/* ---- introspection (tile table) --------------------------------------------------------- */
+typedef struct gemm_info {
+  int32_t config;         /* tile-table index chosen for 16-byte aligned pointers             */
+  int32_t fallback;       /* index used when a pointer is not 16-byte aligned (may equal it)   */
+  int32_t bm, bn, bk;     /* workgroup tile                                                     */
+  int32_t waves;          /* waves per workgroup                                                */
+  int32_t stages;         /* LDS pipeline stages                                                */
+  int32_t lds_bytes;      /* LDS bytes per workgroup                                            */
+  int32_t split_k;        /* workgroups sharing one output tile along K (1: none)              */
+  int64_t grid;           /* workgroups per launch                                              */
+  char name[96];          /* kernel name                                                        */
+} gemm_info;
+
+int gemm_get_info(gemm_t h, gemm_info* info);
+
+/* Number of entries in the compiled tile table, and the name of entry `idx`. */
+int gemm_num_configs(void);
+int gemm_config_name(int idx, char* out, size_t cap);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* HTGEMM_H */

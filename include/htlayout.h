@@ -1,0 +1,96 @@
+/*
+ * htlayout.h -- host-side shape:stride layout functions and tile arithmetic (C ABI).
+ *
+ * A layout is a pair Shape:Stride of congruent (possibly nested) integer tuples; it is a function
+ * from a coordinate to an offset, the inner product of the natural coordinate with the stride.
+ * A single integer coordinate is first split over the shape with the leftmost mode fastest.
+ * Sources: "CUTLASS, CuTe, and CUDA Tile" (learn-kernels.com), introduction and "Partitioning:
+ * complement and divide"; "A10 - CuTe, CUTLASS & CuTile", sections 2 and 3.4; "CUTLASS"
+ * (stanleyjacob.dev), Part V "CuTe layout algebra".
+ *
+ * Layouts cross this interface as text in the pages' notation, for example "(4,3):(3,1)",
+ * "((2,2),3):((24,2),8)" or "12:1" (leading underscores as in "_12:_1" are accepted).
+ * Coordinates are text too: "(1,0)", "5", "(1,(0,1))"; an integer entry may stand for a whole
+ * nested mode and is split over it.
+ *
+ * Output strings are written to caller-owned buffers `out` of `cap` bytes, NUL-terminated;
+ * HT_ERR_CAPACITY means the buffer was too small (nothing useful is written).  Every function is
+ * pure host code, thread-safe and allocation-free from the caller's view.
+ */
+#ifndef HTLAYOUT_H
+#define HTLAYOUT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  HT_OK = 0,
+  HT_ERR_PARSE = 1,           /* text is not a layout / coordinate, or not congruent        */
+  HT_ERR_RANGE = 2,           /* coordinate outside the shape, or an argument out of range   */
+  HT_ERR_NOT_COMPOSABLE = 3,  /* the divisibility conditions of composition fail             */
+  HT_ERR_CAPACITY = 4,        /* output buffer too small                                      */
+  HT_ERR_NO_COMPLEMENT = 5    /* no ordered complement exists under the given size           */
+};
+
+/* Offset of coordinate `coord` in `layout` ("CUTLASS, CuTe, and CUDA Tile", introduction:
+ * (4,3):(3,1) maps (1,0) to 3 and (0,1) to 1). */
+int ht_layout_eval(const char* layout, const char* coord, int64_t* out);
+
+/* Number of coordinates (product of the shape). */
+int ht_layout_size(const char* layout, int64_t* out);
+
+/* The layout on 1-D coordinates 0 .. size-1, written to out[0 .. size-1]; cap is in elements. */
+int ht_layout_table(const char* layout, int64_t* out, int64_t cap);
+
+/* Shortest spelling of the same 1-D function: flatten, drop size-1 modes, merge neighbours
+ * (s0:d0)(s1:d1) whenever d1 == s0*d0 (introduction: coalesce of (2,(1,6)):(1,(6,2)) is 12:1). */
+int ht_layout_coalesce(const char* layout, char* out, size_t cap);
+
+/* Functional composition R = A o B, R(c) = A(B(c)), with R compatible with B (introduction:
+ * (6,2):(8,2) o (4,3):(3,1) = ((2,2),3):((24,2),8)).  HT_ERR_NOT_COMPOSABLE when a stride of B
+ * does not divide through A's modes or a size of B does not fit them. */
+int ht_layout_compose(const char* a, const char* b, char* out, size_t cap);
+
+/* complement(A, M): the ordered layout (positive increasing strides) whose image together with
+ * A's tiles 0 .. M-1 without overlap ("Partitioning: complement and divide":
+ * complement(4:1,24) = 6:4, complement(6:4,24) = 4:1). */
+int ht_layout_complement(const char* a, int64_t m, char* out, size_t cap);
+
+/* logical_divide(A, B) = A o (B, complement(B, size(A))): mode 0 is the tile B selects, mode 1
+ * iterates over the tiles ("Partitioning: complement and divide":
+ * logical_divide((4,2,3):(2,1,8), 4:2) = ((2,2),(2,3)):((4,1),(2,8))). */
+int ht_layout_logical_divide(const char* a, const char* b, char* out, size_t cap);
+
+/* zipped_divide of a rank-2 layout by one tiler per mode, "<t0,t1>" with each t a layout:
+ * ((tile0,tile1),(rest0,rest1)) -- tile modes first, rest modes second. */
+int ht_layout_zipped_divide(const char* a, const char* tiler0, const char* tiler1, char* out,
+                            size_t cap);
+
+/* Swizzle<BBits, MBase, SShift>: offset XOR ((offset & mask) >> SShift), where mask is BBits
+ * ones starting at bit MBase + SShift ("A10 - CuTe, CUTLASS & CuTile", section 3.4). */
+int64_t ht_swizzle(int64_t offset, int bbits, int mbase, int sshift);
+
+/* ---- tile arithmetic ("CuTe DSL / CUDA Tile" blog post, "A tile is a plan for reuse") ---- */
+typedef struct ht_tile_stats {
+  int64_t flops;              /* 2*m*n*k                                                      */
+  int64_t bytes;              /* b*(m*k + k*n + m*n): inputs read once, output written once    */
+  double intensity;           /* flops / bytes                                                 */
+  int64_t double_buffer_bytes;/* two stages of the A and B tiles: 2*b*(m*k + k*n)              */
+  int32_t fits;               /* double_buffer_bytes <= budget_bytes                           */
+} ht_tile_stats;
+
+int ht_tile_plan(int64_t m, int64_t n, int64_t k, int bytes_per_elem, int64_t budget_bytes,
+                 ht_tile_stats* out);
+
+/* Ideal two-engine pipeline time for n tiles ("Pipelining hides a wait only when another
+ * resource can work"): load + compute + (n - 1) * max(load, compute); n == 0 gives 0. */
+double ht_pipeline_time(int64_t n, double load, double compute);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* HTLAYOUT_H */

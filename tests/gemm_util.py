@@ -1,0 +1,146 @@
+"""Shared helpers for the GPU parity tests: build seeded inputs once, run the HIP library through
+its C ABI, and compute the oracle on the same bits."""
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+import torch
+
+import oracle
+from hierarchical_tiling_amd import htgemm as H
+from hierarchical_tiling_amd import inputs
+
+OUT_T = {"f32": "f32", "f16": "f16", "bf16": "bf16", "e4m3": "bf16"}
+# spec tolerances: fp32 relative Frobenius; 16-bit max-abs-relative; fp8 max-abs-relative
+TOL = {"f32": 1e-5, "f16": 1e-2, "bf16": 1e-2, "e4m3": 3e-2}
+
+
+@dataclasses.dataclass
+class Case:
+    M: int
+    N: int
+    K: int
+    dtype: str
+    a_order: str = "row"        # row-major A: unit stride along K
+    b_order: str = "col"        # column-major B: unit stride along K
+    dist: str = "normal"
+    std: float | None = None    # None: 1/sqrt(K) for normal draws
+    alpha: float = 1.0
+    beta: float = 0.0
+    has_c: bool = False
+    bias: bool = False
+    act: str = "none"
+    scale_a: float = 1.0
+    scale_b: float = 1.0
+    a_ld: int | None = None
+    b_ld: int | None = None
+    c_ld: int | None = None
+    d_ld: int | None = None
+    d_order: str = "row"
+    seed: int = 0
+    force: int = -1
+    a_offset: int = 0           # element offset of A's base pointer (misalignment tests)
+    c_fill_nan: bool = False
+
+
+def op(m):
+    return oracle.Operand(m.storage, m.dtype, m.shape, m.strides)
+
+
+class Prepared:
+    def __init__(self, case: Case, device="cuda"):
+        c = self.case = case
+        s = c.seed * 10
+        std = c.std if c.std is not None else (c.K ** -0.5 if c.K else 1.0)
+        kw = dict(std=std) if c.dist == "normal" else {}
+        self.A = inputs.matrix(s + 1, c.M, c.K, c.dtype, c.dist, order=c.a_order, ld=c.a_ld, **kw)
+        self.B = inputs.matrix(s + 2, c.K, c.N, c.dtype, c.dist, order=c.b_order, ld=c.b_ld, **kw)
+        ot = OUT_T[c.dtype]
+        self.C = None
+        if c.has_c:
+            if c.c_fill_nan:
+                nan_bits = oracle.encode_rne(ot, np.array([np.nan]))[0]
+                self.C = inputs.place(np.full(c.M * c.N, nan_bits), c.M, c.N, ot, "row", c.c_ld)
+            else:
+                cdist = "dyadic" if c.dist == "dyadic" else "uniform"
+                self.C = inputs.matrix(s + 3, c.M, c.N, ot, cdist, order="row", ld=c.c_ld)
+        self.bias = None
+        if c.bias:
+            bdist = "dyadic" if c.dist == "dyadic" else "normal"
+            self.bias = inputs.vector(s + 4, c.N, ot, bdist, **({"std": 0.1} if bdist == "normal" else {}))
+        d_strides, n = inputs.layout_strides(c.M, c.N, c.d_order, c.d_ld)
+        self.d_strides = d_strides
+        self.d_len = max(n, 1)
+        self.device = device
+        self.dA = self._upload(self.A, c.a_offset)
+        self.dB = inputs.to_device(self.B, device) if self.B.storage.size else torch.empty(1, device=device)
+        self.dC = inputs.to_device(self.C, device) if self.C is not None else None
+        self.dbias = inputs.to_device(self.bias, device) if self.bias is not None else None
+
+    def _upload(self, m, offset):
+        if m.storage.size == 0:
+            return (torch.empty(8, dtype=torch.uint8, device=self.device), 0)
+        es = inputs.ESIZE[m.dtype]
+        raw = np.zeros((m.storage.size + offset) * es, dtype=np.uint8)
+        raw[offset * es:] = m.storage.view(np.uint8)
+        t = torch.from_numpy(raw).to(self.device)
+        return (t, 0)
+
+    def desc(self):
+        c = self.case
+        return H.make_desc(c.M, c.N, c.K, c.dtype, self.A.strides, self.B.strides, self.d_strides,
+                           c_strides=self.C.strides if self.C is not None else None,
+                           has_bias=c.bias, act=c.act, force_config=c.force)
+
+    def run(self, g: H.Gemm | None = None, out=None):
+        c = self.case
+        g = g or H.Gemm(self.desc())
+        es_out = inputs.ESIZE[OUT_T[c.dtype]]
+        if out is None:
+            out = torch.zeros(self.d_len * es_out, dtype=torch.uint8, device=self.device)
+        a_ptr = self.dA[0].data_ptr() + c.a_offset * inputs.ESIZE[c.dtype]
+        g.run(a_ptr, self.dB, self.dC, out, self.dbias, alpha=c.alpha, beta=c.beta,
+              scale_a=c.scale_a, scale_b=c.scale_b)
+        torch.cuda.synchronize()
+        return g, out
+
+    def decode_out(self, out):
+        c = self.case
+        ot = OUT_T[c.dtype]
+        bits = out.cpu().numpy().view(inputs.STORAGE[ot])
+        vals = oracle.decode(ot, bits)
+        r = np.arange(c.M)[:, None] * self.d_strides[0] + np.arange(c.N)[None, :] * self.d_strides[1]
+        return vals[r], bits[r]
+
+    def oracle_full(self):
+        c = self.case
+        return oracle.gemm(op(self.A), op(self.B), op(self.C) if self.C is not None else None,
+                           op(self.bias) if self.bias is not None else None, alpha=c.alpha,
+                           beta=c.beta, scale_a=c.scale_a, scale_b=c.scale_b, act=c.act)
+
+    def oracle_elems(self, rows, cols):
+        c = self.case
+        return oracle.gemm_elems(op(self.A), op(self.B), rows, cols,
+                                 op(self.C) if self.C is not None else None,
+                                 op(self.bias) if self.bias is not None else None, alpha=c.alpha,
+                                 beta=c.beta, scale_a=c.scale_a, scale_b=c.scale_b, act=c.act)
+
+
+def error(dtype, got, want):
+    """The benchmark spec's metric for `dtype`: relative Frobenius (fp32) or max-abs-relative."""
+    got = np.asarray(got, dtype=np.float64)
+    want = np.asarray(want, dtype=np.float64)
+    if dtype == "f32":
+        return float(np.linalg.norm(got - want) / max(np.linalg.norm(want), 1e-300))
+    return float(np.abs(got - want).max() / max(np.abs(want).max(), 1e-300))
+
+
+def sample_indices(M, N, seed=0, n_rand=4096, n_rows=2, n_cols=2):
+    """Full rows and columns (first, last, random) plus random elements."""
+    rng = np.random.default_rng(seed)
+    rows_sel = sorted({0, M - 1, *rng.integers(0, M, n_rows).tolist()})
+    cols_sel = sorted({0, N - 1, *rng.integers(0, N, n_cols).tolist()})
+    r = [np.full(N, i) for i in rows_sel] + [np.arange(M) for _ in cols_sel] + [rng.integers(0, M, n_rand)]
+    c = [np.arange(N) for _ in rows_sel] + [np.full(M, j) for j in cols_sel] + [rng.integers(0, N, n_rand)]
+    return np.concatenate(r).astype(np.int64), np.concatenate(c).astype(np.int64)

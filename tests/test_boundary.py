@@ -1,0 +1,137 @@
+"""The C-ABI library loads, exports every entry point the headers declare, and validates
+descriptors on the host (no GPU needed: the device check is replaced by HTGEMM_FAKE_ARCH)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from hierarchical_tiling_amd import htgemm as H
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    names = set()
+    for hdr in ("htgemm.h", "htlayout.h"):
+        text = open(os.path.join(ROOT, "include", hdr)).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        for m in re.finditer(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s+(\w+)\s*\(", text, re.M):
+            names.add(m.group(1))
+    return names
+
+
+def test_every_declared_symbol_is_exported():
+    lib = ctypes.CDLL(H.LIB_PATH)
+    names = declared_functions()
+    assert {"gemm_create", "gemm_run", "gemm_destroy", "ht_layout_compose"} <= names
+    for n in sorted(names):
+        assert hasattr(lib, n), n
+    assert names == set(H.EXPORTED)
+
+
+@pytest.fixture
+def fake_gfx950(monkeypatch):
+    monkeypatch.setenv("HTGEMM_FAKE_ARCH", "gfx950")
+
+
+def desc(**kw):
+    base = dict(M=128, N=128, K=64, dtype="bf16", a_strides=(64, 1), b_strides=(1, 64),
+                d_strides=(128, 1))
+    base.update(kw)
+    return H.make_desc(**base)
+
+
+def status_of(d):
+    try:
+        h = H.gemm_create(d)
+    except H.GemmError as e:
+        return e.status
+    H.gemm_destroy(h)
+    return 0
+
+
+def test_status_strings():
+    assert H.gemm_status_string(0) == "success"
+    assert "gfx950" in H.gemm_status_string(5)
+    assert H.gemm_status_string(12345) == "unknown status"
+
+
+def test_valid_descriptor_creates(fake_gfx950):
+    assert status_of(desc()) == 0
+
+
+@pytest.mark.parametrize("mutate,status", [
+    (lambda d: setattr(d, "M", -1), 1),
+    (lambda d: setattr(d, "reserved", 3), 1),
+    (lambda d: setattr(d, "act", 7), 1),
+    (lambda d: setattr(d, "b_type", 1), 2),                      # A bf16 with B fp16
+    (lambda d: setattr(d, "d_type", 0), 2),                      # bf16 inputs, fp32 output
+    (lambda d: (setattr(d, "has_c", 1), setattr(d, "c_type", 1)), 2),
+    (lambda d: (setattr(d, "a_stride_m", 64), setattr(d, "a_stride_k", 2)), 3),  # no unit stride
+    (lambda d: setattr(d, "b_stride_n", -64), 3),
+    (lambda d: setattr(d, "force_config", 10000), 8),
+])
+def test_invalid_descriptors(fake_gfx950, mutate, status):
+    d = desc()
+    mutate(d)
+    assert status_of(d) == status
+
+
+def test_wrong_arch_is_refused(monkeypatch):
+    monkeypatch.setenv("HTGEMM_FAKE_ARCH", "gfx942")
+    assert status_of(desc()) == 5
+
+
+def test_destroyed_and_null_handles(fake_gfx950):
+    h = H.gemm_create(desc())
+    assert H.gemm_workspace_size(h) == 0
+    H.gemm_destroy(h)
+    assert H.lib().gemm_workspace_size(None, ctypes.byref(ctypes.c_size_t())) == 7
+    assert H.lib().gemm_run(None, None, None, None, None, None, 1.0, 0.0, 1.0, 1.0, None, None) == 7
+    assert H.lib().gemm_destroy(None) == 0
+
+
+def test_beta_without_c_and_empty_problem_on_host(fake_gfx950):
+    h = H.gemm_create(desc())
+    # beta != 0 with a handle that has no C: rejected before any device work
+    assert H.lib().gemm_run(h, 16, 16, None, 16, None, 1.0, 0.5, 1.0, 1.0, None, None) == 1
+    H.gemm_destroy(h)
+    h0 = H.gemm_create(desc(M=0))
+    # an empty problem returns success without touching the device
+    assert H.lib().gemm_run(h0, None, None, None, None, None, 1.0, 0.0, 1.0, 1.0, None, None) == 0
+    H.gemm_destroy(h0)
+
+
+def test_misaligned_pointer_is_rejected_on_host(fake_gfx950):
+    h = H.gemm_create(desc())
+    # bf16 pointers must be 2-byte aligned: an odd address is refused before any launch
+    assert H.lib().gemm_run(h, 4097, 8192, None, 8192, None, 1.0, 0.0, 1.0, 1.0, None, None) == 4
+    H.gemm_destroy(h)
+
+
+def _info(d):
+    h = H.gemm_create(d)
+    try:
+        return H.gemm_get_info(h)
+    finally:
+        H.gemm_destroy(h)
+
+
+def test_tile_table_choices(fake_gfx950):
+    names = [H.gemm_config_name(i) for i in range(H.gemm_num_configs())]
+    assert len(set(names)) == len(names)
+    big = _info(desc(M=8192, N=8192, K=8192, a_strides=(8192, 1), b_strides=(1, 8192), d_strides=(8192, 1)))
+    assert (big.bm, big.bn) == (256, 256) and big.name.startswith(b"bf16_ak_bk")
+    assert big.grid == 32 * 32
+    # ragged fp16 with odd leading dimensions: only the element-wise loader can read it
+    rag = _info(H.make_desc(4099, 3071, 2053, "f16", (2053, 1), (3071, 1), (3071, 1), c_strides=(3071, 1)))
+    assert b"narrow" in rag.name and rag.config == rag.fallback
+
+
+def test_forced_config_must_match(fake_gfx950):
+    names = [H.gemm_config_name(i) for i in range(H.gemm_num_configs())]
+    f16 = names.index("f16_ak_bk_128x128x64_w2x2_m32_vec")
+    assert status_of(desc(force_config=f16)) == 8      # bf16 problem, fp16 kernel
+    bf = names.index("bf16_ak_bk_128x128x64_w2x2_m32_narrow")
+    assert _info(desc(force_config=bf)).config == bf

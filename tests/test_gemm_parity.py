@@ -1,0 +1,190 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle on the same seeded bits.
+
+Tolerances are the spec ones: fp32 relative Frobenius <= 1e-5; bf16/fp16 max-abs-relative
+<= 1e-2; fp8 <= 3e-2 (max-abs-relative = max|D - O| / max|O|, with O the unrounded double
+oracle).  Dyadic inputs (multiples of 1/4, exact in every operand type) make every fp32 partial
+sum exact, so there the rounded result must match the oracle bit for bit in any summation order.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from hierarchical_tiling_amd import htgemm as H
+from tests.gemm_util import OUT_T, TOL, Case, Prepared, error, sample_indices
+
+pytestmark = pytest.mark.gpu
+
+
+def table():
+    return [H.gemm_config_name(i) for i in range(H.gemm_num_configs())]
+
+
+def case_for_entry(i, name):
+    dtype = name.split("_")[0]
+    a_order = "row" if "_ak_" in name else "col"
+    b_order = "col" if "_bk_" in name else "row"
+    vec = name.endswith("_vec")
+    # several tiles and a ragged tail in M and N; K spans several k-tiles with a tail
+    if vec:
+        M, N, K = 264, 328, 208 + (16 if dtype == "e4m3" else 0)
+    else:
+        M, N, K = 301, 257, 203
+    variant = i % 4
+    return Case(M=M, N=N, K=K, dtype=dtype, a_order=a_order, b_order=b_order, seed=i,
+                force=i, has_c=variant in (1, 3), beta=(-1.25 if variant in (1, 3) else 0.0),
+                alpha=0.75 if variant != 2 else 1.0, bias=variant >= 2,
+                act=["none", "none", "gelu", "relu"][variant],
+                scale_a=0.5 if dtype == "e4m3" else 1.0, scale_b=0.25 if dtype == "e4m3" else 1.0,
+                dist="normal" if dtype != "f32" else "uniform")
+
+
+@pytest.mark.parametrize("idx", range(len(table())) if os.path.exists(H.LIB_PATH) else [],
+                         ids=lambda i: table()[i])
+def test_every_table_entry_matches_oracle(idx):
+    name = table()[idx]
+    c = case_for_entry(idx, name)
+    p = Prepared(c)
+    g, out = p.run()
+    assert g.info.config == idx
+    got, _ = p.decode_out(out)
+    want = p.oracle_full()
+    err = error(c.dtype, got, want)
+    print(f"{name}: {c.M}x{c.N}x{c.K} err={err:.3e}")
+    assert np.isfinite(got).all()
+    assert err <= TOL[c.dtype], (name, err)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16", "e4m3"])
+@pytest.mark.parametrize("layout", ["row-col", "row-row", "col-col", "col-row"])
+def test_dyadic_inputs_are_bit_exact(dtype, layout):
+    a_order, b_order = layout.split("-")
+    c = Case(M=200, N=136, K=320, dtype=dtype, a_order=a_order, b_order=b_order, dist="dyadic",
+             alpha=2.0, beta=0.5, has_c=True, bias=True, seed=7,
+             scale_a=0.5 if dtype == "e4m3" else 1.0, scale_b=2.0 if dtype == "e4m3" else 1.0)
+    p = Prepared(c)
+    _, out = p.run()
+    _, bits = p.decode_out(out)
+    want = oracle.encode_rne(OUT_T[dtype], p.oracle_full())
+    mism = int((bits != want).sum())
+    assert mism == 0, f"{mism} of {bits.size} outputs differ"
+
+
+# ---- the benchmark workloads at their full sizes ----------------------------------------------
+FULL = {
+    "fp32_256": Case(256, 256, 256, "f32", "row", "row", dist="uniform", alpha=1.5, beta=0.5,
+                     has_c=True, seed=1000),
+    "bf16_4096": Case(4096, 4096, 4096, "bf16", "row", "col", seed=2000),
+    "fp16_ragged": Case(4099, 3071, 2053, "f16", "row", "row", dist="uniform", alpha=0.75,
+                        beta=-1.25, has_c=True, seed=3000),
+    "bf16_8192_gelu": Case(8192, 8192, 8192, "bf16", "row", "col", bias=True, act="gelu",
+                           seed=4000),
+    "e4m3_skinny": Case(16, 16384, 8192, "e4m3", "row", "col", std=1.0, scale_a=0.05,
+                        scale_b=0.05, seed=5000),
+    "e4m3_8192": Case(8192, 8192, 8192, "e4m3", "row", "col", std=1.0, scale_a=0.05,
+                      scale_b=0.05, seed=5100),
+}
+
+
+@pytest.mark.parametrize("name", list(FULL))
+def test_benchmark_workloads(name):
+    c = FULL[name]
+    p = Prepared(c)
+    g, out = p.run()
+    got, _ = p.decode_out(out)
+    assert np.isfinite(got).all()
+    if c.M * c.N * c.K <= 256 ** 3 or c.M <= 16:
+        want, sel = p.oracle_full(), (slice(None), slice(None))
+    else:
+        rows, cols = sample_indices(c.M, c.N, seed=1)
+        want, sel = p.oracle_elems(rows, cols), (rows, cols)
+    err = error(c.dtype, got[sel], want)
+    print(f"{name}: {g.info.name.decode()} err={err:.3e}")
+    assert err <= TOL[c.dtype], err
+
+
+# ---- edge cases ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("shape", [(1, 1, 1), (1, 300, 17), (300, 1, 9), (7, 9, 1), (33, 65, 0)])
+def test_tiny_and_degenerate_shapes(shape):
+    M, N, K = shape
+    c = Case(M, N, K, "bf16", has_c=True, beta=0.5, bias=True, alpha=1.5, seed=11)
+    p = Prepared(c)
+    _, out = p.run()
+    got, _ = p.decode_out(out)
+    assert error("bf16", got, p.oracle_full()) <= TOL["bf16"]
+
+
+def test_beta_zero_ignores_nan_c():
+    c = Case(130, 140, 96, "f16", has_c=True, beta=0.0, c_fill_nan=True, seed=12)
+    p = Prepared(c)
+    _, out = p.run()
+    got, _ = p.decode_out(out)
+    assert np.isfinite(got).all()
+    assert error("f16", got, p.oracle_full()) <= TOL["f16"]
+
+
+def test_misaligned_pointer_uses_narrow_path_with_same_result():
+    base = Case(264, 264, 128, "bf16", seed=13)
+    p0 = Prepared(base)
+    g0, out0 = p0.run()
+    assert g0.info.name.decode().endswith("_vec")
+    shifted = Case(264, 264, 128, "bf16", seed=13, a_offset=1)   # A starts 2 bytes off 16
+    p1 = Prepared(shifted)
+    _, out1 = p1.run()
+    assert torch.equal(out0, out1) or error("bf16", p1.decode_out(out1)[0], p0.decode_out(out0)[0]) <= 1e-2
+    assert error("bf16", p1.decode_out(out1)[0], p1.oracle_full()) <= TOL["bf16"]
+
+
+def test_column_major_output_and_padded_leading_dims():
+    c = Case(190, 170, 150, "f32", "col", "row", dist="uniform", has_c=True, beta=-1.0,
+             a_ld=200, b_ld=180, c_ld=171, d_ld=197, d_order="col", seed=14)
+    p = Prepared(c)
+    _, out = p.run()
+    got, _ = p.decode_out(out)
+    assert error("f32", got, p.oracle_full()) <= TOL["f32"]
+
+
+def test_in_place_d_equals_c():
+    c = Case(256, 192, 128, "bf16", has_c=True, beta=1.0, alpha=-0.5, seed=15)
+    p = Prepared(c)
+    want = p.oracle_full()
+    g = H.Gemm(p.desc())
+    a_ptr = p.dA[0].data_ptr()
+    g.run(a_ptr, p.dB, p.dC, p.dC, None, alpha=c.alpha, beta=c.beta)
+    torch.cuda.synchronize()
+    got, _ = p.decode_out(p.dC.view(torch.uint8))
+    assert error("bf16", got, want) <= TOL["bf16"]
+
+
+def test_repeated_runs_are_bitwise_identical():
+    c = Case(1024, 768, 512, "bf16", bias=True, act="gelu", seed=16)
+    p = Prepared(c)
+    g, out1 = p.run()
+    _, out2 = p.run(g)
+    assert torch.equal(out1, out2)
+
+
+def test_fused_gelu_equals_gemm_then_gelu():
+    base = dict(M=512, N=384, K=256, dtype="bf16", bias=True, seed=17)
+    pf = Prepared(Case(act="gelu", **base))
+    pu = Prepared(Case(act="none", **base))
+    got_f, _ = pf.decode_out(pf.run()[1])
+    # unfused: the GEMM output in double through exact GELU, vs the fused kernel's output
+    from math import erf, sqrt
+    unf = pu.oracle_full()
+    gelu = np.vectorize(lambda x: 0.5 * x * (1.0 + erf(x / sqrt(2.0))))(unf)
+    assert error("bf16", got_f, gelu) <= TOL["bf16"]
+
+
+def test_error_does_not_grow_faster_than_sqrt_k():
+    errs = []
+    for K in (256, 1024, 4096):
+        c = Case(128, 128, K, "bf16", std=1.0, seed=18)
+        p = Prepared(c)
+        got, _ = p.decode_out(p.run()[1])
+        want = p.oracle_full()
+        errs.append(np.abs(got - want).max() / np.sqrt(K))
+    assert errs[2] <= 4 * errs[0] + 1e-12, errs
