@@ -89,7 +89,8 @@ def cpu_baseline(name, host_set, threads, budget_s=12.0):
     M, N, K, dt, ao, bo, dist, std, alpha, beta, has_c, bias, act, sa, sb = WORKLOADS[name]
     A, B, C, bv = host_set
     op = lambda m: oracle.Operand(m.storage, m.dtype, m.shape, m.strides) if m is not None else None  # noqa
-    rows_of = lambda m: np.repeat(np.arange(m), N), np.tile(np.arange(N), m)  # noqa: E731
+    def rows_of(m):
+        return np.repeat(np.arange(m), N), np.tile(np.arange(N), m)
 
     def run(m):
         r, c = rows_of(m)

@@ -146,16 +146,18 @@ template <> struct Atom<DT_F32, 32> {
   static constexpr int G = 2, UNITS = 1, PER_UNIT = 4, NACC = 16;
   typedef f32x16 acc_t;
   __device__ static void mma(acc_t& c, const u32x4* a, const u32x4* b, int sub) {
-    c = __builtin_amdgcn_mfma_f32_32x32x2f32(__builtin_bit_cast(float, a[0][sub]),
-                                             __builtin_bit_cast(float, b[0][sub]), c, 0, 0, 0);
+    // Bit-cast the whole chunk, then pick the element: this compiler folds a scalar bit-cast
+    // of an extracted u32 vector element to element 0.
+    const f32x4 av = __builtin_bit_cast(f32x4, a[0]), bv = __builtin_bit_cast(f32x4, b[0]);
+    c = __builtin_amdgcn_mfma_f32_32x32x2f32(av[sub], bv[sub], c, 0, 0, 0);
   }
 };
 template <> struct Atom<DT_F32, 16> {
   static constexpr int G = 4, UNITS = 1, PER_UNIT = 4, NACC = 4;
   typedef f32x4 acc_t;
   __device__ static void mma(acc_t& c, const u32x4* a, const u32x4* b, int sub) {
-    c = __builtin_amdgcn_mfma_f32_16x16x4f32(__builtin_bit_cast(float, a[0][sub]),
-                                             __builtin_bit_cast(float, b[0][sub]), c, 0, 0, 0);
+    const f32x4 av = __builtin_bit_cast(f32x4, a[0]), bv = __builtin_bit_cast(f32x4, b[0]);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(av[sub], bv[sub], c, 0, 0, 0);
   }
 };
 
