@@ -38,6 +38,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <utility>
+
 #include "gemm_internal.h"
 
 namespace htk {
@@ -80,6 +82,23 @@ template <> struct Out<DT_BF16> {
   __device__ static float load(const void* p, int64_t i) { return bf16_to_f32(((const u16*)p)[i]); }
   __device__ static void store(void* p, int64_t i, float v) { ((u16*)p)[i] = f32_to_bf16(v); }
 };
+
+// Compile-time loop: the body sees its index as a constant, so register arrays indexed by it
+// stay in registers (a runtime index would force the array into scratch memory).
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F> __device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// Output element bits.
+template <int ODT> struct OutBits { typedef u16 T; };
+template <> struct OutBits<DT_F32> { typedef u32 T; };
+__device__ __forceinline__ u16 to_bits(float v, std::integral_constant<int, DT_BF16>) { return f32_to_bf16(v); }
+__device__ __forceinline__ u16 to_bits(float v, std::integral_constant<int, DT_F16>) { return f32_to_f16(v); }
+__device__ __forceinline__ u32 to_bits(float v, std::integral_constant<int, DT_F32>) { return __builtin_bit_cast(u32, v); }
 
 // ------------------------------------------------------------------------------------------
 // MFMA atoms.  G: lane groups along k (64 / MI); UNITS: 16-byte chunks per lane per operand per
@@ -437,29 +456,67 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_tiled(const KParams p) {
     }
   }
 
-  // ---- epilogue: alpha, beta*C, bias[n], activation, one rounding, predicated store ----
+  // ---- epilogue ("CUTLASS", Part IV Stages 5 and 6) ----
+  // Phase 1, in registers: y = act(alpha * acc + beta * C + bias[n]) in fp32, rounded once to the
+  // output type.  Phase 2: the rounded tile goes through LDS so the store to D is 16-byte
+  // row-contiguous chunks instead of the MFMA's column-wise lane layout.
   constexpr int ODT = out_dtype(DT);
   typedef Out<ODT> O;
+  typedef typename OutBits<ODT>::T OT;
+  constexpr int OSZ = (int)sizeof(OT);
+  constexpr bool REPACK = BM * BN * OSZ <= (int)sizeof(lds);
   const bool has_c = p.has_c != 0, has_bias = p.has_bias != 0;
-#pragma unroll
-  for (int i = 0; i < RM; ++i)
-#pragma unroll
-    for (int j = 0; j < RN; ++j) {
-      const int64_t col = n0 + wn * WTN + j * MI + (lane % MI);
+  const int act = p.act;
+  const float alpha = p.alpha, beta = p.beta;
+  OT* tile = reinterpret_cast<OT*>(&lds[0][0]);  // BM x BN, row-major (REPACK only)
+  if (REPACK && nk == 0) __syncthreads();
+  static_for<RM>([&](auto i) {
+    static_for<RN>([&](auto j) {
+      const int lc = wn * WTN + j * MI + (lane % MI);
+      const int64_t col = n0 + lc;
       const bool col_ok = col < p.N;
       const float bv = (has_bias && col_ok) ? O::load(p.bias, col) : 0.f;
-#pragma unroll
-      for (int r = 0; r < At::NACC; ++r) {
-        const int64_t row = m0 + wm * WTM + i * MI + acc_row<MI>(lane, r);
-        if (col_ok && row < p.M) {
-          float v = p.alpha * acc[i][j][r];
-          if (has_c) v += p.beta * O::load(p.C, row * p.c_sm + col * p.c_sn);
-          if (has_bias) v += bv;
-          v = activate(p.act, v);
-          O::store(p.D, row * p.d_sm + col * p.d_sn, v);
+      static_for<At::NACC>([&](auto r) {
+        const int lr = wm * WTM + i * MI + acc_row<MI>(lane, r);
+        const int64_t row = m0 + lr;
+        float v = alpha * acc[i][j][(int)r];
+        if (has_c && col_ok && row < p.M) v += beta * O::load(p.C, row * p.c_sm + col * p.c_sn);
+        if (has_bias) v += bv;
+        v = activate(act, v);
+        if constexpr (REPACK) {
+          tile[lr * BN + lc] = to_bits(v, std::integral_constant<int, ODT>{});
+        } else {
+          if (col_ok && row < p.M) O::store(p.D, row * p.d_sm + col * p.d_sn, v);
         }
+      });
+    });
+  });
+  if constexpr (REPACK) {
+    __syncthreads();
+    constexpr int VO = 16 / OSZ;            // outputs per 16-byte chunk
+    constexpr int CPR = BN / VO;            // chunks per tile row
+    constexpr int NCH = BM * CPR;
+    static_assert(NCH % NT == 0, "output chunks must divide over the threads");
+    const bool vec_ok = p.d_sn == 1 && (p.d_sm * OSZ) % 16 == 0 &&
+                        (reinterpret_cast<uintptr_t>(p.D) % 16) == 0;
+    OT* dst = reinterpret_cast<OT*>(p.D);
+#pragma unroll
+    for (int it = 0; it < NCH / NT; ++it) {
+      const int q = tid + it * NT;
+      const int lr = q / CPR, lc = (q % CPR) * VO;
+      const int64_t row = m0 + lr, col = n0 + lc;
+      if (row >= p.M) continue;
+      const u32x4 val = *reinterpret_cast<const u32x4*>(&tile[lr * BN + lc]);
+      if (vec_ok && col + VO <= p.N) {
+        *reinterpret_cast<u32x4*>(dst + row * p.d_sm + col) = val;
+      } else {
+        const OT* e = reinterpret_cast<const OT*>(&val);
+#pragma unroll
+        for (int x = 0; x < VO; ++x)
+          if (col + x < p.N) dst[row * p.d_sm + (col + x) * p.d_sn] = e[x];
       }
     }
+  }
 }
 
 // ------------------------------------------------------------------------------------------
