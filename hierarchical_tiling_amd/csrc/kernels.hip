@@ -213,32 +213,56 @@ __device__ __forceinline__ float activate(int act, float v) {
 // ------------------------------------------------------------------------------------------
 // Tile loaders: global -> registers -> swizzled LDS.
 // LDS row r (an m of A or an n of B) holds BK elements as CH = BK*SZ/16 chunks.
+// Every loader has the same interface: init() once per tile, load<PRED>(k0) for the k-tile at
+// k0 (PRED: zero-fill elements at k >= K), store() into one LDS stage.
 // ------------------------------------------------------------------------------------------
+// Chunk slot of (row, chunk): the XOR key is (row >> 1) & 7.  A ds_read_b128 phase serves 16
+// lanes = 256 bytes = all 64 banks; the 16 lanes of an MFMA fragment read are 16 consecutive
+// rows at one logical chunk, and with this key their 16-byte chunks land on 16 different
+// 16-byte bank groups (rows 2m and 2m+1 differ in the 128-byte half, rows 2m..2m+14 in the XOR).
+// A 16-lane phase of the row-wise tile store covers two whole rows, also conflict free.
 template <int CH> __device__ __forceinline__ int lds_slot(int row, int chunk) {
   static_assert(CH % 8 == 0, "rows must be a multiple of 128 bytes");
-  return row * CH + (chunk ^ (row & 7));
+  return row * CH + (chunk ^ ((row >> 1) & 7));
 }
 
-// K-contiguous operand, 16-byte loads.  `rows` valid rows starting at row0 (clamped).
+// K-contiguous operand, 16-byte buffer loads.  The buffer descriptor starts at this tile's first
+// row and ends at the operand's last element, so rows past the end read as zero; the k advance
+// is a scalar offset.  The descriptor is rebuilt from uniform scalars at every load (SALU work):
+// kept in the loader object, the compiler can no longer prove it uniform and wraps each load in
+// a readfirstlane loop.  Needs (R*ld + K)*SZ < 2^31 (checked on the host).
 template <int DT, int R, int BKE, int NT>
 struct LoadKMajorVec {
   static constexpr int SZ = Ty<DT>::SZ, VE = 16 / SZ, CH = BKE * SZ / 16;
   static constexpr int N = R * CH / NT;
-  static_assert(R * CH % NT == 0, "tile chunks must divide over the threads");
+  static_assert(R * CH % NT == 0 && NT % CH == 0, "tile chunks must divide over the threads");
   u32x4 r[N];
+  const char* tile;   // first byte of this tile's first row (uniform)
+  int64_t ld, rows_left, K;
+  uint32_t voff;      // this thread's first chunk: row tid/CH, chunk tid%CH
+  int kc;             // element offset of this thread's chunk within a k-tile
+  __device__ __forceinline__ void init(const void* base, int64_t ld_, int64_t row0, int64_t rows,
+                                       int64_t K_, int tid) {
+    tile = (const char*)base + row0 * ld_ * SZ;
+    ld = ld_;
+    rows_left = rows - row0;
+    K = K_;
+    voff = (uint32_t)((tid / CH) * ld_ * SZ + (tid % CH) * 16);
+    kc = (tid % CH) * VE;
+  }
   template <bool PRED>
-  __device__ __forceinline__ void load(const void* base, int64_t ld, int64_t row0, int64_t rows,
-                                       int64_t k0, int64_t K, int tid) {
-    const typename Ty<DT>::T* src = (const typename Ty<DT>::T*)base;
+  __device__ __forceinline__ void load(int64_t k0) {
+    int64_t span = ((rows_left - 1) * ld + K) * SZ;
+    span = span > 0x7fffffff ? 0x7fffffff : (span < 0 ? 0 : span);
+    const __amdgpu_buffer_rsrc_t rsrc =
+        __builtin_amdgcn_make_buffer_rsrc((void*)tile, 0, (int)span, 0x00020000);
+    const int row_step = (int)((NT / CH) * ld * SZ);
+    const bool ok = !PRED || k0 + kc < K;
+    const uint32_t vo = ok ? voff : voff - kc * SZ;
 #pragma unroll
     for (int i = 0; i < N; ++i) {
-      const int q = tid + i * NT, row = q / CH, c = q % CH;
-      const int64_t gr = min(row0 + row, rows - 1);
-      const int64_t k = k0 + (int64_t)c * VE;
-      if (!PRED || k < K)
-        r[i] = *(const u32x4*)(src + gr * ld + k);
-      else
-        r[i] = u32x4{0, 0, 0, 0};
+      u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, vo, (int)(k0 * SZ) + i * row_step, 0);
+      r[i] = ok ? v : u32x4{0, 0, 0, 0};
     }
   }
   __device__ __forceinline__ void store(u32x4* lds, int tid) const {
@@ -260,11 +284,18 @@ struct LoadMNMajorVec {
   static_assert(BLOCKS % NT == 0 || (BLOCKS < NT && BLOCKS % 64 == 0),
                 "transpose blocks must cover whole waves");
   static_assert(SZ == 2 || SZ == 4, "register transpose supports 2- and 4-byte elements");
+  typedef typename Ty<DT>::T T;
   u32x4 r[N][VE];
+  const T* src;
+  int64_t ld, row0, rows, K;
+  int tid;
+  __device__ __forceinline__ void init(const void* base, int64_t ld_, int64_t row0_,
+                                       int64_t rows_, int64_t K_, int tid_) {
+    src = (const T*)base;
+    ld = ld_; row0 = row0_; rows = rows_; K = K_; tid = tid_;
+  }
   template <bool PRED>
-  __device__ __forceinline__ void load(const void* base, int64_t ld, int64_t row0, int64_t rows,
-                                       int64_t k0, int64_t K, int tid) {
-    const typename Ty<DT>::T* src = (const typename Ty<DT>::T*)base;
+  __device__ __forceinline__ void load(int64_t k0) {
 #pragma unroll
     for (int i = 0; i < N; ++i) {
       const int q = tid + i * NT, rb = q % (R / VE), kb = q / (R / VE);
@@ -280,7 +311,7 @@ struct LoadMNMajorVec {
       }
     }
   }
-  __device__ __forceinline__ void store(u32x4* lds, int tid) const {
+  __device__ __forceinline__ void store(u32x4* lds, int) const {
 #pragma unroll
     for (int i = 0; i < N; ++i) {
       const int q = tid + i * NT, rb = q % (R / VE), kb = q / (R / VE);
@@ -314,10 +345,16 @@ struct LoadNarrow {
   static constexpr int N = R * CH / NT;
   static_assert(R * CH % NT == 0, "tile chunks must divide over the threads");
   T e[N][VE];
+  const T* src;
+  int64_t ld, row0, rows, K;
+  int tid;
+  __device__ __forceinline__ void init(const void* base, int64_t ld_, int64_t row0_,
+                                       int64_t rows_, int64_t K_, int tid_) {
+    src = (const T*)base;
+    ld = ld_; row0 = row0_; rows = rows_; K = K_; tid = tid_;
+  }
   template <bool PRED>
-  __device__ __forceinline__ void load(const void* base, int64_t ld, int64_t row0, int64_t rows,
-                                       int64_t k0, int64_t K, int tid) {
-    const T* src = (const T*)base;
+  __device__ __forceinline__ void load(int64_t k0) {
 #pragma unroll
     for (int i = 0; i < N; ++i) {
       const int q = tid + i * NT;
@@ -333,7 +370,7 @@ struct LoadNarrow {
       }
     }
   }
-  __device__ __forceinline__ void store(u32x4* lds, int tid) const {
+  __device__ __forceinline__ void store(u32x4* lds, int) const {
 #pragma unroll
     for (int i = 0; i < N; ++i) {
       const int q = tid + i * NT;
@@ -378,8 +415,14 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_tiled(const KParams p) {
   constexpr int WTM = BM / WM, WTN = BN / WN; // wave tile
   constexpr int RM = WTM / MI, RN = WTN / MI; // atoms per wave tile
   constexpr int UPL = CH / At::G;             // chunks per lane per row per k-tile
+  constexpr int S = UPL / At::UNITS;          // fragment substeps per k-tile
   static_assert(UPL % At::UNITS == 0, "k-tile must hold whole atoms");
   static_assert(WTM % MI == 0 && WTN % MI == 0, "wave tile must hold whole atoms");
+  static_assert(S == 1 || S % 2 == 0, "fragment double buffering needs an even substep count");
+  // The next tile's staging registers are written to LDS (and the tile after it is requested)
+  // two substeps before the end of the current one, leaving the loads a whole k-tile of MFMA
+  // work to arrive.
+  constexpr int SW = S >= 2 ? S - 2 : 0;
 
   __shared__ u32x4 lds[2][(BM + BN) * CH];
 
@@ -390,69 +433,70 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_tiled(const KParams p) {
   const int wm = wave % WM, wn = wave / WM;
 
   acc_t acc[RM][RN];
-#pragma unroll
-  for (int i = 0; i < RM; ++i)
-#pragma unroll
-    for (int j = 0; j < RN; ++j) acc[i][j] = acc_t{};
+  static_for<RM>([&](auto i) { static_for<RN>([&](auto j) { acc[i][j] = acc_t{}; }); });
 
   typename PickLoader<DT, AK, VEC, BM, BKE, NT>::type la;
   typename PickLoader<DT, BKM, VEC, BN, BKE, NT>::type lb;
+  la.init(p.A, p.lda, m0, p.M, p.K, tid);
+  lb.init(p.B, p.ldb, n0, p.N, p.K, tid);
 
   const int nk = (int)((p.K + BKE - 1) / BKE);
   const int nfull = (int)(p.K / BKE);
 
-  // fragment addressing (chunk slots) for this lane
+  // fragment addressing: lane row within an atom, and lane group along k
   const int frow = lane % MI, fgrp = lane / MI;
+  u32x4 fa[2][RM][At::UNITS], fb[2][RN][At::UNITS];
+  auto read_frags = [&](auto buf, const u32x4* stage, auto sub) {
+    const u32x4* As = stage;
+    const u32x4* Bs = stage + BM * CH;
+    static_for<At::UNITS>([&](auto x) {
+      const int c = fgrp + At::G * (sub * At::UNITS + x);
+      static_for<RM>([&](auto i) { fa[buf][i][x] = As[lds_slot<CH>(wm * WTM + i * MI + frow, c)]; });
+      static_for<RN>([&](auto j) { fb[buf][j][x] = Bs[lds_slot<CH>(wn * WTN + j * MI + frow, c)]; });
+    });
+  };
+  auto load_tile = [&](int t) {
+    const int64_t k0 = (int64_t)t * BKE;
+    if (t < nfull) {
+      la.template load<false>(k0);
+      lb.template load<false>(k0);
+    } else {
+      la.template load<true>(k0);
+      lb.template load<true>(k0);
+    }
+  };
 
   if (nk > 0) {
-    if (nfull > 0) {
-      la.template load<false>(p.A, p.lda, m0, p.M, 0, p.K, tid);
-      lb.template load<false>(p.B, p.ldb, n0, p.N, 0, p.K, tid);
-    } else {
-      la.template load<true>(p.A, p.lda, m0, p.M, 0, p.K, tid);
-      lb.template load<true>(p.B, p.ldb, n0, p.N, 0, p.K, tid);
-    }
+    load_tile(0);
     la.store(lds[0], tid);
     lb.store(lds[0] + BM * CH, tid);
+    if (nk > 1) load_tile(1);
     __syncthreads();
+    read_frags(std::integral_constant<int, 0>{}, lds[0], std::integral_constant<int, 0>{});
 
     for (int kt = 0; kt < nk; ++kt) {
       const int cur = kt & 1;
-      if (kt + 1 < nk) {
-        const int64_t k0 = (int64_t)(kt + 1) * BKE;
-        if (kt + 1 < nfull) {
-          la.template load<false>(p.A, p.lda, m0, p.M, k0, p.K, tid);
-          lb.template load<false>(p.B, p.ldb, n0, p.N, k0, p.K, tid);
-        } else {
-          la.template load<true>(p.A, p.lda, m0, p.M, k0, p.K, tid);
-          lb.template load<true>(p.B, p.ldb, n0, p.N, k0, p.K, tid);
+      static_for<S>([&](auto s) {
+        constexpr int bf = (S == 1) ? 0 : (s & 1);
+        if constexpr (s + 1 < S)
+          read_frags(std::integral_constant<int, (s + 1) & 1>{}, lds[cur],
+                     std::integral_constant<int, s + 1>{});
+        if constexpr (s == SW) {
+          if (kt + 1 < nk) {
+            la.store(lds[cur ^ 1], tid);
+            lb.store(lds[cur ^ 1] + BM * CH, tid);
+            if (kt + 2 < nk) load_tile(kt + 2);
+          }
         }
-      }
-      const u32x4* As = lds[cur];
-      const u32x4* Bs = lds[cur] + BM * CH;
-#pragma unroll
-      for (int u = 0; u < UPL; u += At::UNITS) {
-        u32x4 fa[RM][At::UNITS], fb[RN][At::UNITS];
-#pragma unroll
-        for (int x = 0; x < At::UNITS; ++x) {
-          const int c = fgrp + At::G * (u + x);
-#pragma unroll
-          for (int i = 0; i < RM; ++i) fa[i][x] = As[lds_slot<CH>(wm * WTM + i * MI + frow, c)];
-#pragma unroll
-          for (int j = 0; j < RN; ++j) fb[j][x] = Bs[lds_slot<CH>(wn * WTN + j * MI + frow, c)];
-        }
-#pragma unroll
-        for (int s = 0; s < At::PER_UNIT; ++s)
-#pragma unroll
-          for (int i = 0; i < RM; ++i)
-#pragma unroll
-            for (int j = 0; j < RN; ++j) At::mma(acc[i][j], fa[i], fb[j], s);
-      }
-      if (kt + 1 < nk) {
-        la.store(lds[cur ^ 1], tid);
-        lb.store(lds[cur ^ 1] + BM * CH, tid);
-      }
+        static_for<At::PER_UNIT>([&](auto u) {
+          static_for<RM>([&](auto i) {
+            static_for<RN>([&](auto j) { At::mma(acc[i][j], fa[bf][i], fb[bf][j], u); });
+          });
+        });
+      });
       __syncthreads();
+      if (kt + 1 < nk)
+        read_frags(std::integral_constant<int, 0>{}, lds[cur ^ 1], std::integral_constant<int, 0>{});
     }
   }
 
