@@ -67,6 +67,12 @@ bool entry_fits(const KernelEntry& e, const gemm_handle_s& h, bool vec_a, bool v
   if (e.dtype != d.a_type) return false;
   if ((e.a_kmajor != 0) != h.a.kmajor || (e.b_kmajor != 0) != h.b.kmajor) return false;
   if (e.vec && !(vec_a && vec_b)) return false;
+  if (e.vec) {
+    // the 16-byte K-major loaders address one tile with 31-bit buffer offsets
+    const int64_t sz = dtype_size(e.dtype), lim = int64_t(1) << 31;
+    if (h.a.kmajor && (int64_t(e.bm) * h.a.ld + d.K) * sz >= lim) return false;
+    if (h.b.kmajor && (int64_t(e.bn) * h.b.ld + d.K) * sz >= lim) return false;
+  }
   ht_tile_stats st;
   ht_tile_plan(e.bm, e.bn, e.bk, dtype_size(e.dtype), kLdsBudget, &st);
   if (!st.fits) return false;  // double-buffered A and B tiles must fit the LDS budget

@@ -226,11 +226,21 @@ template <int CH> __device__ __forceinline__ int lds_slot(int row, int chunk) {
   return row * CH + (chunk ^ ((row >> 1) & 7));
 }
 
-// K-contiguous operand, 16-byte buffer loads.  The buffer descriptor starts at this tile's first
-// row and ends at the operand's last element, so rows past the end read as zero; the k advance
-// is a scalar offset.  The descriptor is rebuilt from uniform scalars at every load (SALU work):
-// kept in the loader object, the compiler can no longer prove it uniform and wraps each load in
-// a readfirstlane loop.  Needs (R*ld + K)*SZ < 2^31 (checked on the host).
+// Buffer descriptor over `bytes` bytes from `base` (gfx9 raw buffer: stride 0).  Loads whose
+// VGPR offset (plus instruction offset) is at or past `bytes` return zero and touch no memory.
+// The SGPR offset is added to the address but is not part of that range check, so it may only
+// carry offsets that stay inside a valid row (the k position); row offsets go in the base.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const char* base, int64_t bytes) {
+  bytes = bytes > 0x7fffffff ? 0x7fffffff : (bytes < 0 ? 0 : bytes);
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, (int)bytes, 0x00020000);
+}
+
+// K-contiguous operand, 16-byte buffer loads.  The descriptor starts at the tile's first row
+// and ends at the operand's last element; the row offset of each load is in the (range-checked)
+// VGPR offset, so rows past the end read as zero, and the k advance is the scalar offset.  The
+// descriptor is rebuilt from uniform scalars at every load (SALU work): kept in the loader
+// object, the compiler can no longer prove it uniform and wraps each load in a readfirstlane
+// loop.  Needs (R*ld + K)*SZ < 2^31 (checked on the host).
 template <int DT, int R, int BKE, int NT>
 struct LoadKMajorVec {
   static constexpr int SZ = Ty<DT>::SZ, VE = 16 / SZ, CH = BKE * SZ / 16;
@@ -238,30 +248,27 @@ struct LoadKMajorVec {
   static_assert(R * CH % NT == 0 && NT % CH == 0, "tile chunks must divide over the threads");
   u32x4 r[N];
   const char* tile;   // first byte of this tile's first row (uniform)
-  int64_t ld, rows_left, K;
-  uint32_t voff;      // this thread's first chunk: row tid/CH, chunk tid%CH
+  int64_t ld, span, K;
+  uint32_t voff;      // this thread's chunk within a group of NT/CH rows: row tid/CH, chunk tid%CH
   int kc;             // element offset of this thread's chunk within a k-tile
   __device__ __forceinline__ void init(const void* base, int64_t ld_, int64_t row0, int64_t rows,
                                        int64_t K_, int tid) {
     tile = (const char*)base + row0 * ld_ * SZ;
     ld = ld_;
-    rows_left = rows - row0;
+    span = ((rows - row0 - 1) * ld_ + K_) * SZ;  // bytes from the tile start to the last element
     K = K_;
     voff = (uint32_t)((tid / CH) * ld_ * SZ + (tid % CH) * 16);
     kc = (tid % CH) * VE;
   }
   template <bool PRED>
   __device__ __forceinline__ void load(int64_t k0) {
-    int64_t span = ((rows_left - 1) * ld + K) * SZ;
-    span = span > 0x7fffffff ? 0x7fffffff : (span < 0 ? 0 : span);
-    const __amdgpu_buffer_rsrc_t rsrc =
-        __builtin_amdgcn_make_buffer_rsrc((void*)tile, 0, (int)span, 0x00020000);
-    const int row_step = (int)((NT / CH) * ld * SZ);
+    const uint32_t row_step = (uint32_t)((NT / CH) * ld * SZ);
+    const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(tile, span);
     const bool ok = !PRED || k0 + kc < K;
-    const uint32_t vo = ok ? voff : voff - kc * SZ;
+    const uint32_t vo = ok ? voff : voff - kc * SZ;  // an invalid k chunk reads its row start
 #pragma unroll
     for (int i = 0; i < N; ++i) {
-      u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, vo, (int)(k0 * SZ) + i * row_step, 0);
+      u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, vo + i * row_step, (int)(k0 * SZ), 0);
       r[i] = ok ? v : u32x4{0, 0, 0, 0};
     }
   }
