@@ -57,6 +57,9 @@ int classify(int64_t s_row, int64_t s_k, Operand* op) {
 bool vec_ok(const Operand& op, int64_t rows, int64_t K, int dt) {
   const int sz = dtype_size(dt), ve = 16 / sz;
   if ((op.ld * sz) % 16 != 0) return false;
+  // Rows must not overlap: the buffer loaders' range check (on the row offset) then also bounds
+  // the k offset they add outside the check.
+  if (op.ld < (op.kmajor ? K : rows)) return false;
   if (op.kmajor) return K % ve == 0;
   if (dt == DT_F8) return false;  // no transposing vector loader for 1-byte elements
   return rows % ve == 0;
@@ -76,6 +79,7 @@ bool entry_fits(const KernelEntry& e, const gemm_handle_s& h, bool vec_a, bool v
   ht_tile_stats st;
   ht_tile_plan(e.bm, e.bn, e.bk, dtype_size(e.dtype), kLdsBudget, &st);
   if (!st.fits) return false;  // double-buffered A and B tiles must fit the LDS budget
+  if (e.lds_bytes > kLdsBudget) return false;
   return true;
 }
 
@@ -95,7 +99,10 @@ int choose(const gemm_handle_s& h, bool vec_a, bool vec_b, bool want_vec) {
     if (!entry_fits(e, h, vec_a, vec_b)) continue;
     const int64_t wg = cdiv(h.d.M, e.bm) * cdiv(h.d.N, e.bn);
     const int64_t area = int64_t(e.bm) * e.bn;
-    if (wg >= 256 && area > best_area) { best = i; best_area = area; }
+    if (wg >= 256 && (area > best_area || (area == best_area && e.stages > t[best].stages))) {
+      best = i;
+      best_area = area;
+    }
     if (wg > best_small_wg || (wg == best_small_wg && area > int64_t(t[best_small].bm) * t[best_small].bn)) {
       best_small = i;
       best_small_wg = wg;

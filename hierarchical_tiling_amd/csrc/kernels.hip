@@ -410,6 +410,78 @@ struct PickLoader<DT, false, true, R, BKE, NT> {
 };
 
 // ------------------------------------------------------------------------------------------
+// Epilogue ("CUTLASS", Part IV Stages 5 and 6).
+// Phase 1, in registers: y = act(alpha * acc + beta * C + bias[n]) in fp32, rounded once to the
+// output type.  Phase 2: the rounded tile goes through LDS so the store to D is 16-byte
+// row-contiguous chunks instead of the MFMA's column-wise lane layout.  The caller guarantees
+// that no wave still reads the LDS operand stages and no DMA into them is in flight.
+// ------------------------------------------------------------------------------------------
+template <int DT, int MI, int BM, int BN, int WTM, int WTN, int RM, int RN, int NT,
+          size_t LDS_BYTES, class AccT>
+__device__ __forceinline__ void epilogue(const KParams& p, AccT (&acc)[RM][RN], u32x4* lds,
+                                              int64_t m0, int64_t n0, int wm, int wn, int lane,
+                                              int tid, bool no_mainloop) {
+  typedef Atom<DT, MI> At;
+  constexpr int ODT = out_dtype(DT);
+  typedef Out<ODT> O;
+  typedef typename OutBits<ODT>::T OT;
+  constexpr int OSZ = (int)sizeof(OT);
+  constexpr bool REPACK = (size_t)BM * BN * OSZ <= LDS_BYTES;
+  const bool has_c = p.has_c != 0, has_bias = p.has_bias != 0;
+  const int act = p.act;
+  const float alpha = p.alpha, beta = p.beta;
+  OT* tile = reinterpret_cast<OT*>(lds);  // BM x BN, row-major (REPACK only)
+  if (REPACK && no_mainloop) __syncthreads();
+  static_for<RM>([&](auto i) {
+    static_for<RN>([&](auto j) {
+      const int lc = wn * WTN + j * MI + (lane % MI);
+      const int64_t col = n0 + lc;
+      const bool col_ok = col < p.N;
+      const float bv = (has_bias && col_ok) ? O::load(p.bias, col) : 0.f;
+      static_for<At::NACC>([&](auto r) {
+        const int lr = wm * WTM + i * MI + acc_row<MI>(lane, r);
+        const int64_t row = m0 + lr;
+        float v = alpha * acc[i][j][(int)r];
+        if (has_c && col_ok && row < p.M) v += beta * O::load(p.C, row * p.c_sm + col * p.c_sn);
+        if (has_bias) v += bv;
+        v = activate(act, v);
+        if constexpr (REPACK) {
+          tile[lr * BN + lc] = to_bits(v, std::integral_constant<int, ODT>{});
+        } else {
+          if (col_ok && row < p.M) O::store(p.D, row * p.d_sm + col * p.d_sn, v);
+        }
+      });
+    });
+  });
+  if constexpr (REPACK) {
+    __syncthreads();
+    constexpr int VO = 16 / OSZ;            // outputs per 16-byte chunk
+    constexpr int CPR = BN / VO;            // chunks per tile row
+    constexpr int NCH = BM * CPR;
+    static_assert(NCH % NT == 0, "output chunks must divide over the threads");
+    const bool vec_ok = p.d_sn == 1 && (p.d_sm * OSZ) % 16 == 0 &&
+                        (reinterpret_cast<uintptr_t>(p.D) % 16) == 0;
+    OT* dst = reinterpret_cast<OT*>(p.D);
+#pragma unroll
+    for (int it = 0; it < NCH / NT; ++it) {
+      const int q = tid + it * NT;
+      const int lr = q / CPR, lc = (q % CPR) * VO;
+      const int64_t row = m0 + lr, col = n0 + lc;
+      if (row >= p.M) continue;
+      const u32x4 val = *reinterpret_cast<const u32x4*>(&tile[lr * BN + lc]);
+      if (vec_ok && col + VO <= p.N) {
+        *reinterpret_cast<u32x4*>(dst + row * p.d_sm + col) = val;
+      } else {
+        const OT* e = reinterpret_cast<const OT*>(&val);
+#pragma unroll
+        for (int x = 0; x < VO; ++x)
+          if (col + x < p.N) dst[row * p.d_sm + (col + x) * p.d_sn] = e[x];
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------------
 // The tiled kernel.
 // ------------------------------------------------------------------------------------------
 template <int DT, bool AK, bool BKM, bool VEC, int BM, int BN, int BKE, int WM, int WN, int MI>
@@ -507,67 +579,196 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_tiled(const KParams p) {
     }
   }
 
-  // ---- epilogue ("CUTLASS", Part IV Stages 5 and 6) ----
-  // Phase 1, in registers: y = act(alpha * acc + beta * C + bias[n]) in fp32, rounded once to the
-  // output type.  Phase 2: the rounded tile goes through LDS so the store to D is 16-byte
-  // row-contiguous chunks instead of the MFMA's column-wise lane layout.
-  constexpr int ODT = out_dtype(DT);
-  typedef Out<ODT> O;
-  typedef typename OutBits<ODT>::T OT;
-  constexpr int OSZ = (int)sizeof(OT);
-  constexpr bool REPACK = BM * BN * OSZ <= (int)sizeof(lds);
-  const bool has_c = p.has_c != 0, has_bias = p.has_bias != 0;
-  const int act = p.act;
-  const float alpha = p.alpha, beta = p.beta;
-  OT* tile = reinterpret_cast<OT*>(&lds[0][0]);  // BM x BN, row-major (REPACK only)
-  if (REPACK && nk == 0) __syncthreads();
-  static_for<RM>([&](auto i) {
-    static_for<RN>([&](auto j) {
-      const int lc = wn * WTN + j * MI + (lane % MI);
-      const int64_t col = n0 + lc;
-      const bool col_ok = col < p.N;
-      const float bv = (has_bias && col_ok) ? O::load(p.bias, col) : 0.f;
-      static_for<At::NACC>([&](auto r) {
-        const int lr = wm * WTM + i * MI + acc_row<MI>(lane, r);
-        const int64_t row = m0 + lr;
-        float v = alpha * acc[i][j][(int)r];
-        if (has_c && col_ok && row < p.M) v += beta * O::load(p.C, row * p.c_sm + col * p.c_sn);
-        if (has_bias) v += bv;
-        v = activate(act, v);
-        if constexpr (REPACK) {
-          tile[lr * BN + lc] = to_bits(v, std::integral_constant<int, ODT>{});
-        } else {
-          if (col_ok && row < p.M) O::store(p.D, row * p.d_sm + col * p.d_sn, v);
-        }
+  epilogue<DT, MI, BM, BN, WTM, WTN, RM, RN, NT, sizeof(lds)>(p, acc, &lds[0][0], m0, n0, wm, wn,
+                                                              lane, tid, nk == 0);
+}
+
+// ------------------------------------------------------------------------------------------
+// The streaming kernel: global -> LDS by DMA (buffer_load ... lds), a ring of LDS stages.
+//
+// Each LDS stage holds the A and B tiles of one k-tile as 64-byte rows (BK = 64 / esize
+// elements).  A wave-wide buffer_load_dwordx4 with the lds modifier writes 64 lanes x 16 bytes
+// to one contiguous kilobyte of LDS (16 rows) without passing through registers, so the tiles
+// of the next STAGES-1 k-tiles can be in flight at once: the loads get about STAGES-1 k-tiles of
+// MFMA work to arrive instead of one ("CuTe DSL / CUDA Tile" post, "Pipelining hides a wait":
+// buffering lets the slower stage set the pace; "CUTLASS", Part IV Stage 4: the multistage ring
+// of shared-memory buffers).  Swizzle: chunk c of row r lives at slot c ^ ((r >> 2) & 3), so the
+// 16 consecutive rows one ds_read_b128 phase reads at one logical chunk hit 16 different
+// 16-byte bank groups; the DMA lane that owns a slot fetches the logical chunk that belongs
+// there.  Rows past M or N and chunks past K are out of the buffer's range and land as zeros.
+// ------------------------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+__device__ __forceinline__ int slot64(int row, int chunk) { return row * 4 + (chunk ^ ((row >> 2) & 3)); }
+
+// s_waitcnt with vmcnt = V (and lgkmcnt = 0 when LGKM0), other counters left free.
+template <int V, bool LGKM0>
+__device__ __forceinline__ void wait_counts() {
+  static_assert(V >= 0 && V < 64, "vmcnt range");
+  constexpr int imm = (V & 15) | (7 << 4) | ((LGKM0 ? 0 : 15) << 8) | ((V >> 4) << 14);
+  __builtin_amdgcn_s_waitcnt(imm);
+}
+
+// Workgroup barrier without a hardware memory fence (the waits above are explicit); the
+// single-thread signal fences only keep the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void barrier_nofence() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// Values that are the same in every lane, passed through readfirstlane so the compiler keeps
+// them in scalar registers (buffer descriptors must be scalar; a value it cannot prove uniform
+// gets a readfirstlane loop around every use).
+__device__ __forceinline__ int64_t uniform_i64(int64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ const char* uniform_ptr(const char* p) {
+  return (const char*)(uintptr_t)uniform_i64((int64_t)(uintptr_t)p);
+}
+
+template <int DT, int BM, int BN, int WM, int WN, int MI, int STAGES>
+__global__ __launch_bounds__(WM * WN * 64) void gemm_dma(const KParams p) {
+  typedef Atom<DT, MI> At;
+  typedef typename At::acc_t acc_t;
+  constexpr int NW = WM * WN, NT = NW * 64;
+  constexpr int SZ = Ty<DT>::SZ;
+  constexpr int CH = 4;                       // 64-byte LDS rows
+  constexpr int BKE = CH * 16 / SZ;           // elements per k-tile
+  constexpr int VE = 16 / SZ;
+  constexpr int WTM = BM / WM, WTN = BN / WN;
+  constexpr int RM = WTM / MI, RN = WTN / MI;
+  constexpr int UPL = CH / At::G;             // chunks per lane per row per k-tile
+  constexpr int S = UPL / At::UNITS;          // fragment substeps per k-tile
+  constexpr int DA = BM / 16 / NW, DB = BN / 16 / NW;  // DMA instructions per wave per k-tile
+  constexpr int DPT = DA + DB;
+  constexpr int STAGE = (BM + BN) * CH;       // chunks per stage
+  static_assert(UPL % At::UNITS == 0 && S >= 1, "k-tile must hold whole atoms");
+  static_assert(BM % (16 * NW) == 0 && BN % (16 * NW) == 0, "16-row DMA blocks per wave");
+  static_assert(STAGES >= 3 && (STAGES - 2) * DPT < 64, "stage count");
+  static_assert(RM % 2 == 0, "the last substep is issued in two halves");
+
+  __shared__ u32x4 lds[STAGES * STAGE];
+
+  // the wave index is uniform across a wave; saying so keeps M0 (the DMA's LDS address) scalar
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  int tm, tn;
+  tile_of(p, blockIdx.x, gridDim.x, tm, tn);
+  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+  const int wm = wave % WM, wn = wave / WM;
+
+  acc_t acc[RM][RN];
+  static_for<RM>([&](auto i) { static_for<RN>([&](auto j) { acc[i][j] = acc_t{}; }); });
+
+  // DMA addressing: lane l of a 16-row block fills slot l of a kilobyte, i.e. row l/4, slot
+  // l%4, which holds logical chunk (l%4) ^ ((l/16)%4).
+  const int dchunk = (lane & 3) ^ ((lane >> 4) & 3);
+  const int kc = dchunk * VE;
+  const char* a_tile = uniform_ptr((const char*)p.A + m0 * p.lda * SZ);
+  const char* b_tile = uniform_ptr((const char*)p.B + n0 * p.ldb * SZ);
+  const int64_t a_span = uniform_i64(((p.M - m0 - 1) * p.lda + p.K) * SZ);
+  const int64_t b_span = uniform_i64(((p.N - n0 - 1) * p.ldb + p.K) * SZ);
+  const uint32_t a_voff = (uint32_t)((lane >> 2) * p.lda * SZ + dchunk * 16);
+  const uint32_t b_voff = (uint32_t)((lane >> 2) * p.ldb * SZ + dchunk * 16);
+  const uint32_t a_blk = (uint32_t)(16 * p.lda * SZ), b_blk = (uint32_t)(16 * p.ldb * SZ);
+
+  const int nk = (int)((p.K + BKE - 1) / BKE);
+
+  // Tile t into stage t % STAGES.  Tiles past the end of K are all out of range (zeros) and are
+  // issued anyway so every wave always has the same number of DMA operations in flight.
+  auto dma = [&](int t) {
+    const int64_t k0 = (int64_t)t * BKE;
+    const bool ok = k0 + kc < p.K;
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(a_tile, a_span);
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(b_tile, b_span);
+    u32x4* st = lds + (t % STAGES) * STAGE;
+    static_for<DA>([&](auto i) {
+      const int blk = wave + NW * i;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t*)(st + blk * 64), 16,
+                                               ok ? a_voff + blk * a_blk : 0x80000000u,
+                                               (int)(k0 * SZ), 0, 0);
+    });
+    static_for<DB>([&](auto i) {
+      const int blk = wave + NW * i;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void_t*)(st + BM * CH + blk * 64), 16,
+                                               ok ? b_voff + blk * b_blk : 0x80000000u,
+                                               (int)(k0 * SZ), 0, 0);
+    });
+  };
+
+  const int frow = lane % MI, fgrp = lane / MI;
+  u32x4 fa[2][RM][At::UNITS], fb[2][RN][At::UNITS];
+  auto read_frags = [&](auto buf, const u32x4* st, auto sub) {
+    static_for<At::UNITS>([&](auto x) {
+      const int c = fgrp + At::G * (sub * At::UNITS + x);
+      static_for<RM>([&](auto i) { fa[buf][i][x] = st[slot64(wm * WTM + i * MI + frow, c)]; });
+      static_for<RN>([&](auto j) { fb[buf][j][x] = st[BM * CH + slot64(wn * WTN + j * MI + frow, c)]; });
+    });
+  };
+  auto mma_rows = [&](auto buf, auto i0, auto i1) {
+    static_for<At::PER_UNIT>([&](auto u) {
+      static_for<i1 - i0>([&](auto ii) {
+        static_for<RN>([&](auto j) { At::mma(acc[i0 + ii][j], fa[buf][i0 + ii], fb[buf][j], u); });
       });
     });
-  });
-  if constexpr (REPACK) {
-    __syncthreads();
-    constexpr int VO = 16 / OSZ;            // outputs per 16-byte chunk
-    constexpr int CPR = BN / VO;            // chunks per tile row
-    constexpr int NCH = BM * CPR;
-    static_assert(NCH % NT == 0, "output chunks must divide over the threads");
-    const bool vec_ok = p.d_sn == 1 && (p.d_sm * OSZ) % 16 == 0 &&
-                        (reinterpret_cast<uintptr_t>(p.D) % 16) == 0;
-    OT* dst = reinterpret_cast<OT*>(p.D);
-#pragma unroll
-    for (int it = 0; it < NCH / NT; ++it) {
-      const int q = tid + it * NT;
-      const int lr = q / CPR, lc = (q % CPR) * VO;
-      const int64_t row = m0 + lr, col = n0 + lc;
-      if (row >= p.M) continue;
-      const u32x4 val = *reinterpret_cast<const u32x4*>(&tile[lr * BN + lc]);
-      if (vec_ok && col + VO <= p.N) {
-        *reinterpret_cast<u32x4*>(dst + row * p.d_sm + col) = val;
-      } else {
-        const OT* e = reinterpret_cast<const OT*>(&val);
-#pragma unroll
-        for (int x = 0; x < VO; ++x)
-          if (col + x < p.N) dst[row * p.d_sm + (col + x) * p.d_sn] = e[x];
+  };
+
+  if (nk > 0) {
+    static_for<STAGES - 1>([&](auto t) { dma(t); });
+    wait_counts<(STAGES - 2) * DPT, true>();
+    barrier_nofence();
+    read_frags(std::integral_constant<int, 0>{}, lds, std::integral_constant<int, 0>{});
+
+    // One k-tile: DMA of tile t+STAGES-1, fragment substeps of tile t, and before its last half
+    // of MFMAs the barrier that makes tile t+1 readable.  KK is the parity of t when the
+    // fragment buffers alternate between tiles (an odd substep count).
+    auto tile_step = [&](int t, auto KK) {
+      // stage (t-1) % STAGES was released by the barrier that ended tile t-1
+      dma(t + STAGES - 1);
+      const u32x4* st = lds + (t % STAGES) * STAGE;
+      static_for<S>([&](auto s) {
+        constexpr int buf = (KK * S + s) & 1;
+        if constexpr (s + 1 < S) {
+          read_frags(std::integral_constant<int, buf ^ 1>{}, st, std::integral_constant<int, s + 1>{});
+          mma_rows(std::integral_constant<int, buf>{}, std::integral_constant<int, 0>{},
+                   std::integral_constant<int, RM>{});
+        } else {
+          mma_rows(std::integral_constant<int, buf>{}, std::integral_constant<int, 0>{},
+                   std::integral_constant<int, RM / 2>{});
+          // tile t+1 has landed once at most STAGES-2 tiles of DMA are still in flight
+          wait_counts<(STAGES - 2) * DPT, true>();
+          barrier_nofence();
+          // (after the last tile this reads a stale stage; the values are never used)
+          read_frags(std::integral_constant<int, buf ^ 1>{}, lds + ((t + 1) % STAGES) * STAGE,
+                     std::integral_constant<int, 0>{});
+          mma_rows(std::integral_constant<int, buf>{}, std::integral_constant<int, RM / 2>{},
+                   std::integral_constant<int, RM>{});
+        }
+      });
+    };
+    if constexpr (S % 2 == 0) {
+      for (int kt = 0; kt < nk; ++kt) tile_step(kt, std::integral_constant<int, 0>{});
+    } else {
+      int kt = 0;
+      for (; kt + 1 < nk; kt += 2) {
+        tile_step(kt, std::integral_constant<int, 0>{});
+        tile_step(kt + 1, std::integral_constant<int, 1>{});
       }
+      if (kt < nk) tile_step(kt, std::integral_constant<int, 0>{});
     }
+    wait_counts<0, true>();  // the zero-filled tiles issued past the end are still in flight
+    barrier_nofence();
   }
+  epilogue<DT, MI, BM, BN, WTM, WTN, RM, RN, NT, sizeof(lds)>(p, acc, lds, m0, n0, wm, wn, lane,
+                                                              tid, nk == 0);
+}
+
+template <int DT, int BM, int BN, int WM, int WN, int MI, int STAGES>
+static hipError_t launch_dma(const KParams& p, hipStream_t s, dim3 grid) {
+  hipLaunchKernelGGL((gemm_dma<DT, BM, BN, WM, WN, MI, STAGES>), grid, dim3(WM * WN * 64), 0, s, p);
+  return hipGetLastError();
 }
 
 // ------------------------------------------------------------------------------------------
@@ -583,6 +784,10 @@ static hipError_t launch_tiled(const KParams& p, hipStream_t s, dim3 grid) {
 #define HT_TILED(NAME, DT, AK, BKM, VEC, BM, BN, BKE, WM, WN, MI)                        \
   {NAME, DT, AK, BKM, VEC, 0, BM, BN, BKE, WM * WN, 2, 2 * (BM + BN) * BKE * Ty<DT>::SZ, 1, \
    &launch_tiled<DT, AK, BKM, VEC, BM, BN, BKE, WM, WN, MI>}
+
+#define HT_DMA(NAME, DT, BM, BN, WM, WN, MI, ST)                                               \
+  {NAME, DT, 1, 1, 1, 0, BM, BN, 64 / Ty<DT>::SZ, WM * WN, ST, ST * (BM + BN) * 64, 1,           \
+   &launch_dma<DT, BM, BN, WM, WN, MI, ST>}
 
 static const KernelEntry g_table[] = {
     // bf16, BK = 64 (128-byte LDS rows)
@@ -623,6 +828,11 @@ static const KernelEntry g_table[] = {
     HT_TILED("e4m3_ak_bn_128x128x128_w2x2_m32_narrow", DT_F8, 1, 0, 0, 128, 128, 128, 2, 2, 32),
     HT_TILED("e4m3_am_bk_128x128x128_w2x2_m32_narrow", DT_F8, 0, 1, 0, 128, 128, 128, 2, 2, 32),
     HT_TILED("e4m3_am_bn_128x128x128_w2x2_m32_narrow", DT_F8, 0, 0, 0, 128, 128, 128, 2, 2, 32),
+    // DMA-fed LDS rings (64-byte rows: BK = 32 for 16-bit types, 64 for fp8)
+    HT_DMA("bf16_ak_bk_256x256x32_w2x2_m32_dma4", DT_BF16, 256, 256, 2, 2, 32, 4),
+    HT_DMA("bf16_ak_bk_256x256x32_w2x2_m32_dma5", DT_BF16, 256, 256, 2, 2, 32, 5),
+    HT_DMA("f16_ak_bk_256x256x32_w2x2_m32_dma4", DT_F16, 256, 256, 2, 2, 32, 4),
+    HT_DMA("e4m3_ak_bk_256x256x64_w2x2_m32_dma4", DT_F8, 256, 256, 2, 2, 32, 4),
 };
 
 const KernelEntry* table() { return g_table; }

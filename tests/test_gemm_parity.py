@@ -26,7 +26,7 @@ def case_for_entry(i, name):
     dtype = name.split("_")[0]
     a_order = "row" if "_ak_" in name else "col"
     b_order = "col" if "_bk_" in name else "row"
-    vec = name.endswith("_vec")
+    vec = name.endswith("_vec") or "_dma" in name
     # several tiles and a ragged tail in M and N; K spans several k-tiles with a tail
     if vec:
         M, N, K = 264, 328, 208 + (16 if dtype == "e4m3" else 0)
