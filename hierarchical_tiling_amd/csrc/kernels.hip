@@ -599,7 +599,17 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_tiled(const KParams p) {
 // ------------------------------------------------------------------------------------------
 typedef __attribute__((address_space(3))) void lds_void_t;
 
-__device__ __forceinline__ int slot64(int row, int chunk) { return row * 4 + (chunk ^ ((row >> 2) & 3)); }
+// XOR key of a row: 16 consecutive rows (one ds_read_b128 phase) must cover all 16 16-byte
+// positions of a 256-byte bank window.  With 64-byte rows four rows share a window, so rows
+// r, r+4, r+8, r+12 need different keys: (r >> 2) & 3.  With 128-byte rows two rows share a
+// window: (r >> 1) & 7, as in the register-staged kernel.
+template <int CH> __device__ __forceinline__ int row_key(int row) {
+  static_assert(CH == 4 || CH == 8, "64- or 128-byte rows");
+  return CH == 4 ? ((row >> 2) & 3) : ((row >> 1) & 7);
+}
+template <int CH> __device__ __forceinline__ int dslot(int row, int chunk) {
+  return row * CH + (chunk ^ row_key<CH>(row));
+}
 
 // s_waitcnt with vmcnt = V (and lgkmcnt = 0 when LGKM0), other counters left free.
 template <int V, bool LGKM0>
@@ -629,25 +639,25 @@ __device__ __forceinline__ const char* uniform_ptr(const char* p) {
   return (const char*)(uintptr_t)uniform_i64((int64_t)(uintptr_t)p);
 }
 
-template <int DT, int BM, int BN, int WM, int WN, int MI, int STAGES>
-__global__ __launch_bounds__(WM * WN * 64) void gemm_dma(const KParams p) {
+template <int DT, int BM, int BN, int WM, int WN, int MI, int STAGES, int OCC, int CH>
+__global__ __launch_bounds__(WM * WN * 64, OCC) void gemm_dma(const KParams p) {
   typedef Atom<DT, MI> At;
   typedef typename At::acc_t acc_t;
   constexpr int NW = WM * WN, NT = NW * 64;
   constexpr int SZ = Ty<DT>::SZ;
-  constexpr int CH = 4;                       // 64-byte LDS rows
-  constexpr int BKE = CH * 16 / SZ;           // elements per k-tile
+  constexpr int BKE = CH * 16 / SZ;           // elements per k-tile (64- or 128-byte rows)
   constexpr int VE = 16 / SZ;
+  constexpr int RPB = 64 / CH;                // rows per 1-KiB DMA block
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int RM = WTM / MI, RN = WTN / MI;
   constexpr int UPL = CH / At::G;             // chunks per lane per row per k-tile
   constexpr int S = UPL / At::UNITS;          // fragment substeps per k-tile
-  constexpr int DA = BM / 16 / NW, DB = BN / 16 / NW;  // DMA instructions per wave per k-tile
+  constexpr int DA = BM / RPB / NW, DB = BN / RPB / NW;  // DMA instructions per wave per k-tile
   constexpr int DPT = DA + DB;
   constexpr int STAGE = (BM + BN) * CH;       // chunks per stage
   static_assert(UPL % At::UNITS == 0 && S >= 1, "k-tile must hold whole atoms");
-  static_assert(BM % (16 * NW) == 0 && BN % (16 * NW) == 0, "16-row DMA blocks per wave");
-  static_assert(STAGES >= 3 && (STAGES - 2) * DPT < 64, "stage count");
+  static_assert(BM % (RPB * NW) == 0 && BN % (RPB * NW) == 0, "whole DMA blocks per wave");
+  static_assert(STAGES >= 2 && (STAGES - 2) * DPT < 64, "stage count");
   static_assert(RM % 2 == 0, "the last substep is issued in two halves");
 
   __shared__ u32x4 lds[STAGES * STAGE];
@@ -662,17 +672,19 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_dma(const KParams p) {
   acc_t acc[RM][RN];
   static_for<RM>([&](auto i) { static_for<RN>([&](auto j) { acc[i][j] = acc_t{}; }); });
 
-  // DMA addressing: lane l of a 16-row block fills slot l of a kilobyte, i.e. row l/4, slot
-  // l%4, which holds logical chunk (l%4) ^ ((l/16)%4).
-  const int dchunk = (lane & 3) ^ ((lane >> 4) & 3);
-  const int kc = dchunk * VE;
+  // DMA addressing: lane l of a block fills slot l of a kilobyte, i.e. row l/CH, slot l%CH of
+  // the block, which holds logical chunk (l%CH) ^ key(row).
   const char* a_tile = uniform_ptr((const char*)p.A + m0 * p.lda * SZ);
   const char* b_tile = uniform_ptr((const char*)p.B + n0 * p.ldb * SZ);
   const int64_t a_span = uniform_i64(((p.M - m0 - 1) * p.lda + p.K) * SZ);
   const int64_t b_span = uniform_i64(((p.N - n0 - 1) * p.ldb + p.K) * SZ);
-  const uint32_t a_voff = (uint32_t)((lane >> 2) * p.lda * SZ + dchunk * 16);
-  const uint32_t b_voff = (uint32_t)((lane >> 2) * p.ldb * SZ + dchunk * 16);
-  const uint32_t a_blk = (uint32_t)(16 * p.lda * SZ), b_blk = (uint32_t)(16 * p.ldb * SZ);
+  // per-lane source of DMA instruction i (rows blk*RPB + lane/CH of the tile)
+  auto src_off = [&](int blk, int64_t ld, int& kc) -> uint32_t {
+    const int row = blk * RPB + lane / CH;
+    const int c = (lane % CH) ^ row_key<CH>(row);
+    kc = c * VE;
+    return (uint32_t)(row * ld * SZ + c * 16);
+  };
 
   const int nk = (int)((p.K + BKE - 1) / BKE);
 
@@ -680,20 +692,23 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_dma(const KParams p) {
   // issued anyway so every wave always has the same number of DMA operations in flight.
   auto dma = [&](int t) {
     const int64_t k0 = (int64_t)t * BKE;
-    const bool ok = k0 + kc < p.K;
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(a_tile, a_span);
     const __amdgpu_buffer_rsrc_t rb = make_rsrc(b_tile, b_span);
     u32x4* st = lds + (t % STAGES) * STAGE;
     static_for<DA>([&](auto i) {
       const int blk = wave + NW * i;
+      int kc;
+      const uint32_t off = src_off(blk, p.lda, kc);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t*)(st + blk * 64), 16,
-                                               ok ? a_voff + blk * a_blk : 0x80000000u,
+                                               k0 + kc < p.K ? off : 0x80000000u,
                                                (int)(k0 * SZ), 0, 0);
     });
     static_for<DB>([&](auto i) {
       const int blk = wave + NW * i;
+      int kc;
+      const uint32_t off = src_off(blk, p.ldb, kc);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void_t*)(st + BM * CH + blk * 64), 16,
-                                               ok ? b_voff + blk * b_blk : 0x80000000u,
+                                               k0 + kc < p.K ? off : 0x80000000u,
                                                (int)(k0 * SZ), 0, 0);
     });
   };
@@ -703,8 +718,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_dma(const KParams p) {
   auto read_frags = [&](auto buf, const u32x4* st, auto sub) {
     static_for<At::UNITS>([&](auto x) {
       const int c = fgrp + At::G * (sub * At::UNITS + x);
-      static_for<RM>([&](auto i) { fa[buf][i][x] = st[slot64(wm * WTM + i * MI + frow, c)]; });
-      static_for<RN>([&](auto j) { fb[buf][j][x] = st[BM * CH + slot64(wn * WTN + j * MI + frow, c)]; });
+      static_for<RM>([&](auto i) { fa[buf][i][x] = st[dslot<CH>(wm * WTM + i * MI + frow, c)]; });
+      static_for<RN>([&](auto j) { fb[buf][j][x] = st[BM * CH + dslot<CH>(wn * WTN + j * MI + frow, c)]; });
     });
   };
   auto mma_rows = [&](auto buf, auto i0, auto i1) {
@@ -751,12 +766,12 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_dma(const KParams p) {
     if constexpr (S % 2 == 0) {
       for (int kt = 0; kt < nk; ++kt) tile_step(kt, std::integral_constant<int, 0>{});
     } else {
-      int kt = 0;
-      for (; kt + 1 < nk; kt += 2) {
+      // Fragment buffers alternate between tiles: walk tiles in pairs.  An odd tile count runs
+      // one extra tile past K, which the DMA fills with zeros, so it adds exact zeros.
+      for (int kt = 0; kt < nk; kt += 2) {
         tile_step(kt, std::integral_constant<int, 0>{});
         tile_step(kt + 1, std::integral_constant<int, 1>{});
       }
-      if (kt < nk) tile_step(kt, std::integral_constant<int, 0>{});
     }
     wait_counts<0, true>();  // the zero-filled tiles issued past the end are still in flight
     barrier_nofence();
@@ -765,9 +780,10 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_dma(const KParams p) {
                                                               tid, nk == 0);
 }
 
-template <int DT, int BM, int BN, int WM, int WN, int MI, int STAGES>
+template <int DT, int BM, int BN, int WM, int WN, int MI, int STAGES, int OCC, int CH>
 static hipError_t launch_dma(const KParams& p, hipStream_t s, dim3 grid) {
-  hipLaunchKernelGGL((gemm_dma<DT, BM, BN, WM, WN, MI, STAGES>), grid, dim3(WM * WN * 64), 0, s, p);
+  hipLaunchKernelGGL((gemm_dma<DT, BM, BN, WM, WN, MI, STAGES, OCC, CH>), grid,
+                     dim3(WM * WN * 64), 0, s, p);
   return hipGetLastError();
 }
 
@@ -785,9 +801,9 @@ static hipError_t launch_tiled(const KParams& p, hipStream_t s, dim3 grid) {
   {NAME, DT, AK, BKM, VEC, 0, BM, BN, BKE, WM * WN, 2, 2 * (BM + BN) * BKE * Ty<DT>::SZ, 1, \
    &launch_tiled<DT, AK, BKM, VEC, BM, BN, BKE, WM, WN, MI>}
 
-#define HT_DMA(NAME, DT, BM, BN, WM, WN, MI, ST)                                               \
-  {NAME, DT, 1, 1, 1, 0, BM, BN, 64 / Ty<DT>::SZ, WM * WN, ST, ST * (BM + BN) * 64, 1,           \
-   &launch_dma<DT, BM, BN, WM, WN, MI, ST>}
+#define HT_DMA(NAME, DT, BM, BN, WM, WN, MI, ST, OCC, CH)                                      \
+  {NAME, DT, 1, 1, 1, 0, BM, BN, CH * 16 / Ty<DT>::SZ, WM * WN, ST, ST * (BM + BN) * CH * 16, 1, \
+   &launch_dma<DT, BM, BN, WM, WN, MI, ST, OCC, CH>}
 
 static const KernelEntry g_table[] = {
     // bf16, BK = 64 (128-byte LDS rows)
@@ -829,10 +845,20 @@ static const KernelEntry g_table[] = {
     HT_TILED("e4m3_am_bk_128x128x128_w2x2_m32_narrow", DT_F8, 0, 1, 0, 128, 128, 128, 2, 2, 32),
     HT_TILED("e4m3_am_bn_128x128x128_w2x2_m32_narrow", DT_F8, 0, 0, 0, 128, 128, 128, 2, 2, 32),
     // DMA-fed LDS rings (64-byte rows: BK = 32 for 16-bit types, 64 for fp8)
-    HT_DMA("bf16_ak_bk_256x256x32_w2x2_m32_dma4", DT_BF16, 256, 256, 2, 2, 32, 4),
-    HT_DMA("bf16_ak_bk_256x256x32_w2x2_m32_dma5", DT_BF16, 256, 256, 2, 2, 32, 5),
-    HT_DMA("f16_ak_bk_256x256x32_w2x2_m32_dma4", DT_F16, 256, 256, 2, 2, 32, 4),
-    HT_DMA("e4m3_ak_bk_256x256x64_w2x2_m32_dma4", DT_F8, 256, 256, 2, 2, 32, 4),
+    HT_DMA("bf16_ak_bk_256x256x32_w2x2_m32_dma4", DT_BF16, 256, 256, 2, 2, 32, 4, 1, 4),
+    HT_DMA("bf16_ak_bk_256x256x32_w2x2_m32_dma5", DT_BF16, 256, 256, 2, 2, 32, 5, 1, 4),
+    HT_DMA("f16_ak_bk_256x256x32_w2x2_m32_dma4", DT_F16, 256, 256, 2, 2, 32, 4, 1, 4),
+    HT_DMA("e4m3_ak_bk_256x256x64_w2x2_m32_dma4", DT_F8, 256, 256, 2, 2, 32, 4, 1, 4),
+    // two workgroups per CU: the other workgroup's waves keep the matrix cores busy while one
+    // waits at its barrier
+    HT_DMA("bf16_ak_bk_256x128x32_w2x2_m32_dma3_o2", DT_BF16, 256, 128, 2, 2, 32, 3, 2, 4),
+    HT_DMA("bf16_ak_bk_128x256x32_w2x2_m32_dma3_o2", DT_BF16, 128, 256, 2, 2, 32, 3, 2, 4),
+    HT_DMA("bf16_ak_bk_256x128x32_w4x1_m32_dma3_o2", DT_BF16, 256, 128, 4, 1, 32, 3, 2, 4),
+    // 128-byte rows: every DMA lane octet reads one whole cache line
+    HT_DMA("bf16_ak_bk_256x256x64_w2x2_m32_dma2", DT_BF16, 256, 256, 2, 2, 32, 2, 1, 8),
+    HT_DMA("bf16_ak_bk_256x128x64_w2x2_m32_dma3", DT_BF16, 256, 128, 2, 2, 32, 3, 1, 8),
+    HT_DMA("f16_ak_bk_256x256x64_w2x2_m32_dma2", DT_F16, 256, 256, 2, 2, 32, 2, 1, 8),
+    HT_DMA("e4m3_ak_bk_256x256x128_w2x2_m32_dma2", DT_F8, 256, 256, 2, 2, 32, 2, 1, 8),
 };
 
 const KernelEntry* table() { return g_table; }
