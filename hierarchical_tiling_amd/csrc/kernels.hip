@@ -859,6 +859,11 @@ static const KernelEntry g_table[] = {
     HT_DMA("bf16_ak_bk_256x128x64_w2x2_m32_dma3", DT_BF16, 256, 128, 2, 2, 32, 3, 1, 8),
     HT_DMA("f16_ak_bk_256x256x64_w2x2_m32_dma2", DT_F16, 256, 256, 2, 2, 32, 2, 1, 8),
     HT_DMA("e4m3_ak_bk_256x256x128_w2x2_m32_dma2", DT_F8, 256, 256, 2, 2, 32, 2, 1, 8),
+    // eight waves (two per SIMD): one wave's waits are covered by the other's MFMAs, and twice
+    // as many waves keep global loads in flight
+    HT_DMA("bf16_ak_bk_256x256x32_w2x4_m32_dma5", DT_BF16, 256, 256, 2, 4, 32, 5, 1, 4),
+    HT_DMA("bf16_ak_bk_256x256x32_w4x2_m32_dma5", DT_BF16, 256, 256, 4, 2, 32, 5, 1, 4),
+    HT_DMA("bf16_ak_bk_256x256x64_w2x4_m32_dma2", DT_BF16, 256, 256, 2, 4, 32, 2, 1, 8),
 };
 
 const KernelEntry* table() { return g_table; }
