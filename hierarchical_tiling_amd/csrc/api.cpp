@@ -70,6 +70,7 @@ bool entry_fits(const KernelEntry& e, const gemm_handle_s& h, bool vec_a, bool v
   if (e.dtype != d.a_type) return false;
   if ((e.a_kmajor != 0) != h.a.kmajor || (e.b_kmajor != 0) != h.b.kmajor) return false;
   if (e.vec && !(vec_a && vec_b)) return false;
+  if (e.skinny && d.M > e.bm) return false;  // the streaming kernel holds all M rows in one tile
   if (e.vec) {
     // the 16-byte K-major loaders address one tile with 31-bit buffer offsets
     const int64_t sz = dtype_size(e.dtype), lim = int64_t(1) << 31;
@@ -85,21 +86,25 @@ bool entry_fits(const KernelEntry& e, const gemm_handle_s& h, bool vec_a, bool v
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Heuristic choice among fitting entries: the largest tile that still gives at least one
-// workgroup per CU (256 CUs), else the tile with the most workgroups.
+// Heuristic choice among fitting entries.  A product with M <= 16 is bound by streaming B and
+// takes the skinny kernel when one fits.  Otherwise: the largest tile that still gives at least
+// one workgroup per CU (256 CUs), ties broken by the measured rank, else the tile with the most
+// workgroups.
 int choose(const gemm_handle_s& h, bool vec_a, bool vec_b, bool want_vec) {
   const KernelEntry* t = table();
+  for (int i = 0; i < table_size(); ++i)
+    if (t[i].skinny && (t[i].vec != 0) == want_vec && entry_fits(t[i], h, vec_a, vec_b)) return i;
   int best = -1;
   int64_t best_area = -1;
   int best_small = -1;
   int64_t best_small_wg = -1;
   for (int i = 0; i < table_size(); ++i) {
     const KernelEntry& e = t[i];
-    if ((e.vec != 0) != want_vec) continue;
+    if ((e.vec != 0) != want_vec || e.skinny) continue;
     if (!entry_fits(e, h, vec_a, vec_b)) continue;
     const int64_t wg = cdiv(h.d.M, e.bm) * cdiv(h.d.N, e.bn);
     const int64_t area = int64_t(e.bm) * e.bn;
-    if (wg >= 256 && (area > best_area || (area == best_area && e.stages > t[best].stages))) {
+    if (wg >= 256 && (area > best_area || (area == best_area && e.rank > t[best].rank))) {
       best = i;
       best_area = area;
     }

@@ -43,6 +43,7 @@ struct KernelEntry {
   int stages;         // LDS stages
   int lds_bytes;      // LDS per workgroup
   int max_split_k;    // largest split along K the kernel supports (1: none)
+  int rank;           // preference among entries with the same tile area (measured; higher wins)
   launch_fn launch;
 };
 

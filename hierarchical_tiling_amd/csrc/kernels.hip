@@ -677,7 +677,7 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void gemm_dma(const KParams p) {
   const char* a_tile = uniform_ptr((const char*)p.A + m0 * p.lda * SZ);
   const char* b_tile = uniform_ptr((const char*)p.B + n0 * p.ldb * SZ);
   const int64_t a_span = uniform_i64(((p.M - m0 - 1) * p.lda + p.K) * SZ);
-  const int64_t b_span = uniform_i64(((p.N - n0 - 1) * p.ldb + p.K) * SZ);
+  const int64_t b_span = uniform_i64(((min((int64_t)BN, p.N - n0) - 1) * p.ldb + p.K) * SZ);
   // per-lane source of DMA instruction i (rows blk*RPB + lane/CH of the tile)
   auto src_off = [&](int blk, int64_t ld, int& kc) -> uint32_t {
     const int row = blk * RPB + lane / CH;
@@ -788,6 +788,114 @@ static hipError_t launch_dma(const KParams& p, hipStream_t s, dim3 grid) {
 }
 
 // ------------------------------------------------------------------------------------------
+// The skinny kernel: M <= 16 (a decode-like product), bound by streaming B from HBM.
+//
+// "CUTLASS" (stanleyjacob.dev), Part III: a tall-skinny GEMM has too few output tiles to fill
+// the GPU and memory bandwidth, not the matrix units, sets the ceiling; splitting K over blocks
+// restores occupancy (Part IV Stage 6).  Here a workgroup of NW waves owns BN output columns and
+// all M rows; wave w reduces the w-th of NW slices of K, and the NW partial sums meet in LDS.
+// Every byte of B is used by exactly one MFMA, so B goes straight from HBM into registers (no
+// LDS staging); A (M x K, a few hundred KiB) stays in L2 and is read alongside.  Each wave keeps
+// U k-steps of loads in flight, and 16 waves per CU keep enough bytes in flight to cover HBM
+// latency.  Atoms: 16x16xKSTEP MFMA (16x16x128 e4m3, 16x16x32 bf16/fp16); lane l supplies row
+// (or column) l % 16 and the k-run of lane group l / 16.
+// ------------------------------------------------------------------------------------------
+template <int DT, int BN, int NW, int U>
+__global__ __launch_bounds__(NW * 64, 2) void gemm_skinny(const KParams p) {
+  typedef Atom<DT, 16> At;
+  typedef typename At::acc_t acc_t;  // 4 floats: rows 4*(l/16)+r, column l%16
+  constexpr int NT = NW * 64;
+  constexpr int SZ = Ty<DT>::SZ;
+  constexpr int LB = At::UNITS * 16;          // bytes per lane per operand per MFMA
+  constexpr int KSTEP = 4 * LB / SZ;          // elements of K per MFMA
+  constexpr int NB = BN / 16;                 // 16-column blocks per workgroup
+  static_assert(BN % 16 == 0 && At::PER_UNIT == 1, "16-column blocks, one MFMA per k-step");
+
+  __shared__ float part[NW][NB][16][16];      // per-wave partial sums
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t n0 = (int64_t)blockIdx.x * BN;
+  const int lr = lane & 15, lg = lane >> 4;
+
+  // K split: wave w owns k-steps [w*per, min((w+1)*per, nks))
+  const int64_t nks = (p.K + KSTEP - 1) / KSTEP;
+  const int64_t per = (nks + NW - 1) / NW;
+  const int64_t ks0 = wave * per;
+  const int64_t ks1 = min(ks0 + per, nks);
+
+  // A rows lr (zero past M); B columns n0 + 16*b + lr (zero past N, or past this workgroup's
+  // BN columns).  Offsets of a lane's k-run within a k-step: lg*LB bytes.  Both spans stay below
+  // 2^31 bytes (checked on the host), so the offset 0x80000000 is outside either descriptor.
+  const char* a_base = uniform_ptr((const char*)p.A);
+  const char* b_base = uniform_ptr((const char*)p.B + n0 * p.ldb * SZ);
+  const int64_t a_span = uniform_i64(((p.M - 1) * p.lda + p.K) * SZ);
+  const int64_t b_span = uniform_i64(((min((int64_t)BN, p.N - n0) - 1) * p.ldb + p.K) * SZ);
+  const uint32_t a_off = (uint32_t)(lr * p.lda * SZ + lg * LB);
+  const uint32_t b_off = (uint32_t)(lr * p.ldb * SZ + lg * LB);
+  const uint32_t b_blk = (uint32_t)(16 * p.ldb * SZ);
+
+  acc_t acc[NB];
+  static_for<NB>([&](auto b) { acc[b] = acc_t{}; });
+
+  for (int64_t ks = ks0; ks < ks1; ks += U) {
+    u32x4 fa[U][At::UNITS], fb[U][NB][At::UNITS];
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(a_base, a_span);
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(b_base, b_span);
+    // Chunks past K (or past this wave's slice) get an offset beyond every descriptor's range
+    // (spans are < 2^31 bytes), so the buffer unit returns zeros without touching memory and the
+    // loads need no select after them: all U k-steps of loads are in flight together.
+    static_for<U>([&](auto u) {
+      const int64_t k0 = (ks + u) * KSTEP;
+      const bool live = ks + u < ks1;
+      static_for<At::UNITS>([&](auto x) {
+        const int64_t kc = k0 + (lg * LB + x * 16) / SZ;  // first element of this 16-byte chunk
+        const bool ok = live && kc < p.K;
+        const uint32_t ko = (uint32_t)(k0 * SZ) + x * 16;
+        fa[u][x] = __builtin_amdgcn_raw_buffer_load_b128(ra, ok ? a_off + ko : 0x80000000u, 0, 0);
+        static_for<NB>([&](auto b) {
+          fb[u][b][x] = __builtin_amdgcn_raw_buffer_load_b128(
+              rb, ok ? b_off + b * b_blk + ko : 0x80000000u, 0, 0);
+        });
+      });
+    });
+    // keep the scheduler from sinking loads below MFMAs: every load of the group is issued
+    // before the first wait
+    __builtin_amdgcn_sched_barrier(0);
+    static_for<U>([&](auto u) {
+      static_for<NB>([&](auto b) { At::mma(acc[b], fa[u], fb[u][b], 0); });
+    });
+  }
+
+  // partial sums -> LDS; wave-parallel reduction over the NW waves; epilogue
+  static_for<NB>([&](auto b) {
+    static_for<4>([&](auto r) { part[wave][b][4 * lg + r][lr] = acc[b][(int)r]; });
+  });
+  __syncthreads();
+  constexpr int ODT = out_dtype(DT);
+  typedef Out<ODT> O;
+  for (int q = tid; q < 16 * BN; q += NT) {
+    const int row = q / BN, c = q % BN;
+    const int64_t col = n0 + c;
+    if (row >= p.M || col >= p.N) continue;
+    float sum = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) sum += part[w][c / 16][row][c % 16];
+    float v = p.alpha * sum;
+    if (p.has_c) v += p.beta * O::load(p.C, row * p.c_sm + col * p.c_sn);
+    if (p.has_bias) v += O::load(p.bias, col);
+    v = activate(p.act, v);
+    O::store(p.D, row * p.d_sm + col * p.d_sn, v);
+  }
+}
+
+template <int DT, int BN, int NW, int U>
+static hipError_t launch_skinny(const KParams& p, hipStream_t s, dim3) {
+  const dim3 grid((unsigned)((p.N + BN - 1) / BN));
+  hipLaunchKernelGGL((gemm_skinny<DT, BN, NW, U>), grid, dim3(NW * 64), 0, s, p);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------------------
 // Launchers and the tile table.
 // ------------------------------------------------------------------------------------------
 template <int DT, bool AK, bool BKM, bool VEC, int BM, int BN, int BKE, int WM, int WN, int MI>
@@ -798,17 +906,23 @@ static hipError_t launch_tiled(const KParams& p, hipStream_t s, dim3 grid) {
 }
 
 #define HT_TILED(NAME, DT, AK, BKM, VEC, BM, BN, BKE, WM, WN, MI)                        \
-  {NAME, DT, AK, BKM, VEC, 0, BM, BN, BKE, WM * WN, 2, 2 * (BM + BN) * BKE * Ty<DT>::SZ, 1, \
+  {NAME, DT, AK, BKM, VEC, 0, BM, BN, BKE, WM * WN, 2, 2 * (BM + BN) * BKE * Ty<DT>::SZ, 1, 0, \
    &launch_tiled<DT, AK, BKM, VEC, BM, BN, BKE, WM, WN, MI>}
 
-#define HT_DMA(NAME, DT, BM, BN, WM, WN, MI, ST, OCC, CH)                                      \
+#define HT_DMA(NAME, DT, BM, BN, WM, WN, MI, ST, OCC, CH, RANK)                                \
   {NAME, DT, 1, 1, 1, 0, BM, BN, CH * 16 / Ty<DT>::SZ, WM * WN, ST, ST * (BM + BN) * CH * 16, 1, \
-   &launch_dma<DT, BM, BN, WM, WN, MI, ST, OCC, CH>}
+   RANK, &launch_dma<DT, BM, BN, WM, WN, MI, ST, OCC, CH>}
+
+// Skinny entries: bm = 16 rows, bn columns per workgroup, bk = one MFMA k-step.
+#define HT_SKINNY(NAME, DT, BN, NW, U)                                                           \
+  {NAME, DT, 1, 1, 1, 1, 16, BN, 4 * Atom<DT, 16>::UNITS * 16 / Ty<DT>::SZ, NW, 1,             \
+   NW * (BN / 16) * 16 * 16 * 4, 1, 0, &launch_skinny<DT, BN, NW, U>}
 
 static const KernelEntry g_table[] = {
     // bf16, BK = 64 (128-byte LDS rows)
     HT_TILED("bf16_ak_bk_256x256x64_w2x2_m32_vec", DT_BF16, 1, 1, 1, 256, 256, 64, 2, 2, 32),
     HT_TILED("bf16_ak_bk_128x128x64_w2x2_m32_vec", DT_BF16, 1, 1, 1, 128, 128, 64, 2, 2, 32),
+    HT_TILED("bf16_ak_bk_256x256x64_w2x4_m32_vec", DT_BF16, 1, 1, 1, 256, 256, 64, 2, 4, 32),
     HT_TILED("bf16_ak_bn_256x256x64_w2x2_m32_vec", DT_BF16, 1, 0, 1, 256, 256, 64, 2, 2, 32),
     HT_TILED("bf16_ak_bn_128x128x64_w2x2_m32_vec", DT_BF16, 1, 0, 1, 128, 128, 64, 2, 2, 32),
     HT_TILED("bf16_am_bk_128x128x64_w2x2_m32_vec", DT_BF16, 0, 1, 1, 128, 128, 64, 2, 2, 32),
@@ -845,25 +959,30 @@ static const KernelEntry g_table[] = {
     HT_TILED("e4m3_am_bk_128x128x128_w2x2_m32_narrow", DT_F8, 0, 1, 0, 128, 128, 128, 2, 2, 32),
     HT_TILED("e4m3_am_bn_128x128x128_w2x2_m32_narrow", DT_F8, 0, 0, 0, 128, 128, 128, 2, 2, 32),
     // DMA-fed LDS rings (64-byte rows: BK = 32 for 16-bit types, 64 for fp8)
-    HT_DMA("bf16_ak_bk_256x256x32_w2x2_m32_dma4", DT_BF16, 256, 256, 2, 2, 32, 4, 1, 4),
-    HT_DMA("bf16_ak_bk_256x256x32_w2x2_m32_dma5", DT_BF16, 256, 256, 2, 2, 32, 5, 1, 4),
-    HT_DMA("f16_ak_bk_256x256x32_w2x2_m32_dma4", DT_F16, 256, 256, 2, 2, 32, 4, 1, 4),
-    HT_DMA("e4m3_ak_bk_256x256x64_w2x2_m32_dma4", DT_F8, 256, 256, 2, 2, 32, 4, 1, 4),
+    HT_DMA("bf16_ak_bk_256x256x32_w2x2_m32_dma4", DT_BF16, 256, 256, 2, 2, 32, 4, 1, 4, 2),
+    HT_DMA("bf16_ak_bk_256x256x32_w2x2_m32_dma5", DT_BF16, 256, 256, 2, 2, 32, 5, 1, 4, 3),
+    HT_DMA("f16_ak_bk_256x256x32_w2x2_m32_dma4", DT_F16, 256, 256, 2, 2, 32, 4, 1, 4, 2),
+    HT_DMA("e4m3_ak_bk_256x256x64_w2x2_m32_dma4", DT_F8, 256, 256, 2, 2, 32, 4, 1, 4, 2),
     // two workgroups per CU: the other workgroup's waves keep the matrix cores busy while one
     // waits at its barrier
-    HT_DMA("bf16_ak_bk_256x128x32_w2x2_m32_dma3_o2", DT_BF16, 256, 128, 2, 2, 32, 3, 2, 4),
-    HT_DMA("bf16_ak_bk_128x256x32_w2x2_m32_dma3_o2", DT_BF16, 128, 256, 2, 2, 32, 3, 2, 4),
-    HT_DMA("bf16_ak_bk_256x128x32_w4x1_m32_dma3_o2", DT_BF16, 256, 128, 4, 1, 32, 3, 2, 4),
+    HT_DMA("bf16_ak_bk_256x128x32_w2x2_m32_dma3_o2", DT_BF16, 256, 128, 2, 2, 32, 3, 2, 4, 1),
+    HT_DMA("bf16_ak_bk_128x256x32_w2x2_m32_dma3_o2", DT_BF16, 128, 256, 2, 2, 32, 3, 2, 4, 1),
+    HT_DMA("bf16_ak_bk_256x128x32_w4x1_m32_dma3_o2", DT_BF16, 256, 128, 4, 1, 32, 3, 2, 4, 1),
     // 128-byte rows: every DMA lane octet reads one whole cache line
-    HT_DMA("bf16_ak_bk_256x256x64_w2x2_m32_dma2", DT_BF16, 256, 256, 2, 2, 32, 2, 1, 8),
-    HT_DMA("bf16_ak_bk_256x128x64_w2x2_m32_dma3", DT_BF16, 256, 128, 2, 2, 32, 3, 1, 8),
-    HT_DMA("f16_ak_bk_256x256x64_w2x2_m32_dma2", DT_F16, 256, 256, 2, 2, 32, 2, 1, 8),
-    HT_DMA("e4m3_ak_bk_256x256x128_w2x2_m32_dma2", DT_F8, 256, 256, 2, 2, 32, 2, 1, 8),
+    HT_DMA("bf16_ak_bk_256x256x64_w2x2_m32_dma2", DT_BF16, 256, 256, 2, 2, 32, 2, 1, 8, 2),
+    HT_DMA("bf16_ak_bk_256x128x64_w2x2_m32_dma3", DT_BF16, 256, 128, 2, 2, 32, 3, 1, 8, 1),
+    HT_DMA("f16_ak_bk_256x256x64_w2x2_m32_dma2", DT_F16, 256, 256, 2, 2, 32, 2, 1, 8, 3),
+    HT_DMA("e4m3_ak_bk_256x256x128_w2x2_m32_dma2", DT_F8, 256, 256, 2, 2, 32, 2, 1, 8, 3),
     // eight waves (two per SIMD): one wave's waits are covered by the other's MFMAs, and twice
     // as many waves keep global loads in flight
-    HT_DMA("bf16_ak_bk_256x256x32_w2x4_m32_dma5", DT_BF16, 256, 256, 2, 4, 32, 5, 1, 4),
-    HT_DMA("bf16_ak_bk_256x256x32_w4x2_m32_dma5", DT_BF16, 256, 256, 4, 2, 32, 5, 1, 4),
-    HT_DMA("bf16_ak_bk_256x256x64_w2x4_m32_dma2", DT_BF16, 256, 256, 2, 4, 32, 2, 1, 8),
+    HT_DMA("bf16_ak_bk_256x256x32_w2x4_m32_dma5", DT_BF16, 256, 256, 2, 4, 32, 5, 1, 4, 4),
+    HT_DMA("bf16_ak_bk_256x256x32_w4x2_m32_dma5", DT_BF16, 256, 256, 4, 2, 32, 5, 1, 4, 4),
+    HT_DMA("bf16_ak_bk_256x256x64_w2x4_m32_dma2", DT_BF16, 256, 256, 2, 4, 32, 2, 1, 8, 5),
+    HT_DMA("f16_ak_bk_256x256x64_w2x4_m32_dma2", DT_F16, 256, 256, 2, 4, 32, 2, 1, 8, 5),
+    // M <= 16: stream B, split K across the waves of a workgroup
+    HT_SKINNY("e4m3_ak_bk_16x32_w8_skinny", DT_F8, 32, 8, 4),
+    HT_SKINNY("bf16_ak_bk_16x32_w8_skinny", DT_BF16, 32, 8, 4),
+    HT_SKINNY("f16_ak_bk_16x32_w8_skinny", DT_F16, 32, 8, 4),
 };
 
 const KernelEntry* table() { return g_table; }

@@ -127,6 +127,18 @@ def test_tile_table_choices(fake_gfx950):
     # ragged fp16 with odd leading dimensions: only the element-wise loader can read it
     rag = _info(H.make_desc(4099, 3071, 2053, "f16", (2053, 1), (3071, 1), (3071, 1), c_strides=(3071, 1)))
     assert b"narrow" in rag.name and rag.config == rag.fallback
+    # M <= 16 with 16-byte-aligned K-major operands: the streaming (skinny) kernel, one
+    # workgroup per 32 output columns
+    sk = _info(H.make_desc(16, 16384, 8192, "e4m3", (8192, 1), (1, 8192), (16384, 1)))
+    assert b"skinny" in sk.name and sk.bm == 16 and sk.grid == 16384 // 32
+    # one more row: back to the tiled kernels
+    tall = _info(H.make_desc(17, 16384, 8192, "e4m3", (8192, 1), (1, 8192), (16384, 1)))
+    assert b"skinny" not in tall.name
+    # a skinny kernel cannot be forced onto M > 16
+    names = [H.gemm_config_name(i) for i in range(H.gemm_num_configs())]
+    sk_bf16 = names.index("bf16_ak_bk_16x32_w8_skinny")
+    assert status_of(desc(M=17, force_config=sk_bf16)) == 8
+    assert _info(desc(M=16, force_config=sk_bf16)).config == sk_bf16
 
 
 def test_forced_config_must_match(fake_gfx950):
