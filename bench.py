@@ -113,6 +113,22 @@ def cpu_baseline(name, host_set, threads, budget_s=12.0):
             "seconds": round(t, 3)}
 
 
+def copy_calibration(nbytes=1 << 30, copies=5):
+    """Exactly `copies` device-to-device copies of `nbytes` and nothing else on the GPU: the
+    reference that scales the FETCH_SIZE / WRITE_SIZE counters to bytes."""
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(copies):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    print(json.dumps({"copy_bytes": nbytes, "copies": copies,
+                      "GB/s (read+write)": round(2 * nbytes * copies / dt / 1e9, 1)}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -122,10 +138,15 @@ def main():
     ap.add_argument("--force-config", type=int, default=-1)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sets", type=int, default=3)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run 5 plain device copies of 1 GiB (counter calibration) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
 
     import torch
 
@@ -149,20 +170,31 @@ def main():
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    # timed region: K launches back to back on the launch stream, one pair of HIP events around
+    # them (per-launch events would add their own gaps to short kernels)
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    t_start.record(stream)
     for i in range(args.steps):
+        step(i)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = float(wall * 1e3 / args.steps)
+    avg_launch_ms = float(t_start.elapsed_time(t_end)) / args.steps
+    # spread of single launches, in a separate pass (not part of the value)
+    n_pct = min(args.steps, 20)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(n_pct)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(n_pct)]
+    for i in range(n_pct):
         starts[i].record(stream)
         step(i)
         ends[i].record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     per = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])  # ms per launch
-    ms = float(wall * 1e3 / args.steps)
     flops = 2.0 * M * N * K
-    avg_launch_ms = float(per.mean())
     tflops = flops / (ms * 1e-3) / 1e12
     achieved = flops / (avg_launch_ms * 1e-3) / 1e12
     nbytes = algorithmic_bytes(M, N, K, dt, has_c, bias)
@@ -174,10 +206,14 @@ def main():
     else:
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_TFLOPS[dt],
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS[dt], 4), "traffic": None}
-    roof.update({"kernel": info.name.decode(), "launch_ms_mean": round(avg_launch_ms, 4),
-                 "launch_ms_p10": round(float(np.percentile(per, 10)), 4),
-                 "launch_ms_p50": round(float(np.percentile(per, 50)), 4),
-                 "launch_ms_p90": round(float(np.percentile(per, 90)), 4),
+    from hierarchical_tiling_amd import counters
+    traffic, source = counters.traffic_for(info.name.decode(), name, os.path.join(ROOT, "profiles"))
+    roof["traffic"] = traffic
+    roof.update({"traffic_source": source, "kernel": info.name.decode(),
+                 "launch_ms_mean": round(avg_launch_ms, 4),
+                 "single_launch_ms_p10": round(float(np.percentile(per, 10)), 4),
+                 "single_launch_ms_p50": round(float(np.percentile(per, 50)), 4),
+                 "single_launch_ms_p90": round(float(np.percentile(per, 90)), 4),
                  "algorithmic_bytes": nbytes, "algorithmic_flops": flops})
     out = {
         "metric": METRIC, "value": round(tflops, 1), "unit": "TFLOP/s", "n_gpus": 1,

@@ -791,36 +791,38 @@ static hipError_t launch_dma(const KParams& p, hipStream_t s, dim3 grid) {
 // The skinny kernel: M <= 16 (a decode-like product), bound by streaming B from HBM.
 //
 // "CUTLASS" (stanleyjacob.dev), Part III: a tall-skinny GEMM has too few output tiles to fill
-// the GPU and memory bandwidth, not the matrix units, sets the ceiling; splitting K over blocks
-// restores occupancy (Part IV Stage 6).  Here a workgroup of NW waves owns BN output columns and
-// all M rows; wave w reduces the w-th of NW slices of K, and the NW partial sums meet in LDS.
-// Every byte of B is used by exactly one MFMA, so B goes straight from HBM into registers (no
-// LDS staging); A (M x K, a few hundred KiB) stays in L2 and is read alongside.  Each wave keeps
-// U k-steps of loads in flight, and 16 waves per CU keep enough bytes in flight to cover HBM
-// latency.  Atoms: 16x16xKSTEP MFMA (16x16x128 e4m3, 16x16x32 bf16/fp16); lane l supplies row
-// (or column) l % 16 and the k-run of lane group l / 16.
+// the GPU and memory bandwidth, not the matrix units, sets the ceiling; splitting K restores
+// occupancy (Part IV Stage 6).  A workgroup owns BN output columns and all M rows.  Its WK x WN
+// waves form a grid: wave (wk, wn) reduces the wk-th of WK slices of K for the NBW 16-column
+// blocks of column group wn (BN = WN * NBW * 16); the WK partial sums meet in LDS.  Every byte of
+// B is used by exactly one MFMA, so B goes straight from HBM into registers (no LDS staging).
+// A (M x K, a few hundred KiB) stays in L2; the WN waves that share a K slice read the same A
+// lines, so after the first they hit in the CU's vector L1 and A costs the CU's memory pipe
+// 1/WN of what it would if every wave read its own.  Atoms: 16x16xKSTEP MFMA (16x16x128 e4m3,
+// 16x16x32 bf16/fp16); lane l supplies row (or column) l % 16 and the k-run of lane group l / 16.
 // ------------------------------------------------------------------------------------------
-template <int DT, int BN, int NW, int U>
-__global__ __launch_bounds__(NW * 64, 2) void gemm_skinny(const KParams p) {
+template <int DT, int WK, int WN, int NBW, int U, int OCC>
+__global__ __launch_bounds__(WK * WN * 64, OCC) void gemm_skinny(const KParams p) {
   typedef Atom<DT, 16> At;
   typedef typename At::acc_t acc_t;  // 4 floats: rows 4*(l/16)+r, column l%16
-  constexpr int NT = NW * 64;
+  constexpr int NT = WK * WN * 64;
   constexpr int SZ = Ty<DT>::SZ;
   constexpr int LB = At::UNITS * 16;          // bytes per lane per operand per MFMA
   constexpr int KSTEP = 4 * LB / SZ;          // elements of K per MFMA
-  constexpr int NB = BN / 16;                 // 16-column blocks per workgroup
-  static_assert(BN % 16 == 0 && At::PER_UNIT == 1, "16-column blocks, one MFMA per k-step");
+  constexpr int BN = WN * NBW * 16;           // columns per workgroup
+  static_assert(At::PER_UNIT == 1, "one MFMA per k-step");
 
-  __shared__ float part[NW][NB][16][16];      // per-wave partial sums
+  __shared__ float part[WK][BN / 16][16][16];  // partial sums of each K slice
 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wk = wave % WK, wn = wave / WK;
   const int64_t n0 = (int64_t)blockIdx.x * BN;
   const int lr = lane & 15, lg = lane >> 4;
 
-  // K split: wave w owns k-steps [w*per, min((w+1)*per, nks))
+  // K split: wave (wk, .) owns k-steps [wk*per, min((wk+1)*per, nks))
   const int64_t nks = (p.K + KSTEP - 1) / KSTEP;
-  const int64_t per = (nks + NW - 1) / NW;
-  const int64_t ks0 = wave * per;
+  const int64_t per = (nks + WK - 1) / WK;
+  const int64_t ks0 = wk * per;
   const int64_t ks1 = min(ks0 + per, nks);
 
   // A rows lr (zero past M); B columns n0 + 16*b + lr (zero past N, or past this workgroup's
@@ -831,19 +833,22 @@ __global__ __launch_bounds__(NW * 64, 2) void gemm_skinny(const KParams p) {
   const int64_t a_span = uniform_i64(((p.M - 1) * p.lda + p.K) * SZ);
   const int64_t b_span = uniform_i64(((min((int64_t)BN, p.N - n0) - 1) * p.ldb + p.K) * SZ);
   const uint32_t a_off = (uint32_t)(lr * p.lda * SZ + lg * LB);
-  const uint32_t b_off = (uint32_t)(lr * p.ldb * SZ + lg * LB);
   const uint32_t b_blk = (uint32_t)(16 * p.ldb * SZ);
+  const uint32_t b_off = (uint32_t)(lr * p.ldb * SZ + lg * LB) + (uint32_t)(wn * NBW) * b_blk;
 
-  acc_t acc[NB];
-  static_for<NB>([&](auto b) { acc[b] = acc_t{}; });
+  acc_t acc[NBW];
+  static_for<NBW>([&](auto b) { acc[b] = acc_t{}; });
 
-  for (int64_t ks = ks0; ks < ks1; ks += U) {
-    u32x4 fa[U][At::UNITS], fb[U][NB][At::UNITS];
-    const __amdgpu_buffer_rsrc_t ra = make_rsrc(a_base, a_span);
-    const __amdgpu_buffer_rsrc_t rb = make_rsrc(b_base, b_span);
-    // Chunks past K (or past this wave's slice) get an offset beyond every descriptor's range
-    // (spans are < 2^31 bytes), so the buffer unit returns zeros without touching memory and the
-    // loads need no select after them: all U k-steps of loads are in flight together.
+  // Two register batches of U k-steps each: batch i+1 is in flight while batch i feeds the
+  // MFMAs.  Chunks past K or past this wave's slice get an offset beyond every descriptor's
+  // range, so the buffer unit returns zeros without touching memory (no select after the load,
+  // no branch around it).
+  struct Batch {
+    u32x4 a[U][At::UNITS], b[U][NBW][At::UNITS];
+  };
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(a_base, a_span);
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(b_base, b_span);
+  auto load = [&](Batch& f, int64_t ks) {
     static_for<U>([&](auto u) {
       const int64_t k0 = (ks + u) * KSTEP;
       const bool live = ks + u < ks1;
@@ -851,24 +856,36 @@ __global__ __launch_bounds__(NW * 64, 2) void gemm_skinny(const KParams p) {
         const int64_t kc = k0 + (lg * LB + x * 16) / SZ;  // first element of this 16-byte chunk
         const bool ok = live && kc < p.K;
         const uint32_t ko = (uint32_t)(k0 * SZ) + x * 16;
-        fa[u][x] = __builtin_amdgcn_raw_buffer_load_b128(ra, ok ? a_off + ko : 0x80000000u, 0, 0);
-        static_for<NB>([&](auto b) {
-          fb[u][b][x] = __builtin_amdgcn_raw_buffer_load_b128(
+        f.a[u][x] = __builtin_amdgcn_raw_buffer_load_b128(ra, ok ? a_off + ko : 0x80000000u, 0, 0);
+        static_for<NBW>([&](auto b) {
+          f.b[u][b][x] = __builtin_amdgcn_raw_buffer_load_b128(
               rb, ok ? b_off + b * b_blk + ko : 0x80000000u, 0, 0);
         });
       });
     });
-    // keep the scheduler from sinking loads below MFMAs: every load of the group is issued
-    // before the first wait
-    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto mma = [&](const Batch& f) {
     static_for<U>([&](auto u) {
-      static_for<NB>([&](auto b) { At::mma(acc[b], fa[u], fb[u][b], 0); });
+      static_for<NBW>([&](auto b) { At::mma(acc[b], f.a[u], f.b[u][b], 0); });
     });
+  };
+  Batch f0, f1;
+  load(f0, ks0);
+  for (int64_t ks = ks0; ks < ks1; ks += 2 * U) {
+    load(f1, ks + U);
+    // loads stay ahead of the MFMAs that wait on the older batch
+    __builtin_amdgcn_sched_barrier(0);
+    mma(f0);
+    __builtin_amdgcn_sched_barrier(0);
+    load(f0, ks + 2 * U);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(f1);
+    __builtin_amdgcn_sched_barrier(0);
   }
 
-  // partial sums -> LDS; wave-parallel reduction over the NW waves; epilogue
-  static_for<NB>([&](auto b) {
-    static_for<4>([&](auto r) { part[wave][b][4 * lg + r][lr] = acc[b][(int)r]; });
+  // partial sums -> LDS; reduction over the WK slices; epilogue
+  static_for<NBW>([&](auto b) {
+    static_for<4>([&](auto r) { part[wk][wn * NBW + b][4 * lg + r][lr] = acc[b][(int)r]; });
   });
   __syncthreads();
   constexpr int ODT = out_dtype(DT);
@@ -879,7 +896,7 @@ __global__ __launch_bounds__(NW * 64, 2) void gemm_skinny(const KParams p) {
     if (row >= p.M || col >= p.N) continue;
     float sum = 0.f;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) sum += part[w][c / 16][row][c % 16];
+    for (int w = 0; w < WK; ++w) sum += part[w][c / 16][row][c % 16];
     float v = p.alpha * sum;
     if (p.has_c) v += p.beta * O::load(p.C, row * p.c_sm + col * p.c_sn);
     if (p.has_bias) v += O::load(p.bias, col);
@@ -888,10 +905,11 @@ __global__ __launch_bounds__(NW * 64, 2) void gemm_skinny(const KParams p) {
   }
 }
 
-template <int DT, int BN, int NW, int U>
+template <int DT, int WK, int WN, int NBW, int U, int OCC>
 static hipError_t launch_skinny(const KParams& p, hipStream_t s, dim3) {
+  constexpr int BN = WN * NBW * 16;
   const dim3 grid((unsigned)((p.N + BN - 1) / BN));
-  hipLaunchKernelGGL((gemm_skinny<DT, BN, NW, U>), grid, dim3(NW * 64), 0, s, p);
+  hipLaunchKernelGGL((gemm_skinny<DT, WK, WN, NBW, U, OCC>), grid, dim3(WK * WN * 64), 0, s, p);
   return hipGetLastError();
 }
 
@@ -913,10 +931,10 @@ static hipError_t launch_tiled(const KParams& p, hipStream_t s, dim3 grid) {
   {NAME, DT, 1, 1, 1, 0, BM, BN, CH * 16 / Ty<DT>::SZ, WM * WN, ST, ST * (BM + BN) * CH * 16, 1, \
    RANK, &launch_dma<DT, BM, BN, WM, WN, MI, ST, OCC, CH>}
 
-// Skinny entries: bm = 16 rows, bn columns per workgroup, bk = one MFMA k-step.
-#define HT_SKINNY(NAME, DT, BN, NW, U)                                                           \
-  {NAME, DT, 1, 1, 1, 1, 16, BN, 4 * Atom<DT, 16>::UNITS * 16 / Ty<DT>::SZ, NW, 1,             \
-   NW * (BN / 16) * 16 * 16 * 4, 1, 0, &launch_skinny<DT, BN, NW, U>}
+// Skinny entries: bm = 16 rows, bn = WN*NBW*16 columns per workgroup, bk = one MFMA k-step.
+#define HT_SKINNY(NAME, DT, WK, WN, NBW, U, OCC)                                                 \
+  {NAME, DT, 1, 1, 1, 1, 16, WN * NBW * 16, 4 * Atom<DT, 16>::UNITS * 16 / Ty<DT>::SZ, WK * WN, \
+   1, WK * WN * NBW * 16 * 16 * 4, 1, 0, &launch_skinny<DT, WK, WN, NBW, U, OCC>}
 
 static const KernelEntry g_table[] = {
     // bf16, BK = 64 (128-byte LDS rows)
@@ -980,9 +998,9 @@ static const KernelEntry g_table[] = {
     HT_DMA("bf16_ak_bk_256x256x64_w2x4_m32_dma2", DT_BF16, 256, 256, 2, 4, 32, 2, 1, 8, 5),
     HT_DMA("f16_ak_bk_256x256x64_w2x4_m32_dma2", DT_F16, 256, 256, 2, 4, 32, 2, 1, 8, 5),
     // M <= 16: stream B, split K across the waves of a workgroup
-    HT_SKINNY("e4m3_ak_bk_16x32_w8_skinny", DT_F8, 32, 8, 4),
-    HT_SKINNY("bf16_ak_bk_16x32_w8_skinny", DT_BF16, 32, 8, 4),
-    HT_SKINNY("f16_ak_bk_16x32_w8_skinny", DT_F16, 32, 8, 4),
+    HT_SKINNY("e4m3_ak_bk_16x32_w4_skinny", DT_F8, 4, 1, 2, 2, 2),
+    HT_SKINNY("bf16_ak_bk_16x32_w8_skinny", DT_BF16, 8, 1, 2, 2, 4),
+    HT_SKINNY("f16_ak_bk_16x32_w8_skinny", DT_F16, 8, 1, 2, 2, 4),
 };
 
 const KernelEntry* table() { return g_table; }
