@@ -24,9 +24,15 @@ ARCH = "gfx950"
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-command-line-argument"]
 
+HIP = [HIPCC, f"--offload-arch={ARCH}"] + COMMON + DEVICE_FLAGS
+# kernels.h holds the kernel templates; each table_*.hip instantiates one operand type's entries
 SOURCES = [
-    ("kernels.hip", [HIPCC, f"--offload-arch={ARCH}"] + COMMON + DEVICE_FLAGS),
-    ("api.cpp", [HIPCC, f"--offload-arch={ARCH}"] + COMMON + DEVICE_FLAGS),
+    ("table_bf16.hip", HIP),
+    ("table_f16.hip", HIP),
+    ("table_e4m3.hip", HIP),
+    ("table_f32.hip", HIP),
+    ("table.cpp", HIP),
+    ("api.cpp", HIP),
     ("layout.cpp", ["g++"] + COMMON),
 ]
 

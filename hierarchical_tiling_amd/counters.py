@@ -22,7 +22,7 @@ import os
 from collections import defaultdict
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-SOURCES = ("csrc/kernels.hip", "csrc/gemm_internal.h")
+SOURCES = ("csrc/kernels.h", "csrc/gemm_internal.h")
 COPY_BYTES_DEFAULT = 1 << 30
 
 

@@ -1,4 +1,4 @@
-// gemm_internal.h -- declarations shared by the host API (api.cpp) and the kernels (kernels.hip).
+// gemm_internal.h -- declarations shared by the host API (api.cpp) and the kernels (kernels.h).
 #pragma once
 
 #include <hip/hip_runtime.h>

@@ -1,4 +1,5 @@
-// kernels.hip -- gfx950 (MI355X, CDNA4) kernels of the hierarchically tiled GEMM.
+// kernels.h -- gfx950 (MI355X, CDNA4) kernels of the hierarchically tiled GEMM.  The table_*.hip
+// files instantiate them per operand type (one translation unit each, so they build in parallel).
 //
 //   D = act(alpha * (A @ B) + beta * C + bias),  fp32 accumulation.
 //
@@ -35,6 +36,8 @@
 //    operands fall back to a slow path).
 //  * The epilogue applies alpha, beta*C, bias[n] and the activation in fp32 on the accumulator
 //    registers and rounds to the output type once ("CUTLASS", Part IV Stage 5).
+#pragma once
+
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -788,6 +791,172 @@ static hipError_t launch_dma(const KParams& p, hipStream_t s, dim3 grid) {
 }
 
 // ------------------------------------------------------------------------------------------
+// The split-ring kernel: a 256 x 256 workgroup tile whose A and B k-tiles travel in separate
+// LDS rings, so the loads of a k-tile get more than one k-tile of MFMA work to arrive within
+// the 160 KiB of LDS.
+//
+// A stage of a 256 x 256 tile with 128-byte rows (one cache line per row per k-tile, the
+// cheapest DMA pattern) holds 64 KiB, so only two whole stages fit and each k-tile's loads
+// would get exactly one k-tile of compute to land ("CuTe DSL / CUDA Tile" post, "Pipelining
+// hides a wait": the slower of load and compute sets the interval; "CUTLASS", Part IV Stage 4:
+// the multistage ring).  Here the unit of buffering is half a stage (32 KiB, the A or the B
+// tile of one k-tile) and the 5 units of LDS are split into two rings:
+//   * A: 3 slots.  A(t+2) is issued at the start of k-tile t, into the slot A(t-1) released,
+//     and is read at the start of k-tile t+2: two k-tiles of lead.
+//   * B: 2 slots.  Every wave reads all of its B fragments of k-tile t at the start of the
+//     k-tile; after half of the MFMA substeps a barrier confirms that no wave still reads B(t),
+//     and B(t+2) is issued into that slot: one and a half k-tiles of lead.
+// The end-of-tile wait leaves A(t+2) and B(t+2) in flight and needs only A(t+1), B(t+1).
+// Summation order per output is the same as the two-stage DMA kernel's (k-tiles in order,
+// substeps in order), so both produce the same bits.
+// ------------------------------------------------------------------------------------------
+template <int DT, int WM, int WN, int MI>
+__global__ __launch_bounds__(WM * WN * 64, 1) void gemm_ring(const KParams p) {
+  typedef Atom<DT, MI> At;
+  typedef typename At::acc_t acc_t;
+  constexpr int BM = 256, BN = 256, CH = 8;   // 128-byte LDS rows
+  constexpr int NW = WM * WN, NT = NW * 64;
+  constexpr int SZ = Ty<DT>::SZ;
+  constexpr int BKE = CH * 16 / SZ;           // elements per k-tile
+  constexpr int VE = 16 / SZ;
+  constexpr int RPB = 64 / CH;                // rows per 1-KiB DMA block
+  constexpr int WTM = BM / WM, WTN = BN / WN;
+  constexpr int RM = WTM / MI, RN = WTN / MI;
+  constexpr int UPL = CH / At::G;             // chunks per lane per row per k-tile
+  constexpr int S = UPL / At::UNITS;          // fragment substeps per k-tile
+  constexpr int DU = BM / RPB / NW;           // DMA instructions per wave per unit
+  constexpr int SLOT = BM * CH;               // 16-byte chunks per unit (32 KiB)
+  constexpr int MID = S / 2;                  // substeps before B's slot is released
+  static_assert(BM == BN, "A and B units share one slot size");
+  static_assert(UPL % At::UNITS == 0 && S % 2 == 0, "whole, evenly many substeps");
+  static_assert(RM % 2 == 0, "the last substep is issued in two halves");
+  static_assert(BM % (RPB * NW) == 0, "whole DMA blocks per wave");
+
+  __shared__ u32x4 lds[5 * SLOT];  // slots 0..2: A ring; 3..4: B ring
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  int tm, tn;
+  tile_of(p, blockIdx.x, gridDim.x, tm, tn);
+  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+  const int wm = wave % WM, wn = wave / WM;
+
+  acc_t acc[RM][RN];
+  static_for<RM>([&](auto i) { static_for<RN>([&](auto j) { acc[i][j] = acc_t{}; }); });
+
+  const char* a_tile = uniform_ptr((const char*)p.A + m0 * p.lda * SZ);
+  const char* b_tile = uniform_ptr((const char*)p.B + n0 * p.ldb * SZ);
+  const int64_t a_span = uniform_i64(((p.M - m0 - 1) * p.lda + p.K) * SZ);
+  const int64_t b_span = uniform_i64(((min((int64_t)BN, p.N - n0) - 1) * p.ldb + p.K) * SZ);
+  // lane l of a DMA block fills slot l of a kilobyte: row l/CH, slot l%CH, which holds logical
+  // chunk (l%CH) ^ key(row)
+  auto src_off = [&](int blk, int64_t ld, int& kc) -> uint32_t {
+    const int row = blk * RPB + lane / CH;
+    const int c = (lane % CH) ^ row_key<CH>(row);
+    kc = c * VE;
+    return (uint32_t)(row * ld * SZ + c * 16);
+  };
+  const int nk = (int)((p.K + BKE - 1) / BKE);
+
+  // Unit OP (0: A, 1: B) of k-tile t into `slot`.  Units past the end of K are all out of range
+  // (zeros) and are issued anyway, so the wait counts stay the same on every k-tile.
+  auto dma = [&](auto OP, int t, int slot) {
+    const int64_t k0 = (int64_t)t * BKE;
+    const __amdgpu_buffer_rsrc_t r = OP == 0 ? make_rsrc(a_tile, a_span) : make_rsrc(b_tile, b_span);
+    const int64_t ld = OP == 0 ? p.lda : p.ldb;
+    u32x4* st = lds + slot * SLOT;
+    static_for<DU>([&](auto i) {
+      const int blk = wave + NW * i;
+      int kc;
+      const uint32_t off = src_off(blk, ld, kc);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(st + blk * 64), 16,
+                                               k0 + kc < p.K ? off : 0x80000000u,
+                                               (int)(k0 * SZ), 0, 0);
+    });
+  };
+
+  const int frow = lane % MI, fgrp = lane / MI;
+  u32x4 fa[2][RM][At::UNITS], fb[S][RN][At::UNITS];
+  auto read_a = [&](auto buf, const u32x4* sa, auto sub) {
+    static_for<At::UNITS>([&](auto x) {
+      const int c = fgrp + At::G * (sub * At::UNITS + x);
+      static_for<RM>([&](auto i) { fa[buf][i][x] = sa[dslot<CH>(wm * WTM + i * MI + frow, c)]; });
+    });
+  };
+  auto read_b = [&](const u32x4* sb, auto sub) {
+    static_for<At::UNITS>([&](auto x) {
+      const int c = fgrp + At::G * (sub * At::UNITS + x);
+      static_for<RN>([&](auto j) { fb[sub][j][x] = sb[dslot<CH>(wn * WTN + j * MI + frow, c)]; });
+    });
+  };
+  auto mma_rows = [&](auto buf, auto sub, auto i0, auto i1) {
+    static_for<At::PER_UNIT>([&](auto u) {
+      static_for<i1 - i0>([&](auto ii) {
+        static_for<RN>([&](auto j) { At::mma(acc[i0 + ii][j], fa[buf][i0 + ii], fb[sub][j], u); });
+      });
+    });
+  };
+  constexpr std::integral_constant<int, 0> OPA{};
+  constexpr std::integral_constant<int, 1> OPB{};
+  typedef std::integral_constant<int, 0> I0;
+
+  if (nk > 0) {
+    dma(OPA, 0, 0);
+    dma(OPB, 0, 3);
+    dma(OPA, 1, 1);
+    dma(OPB, 1, 4);
+    wait_counts<2 * DU, true>();
+    barrier_nofence();
+    read_a(I0{}, lds, I0{});
+    read_b(lds + 3 * SLOT, I0{});
+    int sa_i = 0;  // slot of A(t) in the A ring
+    for (int t = 0; t < nk; ++t) {
+      const int sb_i = 3 + (t & 1);
+      // A(t-1)'s slot was released by the barrier that ended k-tile t-1
+      dma(OPA, t + 2, sa_i == 0 ? 2 : sa_i - 1);
+      const u32x4* sa = lds + sa_i * SLOT;
+      const u32x4* sb = lds + sb_i * SLOT;
+      static_for<S - 1>([&](auto s) { read_b(sb, std::integral_constant<int, s + 1>{}); });
+      static_for<S>([&](auto s) {
+        constexpr int buf = s & 1;
+        if constexpr (s + 1 < S) {
+          read_a(std::integral_constant<int, buf ^ 1>{}, sa, std::integral_constant<int, s + 1>{});
+          mma_rows(std::integral_constant<int, buf>{}, s, I0{}, std::integral_constant<int, RM>{});
+          if constexpr (s + 1 == MID) {
+            // this wave's reads of B(t) are complete (lgkmcnt 0); after the barrier no wave
+            // reads B(t), and B(t+2) takes its slot
+            wait_counts<63, true>();
+            barrier_nofence();
+            dma(OPB, t + 2, sb_i);
+          }
+        } else {
+          mma_rows(std::integral_constant<int, buf>{}, s, I0{}, std::integral_constant<int, RM / 2>{});
+          // A(t+1) and B(t+1) have landed once at most A(t+2), B(t+2) are in flight
+          wait_counts<2 * DU, true>();
+          barrier_nofence();
+          // (after the last k-tile these read zero-filled slots; the values are never used)
+          const int na = sa_i == 2 ? 0 : sa_i + 1;
+          read_a(std::integral_constant<int, buf ^ 1>{}, lds + na * SLOT, I0{});
+          read_b(lds + (3 + ((t + 1) & 1)) * SLOT, I0{});
+          mma_rows(std::integral_constant<int, buf>{}, s, std::integral_constant<int, RM / 2>{},
+                   std::integral_constant<int, RM>{});
+        }
+      });
+      sa_i = sa_i == 2 ? 0 : sa_i + 1;
+    }
+    wait_counts<0, true>();  // the zero-filled units issued past the end are still in flight
+    barrier_nofence();
+  }
+  epilogue<DT, MI, BM, BN, WTM, WTN, RM, RN, NT, sizeof(lds)>(p, acc, lds, m0, n0, wm, wn, lane,
+                                                              tid, nk == 0);
+}
+
+template <int DT, int WM, int WN, int MI>
+static hipError_t launch_ring(const KParams& p, hipStream_t s, dim3 grid) {
+  hipLaunchKernelGGL((gemm_ring<DT, WM, WN, MI>), grid, dim3(WM * WN * 64), 0, s, p);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------------------
 // The skinny kernel: M <= 16 (a decode-like product), bound by streaming B from HBM.
 //
 // "CUTLASS" (stanleyjacob.dev), Part III: a tall-skinny GEMM has too few output tiles to fill
@@ -931,79 +1100,14 @@ static hipError_t launch_tiled(const KParams& p, hipStream_t s, dim3 grid) {
   {NAME, DT, 1, 1, 1, 0, BM, BN, CH * 16 / Ty<DT>::SZ, WM * WN, ST, ST * (BM + BN) * CH * 16, 1, \
    RANK, &launch_dma<DT, BM, BN, WM, WN, MI, ST, OCC, CH>}
 
+// Split-ring entries: 256 x 256 tiles, 128-byte rows, 5 units of 32 KiB.
+#define HT_RING(NAME, DT, WM, WN, MI, RANK)                                                      \
+  {NAME, DT, 1, 1, 1, 0, 256, 256, 128 / Ty<DT>::SZ, WM * WN, 5, 5 * 256 * 128, 1, RANK,          \
+   &launch_ring<DT, WM, WN, MI>}
+
 // Skinny entries: bm = 16 rows, bn = WN*NBW*16 columns per workgroup, bk = one MFMA k-step.
 #define HT_SKINNY(NAME, DT, WK, WN, NBW, U, OCC)                                                 \
   {NAME, DT, 1, 1, 1, 1, 16, WN * NBW * 16, 4 * Atom<DT, 16>::UNITS * 16 / Ty<DT>::SZ, WK * WN, \
    1, WK * WN * NBW * 16 * 16 * 4, 1, 0, &launch_skinny<DT, WK, WN, NBW, U, OCC>}
-
-static const KernelEntry g_table[] = {
-    // bf16, BK = 64 (128-byte LDS rows)
-    HT_TILED("bf16_ak_bk_256x256x64_w2x2_m32_vec", DT_BF16, 1, 1, 1, 256, 256, 64, 2, 2, 32),
-    HT_TILED("bf16_ak_bk_128x128x64_w2x2_m32_vec", DT_BF16, 1, 1, 1, 128, 128, 64, 2, 2, 32),
-    HT_TILED("bf16_ak_bk_256x256x64_w2x4_m32_vec", DT_BF16, 1, 1, 1, 256, 256, 64, 2, 4, 32),
-    HT_TILED("bf16_ak_bn_256x256x64_w2x2_m32_vec", DT_BF16, 1, 0, 1, 256, 256, 64, 2, 2, 32),
-    HT_TILED("bf16_ak_bn_128x128x64_w2x2_m32_vec", DT_BF16, 1, 0, 1, 128, 128, 64, 2, 2, 32),
-    HT_TILED("bf16_am_bk_128x128x64_w2x2_m32_vec", DT_BF16, 0, 1, 1, 128, 128, 64, 2, 2, 32),
-    HT_TILED("bf16_am_bn_128x128x64_w2x2_m32_vec", DT_BF16, 0, 0, 1, 128, 128, 64, 2, 2, 32),
-    HT_TILED("bf16_ak_bk_128x128x64_w2x2_m32_narrow", DT_BF16, 1, 1, 0, 128, 128, 64, 2, 2, 32),
-    HT_TILED("bf16_ak_bn_128x128x64_w2x2_m32_narrow", DT_BF16, 1, 0, 0, 128, 128, 64, 2, 2, 32),
-    HT_TILED("bf16_am_bk_128x128x64_w2x2_m32_narrow", DT_BF16, 0, 1, 0, 128, 128, 64, 2, 2, 32),
-    HT_TILED("bf16_am_bn_128x128x64_w2x2_m32_narrow", DT_BF16, 0, 0, 0, 128, 128, 64, 2, 2, 32),
-    // fp16
-    HT_TILED("f16_ak_bk_256x256x64_w2x2_m32_vec", DT_F16, 1, 1, 1, 256, 256, 64, 2, 2, 32),
-    HT_TILED("f16_ak_bk_128x128x64_w2x2_m32_vec", DT_F16, 1, 1, 1, 128, 128, 64, 2, 2, 32),
-    HT_TILED("f16_ak_bn_256x256x64_w2x2_m32_vec", DT_F16, 1, 0, 1, 256, 256, 64, 2, 2, 32),
-    HT_TILED("f16_ak_bn_128x128x64_w2x2_m32_vec", DT_F16, 1, 0, 1, 128, 128, 64, 2, 2, 32),
-    HT_TILED("f16_am_bk_128x128x64_w2x2_m32_vec", DT_F16, 0, 1, 1, 128, 128, 64, 2, 2, 32),
-    HT_TILED("f16_am_bn_128x128x64_w2x2_m32_vec", DT_F16, 0, 0, 1, 128, 128, 64, 2, 2, 32),
-    HT_TILED("f16_ak_bk_128x128x64_w2x2_m32_narrow", DT_F16, 1, 1, 0, 128, 128, 64, 2, 2, 32),
-    HT_TILED("f16_ak_bn_128x128x64_w2x2_m32_narrow", DT_F16, 1, 0, 0, 128, 128, 64, 2, 2, 32),
-    HT_TILED("f16_am_bk_128x128x64_w2x2_m32_narrow", DT_F16, 0, 1, 0, 128, 128, 64, 2, 2, 32),
-    HT_TILED("f16_am_bn_128x128x64_w2x2_m32_narrow", DT_F16, 0, 0, 0, 128, 128, 64, 2, 2, 32),
-    // fp32, BK = 32
-    HT_TILED("f32_ak_bk_128x128x32_w2x2_m32_vec", DT_F32, 1, 1, 1, 128, 128, 32, 2, 2, 32),
-    HT_TILED("f32_ak_bn_128x128x32_w2x2_m32_vec", DT_F32, 1, 0, 1, 128, 128, 32, 2, 2, 32),
-    HT_TILED("f32_am_bk_128x128x32_w2x2_m32_vec", DT_F32, 0, 1, 1, 128, 128, 32, 2, 2, 32),
-    HT_TILED("f32_am_bn_128x128x32_w2x2_m32_vec", DT_F32, 0, 0, 1, 128, 128, 32, 2, 2, 32),
-    HT_TILED("f32_ak_bk_64x64x32_w2x2_m16_narrow", DT_F32, 1, 1, 0, 64, 64, 32, 2, 2, 16),
-    HT_TILED("f32_ak_bn_64x64x32_w2x2_m16_narrow", DT_F32, 1, 0, 0, 64, 64, 32, 2, 2, 16),
-    HT_TILED("f32_am_bk_64x64x32_w2x2_m16_narrow", DT_F32, 0, 1, 0, 64, 64, 32, 2, 2, 16),
-    HT_TILED("f32_am_bn_64x64x32_w2x2_m16_narrow", DT_F32, 0, 0, 0, 64, 64, 32, 2, 2, 16),
-    // fp8 e4m3, BK = 128
-    HT_TILED("e4m3_ak_bk_256x256x128_w2x2_m32_vec", DT_F8, 1, 1, 1, 256, 256, 128, 2, 2, 32),
-    HT_TILED("e4m3_ak_bk_128x128x128_w2x2_m32_vec", DT_F8, 1, 1, 1, 128, 128, 128, 2, 2, 32),
-    HT_TILED("e4m3_ak_bk_128x128x128_w2x2_m32_narrow", DT_F8, 1, 1, 0, 128, 128, 128, 2, 2, 32),
-    HT_TILED("e4m3_ak_bn_128x128x128_w2x2_m32_narrow", DT_F8, 1, 0, 0, 128, 128, 128, 2, 2, 32),
-    HT_TILED("e4m3_am_bk_128x128x128_w2x2_m32_narrow", DT_F8, 0, 1, 0, 128, 128, 128, 2, 2, 32),
-    HT_TILED("e4m3_am_bn_128x128x128_w2x2_m32_narrow", DT_F8, 0, 0, 0, 128, 128, 128, 2, 2, 32),
-    // DMA-fed LDS rings (64-byte rows: BK = 32 for 16-bit types, 64 for fp8)
-    HT_DMA("bf16_ak_bk_256x256x32_w2x2_m32_dma4", DT_BF16, 256, 256, 2, 2, 32, 4, 1, 4, 2),
-    HT_DMA("bf16_ak_bk_256x256x32_w2x2_m32_dma5", DT_BF16, 256, 256, 2, 2, 32, 5, 1, 4, 3),
-    HT_DMA("f16_ak_bk_256x256x32_w2x2_m32_dma4", DT_F16, 256, 256, 2, 2, 32, 4, 1, 4, 2),
-    HT_DMA("e4m3_ak_bk_256x256x64_w2x2_m32_dma4", DT_F8, 256, 256, 2, 2, 32, 4, 1, 4, 2),
-    // two workgroups per CU: the other workgroup's waves keep the matrix cores busy while one
-    // waits at its barrier
-    HT_DMA("bf16_ak_bk_256x128x32_w2x2_m32_dma3_o2", DT_BF16, 256, 128, 2, 2, 32, 3, 2, 4, 1),
-    HT_DMA("bf16_ak_bk_128x256x32_w2x2_m32_dma3_o2", DT_BF16, 128, 256, 2, 2, 32, 3, 2, 4, 1),
-    HT_DMA("bf16_ak_bk_256x128x32_w4x1_m32_dma3_o2", DT_BF16, 256, 128, 4, 1, 32, 3, 2, 4, 1),
-    // 128-byte rows: every DMA lane octet reads one whole cache line
-    HT_DMA("bf16_ak_bk_256x256x64_w2x2_m32_dma2", DT_BF16, 256, 256, 2, 2, 32, 2, 1, 8, 2),
-    HT_DMA("bf16_ak_bk_256x128x64_w2x2_m32_dma3", DT_BF16, 256, 128, 2, 2, 32, 3, 1, 8, 1),
-    HT_DMA("f16_ak_bk_256x256x64_w2x2_m32_dma2", DT_F16, 256, 256, 2, 2, 32, 2, 1, 8, 3),
-    HT_DMA("e4m3_ak_bk_256x256x128_w2x2_m32_dma2", DT_F8, 256, 256, 2, 2, 32, 2, 1, 8, 3),
-    // eight waves (two per SIMD): one wave's waits are covered by the other's MFMAs, and twice
-    // as many waves keep global loads in flight
-    HT_DMA("bf16_ak_bk_256x256x32_w2x4_m32_dma5", DT_BF16, 256, 256, 2, 4, 32, 5, 1, 4, 4),
-    HT_DMA("bf16_ak_bk_256x256x32_w4x2_m32_dma5", DT_BF16, 256, 256, 4, 2, 32, 5, 1, 4, 4),
-    HT_DMA("bf16_ak_bk_256x256x64_w2x4_m32_dma2", DT_BF16, 256, 256, 2, 4, 32, 2, 1, 8, 5),
-    HT_DMA("f16_ak_bk_256x256x64_w2x4_m32_dma2", DT_F16, 256, 256, 2, 4, 32, 2, 1, 8, 5),
-    // M <= 16: stream B, split K across the waves of a workgroup
-    HT_SKINNY("e4m3_ak_bk_16x32_w4_skinny", DT_F8, 4, 1, 2, 2, 2),
-    HT_SKINNY("bf16_ak_bk_16x32_w8_skinny", DT_BF16, 8, 1, 2, 2, 4),
-    HT_SKINNY("f16_ak_bk_16x32_w8_skinny", DT_F16, 8, 1, 2, 2, 4),
-};
-
-const KernelEntry* table() { return g_table; }
-int table_size() { return (int)(sizeof(g_table) / sizeof(g_table[0])); }
 
 }  // namespace htk
