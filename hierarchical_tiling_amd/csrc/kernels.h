@@ -207,9 +207,29 @@ __device__ __forceinline__ void tile_of(const KParams& p, int pid, int nwg, int&
   tn = within / gsz;
 }
 
+// ReLU that keeps NaN (max(0, NaN) is NaN, as in the oracle's definition).
+__device__ __forceinline__ float relu(float v) { return v > 0.f ? v : (v == v ? 0.f : v); }
+
+// GELU(x) = x * Phi(x) = x/2 * (1 + erf(x / sqrt 2)), the exact (erf) form.  erf is taken from
+// Abramowitz and Stegun, Handbook of Mathematical Functions, formula 7.1.26 (Hastings):
+//   erf(z) = 1 - (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5) exp(-z^2),  t = 1 / (1 + p z),  z >= 0,
+// with |error| <= 1.5e-7, and erf(-z) = -erf(z).  It has no branches, so a wave evaluates it in a
+// fixed ~16 instructions; the error is far below the 2^-9 (bf16) / 2^-12 (fp16) output rounding.
+__device__ __forceinline__ float gelu(float x) {
+  const float z = __builtin_fabsf(x) * 0.70710678118654752f;
+  const float t = 1.0f / __builtin_fmaf(0.3275911f, z, 1.0f);
+  float poly = __builtin_fmaf(1.061405429f, t, -1.453152027f);
+  poly = __builtin_fmaf(poly, t, 1.421413741f);
+  poly = __builtin_fmaf(poly, t, -0.284496736f);
+  poly = __builtin_fmaf(poly, t, 0.254829592f);
+  poly *= t;
+  const float erf_abs = 1.0f - poly * __expf(-z * z);
+  return 0.5f * x * (1.0f + __builtin_copysignf(erf_abs, x));
+}
+
 __device__ __forceinline__ float activate(int act, float v) {
-  if (act == 1) return v > 0.f ? v : (v == v ? 0.f : v);
-  if (act == 2) return 0.5f * v * (1.0f + erff(v * 0.7071067811865475f));
+  if (act == 1) return relu(v);
+  if (act == 2) return gelu(v);
   return v;
 }
 
@@ -435,23 +455,43 @@ __device__ __forceinline__ void epilogue(const KParams& p, AccT (&acc)[RM][RN], 
   const float alpha = p.alpha, beta = p.beta;
   OT* tile = reinterpret_cast<OT*>(lds);  // BM x BN, row-major (REPACK only)
   if (REPACK && no_mainloop) __syncthreads();
+  // Each stage is one straight-line pass over the accumulator registers, entered on a uniform
+  // condition, so the common case (no C) carries no per-element branches:
+  // y = act((alpha * acc + beta * C) + bias[n]).
+  auto each = [&](auto&& f) {
+    static_for<RM>([&](auto i) {
+      static_for<RN>([&](auto j) { static_for<At::NACC>([&](auto r) { f(i, j, r); }); });
+    });
+  };
+  each([&](auto i, auto j, auto r) { acc[i][j][(int)r] *= alpha; });
+  if (has_c) {
+    each([&](auto i, auto j, auto r) {
+      const int64_t col = n0 + wn * WTN + j * MI + (lane % MI);
+      const int64_t row = m0 + wm * WTM + i * MI + acc_row<MI>(lane, r);
+      if (col < p.N && row < p.M) acc[i][j][(int)r] += beta * O::load(p.C, row * p.c_sm + col * p.c_sn);
+    });
+  }
+  if (has_bias) {
+    static_for<RN>([&](auto j) {
+      const int64_t col = n0 + wn * WTN + j * MI + (lane % MI);
+      const float bv = col < p.N ? O::load(p.bias, col) : 0.f;
+      static_for<RM>([&](auto i) { static_for<At::NACC>([&](auto r) { acc[i][j][(int)r] += bv; }); });
+    });
+  }
+  if (act == 2) each([&](auto i, auto j, auto r) { acc[i][j][(int)r] = gelu(acc[i][j][(int)r]); });
+  else if (act == 1) each([&](auto i, auto j, auto r) { acc[i][j][(int)r] = relu(acc[i][j][(int)r]); });
   static_for<RM>([&](auto i) {
     static_for<RN>([&](auto j) {
       const int lc = wn * WTN + j * MI + (lane % MI);
       const int64_t col = n0 + lc;
-      const bool col_ok = col < p.N;
-      const float bv = (has_bias && col_ok) ? O::load(p.bias, col) : 0.f;
       static_for<At::NACC>([&](auto r) {
         const int lr = wm * WTM + i * MI + acc_row<MI>(lane, r);
-        const int64_t row = m0 + lr;
-        float v = alpha * acc[i][j][(int)r];
-        if (has_c && col_ok && row < p.M) v += beta * O::load(p.C, row * p.c_sm + col * p.c_sn);
-        if (has_bias) v += bv;
-        v = activate(act, v);
+        const float v = acc[i][j][(int)r];
         if constexpr (REPACK) {
           tile[lr * BN + lc] = to_bits(v, std::integral_constant<int, ODT>{});
         } else {
-          if (col_ok && row < p.M) O::store(p.D, row * p.d_sm + col * p.d_sn, v);
+          const int64_t row = m0 + lr;
+          if (col < p.N && row < p.M) O::store(p.D, row * p.d_sm + col * p.d_sn, v);
         }
       });
     });
@@ -898,6 +938,18 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_ring(const KParams p) {
   constexpr std::integral_constant<int, 0> OPA{};
   constexpr std::integral_constant<int, 1> OPB{};
   typedef std::integral_constant<int, 0> I0;
+  // Scheduling hint for one substep: alternate its NDS LDS reads (the next substep's fragments)
+  // with its NMF MFMAs, then fence the region.  Left alone, the scheduler issues each read just
+  // before the MFMA that needs it, and every MFMA then waits for an LDS round trip.
+  auto interleave = [&](auto NDS, auto NMF) {
+    constexpr int nds = NDS, nmf = NMF;
+    constexpr int per = (nmf + nds - 1) / nds;
+    static_for<nds>([&](auto) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+      __builtin_amdgcn_sched_group_barrier(0x008, per, 0); // then `per` MFMAs
+    });
+    __builtin_amdgcn_sched_barrier(0);
+  };
 
   if (nk > 0) {
     dma(OPA, 0, 0);
@@ -921,6 +973,9 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_ring(const KParams p) {
         if constexpr (s + 1 < S) {
           read_a(std::integral_constant<int, buf ^ 1>{}, sa, std::integral_constant<int, s + 1>{});
           mma_rows(std::integral_constant<int, buf>{}, s, I0{}, std::integral_constant<int, RM>{});
+          // the first substep also carries the B reads of the rest of the k-tile
+          interleave(std::integral_constant<int, RM * At::UNITS + (s == 0 ? (S - 1) * RN * At::UNITS : 0)>{},
+                     std::integral_constant<int, RM * RN * At::PER_UNIT>{});
           if constexpr (s + 1 == MID) {
             // this wave's reads of B(t) are complete (lgkmcnt 0); after the barrier no wave
             // reads B(t), and B(t+2) takes its slot
