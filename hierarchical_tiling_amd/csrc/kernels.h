@@ -1138,6 +1138,145 @@ static hipError_t launch_skinny(const KParams& p, hipStream_t s, dim3) {
 }
 
 // ------------------------------------------------------------------------------------------
+// The streaming skinny kernel: M <= 16, B streamed from HBM into LDS by DMA.
+//
+// Same problem as gemm_skinny (a decode-like product whose cost is reading B once: "CUTLASS",
+// Part III, memory bandwidth sets the ceiling), but B travels HBM -> LDS by buffer_load ... lds
+// instead of into registers: each DMA instruction moves 8 columns x 128 bytes of K (whole cache
+// lines), which streams from HBM markedly faster than 16-byte register loads of half lines.
+// A workgroup owns BN = 16 * NBW columns; its WK waves split K into contiguous slices and each
+// wave streams its slice through a private ring of R blocks (a block = 128 bytes of K for all BN
+// columns of B and the 16 rows of A, which stay L2-resident), so no barrier is needed in the
+// loop: a wave only waits for its own DMA, and no load in the loop targets registers.  Within a
+// block, chunk c (16 bytes) of LDS row r sits at slot c ^ ((r >> 1) & 7), so the 16 rows one
+// ds_read_b128 phase reads fall in 16 different 16-byte bank groups.  The WK partial sums meet in
+// LDS at the end.
+// ------------------------------------------------------------------------------------------
+template <int DT, int WK, int NBW, int R, int OCC>
+__global__ __launch_bounds__(WK * 64, OCC) void gemm_skinny_dma(const KParams p) {
+  typedef Atom<DT, 16> At;
+  typedef typename At::acc_t acc_t;               // 4 floats: rows 4*(l/16)+r, column l%16
+  constexpr int SZ = Ty<DT>::SZ;
+  constexpr int BN = NBW * 16;                    // columns per workgroup
+  constexpr int ROWS = BN + 16;                   // LDS rows per block: BN columns of B, 16 rows of A
+  constexpr int BLK = 128;                        // bytes of K per row per block
+  constexpr int BKE = BLK / SZ;                   // elements of K per block
+  constexpr int MPB = 2 / At::UNITS;              // MFMAs per block (8 chunks / (4 groups * UNITS))
+  constexpr int CPB = BN / 8;                     // B DMA instructions per block (8 rows each)
+  constexpr int OPS = CPB + 2;                    // DMA instructions per block per wave (B, then A)
+  constexpr int NT = WK * 64;
+  static_assert(At::PER_UNIT == 1 && MPB * At::UNITS * 4 == 8, "a block is 8 chunks");
+  static_assert((R - 2) * OPS < 64, "vmcnt range");
+
+  __shared__ u32x4 ring[WK][R][ROWS * 8];        // [wave][block][row * 8 + slot]
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t n0 = (int64_t)blockIdx.x * BN;
+  const int lr = lane & 15, lg = lane >> 4;
+
+  // K split: wave w owns blocks [w*per, min((w+1)*per, nb))
+  const int64_t nb = (p.K + BKE - 1) / BKE;
+  const int64_t per = (nb + WK - 1) / WK;
+  const int64_t b0 = wave * per;
+  const int nloc = (int)max((int64_t)0, min(b0 + per, nb) - b0);
+
+  const char* a_base = uniform_ptr((const char*)p.A);
+  const char* b_base = uniform_ptr((const char*)p.B + n0 * p.ldb * SZ);
+  const int64_t a_span = uniform_i64(((p.M - 1) * p.lda + p.K) * SZ);
+  const int64_t b_span = uniform_i64(((min((int64_t)BN, p.N - n0) - 1) * p.ldb + p.K) * SZ);
+  const int64_t kbytes = p.K * SZ;
+  // DMA lane: LDS row 8c + lane/8 of the block, slot lane%8, holding logical chunk slot ^ key(row)
+  auto key = [](int row) { return (row >> 1) & 7; };
+
+  acc_t acc[NBW];
+  static_for<NBW>([&](auto b) { acc[b] = acc_t{}; });
+
+  // Block j (local index) into ring slot `slot`.  Blocks past this wave's slice and chunks past K
+  // are out of range (zeros) and are issued anyway, so every block costs exactly OPS counter slots.
+  auto issue = [&](int j, auto slot) {
+    const bool live = j < nloc;
+    const int64_t kb = (b0 + j) * BLK;            // byte offset of the block along K
+    const int sk = live ? (int)kb : 0;
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(b_base, b_span);
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(a_base, a_span);
+    static_for<CPB + 2>([&](auto c) {
+      constexpr bool IS_A = c >= CPB;
+      const int row = 8 * c + (lane >> 3);        // LDS row; A rows are ROWS-16 .. ROWS-1
+      const int src = IS_A ? row - BN : row;      // column of B or row of A
+      const int ch = (lane & 7) ^ key(row);
+      const bool ok = live && kb + ch * 16 < kbytes;
+      const uint32_t off = (uint32_t)(src * (IS_A ? p.lda : p.ldb) * SZ + ch * 16);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(IS_A ? ra : rb, (lds_void_t*)(&ring[wave][slot][c * 64]),
+                                               16, ok ? off : 0x80000000u, sk, 0, 0);
+    });
+  };
+  auto compute = [&](auto slot) {
+    const u32x4* blk = &ring[wave][slot][0];
+    static_for<MPB>([&](auto m) {
+      u32x4 fa[At::UNITS];
+      static_for<At::UNITS>([&](auto x) {
+        const int row = BN + lr, chunk = (m * 4 + lg) * At::UNITS + x;
+        fa[x] = blk[row * 8 + (chunk ^ key(row))];
+      });
+      static_for<NBW>([&](auto b) {
+        u32x4 fb[At::UNITS];
+        static_for<At::UNITS>([&](auto x) {
+          const int row = 16 * b + lr, chunk = (m * 4 + lg) * At::UNITS + x;
+          fb[x] = blk[row * 8 + (chunk ^ key(row))];
+        });
+        At::mma(acc[b], fa, fb, 0);
+      });
+    });
+  };
+
+  // R-1 blocks in flight; each step waits for the oldest, refills the slot computed on one step
+  // earlier, then computes.  The trip count is rounded up to whole rings (the extra blocks are
+  // zero-filled and add exact zeros) so the loop body has no branches.
+  static_for<R - 1>([&](auto q) { issue(q, q); });
+  for (int j = 0; j < nloc; j += R) {
+    static_for<R>([&](auto q) {
+      // block j+q has landed; lgkmcnt(0) also retires the reads of the slot refilled next
+      wait_counts<(R - 2) * OPS, true>();
+      issue(j + q + R - 1, std::integral_constant<int, (q + R - 1) % R>{});
+      compute(q);
+    });
+  }
+  wait_counts<0, true>();
+
+  // partial sums -> LDS (reusing the ring); reduction over the WK slices; epilogue
+  __syncthreads();
+  float* part = reinterpret_cast<float*>(&ring[0][0][0]);  // [WK][NBW][16][16]
+  static_assert(sizeof(ring) >= sizeof(float) * WK * NBW * 256, "reduction buffer");
+  static_for<NBW>([&](auto b) {
+    static_for<4>([&](auto r) { part[((wave * NBW + b) * 16 + 4 * lg + r) * 16 + lr] = acc[b][(int)r]; });
+  });
+  __syncthreads();
+  constexpr int ODT = out_dtype(DT);
+  typedef Out<ODT> O;
+  for (int q = tid; q < 16 * BN; q += NT) {
+    const int row = q / BN, c = q % BN;
+    const int64_t col = n0 + c;
+    if (row >= p.M || col >= p.N) continue;
+    float sum = 0.f;
+#pragma unroll
+    for (int w = 0; w < WK; ++w) sum += part[((w * NBW + c / 16) * 16 + row) * 16 + c % 16];
+    float v = p.alpha * sum;
+    if (p.has_c) v += p.beta * O::load(p.C, row * p.c_sm + col * p.c_sn);
+    if (p.has_bias) v += O::load(p.bias, col);
+    v = activate(p.act, v);
+    O::store(p.D, row * p.d_sm + col * p.d_sn, v);
+  }
+}
+
+template <int DT, int WK, int NBW, int R, int OCC>
+static hipError_t launch_skinny_dma(const KParams& p, hipStream_t s, dim3) {
+  constexpr int BN = NBW * 16;
+  const dim3 grid((unsigned)((p.N + BN - 1) / BN));
+  hipLaunchKernelGGL((gemm_skinny_dma<DT, WK, NBW, R, OCC>), grid, dim3(WK * 64), 0, s, p);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------------------
 // Launchers and the tile table.
 // ------------------------------------------------------------------------------------------
 template <int DT, bool AK, bool BKM, bool VEC, int BM, int BN, int BKE, int WM, int WN, int MI>
@@ -1159,6 +1298,11 @@ static hipError_t launch_tiled(const KParams& p, hipStream_t s, dim3 grid) {
 #define HT_RING(NAME, DT, WM, WN, MI, RANK)                                                      \
   {NAME, DT, 1, 1, 1, 0, 256, 256, 128 / Ty<DT>::SZ, WM * WN, 5, 5 * 256 * 128, 1, RANK,          \
    &launch_ring<DT, WM, WN, MI>}
+
+// Streaming skinny entries: bm = 16 rows, bn = 16*NBW columns, bk = one 128-byte block of K.
+#define HT_SKINNY_DMA(NAME, DT, WK, NBW, R, OCC)                                                  \
+  {NAME, DT, 1, 1, 1, 1, 16, NBW * 16, 128 / Ty<DT>::SZ, WK, R, WK * R * (NBW + 1) * 16 * 128, 1, 0, \
+   &launch_skinny_dma<DT, WK, NBW, R, OCC>}
 
 // Skinny entries: bm = 16 rows, bn = WN*NBW*16 columns per workgroup, bk = one MFMA k-step.
 #define HT_SKINNY(NAME, DT, WK, WN, NBW, U, OCC)                                                 \
