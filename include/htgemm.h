@@ -37,7 +37,9 @@
  * Conventions where the pages are silent:
  *   - beta == 0 means C is not read at all (C may be NULL; NaNs in C do not propagate).
  *   - alpha == 0 is not special-cased: NaN or Inf in A or B still propagate through 0 * x.
- *   - GELU is the exact form x * Phi(x) = 0.5 * x * (1 + erf(x / sqrt(2))).
+ *   - GELU is the exact form x * Phi(x) = 0.5 * x * (1 + erf(x / sqrt(2))); the kernels evaluate
+ *     erf with the branch-free Abramowitz-Stegun formula 7.1.26 (|error| <= 1.5e-7, far below
+ *     the output rounding), not the tanh approximation.
  *   - fp8 is OCP E4M3 ("fn": bias 7, max 448, no infinities); outputs round to nearest even.
  *   - M == 0 or N == 0 is a valid empty problem; K == 0 gives D = act(beta*C + bias).
  *
