@@ -28,6 +28,7 @@ HIP = [HIPCC, f"--offload-arch={ARCH}"] + COMMON + DEVICE_FLAGS
 # kernels.h holds the kernel templates; each table_*.hip instantiates one operand type's entries
 SOURCES = [
     ("table_bf16.hip", HIP),
+    ("table_bf16_dma.hip", HIP),
     ("table_f16.hip", HIP),
     ("table_e4m3.hip", HIP),
     ("table_f32.hip", HIP),

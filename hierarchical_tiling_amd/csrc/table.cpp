@@ -7,6 +7,7 @@
 namespace htk {
 
 const KernelEntry* table_bf16(int* n);
+const KernelEntry* table_bf16_dma(int* n);
 const KernelEntry* table_f16(int* n);
 const KernelEntry* table_f32(int* n);
 const KernelEntry* table_e4m3(int* n);
@@ -27,6 +28,7 @@ struct Combined {
   }
   Combined() {
     append(table_bf16);
+    append(table_bf16_dma);
     append(table_f16);
     append(table_f32);
     append(table_e4m3);
