@@ -33,6 +33,7 @@ SOURCES = [
     ("table_e4m3.hip", HIP),
     ("table_f32.hip", HIP),
     ("table.cpp", HIP),
+    ("reduce.hip", HIP),
     ("api.cpp", HIP),
     ("layout.cpp", ["g++"] + COMMON),
 ]

@@ -9,6 +9,7 @@
 // the measurement tool ships with the library).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdlib>
 #include <cstring>
 #include <new>
@@ -39,6 +40,8 @@ struct gemm_handle_s {
   int cfg;       // entry used when A and B are 16-byte aligned
   int fallback;  // narrow-load entry
   int group_m;
+  int split_cfg, split_fb;     // K slices of each entry (1: no split)
+  int64_t kps_cfg, kps_fb;     // K elements per slice
 };
 
 namespace {
@@ -90,9 +93,9 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // takes the skinny kernel when one fits.  Otherwise: the largest tile that still gives at least
 // one workgroup per CU (256 CUs), ties broken by the measured rank, else the tile with the most
 // workgroups.
-int choose(const gemm_handle_s& h, bool vec_a, bool vec_b, bool want_vec) {
+int choose(const gemm_handle_s& h, bool vec_a, bool vec_b, bool want_vec, bool need_split) {
   const KernelEntry* t = table();
-  for (int i = 0; i < table_size(); ++i)
+  for (int i = 0; i < table_size() && !need_split; ++i)
     if (t[i].skinny && (t[i].vec != 0) == want_vec && entry_fits(t[i], h, vec_a, vec_b)) return i;
   int best = -1;
   int64_t best_area = -1;
@@ -101,6 +104,7 @@ int choose(const gemm_handle_s& h, bool vec_a, bool vec_b, bool want_vec) {
   for (int i = 0; i < table_size(); ++i) {
     const KernelEntry& e = t[i];
     if ((e.vec != 0) != want_vec || e.skinny) continue;
+    if (need_split && e.max_split_k <= 1) continue;
     if (!entry_fits(e, h, vec_a, vec_b)) continue;
     const int64_t wg = cdiv(h.d.M, e.bm) * cdiv(h.d.N, e.bn);
     const int64_t area = int64_t(e.bm) * e.bn;
@@ -114,6 +118,29 @@ int choose(const gemm_handle_s& h, bool vec_a, bool vec_b, bool want_vec) {
     }
   }
   return best >= 0 ? best : best_small;
+}
+
+// Split along K for entry e: S slices of whole k-tiles ("CUTLASS", Part III: split-K restores
+// occupancy when the output has too few tiles).  req > 1 forces S (at most one slice per
+// k-tile); req == 0 splits automatically when the output tiles fill fewer than half of the 256
+// CUs and K holds at least 32 k-tiles: enough slices for about 256 workgroups, each slice keeping
+// at least 8 k-tiles; req == 1 never splits.
+void plan_split(const KernelEntry& e, const gemm_desc& d, int req, int* S, int64_t* kps) {
+  *S = 1;
+  *kps = d.K;
+  if (req == 1 || e.max_split_k <= 1 || d.K == 0) return;
+  const int64_t tiles = cdiv(d.M, e.bm) * cdiv(d.N, e.bn);
+  const int64_t nkt = cdiv(d.K, e.bk);
+  int64_t s = req;
+  if (req == 0) {
+    if (tiles >= 128 || nkt < 32) return;
+    s = std::min<int64_t>({cdiv(256, tiles), nkt / 8, 16});
+  }
+  s = std::min<int64_t>({s, nkt, (int64_t)e.max_split_k});
+  if (s <= 1) return;
+  const int64_t per = cdiv(nkt, s);  // k-tiles per slice
+  *kps = per * e.bk;
+  *S = (int)cdiv(nkt, per);           // no empty slice
 }
 
 int check_arch() {
@@ -136,7 +163,7 @@ int gemm_create(const gemm_desc* desc, gemm_t* out) {
   if (!desc || !out) return GEMM_ERR_INVALID_ARG;
   *out = nullptr;
   const gemm_desc& d = *desc;
-  if (d.reserved != 0) return GEMM_ERR_INVALID_ARG;
+  if (d.split_k < 0 || d.split_k > 64) return GEMM_ERR_INVALID_ARG;
   if (d.M < 0 || d.N < 0 || d.K < 0) return GEMM_ERR_INVALID_ARG;
   if (d.M > INT32_MAX / 2 || d.N > INT32_MAX / 2 || d.K > INT32_MAX / 2) return GEMM_ERR_INVALID_ARG;
   if (d.act < GEMM_ACT_NONE || d.act > GEMM_ACT_GELU) return GEMM_ERR_INVALID_ARG;
@@ -159,17 +186,21 @@ int gemm_create(const gemm_desc* desc, gemm_t* out) {
   if (rc) return rc;
 
   const bool va = vec_ok(h.a, d.M, d.K, d.a_type), vb = vec_ok(h.b, d.N, d.K, d.b_type);
-  h.fallback = choose(h, va, vb, false);
+  const bool need_split = d.split_k > 1;
+  h.fallback = choose(h, va, vb, false, need_split);
   if (h.fallback < 0) return GEMM_ERR_NO_CONFIG;
   if (d.force_config >= 0) {
     if (d.force_config >= table_size() || !entry_fits(table()[d.force_config], h, va, vb))
       return GEMM_ERR_NO_CONFIG;
+    if (need_split && table()[d.force_config].max_split_k <= 1) return GEMM_ERR_NO_CONFIG;
     h.cfg = d.force_config;
   } else {
-    h.cfg = (va && vb) ? choose(h, va, vb, true) : -1;
+    h.cfg = (va && vb) ? choose(h, va, vb, true, need_split) : -1;
     if (h.cfg < 0) h.cfg = h.fallback;
   }
   h.group_m = 4;
+  plan_split(table()[h.cfg], d, d.split_k, &h.split_cfg, &h.kps_cfg);
+  plan_split(table()[h.fallback], d, d.split_k, &h.split_fb, &h.kps_fb);
 
   gemm_handle_s* p = new (std::nothrow) gemm_handle_s(h);
   if (!p) return GEMM_ERR_INVALID_ARG;
@@ -181,7 +212,8 @@ int gemm_create(const gemm_desc* desc, gemm_t* out) {
 int gemm_workspace_size(gemm_t h, size_t* bytes) {
   if (!h || h->magic != kMagic) return GEMM_ERR_BAD_HANDLE;
   if (!bytes) return GEMM_ERR_INVALID_ARG;
-  *bytes = 0;
+  const int s = std::max(h->split_cfg, h->split_fb);
+  *bytes = s > 1 ? (size_t)s * (size_t)h->d.M * (size_t)h->d.N * sizeof(float) : 0;
   return GEMM_OK;
 }
 
@@ -198,8 +230,8 @@ int gemm_get_info(gemm_t h, gemm_info* info) {
   info->waves = e.waves;
   info->stages = e.stages;
   info->lds_bytes = e.lds_bytes;
-  info->split_k = 1;
-  info->grid = cdiv(h->d.M, e.bm) * cdiv(h->d.N, e.bn);
+  info->split_k = h->split_cfg;
+  info->grid = cdiv(h->d.M, e.bm) * cdiv(h->d.N, e.bn) * h->split_cfg;
   std::strncpy(info->name, e.name, sizeof(info->name) - 1);
   return GEMM_OK;
 }
@@ -207,7 +239,6 @@ int gemm_get_info(gemm_t h, gemm_info* info) {
 int gemm_run(gemm_t h, const void* A, const void* B, const void* C, void* D, const void* bias,
              float alpha, float beta, float scale_a, float scale_b, void* workspace,
              void* stream) {
-  (void)workspace;
   if (!h || h->magic != kMagic) return GEMM_ERR_BAD_HANDLE;
   const gemm_desc& d = h->d;
   const bool read_c = d.has_c && beta != 0.0f;
@@ -223,6 +254,9 @@ int gemm_run(gemm_t h, const void* A, const void* B, const void* C, void* D, con
   int idx = h->cfg;
   if (table()[idx].vec && (!aligned(A, 16) || !aligned(B, 16))) idx = h->fallback;
   const KernelEntry& e = table()[idx];
+  const int split = idx == h->cfg ? h->split_cfg : h->split_fb;
+  const int64_t kps = idx == h->cfg ? h->kps_cfg : h->kps_fb;
+  if (split > 1 && (!workspace || !aligned(workspace, 16))) return GEMM_ERR_INVALID_ARG;
 
   KParams p;
   std::memset(&p, 0, sizeof(p));
@@ -248,11 +282,13 @@ int gemm_run(gemm_t h, const void* A, const void* B, const void* C, void* D, con
   p.tiles_m = (int)cdiv(d.M, e.bm);
   p.tiles_n = (int)cdiv(d.N, e.bn);
   p.group_m = h->group_m;
-  p.split_k = 1;
-  p.k_per_split = (int)d.K;
+  p.split_k = split;
+  p.k_per_split = (int)kps;
+  p.workspace = split > 1 ? static_cast<float*>(workspace) : nullptr;
   const int64_t grid = int64_t(p.tiles_m) * p.tiles_n;
   if (grid <= 0 || grid > INT32_MAX) return GEMM_ERR_INVALID_ARG;
-  hipError_t err = e.launch(p, (hipStream_t)stream, dim3((unsigned)grid));
+  hipError_t err = e.launch(p, (hipStream_t)stream, dim3((unsigned)grid, (unsigned)split));
+  if (err == hipSuccess && split > 1) err = launch_splitk_reduce(p, d.d_type, (hipStream_t)stream);
   return err == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
 }
 

@@ -50,6 +50,10 @@ struct KernelEntry {
 const KernelEntry* table();
 int table_size();
 
+// Second kernel of a split-K run: D = act(alpha * sum of the split_k fp32 planes in
+// p.workspace + beta * C + bias), with out_type the type of C, D and bias.
+hipError_t launch_splitk_reduce(const KParams& p, int out_type, hipStream_t s);
+
 // Output type of a given operand type (htgemm.h type table).
 constexpr int out_dtype(int dt) { return dt == DT_F8 ? DT_BF16 : dt; }
 constexpr int dtype_size(int dt) { return dt == DT_F32 ? 4 : (dt == DT_F8 ? 1 : 2); }

@@ -234,6 +234,59 @@ __device__ __forceinline__ float activate(int act, float v) {
 }
 
 // ------------------------------------------------------------------------------------------
+// Split-K ("CUTLASS", Part III: a problem with too few output tiles to fill the GPU splits its K
+// loop across several workgroups, whose partial sums are reduced afterwards).  Workgroup row
+// blockIdx.y takes the K slice [k_begin, k_begin + k_len); operand pointers are advanced to
+// k_begin so the mainloops see a problem of depth k_len.  Each slice writes its raw fp32 sums to
+// its own M x N plane of the workspace; gemm_splitk_reduce adds the planes in a fixed order and
+// applies the epilogue, so results do not depend on scheduling.
+// ------------------------------------------------------------------------------------------
+struct KRange {
+  int64_t begin, len;
+};
+__device__ __forceinline__ KRange k_range(const KParams& p) {
+  if (p.split_k <= 1) return {0, p.K};
+  const int64_t b = (int64_t)blockIdx.y * p.k_per_split;
+  return {b, max((int64_t)0, min((int64_t)p.k_per_split, p.K - b))};
+}
+// operand base advanced by k elements along K (KMAJ: K is the unit-stride direction)
+template <int DT, bool KMAJ>
+__device__ __forceinline__ const void* advance_k(const void* base, int64_t ld, int64_t k) {
+  return (const char*)base + (KMAJ ? k : k * ld) * Ty<DT>::SZ;
+}
+// raw fp32 partial sums of this workgroup's tile into plane blockIdx.y of the workspace
+template <int DT, int MI, int WTM, int WTN, int RM, int RN, class AccT>
+__device__ __forceinline__ void store_partial(const KParams& p, const AccT (&acc)[RM][RN],
+                                              int64_t m0, int64_t n0, int wm, int wn, int lane) {
+  typedef Atom<DT, MI> At;
+  float* w = p.workspace + (int64_t)blockIdx.y * p.M * p.N;
+  static_for<RM>([&](auto i) {
+    static_for<RN>([&](auto j) {
+      const int64_t col = n0 + wn * WTN + j * MI + (lane % MI);
+      static_for<At::NACC>([&](auto r) {
+        const int64_t row = m0 + wm * WTM + i * MI + acc_row<MI>(lane, r);
+        if (row < p.M && col < p.N) w[row * p.N + col] = acc[i][j][(int)r];
+      });
+    });
+  });
+}
+// D = act(alpha * sum_s W[s] + beta * C + bias) elementwise, the planes added in order s = 0, 1, ...
+template <int ODT>
+__global__ __launch_bounds__(256) void gemm_splitk_reduce(const KParams p) {
+  typedef Out<ODT> O;
+  const int64_t MN = p.M * p.N;
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < MN; e += (int64_t)gridDim.x * 256) {
+    const int64_t row = e / p.N, col = e - row * p.N;
+    float sum = 0.f;
+    for (int s = 0; s < p.split_k; ++s) sum += p.workspace[s * MN + e];
+    float v = p.alpha * sum;
+    if (p.has_c) v += p.beta * O::load(p.C, row * p.c_sm + col * p.c_sn);
+    if (p.has_bias) v += O::load(p.bias, col);
+    O::store(p.D, row * p.d_sm + col * p.d_sn, activate(p.act, v));
+  }
+}
+
+// ------------------------------------------------------------------------------------------
 // Tile loaders: global -> registers -> swizzled LDS.
 // LDS row r (an m of A or an n of B) holds BK elements as CH = BK*SZ/16 chunks.
 // Every loader has the same interface: init() once per tile, load<PRED>(k0) for the k-tile at
@@ -559,11 +612,12 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_tiled(const KParams p) {
 
   typename PickLoader<DT, AK, VEC, BM, BKE, NT>::type la;
   typename PickLoader<DT, BKM, VEC, BN, BKE, NT>::type lb;
-  la.init(p.A, p.lda, m0, p.M, p.K, tid);
-  lb.init(p.B, p.ldb, n0, p.N, p.K, tid);
+  const KRange kr = k_range(p);
+  la.init(advance_k<DT, AK>(p.A, p.lda, kr.begin), p.lda, m0, p.M, kr.len, tid);
+  lb.init(advance_k<DT, BKM>(p.B, p.ldb, kr.begin), p.ldb, n0, p.N, kr.len, tid);
 
-  const int nk = (int)((p.K + BKE - 1) / BKE);
-  const int nfull = (int)(p.K / BKE);
+  const int nk = (int)((kr.len + BKE - 1) / BKE);
+  const int nfull = (int)(kr.len / BKE);
 
   // fragment addressing: lane row within an atom, and lane group along k
   const int frow = lane % MI, fgrp = lane / MI;
@@ -622,8 +676,12 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_tiled(const KParams p) {
     }
   }
 
-  epilogue<DT, MI, BM, BN, WTM, WTN, RM, RN, NT, sizeof(lds)>(p, acc, &lds[0][0], m0, n0, wm, wn,
-                                                              lane, tid, nk == 0);
+  if (p.split_k > 1) {
+    store_partial<DT, MI, WTM, WTN>(p, acc, m0, n0, wm, wn, lane);
+  } else {
+    epilogue<DT, MI, BM, BN, WTM, WTN, RM, RN, NT, sizeof(lds)>(p, acc, &lds[0][0], m0, n0, wm, wn,
+                                                                lane, tid, nk == 0);
+  }
 }
 
 // ------------------------------------------------------------------------------------------
@@ -883,10 +941,13 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_ring(const KParams p) {
   acc_t acc[RM][RN];
   static_for<RM>([&](auto i) { static_for<RN>([&](auto j) { acc[i][j] = acc_t{}; }); });
 
-  const char* a_tile = uniform_ptr((const char*)p.A + m0 * p.lda * SZ);
-  const char* b_tile = uniform_ptr((const char*)p.B + n0 * p.ldb * SZ);
-  const int64_t a_span = uniform_i64(((p.M - m0 - 1) * p.lda + p.K) * SZ);
-  const int64_t b_span = uniform_i64(((min((int64_t)BN, p.N - n0) - 1) * p.ldb + p.K) * SZ);
+  // this workgroup's K slice (all of K unless the product is split along K)
+  const KRange kr = k_range(p);
+  const int64_t K = kr.len;
+  const char* a_tile = uniform_ptr((const char*)p.A + (m0 * p.lda + kr.begin) * SZ);
+  const char* b_tile = uniform_ptr((const char*)p.B + (n0 * p.ldb + kr.begin) * SZ);
+  const int64_t a_span = uniform_i64(((p.M - m0 - 1) * p.lda + K) * SZ);
+  const int64_t b_span = uniform_i64(((min((int64_t)BN, p.N - n0) - 1) * p.ldb + K) * SZ);
   // lane l of a DMA block fills slot l of a kilobyte: row l/CH, slot l%CH, which holds logical
   // chunk (l%CH) ^ key(row)
   auto src_off = [&](int blk, int64_t ld, int& kc) -> uint32_t {
@@ -895,7 +956,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_ring(const KParams p) {
     kc = c * VE;
     return (uint32_t)(row * ld * SZ + c * 16);
   };
-  const int nk = (int)((p.K + BKE - 1) / BKE);
+  const int nk = (int)((K + BKE - 1) / BKE);
 
   // Unit OP (0: A, 1: B) of k-tile t into `slot`.  Units past the end of K are all out of range
   // (zeros) and are issued anyway, so the wait counts stay the same on every k-tile.
@@ -909,7 +970,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_ring(const KParams p) {
       int kc;
       const uint32_t off = src_off(blk, ld, kc);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(st + blk * 64), 16,
-                                               k0 + kc < p.K ? off : 0x80000000u,
+                                               k0 + kc < K ? off : 0x80000000u,
                                                (int)(k0 * SZ), 0, 0);
     });
   };
@@ -1001,8 +1062,12 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_ring(const KParams p) {
     wait_counts<0, true>();  // the zero-filled units issued past the end are still in flight
     barrier_nofence();
   }
-  epilogue<DT, MI, BM, BN, WTM, WTN, RM, RN, NT, sizeof(lds)>(p, acc, lds, m0, n0, wm, wn, lane,
-                                                              tid, nk == 0);
+  if (p.split_k > 1) {
+    store_partial<DT, MI, WTM, WTN>(p, acc, m0, n0, wm, wn, lane);
+  } else {
+    epilogue<DT, MI, BM, BN, WTM, WTN, RM, RN, NT, sizeof(lds)>(p, acc, lds, m0, n0, wm, wn, lane,
+                                                                tid, nk == 0);
+  }
 }
 
 template <int DT, int WM, int WN, int MI>
@@ -1288,7 +1353,7 @@ static hipError_t launch_tiled(const KParams& p, hipStream_t s, dim3 grid) {
 }
 
 #define HT_TILED(NAME, DT, AK, BKM, VEC, BM, BN, BKE, WM, WN, MI)                        \
-  {NAME, DT, AK, BKM, VEC, 0, BM, BN, BKE, WM * WN, 2, 2 * (BM + BN) * BKE * Ty<DT>::SZ, 1, 0, \
+  {NAME, DT, AK, BKM, VEC, 0, BM, BN, BKE, WM * WN, 2, 2 * (BM + BN) * BKE * Ty<DT>::SZ, 64, 0, \
    &launch_tiled<DT, AK, BKM, VEC, BM, BN, BKE, WM, WN, MI>}
 
 #define HT_DMA(NAME, DT, BM, BN, WM, WN, MI, ST, OCC, CH, RANK)                                \
@@ -1297,7 +1362,7 @@ static hipError_t launch_tiled(const KParams& p, hipStream_t s, dim3 grid) {
 
 // Split-ring entries: 256 x 256 tiles, 128-byte rows, 5 units of 32 KiB.
 #define HT_RING(NAME, DT, WM, WN, MI, RANK)                                                      \
-  {NAME, DT, 1, 1, 1, 0, 256, 256, 128 / Ty<DT>::SZ, WM * WN, 5, 5 * 256 * 128, 1, RANK,          \
+  {NAME, DT, 1, 1, 1, 0, 256, 256, 128 / Ty<DT>::SZ, WM * WN, 5, 5 * 256 * 128, 64, RANK,         \
    &launch_ring<DT, WM, WN, MI>}
 
 // Streaming skinny entries: bm = 16 rows, bn = 16*NBW columns, bk = one 128-byte block of K.

@@ -45,7 +45,7 @@ class gemm_desc(ctypes.Structure):
                 ("b_stride_k", ctypes.c_int64), ("b_stride_n", ctypes.c_int64),
                 ("c_stride_m", ctypes.c_int64), ("c_stride_n", ctypes.c_int64),
                 ("d_stride_m", ctypes.c_int64), ("d_stride_n", ctypes.c_int64),
-                ("force_config", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("force_config", ctypes.c_int32), ("split_k", ctypes.c_int32)]
 
 
 class gemm_info(ctypes.Structure):
@@ -164,7 +164,7 @@ def gemm_config_name(i: int) -> str:
 
 
 def make_desc(M, N, K, dtype, a_strides, b_strides, d_strides, c_strides=None, has_bias=False,
-              act="none", force_config=-1) -> gemm_desc:
+              act="none", force_config=-1, split_k=0) -> gemm_desc:
     """a_strides = (stride_m, stride_k); b_strides = (stride_k, stride_n); c/d = (m, n)."""
     out_t = "bf16" if dtype == "e4m3" else dtype
     d = gemm_desc()
@@ -179,7 +179,7 @@ def make_desc(M, N, K, dtype, a_strides, b_strides, d_strides, c_strides=None, h
     d.c_stride_m, d.c_stride_n = c_strides if c_strides is not None else (0, 0)
     d.d_stride_m, d.d_stride_n = d_strides
     d.force_config = force_config
-    d.reserved = 0
+    d.split_k = split_k
     return d
 
 
@@ -194,10 +194,14 @@ class Gemm:
     def info(self) -> gemm_info:
         return gemm_get_info(self.handle)
 
+    @property
+    def workspace_bytes(self) -> int:
+        return gemm_workspace_size(self.handle)
+
     def run(self, A, B, C, D, bias=None, alpha=1.0, beta=0.0, scale_a=1.0, scale_b=1.0,
-            stream=None):
+            stream=None, workspace=None):
         gemm_run(self.handle, _addr(A), _addr(B), _addr(C), _addr(D), _addr(bias), alpha, beta,
-                 scale_a, scale_b, None, _stream(stream))
+                 scale_a, scale_b, _addr(workspace), _stream(stream))
 
     def close(self):
         if self.handle:

@@ -20,7 +20,8 @@
  * reusable handle whose kernel chooses its own grid):
  *   gemm_create         validates the problem ("can_implement") and picks a kernel from the
  *                       tile table; it allocates host memory only.
- *   gemm_workspace_size reports the device scratch the caller must pass to gemm_run (0 here).
+ *   gemm_workspace_size reports the device scratch the caller must pass to gemm_run (non-zero
+ *                       only for a problem split along K).
  *   gemm_run            enqueues the kernel on the caller's HIP stream; asynchronous.
  *   gemm_destroy        frees the handle.
  *
@@ -92,7 +93,8 @@ typedef struct gemm_desc {
   int64_t c_stride_m, c_stride_n;   /* C(m, n); ignored if has_c == 0                            */
   int64_t d_stride_m, d_stride_n;   /* D(m, n)                                                    */
   int32_t force_config;       /* -1: choose from the tile table; else a table index (tuning)     */
-  int32_t reserved;           /* must be 0                                                       */
+  int32_t split_k;            /* split of K across workgroups per output tile: 0 = automatic,    */
+                              /* 1 = never, 2..64 = that many slices (capped at one per k-tile)  */
 } gemm_desc;
 
 typedef struct gemm_handle_s* gemm_t;
@@ -102,7 +104,11 @@ typedef struct gemm_handle_s* gemm_t;
  * GEMM_ERR_LAYOUT, GEMM_ERR_ARCH, GEMM_ERR_NO_CONFIG, GEMM_ERR_HIP. */
 int gemm_create(const gemm_desc* desc, gemm_t* out);
 
-/* Bytes of device workspace gemm_run needs for this handle (currently always 0). */
+/* Bytes of device workspace gemm_run needs for this handle: 0 unless the problem is split along
+ * K ("CUTLASS", Part III: split-K for outputs with too few tiles to fill the GPU), in which case
+ * it is split_k * M * N * 4 (one fp32 plane of partial sums per slice).  The caller owns the
+ * workspace; its contents after a run are unspecified, and two runs in flight at once need two
+ * workspaces. */
 int gemm_workspace_size(gemm_t h, size_t* bytes);
 
 /* Enqueue D = act(alpha*scale_a*scale_b*(A@B) + beta*C + bias) on `stream` (a hipStream_t;
@@ -110,8 +116,11 @@ int gemm_workspace_size(gemm_t h, size_t* bytes);
  * handle was created with has_c == 0 (then beta must be 0); bias must be non-NULL iff the handle
  * has has_bias == 1.  scale_a and scale_b are the per-tensor dequantisation scales (pass 1.0f for
  * non-fp8 operands).  Pointers only need element alignment: the library falls back to a
- * narrow-load kernel when a pointer is not 16-byte aligned.  Returns after the launch is queued;
- * launch failures return GEMM_ERR_LAUNCH. */
+ * narrow-load kernel when a pointer is not 16-byte aligned.  `workspace` is a device buffer of
+ * gemm_workspace_size() bytes, 16-byte aligned (GEMM_ERR_INVALID_ARG if it is needed and missing;
+ * ignored when that size is 0).  A split run is two kernels on `stream`: the K slices, then their
+ * fixed-order sum and the epilogue.  Returns after the launches are queued; launch failures
+ * return GEMM_ERR_LAUNCH. */
 int gemm_run(gemm_t h, const void* A, const void* B, const void* C, void* D, const void* bias,
              float alpha, float beta, float scale_a, float scale_b, void* workspace,
              void* stream);

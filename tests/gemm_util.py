@@ -42,6 +42,7 @@ class Case:
     force: int = -1
     a_offset: int = 0           # element offset of A's base pointer (misalignment tests)
     c_fill_nan: bool = False
+    split_k: int = 0            # 0: the library decides; 1: never; >1: that many K slices
 
 
 def op(m):
@@ -91,7 +92,7 @@ class Prepared:
         c = self.case
         return H.make_desc(c.M, c.N, c.K, c.dtype, self.A.strides, self.B.strides, self.d_strides,
                            c_strides=self.C.strides if self.C is not None else None,
-                           has_bias=c.bias, act=c.act, force_config=c.force)
+                           has_bias=c.bias, act=c.act, force_config=c.force, split_k=c.split_k)
 
     def run(self, g: H.Gemm | None = None, out=None):
         c = self.case
@@ -100,8 +101,12 @@ class Prepared:
         if out is None:
             out = torch.zeros(self.d_len * es_out, dtype=torch.uint8, device=self.device)
         a_ptr = self.dA[0].data_ptr() + c.a_offset * inputs.ESIZE[c.dtype]
+        ws_bytes = g.workspace_bytes
+        # the workspace starts as NaN: every plane element a split run reads must be written first
+        ws = torch.full((max(ws_bytes, 4) // 4,), float("nan"), dtype=torch.float32,
+                        device=self.device) if ws_bytes else None
         g.run(a_ptr, self.dB, self.dC, out, self.dbias, alpha=c.alpha, beta=c.beta,
-              scale_a=c.scale_a, scale_b=c.scale_b)
+              scale_a=c.scale_a, scale_b=c.scale_b, workspace=ws)
         torch.cuda.synchronize()
         return g, out
 

@@ -63,7 +63,8 @@ def test_valid_descriptor_creates(fake_gfx950):
 
 @pytest.mark.parametrize("mutate,status", [
     (lambda d: setattr(d, "M", -1), 1),
-    (lambda d: setattr(d, "reserved", 3), 1),
+    (lambda d: setattr(d, "split_k", -1), 1),
+    (lambda d: setattr(d, "split_k", 65), 1),
     (lambda d: setattr(d, "act", 7), 1),
     (lambda d: setattr(d, "b_type", 1), 2),                      # A bf16 with B fp16
     (lambda d: setattr(d, "d_type", 0), 2),                      # bf16 inputs, fp32 output
@@ -147,3 +148,35 @@ def test_forced_config_must_match(fake_gfx950):
     assert status_of(desc(force_config=f16)) == 8      # bf16 problem, fp16 kernel
     bf = names.index("bf16_ak_bk_128x128x64_w2x2_m32_narrow")
     assert _info(desc(force_config=bf)).config == bf
+
+
+def test_split_k_plan_and_workspace(fake_gfx950):
+    """Split-K ("CUTLASS", Part III: split the K loop when the output has too few tiles): the
+    workspace holds one fp32 M x N plane per K slice; slices are whole k-tiles, never empty."""
+    # automatic: 1024 x 1024 (64 tiles of 128 x 128) with K = 65536 (1024 k-tiles) -> 4 slices
+    h = H.gemm_create(desc(M=1024, N=1024, K=65536, a_strides=(65536, 1), b_strides=(1, 65536),
+                           d_strides=(1024, 1)))
+    try:
+        info = H.gemm_get_info(h)
+        assert info.split_k == 4 and info.grid == (1024 // info.bm) * (1024 // info.bn) * 4
+        assert H.gemm_workspace_size(h) == 4 * 1024 * 1024 * 4
+        # a split run without a workspace is refused before any launch
+        assert H.lib().gemm_run(h, 256, 256, None, 256, None, 1.0, 0.0, 1.0, 1.0, None, None) == 1
+    finally:
+        H.gemm_destroy(h)
+    # enough tiles: no split and no workspace
+    assert _info(desc(M=8192, N=8192, K=65536, a_strides=(65536, 1), b_strides=(1, 65536),
+                      d_strides=(8192, 1))).split_k == 1
+    # forced: 3 slices of K = 64 * 7 (7 k-tiles of 64) -> 3, 3, 1 k-tiles
+    f = _info(desc(K=448, a_strides=(448, 1), b_strides=(1, 448), split_k=3))
+    assert f.split_k == 3
+    # forced beyond the k-tile count: capped at one slice per k-tile
+    assert _info(desc(K=128, a_strides=(128, 1), b_strides=(1, 128), split_k=8)).split_k == 2
+    # split_k = 1 never splits
+    assert _info(desc(M=1024, N=1024, K=65536, a_strides=(65536, 1), b_strides=(1, 65536),
+                      d_strides=(1024, 1), split_k=1)).split_k == 1
+    # the streaming skinny kernel has no split: forcing one selects a tiled kernel
+    names = [H.gemm_config_name(i) for i in range(H.gemm_num_configs())]
+    sk = _info(H.make_desc(16, 16384, 8192, "e4m3", (8192, 1), (1, 8192), (16384, 1), split_k=2))
+    assert b"skinny" not in sk.name and sk.split_k == 2
+    assert status_of(desc(M=16, force_config=names.index("bf16_ak_bk_16x32_w8_skinny"), split_k=2)) == 8

@@ -192,3 +192,71 @@ def test_error_does_not_grow_faster_than_sqrt_k():
         want = p.oracle_full()
         errs.append(np.abs(got - want).max() / np.sqrt(K))
     assert errs[2] <= 4 * errs[0] + 1e-12, errs
+
+
+# ---- split-K ("CUTLASS", Part III: K split across workgroups, partial sums reduced after) ----
+
+def _name_index(name):
+    names = [H.gemm_config_name(i) for i in range(H.gemm_num_configs())]
+    return names.index(name)
+
+
+SPLIT_CASES = {
+    # tiled 16-byte kernel, K tail inside the last slice, C and GELU in the reduction epilogue
+    "bf16_tiled_s3": dict(M=200, N=136, K=64 * 7 + 8, dtype="bf16", split_k=3, has_c=True,
+                          beta=-0.5, bias=True, act="gelu", alpha=0.75),
+    # split-ring kernel forced, ragged M/N tiles, K tail
+    "bf16_ring_s4": dict(M=264, N=328, K=64 * 9 + 16, dtype="bf16", split_k=4, bias=True,
+                         force="bf16_ak_bk_256x256x64_w2x4_m32_ring"),
+    "e4m3_ring_s3": dict(M=264, N=328, K=128 * 5 + 32, dtype="e4m3", split_k=3,
+                         scale_a=0.5, scale_b=0.25, force="e4m3_ak_bk_256x256x128_w2x4_m32_ring"),
+    # element-wise loaders (column-major A, row-major B, odd leading dims)
+    "f16_narrow_s2": dict(M=99, N=70, K=203, dtype="f16", a_order="col", b_order="row", split_k=2,
+                          has_c=True, beta=1.25, act="relu"),
+    "f32_s5": dict(M=130, N=96, K=32 * 10, dtype="f32", dist="uniform", split_k=5, has_c=True,
+                   beta=0.5, alpha=1.5),
+}
+
+
+@pytest.mark.parametrize("name", list(SPLIT_CASES))
+def test_split_k_matches_oracle(name):
+    kw = dict(SPLIT_CASES[name])
+    if isinstance(kw.get("force"), str):
+        kw["force"] = _name_index(kw["force"])
+    c = Case(seed=40 + list(SPLIT_CASES).index(name), **kw)
+    p = Prepared(c)
+    g, out = p.run()
+    assert g.info.split_k == c.split_k, (g.info.split_k, c.split_k)
+    assert g.workspace_bytes == c.split_k * c.M * c.N * 4
+    got, _ = p.decode_out(out)
+    assert np.isfinite(got).all()
+    err = error(c.dtype, got, p.oracle_full())
+    print(f"{name}: {g.info.name.decode()} split {g.info.split_k} err={err:.3e}")
+    assert err <= TOL[c.dtype], (name, err)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "e4m3", "f32"])
+def test_split_k_dyadic_is_bit_exact(dtype):
+    # exact fp32 partial sums: the split result equals the unsplit one and the oracle bit for bit
+    c = Case(M=136, N=200, K=320 if dtype != "e4m3" else 640, dtype=dtype, dist="dyadic",
+             alpha=2.0, beta=0.5, has_c=True, bias=True, seed=47, split_k=3,
+             scale_a=0.5 if dtype == "e4m3" else 1.0, scale_b=2.0 if dtype == "e4m3" else 1.0)
+    p = Prepared(c)
+    g, out = p.run()
+    assert g.info.split_k == 3
+    _, bits = p.decode_out(out)
+    want = oracle.encode_rne(OUT_T[dtype], p.oracle_full())
+    assert int((bits != want).sum()) == 0
+
+
+def test_split_k_automatic_on_few_tiles_and_long_k():
+    # 512 x 512 has 16 tiles of 128 x 128; K = 16384 (256 k-tiles) -> the library splits K
+    c = Case(M=512, N=512, K=16384, dtype="bf16", seed=48, bias=True)
+    p = Prepared(c)
+    g, out = p.run()
+    assert g.info.split_k > 1
+    got, _ = p.decode_out(out)
+    rows, cols = sample_indices(c.M, c.N, seed=2, n_rand=2048)
+    err = error("bf16", got[rows, cols], p.oracle_elems(rows, cols))
+    print(f"auto split {g.info.split_k}: {g.info.name.decode()} err={err:.3e}")
+    assert err <= TOL["bf16"], err
