@@ -1,6 +1,6 @@
 """Build libhtgemm.so (gfx950 HIP kernels + host API + layout helper) in the package directory.
 
-    python -m hierarchical_tiling_amd.build
+    python -m hierarchical_tiling_amd.build [--incremental]
 
 Objects go to _build/ at the repository root; the shared library lands next to this file so the
 binding loads it in-tree.
@@ -39,8 +39,16 @@ SOURCES = [
 ]
 
 
-def _compile(src, cmd):
+HEADERS = [os.path.join(CSRC, "kernels.h"), os.path.join(CSRC, "gemm_internal.h"),
+           os.path.join(ROOT, "include", "htgemm.h"), os.path.join(ROOT, "include", "htlayout.h")]
+
+
+def _compile(src, cmd, incremental=False):
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+    if incremental and os.path.exists(obj):
+        newest = max(os.path.getmtime(f) for f in HEADERS + [os.path.join(CSRC, src)])
+        if os.path.getmtime(obj) > newest:
+            return obj
     full = cmd + ["-c", os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(full, capture_output=True, text=True)
     if res.returncode != 0:
@@ -48,10 +56,12 @@ def _compile(src, cmd):
     return obj
 
 
-def build(verbose: bool = True) -> str:
+def build(verbose: bool = True, incremental: bool = False) -> str:
+    """Compile every source (incremental=True skips objects newer than their source and the
+    shared headers) and link the library."""
     os.makedirs(BUILD, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(lambda sc: _compile(*sc), SOURCES))
+        objs = list(ex.map(lambda sc: _compile(sc[0], sc[1], incremental), SOURCES))
     tmp = OUT + ".tmp"
     link = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
     res = subprocess.run(link, capture_output=True, text=True)
@@ -64,5 +74,5 @@ def build(verbose: bool = True) -> str:
 
 
 if __name__ == "__main__":
-    build()
+    build(incremental="--incremental" in sys.argv)
     sys.exit(0)

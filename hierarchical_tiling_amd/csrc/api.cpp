@@ -89,12 +89,37 @@ bool entry_fits(const KernelEntry& e, const gemm_handle_s& h, bool vec_a, bool v
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Split along K for entry e: S slices of whole k-tiles ("CUTLASS", Part III: split-K restores
+// occupancy when the output has too few tiles).  req > 1 forces S (at most one slice per
+// k-tile); req == 1 never splits; req == 0 (automatic) splits an output of fewer than 256 tiles
+// when K is long (at least 64 k-tiles) into enough slices for about 256 workgroups, at most 16,
+// each slice keeping at least 8 k-tiles.
+void plan_split(const KernelEntry& e, const gemm_desc& d, int req, int* S, int64_t* kps) {
+  *S = 1;
+  *kps = d.K;
+  if (req == 1 || e.max_split_k <= 1 || d.K == 0) return;
+  const int64_t tiles = cdiv(d.M, e.bm) * cdiv(d.N, e.bn);
+  const int64_t nkt = cdiv(d.K, e.bk);
+  int64_t s = req;
+  if (req == 0) {
+    if (tiles >= 256 || nkt < 64) return;
+    s = std::min<int64_t>({cdiv(256, tiles), nkt / 8, 16});
+  }
+  s = std::min<int64_t>({s, nkt, (int64_t)e.max_split_k});
+  if (s <= 1) return;
+  const int64_t per = cdiv(nkt, s);  // k-tiles per slice
+  *kps = per * e.bk;
+  *S = (int)cdiv(nkt, per);           // no empty slice
+}
+
 // Heuristic choice among fitting entries.  A product with M <= 16 is bound by streaming B and
-// takes the skinny kernel when one fits.  Otherwise: the largest tile that still gives at least
-// one workgroup per CU (256 CUs), ties broken by the measured rank, else the tile with the most
-// workgroups.
-int choose(const gemm_handle_s& h, bool vec_a, bool vec_b, bool want_vec, bool need_split) {
+// takes the skinny kernel when one fits.  Otherwise each entry is counted with the split-K plan
+// it would get (plan_split) and the choice is the largest tile whose workgroups (tiles x slices)
+// still number at least 256 (one per CU), ties broken by the measured rank, else the entry with
+// the most workgroups.  A forced split (split_req > 1) admits only entries that can split.
+int choose(const gemm_handle_s& h, bool vec_a, bool vec_b, bool want_vec, int split_req) {
   const KernelEntry* t = table();
+  const bool need_split = split_req > 1;
   for (int i = 0; i < table_size() && !need_split; ++i)
     if (t[i].skinny && (t[i].vec != 0) == want_vec && entry_fits(t[i], h, vec_a, vec_b)) return i;
   int best = -1;
@@ -106,7 +131,10 @@ int choose(const gemm_handle_s& h, bool vec_a, bool vec_b, bool want_vec, bool n
     if ((e.vec != 0) != want_vec || e.skinny) continue;
     if (need_split && e.max_split_k <= 1) continue;
     if (!entry_fits(e, h, vec_a, vec_b)) continue;
-    const int64_t wg = cdiv(h.d.M, e.bm) * cdiv(h.d.N, e.bn);
+    int slices;
+    int64_t kps;
+    plan_split(e, h.d, split_req, &slices, &kps);
+    const int64_t wg = cdiv(h.d.M, e.bm) * cdiv(h.d.N, e.bn) * slices;
     const int64_t area = int64_t(e.bm) * e.bn;
     if (wg >= 256 && (area > best_area || (area == best_area && e.rank > t[best].rank))) {
       best = i;
@@ -118,29 +146,6 @@ int choose(const gemm_handle_s& h, bool vec_a, bool vec_b, bool want_vec, bool n
     }
   }
   return best >= 0 ? best : best_small;
-}
-
-// Split along K for entry e: S slices of whole k-tiles ("CUTLASS", Part III: split-K restores
-// occupancy when the output has too few tiles).  req > 1 forces S (at most one slice per
-// k-tile); req == 0 splits automatically when the output tiles fill fewer than half of the 256
-// CUs and K holds at least 32 k-tiles: enough slices for about 256 workgroups, each slice keeping
-// at least 8 k-tiles; req == 1 never splits.
-void plan_split(const KernelEntry& e, const gemm_desc& d, int req, int* S, int64_t* kps) {
-  *S = 1;
-  *kps = d.K;
-  if (req == 1 || e.max_split_k <= 1 || d.K == 0) return;
-  const int64_t tiles = cdiv(d.M, e.bm) * cdiv(d.N, e.bn);
-  const int64_t nkt = cdiv(d.K, e.bk);
-  int64_t s = req;
-  if (req == 0) {
-    if (tiles >= 128 || nkt < 32) return;
-    s = std::min<int64_t>({cdiv(256, tiles), nkt / 8, 16});
-  }
-  s = std::min<int64_t>({s, nkt, (int64_t)e.max_split_k});
-  if (s <= 1) return;
-  const int64_t per = cdiv(nkt, s);  // k-tiles per slice
-  *kps = per * e.bk;
-  *S = (int)cdiv(nkt, per);           // no empty slice
 }
 
 int check_arch() {
@@ -187,7 +192,7 @@ int gemm_create(const gemm_desc* desc, gemm_t* out) {
 
   const bool va = vec_ok(h.a, d.M, d.K, d.a_type), vb = vec_ok(h.b, d.N, d.K, d.b_type);
   const bool need_split = d.split_k > 1;
-  h.fallback = choose(h, va, vb, false, need_split);
+  h.fallback = choose(h, va, vb, false, d.split_k);
   if (h.fallback < 0) return GEMM_ERR_NO_CONFIG;
   if (d.force_config >= 0) {
     if (d.force_config >= table_size() || !entry_fits(table()[d.force_config], h, va, vb))
@@ -195,7 +200,7 @@ int gemm_create(const gemm_desc* desc, gemm_t* out) {
     if (need_split && table()[d.force_config].max_split_k <= 1) return GEMM_ERR_NO_CONFIG;
     h.cfg = d.force_config;
   } else {
-    h.cfg = (va && vb) ? choose(h, va, vb, true, need_split) : -1;
+    h.cfg = (va && vb) ? choose(h, va, vb, true, d.split_k) : -1;
     if (h.cfg < 0) h.cfg = h.fallback;
   }
   h.group_m = 4;

@@ -153,17 +153,26 @@ def test_forced_config_must_match(fake_gfx950):
 def test_split_k_plan_and_workspace(fake_gfx950):
     """Split-K ("CUTLASS", Part III: split the K loop when the output has too few tiles): the
     workspace holds one fp32 M x N plane per K slice; slices are whole k-tiles, never empty."""
-    # automatic: 1024 x 1024 (64 tiles of 128 x 128) with K = 65536 (1024 k-tiles) -> 4 slices
+    # automatic: 1024 x 1024 with K = 65536: 16 tiles of 256 x 256, 16 slices -> 256 workgroups
     h = H.gemm_create(desc(M=1024, N=1024, K=65536, a_strides=(65536, 1), b_strides=(1, 65536),
                            d_strides=(1024, 1)))
     try:
         info = H.gemm_get_info(h)
-        assert info.split_k == 4 and info.grid == (1024 // info.bm) * (1024 // info.bn) * 4
-        assert H.gemm_workspace_size(h) == 4 * 1024 * 1024 * 4
+        assert (info.bm, info.bn) == (256, 256)
+        assert info.split_k == 16 and info.grid == 16 * 16
+        assert H.gemm_workspace_size(h) == 16 * 1024 * 1024 * 4
         # a split run without a workspace is refused before any launch
         assert H.lib().gemm_run(h, 256, 256, None, 256, None, 1.0, 0.0, 1.0, 1.0, None, None) == 1
     finally:
         H.gemm_destroy(h)
+    # 512 x 512 with K = 16384: only 128 x 128 tiles reach 256 workgroups (16 tiles x 16 slices)
+    small = _info(desc(M=512, N=512, K=16384, a_strides=(16384, 1), b_strides=(1, 16384),
+                       d_strides=(512, 1)))
+    assert (small.bm, small.split_k, small.grid) == (128, 16, 256)
+    # short K: no split even with few tiles (2048 x 2048 x 2048: 128 x 128 tiles, no split)
+    short = _info(desc(M=2048, N=2048, K=2048, a_strides=(2048, 1), b_strides=(1, 2048),
+                       d_strides=(2048, 1)))
+    assert short.split_k == 1 and short.bm == 128
     # enough tiles: no split and no workspace
     assert _info(desc(M=8192, N=8192, K=65536, a_strides=(65536, 1), b_strides=(1, 65536),
                       d_strides=(8192, 1))).split_k == 1
