@@ -80,6 +80,13 @@ bool entry_fits(const KernelEntry& e, const gemm_handle_s& h, bool vec_a, bool v
     if (h.a.kmajor && (int64_t(e.bm) * h.a.ld + d.K) * sz >= lim) return false;
     if (h.b.kmajor && (int64_t(e.bn) * h.b.ld + d.K) * sz >= lim) return false;
   }
+  if (e.realign) {
+    // realigned loaders: 31-bit offsets over a tile's rows (K-major) or over all of K (M/N-major)
+    const int64_t sz = dtype_size(e.dtype), lim = (int64_t(1) << 31) - 64;
+    const int64_t a_span = h.a.kmajor ? int64_t(e.bm) * h.a.ld + d.K : d.K * h.a.ld + e.bm;
+    const int64_t b_span = h.b.kmajor ? int64_t(e.bn) * h.b.ld + d.K : d.K * h.b.ld + e.bn;
+    if (a_span * sz >= lim || b_span * sz >= lim) return false;
+  }
   ht_tile_stats st;
   ht_tile_plan(e.bm, e.bn, e.bk, dtype_size(e.dtype), kLdsBudget, &st);
   if (!st.fits) return false;  // double-buffered A and B tiles must fit the LDS budget

@@ -45,6 +45,7 @@ struct KernelEntry {
   int max_split_k;    // largest split along K the kernel supports (1: none)
   int rank;           // preference among entries with the same tile area (measured; higher wins)
   launch_fn launch;
+  int realign;        // 1: realigned 16-byte loads of 2-byte elements (31-bit tile offsets)
 };
 
 const KernelEntry* table();

@@ -472,17 +472,208 @@ struct LoadNarrow {
   }
 };
 
-template <int DT, bool KMAJ, bool VEC, int R, int BKE, int NT>
+// ------------------------------------------------------------------------------------------
+// 2-byte operands whose rows are only 2-byte aligned (odd leading dimension or base).  Each
+// 16-byte chunk is fetched as the 16 dword-aligned bytes at or below its first element plus the
+// dword after them, and realigned with v_alignbyte only when it is written to LDS: nothing
+// consumes the loads before then, so they overlap the current k-tile's MFMAs as the other
+// loaders' do.  Offsets are 32-bit VGPR offsets from the tile's first byte rounded down to 4
+// bytes.  The descriptor's extent is the operand's end rounded up to a whole dword; a raw buffer
+// load checks each of its dwords against the extent on its own (a 16-byte load that straddles it
+// returns the dwords inside and zeros), and the dword that holds the operand's last element lies
+// in that element's page, so no unmapped byte is read.  Chunks wholly past K or past the last
+// row take an out-of-range offset (zeros); elements of a partial chunk past K, past the last
+// row or column, or past the operand's end are cleared by the element mask.
+// ------------------------------------------------------------------------------------------
+struct Raw16 {
+  u32x4 q;  // the 16 bytes at the dword-aligned address at or below the chunk
+  u32 x;    // the dword after them
+};
+__device__ __forceinline__ Raw16 raw16(__amdgpu_buffer_rsrc_t r, uint32_t a) {
+  return {__builtin_amdgcn_raw_buffer_load_b128(r, a, 0, 0),
+          __builtin_amdgcn_raw_buffer_load_b32(r, a + 16, 0, 0)};
+}
+// the 8 elements that start `sh` bytes into a fetched chunk; element e kept where bit e of emask
+// is set
+__device__ __forceinline__ u32x4 realign16(const Raw16& w, uint32_t sh, uint32_t emask) {
+  u32x4 v;
+  v[0] = __builtin_amdgcn_alignbyte(w.q[1], w.q[0], sh);
+  v[1] = __builtin_amdgcn_alignbyte(w.q[2], w.q[1], sh);
+  v[2] = __builtin_amdgcn_alignbyte(w.q[3], w.q[2], sh);
+  v[3] = __builtin_amdgcn_alignbyte(w.x, w.q[3], sh);
+  if (emask != 0xffu) {
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const uint32_t m2 = (emask >> (2 * d)) & 3u;
+      v[d] &= (m2 & 1u ? 0xffffu : 0u) | (m2 & 2u ? 0xffff0000u : 0u);
+    }
+  }
+  return v;
+}
+constexpr uint32_t kOobOffset = 0x80000000u;  // past any extent (extents are below 2^31)
+
+// K-contiguous 2-byte operand, any element alignment.  Same thread -> chunk map and LDS layout as
+// LoadKMajorVec.
+template <int DT, int R, int BKE, int NT>
+struct LoadKMajorMis {
+  static_assert(Ty<DT>::SZ == 2, "2-byte elements");
+  static constexpr int SZ = 2, VE = 8, CH = BKE * SZ / 16;
+  static constexpr int N = R * CH / NT;
+  static_assert(R * CH % NT == 0 && NT % CH == 0, "tile chunks must divide over the threads");
+  static_assert(N <= 24, "one shift bit per chunk");
+  Raw16 w[N];
+  uint32_t emask;     // element mask of this thread's chunk in the current k-tile
+  uint32_t shifts;    // bit i: chunk i starts 2 bytes past a dword (fixed: k-tiles are 128 bytes)
+  const char* rb;     // the tile's first byte rounded down to 4 bytes (uniform)
+  int64_t ext, K;     // descriptor extent in bytes; K
+  int64_t rows_left;  // rows of the operand from the tile's first row on
+  uint32_t voff, row_step;
+  int row, kc;        // this thread's first row within the tile; its chunk's first k
+  __device__ __forceinline__ void init(const void* base, int64_t ld, int64_t row0, int64_t rows,
+                                       int64_t K_, int tid) {
+    const char* tile = (const char*)base + row0 * ld * SZ;
+    rb = (const char*)((uintptr_t)tile & ~uintptr_t(3));
+    const uint32_t delta = (uint32_t)(tile - rb);
+    K = K_;
+    rows_left = rows - row0;
+    ext = (delta + ((rows_left - 1) * ld + K_) * SZ + 3) & ~int64_t(3);
+    row = tid / CH;
+    kc = (tid % CH) * VE;
+    voff = delta + (uint32_t)((row * ld + kc) * SZ);
+    row_step = (uint32_t)((NT / CH) * ld * SZ);
+    shifts = 0;
+#pragma unroll
+    for (int i = 0; i < N; ++i) shifts |= ((voff + i * row_step) & 2u) >> 1 << i;
+  }
+  template <bool PRED>
+  __device__ __forceinline__ void load(int64_t k0) {
+    const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(rb, ext);
+    const int64_t k = k0 + kc;
+    emask = 0xffu;
+    if (PRED) emask = k >= K ? 0u : (k + VE <= K ? 0xffu : ((1u << (K - k)) - 1u));
+    const uint32_t kb = (uint32_t)(k0 * SZ);
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const bool live = row + i * (NT / CH) < rows_left && emask != 0;
+      w[i] = raw16(rsrc, live ? ((voff + i * row_step + kb) & ~3u) : kOobOffset);
+    }
+  }
+  __device__ __forceinline__ void store(u32x4* lds, int tid) const {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int q = tid + i * NT, rr = q / CH, cc = q % CH;
+      lds[lds_slot<CH>(rr, cc)] = realign16(w[i], ((shifts >> i) & 1u) * 2u, emask);
+    }
+  }
+};
+
+// Row-contiguous (M- or N-contiguous) 2-byte operand, any element alignment: chunks of VE rows at
+// one k, realigned and then transposed in registers into K-contiguous chunks as in
+// LoadMNMajorVec; rows past the operand's last row and k past K are zero.
+template <int DT, int R, int BKE, int NT>
+struct LoadMNMajorMis {
+  static_assert(Ty<DT>::SZ == 2, "2-byte elements");
+  static constexpr int SZ = 2, VE = 8, CH = BKE * SZ / 16;
+  static constexpr int BLOCKS = (BKE / VE) * (R / VE);
+  static constexpr int N = (BLOCKS + NT - 1) / NT;
+  static_assert(BLOCKS % NT == 0 || (BLOCKS < NT && BLOCKS % 64 == 0),
+                "transpose blocks must cover whole waves");
+  static_assert(N <= 3, "mask bytes of the blocks fit one register");
+  Raw16 w[N][VE];
+  uint32_t nmasks;    // byte i: row mask of block i (fixed per tile)
+  uint32_t shifts;    // bit kk: the chunk at k offset kk starts 2 bytes past a dword
+  const char* rb;
+  int64_t ext, K, ld;
+  uint32_t boff[N];   // byte offset of block i at k = 0
+  int tid;
+  __device__ __forceinline__ void init(const void* base, int64_t ld_, int64_t row0, int64_t rows,
+                                       int64_t K_, int tid_) {
+    const char* tile = (const char*)base + row0 * SZ;
+    rb = (const char*)((uintptr_t)tile & ~uintptr_t(3));
+    const uint32_t delta = (uint32_t)(tile - rb);
+    ld = ld_;
+    K = K_;
+    tid = tid_;
+    const int64_t rows_left = rows - row0;
+    ext = (delta + ((K_ - 1) * ld_ + rows_left) * SZ + 3) & ~int64_t(3);
+    nmasks = 0;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int q = tid + i * NT, rbk = q % (R / VE), kb = q / (R / VE);
+      const int64_t n = (int64_t)rbk * VE;
+      const uint32_t m = n >= rows_left ? 0u : (n + VE <= rows_left ? 0xffu : ((1u << (rows_left - n)) - 1u));
+      nmasks |= m << (8 * i);
+      boff[i] = delta + (uint32_t)((kb * VE * ld_ + n) * SZ);
+    }
+    // every block's offset has the same parity in 2-byte units (n and kb * VE * ld are even), so
+    // the shift depends only on kk
+    shifts = 0;
+#pragma unroll
+    for (int kk = 0; kk < VE; ++kk) shifts |= ((boff[0] + (uint32_t)(kk * ld_ * SZ)) & 2u) >> 1 << kk;
+  }
+  template <bool PRED>
+  __device__ __forceinline__ void load(int64_t k0) {
+    const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(rb, ext);
+    const uint32_t kb0 = (uint32_t)(k0 * ld * SZ);
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int q = tid + i * NT, kb = q / (R / VE);
+      if (BLOCKS % NT != 0 && q >= BLOCKS) continue;
+      const bool any = ((nmasks >> (8 * i)) & 0xffu) != 0;
+#pragma unroll
+      for (int kk = 0; kk < VE; ++kk) {
+        const bool live = any && (!PRED || k0 + (int64_t)kb * VE + kk < K);
+        const uint32_t o = boff[i] + kb0 + (uint32_t)(kk * ld * SZ);
+        w[i][kk] = raw16(rsrc, live ? (o & ~3u) : kOobOffset);
+      }
+    }
+  }
+  __device__ __forceinline__ void store(u32x4* lds, int) const {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int q = tid + i * NT, rbk = q % (R / VE), kb = q / (R / VE);
+      if (BLOCKS % NT != 0 && q >= BLOCKS) continue;
+      const uint32_t m = (nmasks >> (8 * i)) & 0xffu;
+      u32x4 c[VE];
+#pragma unroll
+      for (int kk = 0; kk < VE; ++kk) c[kk] = realign16(w[i][kk], ((shifts >> kk) & 1u) * 2u, m);
+#pragma unroll
+      for (int rr = 0; rr < VE; ++rr) {
+        u32x4 o;
+        const int wd = rr >> 1, sh = (rr & 1) * 16;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          const u32 lo = (c[2 * d][wd] >> sh) & 0xffffu;
+          const u32 hi = (c[2 * d + 1][wd] >> sh) & 0xffffu;
+          o[d] = lo | (hi << 16);
+        }
+        lds[lds_slot<CH>(rbk * VE + rr, kb)] = o;
+      }
+    }
+  }
+};
+
+// VEC: 0 element loads (any alignment), 1 16-byte loads (aligned rows), 2 realigned 16-byte
+// loads (2-byte types, any element alignment)
+template <int DT, bool KMAJ, int VEC, int R, int BKE, int NT>
 struct PickLoader {
   typedef LoadNarrow<DT, KMAJ, R, BKE, NT> type;
 };
 template <int DT, int R, int BKE, int NT>
-struct PickLoader<DT, true, true, R, BKE, NT> {
+struct PickLoader<DT, true, 1, R, BKE, NT> {
   typedef LoadKMajorVec<DT, R, BKE, NT> type;
 };
 template <int DT, int R, int BKE, int NT>
-struct PickLoader<DT, false, true, R, BKE, NT> {
+struct PickLoader<DT, false, 1, R, BKE, NT> {
   typedef LoadMNMajorVec<DT, R, BKE, NT> type;
+};
+template <int DT, int R, int BKE, int NT>
+struct PickLoader<DT, true, 2, R, BKE, NT> {
+  typedef LoadKMajorMis<DT, R, BKE, NT> type;
+};
+template <int DT, int R, int BKE, int NT>
+struct PickLoader<DT, false, 2, R, BKE, NT> {
+  typedef LoadMNMajorMis<DT, R, BKE, NT> type;
 };
 
 // ------------------------------------------------------------------------------------------
@@ -580,7 +771,7 @@ __device__ __forceinline__ void epilogue(const KParams& p, AccT (&acc)[RM][RN], 
 // ------------------------------------------------------------------------------------------
 // The tiled kernel.
 // ------------------------------------------------------------------------------------------
-template <int DT, bool AK, bool BKM, bool VEC, int BM, int BN, int BKE, int WM, int WN, int MI>
+template <int DT, bool AK, bool BKM, int VEC, int BM, int BN, int BKE, int WM, int WN, int MI>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_tiled(const KParams p) {
   typedef Atom<DT, MI> At;
   typedef typename At::acc_t acc_t;
@@ -1345,16 +1536,18 @@ static hipError_t launch_skinny_dma(const KParams& p, hipStream_t s, dim3) {
 // ------------------------------------------------------------------------------------------
 // Launchers and the tile table.
 // ------------------------------------------------------------------------------------------
-template <int DT, bool AK, bool BKM, bool VEC, int BM, int BN, int BKE, int WM, int WN, int MI>
+template <int DT, bool AK, bool BKM, int VEC, int BM, int BN, int BKE, int WM, int WN, int MI>
 static hipError_t launch_tiled(const KParams& p, hipStream_t s, dim3 grid) {
   hipLaunchKernelGGL((gemm_tiled<DT, AK, BKM, VEC, BM, BN, BKE, WM, WN, MI>), grid,
                      dim3(WM * WN * 64), 0, s, p);
   return hipGetLastError();
 }
 
-#define HT_TILED(NAME, DT, AK, BKM, VEC, BM, BN, BKE, WM, WN, MI)                        \
-  {NAME, DT, AK, BKM, VEC, 0, BM, BN, BKE, WM * WN, 2, 2 * (BM + BN) * BKE * Ty<DT>::SZ, 64, 0, \
-   &launch_tiled<DT, AK, BKM, VEC, BM, BN, BKE, WM, WN, MI>}
+// VEC 2 (realigned 2-byte loads) entries need no 16-byte alignment, so they count as element-
+// aligned (vec 0) kernels that outrank the element-wise ones (rank 1)
+#define HT_TILED(NAME, DT, AK, BKM, VEC, BM, BN, BKE, WM, WN, MI)                                 \
+  {NAME, DT, AK, BKM, (VEC) == 1, 0, BM, BN, BKE, WM * WN, 2, 2 * (BM + BN) * BKE * Ty<DT>::SZ, 64, \
+   (VEC) == 2 ? 1 : 0, &launch_tiled<DT, AK, BKM, VEC, BM, BN, BKE, WM, WN, MI>, (VEC) == 2}
 
 #define HT_DMA(NAME, DT, BM, BN, WM, WN, MI, ST, OCC, CH, RANK)                                \
   {NAME, DT, 1, 1, 1, 0, BM, BN, CH * 16 / Ty<DT>::SZ, WM * WN, ST, ST * (BM + BN) * CH * 16, 1, \

@@ -125,9 +125,12 @@ def test_tile_table_choices(fake_gfx950):
     big = _info(desc(M=8192, N=8192, K=8192, a_strides=(8192, 1), b_strides=(1, 8192), d_strides=(8192, 1)))
     assert (big.bm, big.bn) == (256, 256) and big.name.startswith(b"bf16_ak_bk")
     assert big.grid == 32 * 32
-    # ragged fp16 with odd leading dimensions: only the element-wise loader can read it
+    # ragged fp16 with odd leading dimensions (2-byte aligned rows): the realigning loader
     rag = _info(H.make_desc(4099, 3071, 2053, "f16", (2053, 1), (3071, 1), (3071, 1), c_strides=(3071, 1)))
-    assert b"narrow" in rag.name and rag.config == rag.fallback
+    assert b"realign" in rag.name and rag.config == rag.fallback
+    # fp8 and fp32 have no realigning loader: element loads
+    rag8 = _info(H.make_desc(301, 257, 203, "e4m3", (203, 1), (1, 203), (257, 1)))
+    assert b"narrow" in rag8.name
     # M <= 16 with 16-byte-aligned K-major operands: the streaming (skinny) kernel, one
     # workgroup per 32 output columns
     sk = _info(H.make_desc(16, 16384, 8192, "e4m3", (8192, 1), (1, 8192), (16384, 1)))

@@ -130,7 +130,7 @@ def test_beta_zero_ignores_nan_c():
     assert error("f16", got, p.oracle_full()) <= TOL["f16"]
 
 
-def test_misaligned_pointer_uses_narrow_path_with_same_result():
+def test_misaligned_pointer_uses_fallback_path_with_same_result():
     base = Case(264, 264, 128, "bf16", seed=13)
     p0 = Prepared(base)
     g0, out0 = p0.run()
@@ -260,3 +260,28 @@ def test_split_k_automatic_on_few_tiles_and_long_k():
     err = error("bf16", got[rows, cols], p.oracle_elems(rows, cols))
     print(f"auto split {g.info.split_k}: {g.info.name.decode()} err={err:.3e}")
     assert err <= TOL["bf16"], err
+
+
+@pytest.mark.parametrize("layout", ["row-col", "row-row", "col-col", "col-row"])
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_realigned_loads_equal_element_loads(dtype, layout):
+    # odd leading dimensions and a base 2 bytes off a dword: the realigning 16-byte loader and the
+    # element-wise loader feed the same tile kernel, so the outputs agree bit for bit
+    a_order, b_order = layout.split("-")
+    names = [H.gemm_config_name(i) for i in range(H.gemm_num_configs())]
+    a = "ak" if a_order == "row" else "am"
+    b = "bk" if b_order == "col" else "bn"
+    outs = []
+    for kind in ("realign", "narrow"):
+        c = Case(M=259, N=197, K=301, dtype=dtype, a_order=a_order, b_order=b_order, seed=51,
+                 a_ld=261 if a_order == "col" else 303, b_ld=199 if b_order == "row" else 301,
+                 has_c=True, beta=0.5, bias=True, act="gelu", a_offset=1,
+                 force=names.index(f"{dtype}_{a}_{b}_128x128x64_w2x2_m32_{kind}"))
+        p = Prepared(c)
+        g, out = p.run()
+        assert g.info.name.decode().endswith(kind)
+        outs.append(out)
+        if kind == "realign":
+            got, _ = p.decode_out(out)
+            assert error(dtype, got, p.oracle_full()) <= TOL[dtype]
+    assert torch.equal(outs[0], outs[1])
