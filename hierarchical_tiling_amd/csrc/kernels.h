@@ -1115,7 +1115,7 @@ static hipError_t launch_dma(const KParams& p, hipStream_t s, dim3 grid) {
 // Summation order per output is the same as the two-stage DMA kernel's (k-tiles in order,
 // substeps in order), so both produce the same bits.
 // ------------------------------------------------------------------------------------------
-template <int DT, int WM, int WN, int MI>
+template <int DT, int WM, int WN, int MI, int NB>
 __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_ring(const KParams p) {
   typedef Atom<DT, MI> At;
   typedef typename At::acc_t acc_t;
@@ -1226,6 +1226,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_ring(const KParams p) {
     dma(OPB, 1, 4);
     wait_counts<2 * DU, true>();
     barrier_nofence();
+    if constexpr (NB == 1) dma(OPA, 2, 2);  // the third A slot is free from the start
     read_a(I0{}, lds, I0{});
     read_b(lds + 3 * SLOT, I0{});
     // Substep s of k-tile t, whose A unit sits in slot sa_i.
@@ -1239,7 +1240,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_ring(const KParams p) {
         // the first substep also carries the B reads of the rest of the k-tile
         interleave(std::integral_constant<int, RM * At::UNITS + (s == 0 ? (S - 1) * RN * At::UNITS : 0)>{},
                    std::integral_constant<int, RM * RN * At::PER_UNIT>{});
-        if constexpr (s + 1 == MID) {
+        if constexpr (s + 1 == MID && NB == 2) {
           // this wave's reads of B(t) are complete (lgkmcnt 0); after the barrier no wave
           // reads B(t), and B(t+2) takes its slot
           wait_counts<63, true>();
@@ -1248,14 +1249,22 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_ring(const KParams p) {
         }
       } else {
         mma_rows(std::integral_constant<int, buf>{}, s, I0{}, std::integral_constant<int, RM / 2>{});
-        // A(t+1) and B(t+1) have landed once at most A(t+2), B(t+2) are in flight
-        wait_counts<2 * DU, true>();
+        // A(t+1) and B(t+1) have landed once at most A(t+2), B(t+2) are in flight (one barrier
+        // per k-tile: once at most A(t+2), issued after B(t+1), is)
+        if constexpr (NB == 2) wait_counts<2 * DU, true>(); else wait_counts<DU, true>();
         barrier_nofence();
         smem_timer_read();
         // (after the last k-tile these read zero-filled slots; the values are never used)
         const int na = sa_i == 2 ? 0 : sa_i + 1;
         read_a(std::integral_constant<int, buf ^ 1>{}, lds + na * SLOT, I0{});
         read_b(lds + (3 + ((t + 1) & 1)) * SLOT, I0{});
+        if constexpr (NB == 1) {
+          // every wave is past k-tile t: B(t+2) and A(t+3) take the slots of B(t) and A(t).
+          // Issued after the reads above, so the compiler cannot move those reads across the
+          // loop's back edge (the DMA may alias them).
+          dma(OPB, t + 2, sb_i);
+          dma(OPA, t + 3, sa_i);
+        }
         mma_rows(std::integral_constant<int, buf>{}, s, std::integral_constant<int, RM / 2>{},
                  std::integral_constant<int, RM>{});
       }
@@ -1263,7 +1272,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_ring(const KParams p) {
     // First half of k-tile t: issue A(t+2) into the slot A(t-1) released, read the rest of the
     // k-tile's B fragments, substeps 0 .. MID-1 (ending with the barrier that releases B(t)).
     auto tile_front = [&](int t, int sa_i) {
-      dma(OPA, t + 2, sa_i == 0 ? 2 : sa_i - 1);
+      if constexpr (NB == 2) dma(OPA, t + 2, sa_i == 0 ? 2 : sa_i - 1);
       const u32x4* sb = lds + (3 + (t & 1)) * SLOT;
       static_for<S - 1>([&](auto s) { read_b(sb, std::integral_constant<int, s + 1>{}); });
       static_for<MID>([&](auto s) { substep(t, sa_i, s); });
@@ -1276,14 +1285,22 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_ring(const KParams p) {
     // prologue's and sink them to the loop head, right before the MFMAs that consume them, so
     // every k-tile would start with an exposed LDS round trip on all waves at once; nothing
     // can be moved across the barrier and DMA that end each half here.
-    tile_front(0, 0);
     int sa_i = 0;  // slot of A(t) in the A ring
-    for (int t = 0; t + 1 < nk; ++t) {
-      tile_back(t, sa_i);
-      sa_i = sa_i == 2 ? 0 : sa_i + 1;
-      tile_front(t + 1, sa_i);
+    if constexpr (NB == 2) {
+      tile_front(0, 0);
+      for (int t = 0; t + 1 < nk; ++t) {
+        tile_back(t, sa_i);
+        sa_i = sa_i == 2 ? 0 : sa_i + 1;
+        tile_front(t + 1, sa_i);
+      }
+      tile_back(nk - 1, sa_i);
+    } else {
+      for (int t = 0; t < nk; ++t) {
+        tile_front(t, sa_i);
+        tile_back(t, sa_i);
+        sa_i = sa_i == 2 ? 0 : sa_i + 1;
+      }
     }
-    tile_back(nk - 1, sa_i);
     wait_counts<0, true>();  // the zero-filled units issued past the end are still in flight
     barrier_nofence();
   }
@@ -1295,9 +1312,9 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_ring(const KParams p) {
   }
 }
 
-template <int DT, int WM, int WN, int MI>
+template <int DT, int WM, int WN, int MI, int NB>
 static hipError_t launch_ring(const KParams& p, hipStream_t s, dim3 grid) {
-  hipLaunchKernelGGL((gemm_ring<DT, WM, WN, MI>), grid, dim3(WM * WN * 64), 0, s, p);
+  hipLaunchKernelGGL((gemm_ring<DT, WM, WN, MI, NB>), grid, dim3(WM * WN * 64), 0, s, p);
   return hipGetLastError();
 }
 
@@ -1588,9 +1605,9 @@ static hipError_t launch_tiled(const KParams& p, hipStream_t s, dim3 grid) {
    RANK, &launch_dma<DT, BM, BN, WM, WN, MI, ST, OCC, CH>}
 
 // Split-ring entries: 256 x 256 tiles, 128-byte rows, 5 units of 32 KiB.
-#define HT_RING(NAME, DT, WM, WN, MI, RANK)                                                      \
+#define HT_RING(NAME, DT, WM, WN, MI, NB, RANK)                                                      \
   {NAME, DT, 1, 1, 1, 0, 256, 256, 128 / Ty<DT>::SZ, WM * WN, 5, 5 * 256 * 128, 64, RANK,         \
-   &launch_ring<DT, WM, WN, MI>}
+   &launch_ring<DT, WM, WN, MI, NB>}
 
 // Streaming skinny entries: bm = 16 rows, bn = 16*NBW columns, bk = one 128-byte block of K.
 #define HT_SKINNY_DMA(NAME, DT, WK, NBW, R, OCC)                                                  \

@@ -210,6 +210,8 @@ SPLIT_CASES = {
                          force="bf16_ak_bk_256x256x64_w2x4_m32_ring"),
     "bf16_ring16_s2": dict(M=300, N=264, K=64 * 5 + 40, dtype="bf16", split_k=2, act="gelu",
                            force="bf16_ak_bk_256x256x64_w2x4_m16_ring"),
+    "bf16_ring1_s3": dict(M=300, N=264, K=64 * 7 + 8, dtype="bf16", split_k=3, bias=True,
+                          force="bf16_ak_bk_256x256x64_w2x4_m16_ring1"),
     "e4m3_ring_s3": dict(M=264, N=328, K=128 * 5 + 32, dtype="e4m3", split_k=3,
                          scale_a=0.5, scale_b=0.25, force="e4m3_ak_bk_256x256x128_w2x4_m32_ring"),
     # element-wise loaders (column-major A, row-major B, odd leading dims)
