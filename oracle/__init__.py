@@ -28,7 +28,7 @@ _LIB_PATH = os.path.join(_HERE, "libhtoracle.so")
 
 # The oracle's own dtype and activation numbering (independent of the GPU library's header).
 DTYPES = {"f32": 0, "f16": 1, "bf16": 2, "e4m3": 3}
-ACTS = {"none": 0, "relu": 1, "gelu": 2}
+ACTS = {"none": 0, "relu": 1, "gelu": 2, "silu": 3}
 _STORAGE = {"f32": np.uint32, "f16": np.uint16, "bf16": np.uint16, "e4m3": np.uint8}
 
 
@@ -56,7 +56,7 @@ def _load():
         lib.oracle_decode.argtypes = [i32, vp, i64, vp]
         lib.oracle_encode_rne.argtypes = [i32, vp, i64, vp]
         common = [i64, i64, i64, i32, vp, i64, i64, i32, vp, i64, i64, i32, vp, i64, i64, i32, vp,
-                  dbl, dbl, dbl, dbl, i32]
+                  vp, vp, dbl, dbl, dbl, dbl, i32]
         lib.oracle_gemm.argtypes = common + [vp, i64, i64, i32]
         lib.oracle_gemm_elems.argtypes = common + [i64, vp, vp, vp, i32]
         for f in (lib.oracle_decode, lib.oracle_encode_rne, lib.oracle_gemm, lib.oracle_gemm_elems):
@@ -109,7 +109,18 @@ class Operand:
         self.strides = tuple(int(s) for s in strides)
 
 
-def _common_args(M, N, K, A, B, C, bias, alpha, beta, scale_a, scale_b, act):
+def _scale_vec(v, n, what):
+    """A float32 scale vector of length n, or None."""
+    if v is None:
+        return None
+    v = np.ascontiguousarray(v, dtype=np.float32)
+    if v.shape != (n,):
+        raise ValueError(f"{what} must have shape ({n},)")
+    return v
+
+
+def _common_args(M, N, K, A, B, C, bias, alpha, beta, scale_a, scale_b, act, row_scale=None,
+                 col_scale=None):
     lib = _load()
     c_type = DTYPES[C.dtype] if C is not None else 0
     c_str = C.strides if C is not None else (0, 0)
@@ -119,19 +130,23 @@ def _common_args(M, N, K, A, B, C, bias, alpha, beta, scale_a, scale_b, act):
             DTYPES[B.dtype], _ptr(B.storage), B.strides[0], B.strides[1],
             c_type, _ptr(C.storage) if C is not None else None, c_str[0], c_str[1],
             b_type, _ptr(bias.storage) if bias is not None else None,
+            _ptr(row_scale), _ptr(col_scale),
             float(alpha), float(beta), float(scale_a), float(scale_b), ACTS[act]]
     return lib, args
 
 
 def gemm(A: Operand, B: Operand, C: Operand | None = None, bias: Operand | None = None, *,
-         alpha=1.0, beta=0.0, scale_a=1.0, scale_b=1.0, act="none", threads=None) -> np.ndarray:
-    """The whole M x N result in float64 (unrounded), row-major."""
+         alpha=1.0, beta=0.0, scale_a=1.0, scale_b=1.0, act="none", row_scale=None,
+         col_scale=None, threads=None) -> np.ndarray:
+    """The whole M x N result in float64 (unrounded), row-major.  row_scale (M) and col_scale (N)
+    are float32 vectors that multiply row i / column j of alpha*sA*sB*(A@B)."""
     M, K = A.shape
     K2, N = B.shape
     if K != K2:
         raise ValueError("inner dimensions differ")
+    rs, cs = _scale_vec(row_scale, M, "row_scale"), _scale_vec(col_scale, N, "col_scale")
     out = np.empty((M, N), dtype=np.float64)
-    lib, args = _common_args(M, N, K, A, B, C, bias, alpha, beta, scale_a, scale_b, act)
+    lib, args = _common_args(M, N, K, A, B, C, bias, alpha, beta, scale_a, scale_b, act, rs, cs)
     rc = lib.oracle_gemm(*args, _ptr(out), N, 1, _threads(threads))
     if rc:
         raise ValueError(f"oracle_gemm failed ({rc})")
@@ -140,16 +155,17 @@ def gemm(A: Operand, B: Operand, C: Operand | None = None, bias: Operand | None 
 
 def gemm_elems(A: Operand, B: Operand, rows, cols, C: Operand | None = None,
                bias: Operand | None = None, *, alpha=1.0, beta=0.0, scale_a=1.0, scale_b=1.0,
-               act="none", threads=None) -> np.ndarray:
+               act="none", row_scale=None, col_scale=None, threads=None) -> np.ndarray:
     """Selected outputs D(rows[e], cols[e]) in float64."""
     M, K = A.shape
     K2, N = B.shape
     if K != K2:
         raise ValueError("inner dimensions differ")
+    rs, cs = _scale_vec(row_scale, M, "row_scale"), _scale_vec(col_scale, N, "col_scale")
     rows = np.ascontiguousarray(rows, dtype=np.int64)
     cols = np.ascontiguousarray(cols, dtype=np.int64)
     out = np.empty(rows.shape, dtype=np.float64)
-    lib, args = _common_args(M, N, K, A, B, C, bias, alpha, beta, scale_a, scale_b, act)
+    lib, args = _common_args(M, N, K, A, B, C, bias, alpha, beta, scale_a, scale_b, act, rs, cs)
     rc = lib.oracle_gemm_elems(*args, rows.size, _ptr(rows), _ptr(cols), _ptr(out),
                                _threads(threads))
     if rc:

@@ -16,6 +16,12 @@
  *    Part IV Stage 5 "The epilogue and fusion"); the bias is one value per output column n.
  *  - A narrow-type GEMM folds a per-tensor dequantisation scale into the epilogue ("CUTLASS",
  *    Part V "Data types and quantization"): y = alpha * sA * sB * s.
+ *  - A fused epilogue may also scale by a per-channel (per output column) dequantisation vector
+ *    and apply other activations ("CUTLASS", Part IV Stage 5 "The epilogue and fusion": the
+ *    epilogue visitor tree fuses bias, activation and a per-channel scale; "A10 - CuTe, CUTLASS &
+ *    CuTile", drill answer 8: bias plus a nonstandard activation plus a quantisation scale in one
+ *    kernel).  Here y = alpha * sA * sB * row_scale[i] * col_scale[j] * s before C and bias; the
+ *    per-row vector is the same broadcast along the other mode (per-token activation scales).
  *  - Inputs are compared on the same rounded inputs ("A10 - CuTe, CUTLASS & CuTile", section 6
  *    Pitfall 5 and drill answer 7): every element is decoded exactly from its stored bits to
  *    double by this file's own codecs; the result is left in double, unrounded.
@@ -23,6 +29,7 @@
  * Readings where the pages are silent:
  *  - beta == 0 means C is not read at all (it may be NULL and NaNs in it do not propagate).
  *  - GELU is the exact erf form 0.5*x*(1+erf(x/sqrt(2))), computed with the C library's erf.
+ *  - SiLU is x * sigmoid(x) = x / (1 + exp(-x)), computed with the C library's exp.
  *  - e4m3 is the OCP "fn" flavour: bias 7, no infinities, S.1111.111 is NaN, max 448
  *    (the FP8 formats paper listed in "CUTLASS", Part XI).
  *
@@ -36,7 +43,7 @@
 #include <string.h>
 
 enum { OR_F32 = 0, OR_F16 = 1, OR_BF16 = 2, OR_E4M3 = 3 };
-enum { OR_ACT_NONE = 0, OR_ACT_RELU = 1, OR_ACT_GELU = 2 };
+enum { OR_ACT_NONE = 0, OR_ACT_RELU = 1, OR_ACT_GELU = 2, OR_ACT_SILU = 3 };
 enum { OR_OK = 0, OR_EINVAL = 1, OR_ENOMEM = 2 };
 
 /* ------------------------------------------------------------------------------------------ */
@@ -204,6 +211,7 @@ typedef struct {
   int64_t M, N, K;
   int a_type, b_type, c_type, bias_type;
   const void *A, *B, *C, *bias;
+  const float *row_scale, *col_scale; /* NULL: not applied */
   int64_t a_sm, a_sk, b_sk, b_sn, c_sm, c_sn;
   double alpha, beta, scale_a, scale_b;
   int act;
@@ -213,6 +221,7 @@ static double activation(int act, double y) {
   switch (act) {
     case OR_ACT_RELU: return y > 0.0 ? y : (y == y ? 0.0 : y); /* max(0, y); NaN stays NaN */
     case OR_ACT_GELU: return 0.5 * y * (1.0 + erf(y / sqrt(2.0)));
+    case OR_ACT_SILU: return y / (1.0 + exp(-y));
     default: return y;
   }
 }
@@ -220,6 +229,8 @@ static double activation(int act, double y) {
 /* One output element from the definition; arow[k] = A(i,k), bcol[k] = B(k,j) already decoded. */
 static double finish(const problem* p, int64_t i, int64_t j, double s) {
   double y = p->alpha * p->scale_a * p->scale_b * s;
+  if (p->row_scale) y *= (double)p->row_scale[i];
+  if (p->col_scale) y *= (double)p->col_scale[j];
   if (p->beta != 0.0) y += p->beta * dec_at(p->c_type, p->C, i * p->c_sm + j * p->c_sn);
   if (p->bias) y += dec_at(p->bias_type, p->bias, j);
   return activation(p->act, y);
@@ -278,6 +289,7 @@ static int check_problem(const problem* p) {
   if ((p->M > 0 && p->K > 0 && !p->A) || (p->N > 0 && p->K > 0 && !p->B)) return OR_EINVAL;
   if (p->beta != 0.0 && (!p->C || !elem_size(p->c_type))) return OR_EINVAL;
   if (p->bias && !elem_size(p->bias_type)) return OR_EINVAL;
+  if (p->act < OR_ACT_NONE || p->act > OR_ACT_SILU) return OR_EINVAL;
   return OR_OK;
 }
 
@@ -301,9 +313,10 @@ static int run_threads(void* (*fn)(void*), void* jobs, size_t job_size, int n) {
 int oracle_gemm(int64_t M, int64_t N, int64_t K, int a_type, const void* A, int64_t a_sm,
                 int64_t a_sk, int b_type, const void* B, int64_t b_sk, int64_t b_sn, int c_type,
                 const void* C, int64_t c_sm, int64_t c_sn, int bias_type, const void* bias,
+                const float* row_scale, const float* col_scale,
                 double alpha, double beta, double scale_a, double scale_b, int act, double* out,
                 int64_t o_sm, int64_t o_sn, int nthreads) {
-  problem p = {M, N, K, a_type, b_type, c_type, bias_type, A, B, C, bias,
+  problem p = {M, N, K, a_type, b_type, c_type, bias_type, A, B, C, bias, row_scale, col_scale,
                a_sm, a_sk, b_sk, b_sn, c_sm, c_sn, alpha, beta, scale_a, scale_b, act};
   int rc = check_problem(&p);
   if (rc) return rc;
@@ -377,10 +390,11 @@ static void* elem_worker(void* arg) {
 int oracle_gemm_elems(int64_t M, int64_t N, int64_t K, int a_type, const void* A, int64_t a_sm,
                       int64_t a_sk, int b_type, const void* B, int64_t b_sk, int64_t b_sn,
                       int c_type, const void* C, int64_t c_sm, int64_t c_sn, int bias_type,
-                      const void* bias, double alpha, double beta, double scale_a, double scale_b,
+                      const void* bias, const float* row_scale, const float* col_scale,
+                      double alpha, double beta, double scale_a, double scale_b,
                       int act, int64_t count, const int64_t* rows, const int64_t* cols,
                       double* out, int nthreads) {
-  problem p = {M, N, K, a_type, b_type, c_type, bias_type, A, B, C, bias,
+  problem p = {M, N, K, a_type, b_type, c_type, bias_type, A, B, C, bias, row_scale, col_scale,
                a_sm, a_sk, b_sk, b_sn, c_sm, c_sn, alpha, beta, scale_a, scale_b, act};
   int rc = check_problem(&p);
   if (rc) return rc;

@@ -26,14 +26,19 @@ def exact_values(bits, dtype):
     return [Fraction(v) for v in oracle.decode(dtype, bits)]
 
 
-def exact_gemm(a, b, c, bias, M, N, K, alpha, beta, sa, sb):
-    """Exact rational D before activation (a, b, c row-major lists of Fractions)."""
+def exact_gemm(a, b, c, bias, M, N, K, alpha, beta, sa, sb, rs=None, cs=None):
+    """Exact rational D before activation (a, b, c row-major lists of Fractions; rs, cs optional
+    per-row / per-column scale lists)."""
     out = []
     for i in range(M):
         row = []
         for j in range(N):
             s = sum((a[i * K + k] * b[k * N + j] for k in range(K)), Fraction(0))
             y = Fraction(alpha) * Fraction(sa) * Fraction(sb) * s
+            if rs is not None:
+                y *= rs[i]
+            if cs is not None:
+                y *= cs[j]
             if beta != 0:
                 y += Fraction(beta) * c[i * N + j]
             if bias is not None:
@@ -73,6 +78,82 @@ def test_brute_force_matches_exact_rationals(seed):
                 mag = sum(a_abs[i * K + k] * b_abs[k * N + j] for k in range(K))
                 bound = (K + 4) * 2.0 ** -52 * float(mag * Fraction(alpha) * Fraction(sa) * Fraction(sb) + abs(w)) + 1e-300
                 assert abs(got[i, j] - float(w)) <= bound
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_scale_vectors_match_exact_rationals(seed):
+    # D = alpha*sA*sB*row_scale[i]*col_scale[j]*(A@B) + beta*C + bias, each scale an exact float32
+    rng = np.random.default_rng(50 + seed)
+    M, N, K = (int(x) for x in rng.integers(1, 7, 3))
+    dt = DT[seed % 4]
+    dist = "dyadic" if seed % 2 == 0 else "normal"
+    a_bits = inputs.quantize(inputs.draw(500 + seed, M * K, dist), dt)
+    b_bits = inputs.quantize(inputs.draw(600 + seed, K * N, dist), dt)
+    c_dt = "bf16" if dt == "e4m3" else dt
+    c_bits = inputs.quantize(inputs.draw(700 + seed, M * N, dist), c_dt)
+    bias_bits = inputs.quantize(inputs.draw(800 + seed, N, dist), c_dt)
+    if dist == "dyadic":   # powers of two: every product stays exact in double
+        rs = np.float32(2.0) ** rng.integers(-3, 4, M).astype(np.float32)
+        cs = np.float32(2.0) ** rng.integers(-3, 4, N).astype(np.float32)
+    else:
+        rs = rng.uniform(0.25, 2.0, M).astype(np.float32)
+        cs = rng.uniform(-2.0, 2.0, N).astype(np.float32)
+    A, _ = operand(a_bits, dt, M, K, "row")
+    B, _ = operand(b_bits, dt, K, N, ["col", "row"][seed % 2])
+    C, _ = operand(c_bits, c_dt, M, N, "row")
+    bias = oracle.Operand(bias_bits, c_dt, (1, N), (N, 1))
+    alpha, beta = 0.75, -1.5
+    got = oracle.gemm(A, B, C, bias, alpha=alpha, beta=beta, row_scale=rs, col_scale=cs)
+    ex_rs = [Fraction(float(v)) for v in rs]
+    ex_cs = [Fraction(float(v)) for v in cs]
+    want = exact_gemm(exact_values(a_bits, dt), exact_values(b_bits, dt), exact_values(c_bits, c_dt),
+                      exact_values(bias_bits, c_dt), M, N, K, alpha, beta, 1.0, 1.0, ex_rs, ex_cs)
+    a_abs = [abs(v) for v in exact_values(a_bits, dt)]
+    b_abs = [abs(v) for v in exact_values(b_bits, dt)]
+    for i in range(M):
+        for j in range(N):
+            w = want[i][j]
+            if dist == "dyadic":
+                assert Fraction(got[i, j]) == w
+            else:
+                mag = sum(a_abs[i * K + k] * b_abs[k * N + j] for k in range(K))
+                scale = abs(Fraction(alpha) * ex_rs[i] * ex_cs[j])
+                bound = (K + 6) * 2.0 ** -52 * float(mag * scale + abs(w)) + 1e-300
+                assert abs(got[i, j] - float(w)) <= bound
+
+
+def test_scale_vectors_are_row_and_column_broadcasts():
+    # with power-of-two scales the fused result equals diag(rs) @ D @ diag(cs) bit for bit
+    M, N, K = 9, 7, 13
+    A, _ = operand(inputs.quantize(inputs.draw(31, M * K), "bf16"), "bf16", M, K, "row")
+    B, _ = operand(inputs.quantize(inputs.draw(32, K * N), "bf16"), "bf16", K, N, "col")
+    rs = np.float32(2.0) ** np.arange(-4, M - 4, dtype=np.float32)
+    cs = np.float32(2.0) ** -np.arange(N, dtype=np.float32)
+    plain = oracle.gemm(A, B)
+    fused = oracle.gemm(A, B, row_scale=rs, col_scale=cs)
+    np.testing.assert_array_equal(fused, rs[:, None].astype(np.float64) * plain * cs[None, :])
+    only_c = oracle.gemm(A, B, col_scale=cs)
+    np.testing.assert_array_equal(only_c, plain * cs[None, :])
+    with pytest.raises(ValueError):
+        oracle.gemm(A, B, row_scale=rs[:-1])
+
+
+def test_silu_odd_part_and_tanh_form():
+    # SiLU(x) = x * sigmoid(x).  Since sigmoid(x) + sigmoid(-x) = 1, SiLU(x) - SiLU(-x) = x; and
+    # sigmoid(x) = (1 + tanh(x / 2)) / 2 gives a second closed form through the library tanh.
+    x = np.array([-30.0, -4.0, -1.0, -0.25, 0.0, 0.25, 1.0, 4.0, 30.0])
+    A, _ = operand(inputs.quantize(np.ones(1), "f32"), "f32", 1, 1, "row")
+    B, _ = operand(inputs.quantize(x, "f32"), "f32", 1, x.size, "row")
+    Bn, _ = operand(inputs.quantize(-x, "f32"), "f32", 1, x.size, "row")
+    silu = oracle.gemm(A, B, act="silu")[0]
+    sneg = oracle.gemm(A, Bn, act="silu")[0]
+    np.testing.assert_allclose(silu - sneg, x, rtol=0, atol=4e-15)
+    # (the tanh form cancels for very negative x, so its absolute error, not its relative one,
+    # stays near 1e-16 there)
+    tanh_form = np.array([v * (1.0 + math.tanh(v / 2.0)) / 2.0 for v in x])
+    np.testing.assert_allclose(silu, tanh_form, rtol=1e-14, atol=1e-14)
+    assert silu[4] == 0.0
+    assert silu[0] < 0 and abs(silu[0]) < 1e-11 and silu[-1] == pytest.approx(30.0, rel=1e-12)
 
 
 @pytest.mark.parametrize("dt", DT)
