@@ -178,8 +178,20 @@ int gemm_create(const gemm_desc* desc, gemm_t* out) {
   if (d.split_k < 0 || d.split_k > 64) return GEMM_ERR_INVALID_ARG;
   if (d.M < 0 || d.N < 0 || d.K < 0) return GEMM_ERR_INVALID_ARG;
   if (d.M > INT32_MAX / 2 || d.N > INT32_MAX / 2 || d.K > INT32_MAX / 2) return GEMM_ERR_INVALID_ARG;
-  if (d.act < GEMM_ACT_NONE || d.act > GEMM_ACT_GELU) return GEMM_ERR_INVALID_ARG;
+  if (d.act < GEMM_ACT_NONE || d.act > GEMM_ACT_SILU) return GEMM_ERR_INVALID_ARG;
   if ((d.has_c != 0 && d.has_c != 1) || (d.has_bias != 0 && d.has_bias != 1)) return GEMM_ERR_INVALID_ARG;
+  if ((d.has_row_scale != 0 && d.has_row_scale != 1) || (d.has_col_scale != 0 && d.has_col_scale != 1))
+    return GEMM_ERR_INVALID_ARG;
+  // batch (the problem shape's L mode): up to 65535 problems, one per grid z index
+  if (d.batch < 0 || d.batch > 65535) return GEMM_ERR_INVALID_ARG;
+  const int64_t L = d.batch > 1 ? d.batch : 1;
+  if (L > 1) {
+    if (d.a_stride_l < 0 || d.b_stride_l < 0 || d.c_stride_l < 0 || d.d_stride_l < 0)
+      return GEMM_ERR_LAYOUT;
+    // distinct problems must not write the same D; split-K is for single problems
+    if (d.d_stride_l == 0 && d.M > 0 && d.N > 0) return GEMM_ERR_INVALID_ARG;
+    if (d.split_k > 1) return GEMM_ERR_INVALID_ARG;
+  }
   if (!valid_type(d.a_type) || !valid_type(d.b_type) || !valid_type(d.d_type)) return GEMM_ERR_DTYPE_COMBO;
   if (d.a_type != d.b_type || d.d_type != out_dtype(d.a_type)) return GEMM_ERR_DTYPE_COMBO;
   if (d.has_c && d.c_type != d.d_type) return GEMM_ERR_DTYPE_COMBO;
@@ -197,9 +209,13 @@ int gemm_create(const gemm_desc* desc, gemm_t* out) {
   rc = check_arch();
   if (rc) return rc;
 
-  const bool va = vec_ok(h.a, d.M, d.K, d.a_type), vb = vec_ok(h.b, d.N, d.K, d.b_type);
+  // the 16-byte loaders need every problem's operand base 16-byte aligned
+  const int64_t isz = dtype_size(d.a_type);
+  const bool va = vec_ok(h.a, d.M, d.K, d.a_type) && (L == 1 || (d.a_stride_l * isz) % 16 == 0);
+  const bool vb = vec_ok(h.b, d.N, d.K, d.b_type) && (L == 1 || (d.b_stride_l * isz) % 16 == 0);
   const bool need_split = d.split_k > 1;
-  h.fallback = choose(h, va, vb, false, d.split_k);
+  const int split_req = L > 1 ? 1 : d.split_k;  // no automatic split of a batch
+  h.fallback = choose(h, va, vb, false, split_req);
   if (h.fallback < 0) return GEMM_ERR_NO_CONFIG;
   if (d.force_config >= 0) {
     if (d.force_config >= table_size() || !entry_fits(table()[d.force_config], h, va, vb))
@@ -207,12 +223,12 @@ int gemm_create(const gemm_desc* desc, gemm_t* out) {
     if (need_split && table()[d.force_config].max_split_k <= 1) return GEMM_ERR_NO_CONFIG;
     h.cfg = d.force_config;
   } else {
-    h.cfg = (va && vb) ? choose(h, va, vb, true, d.split_k) : -1;
+    h.cfg = (va && vb) ? choose(h, va, vb, true, split_req) : -1;
     if (h.cfg < 0) h.cfg = h.fallback;
   }
   h.group_m = 4;
-  plan_split(table()[h.cfg], d, d.split_k, &h.split_cfg, &h.kps_cfg);
-  plan_split(table()[h.fallback], d, d.split_k, &h.split_fb, &h.kps_fb);
+  plan_split(table()[h.cfg], d, split_req, &h.split_cfg, &h.kps_cfg);
+  plan_split(table()[h.fallback], d, split_req, &h.split_fb, &h.kps_fb);
 
   gemm_handle_s* p = new (std::nothrow) gemm_handle_s(h);
   if (!p) return GEMM_ERR_INVALID_ARG;
@@ -243,21 +259,29 @@ int gemm_get_info(gemm_t h, gemm_info* info) {
   info->stages = e.stages;
   info->lds_bytes = e.lds_bytes;
   info->split_k = h->split_cfg;
-  info->grid = cdiv(h->d.M, e.bm) * cdiv(h->d.N, e.bn) * h->split_cfg;
+  info->grid = cdiv(h->d.M, e.bm) * cdiv(h->d.N, e.bn) * h->split_cfg *
+               (h->d.batch > 1 ? h->d.batch : 1);
   std::strncpy(info->name, e.name, sizeof(info->name) - 1);
   return GEMM_OK;
 }
 
-int gemm_run(gemm_t h, const void* A, const void* B, const void* C, void* D, const void* bias,
-             float alpha, float beta, float scale_a, float scale_b, void* workspace,
-             void* stream) {
-  if (!h || h->magic != kMagic) return GEMM_ERR_BAD_HANDLE;
+}  // extern "C"
+
+namespace {
+
+int run_impl(gemm_t h, const void* A, const void* B, const void* C, void* D, const void* bias,
+             const float* row_scale, const float* col_scale, float alpha, float beta,
+             float scale_a, float scale_b, void* workspace, void* stream) {
   const gemm_desc& d = h->d;
   const bool read_c = d.has_c && beta != 0.0f;
   if (!d.has_c && beta != 0.0f) return GEMM_ERR_INVALID_ARG;
+  if ((d.has_row_scale != 0) != (row_scale != nullptr) || (d.has_col_scale != 0) != (col_scale != nullptr))
+    return GEMM_ERR_INVALID_ARG;
   if (d.M == 0 || d.N == 0) return GEMM_OK;
   if (!D || (d.K > 0 && (!A || !B)) || (read_c && !C) || (d.has_bias && !bias))
     return GEMM_ERR_INVALID_ARG;
+  if ((row_scale && !aligned(row_scale, 4)) || (col_scale && !aligned(col_scale, 4)))
+    return GEMM_ERR_MISALIGNED;
   const size_t in_sz = dtype_size(d.a_type), out_sz = dtype_size(d.d_type);
   if (!aligned(A, in_sz) || !aligned(B, in_sz) || !aligned(D, out_sz) ||
       (read_c && !aligned(C, out_sz)) || (d.has_bias && !aligned(bias, out_sz)))
@@ -297,11 +321,42 @@ int gemm_run(gemm_t h, const void* A, const void* B, const void* C, void* D, con
   p.split_k = split;
   p.k_per_split = (int)kps;
   p.workspace = split > 1 ? static_cast<float*>(workspace) : nullptr;
+  p.row_scale = row_scale;
+  p.col_scale = col_scale;
+  p.has_row_scale = row_scale ? 1 : 0;
+  p.has_col_scale = col_scale ? 1 : 0;
+  p.batch = d.batch > 1 ? (int)d.batch : 1;
+  p.a_bstride = d.a_stride_l * (int64_t)in_sz;
+  p.b_bstride = d.b_stride_l * (int64_t)in_sz;
+  p.c_bstride = d.c_stride_l * (int64_t)out_sz;
+  p.d_bstride = d.d_stride_l * (int64_t)out_sz;
   const int64_t grid = int64_t(p.tiles_m) * p.tiles_n;
   if (grid <= 0 || grid > INT32_MAX) return GEMM_ERR_INVALID_ARG;
-  hipError_t err = e.launch(p, (hipStream_t)stream, dim3((unsigned)grid, (unsigned)split));
+  hipError_t err = e.launch(p, (hipStream_t)stream,
+                            dim3((unsigned)grid, (unsigned)split, (unsigned)p.batch));
   if (err == hipSuccess && split > 1) err = launch_splitk_reduce(p, d.d_type, (hipStream_t)stream);
   return err == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gemm_run(gemm_t h, const void* A, const void* B, const void* C, void* D, const void* bias,
+             float alpha, float beta, float scale_a, float scale_b, void* workspace,
+             void* stream) {
+  if (!h || h->magic != kMagic) return GEMM_ERR_BAD_HANDLE;
+  // a handle with scale vectors needs gemm_run_ex to receive them
+  if (h->d.has_row_scale || h->d.has_col_scale) return GEMM_ERR_INVALID_ARG;
+  return run_impl(h, A, B, C, D, bias, nullptr, nullptr, alpha, beta, scale_a, scale_b,
+                  workspace, stream);
+}
+
+int gemm_run_ex(gemm_t h, const gemm_args* a, void* stream) {
+  if (!h || h->magic != kMagic) return GEMM_ERR_BAD_HANDLE;
+  if (!a) return GEMM_ERR_INVALID_ARG;
+  return run_impl(h, a->A, a->B, a->C, a->D, a->bias, a->row_scale, a->col_scale, a->alpha,
+                  a->beta, a->scale_a, a->scale_b, a->workspace, stream);
 }
 
 int gemm_destroy(gemm_t h) {

@@ -26,6 +26,11 @@ struct KParams {
   int split_k;        // workgroups per output tile along K (1: none)
   int k_per_split;    // K elements per split (a multiple of the tile's K step)
   float* workspace;   // fp32 partials when split_k > 1
+  const float* row_scale;  // read only when has_row_scale != 0: M values
+  const float* col_scale;  // read only when has_col_scale != 0: N values
+  int has_row_scale, has_col_scale;
+  int batch;               // problems per launch (gridDim.z); 1: one
+  int64_t a_bstride, b_bstride, c_bstride, d_bstride;  // bytes between consecutive problems
 };
 
 typedef hipError_t (*launch_fn)(const KParams&, hipStream_t, dim3 grid);

@@ -231,10 +231,47 @@ __device__ __forceinline__ float gelu(float x) {
   return x * (x >= 0.f ? 1.0f - q : q);
 }
 
+// SiLU(x) = x * sigmoid(x) = x / (1 + e^-x), with the hardware base-2 exponential and reciprocal
+// (each within 1 ulp).  For x below about -88, e^-x overflows to infinity and the result is -0,
+// where the exact value is below 1e-36 in magnitude.
+__device__ __forceinline__ float silu(float x) {
+  return x * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(x * -1.4426950408889634f));
+}
+
 __device__ __forceinline__ float activate(int act, float v) {
   if (act == 1) return relu(v);
   if (act == 2) return gelu(v);
+  if (act == 3) return silu(v);
   return v;
+}
+
+// The problem of a batched launch that this workgroup computes ("CUTLASS, CuTe, and CUDA Tile",
+// "Assembling a CUTLASS kernel": the problem shape's fourth mode L is a batch of independent
+// problems): problem blockIdx.z moves each operand base by its byte stride; everything else
+// (shape, strides, alpha, beta, bias and the scale vectors) is shared.
+__device__ __forceinline__ KParams batch_view(const KParams& p) {
+  KParams q = p;
+  if (p.batch > 1) {
+    const int64_t z = blockIdx.z;
+    q.A = (const char*)p.A + z * p.a_bstride;
+    q.B = (const char*)p.B + z * p.b_bstride;
+    if (p.has_c) q.C = (const char*)p.C + z * p.c_bstride;
+    q.D = (char*)p.D + z * p.d_bstride;
+  }
+  return q;
+}
+
+// Epilogue of one output element (row, col) from its fp32 sum, for the kernels that finish
+// element by element: y = act((alpha * row_scale[row] * col_scale[col] * sum + beta * C) + bias).
+template <int ODT>
+__device__ __forceinline__ float finish_elem(const KParams& p, int64_t row, int64_t col, float sum) {
+  typedef Out<ODT> O;
+  float v = p.alpha * sum;
+  if (p.has_row_scale) v *= p.row_scale[row];
+  if (p.has_col_scale) v *= p.col_scale[col];
+  if (p.has_c) v += p.beta * O::load(p.C, row * p.c_sm + col * p.c_sn);
+  if (p.has_bias) v += O::load(p.bias, col);
+  return activate(p.act, v);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -276,17 +313,15 @@ __device__ __forceinline__ void store_partial(const KParams& p, const AccT (&acc
 }
 // D = act(alpha * sum_s W[s] + beta * C + bias) elementwise, the planes added in order s = 0, 1, ...
 template <int ODT>
-__global__ __launch_bounds__(256) void gemm_splitk_reduce(const KParams p) {
+__global__ __launch_bounds__(256) void gemm_splitk_reduce(const KParams p_) {
+  const KParams p = batch_view(p_);
   typedef Out<ODT> O;
   const int64_t MN = p.M * p.N;
   for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < MN; e += (int64_t)gridDim.x * 256) {
     const int64_t row = e / p.N, col = e - row * p.N;
     float sum = 0.f;
     for (int s = 0; s < p.split_k; ++s) sum += p.workspace[s * MN + e];
-    float v = p.alpha * sum;
-    if (p.has_c) v += p.beta * O::load(p.C, row * p.c_sm + col * p.c_sn);
-    if (p.has_bias) v += O::load(p.bias, col);
-    O::store(p.D, row * p.d_sm + col * p.d_sn, activate(p.act, v));
+    O::store(p.D, row * p.d_sm + col * p.d_sn, finish_elem<ODT>(p, row, col, sum));
   }
 }
 
@@ -699,6 +734,7 @@ __device__ __forceinline__ void epilogue(const KParams& p, AccT (&acc)[RM][RN], 
   constexpr int OSZ = (int)sizeof(OT);
   constexpr bool REPACK = (size_t)BM * BN * OSZ <= LDS_BYTES;
   const bool has_c = p.has_c != 0, has_bias = p.has_bias != 0;
+  const bool has_rs = p.has_row_scale != 0, has_cs = p.has_col_scale != 0;
   const int act = p.act;
   const float alpha = p.alpha, beta = p.beta;
   OT* tile = reinterpret_cast<OT*>(lds);  // BM x BN, row-major (REPACK only)
@@ -707,16 +743,24 @@ __device__ __forceinline__ void epilogue(const KParams& p, AccT (&acc)[RM][RN], 
   // are live in VGPRs; within a block each stage is one straight-line pass entered on a uniform
   // condition, so the common case (no C) carries no per-element branches:
   // y = act((alpha * acc + beta * C) + bias[n]).
-  float bias_v[RN];
+  float bias_v[RN], cs_v[RN];
   static_for<RN>([&](auto j) {
     const int64_t col = n0 + wn * WTN + j * MI + (lane % MI);
     bias_v[j] = has_bias && col < p.N ? O::load(p.bias, col) : 0.f;
+    cs_v[j] = has_cs && col < p.N ? p.col_scale[col] : 1.f;
   });
   static_for<RM>([&](auto i) {
     auto each = [&](auto&& f) {
       static_for<RN>([&](auto j) { static_for<At::NACC>([&](auto r) { f(j, r); }); });
     };
     if (alpha != 1.f) each([&](auto j, auto r) { acc[i][j][(int)r] *= alpha; });  // x1 is exact
+    if (has_rs) {
+      each([&](auto j, auto r) {
+        const int64_t row = m0 + wm * WTM + i * MI + acc_row<MI>(lane, r);
+        acc[i][j][(int)r] *= row < p.M ? p.row_scale[row] : 1.f;
+      });
+    }
+    if (has_cs) each([&](auto j, auto r) { acc[i][j][(int)r] *= cs_v[j]; });
     if (has_c) {
       each([&](auto j, auto r) {
         const int64_t col = n0 + wn * WTN + j * MI + (lane % MI);
@@ -727,6 +771,7 @@ __device__ __forceinline__ void epilogue(const KParams& p, AccT (&acc)[RM][RN], 
     if (has_bias) each([&](auto j, auto r) { acc[i][j][(int)r] += bias_v[j]; });
     if (act == 2) each([&](auto j, auto r) { acc[i][j][(int)r] = gelu(acc[i][j][(int)r]); });
     else if (act == 1) each([&](auto j, auto r) { acc[i][j][(int)r] = relu(acc[i][j][(int)r]); });
+    else if (act == 3) each([&](auto j, auto r) { acc[i][j][(int)r] = silu(acc[i][j][(int)r]); });
     static_for<RN>([&](auto j) {
       const int lc = wn * WTN + j * MI + (lane % MI);
       const int64_t col = n0 + lc;
@@ -774,7 +819,8 @@ __device__ __forceinline__ void epilogue(const KParams& p, AccT (&acc)[RM][RN], 
 // The tiled kernel.
 // ------------------------------------------------------------------------------------------
 template <int DT, bool AK, bool BKM, int VEC, int BM, int BN, int BKE, int WM, int WN, int MI>
-__global__ __launch_bounds__(WM * WN * 64) void gemm_tiled(const KParams p) {
+__global__ __launch_bounds__(WM * WN * 64) void gemm_tiled(const KParams p_) {
+  const KParams p = batch_view(p_);
   typedef Atom<DT, MI> At;
   typedef typename At::acc_t acc_t;
   constexpr int NT = WM * WN * 64;
@@ -948,7 +994,8 @@ __device__ __forceinline__ const char* uniform_ptr(const char* p) {
 }
 
 template <int DT, int BM, int BN, int WM, int WN, int MI, int STAGES, int OCC, int CH>
-__global__ __launch_bounds__(WM * WN * 64, OCC) void gemm_dma(const KParams p) {
+__global__ __launch_bounds__(WM * WN * 64, OCC) void gemm_dma(const KParams p_) {
+  const KParams p = batch_view(p_);
   typedef Atom<DT, MI> At;
   typedef typename At::acc_t acc_t;
   constexpr int NW = WM * WN, NT = NW * 64;
@@ -1116,7 +1163,8 @@ static hipError_t launch_dma(const KParams& p, hipStream_t s, dim3 grid) {
 // substeps in order), so both produce the same bits.
 // ------------------------------------------------------------------------------------------
 template <int DT, int WM, int WN, int MI, int NB>
-__global__ __launch_bounds__(WM * WN * 64, 1) void gemm_ring(const KParams p) {
+__global__ __launch_bounds__(WM * WN * 64, 1) void gemm_ring(const KParams p_) {
+  const KParams p = batch_view(p_);
   typedef Atom<DT, MI> At;
   typedef typename At::acc_t acc_t;
   constexpr int BM = 256, BN = 256, CH = 8;   // 128-byte LDS rows
@@ -1333,7 +1381,8 @@ static hipError_t launch_ring(const KParams& p, hipStream_t s, dim3 grid) {
 // 16x16x32 bf16/fp16); lane l supplies row (or column) l % 16 and the k-run of lane group l / 16.
 // ------------------------------------------------------------------------------------------
 template <int DT, int WK, int WN, int NBW, int U, int OCC>
-__global__ __launch_bounds__(WK * WN * 64, OCC) void gemm_skinny(const KParams p) {
+__global__ __launch_bounds__(WK * WN * 64, OCC) void gemm_skinny(const KParams p_) {
+  const KParams p = batch_view(p_);
   typedef Atom<DT, 16> At;
   typedef typename At::acc_t acc_t;  // 4 floats: rows 4*(l/16)+r, column l%16
   constexpr int NT = WK * WN * 64;
@@ -1428,18 +1477,14 @@ __global__ __launch_bounds__(WK * WN * 64, OCC) void gemm_skinny(const KParams p
     float sum = 0.f;
 #pragma unroll
     for (int w = 0; w < WK; ++w) sum += part[w][c / 16][row][c % 16];
-    float v = p.alpha * sum;
-    if (p.has_c) v += p.beta * O::load(p.C, row * p.c_sm + col * p.c_sn);
-    if (p.has_bias) v += O::load(p.bias, col);
-    v = activate(p.act, v);
-    O::store(p.D, row * p.d_sm + col * p.d_sn, v);
+    O::store(p.D, row * p.d_sm + col * p.d_sn, finish_elem<ODT>(p, row, col, sum));
   }
 }
 
 template <int DT, int WK, int WN, int NBW, int U, int OCC>
 static hipError_t launch_skinny(const KParams& p, hipStream_t s, dim3) {
   constexpr int BN = WN * NBW * 16;
-  const dim3 grid((unsigned)((p.N + BN - 1) / BN));
+  const dim3 grid((unsigned)((p.N + BN - 1) / BN), 1, (unsigned)p.batch);
   hipLaunchKernelGGL((gemm_skinny<DT, WK, WN, NBW, U, OCC>), grid, dim3(WK * WN * 64), 0, s, p);
   return hipGetLastError();
 }
@@ -1461,7 +1506,8 @@ static hipError_t launch_skinny(const KParams& p, hipStream_t s, dim3) {
 // LDS at the end.
 // ------------------------------------------------------------------------------------------
 template <int DT, int WK, int NBW, int R, int OCC>
-__global__ __launch_bounds__(WK * 64, OCC) void gemm_skinny_dma(const KParams p) {
+__global__ __launch_bounds__(WK * 64, OCC) void gemm_skinny_dma(const KParams p_) {
+  const KParams p = batch_view(p_);
   typedef Atom<DT, 16> At;
   typedef typename At::acc_t acc_t;               // 4 floats: rows 4*(l/16)+r, column l%16
   constexpr int SZ = Ty<DT>::SZ;
@@ -1568,18 +1614,14 @@ __global__ __launch_bounds__(WK * 64, OCC) void gemm_skinny_dma(const KParams p)
     float sum = 0.f;
 #pragma unroll
     for (int w = 0; w < WK; ++w) sum += part[((w * NBW + c / 16) * 16 + row) * 16 + c % 16];
-    float v = p.alpha * sum;
-    if (p.has_c) v += p.beta * O::load(p.C, row * p.c_sm + col * p.c_sn);
-    if (p.has_bias) v += O::load(p.bias, col);
-    v = activate(p.act, v);
-    O::store(p.D, row * p.d_sm + col * p.d_sn, v);
+    O::store(p.D, row * p.d_sm + col * p.d_sn, finish_elem<ODT>(p, row, col, sum));
   }
 }
 
 template <int DT, int WK, int NBW, int R, int OCC>
 static hipError_t launch_skinny_dma(const KParams& p, hipStream_t s, dim3) {
   constexpr int BN = NBW * 16;
-  const dim3 grid((unsigned)((p.N + BN - 1) / BN));
+  const dim3 grid((unsigned)((p.N + BN - 1) / BN), 1, (unsigned)p.batch);
   hipLaunchKernelGGL((gemm_skinny_dma<DT, WK, NBW, R, OCC>), grid, dim3(WK * 64), 0, s, p);
   return hipGetLastError();
 }

@@ -12,12 +12,13 @@ LIB_PATH = os.path.join(_PKG, "libhtgemm.so")
 
 # status codes (htgemm.h)
 GEMM_OK = 0
+GEMM_ERR_INVALID_ARG, GEMM_ERR_LAYOUT, GEMM_ERR_MISALIGNED, GEMM_ERR_NO_CONFIG = 1, 3, 4, 8
 STATUS_NAMES = {0: "GEMM_OK", 1: "GEMM_ERR_INVALID_ARG", 2: "GEMM_ERR_DTYPE_COMBO",
                 3: "GEMM_ERR_LAYOUT", 4: "GEMM_ERR_MISALIGNED", 5: "GEMM_ERR_ARCH",
                 6: "GEMM_ERR_LAUNCH", 7: "GEMM_ERR_BAD_HANDLE", 8: "GEMM_ERR_NO_CONFIG",
                 9: "GEMM_ERR_HIP"}
 DTYPES = {"f32": 0, "f16": 1, "bf16": 2, "e4m3": 3}
-ACTS = {"none": 0, "relu": 1, "gelu": 2}
+ACTS = {"none": 0, "relu": 1, "gelu": 2, "silu": 3}
 # layout status codes (htlayout.h)
 HT_STATUS_NAMES = {0: "HT_OK", 1: "HT_ERR_PARSE", 2: "HT_ERR_RANGE", 3: "HT_ERR_NOT_COMPOSABLE",
                    4: "HT_ERR_CAPACITY", 5: "HT_ERR_NO_COMPLEMENT"}
@@ -45,7 +46,20 @@ class gemm_desc(ctypes.Structure):
                 ("b_stride_k", ctypes.c_int64), ("b_stride_n", ctypes.c_int64),
                 ("c_stride_m", ctypes.c_int64), ("c_stride_n", ctypes.c_int64),
                 ("d_stride_m", ctypes.c_int64), ("d_stride_n", ctypes.c_int64),
-                ("force_config", ctypes.c_int32), ("split_k", ctypes.c_int32)]
+                ("force_config", ctypes.c_int32), ("split_k", ctypes.c_int32),
+                ("has_row_scale", ctypes.c_int32), ("has_col_scale", ctypes.c_int32),
+                ("batch", ctypes.c_int64),
+                ("a_stride_l", ctypes.c_int64), ("b_stride_l", ctypes.c_int64),
+                ("c_stride_l", ctypes.c_int64), ("d_stride_l", ctypes.c_int64)]
+
+
+class gemm_args(ctypes.Structure):
+    _fields_ = [("A", ctypes.c_void_p), ("B", ctypes.c_void_p), ("C", ctypes.c_void_p),
+                ("D", ctypes.c_void_p), ("bias", ctypes.c_void_p),
+                ("row_scale", ctypes.c_void_p), ("col_scale", ctypes.c_void_p),
+                ("alpha", ctypes.c_float), ("beta", ctypes.c_float),
+                ("scale_a", ctypes.c_float), ("scale_b", ctypes.c_float),
+                ("workspace", ctypes.c_void_p)]
 
 
 class gemm_info(ctypes.Structure):
@@ -81,6 +95,7 @@ def lib():
         "gemm_workspace_size": ([vp, ctypes.POINTER(sz)], i32),
         "gemm_run": ([vp, vp, vp, vp, vp, vp, ctypes.c_float, ctypes.c_float, ctypes.c_float,
                       ctypes.c_float, vp, vp], i32),
+        "gemm_run_ex": ([vp, ctypes.POINTER(gemm_args), vp], i32),
         "gemm_destroy": ([vp], i32),
         "gemm_status_string": ([i32], cp),
         "gemm_get_info": ([vp, ctypes.POINTER(gemm_info)], i32),
@@ -106,7 +121,8 @@ def lib():
     return L
 
 
-EXPORTED = ["gemm_create", "gemm_workspace_size", "gemm_run", "gemm_destroy", "gemm_status_string",
+EXPORTED = ["gemm_create", "gemm_workspace_size", "gemm_run", "gemm_run_ex", "gemm_destroy",
+            "gemm_status_string",
             "gemm_get_info", "gemm_num_configs", "gemm_config_name", "ht_layout_eval",
             "ht_layout_size", "ht_layout_table", "ht_layout_coalesce", "ht_layout_compose",
             "ht_layout_complement", "ht_layout_logical_divide", "ht_layout_zipped_divide",
@@ -139,6 +155,13 @@ def gemm_run(h, A, B, C, D, bias, alpha, beta, scale_a=1.0, scale_b=1.0, workspa
            "gemm_run")
 
 
+def gemm_run_ex(h, A, B, C, D, bias, row_scale, col_scale, alpha, beta, scale_a=1.0, scale_b=1.0,
+                workspace=None, stream=None):
+    """gemm_run with the scale vectors (device addresses or None), through the argument struct."""
+    a = gemm_args(A, B, C, D, bias, row_scale, col_scale, alpha, beta, scale_a, scale_b, workspace)
+    _check(lib().gemm_run_ex(h, ctypes.byref(a), stream), "gemm_run_ex")
+
+
 def gemm_destroy(h):
     _check(lib().gemm_destroy(h), "gemm_destroy")
 
@@ -164,8 +187,10 @@ def gemm_config_name(i: int) -> str:
 
 
 def make_desc(M, N, K, dtype, a_strides, b_strides, d_strides, c_strides=None, has_bias=False,
-              act="none", force_config=-1, split_k=0) -> gemm_desc:
-    """a_strides = (stride_m, stride_k); b_strides = (stride_k, stride_n); c/d = (m, n)."""
+              act="none", force_config=-1, split_k=0, row_scale=False, col_scale=False, batch=1,
+              batch_strides=(0, 0, 0, 0)) -> gemm_desc:
+    """a_strides = (stride_m, stride_k); b_strides = (stride_k, stride_n); c/d = (m, n);
+    batch_strides = element offsets between consecutive problems of A, B, C, D."""
     out_t = "bf16" if dtype == "e4m3" else dtype
     d = gemm_desc()
     d.M, d.N, d.K = M, N, K
@@ -180,6 +205,10 @@ def make_desc(M, N, K, dtype, a_strides, b_strides, d_strides, c_strides=None, h
     d.d_stride_m, d.d_stride_n = d_strides
     d.force_config = force_config
     d.split_k = split_k
+    d.has_row_scale = 1 if row_scale else 0
+    d.has_col_scale = 1 if col_scale else 0
+    d.batch = batch
+    d.a_stride_l, d.b_stride_l, d.c_stride_l, d.d_stride_l = batch_strides
     return d
 
 
@@ -199,9 +228,15 @@ class Gemm:
         return gemm_workspace_size(self.handle)
 
     def run(self, A, B, C, D, bias=None, alpha=1.0, beta=0.0, scale_a=1.0, scale_b=1.0,
-            stream=None, workspace=None):
-        gemm_run(self.handle, _addr(A), _addr(B), _addr(C), _addr(D), _addr(bias), alpha, beta,
-                 scale_a, scale_b, _addr(workspace), _stream(stream))
+            stream=None, workspace=None, row_scale=None, col_scale=None):
+        """gemm_run, or gemm_run_ex when a scale vector is given."""
+        if row_scale is None and col_scale is None:
+            gemm_run(self.handle, _addr(A), _addr(B), _addr(C), _addr(D), _addr(bias), alpha,
+                     beta, scale_a, scale_b, _addr(workspace), _stream(stream))
+        else:
+            gemm_run_ex(self.handle, _addr(A), _addr(B), _addr(C), _addr(D), _addr(bias),
+                        _addr(row_scale), _addr(col_scale), alpha, beta, scale_a, scale_b,
+                        _addr(workspace), _stream(stream))
 
     def close(self):
         if self.handle:

@@ -3,17 +3,25 @@
  *
  * Operation (all entry points below compute or describe this one operation):
  *
- *     D = act( alpha * scale_a * scale_b * (A @ B)  +  beta * C  +  bias )
+ *     D = act( alpha * scale_a * scale_b * row_scale[m] * col_scale[n] * (A @ B)
+ *              +  beta * C  +  bias )
  *
  * with A an M x K matrix, B a K x N matrix, C and D M x N matrices and bias a length-N vector
- * added to every row.  This is the GEMM the reference pages are built around ("CUTLASS",
+ * added to every row; row_scale (length M) and col_scale (length N) are optional fp32 vectors
+ * (1 when absent), and a batch of L problems of one shape may run in one call (D_l from A_l,
+ * B_l, C_l, sharing bias and the scale vectors).  This is the GEMM the reference pages are built around ("CUTLASS",
  * stanleyjacob.dev, Part I "The mental model": D = alpha * (A @ B) + beta * C; Part II "Using
  * it": the problem shape, a {pointer, leading dimension} per operand and {alpha, beta}, checked
  * against a success status).  The epilogue order -- alpha/beta, then bias, then activation --
  * follows the same page's Part I diagram and Part IV Stage 5 ("The epilogue and fusion"); the
  * per-tensor dequantisation scales of a narrow-type GEMM are folded into the epilogue as the
- * page's Part V "Data types and quantization" describes.  Products accumulate in fp32 whatever
- * the operand type.
+ * page's Part V "Data types and quantization" describes.  The per-column scale vector is the
+ * per-channel dequantisation scale an epilogue visitor tree fuses (Part IV Stage 5); the per-row
+ * vector is the same broadcast along M (per-token activation scales), and SiLU is a further
+ * activation of the kind the "A10 - CuTe, CUTLASS & CuTile" page's drill answer 8 names (a
+ * custom fused epilogue of bias, a nonstandard activation and a quantisation scale).  The batch
+ * is the fourth mode L of the problem shape [M, N, K, L] ("CUTLASS, CuTe, and CUDA Tile",
+ * "Assembling a CUTLASS kernel").  Products accumulate in fp32 whatever the operand type.
  *
  * Handle life cycle ("CUTLASS", Part IV Stage 1: get_workspace_size, can_implement, initialize,
  * run; and "CUTLASS, CuTe, and CUDA Tile", section "Assembling a CUTLASS kernel": a stateful,
@@ -23,9 +31,11 @@
  *   gemm_workspace_size reports the device scratch the caller must pass to gemm_run (non-zero
  *                       only for a problem split along K).
  *   gemm_run            enqueues the kernel on the caller's HIP stream; asynchronous.
+ *   gemm_run_ex         the same with the arguments in a struct, including the scale vectors.
  *   gemm_destroy        frees the handle.
  *
- * Ownership: the caller owns every device buffer (A, B, C, D, bias, workspace) and the stream.
+ * Ownership: the caller owns every device buffer (A, B, C, D, bias, row_scale, col_scale,
+ * workspace) and the stream.
  * A handle holds host memory only and is immutable after gemm_create, so one handle may be run
  * concurrently on several streams.  Nothing throws across this interface; every function returns
  * a status code (GEMM_OK == 0) that gemm_status_string() describes.
@@ -43,6 +53,10 @@
  *     the output rounding), not the tanh approximation.
  *   - fp8 is OCP E4M3 ("fn": bias 7, max 448, no infinities); outputs round to nearest even.
  *   - M == 0 or N == 0 is a valid empty problem; K == 0 gives D = act(beta*C + bias).
+ *   - SiLU is x * sigmoid(x) = x / (1 + exp(-x)), evaluated with the hardware exponential and
+ *     reciprocal (each within 1 ulp).
+ *   - The scale vectors multiply the product before beta*C and bias are added, in the order
+ *     ((alpha * scale_a * scale_b) * sum) * row_scale[m] * col_scale[n], in fp32.
  *
  * Supported type combinations (A and B share a type; C, D and bias share the output type):
  *     A/B      C/D/bias
@@ -77,7 +91,7 @@ enum {
 
 /* ---- element types and activations ----------------------------------------------------- */
 typedef enum { GEMM_F32 = 0, GEMM_F16 = 1, GEMM_BF16 = 2, GEMM_F8E4M3 = 3 } gemm_dtype;
-typedef enum { GEMM_ACT_NONE = 0, GEMM_ACT_RELU = 1, GEMM_ACT_GELU = 2 } gemm_act;
+typedef enum { GEMM_ACT_NONE = 0, GEMM_ACT_RELU = 1, GEMM_ACT_GELU = 2, GEMM_ACT_SILU = 3 } gemm_act;
 
 /* ---- problem descriptor ------------------------------------------------------------------ */
 typedef struct gemm_desc {
@@ -95,6 +109,12 @@ typedef struct gemm_desc {
   int32_t force_config;       /* -1: choose from the tile table; else a table index (tuning)     */
   int32_t split_k;            /* split of K across workgroups per output tile: 0 = automatic,    */
                               /* 1 = never, 2..64 = that many slices (capped at one per k-tile)  */
+  int32_t has_row_scale;      /* 1: gemm_run_ex multiplies row m of the product by row_scale[m]  */
+  int32_t has_col_scale;      /* 1: gemm_run_ex multiplies column n by col_scale[n]              */
+  int64_t batch;              /* problems of this shape per call, 0..65535 (0 and 1: one); with  */
+                              /* batch > 1 split_k must be 0 or 1 and no split is made           */
+  int64_t a_stride_l, b_stride_l;   /* elements from problem l's A (B) to problem l+1's; >= 0    */
+  int64_t c_stride_l, d_stride_l;   /* the same for C and D; d_stride_l != 0 when batch > 1      */
 } gemm_desc;
 
 typedef struct gemm_handle_s* gemm_t;
@@ -114,7 +134,9 @@ int gemm_workspace_size(gemm_t h, size_t* bytes);
 /* Enqueue D = act(alpha*scale_a*scale_b*(A@B) + beta*C + bias) on `stream` (a hipStream_t;
  * NULL is the default stream).  A, B, D are device pointers; C may be NULL when beta == 0 or the
  * handle was created with has_c == 0 (then beta must be 0); bias must be non-NULL iff the handle
- * has has_bias == 1.  scale_a and scale_b are the per-tensor dequantisation scales (pass 1.0f for
+ * has has_bias == 1.  For a batch (desc.batch > 1) A, B, C, D address problem 0 and the others
+ * follow at the *_stride_l element offsets; the 16-byte kernels are used only when those
+ * offsets keep every problem's A and B 16-byte aligned.  scale_a and scale_b are the per-tensor dequantisation scales (pass 1.0f for
  * non-fp8 operands).  Pointers only need element alignment: the library falls back to a
  * narrow-load kernel when a pointer is not 16-byte aligned.  `workspace` is a device buffer of
  * gemm_workspace_size() bytes, 16-byte aligned (GEMM_ERR_INVALID_ARG if it is needed and missing;
@@ -124,6 +146,29 @@ int gemm_workspace_size(gemm_t h, size_t* bytes);
 int gemm_run(gemm_t h, const void* A, const void* B, const void* C, void* D, const void* bias,
              float alpha, float beta, float scale_a, float scale_b, void* workspace,
              void* stream);
+
+/* Arguments of gemm_run_ex: the pointers and scalars of gemm_run plus the scale vectors.
+ * row_scale (M floats) must be non-NULL iff the handle has has_row_scale == 1, col_scale (N
+ * floats) iff has_col_scale == 1; both are device pointers aligned to 4 bytes and shared by every
+ * problem of a batch, like bias.  For a batch, A, B, C and D point at problem 0 and the others
+ * follow at the descriptor's *_stride_l element offsets. */
+typedef struct gemm_args {
+  const void* A;
+  const void* B;
+  const void* C;
+  void* D;
+  const void* bias;
+  const float* row_scale;
+  const float* col_scale;
+  float alpha, beta, scale_a, scale_b;
+  void* workspace;
+} gemm_args;
+
+/* Enqueue the handle's operation with the arguments in `args` on `stream`; the same checks and
+ * errors as gemm_run, plus GEMM_ERR_INVALID_ARG when a scale vector's presence does not match the
+ * handle and GEMM_ERR_MISALIGNED when one is not 4-byte aligned.  gemm_run itself returns
+ * GEMM_ERR_INVALID_ARG for a handle with scale vectors. */
+int gemm_run_ex(gemm_t h, const gemm_args* args, void* stream);
 
 /* Free a handle.  NULL is accepted. */
 int gemm_destroy(gemm_t h);
@@ -140,7 +185,7 @@ typedef struct gemm_info {
   int32_t stages;         /* LDS pipeline stages                                                */
   int32_t lds_bytes;      /* LDS bytes per workgroup                                            */
   int32_t split_k;        /* workgroups sharing one output tile along K (1: none)              */
-  int64_t grid;           /* workgroups per launch                                              */
+  int64_t grid;           /* workgroups per launch (all problems of a batch)                    */
   char name[96];          /* kernel name                                                        */
 } gemm_info;
 

@@ -43,6 +43,9 @@ class Case:
     a_offset: int = 0           # element offset of A's base pointer (misalignment tests)
     c_fill_nan: bool = False
     split_k: int = 0            # 0: the library decides; 1: never; >1: that many K slices
+    row_scale: bool = False     # per-row fp32 scale vector (gemm_run_ex)
+    col_scale: bool = False     # per-column fp32 scale vector (gemm_run_ex)
+    scale_dist: str = "uniform"  # "uniform": U[0.25, 2] rows, U[-2, 2] columns; "pow2": 2^[-3..3]
 
 
 def op(m):
@@ -70,6 +73,8 @@ class Prepared:
         if c.bias:
             bdist = "dyadic" if c.dist == "dyadic" else "normal"
             self.bias = inputs.vector(s + 4, c.N, ot, bdist, **({"std": 0.1} if bdist == "normal" else {}))
+        self.rs = self._scales(s + 5, c.M, 0.25) if c.row_scale else None
+        self.cs = self._scales(s + 6, c.N, -2.0) if c.col_scale else None
         d_strides, n = inputs.layout_strides(c.M, c.N, c.d_order, c.d_ld)
         self.d_strides = d_strides
         self.d_len = max(n, 1)
@@ -78,6 +83,15 @@ class Prepared:
         self.dB = inputs.to_device(self.B, device) if self.B.storage.size else torch.empty(1, device=device)
         self.dC = inputs.to_device(self.C, device) if self.C is not None else None
         self.dbias = inputs.to_device(self.bias, device) if self.bias is not None else None
+        self.drs = torch.from_numpy(self.rs).to(device) if self.rs is not None else None
+        self.dcs = torch.from_numpy(self.cs).to(device) if self.cs is not None else None
+
+    def _scales(self, seed, n, lo):
+        if self.case.scale_dist == "pow2":
+            e = np.round(inputs.draw(seed, n, "uniform") * 3.0)
+            return (2.0 ** e).astype(np.float32)
+        u = inputs.draw(seed, n, "uniform")          # U[-1, 1]
+        return (lo + (u + 1.0) * (2.0 - lo) / 2.0).astype(np.float32)
 
     def _upload(self, m, offset):
         if m.storage.size == 0:
@@ -92,7 +106,8 @@ class Prepared:
         c = self.case
         return H.make_desc(c.M, c.N, c.K, c.dtype, self.A.strides, self.B.strides, self.d_strides,
                            c_strides=self.C.strides if self.C is not None else None,
-                           has_bias=c.bias, act=c.act, force_config=c.force, split_k=c.split_k)
+                           has_bias=c.bias, act=c.act, force_config=c.force, split_k=c.split_k,
+                           row_scale=c.row_scale, col_scale=c.col_scale)
 
     def run(self, g: H.Gemm | None = None, out=None):
         c = self.case
@@ -106,7 +121,8 @@ class Prepared:
         ws = torch.full((max(ws_bytes, 4) // 4,), float("nan"), dtype=torch.float32,
                         device=self.device) if ws_bytes else None
         g.run(a_ptr, self.dB, self.dC, out, self.dbias, alpha=c.alpha, beta=c.beta,
-              scale_a=c.scale_a, scale_b=c.scale_b, workspace=ws)
+              scale_a=c.scale_a, scale_b=c.scale_b, workspace=ws, row_scale=self.drs,
+              col_scale=self.dcs)
         torch.cuda.synchronize()
         return g, out
 
@@ -122,14 +138,16 @@ class Prepared:
         c = self.case
         return oracle.gemm(op(self.A), op(self.B), op(self.C) if self.C is not None else None,
                            op(self.bias) if self.bias is not None else None, alpha=c.alpha,
-                           beta=c.beta, scale_a=c.scale_a, scale_b=c.scale_b, act=c.act)
+                           beta=c.beta, scale_a=c.scale_a, scale_b=c.scale_b, act=c.act,
+                           row_scale=self.rs, col_scale=self.cs)
 
     def oracle_elems(self, rows, cols):
         c = self.case
         return oracle.gemm_elems(op(self.A), op(self.B), rows, cols,
                                  op(self.C) if self.C is not None else None,
                                  op(self.bias) if self.bias is not None else None, alpha=c.alpha,
-                                 beta=c.beta, scale_a=c.scale_a, scale_b=c.scale_b, act=c.act)
+                                 beta=c.beta, scale_a=c.scale_a, scale_b=c.scale_b, act=c.act,
+                                 row_scale=self.rs, col_scale=self.cs)
 
 
 def error(dtype, got, want):

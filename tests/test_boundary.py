@@ -192,3 +192,54 @@ def test_split_k_plan_and_workspace(fake_gfx950):
     sk = _info(H.make_desc(16, 16384, 8192, "e4m3", (8192, 1), (1, 8192), (16384, 1), split_k=2))
     assert b"skinny" not in sk.name and sk.split_k == 2
     assert status_of(desc(M=16, force_config=names.index("bf16_ak_bk_16x32_w8_skinny"), split_k=2)) == 8
+
+
+def test_scale_vector_and_activation_fields(fake_gfx950):
+    """The fused-epilogue fields ("CUTLASS", Part IV Stage 5: per-channel scales and activations
+    in the epilogue): flags are 0/1, activations 0..3 (SiLU = 3); a handle with a scale vector
+    refuses gemm_run (which cannot pass the vector) before any launch."""
+    assert status_of(desc(act="silu")) == 0
+    d = desc()
+    d.act = 4
+    assert status_of(d) == H.GEMM_ERR_INVALID_ARG
+    d = desc(row_scale=True)
+    d.has_row_scale = 2
+    assert status_of(d) == H.GEMM_ERR_INVALID_ARG
+    h = H.gemm_create(desc(row_scale=True, col_scale=True))
+    try:
+        assert H.lib().gemm_run(h, 256, 256, None, 256, None, 1.0, 0.0, 1.0, 1.0, None, None) == 1
+        # gemm_run_ex: the vectors must match the handle, and be 4-byte aligned
+        run_ex = lambda rs, cs: H.lib().gemm_run_ex(h, H.gemm_args(256, 256, None, 256, None, rs, cs,
+                                                                    1.0, 0.0, 1.0, 1.0, None), None)
+        assert run_ex(None, 1024) == H.GEMM_ERR_INVALID_ARG
+        assert run_ex(1024, None) == H.GEMM_ERR_INVALID_ARG
+        assert run_ex(1026, 1024) == H.GEMM_ERR_MISALIGNED
+    finally:
+        H.gemm_destroy(h)
+
+
+def test_batch_fields(fake_gfx950):
+    """The batch mode (the problem shape's L, "CUTLASS, CuTe, and CUDA Tile", "Assembling a
+    CUTLASS kernel"): grid z holds the problems, distinct problems need distinct D, no split-K,
+    and the 16-byte kernels only when every problem's A and B stay 16-byte aligned."""
+    L = 5
+    base = dict(M=512, N=512, K=4096, a_strides=(4096, 1), b_strides=(1, 4096), d_strides=(512, 1))
+    ok = _info(desc(batch=L, batch_strides=(512 * 4096, 512 * 4096, 0, 512 * 512), **base))
+    assert ok.split_k == 1 and ok.grid == L * (512 // ok.bm) * (512 // ok.bn)
+    assert b"_vec" in ok.name or b"_ring" in ok.name or b"_dma" in ok.name
+    # 512 x 512 x 65536 alone splits K (16 tiles, 1024 k-tiles); as a batch it never does
+    assert _info(desc(batch=L, batch_strides=(0, 0, 0, 512 * 512), **dict(base, K=65536,
+                      a_strides=(65536, 1), b_strides=(1, 65536)))).split_k == 1
+    # a shared B (stride 0) is allowed; a shared D is not
+    assert status_of(desc(batch=L, batch_strides=(512 * 4096, 0, 0, 512 * 512), **base)) == 0
+    assert status_of(desc(batch=L, batch_strides=(512 * 4096, 0, 0, 0), **base)) == H.GEMM_ERR_INVALID_ARG
+    # negative strides, out-of-range batch, forced split with a batch
+    assert status_of(desc(batch=L, batch_strides=(-1, 0, 0, 512 * 512), **base)) == H.GEMM_ERR_LAYOUT
+    assert status_of(desc(batch=65536, batch_strides=(0, 0, 0, 512 * 512), **base)) == H.GEMM_ERR_INVALID_ARG
+    assert status_of(desc(batch=-1, **base)) == H.GEMM_ERR_INVALID_ARG
+    assert status_of(desc(batch=L, split_k=2, batch_strides=(0, 0, 0, 512 * 512), **base)) == H.GEMM_ERR_INVALID_ARG
+    # an A stride off the 16-byte grid (odd element count): only the element-wise loaders
+    odd = _info(desc(batch=2, batch_strides=(512 * 4096 + 1, 0, 0, 512 * 512), **base))
+    assert b"_vec" not in odd.name and b"_ring" not in odd.name and b"_dma" not in odd.name
+    # batch 0 and 1 are one problem
+    assert _info(desc(batch=0, **base)).grid == _info(desc(batch=1, **base)).grid

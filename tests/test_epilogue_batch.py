@@ -1,0 +1,207 @@
+"""GPU parity for the fused-epilogue extensions and the batch mode, through the C ABI.
+
+* Per-row / per-column fp32 scale vectors and SiLU ("CUTLASS", Part IV Stage 5: an epilogue
+  visitor tree fuses a per-channel dequantisation scale and an activation while the accumulator
+  is in registers; "A10 - CuTe, CUTLASS & CuTile", drill answer 8).
+* A batch of L problems of one shape in one call ("CUTLASS, CuTe, and CUDA Tile", "Assembling a
+  CUTLASS kernel": the problem shape [M, N, K, L]).
+
+Tolerances are the spec ones (see test_gemm_parity); dyadic inputs with power-of-two scales
+must match the oracle bit for bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from hierarchical_tiling_amd import htgemm as H
+from hierarchical_tiling_amd import inputs
+from tests.gemm_util import OUT_T, TOL, Case, Prepared, error, op
+
+pytestmark = pytest.mark.gpu
+
+
+def _index(name):
+    return [H.gemm_config_name(i) for i in range(H.gemm_num_configs())].index(name)
+
+
+EPI_CASES = {
+    # split ring, 16x16 MFMA: both vectors, bias, SiLU, ragged M/N and a K tail
+    "bf16_ring_scales_silu": dict(M=300, N=264, K=64 * 5 + 24, dtype="bf16", row_scale=True,
+                                  col_scale=True, bias=True, act="silu",
+                                  force="bf16_ak_bk_256x256x64_w2x4_m16_ring"),
+    # library choice (tiled 16-byte kernel), column scale with C and GELU
+    "bf16_colscale_c_gelu": dict(M=200, N=136, K=200, dtype="bf16", col_scale=True, has_c=True,
+                                 beta=0.5, act="gelu"),
+    # realigned loader (odd leading dims), row scale, C and SiLU
+    "f16_realign_rowscale_silu": dict(M=131, N=97, K=77, dtype="f16", b_order="row", a_ld=81,
+                                      b_ld=99, row_scale=True, has_c=True, beta=-1.0, act="silu"),
+    # streaming skinny kernel with per-token and per-channel dequantisation scales
+    "e4m3_skinny_scales": dict(M=16, N=1040, K=1024, dtype="e4m3", row_scale=True,
+                               col_scale=True, scale_a=0.5, scale_b=0.25),
+    "e4m3_ring_colscale_silu": dict(M=264, N=328, K=128 * 4 + 32, dtype="e4m3", col_scale=True,
+                                    act="silu", force="e4m3_ak_bk_256x256x128_w2x4_m32_ring"),
+    # split-K: the scales are applied in the reduction's epilogue
+    "f32_split_scales_silu": dict(M=130, N=96, K=32 * 10, dtype="f32", dist="uniform", split_k=5,
+                                  row_scale=True, col_scale=True, has_c=True, beta=0.5,
+                                  alpha=1.5, act="silu"),
+    "bf16_ring_split_scales": dict(M=264, N=328, K=64 * 9 + 16, dtype="bf16", split_k=3,
+                                   row_scale=True, col_scale=True, bias=True, act="gelu",
+                                   force="bf16_ak_bk_256x256x64_w2x4_m32_ring"),
+}
+
+
+@pytest.mark.parametrize("name", list(EPI_CASES))
+def test_scale_vectors_and_silu_match_oracle(name):
+    kw = dict(EPI_CASES[name])
+    if isinstance(kw.get("force"), str):
+        kw["force"] = _index(kw["force"])
+    c = Case(seed=60 + list(EPI_CASES).index(name), **kw)
+    p = Prepared(c)
+    g, out = p.run()
+    got, _ = p.decode_out(out)
+    assert np.isfinite(got).all()
+    err = error(c.dtype, got, p.oracle_full())
+    print(f"{name}: {g.info.name.decode()} split {g.info.split_k} err={err:.3e}")
+    assert err <= TOL[c.dtype], (name, err)
+
+
+@pytest.mark.parametrize("dtype,force", [("bf16", "bf16_ak_bk_256x256x64_w2x4_m16_ring"),
+                                         ("e4m3", "e4m3_ak_bk_256x256x128_w2x4_m32_ring"),
+                                         ("f32", None), ("f16", None)])
+def test_power_of_two_scales_are_bit_exact(dtype, force):
+    # dyadic inputs and power-of-two scales keep every fp32 step exact: the rounded output must be
+    # the rounded oracle bit for bit
+    c = Case(M=264, N=200, K=256 if dtype != "e4m3" else 512, dtype=dtype, dist="dyadic",
+             row_scale=True, col_scale=True, scale_dist="pow2", alpha=0.5, beta=2.0, has_c=True,
+             bias=True, seed=71, force=_index(force) if force else -1)
+    p = Prepared(c)
+    g, out = p.run()
+    _, bits = p.decode_out(out)
+    want = oracle.encode_rne(OUT_T[dtype], p.oracle_full())
+    assert int((bits != want).sum()) == 0, g.info.name.decode()
+
+
+def test_fused_silu_equals_gemm_then_silu():
+    base = dict(M=384, N=512, K=320, dtype="bf16", bias=True, seed=72, col_scale=True)
+    pf = Prepared(Case(act="silu", **base))
+    pu = Prepared(Case(act="none", **base))
+    got_f, _ = pf.decode_out(pf.run()[1])
+    unf = pu.oracle_full()
+    silu = unf / (1.0 + np.exp(-unf))
+    assert error("bf16", got_f, silu) <= TOL["bf16"]
+
+
+def test_scale_vector_presence_must_match_the_handle():
+    c = Case(M=64, N=64, K=64, dtype="bf16", row_scale=True, seed=73)
+    p = Prepared(c)
+    g = H.Gemm(p.desc())
+    out = torch.zeros(64 * 64 * 2, dtype=torch.uint8, device="cuda")
+    with pytest.raises(H.GemmError) as e:   # gemm_run cannot pass the vector
+        H.gemm_run(g.handle, p.dA[0].data_ptr(), p.dB.data_ptr(), None, out.data_ptr(), None,
+                   1.0, 0.0)
+    assert e.value.status == H.GEMM_ERR_INVALID_ARG
+    with pytest.raises(H.GemmError) as e:   # gemm_run_ex without it
+        H.gemm_run_ex(g.handle, p.dA[0].data_ptr(), p.dB.data_ptr(), None, out.data_ptr(), None,
+                      None, None, 1.0, 0.0)
+    assert e.value.status == H.GEMM_ERR_INVALID_ARG
+    with pytest.raises(H.GemmError) as e:   # a column vector the handle does not have
+        H.gemm_run_ex(g.handle, p.dA[0].data_ptr(), p.dB.data_ptr(), None, out.data_ptr(), None,
+                      p.drs.data_ptr(), p.drs.data_ptr(), 1.0, 0.0)
+    assert e.value.status == H.GEMM_ERR_INVALID_ARG
+    with pytest.raises(H.GemmError) as e:   # misaligned vector
+        H.gemm_run_ex(g.handle, p.dA[0].data_ptr(), p.dB.data_ptr(), None, out.data_ptr(), None,
+                      p.drs.data_ptr() + 2, None, 1.0, 0.0)
+    assert e.value.status == H.GEMM_ERR_MISALIGNED
+    torch.cuda.synchronize()
+
+
+# ---- batch (the L mode) ------------------------------------------------------------------------
+
+def _stack(mats, pad_elems, align_elems):
+    """Concatenate equal-size storages with one fixed stride between them."""
+    n = mats[0].storage.size
+    # pad > 0 keeps the odd stride (a problem base off the 16-byte grid); else round up
+    stride = n + pad_elems if pad_elems else -(-n // align_elems) * align_elems
+    flat = np.zeros(stride * len(mats), dtype=mats[0].storage.dtype)
+    for i, m in enumerate(mats):
+        flat[i * stride:i * stride + n] = m.storage
+    return flat, stride
+
+
+def _dev(flat):
+    view = {1: np.uint8, 2: np.int16, 4: np.int32}[flat.dtype.itemsize]
+    return torch.from_numpy(np.ascontiguousarray(flat).view(view)).to("cuda")
+
+
+BATCH_CASES = {
+    # split ring, distinct A/B per problem
+    "bf16_ring_L3": dict(L=3, M=264, N=328, K=320, dtype="bf16", bias=True, act="gelu",
+                         force="bf16_ak_bk_256x256x64_w2x4_m16_ring"),
+    # a batch stride that is not a multiple of 16 bytes: the library must leave the 16-byte path
+    "bf16_odd_stride_L2": dict(L=2, M=100, N=72, K=96, dtype="bf16", pad=1, has_c=True, beta=0.5),
+    # skinny streaming kernel, B shared by every problem (stride 0), scale vectors
+    "e4m3_skinny_sharedB_L4": dict(L=4, M=16, N=520, K=512, dtype="e4m3", shared_b=True,
+                                   row_scale=True, col_scale=True, scale_a=0.5, scale_b=0.5),
+    # fp32 with C, MN-major B
+    "f32_C_L2": dict(L=2, M=70, N=90, K=50, dtype="f32", dist="uniform", b_order="row",
+                     has_c=True, beta=-0.5, alpha=2.0),
+    "f16_rowB_silu_L3": dict(L=3, M=96, N=128, K=64, dtype="f16", b_order="row", act="silu",
+                             col_scale=True),
+}
+
+
+@pytest.mark.parametrize("name", list(BATCH_CASES))
+def test_batched_problems_match_oracle_each(name):
+    kw = dict(BATCH_CASES[name])
+    L = kw.pop("L")
+    pad = kw.pop("pad", 0)
+    shared_b = kw.pop("shared_b", False)
+    force = kw.pop("force", None)
+    base_seed = 80 + list(BATCH_CASES).index(name) * 10
+    preps = [Prepared(Case(seed=base_seed + l, **kw)) for l in range(L)]
+    c0, p0 = preps[0].case, preps[0]
+    ot = OUT_T[c0.dtype]
+    align = 16 // inputs.ESIZE[c0.dtype]
+    a_flat, sa = _stack([p.A for p in preps], pad, align)
+    if shared_b:
+        b_flat, sb = p0.B.storage, 0
+    else:
+        b_flat, sb = _stack([p.B for p in preps], pad, align)
+    c_flat, sc = (_stack([p.C for p in preps], 0, 8) if c0.has_c else (None, 0))
+    d_len = p0.d_len
+    sd = -(-(d_len + 5) // 8) * 8       # a gap after every problem's D, checked below
+    out_bits = oracle.encode_rne(ot, np.array([np.nan]))[0]
+    d_host = np.full(sd * L, out_bits, dtype=inputs.STORAGE[ot])
+    dA, dB, dD = _dev(a_flat), _dev(b_flat), _dev(d_host)
+    dC = _dev(c_flat) if c_flat is not None else None
+    desc = H.make_desc(c0.M, c0.N, c0.K, c0.dtype, p0.A.strides, p0.B.strides, p0.d_strides,
+                       c_strides=p0.C.strides if p0.C is not None else None, has_bias=c0.bias,
+                       act=c0.act, force_config=_index(force) if force else -1,
+                       row_scale=c0.row_scale, col_scale=c0.col_scale, batch=L,
+                       batch_strides=(sa, sb, sc, sd))
+    g = H.Gemm(desc)
+    info = g.info
+    tiles = -(-c0.M // info.bm) * -(-c0.N // info.bn)
+    assert info.grid == tiles * L and info.split_k == 1
+    if pad:
+        assert "_vec" not in info.name.decode() and "_ring" not in info.name.decode()
+    g.run(dA, dB, dC, dD, p0.dbias, alpha=c0.alpha, beta=c0.beta, scale_a=c0.scale_a,
+          scale_b=c0.scale_b, row_scale=p0.drs, col_scale=p0.dcs)
+    torch.cuda.synchronize()
+    d_all = dD.cpu().numpy().view(inputs.STORAGE[ot])
+    r = np.arange(c0.M)[:, None] * p0.d_strides[0] + np.arange(c0.N)[None, :] * p0.d_strides[1]
+    written = np.zeros(sd, dtype=bool)
+    written[r.ravel()] = True
+    for l, p in enumerate(preps):
+        seg = d_all[l * sd:(l + 1) * sd]
+        assert (seg[~written] == out_bits).all(), f"problem {l} wrote outside its D"
+        got = oracle.decode(ot, seg)[r]
+        B = p0.B if shared_b else p.B
+        want = oracle.gemm(op(p.A), op(B), op(p.C) if p.C is not None else None,
+                           op(p0.bias) if p0.bias is not None else None, alpha=c0.alpha,
+                           beta=c0.beta, scale_a=c0.scale_a, scale_b=c0.scale_b, act=c0.act,
+                           row_scale=p0.rs, col_scale=p0.cs)
+        err = error(c0.dtype, got, want)
+        print(f"{name}[{l}]: {info.name.decode()} err={err:.3e}")
+        assert err <= TOL[c0.dtype], (name, l, err)
