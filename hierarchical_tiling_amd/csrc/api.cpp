@@ -330,6 +330,10 @@ int run_impl(gemm_t h, const void* A, const void* B, const void* C, void* D, con
   p.b_bstride = d.b_stride_l * (int64_t)in_sz;
   p.c_bstride = d.c_stride_l * (int64_t)out_sz;
   p.d_bstride = d.d_stride_l * (int64_t)out_sz;
+  if (read_c) {
+    const int64_t span = ((d.M - 1) * d.c_stride_m + (d.N - 1) * d.c_stride_n + 1) * (int64_t)out_sz;
+    p.c_span = span < (int64_t(1) << 31) - 64 ? span : 0;
+  }
   const int64_t grid = int64_t(p.tiles_m) * p.tiles_n;
   if (grid <= 0 || grid > INT32_MAX) return GEMM_ERR_INVALID_ARG;
   hipError_t err = e.launch(p, (hipStream_t)stream,

@@ -30,6 +30,8 @@ struct KParams {
   const float* col_scale;  // read only when has_col_scale != 0: N values
   int has_row_scale, has_col_scale;
   int batch;               // problems per launch (gridDim.z); 1: one
+  int64_t c_span;          // bytes from C's base to the end of its last element when below
+                           // 2^31 - 64 (range-checked buffer loads), else 0
   int64_t a_bstride, b_bstride, c_bstride, d_bstride;  // bytes between consecutive problems
 };
 

@@ -76,14 +76,17 @@ template <int ODT> struct Out;
 template <> struct Out<DT_F32> {
   __device__ static float load(const void* p, int64_t i) { return ((const float*)p)[i]; }
   __device__ static void store(void* p, int64_t i, float v) { ((float*)p)[i] = v; }
+  __device__ static float from_bits(u32 b) { return __builtin_bit_cast(float, b); }
 };
 template <> struct Out<DT_F16> {
   __device__ static float load(const void* p, int64_t i) { return f16_to_f32(((const u16*)p)[i]); }
   __device__ static void store(void* p, int64_t i, float v) { ((u16*)p)[i] = f32_to_f16(v); }
+  __device__ static float from_bits(u32 b) { return f16_to_f32((u16)b); }
 };
 template <> struct Out<DT_BF16> {
   __device__ static float load(const void* p, int64_t i) { return bf16_to_f32(((const u16*)p)[i]); }
   __device__ static void store(void* p, int64_t i, float v) { ((u16*)p)[i] = f32_to_bf16(v); }
+  __device__ static float from_bits(u32 b) { return bf16_to_f32((u16)b); }
 };
 
 // Compile-time loop: the body sees its index as a constant, so register arrays indexed by it
@@ -715,6 +718,18 @@ struct PickLoader<DT, false, 2, R, BKE, NT> {
   typedef LoadMNMajorMis<DT, R, BKE, NT> type;
 };
 
+// One element of C through a range-checked buffer load: `off` is its byte offset from C's base,
+// or kOobOffset for an element outside the problem (the load then returns zero bits).  Unlike a
+// predicated pointer load it needs no branch, so the loads of a whole row block issue back to
+// back and are waited for once.
+template <int ODT>
+__device__ __forceinline__ float load_c(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  if constexpr (ODT == DT_F32)
+    return Out<ODT>::from_bits(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+  else
+    return Out<ODT>::from_bits((u32)__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0));
+}
+
 // ------------------------------------------------------------------------------------------
 // Epilogue ("CUTLASS", Part IV Stages 5 and 6).
 // Phase 1, in registers: y = act(alpha * acc + beta * C + bias[n]) in fp32, rounded once to the
@@ -761,7 +776,17 @@ __device__ __forceinline__ void epilogue(const KParams& p, AccT (&acc)[RM][RN], 
       });
     }
     if (has_cs) each([&](auto j, auto r) { acc[i][j][(int)r] *= cs_v[j]; });
-    if (has_c) {
+    if (has_c && p.c_span > 0) {
+      const __amdgpu_buffer_rsrc_t cr = make_rsrc((const char*)p.C, p.c_span);
+      each([&](auto j, auto r) {
+        const int64_t col = n0 + wn * WTN + j * MI + (lane % MI);
+        const int64_t row = m0 + wm * WTM + i * MI + acc_row<MI>(lane, r);
+        const uint32_t off = col < p.N && row < p.M
+                                 ? (uint32_t)((row * p.c_sm + col * p.c_sn) * (int64_t)sizeof(OT))
+                                 : kOobOffset;
+        acc[i][j][(int)r] += beta * load_c<ODT>(cr, off);
+      });
+    } else if (has_c) {  // C spans 2^31 bytes or more: predicated pointer loads
       each([&](auto j, auto r) {
         const int64_t col = n0 + wn * WTN + j * MI + (lane % MI);
         const int64_t row = m0 + wm * WTM + i * MI + acc_row<MI>(lane, r);
@@ -819,7 +844,7 @@ __device__ __forceinline__ void epilogue(const KParams& p, AccT (&acc)[RM][RN], 
 // The tiled kernel.
 // ------------------------------------------------------------------------------------------
 template <int DT, bool AK, bool BKM, int VEC, int BM, int BN, int BKE, int WM, int WN, int MI>
-__global__ __launch_bounds__(WM * WN * 64) void gemm_tiled(const KParams p_) {
+__global__ __launch_bounds__(WM * WN * 64, BM * BN <= 128 * 128 && (AK || BKM) ? 2 : 1) void gemm_tiled(const KParams p_) {
   const KParams p = batch_view(p_);
   typedef Atom<DT, MI> At;
   typedef typename At::acc_t acc_t;
