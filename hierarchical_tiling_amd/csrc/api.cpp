@@ -122,14 +122,16 @@ void plan_split(const KernelEntry& e, const gemm_desc& d, int req, int* S, int64
 // Heuristic choice among fitting entries.  A product with M <= 16 is bound by streaming B and
 // takes the skinny kernel when one fits.  Otherwise each entry is counted with the split-K plan
 // it would get (plan_split) and the choice is the largest tile whose workgroups (tiles x slices)
-// still number at least 256 (one per CU), ties broken by the measured rank, else the entry with
-// the most workgroups.  A forced split (split_req > 1) admits only entries that can split.
+// still number at least 256 (one per CU), ties broken by the measured rank -- the entry's
+// one-round rank when all its workgroups run at once (at most 256), else its rank -- or, when
+// no tile reaches 256 workgroups, the entry with the most workgroups.  A forced split
+// (split_req > 1) admits only entries that can split.
 int choose(const gemm_handle_s& h, bool vec_a, bool vec_b, bool want_vec, int split_req) {
   const KernelEntry* t = table();
   const bool need_split = split_req > 1;
   for (int i = 0; i < table_size() && !need_split; ++i)
     if (t[i].skinny && (t[i].vec != 0) == want_vec && entry_fits(t[i], h, vec_a, vec_b)) return i;
-  int best = -1;
+  int best = -1, best_rank = 0;
   int64_t best_area = -1;
   int best_small = -1;
   int64_t best_small_wg = -1;
@@ -143,9 +145,11 @@ int choose(const gemm_handle_s& h, bool vec_a, bool vec_b, bool want_vec, int sp
     plan_split(e, h.d, split_req, &slices, &kps);
     const int64_t wg = cdiv(h.d.M, e.bm) * cdiv(h.d.N, e.bn) * slices;
     const int64_t area = int64_t(e.bm) * e.bn;
-    if (wg >= 256 && (area > best_area || (area == best_area && e.rank > t[best].rank))) {
+    const int rank = wg <= 256 ? e.rank_one_round : e.rank;
+    if (wg >= 256 && (area > best_area || (area == best_area && rank > best_rank))) {
       best = i;
       best_area = area;
+      best_rank = rank;
     }
     if (wg > best_small_wg || (wg == best_small_wg && area > int64_t(t[best_small].bm) * t[best_small].bn)) {
       best_small = i;

@@ -53,6 +53,7 @@ struct KernelEntry {
   int rank;           // preference among entries with the same tile area (measured; higher wins)
   launch_fn launch;
   int realign;        // 1: realigned 16-byte loads of 2-byte elements (31-bit tile offsets)
+  int rank_one_round; // rank when all workgroups fit on the CUs at once (one tile per CU)
 };
 
 const KernelEntry* table();

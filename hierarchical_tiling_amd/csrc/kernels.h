@@ -1665,16 +1665,17 @@ static hipError_t launch_tiled(const KParams& p, hipStream_t s, dim3 grid) {
 // aligned (vec 0) kernels that outrank the element-wise ones (rank 1)
 #define HT_TILED(NAME, DT, AK, BKM, VEC, BM, BN, BKE, WM, WN, MI)                                 \
   {NAME, DT, AK, BKM, (VEC) == 1, 0, BM, BN, BKE, WM * WN, 2, 2 * (BM + BN) * BKE * Ty<DT>::SZ, 64, \
-   (VEC) == 2 ? 1 : 0, &launch_tiled<DT, AK, BKM, VEC, BM, BN, BKE, WM, WN, MI>, (VEC) == 2}
+   (VEC) == 2 ? 1 : 0, &launch_tiled<DT, AK, BKM, VEC, BM, BN, BKE, WM, WN, MI>, (VEC) == 2, \
+   (VEC) == 2 ? 1 : 0}
 
 #define HT_DMA(NAME, DT, BM, BN, WM, WN, MI, ST, OCC, CH, RANK)                                \
   {NAME, DT, 1, 1, 1, 0, BM, BN, CH * 16 / Ty<DT>::SZ, WM * WN, ST, ST * (BM + BN) * CH * 16, 1, \
-   RANK, &launch_dma<DT, BM, BN, WM, WN, MI, ST, OCC, CH>}
+   RANK, &launch_dma<DT, BM, BN, WM, WN, MI, ST, OCC, CH>, 0, RANK}
 
 // Split-ring entries: 256 x 256 tiles, 128-byte rows, 5 units of 32 KiB.
-#define HT_RING(NAME, DT, WM, WN, MI, NB, RANK)                                                      \
+#define HT_RING(NAME, DT, WM, WN, MI, NB, RANK, RANK1)                                               \
   {NAME, DT, 1, 1, 1, 0, 256, 256, 128 / Ty<DT>::SZ, WM * WN, 5, 5 * 256 * 128, 64, RANK,         \
-   &launch_ring<DT, WM, WN, MI, NB>}
+   &launch_ring<DT, WM, WN, MI, NB>, 0, RANK1}
 
 // Streaming skinny entries: bm = 16 rows, bn = 16*NBW columns, bk = one 128-byte block of K.
 #define HT_SKINNY_DMA(NAME, DT, WK, NBW, R, OCC)                                                  \
