@@ -1279,18 +1279,25 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_ring(const KParams p_) {
   constexpr std::integral_constant<int, 0> OPA{};
   constexpr std::integral_constant<int, 1> OPB{};
   typedef std::integral_constant<int, 0> I0;
-  // Scheduling hint for one substep: alternate its NDS LDS reads (the next substep's fragments)
-  // with its NMF MFMAs, then fence the region.  Left alone, the scheduler issues each read just
-  // before the MFMA that needs it, and every MFMA then waits for an LDS round trip.
-  auto interleave = [&](auto NDS, auto NMF) {
-    constexpr int nds = NDS, nmf = NMF;
-    constexpr int per = (nmf + nds - 1) / nds;
-    static_for<nds>([&](auto) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
-      __builtin_amdgcn_sched_group_barrier(0x008, per, 0); // then `per` MFMAs
-    });
+  // Scheduling hint for one region: spread its NVM DMA instructions and NDS LDS reads (the next
+  // substep's fragments) evenly among its NMF MFMAs, then fence the region.  Left alone, the
+  // scheduler issues each read just before the MFMA that needs it (every MFMA then waits for an
+  // LDS round trip), bunches the DMA issue, and moves MFMAs across the barriers, which with one
+  // or two waves per SIMD leaves the matrix pipe idle at every barrier.
+  auto interleave = [&](auto NVM, auto NDS, auto NMF) {
+    constexpr int nvm = NVM, nds = NDS, nmf = NMF;
+    constexpr int ng = nvm > nds ? nvm : nds;
+    if constexpr (ng > 0) {
+      constexpr int per = (nmf + ng - 1) / ng;
+      static_for<ng>([&](auto g) {
+        if constexpr (g < nvm) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);  // one DMA
+        if constexpr (g < nds) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+        __builtin_amdgcn_sched_group_barrier(0x008, per, 0);                        // MFMAs
+      });
+    }
     __builtin_amdgcn_sched_barrier(0);
   };
+  typedef std::integral_constant<int, 0> Z;
 
   if (nk > 0) {
     dma(OPA, 0, 0);
@@ -1307,21 +1314,29 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_ring(const KParams p_) {
       constexpr int buf = s & 1;
       const int sb_i = 3 + (t & 1);
       const u32x4* sa = lds + sa_i * SLOT;
+      // With two barriers per k-tile, A(t+2) is issued in substep 0, into the slot A(t-1)
+      // released, and B(t+2) in substep MID, after the barrier that released B(t)'s slot.
+      constexpr int nvm = NB == 2 ? (s == 0 ? DU : 0) + (s == MID ? DU : 0) : 0;
+      if constexpr (NB == 2 && s == 0) dma(OPA, t + 2, sa_i == 0 ? 2 : sa_i - 1);
+      if constexpr (NB == 2 && s == MID) dma(OPB, t + 2, sb_i);
       if constexpr (s + 1 < S) {
         read_a(std::integral_constant<int, buf ^ 1>{}, sa, std::integral_constant<int, s + 1>{});
         mma_rows(std::integral_constant<int, buf>{}, s, I0{}, std::integral_constant<int, RM>{});
         // the first substep also carries the B reads of the rest of the k-tile
-        interleave(std::integral_constant<int, RM * At::UNITS + (s == 0 ? (S - 1) * RN * At::UNITS : 0)>{},
+        interleave(std::integral_constant<int, nvm>{},
+                   std::integral_constant<int, RM * At::UNITS + (s == 0 ? (S - 1) * RN * At::UNITS : 0)>{},
                    std::integral_constant<int, RM * RN * At::PER_UNIT>{});
         if constexpr (s + 1 == MID && NB == 2) {
           // this wave's reads of B(t) are complete (lgkmcnt 0); after the barrier no wave
-          // reads B(t), and B(t+2) takes its slot
+          // reads B(t), and B(t+2) may take its slot
           wait_counts<63, true>();
           barrier_nofence();
-          dma(OPB, t + 2, sb_i);
         }
       } else {
         mma_rows(std::integral_constant<int, buf>{}, s, I0{}, std::integral_constant<int, RM / 2>{});
+        // these MFMAs stay before the barrier
+        interleave(std::integral_constant<int, nvm>{}, Z{},
+                   std::integral_constant<int, RM / 2 * RN * At::PER_UNIT>{});
         // A(t+1) and B(t+1) have landed once at most A(t+2), B(t+2) are in flight (one barrier
         // per k-tile: once at most A(t+2), issued after B(t+1), is)
         if constexpr (NB == 2) wait_counts<2 * DU, true>(); else wait_counts<DU, true>();
@@ -1340,12 +1355,14 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_ring(const KParams p_) {
         }
         mma_rows(std::integral_constant<int, buf>{}, s, std::integral_constant<int, RM / 2>{},
                  std::integral_constant<int, RM>{});
+        interleave(std::integral_constant<int, NB == 1 ? 2 * DU : 0>{},
+                   std::integral_constant<int, (RM + RN) * At::UNITS>{},
+                   std::integral_constant<int, RM / 2 * RN * At::PER_UNIT>{});
       }
     };
-    // First half of k-tile t: issue A(t+2) into the slot A(t-1) released, read the rest of the
-    // k-tile's B fragments, substeps 0 .. MID-1 (ending with the barrier that releases B(t)).
+    // First half of k-tile t: read the rest of the k-tile's B fragments, substeps 0 .. MID-1
+    // (ending with the barrier that releases B(t)).
     auto tile_front = [&](int t, int sa_i) {
-      if constexpr (NB == 2) dma(OPA, t + 2, sa_i == 0 ? 2 : sa_i - 1);
       const u32x4* sb = lds + (3 + (t & 1)) * SLOT;
       static_for<S - 1>([&](auto s) { read_b(sb, std::integral_constant<int, s + 1>{}); });
       static_for<MID>([&](auto s) { substep(t, sa_i, s); });
