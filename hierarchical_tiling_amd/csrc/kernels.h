@@ -1342,10 +1342,11 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_ring(const KParams p_) {
         if constexpr (NB == 2) wait_counts<2 * DU, true>(); else wait_counts<DU, true>();
         barrier_nofence();
         smem_timer_read();
-        // (after the last k-tile these read zero-filled slots; the values are never used)
+        // (after the last k-tile these read zero-filled slots; the values are never used).  B
+        // first: the next substep's first MFMAs need A fragment 0 and every B fragment
         const int na = sa_i == 2 ? 0 : sa_i + 1;
-        read_a(std::integral_constant<int, buf ^ 1>{}, lds + na * SLOT, I0{});
         read_b(lds + (3 + ((t + 1) & 1)) * SLOT, I0{});
+        read_a(std::integral_constant<int, buf ^ 1>{}, lds + na * SLOT, I0{});
         if constexpr (NB == 1) {
           // every wave is past k-tile t: B(t+2) and A(t+3) take the slots of B(t) and A(t).
           // Issued after the reads above, so the compiler cannot move those reads across the
