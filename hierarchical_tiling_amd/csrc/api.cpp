@@ -74,6 +74,7 @@ bool entry_fits(const KernelEntry& e, const gemm_handle_s& h, bool vec_a, bool v
   if ((e.a_kmajor != 0) != h.a.kmajor || (e.b_kmajor != 0) != h.b.kmajor) return false;
   if (e.vec && !(vec_a && vec_b)) return false;
   if (e.skinny && d.M > e.bm) return false;  // the streaming kernel holds all M rows in one tile
+  if (e.skinny && d.ragged_m) return false;  // grouped launches use the tile kernels only
   if (e.vec) {
     // the 16-byte K-major loaders address one tile with 31-bit buffer offsets
     const int64_t sz = dtype_size(e.dtype), lim = int64_t(1) << 31;
@@ -129,7 +130,7 @@ void plan_split(const KernelEntry& e, const gemm_desc& d, int req, int* S, int64
 int choose(const gemm_handle_s& h, bool vec_a, bool vec_b, bool want_vec, int split_req) {
   const KernelEntry* t = table();
   const bool need_split = split_req > 1;
-  for (int i = 0; i < table_size() && !need_split; ++i)
+  for (int i = 0; i < table_size() && !need_split && !h.d.ragged_m; ++i)
     if (t[i].skinny && (t[i].vec != 0) == want_vec && entry_fits(t[i], h, vec_a, vec_b)) return i;
   int best = -1, best_rank = 0;
   int64_t best_area = -1;
@@ -189,7 +190,13 @@ int gemm_create(const gemm_desc* desc, gemm_t* out) {
   // batch (the problem shape's L mode): up to 65535 problems, one per grid z index
   if (d.batch < 0 || d.batch > 65535) return GEMM_ERR_INVALID_ARG;
   const int64_t L = d.batch > 1 ? d.batch : 1;
-  if (L > 1) {
+  if (d.ragged_m != 0 && d.ragged_m != 1) return GEMM_ERR_INVALID_ARG;
+  if (d.ragged_m) {
+    // grouped: the groups share A's, C's and D's rows (device offsets at run time); B moves by
+    // b_stride_l per group.  Row offsets must keep 16-byte rows aligned: A is K-major.
+    if (d.b_stride_l < 0) return GEMM_ERR_LAYOUT;
+    if (d.split_k > 1) return GEMM_ERR_INVALID_ARG;
+  } else if (L > 1) {
     if (d.a_stride_l < 0 || d.b_stride_l < 0 || d.c_stride_l < 0 || d.d_stride_l < 0)
       return GEMM_ERR_LAYOUT;
     // distinct problems must not write the same D; split-K is for single problems
@@ -210,15 +217,17 @@ int gemm_create(const gemm_desc* desc, gemm_t* out) {
   if (rc) return rc;
   rc = classify(d.b_stride_n, d.b_stride_k, &h.b);
   if (rc) return rc;
+  if (d.ragged_m && !h.a.kmajor) return GEMM_ERR_LAYOUT;
   rc = check_arch();
   if (rc) return rc;
 
   // the 16-byte loaders need every problem's operand base 16-byte aligned
   const int64_t isz = dtype_size(d.a_type);
-  const bool va = vec_ok(h.a, d.M, d.K, d.a_type) && (L == 1 || (d.a_stride_l * isz) % 16 == 0);
+  const bool va = vec_ok(h.a, d.M, d.K, d.a_type) &&
+                  (L == 1 || d.ragged_m || (d.a_stride_l * isz) % 16 == 0);
   const bool vb = vec_ok(h.b, d.N, d.K, d.b_type) && (L == 1 || (d.b_stride_l * isz) % 16 == 0);
   const bool need_split = d.split_k > 1;
-  const int split_req = L > 1 ? 1 : d.split_k;  // no automatic split of a batch
+  const int split_req = L > 1 || d.ragged_m ? 1 : d.split_k;  // no split of a batch or group
   h.fallback = choose(h, va, vb, false, split_req);
   if (h.fallback < 0) return GEMM_ERR_NO_CONFIG;
   if (d.force_config >= 0) {
@@ -263,8 +272,9 @@ int gemm_get_info(gemm_t h, gemm_info* info) {
   info->stages = e.stages;
   info->lds_bytes = e.lds_bytes;
   info->split_k = h->split_cfg;
-  info->grid = cdiv(h->d.M, e.bm) * cdiv(h->d.N, e.bn) * h->split_cfg *
-               (h->d.batch > 1 ? h->d.batch : 1);
+  const int64_t groups = h->d.batch > 1 ? h->d.batch : 1;
+  info->grid = h->d.ragged_m ? (cdiv(h->d.M, e.bm) + groups) * cdiv(h->d.N, e.bn)
+                             : cdiv(h->d.M, e.bm) * cdiv(h->d.N, e.bn) * h->split_cfg * groups;
   std::strncpy(info->name, e.name, sizeof(info->name) - 1);
   return GEMM_OK;
 }
@@ -275,8 +285,11 @@ namespace {
 
 int run_impl(gemm_t h, const void* A, const void* B, const void* C, void* D, const void* bias,
              const float* row_scale, const float* col_scale, float alpha, float beta,
-             float scale_a, float scale_b, void* workspace, void* stream) {
+             float scale_a, float scale_b, void* workspace, const int32_t* offsets,
+             void* stream) {
   const gemm_desc& d = h->d;
+  if ((d.ragged_m != 0) != (offsets != nullptr)) return GEMM_ERR_INVALID_ARG;
+  if (offsets && !aligned(offsets, 4)) return GEMM_ERR_MISALIGNED;
   const bool read_c = d.has_c && beta != 0.0f;
   if (!d.has_c && beta != 0.0f) return GEMM_ERR_INVALID_ARG;
   if ((d.has_row_scale != 0) != (row_scale != nullptr) || (d.has_col_scale != 0) != (col_scale != nullptr))
@@ -338,10 +351,20 @@ int run_impl(gemm_t h, const void* A, const void* B, const void* C, void* D, con
     const int64_t span = ((d.M - 1) * d.c_stride_m + (d.N - 1) * d.c_stride_n + 1) * (int64_t)out_sz;
     p.c_span = span < (int64_t(1) << 31) - 64 ? span : 0;
   }
-  const int64_t grid = int64_t(p.tiles_m) * p.tiles_n;
+  int64_t grid = int64_t(p.tiles_m) * p.tiles_n;
+  unsigned gz = (unsigned)p.batch;
+  if (offsets) {
+    // grouped: every group's tiles in one x range, sized for the most tiles any split of the M
+    // rows into `batch` groups can need (each group adds at most one partial tile row)
+    p.offsets = offsets;
+    p.a_row_bytes = h->a.ld * (int64_t)in_sz;
+    p.c_row_bytes = d.c_stride_m * (int64_t)out_sz;
+    p.d_row_bytes = d.d_stride_m * (int64_t)out_sz;
+    grid = (int64_t(p.tiles_m) + p.batch) * p.tiles_n;
+    gz = 1;
+  }
   if (grid <= 0 || grid > INT32_MAX) return GEMM_ERR_INVALID_ARG;
-  hipError_t err = e.launch(p, (hipStream_t)stream,
-                            dim3((unsigned)grid, (unsigned)split, (unsigned)p.batch));
+  hipError_t err = e.launch(p, (hipStream_t)stream, dim3((unsigned)grid, (unsigned)split, gz));
   if (err == hipSuccess && split > 1) err = launch_splitk_reduce(p, d.d_type, (hipStream_t)stream);
   return err == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
 }
@@ -357,14 +380,21 @@ int gemm_run(gemm_t h, const void* A, const void* B, const void* C, void* D, con
   // a handle with scale vectors needs gemm_run_ex to receive them
   if (h->d.has_row_scale || h->d.has_col_scale) return GEMM_ERR_INVALID_ARG;
   return run_impl(h, A, B, C, D, bias, nullptr, nullptr, alpha, beta, scale_a, scale_b,
-                  workspace, stream);
+                  workspace, nullptr, stream);
 }
 
 int gemm_run_ex(gemm_t h, const gemm_args* a, void* stream) {
   if (!h || h->magic != kMagic) return GEMM_ERR_BAD_HANDLE;
   if (!a) return GEMM_ERR_INVALID_ARG;
   return run_impl(h, a->A, a->B, a->C, a->D, a->bias, a->row_scale, a->col_scale, a->alpha,
-                  a->beta, a->scale_a, a->scale_b, a->workspace, stream);
+                  a->beta, a->scale_a, a->scale_b, a->workspace, nullptr, stream);
+}
+
+int gemm_run_grouped(gemm_t h, const gemm_args* a, const int32_t* offsets, void* stream) {
+  if (!h || h->magic != kMagic) return GEMM_ERR_BAD_HANDLE;
+  if (!a || !offsets) return GEMM_ERR_INVALID_ARG;
+  return run_impl(h, a->A, a->B, a->C, a->D, a->bias, a->row_scale, a->col_scale, a->alpha,
+                  a->beta, a->scale_a, a->scale_b, a->workspace, offsets, stream);
 }
 
 int gemm_destroy(gemm_t h) {

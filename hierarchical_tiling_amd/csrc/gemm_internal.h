@@ -32,6 +32,8 @@ struct KParams {
   int batch;               // problems per launch (gridDim.z); 1: one
   int64_t c_span;          // bytes from C's base to the end of its last element when below
                            // 2^31 - 64 (range-checked buffer loads), else 0
+  const int32_t* offsets;  // grouped launch: batch + 1 row offsets (device); nullptr otherwise
+  int64_t a_row_bytes, c_row_bytes, d_row_bytes;  // bytes between consecutive rows (grouped)
   int64_t a_bstride, b_bstride, c_bstride, d_bstride;  // bytes between consecutive problems
 };
 

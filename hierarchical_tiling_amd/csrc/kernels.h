@@ -254,7 +254,7 @@ __device__ __forceinline__ float activate(int act, float v) {
 // (shape, strides, alpha, beta, bias and the scale vectors) is shared.
 __device__ __forceinline__ KParams batch_view(const KParams& p) {
   KParams q = p;
-  if (p.batch > 1) {
+  if (p.batch > 1 && !p.offsets) {
     const int64_t z = blockIdx.z;
     q.A = (const char*)p.A + z * p.a_bstride;
     q.B = (const char*)p.B + z * p.b_bstride;
@@ -262,6 +262,49 @@ __device__ __forceinline__ KParams batch_view(const KParams& p) {
     q.D = (char*)p.D + z * p.d_bstride;
   }
   return q;
+}
+
+// The problem and tile of a workgroup of a tile kernel.  Plain and batched launches: tile
+// blockIdx.x of gridDim.x.  A grouped launch with ragged M (mixture-of-experts: "CUTLASS",
+// Part V, a grouped GEMM in which each expert is one problem of a batch of differently shaped
+// problems) shares A's, C's and D's row space among the groups: group e owns rows
+// [offsets[e], offsets[e+1]) and multiplies them by its own B, and the grid enumerates the tiles
+// of every group in order.  Offsets are clamped into [0, M] and made non-decreasing, so no
+// offset array can send a workgroup outside the operands.  Returns false for a workgroup past
+// the last group's tiles (the grid is sized for the most tiles any split of M can need); such a
+// workgroup exits before its first barrier.
+template <int BM>
+__device__ __forceinline__ bool problem_view(const KParams& in, KParams& p, int& pid, int& nwg) {
+  p = batch_view(in);
+  pid = blockIdx.x;
+  nwg = gridDim.x;
+  if (!in.offsets) return true;
+  const int M = (int)in.M;
+  int64_t base = 0;
+  int lo = 0;
+  for (int e = 0; e < in.batch; ++e) {
+    lo = min(max(in.offsets[e], lo), M);
+    const int hi = min(max(in.offsets[e + 1], lo), M);
+    const int tm = (hi - lo + BM - 1) / BM;
+    const int64_t nt = (int64_t)tm * in.tiles_n;
+    if ((int64_t)blockIdx.x < base + nt) {
+      p.A = (const char*)in.A + lo * in.a_row_bytes;
+      p.B = (const char*)in.B + e * in.b_bstride;
+      if (in.has_c) {
+        p.C = (const char*)in.C + lo * in.c_row_bytes;
+        if (in.c_span > 0) p.c_span = in.c_span - lo * in.c_row_bytes;
+      }
+      p.D = (char*)in.D + lo * in.d_row_bytes;
+      if (in.has_row_scale) p.row_scale = in.row_scale + lo;
+      p.M = hi - lo;
+      p.tiles_m = tm;
+      pid = (int)((int64_t)blockIdx.x - base);
+      nwg = (int)nt;
+      return true;
+    }
+    base += nt;
+  }
+  return false;
 }
 
 // Epilogue of one output element (row, col) from its fp32 sum, for the kernels that finish
@@ -845,7 +888,9 @@ __device__ __forceinline__ void epilogue(const KParams& p, AccT (&acc)[RM][RN], 
 // ------------------------------------------------------------------------------------------
 template <int DT, bool AK, bool BKM, int VEC, int BM, int BN, int BKE, int WM, int WN, int MI>
 __global__ __launch_bounds__(WM * WN * 64, BM * BN <= 128 * 128 && (AK || BKM) ? 2 : 1) void gemm_tiled(const KParams p_) {
-  const KParams p = batch_view(p_);
+  KParams p;
+  int pid, nwg;
+  if (!problem_view<BM>(p_, p, pid, nwg)) return;
   typedef Atom<DT, MI> At;
   typedef typename At::acc_t acc_t;
   constexpr int NT = WM * WN * 64;
@@ -867,7 +912,7 @@ __global__ __launch_bounds__(WM * WN * 64, BM * BN <= 128 * 128 && (AK || BKM) ?
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int tm, tn;
-  tile_of(p, blockIdx.x, gridDim.x, tm, tn);
+  tile_of(p, pid, nwg, tm, tn);
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
   const int wm = wave % WM, wn = wave / WM;
 
@@ -1020,7 +1065,9 @@ __device__ __forceinline__ const char* uniform_ptr(const char* p) {
 
 template <int DT, int BM, int BN, int WM, int WN, int MI, int STAGES, int OCC, int CH>
 __global__ __launch_bounds__(WM * WN * 64, OCC) void gemm_dma(const KParams p_) {
-  const KParams p = batch_view(p_);
+  KParams p;
+  int pid, nwg;
+  if (!problem_view<BM>(p_, p, pid, nwg)) return;
   typedef Atom<DT, MI> At;
   typedef typename At::acc_t acc_t;
   constexpr int NW = WM * WN, NT = NW * 64;
@@ -1045,7 +1092,7 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void gemm_dma(const KParams p_) 
   // the wave index is uniform across a wave; saying so keeps M0 (the DMA's LDS address) scalar
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   int tm, tn;
-  tile_of(p, blockIdx.x, gridDim.x, tm, tn);
+  tile_of(p, pid, nwg, tm, tn);
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
   const int wm = wave % WM, wn = wave / WM;
 
@@ -1189,7 +1236,9 @@ static hipError_t launch_dma(const KParams& p, hipStream_t s, dim3 grid) {
 // ------------------------------------------------------------------------------------------
 template <int DT, int WM, int WN, int MI, int NB>
 __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_ring(const KParams p_) {
-  const KParams p = batch_view(p_);
+  KParams p;
+  int pid, nwg;
+  if (!problem_view<256>(p_, p, pid, nwg)) return;
   typedef Atom<DT, MI> At;
   typedef typename At::acc_t acc_t;
   constexpr int BM = 256, BN = 256, CH = 8;   // 128-byte LDS rows
@@ -1214,7 +1263,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_ring(const KParams p_) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   int tm, tn;
-  tile_of(p, blockIdx.x, gridDim.x, tm, tn);
+  tile_of(p, pid, nwg, tm, tn);
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
   const int wm = wave % WM, wn = wave / WM;
 

@@ -50,7 +50,8 @@ class gemm_desc(ctypes.Structure):
                 ("has_row_scale", ctypes.c_int32), ("has_col_scale", ctypes.c_int32),
                 ("batch", ctypes.c_int64),
                 ("a_stride_l", ctypes.c_int64), ("b_stride_l", ctypes.c_int64),
-                ("c_stride_l", ctypes.c_int64), ("d_stride_l", ctypes.c_int64)]
+                ("c_stride_l", ctypes.c_int64), ("d_stride_l", ctypes.c_int64),
+                ("ragged_m", ctypes.c_int32)]
 
 
 class gemm_args(ctypes.Structure):
@@ -96,6 +97,7 @@ def lib():
         "gemm_run": ([vp, vp, vp, vp, vp, vp, ctypes.c_float, ctypes.c_float, ctypes.c_float,
                       ctypes.c_float, vp, vp], i32),
         "gemm_run_ex": ([vp, ctypes.POINTER(gemm_args), vp], i32),
+        "gemm_run_grouped": ([vp, ctypes.POINTER(gemm_args), vp, vp], i32),
         "gemm_destroy": ([vp], i32),
         "gemm_status_string": ([i32], cp),
         "gemm_get_info": ([vp, ctypes.POINTER(gemm_info)], i32),
@@ -121,7 +123,8 @@ def lib():
     return L
 
 
-EXPORTED = ["gemm_create", "gemm_workspace_size", "gemm_run", "gemm_run_ex", "gemm_destroy",
+EXPORTED = ["gemm_create", "gemm_workspace_size", "gemm_run", "gemm_run_ex", "gemm_run_grouped",
+            "gemm_destroy",
             "gemm_status_string",
             "gemm_get_info", "gemm_num_configs", "gemm_config_name", "ht_layout_eval",
             "ht_layout_size", "ht_layout_table", "ht_layout_coalesce", "ht_layout_compose",
@@ -162,6 +165,13 @@ def gemm_run_ex(h, A, B, C, D, bias, row_scale, col_scale, alpha, beta, scale_a=
     _check(lib().gemm_run_ex(h, ctypes.byref(a), stream), "gemm_run_ex")
 
 
+def gemm_run_grouped(h, A, B, C, D, bias, row_scale, col_scale, offsets, alpha, beta,
+                     scale_a=1.0, scale_b=1.0, stream=None):
+    """Grouped ragged-M run: `offsets` is the device address of batch + 1 int32 row offsets."""
+    a = gemm_args(A, B, C, D, bias, row_scale, col_scale, alpha, beta, scale_a, scale_b, None)
+    _check(lib().gemm_run_grouped(h, ctypes.byref(a), offsets, stream), "gemm_run_grouped")
+
+
 def gemm_destroy(h):
     _check(lib().gemm_destroy(h), "gemm_destroy")
 
@@ -188,7 +198,7 @@ def gemm_config_name(i: int) -> str:
 
 def make_desc(M, N, K, dtype, a_strides, b_strides, d_strides, c_strides=None, has_bias=False,
               act="none", force_config=-1, split_k=0, row_scale=False, col_scale=False, batch=1,
-              batch_strides=(0, 0, 0, 0)) -> gemm_desc:
+              batch_strides=(0, 0, 0, 0), ragged_m=False) -> gemm_desc:
     """a_strides = (stride_m, stride_k); b_strides = (stride_k, stride_n); c/d = (m, n);
     batch_strides = element offsets between consecutive problems of A, B, C, D."""
     out_t = "bf16" if dtype == "e4m3" else dtype
@@ -209,6 +219,7 @@ def make_desc(M, N, K, dtype, a_strides, b_strides, d_strides, c_strides=None, h
     d.has_col_scale = 1 if col_scale else 0
     d.batch = batch
     d.a_stride_l, d.b_stride_l, d.c_stride_l, d.d_stride_l = batch_strides
+    d.ragged_m = 1 if ragged_m else 0
     return d
 
 

@@ -32,6 +32,7 @@
  *                       only for a problem split along K).
  *   gemm_run            enqueues the kernel on the caller's HIP stream; asynchronous.
  *   gemm_run_ex         the same with the arguments in a struct, including the scale vectors.
+ *   gemm_run_grouped    a grouped GEMM whose groups split M by device offsets.
  *   gemm_destroy        frees the handle.
  *
  * Ownership: the caller owns every device buffer (A, B, C, D, bias, row_scale, col_scale,
@@ -115,6 +116,10 @@ typedef struct gemm_desc {
                               /* batch > 1 split_k must be 0 or 1 and no split is made           */
   int64_t a_stride_l, b_stride_l;   /* elements from problem l's A (B) to problem l+1's; >= 0    */
   int64_t c_stride_l, d_stride_l;   /* the same for C and D; d_stride_l != 0 when batch > 1      */
+  int32_t ragged_m;           /* 1: grouped GEMM with ragged M, run by gemm_run_grouped: the     */
+                              /* `batch` groups share A's, C's and D's M rows (and row_scale),   */
+                              /* split by device offsets; B of group e is at B + e*b_stride_l;   */
+                              /* A must be K-major (row-major); a/c/d_stride_l are ignored       */
 } gemm_desc;
 
 typedef struct gemm_handle_s* gemm_t;
@@ -169,6 +174,19 @@ typedef struct gemm_args {
  * handle and GEMM_ERR_MISALIGNED when one is not 4-byte aligned.  gemm_run itself returns
  * GEMM_ERR_INVALID_ARG for a handle with scale vectors. */
 int gemm_run_ex(gemm_t h, const gemm_args* args, void* stream);
+
+/* Grouped GEMM with ragged M, the mixture-of-experts case ("CUTLASS", Part V: a grouped GEMM in
+ * which each expert is one problem of a batch of differently shaped problems).  For a handle
+ * created with ragged_m == 1 and batch == G groups: group e computes rows
+ * [offsets[e], offsets[e+1]) of D from the same rows of A (and C, row_scale) and its own
+ * B_e = B + e * b_stride_l, with shared N, K, bias, col_scale, alpha and beta.  `offsets` is a
+ * device array of G + 1 int32 values, 4-byte aligned, non-decreasing from 0 to M; it is read
+ * on the device, so routing decided on the GPU needs no host round trip.  Out-of-range or
+ * decreasing offsets are clamped into [0, M] and made non-decreasing, so they cannot send the
+ * kernel outside the operands, but the rows they drop are not written.  The other pointers and
+ * scalars are those of gemm_run_ex.  gemm_run and gemm_run_ex refuse a ragged handle, and this
+ * entry point refuses any other (GEMM_ERR_INVALID_ARG). */
+int gemm_run_grouped(gemm_t h, const gemm_args* args, const int32_t* offsets, void* stream);
 
 /* Free a handle.  NULL is accepted. */
 int gemm_destroy(gemm_t h);

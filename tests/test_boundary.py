@@ -243,3 +243,36 @@ def test_batch_fields(fake_gfx950):
     assert b"_vec" not in odd.name and b"_ring" not in odd.name and b"_dma" not in odd.name
     # batch 0 and 1 are one problem
     assert _info(desc(batch=0, **base)).grid == _info(desc(batch=1, **base)).grid
+
+
+def test_grouped_ragged_m_fields(fake_gfx950):
+    """Grouped GEMM with ragged M (mixture-of-experts, "CUTLASS", Part V): A K-major, no split,
+    no skinny kernel, a grid sized for any split of M into the groups, and each run entry point
+    accepts only its own kind of handle (checked before any launch)."""
+    G = 8
+    base = dict(M=1000, N=512, K=256, a_strides=(256, 1), b_strides=(1, 256), d_strides=(512, 1),
+                batch=G, batch_strides=(0, 256 * 512, 0, 0), ragged_m=True)
+    info = _info(desc(**base))
+    assert info.split_k == 1 and info.grid == (-(-1000 // info.bm) + G) * (512 // info.bn)
+    assert status_of(desc(**dict(base, a_strides=(1, 1000)))) == H.GEMM_ERR_LAYOUT
+    assert status_of(desc(**dict(base, split_k=2))) == H.GEMM_ERR_INVALID_ARG
+    d = desc(**base)
+    d.ragged_m = 2
+    assert status_of(d) == H.GEMM_ERR_INVALID_ARG
+    small = _info(H.make_desc(16, 16384, 8192, "e4m3", (8192, 1), (1, 8192), (16384, 1), batch=4,
+                              batch_strides=(0, 16384 * 8192, 0, 0), ragged_m=True))
+    assert b"skinny" not in small.name
+    args = H.gemm_args(256, 256, None, 256, None, None, None, 1.0, 0.0, 1.0, 1.0, None)
+    h = H.gemm_create(desc(**base))
+    try:
+        assert H.lib().gemm_run(h, 256, 256, None, 256, None, 1.0, 0.0, 1.0, 1.0, None, None) == 1
+        assert H.lib().gemm_run_ex(h, ctypes.byref(args), None) == 1
+        assert H.lib().gemm_run_grouped(h, ctypes.byref(args), None, None) == 1
+        assert H.lib().gemm_run_grouped(h, ctypes.byref(args), 1026, None) == H.GEMM_ERR_MISALIGNED
+    finally:
+        H.gemm_destroy(h)
+    h = H.gemm_create(desc())
+    try:   # a plain handle refuses the grouped entry point
+        assert H.lib().gemm_run_grouped(h, ctypes.byref(args), 1024, None) == 1
+    finally:
+        H.gemm_destroy(h)

@@ -205,3 +205,84 @@ def test_batched_problems_match_oracle_each(name):
         err = error(c0.dtype, got, want)
         print(f"{name}[{l}]: {info.name.decode()} err={err:.3e}")
         assert err <= TOL[c0.dtype], (name, l, err)
+
+
+# ---- grouped GEMM with ragged M (mixture-of-experts) -----------------------------------------
+
+GROUP_CASES = {
+    # split ring: an empty group, a one-row group and groups spanning tile boundaries
+    "bf16_ring_moe": dict(sizes=[300, 0, 1, 517, 211], N=264, K=320, dtype="bf16", bias=True,
+                          act="silu", row_scale=True, col_scale=True,
+                          force="bf16_ak_bk_256x256x64_w2x4_m16_ring"),
+    "bf16_lib_moe_c": dict(sizes=[17, 128, 0, 95], N=200, K=128, dtype="bf16", has_c=True,
+                           beta=0.5),
+    # MN-major B per expert (tiled kernel), GELU
+    "f16_rowB_moe": dict(sizes=[40, 77, 10], N=96, K=64, dtype="f16", b_order="row", act="gelu"),
+    # 33 rows in all: the streaming skinny kernel must not be chosen for a grouped launch
+    "e4m3_moe_small": dict(sizes=[3, 9, 0, 14, 2, 5], N=520, K=512, dtype="e4m3", scale_a=0.5,
+                           scale_b=0.25),
+    "f32_moe_c": dict(sizes=[33, 31], N=40, K=50, dtype="f32", dist="uniform", has_c=True,
+                      beta=-1.0, alpha=2.0),
+}
+
+
+@pytest.mark.parametrize("name", list(GROUP_CASES))
+def test_grouped_ragged_m_matches_oracle_per_group(name):
+    kw = dict(GROUP_CASES[name])
+    sizes = kw.pop("sizes")
+    force = kw.pop("force", None)
+    b_order = kw.pop("b_order", "col")
+    G, M = len(sizes), int(sum(sizes))
+    seed = 200 + list(GROUP_CASES).index(name) * 10
+    p = Prepared(Case(M=M, seed=seed, b_order=b_order, **kw))   # A, C, D, bias, scale vectors
+    c = p.case
+    std = c.K ** -0.5 if c.dist == "normal" else None
+    bkw = dict(std=std) if std else {}
+    Bs = [inputs.matrix(seed + 5 + e, c.K, c.N, c.dtype, c.dist, order=b_order, **bkw)
+          for e in range(G)]
+    b_flat, sb = _stack(Bs, 0, 16)
+    offsets = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    ot = OUT_T[c.dtype]
+    tail = 37                                                     # sentinel after D
+    d_rows = M * p.d_strides[0]
+    sentinel = oracle.encode_rne(ot, np.array([np.nan]))[0]
+    d_host = np.full(d_rows + tail, sentinel, dtype=inputs.STORAGE[ot])
+    dB, dD = _dev(b_flat), _dev(d_host)
+    doff = torch.from_numpy(offsets).to("cuda")
+    desc = H.make_desc(M, c.N, c.K, c.dtype, p.A.strides, Bs[0].strides, p.d_strides,
+                       c_strides=p.C.strides if p.C is not None else None, has_bias=c.bias,
+                       act=c.act, force_config=_index(force) if force else -1,
+                       row_scale=c.row_scale, col_scale=c.col_scale, batch=G,
+                       batch_strides=(0, sb, 0, 0), ragged_m=True)
+    g = H.Gemm(desc)
+    info = g.info
+    assert b"skinny" not in info.name and info.split_k == 1
+    assert info.grid == (-(-M // info.bm) + G) * -(-c.N // info.bn)
+    a_ptr = p.dA[0].data_ptr()
+    H.gemm_run_grouped(g.handle, a_ptr, dB.data_ptr(), p.dC.data_ptr() if p.dC is not None else None,
+                       dD.data_ptr(), p.dbias.data_ptr() if p.dbias is not None else None,
+                       p.drs.data_ptr() if p.drs is not None else None,
+                       p.dcs.data_ptr() if p.dcs is not None else None, doff.data_ptr(),
+                       c.alpha, c.beta, c.scale_a, c.scale_b,
+                       torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    d_all = dD.cpu().numpy().view(inputs.STORAGE[ot])
+    assert (d_all[d_rows:] == sentinel).all(), "a group wrote past D"
+    vals = oracle.decode(ot, d_all[:d_rows])
+    ld_a, ld_d = p.A.strides[0], p.d_strides[0]
+    for e in range(G):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi == lo:
+            continue
+        A_e = oracle.Operand(p.A.storage[lo * ld_a:], c.dtype, (hi - lo, c.K), p.A.strides)
+        C_e = (oracle.Operand(p.C.storage[lo * p.C.strides[0]:], ot, (hi - lo, c.N), p.C.strides)
+               if p.C is not None else None)
+        want = oracle.gemm(A_e, op(Bs[e]), C_e, op(p.bias) if p.bias is not None else None,
+                           alpha=c.alpha, beta=c.beta, scale_a=c.scale_a, scale_b=c.scale_b,
+                           act=c.act, row_scale=p.rs[lo:hi] if p.rs is not None else None,
+                           col_scale=p.cs)
+        r = np.arange(lo, hi)[:, None] * ld_d + np.arange(c.N)[None, :] * p.d_strides[1]
+        got = vals[r]
+        err = error(c.dtype, got, want)
+        print(f"{name}[{e}] rows {lo}:{hi}: {info.name.decode()} err={err:.3e}")
+        assert err <= TOL[c.dtype], (name, e, err)
