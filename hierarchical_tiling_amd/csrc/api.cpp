@@ -75,6 +75,9 @@ bool entry_fits(const KernelEntry& e, const gemm_handle_s& h, bool vec_a, bool v
   if (e.vec && !(vec_a && vec_b)) return false;
   if (e.skinny && d.M > e.bm) return false;  // the streaming kernel holds all M rows in one tile
   if (e.skinny && d.ragged_m) return false;  // grouped launches use the tile kernels only
+  // the row reduction reads the output tile repacked in LDS: tile kernels whose LDS holds it
+  if (d.has_row_sumsq && (e.skinny || int64_t(e.bm) * e.bn * dtype_size(d.d_type) > e.lds_bytes))
+    return false;
   if (e.vec) {
     // the 16-byte K-major loaders address one tile with 31-bit buffer offsets
     const int64_t sz = dtype_size(e.dtype), lim = int64_t(1) << 31;
@@ -130,7 +133,7 @@ void plan_split(const KernelEntry& e, const gemm_desc& d, int req, int* S, int64
 int choose(const gemm_handle_s& h, bool vec_a, bool vec_b, bool want_vec, int split_req) {
   const KernelEntry* t = table();
   const bool need_split = split_req > 1;
-  for (int i = 0; i < table_size() && !need_split && !h.d.ragged_m; ++i)
+  for (int i = 0; i < table_size() && !need_split && !h.d.ragged_m && !h.d.has_row_sumsq; ++i)
     if (t[i].skinny && (t[i].vec != 0) == want_vec && entry_fits(t[i], h, vec_a, vec_b)) return i;
   int best = -1, best_rank = 0;
   int64_t best_area = -1;
@@ -191,6 +194,9 @@ int gemm_create(const gemm_desc* desc, gemm_t* out) {
   if (d.batch < 0 || d.batch > 65535) return GEMM_ERR_INVALID_ARG;
   const int64_t L = d.batch > 1 ? d.batch : 1;
   if (d.ragged_m != 0 && d.ragged_m != 1) return GEMM_ERR_INVALID_ARG;
+  if (d.has_row_sumsq != 0 && d.has_row_sumsq != 1) return GEMM_ERR_INVALID_ARG;
+  // the row reduction covers one problem and is not split along K
+  if (d.has_row_sumsq && (L > 1 || d.ragged_m || d.split_k > 1)) return GEMM_ERR_INVALID_ARG;
   if (d.ragged_m) {
     // grouped: the groups share A's, C's and D's rows (device offsets at run time); B moves by
     // b_stride_l per group.  Row offsets must keep 16-byte rows aligned: A is K-major.
@@ -227,7 +233,8 @@ int gemm_create(const gemm_desc* desc, gemm_t* out) {
                   (L == 1 || d.ragged_m || (d.a_stride_l * isz) % 16 == 0);
   const bool vb = vec_ok(h.b, d.N, d.K, d.b_type) && (L == 1 || (d.b_stride_l * isz) % 16 == 0);
   const bool need_split = d.split_k > 1;
-  const int split_req = L > 1 || d.ragged_m ? 1 : d.split_k;  // no split of a batch or group
+  // no split of a batch, a group or a product with a row reduction
+  const int split_req = L > 1 || d.ragged_m || d.has_row_sumsq ? 1 : d.split_k;
   h.fallback = choose(h, va, vb, false, split_req);
   if (h.fallback < 0) return GEMM_ERR_NO_CONFIG;
   if (d.force_config >= 0) {
@@ -255,6 +262,11 @@ int gemm_workspace_size(gemm_t h, size_t* bytes) {
   if (!bytes) return GEMM_ERR_INVALID_ARG;
   const int s = std::max(h->split_cfg, h->split_fb);
   *bytes = s > 1 ? (size_t)s * (size_t)h->d.M * (size_t)h->d.N * sizeof(float) : 0;
+  if (h->d.has_row_sumsq) {
+    // one fp32 partial per (tile column, row), for whichever entry the run uses
+    const int64_t tn = std::max(cdiv(h->d.N, table()[h->cfg].bn), cdiv(h->d.N, table()[h->fallback].bn));
+    *bytes = (size_t)tn * (size_t)h->d.M * sizeof(float);
+  }
   return GEMM_OK;
 }
 
@@ -286,8 +298,10 @@ namespace {
 int run_impl(gemm_t h, const void* A, const void* B, const void* C, void* D, const void* bias,
              const float* row_scale, const float* col_scale, float alpha, float beta,
              float scale_a, float scale_b, void* workspace, const int32_t* offsets,
-             void* stream) {
+             float* row_sumsq, void* stream) {
   const gemm_desc& d = h->d;
+  if ((d.has_row_sumsq != 0) != (row_sumsq != nullptr)) return GEMM_ERR_INVALID_ARG;
+  if (row_sumsq && !aligned(row_sumsq, 4)) return GEMM_ERR_MISALIGNED;
   if ((d.ragged_m != 0) != (offsets != nullptr)) return GEMM_ERR_INVALID_ARG;
   if (offsets && !aligned(offsets, 4)) return GEMM_ERR_MISALIGNED;
   const bool read_c = d.has_c && beta != 0.0f;
@@ -309,7 +323,7 @@ int run_impl(gemm_t h, const void* A, const void* B, const void* C, void* D, con
   const KernelEntry& e = table()[idx];
   const int split = idx == h->cfg ? h->split_cfg : h->split_fb;
   const int64_t kps = idx == h->cfg ? h->kps_cfg : h->kps_fb;
-  if (split > 1 && (!workspace || !aligned(workspace, 16))) return GEMM_ERR_INVALID_ARG;
+  if ((split > 1 || row_sumsq) && (!workspace || !aligned(workspace, 16))) return GEMM_ERR_INVALID_ARG;
 
   KParams p;
   std::memset(&p, 0, sizeof(p));
@@ -338,6 +352,7 @@ int run_impl(gemm_t h, const void* A, const void* B, const void* C, void* D, con
   p.split_k = split;
   p.k_per_split = (int)kps;
   p.workspace = split > 1 ? static_cast<float*>(workspace) : nullptr;
+  p.rsq_ws = row_sumsq ? static_cast<float*>(workspace) : nullptr;
   p.row_scale = row_scale;
   p.col_scale = col_scale;
   p.has_row_scale = row_scale ? 1 : 0;
@@ -366,6 +381,8 @@ int run_impl(gemm_t h, const void* A, const void* B, const void* C, void* D, con
   if (grid <= 0 || grid > INT32_MAX) return GEMM_ERR_INVALID_ARG;
   hipError_t err = e.launch(p, (hipStream_t)stream, dim3((unsigned)grid, (unsigned)split, gz));
   if (err == hipSuccess && split > 1) err = launch_splitk_reduce(p, d.d_type, (hipStream_t)stream);
+  if (err == hipSuccess && row_sumsq)
+    err = launch_row_sumsq_reduce(p.rsq_ws, row_sumsq, d.M, p.tiles_n, (hipStream_t)stream);
   return err == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
 }
 
@@ -377,24 +394,24 @@ int gemm_run(gemm_t h, const void* A, const void* B, const void* C, void* D, con
              float alpha, float beta, float scale_a, float scale_b, void* workspace,
              void* stream) {
   if (!h || h->magic != kMagic) return GEMM_ERR_BAD_HANDLE;
-  // a handle with scale vectors needs gemm_run_ex to receive them
-  if (h->d.has_row_scale || h->d.has_col_scale) return GEMM_ERR_INVALID_ARG;
+  // a handle with scale vectors or a row reduction needs gemm_run_ex to receive them
+  if (h->d.has_row_scale || h->d.has_col_scale || h->d.has_row_sumsq) return GEMM_ERR_INVALID_ARG;
   return run_impl(h, A, B, C, D, bias, nullptr, nullptr, alpha, beta, scale_a, scale_b,
-                  workspace, nullptr, stream);
+                  workspace, nullptr, nullptr, stream);
 }
 
 int gemm_run_ex(gemm_t h, const gemm_args* a, void* stream) {
   if (!h || h->magic != kMagic) return GEMM_ERR_BAD_HANDLE;
   if (!a) return GEMM_ERR_INVALID_ARG;
   return run_impl(h, a->A, a->B, a->C, a->D, a->bias, a->row_scale, a->col_scale, a->alpha,
-                  a->beta, a->scale_a, a->scale_b, a->workspace, nullptr, stream);
+                  a->beta, a->scale_a, a->scale_b, a->workspace, nullptr, a->row_sumsq, stream);
 }
 
 int gemm_run_grouped(gemm_t h, const gemm_args* a, const int32_t* offsets, void* stream) {
   if (!h || h->magic != kMagic) return GEMM_ERR_BAD_HANDLE;
   if (!a || !offsets) return GEMM_ERR_INVALID_ARG;
   return run_impl(h, a->A, a->B, a->C, a->D, a->bias, a->row_scale, a->col_scale, a->alpha,
-                  a->beta, a->scale_a, a->scale_b, a->workspace, offsets, stream);
+                  a->beta, a->scale_a, a->scale_b, a->workspace, offsets, a->row_sumsq, stream);
 }
 
 int gemm_destroy(gemm_t h) {

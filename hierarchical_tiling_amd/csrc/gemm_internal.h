@@ -34,6 +34,7 @@ struct KParams {
                            // 2^31 - 64 (range-checked buffer loads), else 0
   const int32_t* offsets;  // grouped launch: batch + 1 row offsets (device); nullptr otherwise
   int64_t a_row_bytes, c_row_bytes, d_row_bytes;  // bytes between consecutive rows (grouped)
+  float* rsq_ws;           // row sums of squares: one partial per (tile column, row), or nullptr
   int64_t a_bstride, b_bstride, c_bstride, d_bstride;  // bytes between consecutive problems
 };
 
@@ -64,6 +65,9 @@ int table_size();
 // Second kernel of a split-K run: D = act(alpha * sum of the split_k fp32 planes in
 // p.workspace + beta * C + bias), with out_type the type of C, D and bias.
 hipError_t launch_splitk_reduce(const KParams& p, int out_type, hipStream_t s);
+// Sums the per-tile-column partials of the row sums of squares in fixed order: out[m] =
+// sum over t < tiles_n of ws[t * M + m].
+hipError_t launch_row_sumsq_reduce(const float* ws, float* out, int64_t M, int tiles_n, hipStream_t s);
 
 // Output type of a given operand type (htgemm.h type table).
 constexpr int out_dtype(int dt) { return dt == DT_F8 ? DT_BF16 : dt; }

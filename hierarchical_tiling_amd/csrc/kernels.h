@@ -880,6 +880,25 @@ __device__ __forceinline__ void epilogue(const KParams& p, AccT (&acc)[RM][RN], 
           if (col + x < p.N) dst[row * p.d_sm + (col + x) * p.d_sn] = e[x];
       }
     }
+    if (p.rsq_ws) {
+      // Row reduction for the next layer's norm ("CUTLASS", Part IV Stage 5: an epilogue visitor
+      // tree can fuse a reduction): the sum of squares of this tile's stored values of each row,
+      // one wave per row, lanes striding the columns, then a fixed-order butterfly.  The
+      // partial goes to plane (tile column) of the workspace; a second kernel adds the planes.
+      constexpr int NW = NT / 64;
+      const int wave = tid >> 6;
+      for (int lr = wave; lr < BM && m0 + lr < p.M; lr += NW) {
+        float sq = 0.f;
+#pragma unroll
+        for (int c = lane; c < BN; c += 64) {
+          const float v = n0 + c < p.N ? O::from_bits((u32)tile[lr * BN + c]) : 0.f;
+          sq += v * v;
+        }
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) sq += __shfl_xor(sq, o, 64);
+        if (lane == 0) p.rsq_ws[(n0 / BN) * p.M + m0 + lr] = sq;
+      }
+    }
   }
 }
 

@@ -276,3 +276,29 @@ def test_grouped_ragged_m_fields(fake_gfx950):
         assert H.lib().gemm_run_grouped(h, ctypes.byref(args), 1024, None) == 1
     finally:
         H.gemm_destroy(h)
+
+
+def test_row_sumsq_fields(fake_gfx950):
+    """The fused row reduction ("CUTLASS", Part IV Stage 5: a reduction for the next layer's
+    norm): one problem, no split, no skinny kernel, a workspace of one fp32 partial per tile
+    column and row, and gemm_run_ex only (checked before any launch)."""
+    i = _info(desc(M=16, N=1040, K=512, a_strides=(512, 1), b_strides=(1, 512),
+                   d_strides=(1040, 1), row_sumsq=True))
+    assert b"skinny" not in i.name and i.split_k == 1
+    h = H.gemm_create(desc(M=300, N=600, K=256, a_strides=(256, 1), b_strides=(1, 256),
+                           d_strides=(600, 1), row_sumsq=True))
+    try:
+        info = H.gemm_get_info(h)
+        assert H.gemm_workspace_size(h) >= -(-600 // info.bn) * 300 * 4
+        assert H.lib().gemm_run(h, 256, 256, None, 256, None, 1.0, 0.0, 1.0, 1.0, 1024, None) == 1
+        run_ex = lambda ws, rsq: H.lib().gemm_run_ex(h, H.gemm_args(256, 256, None, 256, None, None,
+                                                                    None, 1.0, 0.0, 1.0, 1.0, ws,
+                                                                    rsq), None)
+        assert run_ex(1024, None) == H.GEMM_ERR_INVALID_ARG      # the handle expects the vector
+        assert run_ex(None, 1024) == H.GEMM_ERR_INVALID_ARG      # the workspace is required
+        assert run_ex(1024, 1026) == H.GEMM_ERR_MISALIGNED
+    finally:
+        H.gemm_destroy(h)
+    for bad in (dict(split_k=2), dict(batch=2, batch_strides=(0, 0, 0, 128 * 128)),
+                dict(batch=2, batch_strides=(0, 0, 0, 0), ragged_m=True)):
+        assert status_of(desc(row_sumsq=True, **bad)) == H.GEMM_ERR_INVALID_ARG

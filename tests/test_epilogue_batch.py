@@ -286,3 +286,52 @@ def test_grouped_ragged_m_matches_oracle_per_group(name):
         err = error(c.dtype, got, want)
         print(f"{name}[{e}] rows {lo}:{hi}: {info.name.decode()} err={err:.3e}")
         assert err <= TOL[c.dtype], (name, e, err)
+
+
+# ---- fused row reduction (sum of squares of each stored row, for the next layer's norm) ------
+
+RSQ_CASES = {
+    "bf16_ring_gelu": dict(M=300, N=600, K=320, dtype="bf16", bias=True, act="gelu",
+                           force="bf16_ak_bk_256x256x64_w2x4_m16_ring"),
+    "f16_realign_c": dict(M=131, N=97, K=77, dtype="f16", b_order="row", a_ld=81, b_ld=99,
+                          has_c=True, beta=-1.0),
+    "e4m3_ring_scales": dict(M=264, N=328, K=256, dtype="e4m3", scale_a=0.5, scale_b=0.25,
+                             col_scale=True, force="e4m3_ak_bk_256x256x128_w2x4_m32_ring"),
+    "f32_uniform": dict(M=130, N=300, K=64, dtype="f32", dist="uniform"),
+    # 16 rows would take the streaming skinny kernel, which has no row reduction
+    "bf16_m16": dict(M=16, N=1040, K=512, dtype="bf16"),
+}
+
+
+@pytest.mark.parametrize("name", list(RSQ_CASES))
+def test_row_sum_of_squares_matches_oracle(name):
+    kw = dict(RSQ_CASES[name])
+    if isinstance(kw.get("force"), str):
+        kw["force"] = _index(kw["force"])
+    c = Case(seed=300 + list(RSQ_CASES).index(name), row_sumsq=True, **kw)
+    p = Prepared(c)
+    g, out = p.run()
+    assert b"skinny" not in g.info.name and g.workspace_bytes > 0
+    got_d, _ = p.decode_out(out)
+    rsq = p.rsq.cpu().numpy().astype(np.float64)
+    # against the oracle: its output rounded to the output type, squared and summed in double
+    ot = OUT_T[c.dtype]
+    want_d = oracle.decode(ot, oracle.encode_rne(ot, p.oracle_full()))
+    want = (want_d ** 2).sum(axis=1)
+    err = error("f32" if c.dtype == "f32" else c.dtype, rsq, want)
+    # against the kernel's own stored D (fp32 accumulation of the same squares)
+    own = (got_d ** 2).sum(axis=1)
+    own_err = float(np.abs(rsq - own).max() / max(np.abs(own).max(), 1e-300))
+    print(f"{name}: {g.info.name.decode()} err={err:.3e} vs own D {own_err:.3e}")
+    assert err <= TOL[c.dtype], (name, err)
+    assert own_err <= 1e-5, (name, own_err)
+
+
+def test_row_sum_of_squares_is_exact_on_dyadic_inputs():
+    # dyadic inputs: every D value and every square is exact, and the fp32 sums stay exact
+    c = Case(M=200, N=392, K=128, dtype="bf16", dist="dyadic", seed=310, row_sumsq=True)
+    p = Prepared(c)
+    g, out = p.run()
+    got_d, _ = p.decode_out(out)
+    want = (got_d ** 2).sum(axis=1)
+    assert np.array_equal(p.rsq.cpu().numpy().astype(np.float64), want), g.info.name.decode()
