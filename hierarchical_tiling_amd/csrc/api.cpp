@@ -76,7 +76,8 @@ bool entry_fits(const KernelEntry& e, const gemm_handle_s& h, bool vec_a, bool v
   if (e.skinny && d.M > e.bm) return false;  // the streaming kernel holds all M rows in one tile
   if (e.skinny && d.ragged_m) return false;  // grouped launches use the tile kernels only
   // the row reduction reads the output tile repacked in LDS: tile kernels whose LDS holds it
-  if (d.has_row_sumsq && (e.skinny || int64_t(e.bm) * e.bn * dtype_size(d.d_type) > e.lds_bytes))
+  if ((d.has_row_sumsq || d.has_col_sum) &&
+      (e.skinny || int64_t(e.bm) * e.bn * dtype_size(d.d_type) > e.lds_bytes))
     return false;
   if (e.vec) {
     // the 16-byte K-major loaders address one tile with 31-bit buffer offsets
@@ -99,6 +100,12 @@ bool entry_fits(const KernelEntry& e, const gemm_handle_s& h, bool vec_a, bool v
 }
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Row groups per tile of the column-sum partials (the epilogue's wave split of a tile's rows).
+int col_sum_row_groups(const KernelEntry& e) {
+  const int cg = e.bn / 64;
+  return e.waves >= cg ? e.waves / cg : 1;
+}
 
 // Split along K for entry e: S slices of whole k-tiles ("CUTLASS", Part III: split-K restores
 // occupancy when the output has too few tiles).  req > 1 forces S (at most one slice per
@@ -133,7 +140,8 @@ void plan_split(const KernelEntry& e, const gemm_desc& d, int req, int* S, int64
 int choose(const gemm_handle_s& h, bool vec_a, bool vec_b, bool want_vec, int split_req) {
   const KernelEntry* t = table();
   const bool need_split = split_req > 1;
-  for (int i = 0; i < table_size() && !need_split && !h.d.ragged_m && !h.d.has_row_sumsq; ++i)
+  for (int i = 0; i < table_size() && !need_split && !h.d.ragged_m && !h.d.has_row_sumsq &&
+                  !h.d.has_col_sum; ++i)
     if (t[i].skinny && (t[i].vec != 0) == want_vec && entry_fits(t[i], h, vec_a, vec_b)) return i;
   int best = -1, best_rank = 0;
   int64_t best_area = -1;
@@ -195,8 +203,10 @@ int gemm_create(const gemm_desc* desc, gemm_t* out) {
   const int64_t L = d.batch > 1 ? d.batch : 1;
   if (d.ragged_m != 0 && d.ragged_m != 1) return GEMM_ERR_INVALID_ARG;
   if (d.has_row_sumsq != 0 && d.has_row_sumsq != 1) return GEMM_ERR_INVALID_ARG;
-  // the row reduction covers one problem and is not split along K
-  if (d.has_row_sumsq && (L > 1 || d.ragged_m || d.split_k > 1)) return GEMM_ERR_INVALID_ARG;
+  if (d.has_col_sum != 0 && d.has_col_sum != 1) return GEMM_ERR_INVALID_ARG;
+  // the reductions cover one problem and are not split along K
+  if ((d.has_row_sumsq || d.has_col_sum) && (L > 1 || d.ragged_m || d.split_k > 1))
+    return GEMM_ERR_INVALID_ARG;
   if (d.ragged_m) {
     // grouped: the groups share A's, C's and D's rows (device offsets at run time); B moves by
     // b_stride_l per group.  Row offsets must keep 16-byte rows aligned: A is K-major.
@@ -234,7 +244,7 @@ int gemm_create(const gemm_desc* desc, gemm_t* out) {
   const bool vb = vec_ok(h.b, d.N, d.K, d.b_type) && (L == 1 || (d.b_stride_l * isz) % 16 == 0);
   const bool need_split = d.split_k > 1;
   // no split of a batch, a group or a product with a row reduction
-  const int split_req = L > 1 || d.ragged_m || d.has_row_sumsq ? 1 : d.split_k;
+  const int split_req = L > 1 || d.ragged_m || d.has_row_sumsq || d.has_col_sum ? 1 : d.split_k;
   h.fallback = choose(h, va, vb, false, split_req);
   if (h.fallback < 0) return GEMM_ERR_NO_CONFIG;
   if (d.force_config >= 0) {
@@ -257,16 +267,35 @@ int gemm_create(const gemm_desc* desc, gemm_t* out) {
   return GEMM_OK;
 }
 
+}  // extern "C"
+
+namespace {
+// Workspace of the fused reductions, for whichever entry a run uses: the row partials (one per
+// tile column and row) first, then the column partials (one per tile row, row group and column);
+// *col_off receives the byte offset of the column part.
+size_t reduction_bytes(const gemm_handle_s& h, size_t* col_off) {
+  const KernelEntry& c = table()[h.cfg];
+  const KernelEntry& f = table()[h.fallback];
+  size_t rows = 0, cols = 0;
+  if (h.d.has_row_sumsq)
+    rows = (size_t)std::max(cdiv(h.d.N, c.bn), cdiv(h.d.N, f.bn)) * (size_t)h.d.M * sizeof(float);
+  if (h.d.has_col_sum)
+    cols = (size_t)std::max(cdiv(h.d.M, c.bm) * col_sum_row_groups(c),
+                            cdiv(h.d.M, f.bm) * col_sum_row_groups(f)) * (size_t)h.d.N * sizeof(float);
+  rows = (rows + 255) / 256 * 256;
+  if (col_off) *col_off = rows;
+  return rows + cols;
+}
+}  // namespace
+
+extern "C" {
+
 int gemm_workspace_size(gemm_t h, size_t* bytes) {
   if (!h || h->magic != kMagic) return GEMM_ERR_BAD_HANDLE;
   if (!bytes) return GEMM_ERR_INVALID_ARG;
   const int s = std::max(h->split_cfg, h->split_fb);
   *bytes = s > 1 ? (size_t)s * (size_t)h->d.M * (size_t)h->d.N * sizeof(float) : 0;
-  if (h->d.has_row_sumsq) {
-    // one fp32 partial per (tile column, row), for whichever entry the run uses
-    const int64_t tn = std::max(cdiv(h->d.N, table()[h->cfg].bn), cdiv(h->d.N, table()[h->fallback].bn));
-    *bytes = (size_t)tn * (size_t)h->d.M * sizeof(float);
-  }
+  if (h->d.has_row_sumsq || h->d.has_col_sum) *bytes = reduction_bytes(*h, nullptr);
   return GEMM_OK;
 }
 
@@ -298,10 +327,12 @@ namespace {
 int run_impl(gemm_t h, const void* A, const void* B, const void* C, void* D, const void* bias,
              const float* row_scale, const float* col_scale, float alpha, float beta,
              float scale_a, float scale_b, void* workspace, const int32_t* offsets,
-             float* row_sumsq, void* stream) {
+             float* row_sumsq, float* col_sum, void* stream) {
   const gemm_desc& d = h->d;
   if ((d.has_row_sumsq != 0) != (row_sumsq != nullptr)) return GEMM_ERR_INVALID_ARG;
-  if (row_sumsq && !aligned(row_sumsq, 4)) return GEMM_ERR_MISALIGNED;
+  if ((d.has_col_sum != 0) != (col_sum != nullptr)) return GEMM_ERR_INVALID_ARG;
+  if ((row_sumsq && !aligned(row_sumsq, 4)) || (col_sum && !aligned(col_sum, 4)))
+    return GEMM_ERR_MISALIGNED;
   if ((d.ragged_m != 0) != (offsets != nullptr)) return GEMM_ERR_INVALID_ARG;
   if (offsets && !aligned(offsets, 4)) return GEMM_ERR_MISALIGNED;
   const bool read_c = d.has_c && beta != 0.0f;
@@ -323,7 +354,8 @@ int run_impl(gemm_t h, const void* A, const void* B, const void* C, void* D, con
   const KernelEntry& e = table()[idx];
   const int split = idx == h->cfg ? h->split_cfg : h->split_fb;
   const int64_t kps = idx == h->cfg ? h->kps_cfg : h->kps_fb;
-  if ((split > 1 || row_sumsq) && (!workspace || !aligned(workspace, 16))) return GEMM_ERR_INVALID_ARG;
+  if ((split > 1 || row_sumsq || col_sum) && (!workspace || !aligned(workspace, 16)))
+    return GEMM_ERR_INVALID_ARG;
 
   KParams p;
   std::memset(&p, 0, sizeof(p));
@@ -352,7 +384,10 @@ int run_impl(gemm_t h, const void* A, const void* B, const void* C, void* D, con
   p.split_k = split;
   p.k_per_split = (int)kps;
   p.workspace = split > 1 ? static_cast<float*>(workspace) : nullptr;
+  size_t col_off = 0;
+  if (row_sumsq || col_sum) reduction_bytes(*h, &col_off);
   p.rsq_ws = row_sumsq ? static_cast<float*>(workspace) : nullptr;
+  p.csum_ws = col_sum ? reinterpret_cast<float*>(static_cast<char*>(workspace) + col_off) : nullptr;
   p.row_scale = row_scale;
   p.col_scale = col_scale;
   p.has_row_scale = row_scale ? 1 : 0;
@@ -383,6 +418,9 @@ int run_impl(gemm_t h, const void* A, const void* B, const void* C, void* D, con
   if (err == hipSuccess && split > 1) err = launch_splitk_reduce(p, d.d_type, (hipStream_t)stream);
   if (err == hipSuccess && row_sumsq)
     err = launch_row_sumsq_reduce(p.rsq_ws, row_sumsq, d.M, p.tiles_n, (hipStream_t)stream);
+  if (err == hipSuccess && col_sum)
+    err = launch_row_sumsq_reduce(p.csum_ws, col_sum, d.N, p.tiles_m * col_sum_row_groups(e),
+                                  (hipStream_t)stream);
   return err == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
 }
 
@@ -395,23 +433,26 @@ int gemm_run(gemm_t h, const void* A, const void* B, const void* C, void* D, con
              void* stream) {
   if (!h || h->magic != kMagic) return GEMM_ERR_BAD_HANDLE;
   // a handle with scale vectors or a row reduction needs gemm_run_ex to receive them
-  if (h->d.has_row_scale || h->d.has_col_scale || h->d.has_row_sumsq) return GEMM_ERR_INVALID_ARG;
+  if (h->d.has_row_scale || h->d.has_col_scale || h->d.has_row_sumsq || h->d.has_col_sum)
+    return GEMM_ERR_INVALID_ARG;
   return run_impl(h, A, B, C, D, bias, nullptr, nullptr, alpha, beta, scale_a, scale_b,
-                  workspace, nullptr, nullptr, stream);
+                  workspace, nullptr, nullptr, nullptr, stream);
 }
 
 int gemm_run_ex(gemm_t h, const gemm_args* a, void* stream) {
   if (!h || h->magic != kMagic) return GEMM_ERR_BAD_HANDLE;
   if (!a) return GEMM_ERR_INVALID_ARG;
   return run_impl(h, a->A, a->B, a->C, a->D, a->bias, a->row_scale, a->col_scale, a->alpha,
-                  a->beta, a->scale_a, a->scale_b, a->workspace, nullptr, a->row_sumsq, stream);
+                  a->beta, a->scale_a, a->scale_b, a->workspace, nullptr, a->row_sumsq, a->col_sum,
+                  stream);
 }
 
 int gemm_run_grouped(gemm_t h, const gemm_args* a, const int32_t* offsets, void* stream) {
   if (!h || h->magic != kMagic) return GEMM_ERR_BAD_HANDLE;
   if (!a || !offsets) return GEMM_ERR_INVALID_ARG;
   return run_impl(h, a->A, a->B, a->C, a->D, a->bias, a->row_scale, a->col_scale, a->alpha,
-                  a->beta, a->scale_a, a->scale_b, a->workspace, offsets, a->row_sumsq, stream);
+                  a->beta, a->scale_a, a->scale_b, a->workspace, offsets, a->row_sumsq, a->col_sum,
+                  stream);
 }
 
 int gemm_destroy(gemm_t h) {

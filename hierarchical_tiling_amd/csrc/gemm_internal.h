@@ -35,6 +35,7 @@ struct KParams {
   const int32_t* offsets;  // grouped launch: batch + 1 row offsets (device); nullptr otherwise
   int64_t a_row_bytes, c_row_bytes, d_row_bytes;  // bytes between consecutive rows (grouped)
   float* rsq_ws;           // row sums of squares: one partial per (tile column, row), or nullptr
+  float* csum_ws;          // column sums: one partial per (tile row, row group, column), or nullptr
   int64_t a_bstride, b_bstride, c_bstride, d_bstride;  // bytes between consecutive problems
 };
 
@@ -68,6 +69,8 @@ hipError_t launch_splitk_reduce(const KParams& p, int out_type, hipStream_t s);
 // Sums the per-tile-column partials of the row sums of squares in fixed order: out[m] =
 // sum over t < tiles_n of ws[t * M + m].
 hipError_t launch_row_sumsq_reduce(const float* ws, float* out, int64_t M, int tiles_n, hipStream_t s);
+// The same fixed-order sum for the column sums: out[n] = sum over t < planes of ws[t * N + n].
+// (The row reduction is this with N = M and planes = tiles_n.)
 
 // Output type of a given operand type (htgemm.h type table).
 constexpr int out_dtype(int dt) { return dt == DT_F8 ? DT_BF16 : dt; }

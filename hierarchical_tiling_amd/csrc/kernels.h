@@ -899,6 +899,23 @@ __device__ __forceinline__ void epilogue(const KParams& p, AccT (&acc)[RM][RN], 
         if (lane == 0) p.rsq_ws[(n0 / BN) * p.M + m0 + lr] = sq;
       }
     }
+    if (p.csum_ws) {
+      // Column sums of the stored tile: a wave takes 64 consecutive columns (one per lane, no
+      // bank conflicts) and a group of rows; RG row groups give RG partials per column, written
+      // to plane (tile row) * RG + (row group).
+      constexpr int NW = NT / 64, CG = BN / 64, RG = NW >= CG ? NW / CG : 1;
+      static_assert(BN % 64 == 0 && (NW % CG == 0 || NW < CG), "column groups over the waves");
+      const int wave = tid >> 6;
+      for (int cg = wave % CG; cg < CG; cg += NW >= CG ? CG : NW) {
+        const int rg = NW >= CG ? wave / CG : 0;
+        const int c = cg * 64 + lane;
+        constexpr int RPG = BM / RG;  // rows per group
+        float cs = 0.f;
+        for (int r = rg * RPG; r < (rg + 1) * RPG && m0 + r < p.M; ++r)
+          cs += O::from_bits((u32)tile[r * BN + c]);
+        if (n0 + c < p.N) p.csum_ws[((m0 / BM) * RG + rg) * p.N + n0 + c] = cs;
+      }
+    }
   }
 }
 

@@ -51,7 +51,8 @@ class gemm_desc(ctypes.Structure):
                 ("batch", ctypes.c_int64),
                 ("a_stride_l", ctypes.c_int64), ("b_stride_l", ctypes.c_int64),
                 ("c_stride_l", ctypes.c_int64), ("d_stride_l", ctypes.c_int64),
-                ("ragged_m", ctypes.c_int32), ("has_row_sumsq", ctypes.c_int32)]
+                ("ragged_m", ctypes.c_int32), ("has_row_sumsq", ctypes.c_int32),
+                ("has_col_sum", ctypes.c_int32)]
 
 
 class gemm_args(ctypes.Structure):
@@ -60,7 +61,8 @@ class gemm_args(ctypes.Structure):
                 ("row_scale", ctypes.c_void_p), ("col_scale", ctypes.c_void_p),
                 ("alpha", ctypes.c_float), ("beta", ctypes.c_float),
                 ("scale_a", ctypes.c_float), ("scale_b", ctypes.c_float),
-                ("workspace", ctypes.c_void_p), ("row_sumsq", ctypes.c_void_p)]
+                ("workspace", ctypes.c_void_p), ("row_sumsq", ctypes.c_void_p),
+                ("col_sum", ctypes.c_void_p)]
 
 
 class gemm_info(ctypes.Structure):
@@ -159,11 +161,11 @@ def gemm_run(h, A, B, C, D, bias, alpha, beta, scale_a=1.0, scale_b=1.0, workspa
 
 
 def gemm_run_ex(h, A, B, C, D, bias, row_scale, col_scale, alpha, beta, scale_a=1.0, scale_b=1.0,
-                workspace=None, stream=None, row_sumsq=None):
+                workspace=None, stream=None, row_sumsq=None, col_sum=None):
     """gemm_run with the scale vectors and the row reduction (device addresses or None),
     through the argument struct."""
     a = gemm_args(A, B, C, D, bias, row_scale, col_scale, alpha, beta, scale_a, scale_b, workspace,
-                  row_sumsq)
+                  row_sumsq, col_sum)
     _check(lib().gemm_run_ex(h, ctypes.byref(a), stream), "gemm_run_ex")
 
 
@@ -200,7 +202,8 @@ def gemm_config_name(i: int) -> str:
 
 def make_desc(M, N, K, dtype, a_strides, b_strides, d_strides, c_strides=None, has_bias=False,
               act="none", force_config=-1, split_k=0, row_scale=False, col_scale=False, batch=1,
-              batch_strides=(0, 0, 0, 0), ragged_m=False, row_sumsq=False) -> gemm_desc:
+              batch_strides=(0, 0, 0, 0), ragged_m=False, row_sumsq=False,
+              col_sum=False) -> gemm_desc:
     """a_strides = (stride_m, stride_k); b_strides = (stride_k, stride_n); c/d = (m, n);
     batch_strides = element offsets between consecutive problems of A, B, C, D."""
     out_t = "bf16" if dtype == "e4m3" else dtype
@@ -223,6 +226,7 @@ def make_desc(M, N, K, dtype, a_strides, b_strides, d_strides, c_strides=None, h
     d.a_stride_l, d.b_stride_l, d.c_stride_l, d.d_stride_l = batch_strides
     d.ragged_m = 1 if ragged_m else 0
     d.has_row_sumsq = 1 if row_sumsq else 0
+    d.has_col_sum = 1 if col_sum else 0
     return d
 
 
@@ -242,15 +246,16 @@ class Gemm:
         return gemm_workspace_size(self.handle)
 
     def run(self, A, B, C, D, bias=None, alpha=1.0, beta=0.0, scale_a=1.0, scale_b=1.0,
-            stream=None, workspace=None, row_scale=None, col_scale=None, row_sumsq=None):
-        """gemm_run, or gemm_run_ex when a scale vector or the row reduction is given."""
-        if row_scale is None and col_scale is None and row_sumsq is None:
+            stream=None, workspace=None, row_scale=None, col_scale=None, row_sumsq=None,
+            col_sum=None):
+        """gemm_run, or gemm_run_ex when a scale vector or a reduction output is given."""
+        if row_scale is None and col_scale is None and row_sumsq is None and col_sum is None:
             gemm_run(self.handle, _addr(A), _addr(B), _addr(C), _addr(D), _addr(bias), alpha,
                      beta, scale_a, scale_b, _addr(workspace), _stream(stream))
         else:
             gemm_run_ex(self.handle, _addr(A), _addr(B), _addr(C), _addr(D), _addr(bias),
                         _addr(row_scale), _addr(col_scale), alpha, beta, scale_a, scale_b,
-                        _addr(workspace), _stream(stream), _addr(row_sumsq))
+                        _addr(workspace), _stream(stream), _addr(row_sumsq), _addr(col_sum))
 
     def close(self):
         if self.handle:

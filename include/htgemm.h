@@ -122,6 +122,8 @@ typedef struct gemm_desc {
                               /* A must be K-major (row-major); a/c/d_stride_l are ignored       */
   int32_t has_row_sumsq;      /* 1: gemm_run_ex also writes row_sumsq[m] = sum over n of D(m,n)^2 */
                               /* of the stored (rounded) D; one problem, no split (see gemm_args) */
+  int32_t has_col_sum;        /* 1: gemm_run_ex also writes col_sum[n] = sum over m of D(m,n) of  */
+                              /* the stored D; the same conditions                               */
 } gemm_desc;
 
 typedef struct gemm_handle_s* gemm_t;
@@ -134,7 +136,7 @@ int gemm_create(const gemm_desc* desc, gemm_t* out);
 /* Bytes of device workspace gemm_run needs for this handle: 0 unless the problem is split along
  * K ("CUTLASS", Part III: split-K for outputs with too few tiles to fill the GPU), in which case
  * it is split_k * M * N * 4 (one fp32 plane of partial sums per slice); with has_row_sumsq it
- * is the number of N tiles * M * 4.  The caller owns the
+ * is the number of N tiles * M * 4, and has_col_sum adds (M tiles * row groups) * N * 4.  The caller owns the
  * workspace; its contents after a run are unspecified, and two runs in flight at once need two
  * workspaces. */
 int gemm_workspace_size(gemm_t h, size_t* bytes);
@@ -159,8 +161,10 @@ int gemm_run(gemm_t h, const void* A, const void* B, const void* C, void* D, con
  * row reduction.  row_sumsq receives, for every row m, the sum over n of the squares of the
  * stored D(m, n) (the rounded outputs), accumulated in fp32 in a fixed order; it is the
  * reduction a following RMS normalisation needs ("CUTLASS", Part IV Stage 5: a fused reduction
- * for the next layer's normalisation).  It uses the workspace (gemm_workspace_size bytes, one
- * fp32 partial per tile column and row) and a second kernel on the same stream.
+ * for the next layer's normalisation).  col_sum receives, for every column n, the sum over m of
+ * the stored D(m, n) (the reduction over rows, e.g. a bias gradient when D is an upstream
+ * gradient).  Both are accumulated in fp32 in a fixed order, use the workspace
+ * (gemm_workspace_size bytes of per-tile partials) and one more kernel each on the same stream.
  * row_scale (M floats) must be non-NULL iff the handle has has_row_scale == 1, col_scale (N
  * floats) iff has_col_scale == 1; both are device pointers aligned to 4 bytes and shared by every
  * problem of a batch, like bias.  For a batch, A, B, C and D point at problem 0 and the others
@@ -176,6 +180,7 @@ typedef struct gemm_args {
   float alpha, beta, scale_a, scale_b;
   void* workspace;
   float* row_sumsq;   /* M floats, non-NULL iff the handle has has_row_sumsq == 1 */
+  float* col_sum;     /* N floats, non-NULL iff the handle has has_col_sum == 1 */
 } gemm_args;
 
 /* Enqueue the handle's operation with the arguments in `args` on `stream`; the same checks and

@@ -47,6 +47,7 @@ class Case:
     col_scale: bool = False     # per-column fp32 scale vector (gemm_run_ex)
     scale_dist: str = "uniform"  # "uniform": U[0.25, 2] rows, U[-2, 2] columns; "pow2": 2^[-3..3]
     row_sumsq: bool = False     # also compute the row sums of squares of D (gemm_run_ex)
+    col_sum: bool = False       # also compute the column sums of D (gemm_run_ex)
 
 
 def op(m):
@@ -108,7 +109,8 @@ class Prepared:
         return H.make_desc(c.M, c.N, c.K, c.dtype, self.A.strides, self.B.strides, self.d_strides,
                            c_strides=self.C.strides if self.C is not None else None,
                            has_bias=c.bias, act=c.act, force_config=c.force, split_k=c.split_k,
-                           row_scale=c.row_scale, col_scale=c.col_scale, row_sumsq=c.row_sumsq)
+                           row_scale=c.row_scale, col_scale=c.col_scale, row_sumsq=c.row_sumsq,
+                           col_sum=c.col_sum)
 
     def run(self, g: H.Gemm | None = None, out=None):
         c = self.case
@@ -123,9 +125,11 @@ class Prepared:
                         device=self.device) if ws_bytes else None
         self.rsq = (torch.full((max(c.M, 1),), float("nan"), dtype=torch.float32, device=self.device)
                     if c.row_sumsq else None)
+        self.csum = (torch.full((max(c.N, 1),), float("nan"), dtype=torch.float32, device=self.device)
+                     if c.col_sum else None)
         g.run(a_ptr, self.dB, self.dC, out, self.dbias, alpha=c.alpha, beta=c.beta,
               scale_a=c.scale_a, scale_b=c.scale_b, workspace=ws, row_scale=self.drs,
-              col_scale=self.dcs, row_sumsq=self.rsq)
+              col_scale=self.dcs, row_sumsq=self.rsq, col_sum=self.csum)
         torch.cuda.synchronize()
         return g, out
 

@@ -302,3 +302,29 @@ def test_row_sumsq_fields(fake_gfx950):
     for bad in (dict(split_k=2), dict(batch=2, batch_strides=(0, 0, 0, 128 * 128)),
                 dict(batch=2, batch_strides=(0, 0, 0, 0), ragged_m=True)):
         assert status_of(desc(row_sumsq=True, **bad)) == H.GEMM_ERR_INVALID_ARG
+
+
+def test_col_sum_fields(fake_gfx950):
+    """Column sums of D: the same conditions as the row reduction, and a workspace holding the
+    row partials followed by one fp32 partial per (tile row, row group, column)."""
+    base = dict(M=300, N=600, K=256, a_strides=(256, 1), b_strides=(1, 256), d_strides=(600, 1))
+    h = H.gemm_create(desc(col_sum=True, **base))
+    try:
+        info = H.gemm_get_info(h)
+        groups = max(info.waves // (info.bn // 64), 1)
+        assert H.gemm_workspace_size(h) >= -(-300 // info.bm) * groups * 600 * 4
+        args = H.gemm_args(256, 256, None, 256, None, None, None, 1.0, 0.0, 1.0, 1.0, 1024, None, None)
+        assert H.lib().gemm_run_ex(h, ctypes.byref(args), None) == H.GEMM_ERR_INVALID_ARG
+    finally:
+        H.gemm_destroy(h)
+    only_rows = H.gemm_create(desc(row_sumsq=True, **base))
+    both = H.gemm_create(desc(col_sum=True, row_sumsq=True, **base))
+    try:
+        assert H.gemm_workspace_size(both) > H.gemm_workspace_size(only_rows)
+    finally:
+        H.gemm_destroy(both)
+        H.gemm_destroy(only_rows)
+    assert status_of(desc(col_sum=True, split_k=3, **base)) == H.GEMM_ERR_INVALID_ARG
+    d = desc(**base)
+    d.has_col_sum = 2
+    assert status_of(d) == H.GEMM_ERR_INVALID_ARG

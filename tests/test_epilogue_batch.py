@@ -288,7 +288,7 @@ def test_grouped_ragged_m_matches_oracle_per_group(name):
         assert err <= TOL[c.dtype], (name, e, err)
 
 
-# ---- fused row reduction (sum of squares of each stored row, for the next layer's norm) ------
+# ---- fused reductions: row sums of squares (the next layer's norm) and column sums ------------
 
 RSQ_CASES = {
     "bf16_ring_gelu": dict(M=300, N=600, K=320, dtype="bf16", bias=True, act="gelu",
@@ -335,3 +335,41 @@ def test_row_sum_of_squares_is_exact_on_dyadic_inputs():
     got_d, _ = p.decode_out(out)
     want = (got_d ** 2).sum(axis=1)
     assert np.array_equal(p.rsq.cpu().numpy().astype(np.float64), want), g.info.name.decode()
+
+
+@pytest.mark.parametrize("name", list(RSQ_CASES))
+def test_column_sums_match_oracle(name):
+    kw = dict(RSQ_CASES[name])
+    if isinstance(kw.get("force"), str):
+        kw["force"] = _index(kw["force"])
+    both = list(RSQ_CASES).index(name) % 2 == 0     # every other case asks for both reductions
+    c = Case(seed=320 + list(RSQ_CASES).index(name), col_sum=True, row_sumsq=both, **kw)
+    p = Prepared(c)
+    g, out = p.run()
+    got_d, _ = p.decode_out(out)
+    cs = p.csum.cpu().numpy().astype(np.float64)
+    ot = OUT_T[c.dtype]
+    want_d = oracle.decode(ot, oracle.encode_rne(ot, p.oracle_full()))
+    want = want_d.sum(axis=0)
+    # column sums of signed values can cancel: measure against the sum of magnitudes
+    scale = np.abs(want_d).sum(axis=0).max()
+    err = float(np.abs(cs - want).max() / scale)
+    own = got_d.sum(axis=0)
+    own_err = float(np.abs(cs - own).max() / np.abs(got_d).sum(axis=0).max())
+    print(f"{name}: {g.info.name.decode()} err={err:.3e} vs own D {own_err:.3e}")
+    assert err <= TOL[c.dtype], (name, err)
+    assert own_err <= 1e-5, (name, own_err)
+    if both:
+        rsq = p.rsq.cpu().numpy().astype(np.float64)
+        assert float(np.abs(rsq - (got_d ** 2).sum(axis=1)).max()
+                     / max((got_d ** 2).sum(axis=1).max(), 1e-300)) <= 1e-5
+
+
+def test_column_sums_are_exact_on_dyadic_inputs():
+    c = Case(M=520, N=200, K=128, dtype="bf16", dist="dyadic", seed=330, col_sum=True,
+             row_sumsq=True)
+    p = Prepared(c)
+    g, out = p.run()
+    got_d, _ = p.decode_out(out)
+    assert np.array_equal(p.csum.cpu().numpy().astype(np.float64), got_d.sum(axis=0)), g.info.name.decode()
+    assert np.array_equal(p.rsq.cpu().numpy().astype(np.float64), (got_d ** 2).sum(axis=1))
