@@ -273,6 +273,17 @@ __device__ __forceinline__ KParams batch_view(const KParams& p) {
 // offset array can send a workgroup outside the operands.  Returns false for a workgroup past
 // the last group's tiles (the grid is sized for the most tiles any split of M can need); such a
 // workgroup exits before its first barrier.
+// The kernel argument read again from the kernarg segment (the kernel's only argument, at offset
+// 0).  The pointer passes through an empty asm, so these loads cannot be merged with those made
+// at entry: values needed only after the main loop are loaded there instead of occupying SGPRs
+// across it.
+typedef __attribute__((address_space(4))) const KParams kparams_const_t;
+__device__ __forceinline__ KParams reload_args() {
+  kparams_const_t* q = (kparams_const_t*)__builtin_amdgcn_kernarg_segment_ptr();
+  asm volatile("" : "+s"(q));
+  return *(const KParams*)q;
+}
+
 template <int BM>
 __device__ __forceinline__ bool problem_view(const KParams& in, KParams& p, int& pid, int& nwg) {
   p = batch_view(in);
@@ -1021,10 +1032,12 @@ __global__ __launch_bounds__(WM * WN * 64, BM * BN <= 128 * 128 && (AK || BKM) ?
     }
   }
 
-  if (p.split_k > 1) {
-    store_partial<DT, MI, WTM, WTN>(p, acc, m0, n0, wm, wn, lane);
+  KParams pe;
+  problem_view<BM>(reload_args(), pe, pid, nwg);
+  if (pe.split_k > 1) {
+    store_partial<DT, MI, WTM, WTN>(pe, acc, m0, n0, wm, wn, lane);
   } else {
-    epilogue<DT, MI, BM, BN, WTM, WTN, RM, RN, NT, sizeof(lds)>(p, acc, &lds[0][0], m0, n0, wm, wn,
+    epilogue<DT, MI, BM, BN, WTM, WTN, RM, RN, NT, sizeof(lds)>(pe, acc, &lds[0][0], m0, n0, wm, wn,
                                                                 lane, tid, nk == 0);
   }
 }
@@ -1239,7 +1252,9 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void gemm_dma(const KParams p_) 
     wait_counts<0, true>();  // the zero-filled tiles issued past the end are still in flight
     barrier_nofence();
   }
-  epilogue<DT, MI, BM, BN, WTM, WTN, RM, RN, NT, sizeof(lds)>(p, acc, lds, m0, n0, wm, wn, lane,
+  KParams pe;
+  problem_view<BM>(reload_args(), pe, pid, nwg);
+  epilogue<DT, MI, BM, BN, WTM, WTN, RM, RN, NT, sizeof(lds)>(pe, acc, lds, m0, n0, wm, wn, lane,
                                                               tid, nk == 0);
 }
 
@@ -1261,12 +1276,16 @@ static hipError_t launch_dma(const KParams& p, hipStream_t s, dim3 grid) {
 // hides a wait": the slower of load and compute sets the interval; "CUTLASS", Part IV Stage 4:
 // the multistage ring).  Here the unit of buffering is half a stage (32 KiB, the A or the B
 // tile of one k-tile) and the 5 units of LDS are split into two rings:
-//   * A: 3 slots.  A(t+2) is issued at the start of k-tile t, into the slot A(t-1) released,
-//     and is read at the start of k-tile t+2: two k-tiles of lead.
+//   * A: 3 slots.  A(t+2) is issued during the first substep of k-tile t, into the slot A(t-1)
+//     released, and is read at the start of k-tile t+2: two k-tiles of lead.
 //   * B: 2 slots.  Every wave reads all of its B fragments of k-tile t at the start of the
 //     k-tile; after half of the MFMA substeps a barrier confirms that no wave still reads B(t),
-//     and B(t+2) is issued into that slot: one and a half k-tiles of lead.
+//     and B(t+2) is issued into that slot during the next substep: one and a half k-tiles of
+//     lead.
 // The end-of-tile wait leaves A(t+2) and B(t+2) in flight and needs only A(t+1), B(t+1).
+// With NB = 1 there is no mid-tile barrier: B(t+2) and A(t+3) are issued after the end-of-tile
+// barrier of k-tile t (one and two k-tiles of lead).  The DMA instructions are spread among the
+// MFMAs of the substep that issues them (see `interleave`).
 // Summation order per output is the same as the two-stage DMA kernel's (k-tiles in order,
 // substeps in order), so both produce the same bits.
 // ------------------------------------------------------------------------------------------
@@ -1308,34 +1327,42 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_ring(const KParams p_) {
 
   // this workgroup's K slice (all of K unless the product is split along K)
   const KRange kr = k_range(p);
-  const int64_t K = kr.len;
+  const int64_t K = uniform_i64(kr.len);
   const char* a_tile = uniform_ptr((const char*)p.A + (m0 * p.lda + kr.begin) * SZ);
   const char* b_tile = uniform_ptr((const char*)p.B + (n0 * p.ldb + kr.begin) * SZ);
   const int64_t a_span = uniform_i64(((p.M - m0 - 1) * p.lda + K) * SZ);
   const int64_t b_span = uniform_i64(((min((int64_t)BN, p.N - n0) - 1) * p.ldb + K) * SZ);
-  // lane l of a DMA block fills slot l of a kilobyte: row l/CH, slot l%CH, which holds logical
-  // chunk (l%CH) ^ key(row)
-  auto src_off = [&](int blk, int64_t ld, int& kc) -> uint32_t {
-    const int row = blk * RPB + lane / CH;
-    const int c = (lane % CH) ^ row_key<CH>(row);
-    kc = c * VE;
-    return (uint32_t)(row * ld * SZ + c * 16);
-  };
+  // Lane l of DMA block blk fills slot l of a kilobyte: row blk * RPB + l / CH, slot l % CH,
+  // which holds logical chunk (l % CH) ^ key(row).  A wave's blocks are NW apart, so its rows
+  // differ by multiples of RPB * NW; the key takes row bits 1..3 (2..3 for 64-byte rows), so
+  // with RPB * NW a multiple of 16 every block of the wave has the same chunk per lane, and the
+  // source offsets differ only by a uniform row stride.
+  static_assert((RPB * NW) % 16 == 0, "one chunk per lane across a wave's DMA blocks");
+  const int row0 = wave * RPB + lane / CH;
+  const int kc = ((lane % CH) ^ row_key<CH>(row0)) * VE;  // this lane's first k of its chunk
+  const uint32_t a_off0 = (uint32_t)(row0 * p.lda * SZ + kc * SZ);
+  const uint32_t b_off0 = (uint32_t)(row0 * p.ldb * SZ + kc * SZ);
   const int nk = (int)((K + BKE - 1) / BKE);
 
   // Unit OP (0: A, 1: B) of k-tile t into `slot`.  Units past the end of K are all out of range
   // (zeros) and are issued anyway, so the wait counts stay the same on every k-tile.
   auto dma = [&](auto OP, int t, int slot) {
     const int64_t k0 = (int64_t)t * BKE;
+    // elements of this k-tile inside K (at most BKE; zero or less past the end): the per-lane
+    // tail check is one 32-bit compare against this uniform value
+    const int rem = (int)min(K - k0, (int64_t)BKE);
     const __amdgpu_buffer_rsrc_t r = OP == 0 ? make_rsrc(a_tile, a_span) : make_rsrc(b_tile, b_span);
-    const int64_t ld = OP == 0 ? p.lda : p.ldb;
+    const uint32_t step = (uint32_t)((OP == 0 ? p.lda : p.ldb) * (RPB * NW * SZ));
+    // The base passes through an empty asm so that the per-block sums are formed here, at the
+    // issue, and not hoisted out of the k-loop as DU more live registers per operand.
+    uint32_t off0 = OP == 0 ? a_off0 : b_off0;
+    asm volatile("" : "+v"(off0));
+    const bool in_k = kc < rem;
     u32x4* st = lds + slot * SLOT;
     static_for<DU>([&](auto i) {
       const int blk = wave + NW * i;
-      int kc;
-      const uint32_t off = src_off(blk, ld, kc);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(st + blk * 64), 16,
-                                               k0 + kc < K ? off : 0x80000000u,
+                                               in_k ? off0 + (uint32_t)i * step : kOobOffset,
                                                (int)(k0 * SZ), 0, 0);
     });
   };
@@ -1480,10 +1507,12 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_ring(const KParams p_) {
     wait_counts<0, true>();  // the zero-filled units issued past the end are still in flight
     barrier_nofence();
   }
-  if (p.split_k > 1) {
-    store_partial<DT, MI, WTM, WTN>(p, acc, m0, n0, wm, wn, lane);
+  KParams pe;
+  problem_view<256>(reload_args(), pe, pid, nwg);
+  if (pe.split_k > 1) {
+    store_partial<DT, MI, WTM, WTN>(pe, acc, m0, n0, wm, wn, lane);
   } else {
-    epilogue<DT, MI, BM, BN, WTM, WTN, RM, RN, NT, sizeof(lds)>(p, acc, lds, m0, n0, wm, wn, lane,
+    epilogue<DT, MI, BM, BN, WTM, WTN, RM, RN, NT, sizeof(lds)>(pe, acc, lds, m0, n0, wm, wn, lane,
                                                                 tid, nk == 0);
   }
 }
