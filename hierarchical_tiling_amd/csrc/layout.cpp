@@ -303,6 +303,112 @@ int logical_divide(const Layout& a, const Layout& b, Layout* out) {
   return compose(a, cat, out);
 }
 
+// A flat tuple whose entries are integers or "_" (keep the whole mode), e.g. "(1,_)", "_" or
+// "3"; "X" entries are accepted when `allow_x` (projection steps, "(1,X,1)").  Kept entries are
+// returned as -1, X entries as -2.
+bool parse_slots(const char* text, bool allow_x, std::vector<int64_t>* out) {
+  if (!text) return false;
+  std::string t;
+  for (const char* q = text; *q; ++q)
+    if (*q != ' ' && *q != '\t') t += *q;
+  if (t.empty()) return false;
+  if (t.front() == '(') {
+    if (t.back() != ')') return false;
+    t = t.substr(1, t.size() - 2);
+  }
+  std::vector<int64_t> v;
+  size_t i = 0;
+  while (true) {
+    size_t j = t.find(',', i);
+    std::string e = t.substr(i, j == std::string::npos ? std::string::npos : j - i);
+    if (e == "_") {
+      v.push_back(-1);
+    } else if (e == "X" && allow_x) {
+      v.push_back(-2);
+    } else {
+      if (e.empty() || e.size() > 18) return false;
+      int64_t x = 0;
+      for (char ch : e) {
+        if (ch < '0' || ch > '9') return false;
+        x = x * 10 + (ch - '0');
+      }
+      v.push_back(x);
+    }
+    if (j == std::string::npos) break;
+    i = j + 1;
+  }
+  *out = std::move(v);
+  return true;
+}
+
+// Top-level modes of a layout (a rank-1 layout with a leaf shape is its own single mode).
+std::vector<Layout> modes_of(const Layout& l) {
+  std::vector<Layout> m;
+  if (l.shape.leaf) {
+    m.push_back(l);
+  } else {
+    for (size_t i = 0; i < l.shape.c.size(); ++i) m.push_back({l.shape.c[i], l.stride.c[i]});
+  }
+  return m;
+}
+
+// zipped_divide by a by-mode tiler of tile sizes: mode i < tiles.size() is logically divided by
+// tiles[i]:1 into (tile_i, rest_i); the modes past the tiler stay whole in the rest part.  The
+// result is returned as the list of tile modes and the list of rest modes, in order.  Each tile
+// size must divide its mode's size.
+int zipped_divide_by(const Layout& a, const std::vector<int64_t>& tiles, std::vector<Layout>* tile,
+                     std::vector<Layout>* rest) {
+  std::vector<Layout> m = modes_of(a);
+  if (tiles.size() > m.size()) return HT_ERR_RANGE;
+  tile->clear();
+  rest->clear();
+  for (size_t i = 0; i < m.size(); ++i) {
+    if (i >= tiles.size()) {
+      rest->push_back(m[i]);
+      continue;
+    }
+    if (tiles[i] < 1 || size_of(m[i].shape) % tiles[i] != 0) return HT_ERR_NOT_COMPOSABLE;
+    Layout d;
+    int rc = logical_divide(m[i], Layout{Tup::L(tiles[i]), Tup::L(1)}, &d);
+    if (rc) return rc;
+    tile->push_back({d.shape.c[0], d.stride.c[0]});
+    rest->push_back({d.shape.c[1], d.stride.c[1]});
+  }
+  return HT_OK;
+}
+
+// Slices a list of modes: entries >= 0 fix a (1-D) coordinate of that mode, whose offset is
+// added to *offset; entries -1 keep the mode, appended to `kept`.
+int slice_modes(const std::vector<Layout>& modes, const std::vector<int64_t>& coord,
+                int64_t* offset, std::vector<Layout>* kept) {
+  if (coord.size() != modes.size()) return HT_ERR_RANGE;
+  for (size_t i = 0; i < modes.size(); ++i) {
+    if (coord[i] == -1) {
+      kept->push_back(modes[i]);
+      continue;
+    }
+    if (coord[i] < 0 || coord[i] >= size_of(modes[i].shape)) return HT_ERR_RANGE;
+    int64_t acc = 0;
+    inner(Tup::L(coord[i]), modes[i].shape, modes[i].stride, &acc);
+    *offset += acc;
+  }
+  return HT_OK;
+}
+
+Layout join_modes(const std::vector<Layout>& m) {
+  if (m.empty()) return Layout{Tup::L(1), Tup::L(0)};
+  if (m.size() == 1) return m[0];
+  Layout r;
+  std::vector<Tup> s, d;
+  for (auto& x : m) {
+    s.push_back(x.shape);
+    d.push_back(x.stride);
+  }
+  r.shape = Tup::N(std::move(s));
+  r.stride = Tup::N(std::move(d));
+  return r;
+}
+
 }  // namespace
 
 extern "C" {
@@ -389,6 +495,74 @@ int ht_layout_zipped_divide(const char* a, const char* tiler0, const char* tiler
   z.shape = Tup::N({Tup::N({d0.shape.c[0], d1.shape.c[0]}), Tup::N({d0.shape.c[1], d1.shape.c[1]})});
   z.stride = Tup::N({Tup::N({d0.stride.c[0], d1.stride.c[0]}), Tup::N({d0.stride.c[1], d1.stride.c[1]})});
   return emit(to_string(z), out, cap);
+}
+
+int ht_layout_local_tile(const char* a, const char* tiler, const char* coord, const char* proj,
+                         int64_t* offset, char* out, size_t cap) {
+  Layout la;
+  if (!parse_layout(a, &la) || !positive_shape(la.shape) || !offset) return HT_ERR_PARSE;
+  std::vector<int64_t> tiles, crd;
+  if (!parse_slots(tiler, false, &tiles) || !parse_slots(coord, false, &crd)) return HT_ERR_PARSE;
+  for (int64_t t : tiles)
+    if (t < 1) return HT_ERR_PARSE;  // a tiler entry is a tile size, never "_"
+  if (proj) {
+    // keep the tiler and coordinate entries whose step is 1, drop those marked X
+    std::vector<int64_t> step;
+    if (!parse_slots(proj, true, &step)) return HT_ERR_PARSE;
+    if (step.size() != tiles.size() || step.size() != crd.size()) return HT_ERR_RANGE;
+    std::vector<int64_t> t2, c2;
+    for (size_t i = 0; i < step.size(); ++i) {
+      if (step[i] == -2) continue;
+      if (step[i] != 1) return HT_ERR_PARSE;
+      t2.push_back(tiles[i]);
+      c2.push_back(crd[i]);
+    }
+    tiles.swap(t2);
+    crd.swap(c2);
+  }
+  std::vector<Layout> tile, rest, kept;
+  int rc = zipped_divide_by(la, tiles, &tile, &rest);
+  if (rc) return rc;
+  int64_t off = 0;
+  rc = slice_modes(rest, crd, &off, &kept);
+  if (rc) return rc;
+  std::vector<Layout> res = tile;
+  res.insert(res.end(), kept.begin(), kept.end());
+  rc = emit(to_string(join_modes(res)), out, cap);
+  if (rc) return rc;
+  *offset = off;
+  return HT_OK;
+}
+
+int ht_layout_local_partition(const char* a, const char* thr_shape, int64_t idx, int64_t* offset,
+                              char* out, size_t cap) {
+  Layout la;
+  if (!parse_layout(a, &la) || !positive_shape(la.shape) || !offset) return HT_ERR_PARSE;
+  std::vector<int64_t> thr;
+  if (!parse_slots(thr_shape, false, &thr)) return HT_ERR_PARSE;
+  int64_t nthr = 1;
+  for (int64_t t : thr) {
+    if (t < 1) return HT_ERR_PARSE;
+    nthr *= t;
+  }
+  if (idx < 0 || idx >= nthr) return HT_ERR_RANGE;
+  std::vector<Layout> tile, rest;
+  int rc = zipped_divide_by(la, thr, &tile, &rest);
+  if (rc) return rc;
+  // the thread's coordinate in the thread shape, leftmost mode fastest
+  std::vector<int64_t> tc;
+  for (int64_t t : thr) {
+    tc.push_back(idx % t);
+    idx /= t;
+  }
+  int64_t off = 0;
+  std::vector<Layout> none;
+  rc = slice_modes(tile, tc, &off, &none);
+  if (rc) return rc;
+  rc = emit(to_string(join_modes(rest)), out, cap);
+  if (rc) return rc;
+  *offset = off;
+  return HT_OK;
 }
 
 int64_t ht_swizzle(int64_t offset, int bbits, int mbase, int sshift) {

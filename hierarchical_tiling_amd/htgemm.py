@@ -113,6 +113,8 @@ def lib():
         "ht_layout_complement": ([cp, i64, ctypes.c_char_p, sz], i32),
         "ht_layout_logical_divide": ([cp, cp, ctypes.c_char_p, sz], i32),
         "ht_layout_zipped_divide": ([cp, cp, cp, ctypes.c_char_p, sz], i32),
+        "ht_layout_local_tile": ([cp, cp, cp, cp, ctypes.POINTER(i64), ctypes.c_char_p, sz], i32),
+        "ht_layout_local_partition": ([cp, cp, i64, ctypes.POINTER(i64), ctypes.c_char_p, sz], i32),
         "ht_swizzle": ([i64, i32, i32, i32], i64),
         "ht_tile_plan": ([i64, i64, i64, i32, i64, ctypes.POINTER(ht_tile_stats)], i32),
         "ht_pipeline_time": ([i64, ctypes.c_double, ctypes.c_double], ctypes.c_double),
@@ -131,7 +133,7 @@ EXPORTED = ["gemm_create", "gemm_workspace_size", "gemm_run", "gemm_run_ex", "ge
             "gemm_get_info", "gemm_num_configs", "gemm_config_name", "ht_layout_eval",
             "ht_layout_size", "ht_layout_table", "ht_layout_coalesce", "ht_layout_compose",
             "ht_layout_complement", "ht_layout_logical_divide", "ht_layout_zipped_divide",
-            "ht_swizzle", "ht_tile_plan", "ht_pipeline_time"]
+            "ht_layout_local_tile", "ht_layout_local_partition", "ht_swizzle", "ht_tile_plan", "ht_pipeline_time"]
 
 
 def _check(rc, where):
@@ -344,6 +346,32 @@ def ht_layout_logical_divide(a: str, b: str) -> str:
 
 def ht_layout_zipped_divide(a: str, t0: str, t1: str) -> str:
     return _out_str(lib().ht_layout_zipped_divide, a.encode(), t0.encode(), t1.encode())
+
+
+def _slots(x):
+    if isinstance(x, str):
+        return x
+    return "(" + ",".join("_" if v is None else str(v) for v in x) + ")"
+
+
+def ht_layout_local_tile(a: str, tiler, coord, proj=None):
+    """(offset, layout): the view of `a`'s tile at `coord` (None or "_" keeps a mode)."""
+    buf = ctypes.create_string_buffer(4096)
+    off = ctypes.c_int64()
+    _lcheck(lib().ht_layout_local_tile(a.encode(), _slots(tiler).encode(), _slots(coord).encode(),
+                                       None if proj is None else _slots(proj).encode(),
+                                       ctypes.byref(off), buf, 4096), "ht_layout_local_tile")
+    return off.value, buf.value.decode()
+
+
+def ht_layout_local_partition(a: str, thr_shape, idx: int):
+    """(offset, layout): thread `idx`'s elements of `a` under a thread layout of `thr_shape`."""
+    buf = ctypes.create_string_buffer(4096)
+    off = ctypes.c_int64()
+    _lcheck(lib().ht_layout_local_partition(a.encode(), _slots(thr_shape).encode(), int(idx),
+                                            ctypes.byref(off), buf, 4096),
+            "ht_layout_local_partition")
+    return off.value, buf.value.decode()
 
 
 def ht_swizzle(offset: int, bbits: int, mbase: int, sshift: int) -> int:

@@ -70,6 +70,33 @@ int ht_layout_logical_divide(const char* a, const char* b, char* out, size_t cap
 int ht_layout_zipped_divide(const char* a, const char* tiler0, const char* tiler1, char* out,
                             size_t cap);
 
+/* local_tile: a block's view of a big layout ("CUTLASS, CuTe, and CUDA Tile", "Partitioning:
+ * complement and divide", the local_tile listing; "CUTLASS" (stanleyjacob.dev), Part V).  Two
+ * steps: zipped_divide of `a` by the tiler, then the rest part sliced at `coord`.
+ *   tiler  tile sizes, one per leading mode of `a`, e.g. "(128,64)"; mode i is divided by the
+ *          tile t_i:1 and must have a size that t_i divides (else HT_ERR_NOT_COMPOSABLE); modes
+ *          past the tiler are kept whole in the rest part.
+ *   coord  one entry per mode of `a`: an integer selects that tile (1-D index into the mode's
+ *          rest part), "_" keeps the whole rest mode, e.g. "(1,_)".
+ *   proj   NULL, or a step tuple such as "(1,X,1)" with one entry per tiler and coord entry:
+ *          entries marked X are dropped from both before the two steps.
+ * The result is written as one layout whose modes are the tile modes followed by the kept rest
+ * modes, e.g. (BLK_M,BLK_K,k), plus the base offset of the selected tile in *offset: element c
+ * of the view is at *offset + result(c).  HT_ERR_RANGE for a coordinate outside its mode or a
+ * rank mismatch. */
+int ht_layout_local_tile(const char* a, const char* tiler, const char* coord, const char* proj,
+                         int64_t* offset, char* out, size_t cap);
+
+/* local_partition: a thread's elements of a tile under a thread layout of shape `thr_shape`
+ * (same pages; "A10 - CuTe, CUTLASS & CuTile", "Partitioning Tensors").  The pages give only
+ * the purpose; the reading implemented is zipped_divide of `a` by the thread shape (one entry per
+ * leading mode) with the tile part sliced at thread `idx`'s coordinate (leftmost mode fastest),
+ * keeping every rest mode: thread idx owns one element per tile, at the same place in each.
+ * The result is the rest layout plus *offset, as for local_tile.  HT_ERR_RANGE when idx is not
+ * below the number of threads. */
+int ht_layout_local_partition(const char* a, const char* thr_shape, int64_t idx, int64_t* offset,
+                              char* out, size_t cap);
+
 /* Swizzle<BBits, MBase, SShift>: offset XOR ((offset & mask) >> SShift), where mask is BBits
  * ones starting at bit MBase + SShift ("A10 - CuTe, CUTLASS & CuTile", section 3.4). */
 int64_t ht_swizzle(int64_t offset, int bbits, int mbase, int sshift);

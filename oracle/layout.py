@@ -15,7 +15,13 @@ Sources (page title and section):
 * "A10 - CuTe, CUTLASS & CuTile", section 2: the index is the inner product of the natural
   coordinate with the stride; the hierarchical table of (2,(2,2)):(4,(2,1)) fixes how a single
   integer is split over a nested mode (leftmost sub-mode fastest).
-* Same page, section 3.4: Swizzle<BBits, MBase, SShift> XORs the BBits-wide field that starts
+* "CUTLASS, CuTe, and CUDA Tile", the local_tile listing after "Partitioning: complement and
+  divide": local_tile is zipped_divide by the tiler followed by slicing the rest part with the
+  block's coordinate ("_" keeps a mode); a Step with X entries first drops modes.  "CUTLASS"
+  (stanleyjacob.dev), Part V, and "A10 - CuTe, CUTLASS & CuTile", "Partitioning Tensors":
+  local_partition hands a thread its elements of a tile under a thread layout (the reading used:
+  the tile part is sliced at the thread's coordinate and every rest mode is kept).
+* "A10 - CuTe, CUTLASS & CuTile", section 3.4: Swizzle<BBits, MBase, SShift> XORs the BBits-wide field that starts
   SShift bits above MBase into the field that starts at MBase.
 """
 from __future__ import annotations
@@ -208,3 +214,93 @@ def complement_brute(a, m: int):
     if len(shape) == 1:
         return (shape[0], stride[0])
     return (tuple(shape), tuple(stride))
+
+
+# ---- local_tile / local_partition -----------------------------------------------------------
+
+def _modes(layout):
+    shape, stride = layout
+    if isinstance(shape, tuple):
+        return list(zip(shape, stride))
+    return [(shape, stride)]
+
+
+def divide_mode(mode, t: int):
+    """logical_divide(mode, t:1) by its definition, mode o (t:1, complement(t:1, size(mode))),
+    as a table over the 1-D coordinates x + t*r of the concatenation, and the rest size."""
+    comp = complement_brute((t, 1), size(mode[0]))
+    if comp is None:
+        raise ValueError("no complement")
+    concat = ((t, comp[0]), (1, comp[1]))
+    return compose_table(mode, concat), size(comp[0])
+
+
+def zipped_divide_by(layout, tiles):
+    """zipped_divide by a by-mode tiler of tile sizes: mode i < len(tiles) is divided by
+    tiles[i]:1, later modes stay whole in the rest part.  Returns (tile sizes, rest sizes, f)
+    with f(tile_coord, rest_coord) the offset, each coordinate a tuple of 1-D mode indices."""
+    modes = _modes(layout)
+    if len(tiles) > len(modes):
+        raise ValueError("tiler longer than the layout")
+    tabs, rest = [], []
+    for i, m in enumerate(modes):
+        if i < len(tiles):
+            if size(m[0]) % tiles[i]:
+                raise ValueError("tile size does not divide the mode")
+            tab, nr = divide_mode(m, tiles[i])
+            tabs.append(tab)
+            rest.append(nr)
+        else:
+            rest.append(size(m[0]))
+
+    def f(tc, rc):
+        off = 0
+        for i, m in enumerate(modes):
+            if i < len(tiles):
+                off += tabs[i][tc[i] + tiles[i] * rc[i]]
+            else:
+                off += evaluate(m, rc[i])
+        return off
+
+    return tuple(tiles), tuple(rest), f
+
+
+def local_tile(layout, tiler, coord, proj=None):
+    """Block view: zipped_divide by `tiler`, then the rest part sliced at `coord` (None keeps a
+    mode).  `proj` entries of "X" drop the matching tiler and coord entries first.  Returns
+    (mode sizes of the view, g) with g(c) the offset of view coordinate c (a tuple of 1-D mode
+    indices: the tile modes, then the kept rest modes)."""
+    if proj is not None:
+        keep = [i for i, st in enumerate(proj) if st != "X"]
+        tiler = [tiler[i] for i in keep]
+        coord = [coord[i] for i in keep]
+    tiles, rest, f = zipped_divide_by(layout, tiler)
+    if len(coord) != len(rest):
+        raise ValueError("coordinate rank does not match the rest part")
+    kept = [i for i, c in enumerate(coord) if c is None]
+    for i, c in enumerate(coord):
+        if c is not None and not 0 <= c < rest[i]:
+            raise ValueError("coordinate outside its mode")
+
+    def g(c):
+        rc = list(coord)
+        for j, i in enumerate(kept):
+            rc[i] = c[len(tiles) + j]
+        return f(tuple(c[:len(tiles)]), tuple(rc))
+
+    return tuple(tiles) + tuple(rest[i] for i in kept), g
+
+
+def local_partition(layout, thr_shape, idx: int):
+    """Thread view: zipped_divide by the thread shape, then the tile part sliced at thread idx's
+    coordinate in that shape (leftmost fastest); every rest mode is kept.  Returns (mode sizes, g)
+    as local_tile does."""
+    n = size(tuple(thr_shape))
+    if not 0 <= idx < n:
+        raise ValueError("thread index outside the thread shape")
+    tiles, rest, f = zipped_divide_by(layout, thr_shape)
+    tc = []
+    for t in thr_shape:
+        tc.append(idx % t)
+        idx //= t
+    return tuple(rest), lambda c: f(tuple(tc), tuple(c))

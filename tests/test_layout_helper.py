@@ -1,5 +1,6 @@
 """The library's layout helper (C++, through the C ABI) against the pages' printed values and,
 point by point, against the oracle's definitions (oracle.layout), bit-exact."""
+import itertools
 import json
 import os
 import random
@@ -212,3 +213,81 @@ def test_logical_and_zipped_divide_match_definition():
                 for r1 in range(4):
                     want = L.evaluate(m0, i0 + 4 * r0) + L.evaluate(m1, i1 + 3 * r1)
                     assert L.evaluate(zl, ((i0, i1), (r0, r1))) == want
+
+
+def _view_table(off, text, sizes):
+    """Offsets of a helper view at every coordinate (one 1-D index per top-level mode)."""
+    lay = L.parse(text)
+    out = []
+    for c in itertools.product(*[range(s) for s in sizes]):
+        out.append(off + L.evaluate(lay, c if len(c) > 1 else c[0]))
+    return out
+
+
+def test_local_tile_matches_oracle():
+    rng = random.Random(11)
+    layouts = ["(8,12):(12,1)", "(8,12):(1,8)", "((2,4),12):((1,24),2)", "(8,6,3):(6,1,48)",
+               "(16,(2,6)):(1,(16,32))"]
+    checked = 0
+    for _ in range(300):
+        a = rng.choice(layouts)
+        la = L.parse(a)
+        sz = L.top_sizes(la)
+        t0 = rng.choice([d for d in (1, 2, 4, 8) if sz[0] % d == 0])
+        t1 = rng.choice([d for d in (1, 2, 3, 4, 6, 12) if sz[1] % d == 0])
+        tiler = (t0, t1)
+        rest = (sz[0] // t0, sz[1] // t1) + sz[2:]
+        coord = tuple(None if rng.random() < 0.4 else rng.randrange(r) for r in rest)
+        try:
+            off, text = H.ht_layout_local_tile(a, tiler, coord)
+        except H.LayoutError as e:
+            # composition needs each tile size to divide, or be a multiple of, the size of the
+            # first sub-mode it enters: 3:1 into (2,6) does neither
+            first = [m[0][0] if isinstance(m[0], tuple) else m[0] for m in L._modes(la)]
+            assert e.status == 3 and any(t % f and f % t for t, f in zip(tiler, first))
+            continue
+        sizes, g = L.local_tile(la, tiler, coord)
+        assert L.top_sizes(L.parse(text)) == sizes, (a, tiler, coord, text)
+        want = [g(c) for c in itertools.product(*[range(s) for s in sizes])]
+        assert _view_table(off, text, sizes) == want, (a, tiler, coord, off, text)
+        checked += 1
+    assert checked > 250
+
+
+def test_local_tile_projection_matches_oracle():
+    a, tiler, coord = "(8,6):(6,1)", (4, 3, 2), (1, 2, None)
+    for proj in (("1", "X", "1"), "(1,X,1)"):
+        off, text = H.ht_layout_local_tile(a, tiler, coord, proj)
+        sizes, g = L.local_tile(L.parse(a), tiler, coord, ("1", "X", "1"))
+        assert (off, text) == (6 * 4, "(4,2,3):(6,1,2)")
+        assert _view_table(off, text, sizes) == [g(c) for c in itertools.product(*map(range, sizes))]
+
+
+def test_local_partition_matches_oracle():
+    cases = [("64:1", (32,)), ("(16,64):(64,1)", (2, 16)), ("(8,12):(1,8)", (4, 3)),
+             ("((2,4),6):((6,1),12)", (2, 3)), ("(8,6,3):(6,1,48)", (2, 2))]
+    for a, thr in cases:
+        n = 1
+        for t in thr:
+            n *= t
+        for idx in range(n):
+            off, text = H.ht_layout_local_partition(a, thr, idx)
+            sizes, g = L.local_partition(L.parse(a), thr, idx)
+            assert L.top_sizes(L.parse(text)) == sizes, (a, thr, idx, text)
+            want = [g(c) for c in itertools.product(*[range(s) for s in sizes])]
+            assert _view_table(off, text, sizes) == want, (a, thr, idx)
+
+
+@pytest.mark.parametrize("call,code", [
+    (lambda: H.ht_layout_local_tile("(8,12):(12,1)", (3, 3), (0, None)), 3),   # 3 does not divide 8
+    (lambda: H.ht_layout_local_tile("(8,12):(12,1)", (4, 3), (2, None)), 2),   # 2 row blocks only
+    (lambda: H.ht_layout_local_tile("(8,12):(12,1)", (4, 3), (0,)), 2),        # rank mismatch
+    (lambda: H.ht_layout_local_tile("(8,12):(12,1)", (4, 3, 2), (0, 0, 0), "(1,X)"), 2),
+    (lambda: H.ht_layout_local_tile("(8,12):(12,1)", "(4,_)", (0, 0)), 1),     # "_" is no tile size
+    (lambda: H.ht_layout_local_partition("(8,12):(12,1)", (4, 3), 12), 2),     # threads 0 .. 11
+    (lambda: H.ht_layout_local_partition("(8,12):(12,1)", (3, 3), 0), 3),
+])
+def test_local_tile_and_partition_errors(call, code):
+    with pytest.raises(H.LayoutError) as e:
+        call()
+    assert e.value.status == code

@@ -125,3 +125,115 @@ def test_fragment_closure_method():
     assert p["m"] * p["k"] == p["a_per_lane"] * p["lanes"]
     assert p["k"] * p["n"] == p["b_per_lane"] * p["lanes"]
     assert p["m"] * p["n"] == p["c_per_lane"] * p["lanes"]
+
+
+# ---- local_tile / local_partition ------------------------------------------------------------
+# Pins by direct indexing of the original layout: a block's view must be the original layout
+# read at (block index * tile size + position), whatever the divide machinery does inside.
+
+def _views(sizes):
+    return itertools.product(*[range(s) for s in sizes])
+
+
+TILE_LAYOUTS = [
+    ((8, 12), (12, 1)),               # row-major M x K
+    ((8, 12), (1, 8)),                # column-major
+    (((2, 4), 12), ((1, 24), 2)),     # nested row mode
+    ((8, 6, 3), (6, 1, 48)),          # batched: (M, K, L)
+]
+
+
+@pytest.mark.parametrize("lay", TILE_LAYOUTS, ids=str)
+def test_local_tile_is_the_blocks_slab(lay):
+    modes = L._modes(lay)
+    m0, m1 = modes[0], modes[1]
+    extra = modes[2:]
+    for b0, b1 in ((4, 3), (2, 6), (8, 2)):
+        if L.size(m0[0]) % b0 or L.size(m1[0]) % b1:
+            continue
+        r0, r1 = L.size(m0[0]) // b0, L.size(m1[0]) // b1
+        for bm in range(r0):
+            # keep the k mode whole (and a batch mode whole when present), as the pages' gA does
+            coord = (bm, None) + tuple(None for _ in extra)
+            sizes, g = L.local_tile(lay, (b0, b1), coord)
+            assert sizes == (b0, b1, r1) + tuple(L.size(e[0]) for e in extra)
+            for c in _views(sizes):
+                i, j, kk = c[0], c[1], c[2]
+                want = L.evaluate(m0, bm * b0 + i) + L.evaluate(m1, kk * b1 + j)
+                want += sum(L.evaluate(e, x) for e, x in zip(extra, c[3:]))
+                assert g(c) == want, (lay, b0, b1, bm, c)
+
+
+def test_local_tile_projection_gives_a_b_and_c_tiles():
+    # CTA tiler (BLK_M, BLK_N, BLK_K) with Step<1,X,1> for A, <X,1,1> for B, <1,1,X> for C
+    M, N, K, bM, bN, bK = 8, 12, 6, 4, 3, 2
+    mA, mB, mC = ((M, K), (K, 1)), ((N, K), (K, 1)), ((M, N), (N, 1))
+    m, n = 1, 2
+    tiler, coord = (bM, bN, bK), (m, n, None)
+    sA, gA = L.local_tile(mA, tiler, coord, ("1", "X", "1"))
+    sB, gB = L.local_tile(mB, tiler, coord, ("X", "1", "1"))
+    sC, gC = L.local_tile(mC, tiler, coord, ("1", "1", "X"))
+    assert (sA, sB, sC) == ((bM, bK, K // bK), (bN, bK, K // bK), (bM, bN))
+    for i, kk, k in _views(sA):
+        assert gA((i, kk, k)) == (m * bM + i) * K + k * bK + kk
+    for j, kk, k in _views(sB):
+        assert gB((j, kk, k)) == (n * bN + j) * K + k * bK + kk
+    for i, j in _views(sC):
+        assert gC((i, j)) == (m * bM + i) * N + n * bN + j
+
+
+def test_tile_mode_is_the_composition_with_the_tiler():
+    # the tile part of the divide (coordinate 0 in every rest mode) is A composed mode by mode
+    # with t_i:1 (learn-kernels page: layout<0>(zd) equals composition(a, b))
+    lay = (((2, 4), 12), ((1, 24), 2))
+    sizes, g = L.local_tile(lay, (4, 6), (0, 0))
+    modes = L._modes(lay)
+    t0 = L.compose_table(modes[0], (4, 1))
+    t1 = L.compose_table(modes[1], (6, 1))
+    assert sizes == (4, 6)
+    for i, j in _views(sizes):
+        assert g((i, j)) == t0[i] + t1[j]
+
+
+def test_zipped_divide_order_tile_first():
+    # 128 x 128 by 32 x 32: tile modes (32, 32) first, rest (4, 4) second (the learn-kernels
+    # page's order; the A10 page's listing prints the two parts the other way round)
+    tiles, rest, _ = L.zipped_divide_by(((128, 128), (1, 128)), (32, 32))
+    assert (tiles, rest) == ((32, 32), (4, 4))
+
+
+@pytest.mark.parametrize("lay,thr", [(((64,), (1,)), (32,)), (((16, 64), (64, 1)), (2, 16)),
+                                     (((8, 12), (1, 8)), (4, 3)), ((((2, 4), 6), ((6, 1), 12)), (2, 3))],
+                         ids=str)
+def test_local_partition_covers_each_element_once(lay, thr):
+    nthr = L.size(tuple(thr))
+    seen = []
+    for t in range(nthr):
+        sizes, g = L.local_partition(lay, thr, t)
+        assert L.size(tuple(sizes)) * nthr == L.size(lay[0])
+        seen += [g(c) for c in _views(sizes)]
+    assert sorted(seen) == sorted(L.table(lay))
+
+
+def test_local_partition_is_cyclic_over_threads():
+    # 1-D: thread t of T owns t, t + T, t + 2T, ...
+    for t in range(32):
+        sizes, g = L.local_partition((128, 1), (32,), t)
+        assert sizes == (4,) and [g((r,)) for r in range(4)] == [t + 32 * r for r in range(4)]
+    # 2-D: thread idx = t0 + 2 * t1 of a (2, 16) thread shape owns element (t0 + 2 r0, t1 + 16 r1)
+    lay = ((16, 64), (64, 1))
+    for idx in range(32):
+        t0, t1 = idx % 2, idx // 2
+        sizes, g = L.local_partition(lay, (2, 16), idx)
+        assert sizes == (8, 4)
+        for r0, r1 in _views(sizes):
+            assert g((r0, r1)) == (t0 + 2 * r0) * 64 + (t1 + 16 * r1)
+
+
+def test_local_tile_rejects_bad_arguments():
+    with pytest.raises(ValueError):
+        L.local_tile(((8, 12), (12, 1)), (3, 3), (0, None))       # 3 does not divide 8
+    with pytest.raises(ValueError):
+        L.local_tile(((8, 12), (12, 1)), (4, 3), (2, None))       # only 2 row blocks
+    with pytest.raises(ValueError):
+        L.local_partition(((8, 12), (12, 1)), (4, 3), 12)         # 12 threads: 0 .. 11
