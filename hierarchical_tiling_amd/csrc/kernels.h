@@ -801,12 +801,18 @@ __device__ __forceinline__ void epilogue(const KParams& p, AccT (&acc)[RM][RN], 
   typedef Out<ODT> O;
   typedef typename OutBits<ODT>::T OT;
   constexpr int OSZ = (int)sizeof(OT);
-  constexpr bool REPACK = (size_t)BM * BN * OSZ <= LDS_BYTES;
+  // Rows of the LDS tile are PITCH outputs apart.  With the 16x16 atom one store instruction
+  // writes rows r and r + 4 from the two quarter-waves of each half-wave; 16 bytes of padding per
+  // row put those rows on different banks (with BN * OSZ a multiple of 256 bytes they would
+  // share them).  The padding is used only where the padded tile still fits.
+  constexpr int PAD = 16 / OSZ;
+  constexpr int PITCH = MI == 16 && (size_t)BM * (BN + PAD) * OSZ <= LDS_BYTES ? BN + PAD : BN;
+  constexpr bool REPACK = (size_t)BM * PITCH * OSZ <= LDS_BYTES;
   const bool has_c = p.has_c != 0, has_bias = p.has_bias != 0;
   const bool has_rs = p.has_row_scale != 0, has_cs = p.has_col_scale != 0;
   const int act = p.act;
   const float alpha = p.alpha, beta = p.beta;
-  OT* tile = reinterpret_cast<OT*>(lds);  // BM x BN, row-major (REPACK only)
+  OT* tile = reinterpret_cast<OT*>(lds);  // BM x BN, row-major, rows PITCH apart (REPACK only)
   if (REPACK && no_mainloop) __syncthreads();
   // The stages run one row block of atoms (acc[i][*]) at a time, so only that block's values
   // are live in VGPRs; within a block each stage is one straight-line pass entered on a uniform
@@ -858,7 +864,7 @@ __device__ __forceinline__ void epilogue(const KParams& p, AccT (&acc)[RM][RN], 
         const int lr = wm * WTM + i * MI + acc_row<MI>(lane, r);
         const float v = acc[i][j][(int)r];
         if constexpr (REPACK) {
-          tile[lr * BN + lc] = to_bits(v, std::integral_constant<int, ODT>{});
+          tile[lr * PITCH + lc] = to_bits(v, std::integral_constant<int, ODT>{});
         } else {
           const int64_t row = m0 + lr;
           if (col < p.N && row < p.M) O::store(p.D, row * p.d_sm + col * p.d_sn, v);
@@ -881,7 +887,7 @@ __device__ __forceinline__ void epilogue(const KParams& p, AccT (&acc)[RM][RN], 
       const int lr = q / CPR, lc = (q % CPR) * VO;
       const int64_t row = m0 + lr, col = n0 + lc;
       if (row >= p.M) continue;
-      const u32x4 val = *reinterpret_cast<const u32x4*>(&tile[lr * BN + lc]);
+      const u32x4 val = *reinterpret_cast<const u32x4*>(&tile[lr * PITCH + lc]);
       if (vec_ok && col + VO <= p.N) {
         *reinterpret_cast<u32x4*>(dst + row * p.d_sm + col) = val;
       } else {
@@ -902,7 +908,7 @@ __device__ __forceinline__ void epilogue(const KParams& p, AccT (&acc)[RM][RN], 
         float sq = 0.f;
 #pragma unroll
         for (int c = lane; c < BN; c += 64) {
-          const float v = n0 + c < p.N ? O::from_bits((u32)tile[lr * BN + c]) : 0.f;
+          const float v = n0 + c < p.N ? O::from_bits((u32)tile[lr * PITCH + c]) : 0.f;
           sq += v * v;
         }
 #pragma unroll
@@ -923,7 +929,7 @@ __device__ __forceinline__ void epilogue(const KParams& p, AccT (&acc)[RM][RN], 
         constexpr int RPG = BM / RG;  // rows per group
         float cs = 0.f;
         for (int r = rg * RPG; r < (rg + 1) * RPG && m0 + r < p.M; ++r)
-          cs += O::from_bits((u32)tile[r * BN + c]);
+          cs += O::from_bits((u32)tile[r * PITCH + c]);
         if (n0 + c < p.N) p.csum_ws[((m0 / BM) * RG + rg) * p.N + n0 + c] = cs;
       }
     }
