@@ -42,6 +42,8 @@ struct gemm_handle_s {
   int group_m;
   int split_cfg, split_fb;     // K slices of each entry (1: no split)
   int64_t kps_cfg, kps_fb;     // K elements per slice
+  int tail_tiles, tail_split;  // split tail of the cfg entry (tail_split 1: none)
+  int64_t tail_kps;            // K elements per slice of a tail tile
 };
 
 namespace {
@@ -128,6 +130,38 @@ void plan_split(const KernelEntry& e, const gemm_desc& d, int req, int* S, int64
   const int64_t per = cdiv(nkt, s);  // k-tiles per slice
   *kps = per * e.bk;
   *S = (int)cdiv(nkt, per);           // no empty slice
+}
+
+// Split tail (the data-parallel plus split-K hybrid of Stream-K scheduling; "CUTLASS", Part III:
+// Stream-K evens out work when the tiles do not divide over the processors).  An entry whose LDS
+// allows one workgroup per CU runs 256 tiles per round.  When more than one round is needed and
+// the last is at most half full, the R = tiles mod 256 tiles of that round are split along K into
+// S slices each, about R * S <= 256 workgroups, written as compact fp32 partials and summed in
+// fixed order by a second kernel; the other tiles run whole.  Only when the library decides the
+// split (split_k = 0, one plain product) and no whole-problem split is planned.
+void plan_tail(const KernelEntry& e, const gemm_desc& d, int split_req, int split_whole, int* R,
+               int* S, int64_t* kps) {
+  *R = 0;
+  *S = 1;
+  *kps = d.K;
+  if (split_req != 0 || split_whole > 1 || e.max_split_k <= 1 || e.skinny) return;
+  if (2 * int64_t(e.lds_bytes) <= kLdsBudget) return;  // room for a second workgroup per CU
+  const int64_t tiles = cdiv(d.M, e.bm) * cdiv(d.N, e.bn);
+  const int64_t rem = tiles % 256;
+  if (tiles <= 256 || rem == 0 || rem > 128) return;
+  // Each slice carries fixed costs (pipeline fill, an fp32 partial tile, its share of the sum
+  // kernel).  Measured on MI355X, the split pays from 64 k-tiles per tile with at least 8 per
+  // slice (bf16 4352^2 x 4096: -10 %; at 16 or 32 k-tiles it was 3-11 % slower).
+  const int64_t nkt = cdiv(d.K, e.bk);
+  if (nkt < 64) return;
+  const int64_t s = std::min<int64_t>({256 / rem, nkt / 8, (int64_t)e.max_split_k, 16});
+  if (s < 2) return;
+  const int64_t per = cdiv(nkt, s);  // k-tiles per slice, at least 8
+  const int64_t slices = cdiv(nkt, per);
+  if (slices < 2) return;
+  *R = (int)rem;
+  *S = (int)slices;
+  *kps = per * e.bk;
 }
 
 // Heuristic choice among fitting entries.  A product with M <= 16 is bound by streaming B and
@@ -259,6 +293,7 @@ int gemm_create(const gemm_desc* desc, gemm_t* out) {
   h.group_m = 4;
   plan_split(table()[h.cfg], d, split_req, &h.split_cfg, &h.kps_cfg);
   plan_split(table()[h.fallback], d, split_req, &h.split_fb, &h.kps_fb);
+  plan_tail(table()[h.cfg], d, split_req, h.split_cfg, &h.tail_tiles, &h.tail_split, &h.tail_kps);
 
   gemm_handle_s* p = new (std::nothrow) gemm_handle_s(h);
   if (!p) return GEMM_ERR_INVALID_ARG;
@@ -295,6 +330,11 @@ int gemm_workspace_size(gemm_t h, size_t* bytes) {
   if (!bytes) return GEMM_ERR_INVALID_ARG;
   const int s = std::max(h->split_cfg, h->split_fb);
   *bytes = s > 1 ? (size_t)s * (size_t)h->d.M * (size_t)h->d.N * sizeof(float) : 0;
+  if (h->tail_split > 1) {
+    const KernelEntry& e = table()[h->cfg];
+    *bytes = std::max(*bytes, (size_t)h->tail_split * (size_t)h->tail_tiles * (size_t)e.bm *
+                                  (size_t)e.bn * sizeof(float));
+  }
   if (h->d.has_row_sumsq || h->d.has_col_sum) *bytes = reduction_bytes(*h, nullptr);
   return GEMM_OK;
 }
@@ -317,6 +357,8 @@ int gemm_get_info(gemm_t h, gemm_info* info) {
   info->grid = h->d.ragged_m ? (cdiv(h->d.M, e.bm) + groups) * cdiv(h->d.N, e.bn)
                              : cdiv(h->d.M, e.bm) * cdiv(h->d.N, e.bn) * h->split_cfg * groups;
   std::strncpy(info->name, e.name, sizeof(info->name) - 1);
+  info->tail_tiles = h->tail_split > 1 ? h->tail_tiles : 0;
+  info->tail_split = h->tail_split;
   return GEMM_OK;
 }
 
@@ -354,7 +396,8 @@ int run_impl(gemm_t h, const void* A, const void* B, const void* C, void* D, con
   const KernelEntry& e = table()[idx];
   const int split = idx == h->cfg ? h->split_cfg : h->split_fb;
   const int64_t kps = idx == h->cfg ? h->kps_cfg : h->kps_fb;
-  if ((split > 1 || row_sumsq || col_sum) && (!workspace || !aligned(workspace, 16)))
+  const bool tail = idx == h->cfg && h->tail_split > 1;
+  if ((split > 1 || tail || row_sumsq || col_sum) && (!workspace || !aligned(workspace, 16)))
     return GEMM_ERR_INVALID_ARG;
 
   KParams p;
@@ -380,6 +423,8 @@ int run_impl(gemm_t h, const void* A, const void* B, const void* C, void* D, con
   p.act = d.act;
   p.tiles_m = (int)cdiv(d.M, e.bm);
   p.tiles_n = (int)cdiv(d.N, e.bn);
+  p.tile_bm = e.bm;
+  p.tile_bn = e.bn;
   p.group_m = h->group_m;
   p.split_k = split;
   p.k_per_split = (int)kps;
@@ -414,6 +459,22 @@ int run_impl(gemm_t h, const void* A, const void* B, const void* C, void* D, con
     gz = 1;
   }
   if (grid <= 0 || grid > INT32_MAX) return GEMM_ERR_INVALID_ARG;
+  if (tail) {
+    // whole tiles first (tile order 0 .. grid - R - 1), then the R tail tiles split along K,
+    // then their fixed-order sum and epilogue
+    const int64_t whole = grid - h->tail_tiles;
+    hipError_t err = e.launch(p, (hipStream_t)stream, dim3((unsigned)whole, 1, 1));
+    KParams q = p;
+    q.tile_base = (int)whole;
+    q.tail_tiles = h->tail_tiles;
+    q.split_k = h->tail_split;
+    q.k_per_split = (int)h->tail_kps;
+    q.workspace = static_cast<float*>(workspace);
+    if (err == hipSuccess)
+      err = e.launch(q, (hipStream_t)stream, dim3((unsigned)h->tail_tiles, (unsigned)h->tail_split, 1));
+    if (err == hipSuccess) err = launch_tail_reduce(q, d.d_type, (hipStream_t)stream);
+    return err == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
+  }
   hipError_t err = e.launch(p, (hipStream_t)stream, dim3((unsigned)grid, (unsigned)split, gz));
   if (err == hipSuccess && split > 1) err = launch_splitk_reduce(p, d.d_type, (hipStream_t)stream);
   if (err == hipSuccess && row_sumsq)

@@ -37,6 +37,11 @@ struct KParams {
   float* rsq_ws;           // row sums of squares: one partial per (tile column, row), or nullptr
   float* csum_ws;          // column sums: one partial per (tile row, row group, column), or nullptr
   int64_t a_bstride, b_bstride, c_bstride, d_bstride;  // bytes between consecutive problems
+  // Split tail: the tiles of an incomplete last round, each split along K.  Workgroup x of such
+  // a launch takes tile order index tile_base + (its place in the tile order of gridDim.x
+  // workgroups); with tail_tiles > 0 its fp32 partials go to a compact workspace of
+  // split_k x tail_tiles tiles of tile_bm x tile_bn (plane blockIdx.y, slot blockIdx.x).
+  int tile_base, tail_tiles, tile_bm, tile_bn;
 };
 
 typedef hipError_t (*launch_fn)(const KParams&, hipStream_t, dim3 grid);
@@ -66,6 +71,9 @@ int table_size();
 // Second kernel of a split-K run: D = act(alpha * sum of the split_k fp32 planes in
 // p.workspace + beta * C + bias), with out_type the type of C, D and bias.
 hipError_t launch_splitk_reduce(const KParams& p, int out_type, hipStream_t s);
+// Second kernel of a split tail: for each of the p.tail_tiles tiles, D = act(alpha * sum of its
+// split_k compact fp32 partials + beta * C + bias) over that tile.
+hipError_t launch_tail_reduce(const KParams& p, int out_type, hipStream_t s);
 // Sums the per-tile-column partials of the row sums of squares in fixed order: out[m] =
 // sum over t < tiles_n of ws[t * M + m].
 hipError_t launch_row_sumsq_reduce(const float* ws, float* out, int64_t M, int tiles_n, hipStream_t s);

@@ -196,11 +196,12 @@ template <int MI> __device__ __forceinline__ int acc_row(int l, int r) {
 // Workgroup -> output tile.  Dispatch hands consecutive workgroup ids to the 8 XCDs in turn;
 // the remap gives XCD x the contiguous tile range [start(x), start(x) + count(x)), and tiles
 // are walked GROUP_M tile rows at a time so concurrently resident neighbours share A and B.
+// A split-tail launch covers the tile order from p.tile_base on.
 // ------------------------------------------------------------------------------------------
 __device__ __forceinline__ void tile_of(const KParams& p, int pid, int nwg, int& tm, int& tn) {
   const int per = nwg >> 3, extra = nwg & 7;
   const int xcd = pid & 7, local = pid >> 3;
-  const int t = xcd * per + min(xcd, extra) + local;
+  const int t = xcd * per + min(xcd, extra) + local + p.tile_base;
   const int width = p.group_m * p.tiles_n;
   const int group = t / width;
   const int first = group * p.group_m;
@@ -353,17 +354,22 @@ __device__ __forceinline__ const void* advance_k(const void* base, int64_t ld, i
   return (const char*)base + (KMAJ ? k : k * ld) * Ty<DT>::SZ;
 }
 // raw fp32 partial sums of this workgroup's tile into plane blockIdx.y of the workspace
-template <int DT, int MI, int WTM, int WTN, int RM, int RN, class AccT>
+template <int DT, int MI, int BM, int BN, int WTM, int WTN, int RM, int RN, class AccT>
 __device__ __forceinline__ void store_partial(const KParams& p, const AccT (&acc)[RM][RN],
                                               int64_t m0, int64_t n0, int wm, int wn, int lane) {
   typedef Atom<DT, MI> At;
-  float* w = p.workspace + (int64_t)blockIdx.y * p.M * p.N;
+  // whole-problem split: plane blockIdx.y of M x N; split tail: the compact BM x BN slot of
+  // tail workgroup blockIdx.x in plane blockIdx.y
+  const bool tail = p.tail_tiles > 0;
+  float* w = tail ? p.workspace + ((int64_t)blockIdx.y * p.tail_tiles + blockIdx.x) * (BM * BN)
+                  : p.workspace + (int64_t)blockIdx.y * p.M * p.N;
   static_for<RM>([&](auto i) {
     static_for<RN>([&](auto j) {
       const int64_t col = n0 + wn * WTN + j * MI + (lane % MI);
       static_for<At::NACC>([&](auto r) {
         const int64_t row = m0 + wm * WTM + i * MI + acc_row<MI>(lane, r);
-        if (row < p.M && col < p.N) w[row * p.N + col] = acc[i][j][(int)r];
+        if (row < p.M && col < p.N)
+          w[tail ? (row - m0) * BN + (col - n0) : row * p.N + col] = acc[i][j][(int)r];
       });
     });
   });
@@ -378,6 +384,26 @@ __global__ __launch_bounds__(256) void gemm_splitk_reduce(const KParams p_) {
     const int64_t row = e / p.N, col = e - row * p.N;
     float sum = 0.f;
     for (int s = 0; s < p.split_k; ++s) sum += p.workspace[s * MN + e];
+    O::store(p.D, row * p.d_sm + col * p.d_sn, finish_elem<ODT>(p, row, col, sum));
+  }
+}
+
+// Second kernel of a split tail.  Block (x, y) takes tail tile x -- found with the same tile
+// order as tail workgroup x of the first kernel -- and elements y, y + gridDim.y, ... of it:
+// D = act(alpha * sum_s W[s] + beta * C + bias), the split_k partials added in order.
+template <int ODT>
+__global__ __launch_bounds__(256) void gemm_tail_reduce(const KParams p) {
+  typedef Out<ODT> O;
+  int tm, tn;
+  tile_of(p, blockIdx.x, gridDim.x, tm, tn);
+  const int64_t m0 = (int64_t)tm * p.tile_bm, n0 = (int64_t)tn * p.tile_bn;
+  const int64_t area = (int64_t)p.tile_bm * p.tile_bn, plane = area * p.tail_tiles;
+  const float* w = p.workspace + (int64_t)blockIdx.x * area;
+  for (int64_t e = (int64_t)blockIdx.y * 256 + threadIdx.x; e < area; e += (int64_t)gridDim.y * 256) {
+    const int64_t row = m0 + e / p.tile_bn, col = n0 + e % p.tile_bn;
+    if (row >= p.M || col >= p.N) continue;
+    float sum = 0.f;
+    for (int s = 0; s < p.split_k; ++s) sum += w[s * plane + e];
     O::store(p.D, row * p.d_sm + col * p.d_sn, finish_elem<ODT>(p, row, col, sum));
   }
 }
@@ -1041,7 +1067,7 @@ __global__ __launch_bounds__(WM * WN * 64, BM * BN <= 128 * 128 && (AK || BKM) ?
   KParams pe;
   problem_view<BM>(reload_args(), pe, pid, nwg);
   if (pe.split_k > 1) {
-    store_partial<DT, MI, WTM, WTN>(pe, acc, m0, n0, wm, wn, lane);
+    store_partial<DT, MI, BM, BN, WTM, WTN>(pe, acc, m0, n0, wm, wn, lane);
   } else {
     epilogue<DT, MI, BM, BN, WTM, WTN, RM, RN, NT, sizeof(lds)>(pe, acc, &lds[0][0], m0, n0, wm, wn,
                                                                 lane, tid, nk == 0);
@@ -1516,7 +1542,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_ring(const KParams p_) {
   KParams pe;
   problem_view<256>(reload_args(), pe, pid, nwg);
   if (pe.split_k > 1) {
-    store_partial<DT, MI, WTM, WTN>(pe, acc, m0, n0, wm, wn, lane);
+    store_partial<DT, MI, BM, BN, WTM, WTN>(pe, acc, m0, n0, wm, wn, lane);
   } else {
     epilogue<DT, MI, BM, BN, WTM, WTN, RM, RN, NT, sizeof(lds)>(pe, acc, lds, m0, n0, wm, wn, lane,
                                                                 tid, nk == 0);

@@ -1,5 +1,5 @@
-// reduce.hip -- second kernels: the split-K reduction, and the fixed-order sum of the row
-// sums-of-squares partials.
+// reduce.hip -- second kernels: the split-K and split-tail reductions, and the fixed-order sum of
+// the row sums-of-squares partials.
 #include "kernels.h"
 
 namespace htk {
@@ -12,6 +12,19 @@ hipError_t launch_splitk_reduce(const KParams& p, int out_type, hipStream_t s) {
     case DT_F32: hipLaunchKernelGGL(gemm_splitk_reduce<DT_F32>, dim3(blocks), dim3(256), 0, s, p); break;
     case DT_F16: hipLaunchKernelGGL(gemm_splitk_reduce<DT_F16>, dim3(blocks), dim3(256), 0, s, p); break;
     case DT_BF16: hipLaunchKernelGGL(gemm_splitk_reduce<DT_BF16>, dim3(blocks), dim3(256), 0, s, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_tail_reduce(const KParams& p, int out_type, hipStream_t s) {
+  if (p.tail_tiles <= 0) return hipSuccess;
+  const int64_t area = (int64_t)p.tile_bm * p.tile_bn;
+  const dim3 grid((unsigned)p.tail_tiles, (unsigned)min((area + 255) / 256, (int64_t)32));
+  switch (out_type) {
+    case DT_F32: hipLaunchKernelGGL(gemm_tail_reduce<DT_F32>, grid, dim3(256), 0, s, p); break;
+    case DT_F16: hipLaunchKernelGGL(gemm_tail_reduce<DT_F16>, grid, dim3(256), 0, s, p); break;
+    case DT_BF16: hipLaunchKernelGGL(gemm_tail_reduce<DT_BF16>, grid, dim3(256), 0, s, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

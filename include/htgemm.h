@@ -109,7 +109,9 @@ typedef struct gemm_desc {
   int64_t d_stride_m, d_stride_n;   /* D(m, n)                                                    */
   int32_t force_config;       /* -1: choose from the tile table; else a table index (tuning)     */
   int32_t split_k;            /* split of K across workgroups per output tile: 0 = automatic,    */
-                              /* 1 = never, 2..64 = that many slices (capped at one per k-tile)  */
+                              /* 1 = never, 2..64 = that many slices (capped at one per k-tile); */
+                              /* automatic also splits the tiles of a mostly idle last round     */
+                              /* (the split tail, see gemm_workspace_size)                       */
   int32_t has_row_scale;      /* 1: gemm_run_ex multiplies row m of the product by row_scale[m]  */
   int32_t has_col_scale;      /* 1: gemm_run_ex multiplies column n by col_scale[n]              */
   int64_t batch;              /* problems of this shape per call, 0..65535 (0 and 1: one); with  */
@@ -135,7 +137,9 @@ int gemm_create(const gemm_desc* desc, gemm_t* out);
 
 /* Bytes of device workspace gemm_run needs for this handle: 0 unless the problem is split along
  * K ("CUTLASS", Part III: split-K for outputs with too few tiles to fill the GPU), in which case
- * it is split_k * M * N * 4 (one fp32 plane of partial sums per slice); with has_row_sumsq it
+ * it is split_k * M * N * 4 (one fp32 plane of partial sums per slice).  A split tail (the
+ * Stream-K idea, same Part: the tiles of a last round that would leave most CUs idle are each
+ * split along K) needs tail_split * tail_tiles * bm * bn * 4 (gemm_info).  With has_row_sumsq it
  * is the number of N tiles * M * 4, and has_col_sum adds (M tiles * row groups) * N * 4.  The caller owns the
  * workspace; its contents after a run are unspecified, and two runs in flight at once need two
  * workspaces. */
@@ -151,7 +155,8 @@ int gemm_workspace_size(gemm_t h, size_t* bytes);
  * narrow-load kernel when a pointer is not 16-byte aligned.  `workspace` is a device buffer of
  * gemm_workspace_size() bytes, 16-byte aligned (GEMM_ERR_INVALID_ARG if it is needed and missing;
  * ignored when that size is 0).  A split run is two kernels on `stream`: the K slices, then their
- * fixed-order sum and the epilogue.  Returns after the launches are queued; launch failures
+ * fixed-order sum and the epilogue; a split-tail run is three: the whole tiles, the tail tiles'
+ * K slices, then their fixed-order sum and epilogue.  Returns after the launches are queued; launch failures
  * return GEMM_ERR_LAUNCH. */
 int gemm_run(gemm_t h, const void* A, const void* B, const void* C, void* D, const void* bias,
              float alpha, float beta, float scale_a, float scale_b, void* workspace,
@@ -219,6 +224,8 @@ typedef struct gemm_info {
   int32_t split_k;        /* workgroups sharing one output tile along K (1: none)              */
   int64_t grid;           /* workgroups per launch (all problems of a batch)                    */
   char name[96];          /* kernel name                                                        */
+  int32_t tail_tiles;     /* tiles of an incomplete last round run split along K (0: none)      */
+  int32_t tail_split;     /* K slices of each such tile (1: none)                               */
 } gemm_info;
 
 int gemm_get_info(gemm_t h, gemm_info* info);
