@@ -114,6 +114,9 @@ int col_sum_row_groups(const KernelEntry& e) {
 // k-tile); req == 1 never splits; req == 0 (automatic) splits an output of fewer than 256 tiles
 // when K is long (at least 64 k-tiles) into enough slices for about 256 workgroups, at most 16,
 // each slice keeping at least 8 k-tiles.
+// An entry whose LDS leaves no room for a second workgroup runs one per CU: 256 make a round.
+bool one_per_cu(const KernelEntry& e) { return 2 * int64_t(e.lds_bytes) > kLdsBudget; }
+
 void plan_split(const KernelEntry& e, const gemm_desc& d, int req, int* S, int64_t* kps) {
   *S = 1;
   *kps = d.K;
@@ -123,7 +126,9 @@ void plan_split(const KernelEntry& e, const gemm_desc& d, int req, int* S, int64
   int64_t s = req;
   if (req == 0) {
     if (tiles >= 256 || nkt < 64) return;
-    s = std::min<int64_t>({cdiv(256, tiles), nkt / 8, 16});
+    // slices that fill one round: for one workgroup per CU no more than 256 / tiles (one more
+    // would start a second round: 1536^2 x 8192 ring, 8 slices 0.082 ms, 7 slices 0.060 ms)
+    s = std::min<int64_t>({one_per_cu(e) ? 256 / tiles : cdiv(256, tiles), nkt / 8, 16});
   }
   s = std::min<int64_t>({s, nkt, (int64_t)e.max_split_k});
   if (s <= 1) return;
@@ -167,10 +172,10 @@ void plan_tail(const KernelEntry& e, const gemm_desc& d, int split_req, int spli
 // Heuristic choice among fitting entries.  A product with M <= 16 is bound by streaming B and
 // takes the skinny kernel when one fits.  Otherwise each entry is counted with the split-K plan
 // it would get (plan_split) and the choice is the largest tile whose workgroups (tiles x slices)
-// still number at least 256 (one per CU), ties broken by the measured rank -- the entry's
-// one-round rank when all its workgroups run at once (at most 256), else its rank -- or, when
-// no tile reaches 256 workgroups, the entry with the most workgroups.  A forced split
-// (split_req > 1) admits only entries that can split.
+// still fill the GPU (at least 256, or one round over half full for a one-per-CU kernel), ties
+// broken by the measured rank -- the entry's one-round rank when all its workgroups run at once
+// (at most 256), else its rank -- or, when no tile fills it, the entry with the most
+// workgroups.  A forced split (split_req > 1) admits only entries that can split.
 int choose(const gemm_handle_s& h, bool vec_a, bool vec_b, bool want_vec, int split_req) {
   const KernelEntry* t = table();
   const bool need_split = split_req > 1;
@@ -192,7 +197,13 @@ int choose(const gemm_handle_s& h, bool vec_a, bool vec_b, bool want_vec, int sp
     const int64_t wg = cdiv(h.d.M, e.bm) * cdiv(h.d.N, e.bn) * slices;
     const int64_t area = int64_t(e.bm) * e.bn;
     const int rank = wg <= 256 ? e.rank_one_round : e.rank;
-    if (wg >= 256 && (area > best_area || (area == best_area && rank > best_rank))) {
+    // An entry fills the GPU with 256 workgroups or more, or, running one per CU, with a single
+    // round more than half full: a tile of half the area then needs two per CU somewhere, so
+    // each CU does the same work either way and the larger tile's higher efficiency decides
+    // (MI355X, bf16: 3072^3 ring 0.068 ms vs 256x128 0.093 ms; 3328^2 x 4096 0.093 vs 0.130;
+    // with exactly 128 ring tiles, 2048 x 4096 x 2048, the 256x128 kernel is faster).
+    const bool fills = wg >= 256 || (one_per_cu(e) && wg > 128);
+    if (fills && (area > best_area || (area == best_area && rank > best_rank))) {
       best = i;
       best_area = area;
       best_rank = rank;

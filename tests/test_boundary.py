@@ -328,3 +328,27 @@ def test_col_sum_fields(fake_gfx950):
     d = desc(**base)
     d.has_col_sum = 2
     assert status_of(d) == H.GEMM_ERR_INVALID_ARG
+
+
+# Kernel choice for mid-size and large bf16 products (A row-major, B column-major).  One-round
+# rules measured on MI355X: a one-workgroup-per-CU tile is used when its single round is over
+# half full; automatic K slices stay within one round; leftover tiles of an incomplete last round
+# are split along K (split tail).
+@pytest.mark.parametrize("shape,kernel,split,tail", [
+    ((3072, 3072, 3072), "m16_ring", 1, (0, 1)),       # 144 ring tiles
+    ((3328, 3328, 4096), "m16_ring", 1, (0, 1)),       # 169: no split, 2 slices would be 338
+    ((2816, 2816, 4096), "m16_ring", 2, (0, 1)),       # 121 tiles x 2 = 242
+    ((1536, 1536, 8192), "m16_ring", 7, (0, 1)),       # 36 x 7 = 252; 8 would start a round
+    ((2048, 2048, 4096), "m16_ring", 4, (0, 1)),
+    ((2048, 4096, 2048), "256x128x32", 1, (0, 1)),     # exactly 128 ring tiles: half-size tile
+    ((2048, 2048, 2048), "128x128x64", 1, (0, 1)),
+    ((512, 512, 16384), "128x128x64", 16, (0, 1)),
+    ((8192, 8192, 8192), "m16_ring", 1, (0, 1)),
+    ((4352, 4352, 4096), "m16_ring", 1, (33, 7)),
+])
+def test_kernel_choice_by_rounds(fake_gfx950, shape, kernel, split, tail):
+    M, N, K = shape
+    info = _info(desc(M=M, N=N, K=K, a_strides=(K, 1), b_strides=(1, K), d_strides=(N, 1)))
+    name = info.name.decode()
+    assert kernel in name and not name.endswith("ring1"), name
+    assert (info.split_k, info.tail_tiles, info.tail_split) == (split,) + tail, name
