@@ -64,3 +64,45 @@ def test_random_problem_matches_oracle(i):
     else:
         assert np.isfinite(got).all()
         assert error(c.dtype, got, want) <= TOL[c.dtype], name
+
+
+# Mid-size problems (one-round ring choices, K splits, split tails), checked on sampled outputs:
+# whole first/last rows and columns plus random elements.
+N_MID = 10
+
+
+def draw_mid(i):
+    rng = random.Random(9500 + i)
+    dtype = rng.choice(["bf16", "bf16", "f16", "e4m3"])
+    M, N = rng.randint(1100, 4400), rng.randint(1100, 4400)
+    if rng.random() < 0.6:
+        M, N = M - M % 16, N - N % 16
+    K = rng.choice([512, 1024, 2048, 4096, 8192]) + rng.choice([0, 0, 64, 48])
+    dyadic = rng.random() < 0.5
+    c = Case(M=M, N=N, K=K, dtype=dtype, a_order="row", b_order="col",
+             dist="dyadic" if dyadic else "normal", alpha=1.0 if dyadic else 0.75,
+             beta=0.5 if rng.random() < 0.4 else 0.0, bias=rng.random() < 0.5,
+             act="none" if dyadic else rng.choice(["none", "gelu", "silu"]),
+             scale_a=0.5 if dtype == "e4m3" else 1.0, scale_b=0.5 if dtype == "e4m3" else 1.0,
+             seed=9500 + i)
+    c.has_c = c.beta != 0.0
+    return c, dyadic
+
+
+@pytest.mark.parametrize("i", range(N_MID))
+def test_random_mid_size_problem_matches_oracle(i):
+    from tests.gemm_util import sample_indices
+    c, dyadic = draw_mid(i)
+    p = Prepared(c)
+    g, out = p.run()
+    got, bits = p.decode_out(out)
+    rows, cols = sample_indices(c.M, c.N, seed=i)
+    want = p.oracle_elems(rows, cols)
+    inf = g.info
+    print(f"mid {i}: {c.dtype} {c.M}x{c.N}x{c.K} C={c.has_c} bias={c.bias} act={c.act} -> "
+          f"{inf.name.decode()} split={inf.split_k} tail={inf.tail_tiles}x{inf.tail_split}")
+    if dyadic:
+        assert int((bits[rows, cols] != oracle.encode_rne(OUT_T[c.dtype], want)).sum()) == 0
+    else:
+        assert np.isfinite(got).all()
+        assert error(c.dtype, got[rows, cols], want) <= TOL[c.dtype]
