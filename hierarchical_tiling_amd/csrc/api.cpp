@@ -150,7 +150,7 @@ void plan_tail(const KernelEntry& e, const gemm_desc& d, int split_req, int spli
   *S = 1;
   *kps = d.K;
   if (split_req != 0 || split_whole > 1 || e.max_split_k <= 1 || e.skinny) return;
-  if (2 * int64_t(e.lds_bytes) <= kLdsBudget) return;  // room for a second workgroup per CU
+  if (!one_per_cu(e)) return;
   const int64_t tiles = cdiv(d.M, e.bm) * cdiv(d.N, e.bn);
   const int64_t rem = tiles % 256;
   if (tiles <= 256 || rem == 0 || rem > 128) return;

@@ -265,15 +265,6 @@ __device__ __forceinline__ KParams batch_view(const KParams& p) {
   return q;
 }
 
-// The problem and tile of a workgroup of a tile kernel.  Plain and batched launches: tile
-// blockIdx.x of gridDim.x.  A grouped launch with ragged M (mixture-of-experts: "CUTLASS",
-// Part V, a grouped GEMM in which each expert is one problem of a batch of differently shaped
-// problems) shares A's, C's and D's row space among the groups: group e owns rows
-// [offsets[e], offsets[e+1]) and multiplies them by its own B, and the grid enumerates the tiles
-// of every group in order.  Offsets are clamped into [0, M] and made non-decreasing, so no
-// offset array can send a workgroup outside the operands.  Returns false for a workgroup past
-// the last group's tiles (the grid is sized for the most tiles any split of M can need); such a
-// workgroup exits before its first barrier.
 // The kernel argument read again from the kernarg segment (the kernel's only argument, at offset
 // 0).  The pointer passes through an empty asm, so these loads cannot be merged with those made
 // at entry: values needed only after the main loop are loaded there instead of occupying SGPRs
@@ -285,6 +276,15 @@ __device__ __forceinline__ KParams reload_args() {
   return *(const KParams*)q;
 }
 
+// The problem and tile of a workgroup of a tile kernel.  Plain and batched launches: tile
+// blockIdx.x of gridDim.x.  A grouped launch with ragged M (mixture-of-experts: "CUTLASS",
+// Part V, a grouped GEMM in which each expert is one problem of a batch of differently shaped
+// problems) shares A's, C's and D's row space among the groups: group e owns rows
+// [offsets[e], offsets[e+1]) and multiplies them by its own B, and the grid enumerates the tiles
+// of every group in order.  Offsets are clamped into [0, M] and made non-decreasing, so no
+// offset array can send a workgroup outside the operands.  Returns false for a workgroup past
+// the last group's tiles (the grid is sized for the most tiles any split of M can need); such a
+// workgroup exits before its first barrier.
 template <int BM>
 __device__ __forceinline__ bool problem_view(const KParams& in, KParams& p, int& pid, int& nwg) {
   p = batch_view(in);
