@@ -9,6 +9,10 @@ static const KernelEntry g_f32[] = {
     HT_TILED("f32_ak_bn_128x128x32_w2x2_m32_vec", DT_F32, 1, 0, 1, 128, 128, 32, 2, 2, 32),
     HT_TILED("f32_am_bk_128x128x32_w2x2_m32_vec", DT_F32, 0, 1, 1, 128, 128, 32, 2, 2, 32),
     HT_TILED("f32_am_bn_128x128x32_w2x2_m32_vec", DT_F32, 0, 0, 1, 128, 128, 32, 2, 2, 32),
+    HT_TILED("f32_ak_bk_64x64x32_w2x2_m16_vec", DT_F32, 1, 1, 1, 64, 64, 32, 2, 2, 16),
+    HT_TILED("f32_ak_bn_64x64x32_w2x2_m16_vec", DT_F32, 1, 0, 1, 64, 64, 32, 2, 2, 16),
+    HT_TILED("f32_am_bk_64x64x32_w2x2_m16_vec", DT_F32, 0, 1, 1, 64, 64, 32, 2, 2, 16),
+    HT_TILED("f32_am_bn_64x64x32_w2x2_m16_vec", DT_F32, 0, 0, 1, 64, 64, 32, 2, 2, 16),
     HT_TILED("f32_ak_bk_64x64x32_w2x2_m16_narrow", DT_F32, 1, 1, 0, 64, 64, 32, 2, 2, 16),
     HT_TILED("f32_ak_bn_64x64x32_w2x2_m16_narrow", DT_F32, 1, 0, 0, 64, 64, 32, 2, 2, 16),
     HT_TILED("f32_am_bk_64x64x32_w2x2_m16_narrow", DT_F32, 0, 1, 0, 64, 64, 32, 2, 2, 16),
