@@ -7,6 +7,7 @@ namespace htk {
 static const KernelEntry g_e4m3[] = {
     HT_TILED("e4m3_ak_bk_256x256x128_w2x2_m32_vec", DT_F8, 1, 1, 1, 256, 256, 128, 2, 2, 32),
     HT_TILED("e4m3_ak_bk_128x128x128_w2x2_m32_vec", DT_F8, 1, 1, 1, 128, 128, 128, 2, 2, 32),
+    HT_TILED("e4m3_ak_bk_64x64x128_w2x2_m16_vec", DT_F8, 1, 1, 1, 64, 64, 128, 2, 2, 16),
     HT_TILED("e4m3_ak_bk_128x128x128_w2x2_m32_narrow", DT_F8, 1, 1, 0, 128, 128, 128, 2, 2, 32),
     HT_TILED("e4m3_ak_bn_128x128x128_w2x2_m32_narrow", DT_F8, 1, 0, 0, 128, 128, 128, 2, 2, 32),
     HT_TILED("e4m3_am_bk_128x128x128_w2x2_m32_narrow", DT_F8, 0, 1, 0, 128, 128, 128, 2, 2, 32),
