@@ -16,6 +16,10 @@ static const KernelEntry g_f16[] = {
     HT_TILED("f16_am_bk_64x64x64_w2x2_m16_vec", DT_F16, 0, 1, 1, 64, 64, 64, 2, 2, 16),
     HT_TILED("f16_am_bn_64x64x64_w2x2_m16_vec", DT_F16, 0, 0, 1, 64, 64, 64, 2, 2, 16),
     HT_TILED("f16_ak_bk_128x128x64_w2x2_m32_narrow", DT_F16, 1, 1, 0, 128, 128, 64, 2, 2, 32),
+    HT_TILED("f16_ak_bk_64x64x64_w2x2_m16_narrow", DT_F16, 1, 1, 0, 64, 64, 64, 2, 2, 16),
+    HT_TILED("f16_ak_bn_64x64x64_w2x2_m16_narrow", DT_F16, 1, 0, 0, 64, 64, 64, 2, 2, 16),
+    HT_TILED("f16_am_bk_64x64x64_w2x2_m16_narrow", DT_F16, 0, 1, 0, 64, 64, 64, 2, 2, 16),
+    HT_TILED("f16_am_bn_64x64x64_w2x2_m16_narrow", DT_F16, 0, 0, 0, 64, 64, 64, 2, 2, 16),
     HT_TILED("f16_ak_bn_128x128x64_w2x2_m32_narrow", DT_F16, 1, 0, 0, 128, 128, 64, 2, 2, 32),
     HT_TILED("f16_am_bk_128x128x64_w2x2_m32_narrow", DT_F16, 0, 1, 0, 128, 128, 64, 2, 2, 32),
     HT_TILED("f16_am_bn_128x128x64_w2x2_m32_narrow", DT_F16, 0, 0, 0, 128, 128, 64, 2, 2, 32),
