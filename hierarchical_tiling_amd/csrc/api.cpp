@@ -175,7 +175,8 @@ void plan_tail(const KernelEntry& e, const gemm_desc& d, int split_req, int spli
 // still fill the GPU (at least 256, or one round over half full for a one-per-CU kernel), ties
 // broken by the measured rank -- the entry's one-round rank when all its workgroups run at once
 // (at most 256), else its rank -- or, when no tile fills it, the entry with the most
-// workgroups.  A forced split (split_req > 1) admits only entries that can split.
+// workgroups (ties: larger tile, then rank).  A forced split (split_req > 1) admits only entries
+// that can split.
 int choose(const gemm_handle_s& h, bool vec_a, bool vec_b, bool want_vec, int split_req) {
   const KernelEntry* t = table();
   const bool need_split = split_req > 1;
@@ -184,8 +185,8 @@ int choose(const gemm_handle_s& h, bool vec_a, bool vec_b, bool want_vec, int sp
     if (t[i].skinny && (t[i].vec != 0) == want_vec && entry_fits(t[i], h, vec_a, vec_b)) return i;
   int best = -1, best_rank = 0;
   int64_t best_area = -1;
-  int best_small = -1;
-  int64_t best_small_wg = -1;
+  int best_small = -1, best_small_rank = 0;
+  int64_t best_small_wg = -1, best_small_area = -1;
   for (int i = 0; i < table_size(); ++i) {
     const KernelEntry& e = t[i];
     if ((e.vec != 0) != want_vec || e.skinny) continue;
@@ -208,9 +209,13 @@ int choose(const gemm_handle_s& h, bool vec_a, bool vec_b, bool want_vec, int sp
       best_area = area;
       best_rank = rank;
     }
-    if (wg > best_small_wg || (wg == best_small_wg && area > int64_t(t[best_small].bm) * t[best_small].bn)) {
+    if (wg > best_small_wg ||
+        (wg == best_small_wg && (area > best_small_area ||
+                                 (area == best_small_area && rank > best_small_rank)))) {
       best_small = i;
       best_small_wg = wg;
+      best_small_area = area;
+      best_small_rank = rank;
     }
   }
   return best >= 0 ? best : best_small;

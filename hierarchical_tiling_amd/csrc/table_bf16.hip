@@ -29,6 +29,10 @@ static const KernelEntry g_bf16[] = {
     HT_TILED("bf16_ak_bn_128x128x64_w2x2_m32_realign", DT_BF16, 1, 0, 2, 128, 128, 64, 2, 2, 32),
     HT_TILED("bf16_am_bk_128x128x64_w2x2_m32_realign", DT_BF16, 0, 1, 2, 128, 128, 64, 2, 2, 32),
     HT_TILED("bf16_am_bn_128x128x64_w2x2_m32_realign", DT_BF16, 0, 0, 2, 128, 128, 64, 2, 2, 32),
+    HT_TILED("bf16_ak_bk_64x64x64_w2x2_m16_realign", DT_BF16, 1, 1, 2, 64, 64, 64, 2, 2, 16),
+    HT_TILED("bf16_ak_bn_64x64x64_w2x2_m16_realign", DT_BF16, 1, 0, 2, 64, 64, 64, 2, 2, 16),
+    HT_TILED("bf16_am_bk_64x64x64_w2x2_m16_realign", DT_BF16, 0, 1, 2, 64, 64, 64, 2, 2, 16),
+    HT_TILED("bf16_am_bn_64x64x64_w2x2_m16_realign", DT_BF16, 0, 0, 2, 64, 64, 64, 2, 2, 16),
 };
 
 const KernelEntry* table_bf16(int* n) {

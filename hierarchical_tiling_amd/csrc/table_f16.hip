@@ -28,6 +28,10 @@ static const KernelEntry g_f16[] = {
     HT_TILED("f16_ak_bn_128x128x64_w2x2_m32_realign", DT_F16, 1, 0, 2, 128, 128, 64, 2, 2, 32),
     HT_TILED("f16_am_bk_128x128x64_w2x2_m32_realign", DT_F16, 0, 1, 2, 128, 128, 64, 2, 2, 32),
     HT_TILED("f16_am_bn_128x128x64_w2x2_m32_realign", DT_F16, 0, 0, 2, 128, 128, 64, 2, 2, 32),
+    HT_TILED("f16_ak_bk_64x64x64_w2x2_m16_realign", DT_F16, 1, 1, 2, 64, 64, 64, 2, 2, 16),
+    HT_TILED("f16_ak_bn_64x64x64_w2x2_m16_realign", DT_F16, 1, 0, 2, 64, 64, 64, 2, 2, 16),
+    HT_TILED("f16_am_bk_64x64x64_w2x2_m16_realign", DT_F16, 0, 1, 2, 64, 64, 64, 2, 2, 16),
+    HT_TILED("f16_am_bn_64x64x64_w2x2_m16_realign", DT_F16, 0, 0, 2, 64, 64, 64, 2, 2, 16),
     HT_DMA("f16_ak_bk_256x256x32_w2x2_m32_dma4", DT_F16, 256, 256, 2, 2, 32, 4, 1, 4, 2),
     HT_DMA("f16_ak_bk_256x256x64_w2x2_m32_dma2", DT_F16, 256, 256, 2, 2, 32, 2, 1, 8, 3),
     HT_DMA("f16_ak_bk_256x256x64_w2x4_m32_dma2", DT_F16, 256, 256, 2, 4, 32, 2, 1, 8, 5),
