@@ -172,7 +172,7 @@ void plan_tail(const KernelEntry& e, const gemm_desc& d, int split_req, int spli
 // Heuristic choice among fitting entries.  A product with M <= 16 is bound by streaming B and
 // takes the skinny kernel when one fits.  Otherwise each entry is counted with the split-K plan
 // it would get (plan_split) and the choice is the largest tile whose workgroups (tiles x slices)
-// still fill the GPU (at least 256, or one round over half full for a one-per-CU kernel), ties
+// still fill the GPU (at least 256, or over 128 for a one-per-CU or realigned 128 x 128 tile), ties
 // broken by the measured rank -- the entry's one-round rank when all its workgroups run at once
 // (at most 256), else its rank -- or, when no tile fills it, the entry with the most
 // workgroups (ties: larger tile, then rank).  A forced split (split_req > 1) admits only entries
@@ -198,12 +198,16 @@ int choose(const gemm_handle_s& h, bool vec_a, bool vec_b, bool want_vec, int sp
     const int64_t wg = cdiv(h.d.M, e.bm) * cdiv(h.d.N, e.bn) * slices;
     const int64_t area = int64_t(e.bm) * e.bn;
     const int rank = wg <= 256 ? e.rank_one_round : e.rank;
-    // An entry fills the GPU with 256 workgroups or more, or, running one per CU, with a single
-    // round more than half full: a tile of half the area then needs two per CU somewhere, so
-    // each CU does the same work either way and the larger tile's higher efficiency decides
-    // (MI355X, bf16: 3072^3 ring 0.068 ms vs 256x128 0.093 ms; 3328^2 x 4096 0.093 vs 0.130;
-    // with exactly 128 ring tiles, 2048 x 4096 x 2048, the 256x128 kernel is faster).
-    const bool fills = wg >= 256 || (one_per_cu(e) && wg > 128);
+    // An entry fills the GPU with 256 workgroups or more.  A kernel that runs one per CU, or a
+    // 128 x 128 tile with the realigned loaders (whose smaller tile is much less efficient),
+    // also fills it with more than 128: a tile of half the area then needs two per CU somewhere
+    // (a quarter, three or more), so no CU does much less work with it, and the larger tile's
+    // higher efficiency decides.  MI355X: bf16 3072^3 ring 0.068 ms vs 256x128 0.093 ms;
+    // 3328^2 x 4096 0.093 vs 0.130; fp16 2051 x 1533 x 1027 with odd leading dims, 128x128
+    // realigned (204 workgroups) 47 us vs 64x64 (792) 65 us.  With exactly 128 ring tiles
+    // (2048 x 4096 x 2048) the 256x128 kernel is faster; for the 16-byte loaders 64x64 tiles
+    // were as fast or faster than 144-192 workgroups of 128x128 (f32 1536^3 111 vs 134 us).
+    const bool fills = wg >= 256 || (wg > 128 && (one_per_cu(e) || (e.realign && area >= 128 * 128)));
     if (fills && (area > best_area || (area == best_area && rank > best_rank))) {
       best = i;
       best_area = area;
