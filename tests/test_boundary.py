@@ -352,3 +352,23 @@ def test_kernel_choice_by_rounds(fake_gfx950, shape, kernel, split, tail):
     name = info.name.decode()
     assert kernel in name and not name.endswith("ring1"), name
     assert (info.split_k, info.tail_tiles, info.tail_split) == (split,) + tail, name
+
+
+@pytest.mark.parametrize("dtype,shape,orders,kernel", [
+    ("bf16", (1024, 1024, 1024), ("row", "col"), "_64x64x64_w2x2_m16_vec"),         # 256 small tiles
+    ("e4m3", (1024, 1024, 1024), ("row", "col"), "_64x64x128_w2x2_m16_vec"),
+    ("f32", (256, 256, 256), ("row", "row"), "_64x64x32_w2x2_m16_vec"),
+    ("bf16", (1536, 1536, 1024), ("row", "col"), "_64x64x64_w2x2_m16_vec"),          # 144 of 128x128
+    ("bf16", (2048, 2048, 2048), ("row", "col"), "_128x128x64_w2x2_m32_vec"),
+    # odd leading dimensions: realigned loaders; 128x128 from 129 workgroups
+    ("f16", (1001, 999, 1003), ("row", "row"), "_64x64x64_w2x2_m16_realign"),
+    ("f16", (2051, 1533, 1027), ("row", "row"), "_128x128x64_w2x2_m32_realign"),
+    ("f16", (4099, 3071, 2053), ("row", "row"), "_128x128x64_w2x2_m32_realign"),
+    ("bf16", (255, 257, 251), ("row", "row"), "_64x64x64_w2x2_m16_realign"),         # rank breaks the tie
+])
+def test_kernel_choice_small_and_realigned(fake_gfx950, dtype, shape, orders, kernel):
+    M, N, K = shape
+    a = (K, 1) if orders[0] == "row" else (1, M)
+    b = (N, 1) if orders[1] == "row" else (1, K)
+    info = _info(desc(M=M, N=N, K=K, dtype=dtype, a_strides=a, b_strides=b, d_strides=(N, 1)))
+    assert info.name.decode().endswith(kernel), info.name.decode()
