@@ -133,7 +133,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=30)  # untimed; lets the clock settle
     ap.add_argument("--workload", default="bf16_8192_gelu", choices=sorted(WORKLOADS))
     ap.add_argument("--force-config", type=int, default=-1)
     ap.add_argument("--no-cpu-baseline", action="store_true")
