@@ -1,4 +1,4 @@
-"""GPU parity on seeded random problems through the library's own kernel choice.
+"""GPU parity on seeded random problems through the library's own kernel choice (160 small, 16 mid-size).
 
 Each case draws a shape (small to a few tiles, with ragged tails in M, N and K), operand type,
 layouts, padded leading dimensions, output order and epilogue (alpha, beta with C, bias,
@@ -16,7 +16,7 @@ from tests.gemm_util import OUT_T, TOL, Case, Prepared, error
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 64
+N_CASES = 160
 
 
 def draw(i):
@@ -68,7 +68,7 @@ def test_random_problem_matches_oracle(i):
 
 # Mid-size problems (one-round ring choices, K splits, split tails), checked on sampled outputs:
 # whole first/last rows and columns plus random elements.
-N_MID = 10
+N_MID = 16
 
 
 def draw_mid(i):
