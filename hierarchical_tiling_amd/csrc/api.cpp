@@ -195,7 +195,10 @@ int choose(const gemm_handle_s& h, bool vec_a, bool vec_b, bool want_vec, int sp
     int slices;
     int64_t kps;
     plan_split(e, h.d, split_req, &slices, &kps);
-    const int64_t wg = cdiv(h.d.M, e.bm) * cdiv(h.d.N, e.bn) * slices;
+    // a batch runs every problem's tiles in one launch (a grouped launch's M already spans
+    // all of its groups)
+    const int64_t problems = h.d.batch > 1 && !h.d.ragged_m ? h.d.batch : 1;
+    const int64_t wg = cdiv(h.d.M, e.bm) * cdiv(h.d.N, e.bn) * slices * problems;
     const int64_t area = int64_t(e.bm) * e.bn;
     const int rank = wg <= 256 ? e.rank_one_round : e.rank;
     // An entry fills the GPU with 256 workgroups or more.  A kernel that runs one per CU, or a

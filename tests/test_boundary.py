@@ -372,3 +372,15 @@ def test_kernel_choice_small_and_realigned(fake_gfx950, dtype, shape, orders, ke
     b = (N, 1) if orders[1] == "row" else (1, K)
     info = _info(desc(M=M, N=N, K=K, dtype=dtype, a_strides=a, b_strides=b, d_strides=(N, 1)))
     assert info.name.decode().endswith(kernel), info.name.decode()
+
+
+@pytest.mark.parametrize("L,shape,kernel", [
+    (16, (1024, 1024, 512), "_m16_ring"),          # 16 tiles x 16 problems fill one ring round
+    (64, (256, 256, 1024), "_128x128x64_w2x2_m32_vec"),
+    (1, (1024, 1024, 1024), "_64x64x64_w2x2_m16_vec"),
+])
+def test_kernel_choice_counts_batch_problems(fake_gfx950, L, shape, kernel):
+    M, N, K = shape
+    d = desc(M=M, N=N, K=K, a_strides=(K, 1), b_strides=(1, K), d_strides=(N, 1), batch=L,
+             batch_strides=(M * K, N * K, 0, M * N))
+    assert _info(d).name.decode().endswith(kernel)
