@@ -266,7 +266,9 @@ int gemm_create(const gemm_desc* desc, gemm_t* out) {
     return GEMM_ERR_INVALID_ARG;
   if (d.ragged_m) {
     // grouped: the groups share A's, C's and D's rows (device offsets at run time); B moves by
-    // b_stride_l per group.  Row offsets must keep 16-byte rows aligned: A is K-major.
+    // b_stride_l per group.  Row offsets must keep 16-byte rows aligned: A is K-major.  The
+    // batch field is the group count G (offsets holds G + 1 values), so it must be at least 1.
+    if (d.batch < 1) return GEMM_ERR_INVALID_ARG;
     if (d.b_stride_l < 0) return GEMM_ERR_LAYOUT;
     if (d.split_k > 1) return GEMM_ERR_INVALID_ARG;
   } else if (L > 1) {

@@ -413,7 +413,28 @@ Layout join_modes(const std::vector<Layout>& m) {
 
 extern "C" {
 
-int ht_layout_eval(const char* layout, const char* coord, int64_t* out) {
+int ht_layout_eval(const char* layout, const int64_t* coord, int rank, int64_t* out) {
+  Layout l;
+  if (!parse_layout(layout, &l) || !out || (rank > 0 && !coord)) return HT_ERR_PARSE;
+  // rank 1: one integer over the whole layout; rank r > 1: one integer per top-level mode
+  Tup c;
+  if (rank == 1) {
+    c = Tup::L(coord[0]);
+  } else if (rank > 1 && !l.shape.leaf && (size_t)rank == l.shape.c.size()) {
+    std::vector<Tup> xs;
+    for (int i = 0; i < rank; ++i) xs.push_back(Tup::L(coord[i]));
+    c = Tup::N(std::move(xs));
+  } else {
+    return HT_ERR_RANGE;
+  }
+  if (!in_range(c, l.shape)) return HT_ERR_RANGE;
+  int64_t acc = 0;
+  if (!inner(c, l.shape, l.stride, &acc)) return HT_ERR_RANGE;
+  *out = acc;
+  return HT_OK;
+}
+
+int ht_layout_eval_str(const char* layout, const char* coord, int64_t* out) {
   Layout l;
   if (!parse_layout(layout, &l) || !coord || !out) return HT_ERR_PARSE;
   Tup c;

@@ -18,7 +18,7 @@ STATUS_NAMES = {0: "GEMM_OK", 1: "GEMM_ERR_INVALID_ARG", 2: "GEMM_ERR_DTYPE_COMB
                 6: "GEMM_ERR_LAUNCH", 7: "GEMM_ERR_BAD_HANDLE", 8: "GEMM_ERR_NO_CONFIG",
                 9: "GEMM_ERR_HIP"}
 DTYPES = {"f32": 0, "f16": 1, "bf16": 2, "e4m3": 3}
-ACTS = {"none": 0, "relu": 1, "gelu": 2, "silu": 3}
+ACTS = {"none": 0, "relu": 1, "gelu": 2, "gelu_erf": 2, "silu": 3}
 # layout status codes (htlayout.h)
 HT_STATUS_NAMES = {0: "HT_OK", 1: "HT_ERR_PARSE", 2: "HT_ERR_RANGE", 3: "HT_ERR_NOT_COMPOSABLE",
                    4: "HT_ERR_CAPACITY", 5: "HT_ERR_NO_COMPLEMENT"}
@@ -106,7 +106,8 @@ def lib():
         "gemm_get_info": ([vp, ctypes.POINTER(gemm_info)], i32),
         "gemm_num_configs": ([], i32),
         "gemm_config_name": ([i32, ctypes.c_char_p, sz], i32),
-        "ht_layout_eval": ([cp, cp, ctypes.POINTER(i64)], i32),
+        "ht_layout_eval": ([cp, ctypes.POINTER(i64), i32, ctypes.POINTER(i64)], i32),
+        "ht_layout_eval_str": ([cp, cp, ctypes.POINTER(i64)], i32),
         "ht_layout_size": ([cp, ctypes.POINTER(i64)], i32),
         "ht_layout_table": ([cp, ctypes.POINTER(i64), i64], i32),
         "ht_layout_coalesce": ([cp, ctypes.c_char_p, sz], i32),
@@ -132,6 +133,7 @@ EXPORTED = ["gemm_create", "gemm_workspace_size", "gemm_run", "gemm_run_ex", "ge
             "gemm_destroy",
             "gemm_status_string",
             "gemm_get_info", "gemm_num_configs", "gemm_config_name", "ht_layout_eval",
+            "ht_layout_eval_str",
             "ht_layout_size", "ht_layout_table", "ht_layout_coalesce", "ht_layout_compose",
             "ht_layout_complement", "ht_layout_logical_divide", "ht_layout_zipped_divide",
             "ht_layout_local_tile", "ht_layout_local_partition", "ht_swizzle", "ht_tile_plan", "ht_pipeline_time"]
@@ -303,10 +305,18 @@ def _out_str(fn, *args):
 
 
 def ht_layout_eval(layout: str, coord) -> int:
-    if not isinstance(coord, str):
-        coord = _coord_str(coord)
+    """Offset of `coord`: an int (a 1-D coordinate), a flat tuple of ints (one per top-level
+    mode), or text / a nested tuple (passed to ht_layout_eval_str)."""
     out = ctypes.c_int64()
-    _lcheck(lib().ht_layout_eval(layout.encode(), coord.encode(), ctypes.byref(out)), "ht_layout_eval")
+    if isinstance(coord, str) or (isinstance(coord, (tuple, list))
+                                  and any(isinstance(x, (tuple, list)) for x in coord)):
+        text = coord if isinstance(coord, str) else _coord_str(coord)
+        _lcheck(lib().ht_layout_eval_str(layout.encode(), text.encode(), ctypes.byref(out)),
+                "ht_layout_eval_str")
+        return out.value
+    vals = [int(coord)] if not isinstance(coord, (tuple, list)) else [int(x) for x in coord]
+    arr = (ctypes.c_int64 * max(len(vals), 1))(*vals)
+    _lcheck(lib().ht_layout_eval(layout.encode(), arr, len(vals), ctypes.byref(out)), "ht_layout_eval")
     return out.value
 
 

@@ -92,7 +92,15 @@ enum {
 
 /* ---- element types and activations ----------------------------------------------------- */
 typedef enum { GEMM_F32 = 0, GEMM_F16 = 1, GEMM_BF16 = 2, GEMM_F8E4M3 = 3 } gemm_dtype;
-typedef enum { GEMM_ACT_NONE = 0, GEMM_ACT_RELU = 1, GEMM_ACT_GELU = 2, GEMM_ACT_SILU = 3 } gemm_act;
+/* GEMM_ACT_GELU_ERF is the exact (erf) GELU; GEMM_ACT_GELU is the same value under a shorter
+ * name. */
+typedef enum {
+  GEMM_ACT_NONE = 0,
+  GEMM_ACT_RELU = 1,
+  GEMM_ACT_GELU_ERF = 2,
+  GEMM_ACT_GELU = GEMM_ACT_GELU_ERF,
+  GEMM_ACT_SILU = 3
+} gemm_act;
 
 /* ---- problem descriptor ------------------------------------------------------------------ */
 typedef struct gemm_desc {
@@ -119,7 +127,7 @@ typedef struct gemm_desc {
   int64_t a_stride_l, b_stride_l;   /* elements from problem l's A (B) to problem l+1's; >= 0    */
   int64_t c_stride_l, d_stride_l;   /* the same for C and D; d_stride_l != 0 when batch > 1      */
   int32_t ragged_m;           /* 1: grouped GEMM with ragged M, run by gemm_run_grouped: the     */
-                              /* `batch` groups share A's, C's and D's M rows (and row_scale),   */
+                              /* `batch` >= 1 groups share A's, C's and D's M rows (row_scale),  */
                               /* split by device offsets; B of group e is at B + e*b_stride_l;   */
                               /* A must be K-major (row-major); a/c/d_stride_l are ignored       */
   int32_t has_row_sumsq;      /* 1: gemm_run_ex also writes row_sumsq[m] = sum over n of D(m,n)^2 */

@@ -10,8 +10,8 @@
  *
  * Layouts cross this interface as text in the pages' notation, for example "(4,3):(3,1)",
  * "((2,2),3):((24,2),8)" or "12:1" (leading underscores as in "_12:_1" are accepted).
- * Coordinates are text too: "(1,0)", "5", "(1,(0,1))"; an integer entry may stand for a whole
- * nested mode and is split over it.
+ * Coordinates are arrays of integers (ht_layout_eval) or text (ht_layout_eval_str, "(1,(0,1))");
+ * an integer entry may stand for a whole nested mode and is split over it.
  *
  * Output strings are written to caller-owned buffers `out` of `cap` bytes, NUL-terminated;
  * HT_ERR_CAPACITY means the buffer was too small (nothing useful is written).  Every function is
@@ -36,9 +36,17 @@ enum {
   HT_ERR_NO_COMPLEMENT = 5    /* no ordered complement exists under the given size           */
 };
 
-/* Offset of coordinate `coord` in `layout` ("CUTLASS, CuTe, and CUDA Tile", introduction:
- * (4,3):(3,1) maps (1,0) to 3 and (0,1) to 1). */
-int ht_layout_eval(const char* layout, const char* coord, int64_t* out);
+/* Offset of a coordinate in `layout` ("CUTLASS, CuTe, and CUDA Tile", introduction:
+ * (4,3):(3,1) maps (1,0) to 3 and (0,1) to 1).  `coord` holds `rank` integers owned by the
+ * caller: rank 1 is a single integer over the whole layout (split over its modes, leftmost
+ * fastest, as a 1-D coordinate); rank r > 1 gives one integer per top-level mode of a layout
+ * with r top-level modes, each split over its mode if that mode is nested.  HT_ERR_RANGE for
+ * another rank or a coordinate outside the shape; HT_ERR_PARSE for bad text or NULL. */
+int ht_layout_eval(const char* layout, const int64_t* coord, int rank, int64_t* out);
+
+/* The same with the coordinate as text in the pages' notation, nested as deep as the shape:
+ * "(1,0)", "5", "(1,(0,1))". */
+int ht_layout_eval_str(const char* layout, const char* coord, int64_t* out);
 
 /* Number of coordinates (product of the shape). */
 int ht_layout_size(const char* layout, int64_t* out);

@@ -7,6 +7,8 @@ inputs and nothing else.
 
 * ``oracle.gemm`` / ``oracle.gemm_elems`` / ``oracle.decode`` / ``oracle.encode_rne`` wrap the
   plain-C triple loop in ``htoracle.c`` (double accumulation, exact decode of every input).
+* ``oracle.row_sumsq`` / ``oracle.col_sum`` reduce the output as stored: each value rounded to
+  the output type, then squared and summed along a row, or summed along a column, in double.
 * ``oracle.layout`` holds the pointwise definitions of the layout algebra (evaluate, compose,
   coalesce, complement, divide, swizzle).
 * ``oracle.tile`` holds the pages' tile-arithmetic and pipeline formulas.
@@ -59,7 +61,10 @@ def _load():
                   vp, vp, dbl, dbl, dbl, dbl, i32]
         lib.oracle_gemm.argtypes = common + [vp, i64, i64, i32]
         lib.oracle_gemm_elems.argtypes = common + [i64, vp, vp, vp, i32]
-        for f in (lib.oracle_decode, lib.oracle_encode_rne, lib.oracle_gemm, lib.oracle_gemm_elems):
+        lib.oracle_row_sumsq.argtypes = [i32, vp, i64, i64, i64, vp]
+        lib.oracle_col_sum.argtypes = [i32, vp, i64, i64, i64, vp]
+        for f in (lib.oracle_decode, lib.oracle_encode_rne, lib.oracle_gemm, lib.oracle_gemm_elems,
+                  lib.oracle_row_sumsq, lib.oracle_col_sum):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -171,3 +176,27 @@ def gemm_elems(A: Operand, B: Operand, rows, cols, C: Operand | None = None,
     if rc:
         raise ValueError(f"oracle_gemm_elems failed ({rc})")
     return out
+
+
+def _reduce(fn, D, out_type, n_out):
+    D = np.ascontiguousarray(D, dtype=np.float64)
+    if D.ndim != 2:
+        raise ValueError("D must be a matrix")
+    M, N = D.shape
+    out = np.empty(n_out(M, N), dtype=np.float64)
+    rc = fn(DTYPES[out_type], _ptr(D), M, N, N, _ptr(out))
+    if rc:
+        raise ValueError(f"{fn.__name__} failed ({rc})")
+    return out
+
+
+def row_sumsq(D, out_type: str) -> np.ndarray:
+    """For each row i of the double result D: the sum over j of the square of D[i, j] rounded to
+    `out_type` (the stored output), in double."""
+    return _reduce(_load().oracle_row_sumsq, D, out_type, lambda M, N: M)
+
+
+def col_sum(D, out_type: str) -> np.ndarray:
+    """For each column j of the double result D: the sum over i of D[i, j] rounded to
+    `out_type`, in double."""
+    return _reduce(_load().oracle_col_sum, D, out_type, lambda M, N: N)

@@ -414,3 +414,47 @@ int oracle_gemm_elems(int64_t M, int64_t N, int64_t K, int a_type, const void* A
   free(ej);
   return OR_OK;
 }
+
+/* ------------------------------------------------------------------------------------------ */
+/* Reductions of the stored output for the next layer ("CUTLASS", stanleyjacob.dev, Part IV      */
+/* Stage 5 "The epilogue and fusion": an epilogue visitor tree can fuse a reduction that a       */
+/* following normalisation needs).  The pages name the reduction without fixing it; the reading  */
+/* taken here is the plain definition over what a caller would read back from D:                */
+/*   row_sumsq[i] = sum over j of  r(D[i][j])^2,   col_sum[j] = sum over i of  r(D[i][j]),       */
+/* with r() the round-to-nearest-even of the double result to the output type (the stored value) */
+/* and both sums in double, in index order.                                                      */
+/* ------------------------------------------------------------------------------------------ */
+
+static double round_to(int t, double x) {
+  switch (t) {
+    case OR_F32: return dec_f32(enc_f32(x));
+    case OR_F16: return dec_f16(enc_f16(x));
+    case OR_BF16: return dec_bf16(enc_bf16(x));
+    case OR_E4M3: return dec_e4m3(enc_e4m3(x));
+    default: return NAN;
+  }
+}
+
+/* D is M x N with element (i, j) at D[i * ld + j]. */
+int oracle_row_sumsq(int out_type, const double* D, int64_t M, int64_t N, int64_t ld, double* out) {
+  if (!elem_size(out_type) || M < 0 || N < 0 || ld < N || (M > 0 && (!D || !out))) return OR_EINVAL;
+  for (int64_t i = 0; i < M; i++) {
+    double s = 0.0;
+    for (int64_t j = 0; j < N; j++) {
+      double v = round_to(out_type, D[i * ld + j]);
+      s += v * v;
+    }
+    out[i] = s;
+  }
+  return OR_OK;
+}
+
+int oracle_col_sum(int out_type, const double* D, int64_t M, int64_t N, int64_t ld, double* out) {
+  if (!elem_size(out_type) || M < 0 || N < 0 || ld < N || (N > 0 && (!D || !out))) return OR_EINVAL;
+  for (int64_t j = 0; j < N; j++) {
+    double s = 0.0;
+    for (int64_t i = 0; i < M; i++) s += round_to(out_type, D[i * ld + j]);
+    out[j] = s;
+  }
+  return OR_OK;
+}

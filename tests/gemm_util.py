@@ -3,6 +3,7 @@ its C ABI, and compute the oracle on the same bits."""
 from __future__ import annotations
 
 import dataclasses
+import os
 
 import numpy as np
 import torch
@@ -12,6 +13,9 @@ from hierarchical_tiling_amd import htgemm as H
 from hierarchical_tiling_amd import inputs
 
 OUT_T = {"f32": "f32", "f16": "f16", "bf16": "bf16", "e4m3": "bf16"}
+# host threads for the oracle: every core this process may use, at most 16 (a GPU machine gives a
+# one-GPU job 16 CPU threads whatever the machine's core count)
+THREADS = max(1, min(16, len(os.sched_getaffinity(0))))
 # spec tolerances: fp32 relative Frobenius; 16-bit max-abs-relative; fp8 max-abs-relative
 TOL = {"f32": 1e-5, "f16": 1e-2, "bf16": 1e-2, "e4m3": 3e-2}
 
@@ -146,7 +150,7 @@ class Prepared:
         return oracle.gemm(op(self.A), op(self.B), op(self.C) if self.C is not None else None,
                            op(self.bias) if self.bias is not None else None, alpha=c.alpha,
                            beta=c.beta, scale_a=c.scale_a, scale_b=c.scale_b, act=c.act,
-                           row_scale=self.rs, col_scale=self.cs)
+                           row_scale=self.rs, col_scale=self.cs, threads=THREADS)
 
     def oracle_elems(self, rows, cols):
         c = self.case
@@ -154,7 +158,66 @@ class Prepared:
                                  op(self.C) if self.C is not None else None,
                                  op(self.bias) if self.bias is not None else None, alpha=c.alpha,
                                  beta=c.beta, scale_a=c.scale_a, scale_b=c.scale_b, act=c.act,
-                                 row_scale=self.rs, col_scale=self.cs)
+                                 row_scale=self.rs, col_scale=self.cs, threads=THREADS)
+
+    def oracle_rows(self, rows):
+        """Oracle D of whole rows `rows` (len(rows) x N): the oracle's own GEMM on the gathered
+        rows of A (and C, row_scale), so every operand element is decoded once."""
+        c = self.case
+        rows = np.asarray(rows, dtype=np.int64)
+        A = _gather(self.A, rows, np.arange(c.K))
+        C = _gather(self.C, rows, np.arange(c.N)) if self.C is not None else None
+        return oracle.gemm(A, op(self.B), C, op(self.bias) if self.bias is not None else None,
+                           alpha=c.alpha, beta=c.beta, scale_a=c.scale_a, scale_b=c.scale_b,
+                           act=c.act, row_scale=self.rs[rows] if self.rs is not None else None,
+                           col_scale=self.cs, threads=THREADS)
+
+    def oracle_cols(self, cols):
+        """Oracle D of whole columns `cols` (M x len(cols)), from the gathered columns of B (and
+        C, bias, col_scale)."""
+        c = self.case
+        cols = np.asarray(cols, dtype=np.int64)
+        B = _gather(self.B, np.arange(c.K), cols)
+        C = _gather(self.C, np.arange(c.M), cols) if self.C is not None else None
+        bias = (oracle.Operand(self.bias.storage[cols], self.bias.dtype, (1, cols.size), (cols.size, 1))
+                if self.bias is not None else None)
+        return oracle.gemm(op(self.A), B, C, bias, alpha=c.alpha, beta=c.beta,
+                           scale_a=c.scale_a, scale_b=c.scale_b, act=c.act, row_scale=self.rs,
+                           col_scale=self.cs[cols] if self.cs is not None else None,
+                           threads=THREADS)
+
+    def oracle_sample(self, got, seed=0, n_rows=64, n_cols=64, n_rand=4096):
+        """The outputs of D the oracle computes at a size where the whole product would take too
+        long on the host: n_rows whole rows and n_cols whole columns (the first and last of each
+        among them) and n_rand random elements.  Returns (got values, oracle values, what was
+        sampled), with `got` the decoded M x N device result."""
+        c = self.case
+        rng = np.random.default_rng(seed)
+        rows = _pick(rng, c.M, n_rows)
+        cols = _pick(rng, c.N, n_cols)
+        r = rng.integers(0, c.M, n_rand)
+        k = rng.integers(0, c.N, n_rand)
+        want = np.concatenate([self.oracle_rows(rows).ravel(), self.oracle_cols(cols).ravel(),
+                               self.oracle_elems(r, k)])
+        have = np.concatenate([got[rows, :].ravel(), got[:, cols].ravel(), got[r, k]])
+        what = (f"{rows.size} full rows, {cols.size} full columns and {n_rand} random outputs "
+                f"({want.size} values, {100.0 * want.size / (c.M * c.N):.2f}% of D)")
+        return have, want, what
+
+
+def _pick(rng, n, count):
+    """`count` distinct indices below n (all of them if n <= count), always with 0 and n - 1."""
+    if n <= count:
+        return np.arange(n, dtype=np.int64)
+    mid = rng.choice(np.arange(1, n - 1), size=count - 2, replace=False)
+    return np.sort(np.concatenate([[0, n - 1], mid])).astype(np.int64)
+
+
+def _gather(m, rows, cols):
+    """Operand holding elements (rows[i], cols[j]) of host matrix m, row-major."""
+    idx = rows[:, None] * m.strides[0] + cols[None, :] * m.strides[1]
+    bits = m.storage[idx.ravel()] if idx.size else m.storage[:0]
+    return oracle.Operand(bits, m.dtype, (rows.size, cols.size), (max(cols.size, 1), 1))
 
 
 def error(dtype, got, want):

@@ -259,6 +259,10 @@ def test_grouped_ragged_m_fields(fake_gfx950):
     d = desc(**base)
     d.ragged_m = 2
     assert status_of(d) == H.GEMM_ERR_INVALID_ARG
+    # the batch field counts the groups (offsets holds batch + 1 values): at least one group
+    for groups in (0, -1):
+        assert status_of(desc(**dict(base, batch=groups))) == H.GEMM_ERR_INVALID_ARG
+    assert _info(desc(**dict(base, batch=1))).split_k == 1
     small = _info(H.make_desc(16, 16384, 8192, "e4m3", (8192, 1), (1, 8192), (16384, 1), batch=4,
                               batch_strides=(0, 16384 * 8192, 0, 0), ragged_m=True))
     assert b"skinny" not in small.name

@@ -291,3 +291,26 @@ def test_local_tile_and_partition_errors(call, code):
     with pytest.raises(H.LayoutError) as e:
         call()
     assert e.value.status == code
+
+
+def test_eval_through_the_c_abi_with_integer_coordinates():
+    # the boundary's own form: a caller-owned int64 array and its rank ("CUTLASS, CuTe, and CUDA
+    # Tile", introduction: (4,3):(3,1) maps (1,0) to 3 and (0,1) to 1)
+    import ctypes
+    L = H.lib()
+    out = ctypes.c_int64()
+
+    def ev(layout, coord):
+        arr = (ctypes.c_int64 * len(coord))(*coord)
+        rc = L.ht_layout_eval(layout.encode(), arr, len(coord), ctypes.byref(out))
+        return rc, out.value
+
+    assert ev("(4,3):(3,1)", [1, 0]) == (0, 3)
+    assert ev("(4,3):(3,1)", [0, 1]) == (0, 1)
+    # rank 1 is a 1-D coordinate (leftmost mode fastest): 5 -> (1, 1) -> 3 + 1
+    assert ev("(4,3):(3,1)", [5]) == (0, 4)
+    # one integer per top-level mode of a nested layout: the composition pin's element 11
+    assert ev("((2,2),3):((24,2),8)", [3, 2]) == (0, 42)
+    assert ev("(4,3):(3,1)", [4, 0])[0] == 2        # outside the shape: HT_ERR_RANGE
+    assert ev("(4,3):(3,1)", [1, 0, 0])[0] == 2     # rank is neither 1 nor the mode count
+    assert ev("(4,3):(3", [0, 0])[0] == 1           # bad text: HT_ERR_PARSE

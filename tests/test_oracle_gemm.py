@@ -281,3 +281,51 @@ def test_empty_shapes():
     A0 = oracle.Operand(np.zeros(0, np.uint16), "bf16", (3, 0), (1, 1))
     B0 = oracle.Operand(np.zeros(0, np.uint16), "bf16", (0, 2), (1, 1))
     np.testing.assert_array_equal(oracle.gemm(A0, B0), np.zeros((3, 2)))   # K = 0: empty sum
+
+
+# ---- reductions of the stored output (the next layer's normalisation inputs) ----------------
+# Reading of "CUTLASS", Part IV Stage 5 (a fused reduction for the next layer's norm): the sum of
+# squares of each row and the sum of each column of D as stored, i.e. rounded to the output type.
+
+def test_reductions_round_before_summing_hand_values():
+    # 1 + 2^-9 lies below the bf16 midpoint of 1 and 1 + 2^-7 and rounds to 1; 1 + 2^-8 is that
+    # midpoint and rounds to the even neighbour 1; both are exact in fp16 (10 stored bits).
+    D = np.array([[1 + 2.0 ** -9, 3.0, -0.5], [2.0, 1 + 2.0 ** -8, 0.25]])
+    assert oracle.row_sumsq(D, "bf16").tolist() == [1 + 9 + 0.25, 4 + 1 + 0.0625]
+    assert oracle.col_sum(D, "bf16").tolist() == [3.0, 4.0, -0.25]
+    f16 = oracle.row_sumsq(D, "f16")
+    x, y = Fraction(1) + Fraction(1, 512), Fraction(1) + Fraction(1, 256)
+    assert Fraction(f16[0]) == x * x + 9 + Fraction(1, 4)
+    assert Fraction(f16[1]) == 4 + y * y + Fraction(1, 16)
+    assert oracle.col_sum(D, "f16").tolist() == [3 + 2.0 ** -9, 4 + 2.0 ** -8, -0.25]
+
+
+@pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
+def test_reductions_of_a_constant_matrix(dt):
+    # every stored value is r = round(1/3): row sums of squares are N r^2, column sums M r
+    M, N = 7, 5
+    r = Fraction(float(oracle.decode(dt, oracle.encode_rne(dt, np.array([1 / 3])))[0]))
+    D = np.full((M, N), 1 / 3)
+    assert all(Fraction(v) == N * r * r for v in oracle.row_sumsq(D, dt))
+    assert all(Fraction(v) == M * r for v in oracle.col_sum(D, dt))
+
+
+def test_reductions_of_identity_times_b_are_those_of_b():
+    # D = I @ B with B already in the output type: every stored D value is B's, so the reductions
+    # are B's own row sums of squares and column sums, computed here with exact rationals
+    K, N = 6, 9
+    b_bits = inputs.quantize(inputs.draw(77, K * N, "normal"), "bf16")
+    eye = inputs.quantize(np.eye(K).ravel(), "bf16")
+    A, _ = operand(eye, "bf16", K, K, "row")
+    B, _ = operand(b_bits, "bf16", K, N, "col")
+    D = oracle.gemm(A, B)
+    b = exact_values(b_bits, "bf16")
+    for i, v in enumerate(oracle.row_sumsq(D, "bf16")):
+        assert Fraction(v) == sum(b[i * N + j] ** 2 for j in range(N))
+    for j, v in enumerate(oracle.col_sum(D, "bf16")):
+        assert Fraction(v) == sum(b[i * N + j] for i in range(K))
+
+
+def test_reductions_of_empty_shapes():
+    assert oracle.row_sumsq(np.zeros((3, 0)), "bf16").tolist() == [0.0, 0.0, 0.0]
+    assert oracle.col_sum(np.zeros((0, 2)), "bf16").tolist() == [0.0, 0.0]
