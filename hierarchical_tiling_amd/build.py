@@ -34,12 +34,14 @@ SOURCES = [
     ("table_f32.hip", HIP),
     ("table.cpp", HIP),
     ("reduce.hip", HIP),
+    ("probe.hip", HIP),
     ("api.cpp", HIP),
     ("layout.cpp", ["g++"] + COMMON),
 ]
 
 
 HEADERS = [os.path.join(CSRC, "kernels.h"), os.path.join(CSRC, "gemm_internal.h"),
+           os.path.join(CSRC, "atom_maps.h"),
            os.path.join(ROOT, "include", "htgemm.h"), os.path.join(ROOT, "include", "htlayout.h")]
 
 

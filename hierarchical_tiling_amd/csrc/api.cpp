@@ -10,12 +10,16 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cstdlib>
 #include <cstring>
 #include <new>
+#include <utility>
+#include <vector>
 
 #include "../../include/htgemm.h"
 #include "../../include/htlayout.h"
+#include "atom_maps.h"
 #include "gemm_internal.h"
 
 using namespace htk;
@@ -228,6 +232,95 @@ int choose(const gemm_handle_s& h, bool vec_a, bool vec_b, bool want_vec, int sp
   return best >= 0 ? best : best_small;
 }
 
+// ---- lane maps checked with the layout helper ---------------------------------------------
+// An MFMA atom's A/B and C fragment maps are layouts from (lane, value) to a place in the
+// instruction's tile; a wrong map gives silently wrong results ("A10 - CuTe, CUTLASS & CuTile",
+// section 3.3 and section 6 Pitfall 2; "CUTLASS", Part V: the layout algebra is what catches a
+// wrong thread layout).  Once per atom the kernels' tables (atom_maps.h) are checked against the
+// layout helper's evaluation of the same layouts written in the pages' notation: same function,
+// a bijection onto the tile (the fragment closure: 64 lanes x values per lane = the tile), and
+// lane l on row / column l % MI as the instruction requires.  The LDS swizzles are checked the
+// same way against the helper's Swizzle functor.
+
+// the helper's table of `text`, or empty if it does not parse or has the wrong size
+std::vector<int64_t> helper_table(const char* text, int64_t n) {
+  int64_t size = 0;
+  if (ht_layout_size(text, &size) != HT_OK || size != n) return {};
+  std::vector<int64_t> t((size_t)n);
+  if (ht_layout_table(text, t.data(), n) != HT_OK) return {};
+  return t;
+}
+
+bool is_bijection(const std::vector<int64_t>& t, int64_t n) {
+  std::vector<char> seen((size_t)n, 0);
+  for (int64_t v : t) {
+    if (v < 0 || v >= n || seen[(size_t)v]) return false;
+    seen[(size_t)v] = 1;
+  }
+  return (int64_t)t.size() == n;
+}
+
+bool check_atom_now(int idx) {
+  const AtomMaps& M = kAtomMaps[idx];
+  const std::vector<int64_t> op = helper_table(M.op.text, 64 * M.vpl);
+  const std::vector<int64_t> acc = helper_table(M.acc.text, 64 * M.nacc);
+  if (op.empty() || acc.empty()) return false;
+  if (64 * M.vpl != M.mi * M.ki || 64 * M.nacc != M.mi * M.mi) return false;  // closure
+  if (!is_bijection(op, (int64_t)M.mi * M.ki) || !is_bijection(acc, (int64_t)M.mi * M.mi)) return false;
+  for (int i = 0; i < 64 * M.vpl; ++i)
+    if (op[(size_t)i] != layout_eval(M.op, i) || (i < 64 && layout_eval(M.op, i) % M.mi != i % M.mi))
+      return false;
+  for (int i = 0; i < 64 * M.nacc; ++i)
+    if (acc[(size_t)i] != layout_eval(M.acc, i) || layout_eval(M.acc, i) / M.mi != (i % 64) % M.mi)
+      return false;
+  return true;
+}
+
+template <int CH> bool check_swizzle_now() {
+  for (int row = 0; row < 256; ++row)
+    for (int c = 0; c < CH; ++c) {
+      const int slot = swizzled_slot<CH>(row, c);
+      if (slot != (int)ht_swizzle(row * CH + c, RowSwizzle<CH>::B, RowSwizzle<CH>::M, RowSwizzle<CH>::S))
+        return false;
+      if (slot / CH != row) return false;  // the swizzle stays within the row
+    }
+  return true;
+}
+
+// 0: not checked yet, 1: agrees, 2: disagrees (the result is the same every time)
+std::atomic<int> g_atom_state[kNumAtomMaps];
+std::atomic<int> g_swizzle_state[2];
+
+bool cached(std::atomic<int>& st, bool (*fn)()) {
+  int v = st.load(std::memory_order_acquire);
+  if (v == 0) {
+    v = fn() ? 1 : 2;
+    st.store(v, std::memory_order_release);
+  }
+  return v == 1;
+}
+
+template <int IDX> bool check_atom_fn() { return check_atom_now(IDX); }
+template <int... I>
+bool check_atom_dispatch(int idx, std::integer_sequence<int, I...>) {
+  bool ok = false;
+  ((idx == I ? (ok = cached(g_atom_state[I], &check_atom_fn<I>), 0) : 0), ...);
+  return ok;
+}
+
+bool atom_ok(int dtype, int mi) {
+  const int idx = atom_index(dtype, mi);
+  return idx >= 0 && check_atom_dispatch(idx, std::make_integer_sequence<int, kNumAtomMaps>{});
+}
+
+// The lane maps and LDS swizzle of table entry e agree with the layout helper.
+bool entry_maps_ok(const KernelEntry& e) {
+  if (!atom_ok(e.dtype, e.mi)) return false;
+  if (e.lds_row_chunks == 8) return cached(g_swizzle_state[1], &check_swizzle_now<8>);
+  if (e.lds_row_chunks == 4) return cached(g_swizzle_state[0], &check_swizzle_now<4>);
+  return e.lds_row_chunks == 0;
+}
+
 int check_arch() {
   const char* fake = std::getenv("HTGEMM_FAKE_ARCH");
   if (fake && *fake) return std::strncmp(fake, "gfx950", 6) == 0 ? GEMM_OK : GEMM_ERR_ARCH;
@@ -315,6 +408,8 @@ int gemm_create(const gemm_desc* desc, gemm_t* out) {
     h.cfg = (va && vb) ? choose(h, va, vb, true, split_req) : -1;
     if (h.cfg < 0) h.cfg = h.fallback;
   }
+  // the chosen kernels' thread-to-data maps, checked once per atom against the layout helper
+  if (!entry_maps_ok(table()[h.cfg]) || !entry_maps_ok(table()[h.fallback])) return GEMM_ERR_LANE_MAP;
   h.group_m = 4;
   plan_split(table()[h.cfg], d, split_req, &h.split_cfg, &h.kps_cfg);
   plan_split(table()[h.fallback], d, split_req, &h.split_fb, &h.kps_fb);
@@ -561,11 +656,23 @@ const char* gemm_status_string(int status) {
     case GEMM_ERR_BAD_HANDLE: return "invalid or destroyed handle";
     case GEMM_ERR_NO_CONFIG: return "no tile-table entry can run this problem";
     case GEMM_ERR_HIP: return "HIP runtime error";
+    case GEMM_ERR_LANE_MAP: return "a kernel lane map disagrees with the layout helper";
     default: return "unknown status";
   }
 }
 
 int gemm_num_configs(void) { return table_size(); }
+
+int gemm_atom_layouts(int dtype, int mi, char* op, char* acc, size_t cap) {
+  const int idx = atom_index(dtype, mi);
+  if (idx < 0 || !op || !acc) return GEMM_ERR_INVALID_ARG;
+  const AtomMaps& M = kAtomMaps[idx];
+  const size_t a = std::strlen(M.op.text), c = std::strlen(M.acc.text);
+  if (a + 1 > cap || c + 1 > cap) return GEMM_ERR_INVALID_ARG;
+  std::memcpy(op, M.op.text, a + 1);
+  std::memcpy(acc, M.acc.text, c + 1);
+  return atom_ok(dtype, mi) ? GEMM_OK : GEMM_ERR_LANE_MAP;
+}
 
 int gemm_config_name(int idx, char* out, size_t cap) {
   if (idx < 0 || idx >= table_size() || !out) return GEMM_ERR_INVALID_ARG;

@@ -63,6 +63,8 @@ struct KernelEntry {
   launch_fn launch;
   int realign;        // 1: realigned 16-byte loads of 2-byte elements (31-bit tile offsets)
   int rank_one_round; // rank when all workgroups fit on the CUs at once (one tile per CU)
+  int mi;             // MFMA atom: MI x MI output block (its layouts are in atom_maps.h)
+  int lds_row_chunks; // 16-byte chunks per swizzled LDS row of the operand tiles (4 or 8)
 };
 
 const KernelEntry* table();

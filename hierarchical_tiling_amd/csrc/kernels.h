@@ -43,6 +43,7 @@
 
 #include <utility>
 
+#include "atom_maps.h"
 #include "gemm_internal.h"
 
 namespace htk {
@@ -186,10 +187,68 @@ template <> struct Atom<DT_F32, 16> {
   }
 };
 
-// Row (within the MI x MI block) of accumulator register r of lane l.
-template <int MI> __device__ __forceinline__ int acc_row(int l, int r) {
-  if constexpr (MI == 32) return 8 * (r >> 2) + 4 * (l >> 5) + (r & 3);
-  else return 4 * (l >> 4) + r;
+// Positions taken from the atom's layouts (atom_maps.h), so the kernels' fragment addressing and
+// accumulator placement are the layout functions the host checks against the layout helper and
+// the index probe checks against the hardware.
+template <int DT, int MI> struct Maps {
+  static constexpr int idx = atom_index(DT, MI);
+  static_assert(idx >= 0, "no layout for this atom");
+  static constexpr AtomMaps M = kAtomMaps[idx];
+  // values of one lane's contiguous k run per instruction (16 bytes, or one f32)
+  static constexpr int RUN = M.vpl < 16 / dtype_size(DT) ? M.vpl : 16 / dtype_size(DT);
+  // the accumulator registers of a lane all lie in one column (offsets of the value modes stay
+  // below MI), so the column of a lane's accumulators is taken once per lane
+  static constexpr bool one_column() {
+    for (int r = 0; r < M.nacc; ++r)
+      if (value_offset(M.acc, r) >= MI) return false;
+    return true;
+  }
+  static_assert(one_column(), "accumulator values of a lane span one column");
+};
+// Offset of layout WHICH (0: operand, 1: accumulator) of atom IDX at a lane, with the shape and
+// stride as compile-time constants: a sum of ((l / P_i) % S_i) * D_i over the lane modes (P_i the
+// product of the shapes before mode i).
+template <int IDX, int WHICH> struct LaneOffset {
+  static constexpr const AtomLayout& L() { return WHICH == 0 ? kAtomMaps[IDX].op : kAtomMaps[IDX].acc; }
+  static constexpr int prod(int i) {
+    int p = 1;
+    for (int j = 0; j < i; ++j) p *= L().shape[j];
+    return p;
+  }
+  template <int I> __device__ static __forceinline__ int term(unsigned l) {
+    constexpr int P = prod(I);
+    if constexpr (I >= L().n || P >= 64) return 0;  // past the lane modes
+    else return (int)((l / (unsigned)P) % (unsigned)L().shape[I]) * L().stride[I];
+  }
+  __device__ static __forceinline__ int at(unsigned l) {
+    return term<0>(l) + term<1>(l) + term<2>(l) + term<3>(l);
+  }
+};
+template <int DT, int MI> struct MapRefs {
+  typedef LaneOffset<atom_index(DT, MI), 0> op;
+  typedef LaneOffset<atom_index(DT, MI), 1> acc;
+};
+// Row (within the MI x MI block) and column of accumulator register r of lane l.
+template <int DT, int MI, class R> __device__ __forceinline__ int acc_row(int l, R) {
+  constexpr int vo = value_offset(Maps<DT, MI>::M.acc, R::value);
+  const int lo = MapRefs<DT, MI>::acc::at((unsigned)l);
+  return (int)((unsigned)(lo + vo) % (unsigned)MI);
+}
+template <int DT, int MI, class R> __device__ __forceinline__ int acc_col(int l, R) {
+  constexpr int vo = value_offset(Maps<DT, MI>::M.acc, R::value);
+  const int lo = MapRefs<DT, MI>::acc::at((unsigned)l);
+  return (int)((unsigned)(lo + vo) / (unsigned)MI);
+}
+// Operand fragments: the row of A (column of B) lane l supplies, and the 16-byte chunk of an LDS
+// row holding the start of its first k run (chunks of later runs and substeps follow every
+// 64 / MI chunks).
+template <int DT, int MI> __device__ __forceinline__ int frag_row(int l) {
+  const int lo = MapRefs<DT, MI>::op::at((unsigned)l);
+  return (int)((unsigned)lo % (unsigned)MI);
+}
+template <int DT, int MI> __device__ __forceinline__ int frag_chunk(int l) {
+  const int lo = MapRefs<DT, MI>::op::at((unsigned)l);
+  return (int)((unsigned)lo / (unsigned)(MI * Maps<DT, MI>::RUN));
 }
 
 // ------------------------------------------------------------------------------------------
@@ -365,9 +424,9 @@ __device__ __forceinline__ void store_partial(const KParams& p, const AccT (&acc
                   : p.workspace + (int64_t)blockIdx.y * p.M * p.N;
   static_for<RM>([&](auto i) {
     static_for<RN>([&](auto j) {
-      const int64_t col = n0 + wn * WTN + j * MI + (lane % MI);
       static_for<At::NACC>([&](auto r) {
-        const int64_t row = m0 + wm * WTM + i * MI + acc_row<MI>(lane, r);
+        const int64_t col = n0 + wn * WTN + j * MI + acc_col<DT, MI>(lane, r);
+        const int64_t row = m0 + wm * WTM + i * MI + acc_row<DT, MI>(lane, r);
         if (row < p.M && col < p.N)
           w[tail ? (row - m0) * BN + (col - n0) : row * p.N + col] = acc[i][j][(int)r];
       });
@@ -414,14 +473,16 @@ __global__ __launch_bounds__(256) void gemm_tail_reduce(const KParams p) {
 // Every loader has the same interface: init() once per tile, load<PRED>(k0) for the k-tile at
 // k0 (PRED: zero-fill elements at k >= K), store() into one LDS stage.
 // ------------------------------------------------------------------------------------------
-// Chunk slot of (row, chunk): the XOR key is (row >> 1) & 7.  A ds_read_b128 phase serves 16
-// lanes = 256 bytes = all 64 banks; the 16 lanes of an MFMA fragment read are 16 consecutive
-// rows at one logical chunk, and with this key their 16-byte chunks land on 16 different
-// 16-byte bank groups (rows 2m and 2m+1 differ in the 128-byte half, rows 2m..2m+14 in the XOR).
-// A 16-lane phase of the row-wise tile store covers two whole rows, also conflict free.
+// Chunk slot of (row, chunk): Swizzle<3,0,4> on the chunk offset row * 8 + chunk, i.e. the XOR
+// key is (row >> 1) & 7 (atom_maps.h).  A ds_read_b128 phase serves 16 lanes = 256 bytes = all
+// 64 banks; the 16 lanes of an MFMA fragment read are 16 consecutive rows at one logical chunk,
+// and with this key their 16-byte chunks land on 16 different 16-byte bank groups (rows 2m and
+// 2m+1 differ in the 128-byte half, rows 2m..2m+14 in the XOR).  A 16-lane phase of the row-wise
+// tile store covers two whole rows, also conflict free.  Rows longer than 128 bytes (CH a
+// multiple of 8) keep the key of their first 8 chunks in every 8-chunk group.
 template <int CH> __device__ __forceinline__ int lds_slot(int row, int chunk) {
   static_assert(CH % 8 == 0, "rows must be a multiple of 128 bytes");
-  return row * CH + (chunk ^ ((row >> 1) & 7));
+  return row * CH + (chunk & ~7) + (swizzled_slot<8>(row, chunk & 7) - row * 8);
 }
 
 // Buffer descriptor over `bytes` bytes from `base` (gfx9 raw buffer: stride 0).  Loads whose
@@ -845,8 +906,9 @@ __device__ __forceinline__ void epilogue(const KParams& p, AccT (&acc)[RM][RN], 
   // condition, so the common case (no C) carries no per-element branches:
   // y = act((alpha * acc + beta * C) + bias[n]).
   float bias_v[RN], cs_v[RN];
+  const int acol = acc_col<DT, MI>(lane, std::integral_constant<int, 0>{});  // the same for every register of the lane
   static_for<RN>([&](auto j) {
-    const int64_t col = n0 + wn * WTN + j * MI + (lane % MI);
+    const int64_t col = n0 + wn * WTN + j * MI + acol;
     bias_v[j] = has_bias && col < p.N ? O::load(p.bias, col) : 0.f;
     cs_v[j] = has_cs && col < p.N ? p.col_scale[col] : 1.f;
   });
@@ -857,7 +919,7 @@ __device__ __forceinline__ void epilogue(const KParams& p, AccT (&acc)[RM][RN], 
     if (alpha != 1.f) each([&](auto j, auto r) { acc[i][j][(int)r] *= alpha; });  // x1 is exact
     if (has_rs) {
       each([&](auto j, auto r) {
-        const int64_t row = m0 + wm * WTM + i * MI + acc_row<MI>(lane, r);
+        const int64_t row = m0 + wm * WTM + i * MI + acc_row<DT, MI>(lane, r);
         acc[i][j][(int)r] *= row < p.M ? p.row_scale[row] : 1.f;
       });
     }
@@ -865,8 +927,8 @@ __device__ __forceinline__ void epilogue(const KParams& p, AccT (&acc)[RM][RN], 
     if (has_c && p.c_span > 0) {
       const __amdgpu_buffer_rsrc_t cr = make_rsrc((const char*)p.C, p.c_span);
       each([&](auto j, auto r) {
-        const int64_t col = n0 + wn * WTN + j * MI + (lane % MI);
-        const int64_t row = m0 + wm * WTM + i * MI + acc_row<MI>(lane, r);
+        const int64_t col = n0 + wn * WTN + j * MI + acol;
+        const int64_t row = m0 + wm * WTM + i * MI + acc_row<DT, MI>(lane, r);
         const uint32_t off = col < p.N && row < p.M
                                  ? (uint32_t)((row * p.c_sm + col * p.c_sn) * (int64_t)sizeof(OT))
                                  : kOobOffset;
@@ -874,8 +936,8 @@ __device__ __forceinline__ void epilogue(const KParams& p, AccT (&acc)[RM][RN], 
       });
     } else if (has_c) {  // C spans 2^31 bytes or more: predicated pointer loads
       each([&](auto j, auto r) {
-        const int64_t col = n0 + wn * WTN + j * MI + (lane % MI);
-        const int64_t row = m0 + wm * WTM + i * MI + acc_row<MI>(lane, r);
+        const int64_t col = n0 + wn * WTN + j * MI + acol;
+        const int64_t row = m0 + wm * WTM + i * MI + acc_row<DT, MI>(lane, r);
         if (col < p.N && row < p.M) acc[i][j][(int)r] += beta * O::load(p.C, row * p.c_sm + col * p.c_sn);
       });
     }
@@ -884,10 +946,10 @@ __device__ __forceinline__ void epilogue(const KParams& p, AccT (&acc)[RM][RN], 
     else if (act == 1) each([&](auto j, auto r) { acc[i][j][(int)r] = relu(acc[i][j][(int)r]); });
     else if (act == 3) each([&](auto j, auto r) { acc[i][j][(int)r] = silu(acc[i][j][(int)r]); });
     static_for<RN>([&](auto j) {
-      const int lc = wn * WTN + j * MI + (lane % MI);
+      const int lc = wn * WTN + j * MI + acol;
       const int64_t col = n0 + lc;
       static_for<At::NACC>([&](auto r) {
-        const int lr = wm * WTM + i * MI + acc_row<MI>(lane, r);
+        const int lr = wm * WTM + i * MI + acc_row<DT, MI>(lane, r);
         const float v = acc[i][j][(int)r];
         if constexpr (REPACK) {
           tile[lr * PITCH + lc] = to_bits(v, std::integral_constant<int, ODT>{});
@@ -1008,7 +1070,7 @@ __global__ __launch_bounds__(WM * WN * 64, BM * BN <= 128 * 128 && (AK || BKM) ?
   const int nfull = (int)(kr.len / BKE);
 
   // fragment addressing: lane row within an atom, and lane group along k
-  const int frow = lane % MI, fgrp = lane / MI;
+  const int frow = frag_row<DT, MI>(lane), fgrp = frag_chunk<DT, MI>(lane);
   u32x4 fa[2][RM][At::UNITS], fb[2][RN][At::UNITS];
   auto read_frags = [&](auto buf, const u32x4* stage, auto sub) {
     const u32x4* As = stage;
@@ -1092,14 +1154,15 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 
 // XOR key of a row: 16 consecutive rows (one ds_read_b128 phase) must cover all 16 16-byte
 // positions of a 256-byte bank window.  With 64-byte rows four rows share a window, so rows
-// r, r+4, r+8, r+12 need different keys: (r >> 2) & 3.  With 128-byte rows two rows share a
-// window: (r >> 1) & 7, as in the register-staged kernel.
+// r, r+4, r+8, r+12 need different keys: (r >> 2) & 3, Swizzle<2,0,4> on the chunk offset.
+// With 128-byte rows two rows share a window: (r >> 1) & 7, Swizzle<3,0,4>, as in the
+// register-staged kernel (atom_maps.h).
 template <int CH> __device__ __forceinline__ int row_key(int row) {
   static_assert(CH == 4 || CH == 8, "64- or 128-byte rows");
-  return CH == 4 ? ((row >> 2) & 3) : ((row >> 1) & 7);
+  return swizzled_slot<CH>(row, 0) - row * CH;
 }
 template <int CH> __device__ __forceinline__ int dslot(int row, int chunk) {
-  return row * CH + (chunk ^ row_key<CH>(row));
+  return swizzled_slot<CH>(row, chunk);
 }
 
 // s_waitcnt with vmcnt = V (and lgkmcnt = 0 when LGKM0), other counters left free.
@@ -1221,7 +1284,7 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void gemm_dma(const KParams p_) 
     });
   };
 
-  const int frow = lane % MI, fgrp = lane / MI;
+  const int frow = frag_row<DT, MI>(lane), fgrp = frag_chunk<DT, MI>(lane);
   u32x4 fa[2][RM][At::UNITS], fb[2][RN][At::UNITS];
   auto read_frags = [&](auto buf, const u32x4* st, auto sub) {
     static_for<At::UNITS>([&](auto x) {
@@ -1399,7 +1462,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_ring(const KParams p_) {
     });
   };
 
-  const int frow = lane % MI, fgrp = lane / MI;
+  const int frow = frag_row<DT, MI>(lane), fgrp = frag_chunk<DT, MI>(lane);
   u32x4 fa[2][RM][At::UNITS], fb[S][RN][At::UNITS];
   auto read_a = [&](auto buf, const u32x4* sa, auto sub) {
     static_for<At::UNITS>([&](auto x) {
@@ -1567,13 +1630,14 @@ static hipError_t launch_ring(const KParams& p, hipStream_t s, dim3 grid) {
 // A (M x K, a few hundred KiB) stays in L2; the WN waves that share a K slice read the same A
 // lines, so after the first they hit in the CU's vector L1 and A costs the CU's memory pipe
 // 1/WN of what it would if every wave read its own.  Atoms: 16x16xKSTEP MFMA (16x16x128 e4m3,
-// 16x16x32 bf16/fp16); lane l supplies row (or column) l % 16 and the k-run of lane group l / 16.
+// 16x16x32 bf16/fp16) with the atoms' layouts (atom_maps.h): lane l supplies row (or column)
+// l % 16 and the 16-byte chunks l / 16 (+ 4 for the second chunk of an e4m3 lane) of a k-step.
 // ------------------------------------------------------------------------------------------
 template <int DT, int WK, int WN, int NBW, int U, int OCC>
 __global__ __launch_bounds__(WK * WN * 64, OCC) void gemm_skinny(const KParams p_) {
   const KParams p = batch_view(p_);
   typedef Atom<DT, 16> At;
-  typedef typename At::acc_t acc_t;  // 4 floats: rows 4*(l/16)+r, column l%16
+  typedef typename At::acc_t acc_t;  // 4 floats: rows acc_row(l, r), column acc_col(l, r)
   constexpr int NT = WK * WN * 64;
   constexpr int SZ = Ty<DT>::SZ;
   constexpr int LB = At::UNITS * 16;          // bytes per lane per operand per MFMA
@@ -1586,7 +1650,7 @@ __global__ __launch_bounds__(WK * WN * 64, OCC) void gemm_skinny(const KParams p
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wk = wave % WK, wn = wave / WK;
   const int64_t n0 = (int64_t)blockIdx.x * BN;
-  const int lr = lane & 15, lg = lane >> 4;
+  const int lr = frag_row<DT, 16>(lane), lg = frag_chunk<DT, 16>(lane);
 
   // K split: wave (wk, .) owns k-steps [wk*per, min((wk+1)*per, nks))
   const int64_t nks = (p.K + KSTEP - 1) / KSTEP;
@@ -1595,15 +1659,16 @@ __global__ __launch_bounds__(WK * WN * 64, OCC) void gemm_skinny(const KParams p
   const int64_t ks1 = min(ks0 + per, nks);
 
   // A rows lr (zero past M); B columns n0 + 16*b + lr (zero past N, or past this workgroup's
-  // BN columns).  Offsets of a lane's k-run within a k-step: lg*LB bytes.  Both spans stay below
-  // 2^31 bytes (checked on the host), so the offset 0x80000000 is outside either descriptor.
+  // BN columns).  Offset of chunk x of a lane's k-runs within a k-step: (lg + 4x)*16 bytes.  Both
+  // spans stay below 2^31 bytes (checked on the host), so the offset 0x80000000 is outside
+  // either descriptor.
   const char* a_base = uniform_ptr((const char*)p.A);
   const char* b_base = uniform_ptr((const char*)p.B + n0 * p.ldb * SZ);
   const int64_t a_span = uniform_i64(((p.M - 1) * p.lda + p.K) * SZ);
   const int64_t b_span = uniform_i64(((min((int64_t)BN, p.N - n0) - 1) * p.ldb + p.K) * SZ);
-  const uint32_t a_off = (uint32_t)(lr * p.lda * SZ + lg * LB);
+  const uint32_t a_off = (uint32_t)(lr * p.lda * SZ + lg * 16);
   const uint32_t b_blk = (uint32_t)(16 * p.ldb * SZ);
-  const uint32_t b_off = (uint32_t)(lr * p.ldb * SZ + lg * LB) + (uint32_t)(wn * NBW) * b_blk;
+  const uint32_t b_off = (uint32_t)(lr * p.ldb * SZ + lg * 16) + (uint32_t)(wn * NBW) * b_blk;
 
   acc_t acc[NBW];
   static_for<NBW>([&](auto b) { acc[b] = acc_t{}; });
@@ -1622,9 +1687,9 @@ __global__ __launch_bounds__(WK * WN * 64, OCC) void gemm_skinny(const KParams p
       const int64_t k0 = (ks + u) * KSTEP;
       const bool live = ks + u < ks1;
       static_for<At::UNITS>([&](auto x) {
-        const int64_t kc = k0 + (lg * LB + x * 16) / SZ;  // first element of this 16-byte chunk
+        const int64_t kc = k0 + (lg + 4 * x) * (16 / SZ);  // first element of this chunk
         const bool ok = live && kc < p.K;
-        const uint32_t ko = (uint32_t)(k0 * SZ) + x * 16;
+        const uint32_t ko = (uint32_t)(k0 * SZ) + x * 64;
         f.a[u][x] = __builtin_amdgcn_raw_buffer_load_b128(ra, ok ? a_off + ko : 0x80000000u, 0, 0);
         static_for<NBW>([&](auto b) {
           f.b[u][b][x] = __builtin_amdgcn_raw_buffer_load_b128(
@@ -1654,7 +1719,9 @@ __global__ __launch_bounds__(WK * WN * 64, OCC) void gemm_skinny(const KParams p
 
   // partial sums -> LDS; reduction over the WK slices; epilogue
   static_for<NBW>([&](auto b) {
-    static_for<4>([&](auto r) { part[wk][wn * NBW + b][4 * lg + r][lr] = acc[b][(int)r]; });
+    static_for<4>([&](auto r) {
+      part[wk][wn * NBW + b][acc_row<DT, 16>(lane, r)][acc_col<DT, 16>(lane, r)] = acc[b][(int)r];
+    });
   });
   __syncthreads();
   constexpr int ODT = out_dtype(DT);
@@ -1698,7 +1765,7 @@ template <int DT, int WK, int NBW, int R, int OCC>
 __global__ __launch_bounds__(WK * 64, OCC) void gemm_skinny_dma(const KParams p_) {
   const KParams p = batch_view(p_);
   typedef Atom<DT, 16> At;
-  typedef typename At::acc_t acc_t;               // 4 floats: rows 4*(l/16)+r, column l%16
+  typedef typename At::acc_t acc_t;               // 4 floats: rows acc_row(l, r), column acc_col(l, r)
   constexpr int SZ = Ty<DT>::SZ;
   constexpr int BN = NBW * 16;                    // columns per workgroup
   constexpr int ROWS = BN + 16;                   // LDS rows per block: BN columns of B, 16 rows of A
@@ -1715,7 +1782,7 @@ __global__ __launch_bounds__(WK * 64, OCC) void gemm_skinny_dma(const KParams p_
 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t n0 = (int64_t)blockIdx.x * BN;
-  const int lr = lane & 15, lg = lane >> 4;
+  const int lr = frag_row<DT, 16>(lane), lg = frag_chunk<DT, 16>(lane);
 
   // K split: wave w owns blocks [w*per, min((w+1)*per, nb))
   const int64_t nb = (p.K + BKE - 1) / BKE;
@@ -1729,7 +1796,7 @@ __global__ __launch_bounds__(WK * 64, OCC) void gemm_skinny_dma(const KParams p_
   const int64_t b_span = uniform_i64(((min((int64_t)BN, p.N - n0) - 1) * p.ldb + p.K) * SZ);
   const int64_t kbytes = p.K * SZ;
   // DMA lane: LDS row 8c + lane/8 of the block, slot lane%8, holding logical chunk slot ^ key(row)
-  auto key = [](int row) { return (row >> 1) & 7; };
+  auto key = [](int row) { return row_key<8>(row); };
 
   acc_t acc[NBW];
   static_for<NBW>([&](auto b) { acc[b] = acc_t{}; });
@@ -1758,13 +1825,13 @@ __global__ __launch_bounds__(WK * 64, OCC) void gemm_skinny_dma(const KParams p_
     static_for<MPB>([&](auto m) {
       u32x4 fa[At::UNITS];
       static_for<At::UNITS>([&](auto x) {
-        const int row = BN + lr, chunk = (m * 4 + lg) * At::UNITS + x;
+        const int row = BN + lr, chunk = lg + 4 * (m * At::UNITS + x);
         fa[x] = blk[row * 8 + (chunk ^ key(row))];
       });
       static_for<NBW>([&](auto b) {
         u32x4 fb[At::UNITS];
         static_for<At::UNITS>([&](auto x) {
-          const int row = 16 * b + lr, chunk = (m * 4 + lg) * At::UNITS + x;
+          const int row = 16 * b + lr, chunk = lg + 4 * (m * At::UNITS + x);
           fb[x] = blk[row * 8 + (chunk ^ key(row))];
         });
         At::mma(acc[b], fa, fb, 0);
@@ -1791,7 +1858,9 @@ __global__ __launch_bounds__(WK * 64, OCC) void gemm_skinny_dma(const KParams p_
   float* part = reinterpret_cast<float*>(&ring[0][0][0]);  // [WK][NBW][16][16]
   static_assert(sizeof(ring) >= sizeof(float) * WK * NBW * 256, "reduction buffer");
   static_for<NBW>([&](auto b) {
-    static_for<4>([&](auto r) { part[((wave * NBW + b) * 16 + 4 * lg + r) * 16 + lr] = acc[b][(int)r]; });
+    static_for<4>([&](auto r) {
+      part[((wave * NBW + b) * 16 + acc_row<DT, 16>(lane, r)) * 16 + acc_col<DT, 16>(lane, r)] = acc[b][(int)r];
+    });
   });
   __syncthreads();
   constexpr int ODT = out_dtype(DT);
@@ -1830,25 +1899,26 @@ static hipError_t launch_tiled(const KParams& p, hipStream_t s, dim3 grid) {
 #define HT_TILED(NAME, DT, AK, BKM, VEC, BM, BN, BKE, WM, WN, MI)                                 \
   {NAME, DT, AK, BKM, (VEC) == 1, 0, BM, BN, BKE, WM * WN, 2, 2 * (BM + BN) * BKE * Ty<DT>::SZ, 64, \
    (VEC) == 2 ? 1 : 0, &launch_tiled<DT, AK, BKM, VEC, BM, BN, BKE, WM, WN, MI>, (VEC) == 2, \
-   (VEC) == 2 ? 1 : 0}
+   (VEC) == 2 ? 1 : 0, MI, BKE * Ty<DT>::SZ / 16}
 
 #define HT_DMA(NAME, DT, BM, BN, WM, WN, MI, ST, OCC, CH, RANK)                                \
   {NAME, DT, 1, 1, 1, 0, BM, BN, CH * 16 / Ty<DT>::SZ, WM * WN, ST, ST * (BM + BN) * CH * 16, 1, \
-   RANK, &launch_dma<DT, BM, BN, WM, WN, MI, ST, OCC, CH>, 0, RANK}
+   RANK, &launch_dma<DT, BM, BN, WM, WN, MI, ST, OCC, CH>, 0, RANK, MI, CH}
 
 // Split-ring entries: 256 x 256 tiles, 128-byte rows, 5 units of 32 KiB.
 #define HT_RING(NAME, DT, WM, WN, MI, NB, RANK, RANK1)                                               \
   {NAME, DT, 1, 1, 1, 0, 256, 256, 128 / Ty<DT>::SZ, WM * WN, 5, 5 * 256 * 128, 64, RANK,         \
-   &launch_ring<DT, WM, WN, MI, NB>, 0, RANK1}
+   &launch_ring<DT, WM, WN, MI, NB>, 0, RANK1, MI, 8}
 
 // Streaming skinny entries: bm = 16 rows, bn = 16*NBW columns, bk = one 128-byte block of K.
 #define HT_SKINNY_DMA(NAME, DT, WK, NBW, R, OCC)                                                  \
   {NAME, DT, 1, 1, 1, 1, 16, NBW * 16, 128 / Ty<DT>::SZ, WK, R, WK * R * (NBW + 1) * 16 * 128, 1, 0, \
-   &launch_skinny_dma<DT, WK, NBW, R, OCC>}
+   &launch_skinny_dma<DT, WK, NBW, R, OCC>, 0, 0, 16, 8}
 
-// Skinny entries: bm = 16 rows, bn = WN*NBW*16 columns per workgroup, bk = one MFMA k-step.
+// Skinny entries: bm = 16 rows, bn = WN*NBW*16 columns per workgroup, bk = one MFMA k-step (no
+// LDS operand tiles).
 #define HT_SKINNY(NAME, DT, WK, WN, NBW, U, OCC)                                                 \
   {NAME, DT, 1, 1, 1, 1, 16, WN * NBW * 16, 4 * Atom<DT, 16>::UNITS * 16 / Ty<DT>::SZ, WK * WN, \
-   1, WK * WN * NBW * 16 * 16 * 4, 1, 0, &launch_skinny<DT, WK, WN, NBW, U, OCC>}
+   1, WK * WN * NBW * 16 * 16 * 4, 1, 0, &launch_skinny<DT, WK, WN, NBW, U, OCC>, 0, 0, 16, 0}
 
 }  // namespace htk

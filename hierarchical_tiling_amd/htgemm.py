@@ -16,7 +16,8 @@ GEMM_ERR_INVALID_ARG, GEMM_ERR_LAYOUT, GEMM_ERR_MISALIGNED, GEMM_ERR_NO_CONFIG =
 STATUS_NAMES = {0: "GEMM_OK", 1: "GEMM_ERR_INVALID_ARG", 2: "GEMM_ERR_DTYPE_COMBO",
                 3: "GEMM_ERR_LAYOUT", 4: "GEMM_ERR_MISALIGNED", 5: "GEMM_ERR_ARCH",
                 6: "GEMM_ERR_LAUNCH", 7: "GEMM_ERR_BAD_HANDLE", 8: "GEMM_ERR_NO_CONFIG",
-                9: "GEMM_ERR_HIP"}
+                9: "GEMM_ERR_HIP", 10: "GEMM_ERR_LANE_MAP"}
+GEMM_PROBE_INTS = 8192
 DTYPES = {"f32": 0, "f16": 1, "bf16": 2, "e4m3": 3}
 ACTS = {"none": 0, "relu": 1, "gelu": 2, "gelu_erf": 2, "silu": 3}
 # layout status codes (htlayout.h)
@@ -106,6 +107,8 @@ def lib():
         "gemm_get_info": ([vp, ctypes.POINTER(gemm_info)], i32),
         "gemm_num_configs": ([], i32),
         "gemm_config_name": ([i32, ctypes.c_char_p, sz], i32),
+        "gemm_atom_layouts": ([i32, i32, ctypes.c_char_p, ctypes.c_char_p, sz], i32),
+        "gemm_probe_atom": ([i32, i32, vp, vp], i32),
         "ht_layout_eval": ([cp, ctypes.POINTER(i64), i32, ctypes.POINTER(i64)], i32),
         "ht_layout_eval_str": ([cp, cp, ctypes.POINTER(i64)], i32),
         "ht_layout_size": ([cp, ctypes.POINTER(i64)], i32),
@@ -132,7 +135,8 @@ def lib():
 EXPORTED = ["gemm_create", "gemm_workspace_size", "gemm_run", "gemm_run_ex", "gemm_run_grouped",
             "gemm_destroy",
             "gemm_status_string",
-            "gemm_get_info", "gemm_num_configs", "gemm_config_name", "ht_layout_eval",
+            "gemm_get_info", "gemm_num_configs", "gemm_config_name", "gemm_atom_layouts",
+            "gemm_probe_atom", "ht_layout_eval",
             "ht_layout_eval_str",
             "ht_layout_size", "ht_layout_table", "ht_layout_coalesce", "ht_layout_compose",
             "ht_layout_complement", "ht_layout_logical_divide", "ht_layout_zipped_divide",
@@ -203,6 +207,20 @@ def gemm_config_name(i: int) -> str:
     buf = ctypes.create_string_buffer(128)
     _check(lib().gemm_config_name(i, buf, 128), "gemm_config_name")
     return buf.value.decode()
+
+
+def gemm_atom_layouts(dtype: str, mi: int):
+    """(operand layout, accumulator layout) of the MFMA atom the kernels use, as text."""
+    a = ctypes.create_string_buffer(256)
+    c = ctypes.create_string_buffer(256)
+    _check(lib().gemm_atom_layouts(DTYPES[dtype], mi, a, c, 256), "gemm_atom_layouts")
+    return a.value.decode(), c.value.decode()
+
+
+def gemm_probe_atom(dtype: str, mi: int, out, stream=None):
+    """Enqueue the index probe of atom (dtype, mi); `out` is a device buffer of GEMM_PROBE_INTS
+    int32 values (a device address or a tensor)."""
+    _check(lib().gemm_probe_atom(DTYPES[dtype], mi, _addr(out), _stream(stream)), "gemm_probe_atom")
 
 
 def make_desc(M, N, K, dtype, a_strides, b_strides, d_strides, c_strides=None, has_bias=False,

@@ -87,7 +87,9 @@ enum {
   GEMM_ERR_LAUNCH = 6,       /* the kernel launch failed (hipGetLastError)                       */
   GEMM_ERR_BAD_HANDLE = 7,   /* NULL or destroyed handle                                         */
   GEMM_ERR_NO_CONFIG = 8,    /* the forced tile-table entry cannot run this problem              */
-  GEMM_ERR_HIP = 9           /* another HIP runtime error (device query failed, ...)            */
+  GEMM_ERR_HIP = 9,          /* another HIP runtime error (device query failed, ...)            */
+  GEMM_ERR_LANE_MAP = 10     /* a kernel's lane map disagrees with the layout helper (a defect  */
+                             /* of the build, never of the arguments)                            */
 };
 
 /* ---- element types and activations ----------------------------------------------------- */
@@ -139,8 +141,10 @@ typedef struct gemm_desc {
 typedef struct gemm_handle_s* gemm_t;
 
 /* Validate `desc` and pick a kernel.  On success *out is a new handle.  Host-only: allocates
- * no device memory and launches nothing.  Errors: GEMM_ERR_INVALID_ARG, GEMM_ERR_DTYPE_COMBO,
- * GEMM_ERR_LAYOUT, GEMM_ERR_ARCH, GEMM_ERR_NO_CONFIG, GEMM_ERR_HIP. */
+ * no device memory and launches nothing.  The chosen kernels' MFMA lane maps and LDS swizzle
+ * are checked once per process against the layout helper (htlayout.h).  Errors:
+ * GEMM_ERR_INVALID_ARG, GEMM_ERR_DTYPE_COMBO, GEMM_ERR_LAYOUT, GEMM_ERR_ARCH, GEMM_ERR_NO_CONFIG,
+ * GEMM_ERR_HIP, GEMM_ERR_LANE_MAP. */
 int gemm_create(const gemm_desc* desc, gemm_t* out);
 
 /* Bytes of device workspace gemm_run needs for this handle: 0 unless the problem is split along
@@ -241,6 +245,33 @@ int gemm_get_info(gemm_t h, gemm_info* info);
 /* Number of entries in the compiled tile table, and the name of entry `idx`. */
 int gemm_num_configs(void);
 int gemm_config_name(int idx, char* out, size_t cap);
+
+/* ---- MFMA lane maps ("A10 - CuTe, CUTLASS & CuTile", section 3.3: an MMA atom's fragments are
+ * layouts from (thread, value) to the instruction's tile; section 6 Pitfall 2) ------------------ */
+/* The layouts the kernels use for the atom of operand type `dtype` (gemm_dtype) with an MI x MI
+ * output block (MI = 16 or 32), in the pages' shape:stride notation, written to `op` and `acc`
+ * (caller buffers of `cap` bytes).  Index i = lane + 64 * v (lane fastest).  op maps to
+ * m + MI * k of A (and n + MI * k of B, which uses the same map); acc maps to m + MI * n.
+ * Returns GEMM_OK, GEMM_ERR_INVALID_ARG (no such atom, NULL, or cap too small) or
+ * GEMM_ERR_LANE_MAP (the layouts disagree with the layout helper). */
+int gemm_atom_layouts(int dtype, int mi, char* op, char* acc, size_t cap);
+
+/* Index probe: runs the atom (dtype, mi) on the current device, on `stream`, and writes into
+ * the caller's device buffer `out` (GEMM_PROBE_INTS int32 values, four sections of 2048):
+ *   [0, 2048)     for each accumulator slot i = lane + 64 r: m + MI * n of the output element the
+ *                 hardware placed there, with the operands fed through the kernels' LDS tiles,
+ *                 swizzle and fragment addressing from inputs that encode m and n in D;
+ *   [2048, 4096)  the kernels' belief for the same slot: acc_row + MI * acc_col;
+ *   [4096, 6144)  for each operand slot i = lane + 64 v: the row of D that a one-hot A in that
+ *                 slot (B all ones) makes non-zero, the hardware's m of the slot;
+ *   [6144, 8192)  for the same slot: the number of columns n for which D(m, n) is 1 when B holds
+ *                 ones exactly in the slots the op layout gives the same k (MI if those slots
+ *                 meet A's slot in the hardware's k, fewer otherwise), or -1 if D is non-zero off
+ *                 row m.
+ * Unused entries are -2.  Asynchronous; GEMM_ERR_INVALID_ARG for an unknown atom or NULL out,
+ * GEMM_ERR_LAUNCH if the launch fails. */
+#define GEMM_PROBE_INTS 8192
+int gemm_probe_atom(int dtype, int mi, int32_t* out, void* stream);
 
 #ifdef __cplusplus
 }
