@@ -13,6 +13,7 @@
 #include <atomic>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <utility>
 #include <vector>
@@ -636,6 +637,58 @@ int gemm_run_grouped(gemm_t h, const gemm_args* a, const int32_t* offsets, void*
                   stream);
 }
 
+}  // extern "C"
+
+// ---- the entry point that allocates nothing ----------------------------------------------
+// Scratch for gemm_run_noalloc: one static device array per GPU, held until the process ends.
+// Host code never uses the array's name as an address (it is a host-side stand-in); the device
+// address comes from hipGetSymbolAddress, once per device, with that device current.
+static __device__ __align__(256) char scratch[GEMM_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+
+// Device address of `scratch` on the current device.
+int scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return GEMM_ERR_HIP;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return GEMM_ERR_HIP;
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return GEMM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gemm_run_noalloc(gemm_t h, const gemm_args* a, void* stream) {
+  if (!h || h->magic != kMagic) return GEMM_ERR_BAD_HANDLE;
+  if (!a || a->workspace) return GEMM_ERR_INVALID_ARG;  // the library supplies the scratch
+  size_t need = 0;
+  int rc = gemm_workspace_size(h, &need);
+  if (rc) return rc;
+  if (need > (size_t)GEMM_NOALLOC_SCRATCH_BYTES) return GEMM_ERR_SCRATCH_LIMIT;
+  void* ws = nullptr;
+  if (need > 0) {
+    rc = scratch_address(&ws);
+    if (rc) return rc;
+  }
+  if (h->d.ragged_m) return GEMM_ERR_INVALID_ARG;  // grouped handles run through gemm_run_grouped
+  return run_impl(h, a->A, a->B, a->C, a->D, a->bias, a->row_scale, a->col_scale, a->alpha,
+                  a->beta, a->scale_a, a->scale_b, ws, nullptr, a->row_sumsq, a->col_sum, stream);
+}
+
 int gemm_destroy(gemm_t h) {
   if (!h) return GEMM_OK;
   if (h->magic != kMagic) return GEMM_ERR_BAD_HANDLE;
@@ -657,6 +710,7 @@ const char* gemm_status_string(int status) {
     case GEMM_ERR_NO_CONFIG: return "no tile-table entry can run this problem";
     case GEMM_ERR_HIP: return "HIP runtime error";
     case GEMM_ERR_LANE_MAP: return "a kernel lane map disagrees with the layout helper";
+    case GEMM_ERR_SCRATCH_LIMIT: return "the problem needs more scratch than gemm_run_noalloc holds";
     default: return "unknown status";
   }
 }

@@ -16,7 +16,9 @@ GEMM_ERR_INVALID_ARG, GEMM_ERR_LAYOUT, GEMM_ERR_MISALIGNED, GEMM_ERR_NO_CONFIG =
 STATUS_NAMES = {0: "GEMM_OK", 1: "GEMM_ERR_INVALID_ARG", 2: "GEMM_ERR_DTYPE_COMBO",
                 3: "GEMM_ERR_LAYOUT", 4: "GEMM_ERR_MISALIGNED", 5: "GEMM_ERR_ARCH",
                 6: "GEMM_ERR_LAUNCH", 7: "GEMM_ERR_BAD_HANDLE", 8: "GEMM_ERR_NO_CONFIG",
-                9: "GEMM_ERR_HIP", 10: "GEMM_ERR_LANE_MAP"}
+                9: "GEMM_ERR_HIP", 10: "GEMM_ERR_LANE_MAP", 11: "GEMM_ERR_SCRATCH_LIMIT"}
+GEMM_ERR_SCRATCH_LIMIT = 11
+GEMM_NOALLOC_SCRATCH_BYTES = 32 << 20
 GEMM_PROBE_INTS = 8192
 DTYPES = {"f32": 0, "f16": 1, "bf16": 2, "e4m3": 3}
 ACTS = {"none": 0, "relu": 1, "gelu": 2, "gelu_erf": 2, "silu": 3}
@@ -102,6 +104,7 @@ def lib():
                       ctypes.c_float, vp, vp], i32),
         "gemm_run_ex": ([vp, ctypes.POINTER(gemm_args), vp], i32),
         "gemm_run_grouped": ([vp, ctypes.POINTER(gemm_args), vp, vp], i32),
+        "gemm_run_noalloc": ([vp, ctypes.POINTER(gemm_args), vp], i32),
         "gemm_destroy": ([vp], i32),
         "gemm_status_string": ([i32], cp),
         "gemm_get_info": ([vp, ctypes.POINTER(gemm_info)], i32),
@@ -133,6 +136,7 @@ def lib():
 
 
 EXPORTED = ["gemm_create", "gemm_workspace_size", "gemm_run", "gemm_run_ex", "gemm_run_grouped",
+            "gemm_run_noalloc",
             "gemm_destroy",
             "gemm_status_string",
             "gemm_get_info", "gemm_num_configs", "gemm_config_name", "gemm_atom_layouts",
@@ -183,6 +187,14 @@ def gemm_run_grouped(h, A, B, C, D, bias, row_scale, col_scale, offsets, alpha, 
     """Grouped ragged-M run: `offsets` is the device address of batch + 1 int32 row offsets."""
     a = gemm_args(A, B, C, D, bias, row_scale, col_scale, alpha, beta, scale_a, scale_b, None)
     _check(lib().gemm_run_grouped(h, ctypes.byref(a), offsets, stream), "gemm_run_grouped")
+
+
+def gemm_run_noalloc(h, A, B, C, D, bias, row_scale, col_scale, alpha, beta, scale_a=1.0,
+                     scale_b=1.0, stream=None, row_sumsq=None, col_sum=None):
+    """gemm_run_ex with the library's static scratch as the workspace (no allocation)."""
+    a = gemm_args(A, B, C, D, bias, row_scale, col_scale, alpha, beta, scale_a, scale_b, None,
+                  row_sumsq, col_sum)
+    _check(lib().gemm_run_noalloc(h, ctypes.byref(a), stream), "gemm_run_noalloc")
 
 
 def gemm_destroy(h):

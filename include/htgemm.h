@@ -88,8 +88,10 @@ enum {
   GEMM_ERR_BAD_HANDLE = 7,   /* NULL or destroyed handle                                         */
   GEMM_ERR_NO_CONFIG = 8,    /* the forced tile-table entry cannot run this problem              */
   GEMM_ERR_HIP = 9,          /* another HIP runtime error (device query failed, ...)            */
-  GEMM_ERR_LANE_MAP = 10     /* a kernel's lane map disagrees with the layout helper (a defect  */
+  GEMM_ERR_LANE_MAP = 10,    /* a kernel's lane map disagrees with the layout helper (a defect  */
                              /* of the build, never of the arguments)                            */
+  GEMM_ERR_SCRATCH_LIMIT = 11 /* gemm_run_noalloc: the handle needs more than                    */
+                             /* GEMM_NOALLOC_SCRATCH_BYTES of workspace                          */
 };
 
 /* ---- element types and activations ----------------------------------------------------- */
@@ -218,6 +220,20 @@ int gemm_run_ex(gemm_t h, const gemm_args* args, void* stream);
  * scalars are those of gemm_run_ex.  gemm_run and gemm_run_ex refuse a ragged handle, and this
  * entry point refuses any other (GEMM_ERR_INVALID_ARG). */
 int gemm_run_grouped(gemm_t h, const gemm_args* args, const int32_t* offsets, void* stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation): gemm_run_ex with the workspace taken from a static
+ * device array of GEMM_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it runs on until
+ * the process ends.  args->workspace must be NULL.  It allocates nothing and calls no allocating
+ * routine; the first call on a device looks up that device's copy of the array.  Returns
+ * GEMM_ERR_SCRATCH_LIMIT when gemm_workspace_size(h) exceeds GEMM_NOALLOC_SCRATCH_BYTES (create
+ * the handle with split_k = 1 to need none), GEMM_ERR_INVALID_ARG for a grouped handle or a
+ * non-NULL workspace, otherwise the results and errors of gemm_run_ex.  All calls on one GPU share
+ * its array, which keeps the last call's contents (every byte a run reads there it has written
+ * first), so calls that overlap in time on one GPU -- on different streams or threads -- race
+ * and give undefined results; calls ordered on one stream do not. */
+#define GEMM_NOALLOC_SCRATCH_BYTES (32u << 20)
+int gemm_run_noalloc(gemm_t h, const gemm_args* args, void* stream);
 
 /* Free a handle.  NULL is accepted. */
 int gemm_destroy(gemm_t h);

@@ -388,3 +388,20 @@ def test_kernel_choice_counts_batch_problems(fake_gfx950, L, shape, kernel):
     d = desc(M=M, N=N, K=K, a_strides=(K, 1), b_strides=(1, K), d_strides=(N, 1), batch=L,
              batch_strides=(M * K, N * K, 0, M * N))
     assert _info(d).name.decode().endswith(kernel)
+
+
+def test_noalloc_scratch_limit_and_arguments(fake_gfx950):
+    """gemm_run_noalloc refuses, before touching the device, a handle whose workspace exceeds the
+    static scratch, a caller workspace, and a grouped handle."""
+    big = H.gemm_create(H.make_desc(2048, 2048, 65536, "bf16", (65536, 1), (1, 65536), (2048, 1),
+                                    split_k=8))
+    try:
+        assert H.gemm_workspace_size(big) > H.GEMM_NOALLOC_SCRATCH_BYTES
+        args = H.gemm_args(256, 256, None, 256, None, None, None, 1.0, 0.0, 1.0, 1.0, None)
+        assert H.lib().gemm_run_noalloc(big, ctypes.byref(args), None) == H.GEMM_ERR_SCRATCH_LIMIT
+        args.workspace = 256
+        assert H.lib().gemm_run_noalloc(big, ctypes.byref(args), None) == H.GEMM_ERR_INVALID_ARG
+    finally:
+        H.gemm_destroy(big)
+    assert H.lib().gemm_run_noalloc(None, None, None) == 7   # GEMM_ERR_BAD_HANDLE
+    assert H.gemm_status_string(H.GEMM_ERR_SCRATCH_LIMIT).startswith("the problem needs more")
