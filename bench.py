@@ -1,19 +1,24 @@
 """Benchmark of the hierarchically tiled GEMM on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-sub]
+                    [--no-cpu-baseline]
 
 A step is one launch of the whole hot path -- D = act(alpha*(A@B) + beta*C + bias) -- over one
 set of synthetic inputs already resident in HBM.  The default workload is the headline one:
 bf16 8192 x 8192 x 8192, A row-major, B column-major, D = GELU(A@B + bias[n]), fp32 accumulate,
-bf16 output.  Three input sets are rotated so consecutive steps do not reuse the 256 MiB
-last-level cache.  Prints one JSON line.
+bf16 output; `value` is its throughput.  The other benchmark workloads are timed after it the same
+way and reported as `sub_results`, each with its own roofline fraction.  Input sets are rotated
+so that consecutive steps do not find their operands in the 256 MiB last-level cache.  Prints one
+JSON line.
 """
 from __future__ import annotations
 
 import argparse
 import json
 import os
+import subprocess
 import sys
+import threading
 import time
 
 import numpy as np
@@ -31,6 +36,8 @@ WORKLOADS = {
     # name: (M, N, K, dtype, a_order, b_order, dist, std, alpha, beta, has_c, bias, act, sA, sB)
     "bf16_8192_gelu": (8192, 8192, 8192, "bf16", "row", "col", "normal", 8192 ** -0.5, 1.0, 0.0,
                        False, True, "gelu", 1.0, 1.0),
+    "bf16_8192_gelu_bn": (8192, 8192, 8192, "bf16", "row", "row", "normal", 8192 ** -0.5, 1.0,
+                          0.0, False, True, "gelu", 1.0, 1.0),
     "bf16_4096": (4096, 4096, 4096, "bf16", "row", "col", "normal", 4096 ** -0.5, 1.0, 0.0,
                   False, False, "none", 1.0, 1.0),
     "fp16_ragged": (4099, 3071, 2053, "f16", "row", "row", "uniform", None, 0.75, -1.25, True,
@@ -44,14 +51,23 @@ WORKLOADS = {
 }
 DESCRIBE = {
     "bf16_8192_gelu": "bf16 GEMM 8192x8192x8192, D=GELU(A@B+bias[n]), A row-major, B column-major, fp32 accumulate, bf16 out",
+    "bf16_8192_gelu_bn": "bf16 GEMM 8192x8192x8192, D=GELU(A@B+bias[n]), A row-major, B row-major, fp32 accumulate, bf16 out",
     "bf16_4096": "bf16 GEMM 4096x4096x4096, D=A@B, A row-major, B column-major, bf16 out",
     "fp16_ragged": "fp16 GEMM 4099x3071x2053, D=0.75*A@B-1.25*C, A/B/C row-major (odd leading dims)",
     "e4m3_skinny": "e4m3 GEMM 16x16384x8192, D=sA*sB*A@B, A row-major, B column-major, bf16 out",
     "e4m3_8192": "e4m3 GEMM 8192x8192x8192, D=sA*sB*A@B, A row-major, B column-major, bf16 out",
     "fp32_256": "fp32 GEMM 256x256x256, D=1.5*A@B+0.5*C, all row-major",
 }
-SEEDS = {"bf16_8192_gelu": 4000, "bf16_4096": 2000, "fp16_ragged": 3000, "e4m3_skinny": 5000,
-         "e4m3_8192": 5100, "fp32_256": 1000}
+SEEDS = {"bf16_8192_gelu": 4000, "bf16_8192_gelu_bn": 4200, "bf16_4096": 2000,
+         "fp16_ragged": 3000, "e4m3_skinny": 5000, "e4m3_8192": 5100, "fp32_256": 1000}
+# input sets rotated per workload: at least 512 MiB of operands (twice the last-level cache)
+# wherever the operands are that large
+SETS = {"bf16_8192_gelu": 3, "bf16_8192_gelu_bn": 3, "bf16_4096": 6, "fp16_ragged": 6,
+        "e4m3_skinny": 4, "e4m3_8192": 4, "fp32_256": 1}
+# the HBM-bound workload (its roofline is bytes, not FLOPs)
+MEMORY_BOUND = {"e4m3_skinny"}
+SUB_WORKLOADS = ["e4m3_skinny", "e4m3_8192", "bf16_4096", "fp16_ragged", "bf16_8192_gelu_bn",
+                 "fp32_256"]
 
 
 def algorithmic_bytes(M, N, K, dtype, has_c, bias):
@@ -76,10 +92,178 @@ def build_inputs(name, n_sets, device):
         B = inputs.matrix(seed + 2 + 10 * s, K, N, dt, dist, order=bo, **kw)
         C = inputs.matrix(seed + 3 + 10 * s, M, N, out_t, "uniform", order="row") if has_c else None
         bv = inputs.vector(seed + 4 + 10 * s, N, out_t, "normal", std=0.1) if bias else None
-        host.append((A, B, C, bv))
+        host.append((A, B, C, bv) if s == 0 else None)   # the host copy of set 0 feeds the oracle
         sets.append(tuple(inputs.to_device(x, device) if x is not None else None for x in (A, B, C, bv)))
     D = torch.empty(M * N * inputs.ESIZE[out_t], dtype=torch.uint8, device=device)
     return host, sets, D
+
+
+def measure(name, steps, warmup, device, clock_sampler=None):
+    """Time `steps` back-to-back launches of workload `name` after `warmup` untimed ones."""
+    import torch
+
+    from hierarchical_tiling_amd import counters
+    from hierarchical_tiling_amd import htgemm as H
+    M, N, K, dt, ao, bo, dist, std, alpha, beta, has_c, bias, act, sa, sb = WORKLOADS[name]
+    host, sets, D = build_inputs(name, SETS[name], device)
+    A0, B0, C0, _ = host[0]
+    desc = H.make_desc(M, N, K, dt, A0.strides, B0.strides, (N, 1),
+                       c_strides=C0.strides if C0 is not None else None, has_bias=bias, act=act)
+    g = H.Gemm(desc)
+    info = g.info
+    ws = None
+    if g.workspace_bytes:
+        ws = torch.empty(g.workspace_bytes, dtype=torch.uint8, device=device)
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        a, b, c, bv = sets[i % len(sets)]
+        g.run(a, b, c, D, bv, alpha=alpha, beta=beta, scale_a=sa, scale_b=sb, stream=stream,
+              workspace=ws)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    # timed region: the launches back to back on the launch stream, one pair of HIP events
+    # around them (events between launches would add their own gaps to short kernels)
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    t_start.record(stream)
+    for i in range(steps):
+        step(i)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+    launch_ms = float(t_start.elapsed_time(t_end)) / steps
+    # spread of single launches, in a separate pass (not part of the value)
+    n_pct = min(steps, 20)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(n_pct)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(n_pct)]
+    for i in range(n_pct):
+        starts[i].record(stream)
+        step(i)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    per = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
+    clock = None
+    if clock_sampler is not None:
+        # shader clock while the kernel runs back to back for about a second (its own pass)
+        n_sus = max(1, int(1000.0 / max(launch_ms, 1e-3)))
+        with clock_sampler:
+            for i in range(n_sus):
+                step(i)
+            torch.cuda.synchronize()
+        clock = clock_sampler.summary()
+    flops = 2.0 * M * N * K
+    nbytes = algorithmic_bytes(M, N, K, dt, has_c, bias)
+    if name in MEMORY_BOUND:
+        ach = nbytes / (launch_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(ach / PEAK_HBM_GBS, 4)}
+    else:
+        ach = flops / (launch_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_TFLOPS[dt],
+                "unit": "TFLOP/s", "frac": round(ach / PEAK_TFLOPS[dt], 4)}
+    kname = info.name.decode()
+    traffic, source = counters.traffic_for(kname, name, os.path.join(ROOT, "profiles"))
+    roof["traffic"] = traffic
+    roof.update({"traffic_source": source, "kernel": kname, "launch_ms_mean": round(launch_ms, 4),
+                 "single_launch_ms_p10": round(float(np.percentile(per, 10)), 4),
+                 "single_launch_ms_p50": round(float(np.percentile(per, 50)), 4),
+                 "single_launch_ms_p90": round(float(np.percentile(per, 90)), 4),
+                 "algorithmic_bytes": nbytes, "algorithmic_flops": flops})
+    res = {"workload": DESCRIBE[name], "name": name, "M": M, "N": N, "K": K, "dtype": dt,
+           "tile": [info.bm, info.bn, info.bk], "grid": int(info.grid), "split_k": int(info.split_k),
+           "steps": steps, "warmup": warmup, "input_sets": SETS[name], "ms_per_step": round(wall_ms, 4),
+           "tflops": round(flops / (wall_ms * 1e-3) / 1e12, 1), "roofline": roof}
+    if clock is not None:
+        res["sclk_mhz_during_sustained_run"] = clock
+    return res, host[0]
+
+
+class ClockSampler:
+    """Samples the GPU's current graphics clock (amdsmi, in-process) every few milliseconds while
+    it is entered; summary() gives the median and range in MHz, or None if unavailable."""
+
+    def __init__(self):
+        self.samples = []
+        self._stop = threading.Event()
+        self._handle = None
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            handles = amdsmi.amdsmi_get_processor_handles()
+            self._amdsmi = amdsmi
+            self._handle = handles[0] if handles else None
+        except Exception:
+            self._handle = None
+
+    def _read(self):
+        info = self._amdsmi.amdsmi_get_clock_info(self._handle, self._amdsmi.AmdSmiClkType.GFX)
+        return float(info.get("clk", info.get("cur_clk")))
+
+    def __enter__(self):
+        self.samples = []
+        self._stop.clear()
+        if self._handle is not None:
+            def run():
+                while not self._stop.is_set():
+                    try:
+                        self.samples.append(self._read())
+                    except Exception:
+                        return
+                    time.sleep(0.005)
+            self._t = threading.Thread(target=run, daemon=True)
+            self._t.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        if self._handle is not None:
+            self._t.join(timeout=2)
+        return False
+
+    def max_mhz(self):
+        try:
+            info = self._amdsmi.amdsmi_get_clock_info(self._handle, self._amdsmi.AmdSmiClkType.GFX)
+            return float(info.get("max_clk"))
+        except Exception:
+            return None
+
+    def summary(self):
+        if not self.samples:
+            return None
+        s = np.array(self.samples)
+        return {"median": float(np.median(s)), "min": float(s.min()), "max": float(s.max()),
+                "samples": int(s.size), "max_sclk": self.max_mhz()}
+
+
+def run_metadata(threads):
+    import torch
+    props = torch.cuda.get_device_properties(0)
+    meta = {"device": props.name, "arch": getattr(props, "gcnArchName", None),
+            "compute_units": props.multi_processor_count,
+            "hbm_gib": round(props.total_memory / 2 ** 30, 1),
+            "torch": torch.__version__, "torch_hip": torch.version.hip}
+    try:
+        meta["rocm"] = open("/opt/rocm/.info/version").read().strip()
+    except OSError:
+        meta["rocm"] = None
+    try:
+        out = subprocess.run(["/opt/rocm/bin/hipcc", "--version"], capture_output=True, text=True,
+                             timeout=30).stdout.splitlines()
+        meta["hipcc"] = next((line for line in out if line.startswith("HIP version")), None)
+    except Exception:
+        meta["hipcc"] = None
+    try:
+        meta["cpu_model"] = next(line.split(":", 1)[1].strip() for line in open("/proc/cpuinfo")
+                                 if line.startswith("model name"))
+    except Exception:
+        meta["cpu_model"] = None
+    meta["host_cpus_available"] = len(os.sched_getaffinity(0))
+    meta["host_threads_used"] = threads
+    return meta
 
 
 def cpu_baseline(name, host_set, threads, budget_s=12.0):
@@ -89,6 +273,7 @@ def cpu_baseline(name, host_set, threads, budget_s=12.0):
     M, N, K, dt, ao, bo, dist, std, alpha, beta, has_c, bias, act, sa, sb = WORKLOADS[name]
     A, B, C, bv = host_set
     op = lambda m: oracle.Operand(m.storage, m.dtype, m.shape, m.strides) if m is not None else None  # noqa
+
     def rows_of(m):
         return np.repeat(np.arange(m), N), np.tile(np.arange(N), m)
 
@@ -135,9 +320,10 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=30)  # untimed; lets the clock settle
     ap.add_argument("--workload", default="bf16_8192_gelu", choices=sorted(WORKLOADS))
-    ap.add_argument("--force-config", type=int, default=-1)
+    ap.add_argument("--no-sub", action="store_true", help="time only --workload")
+    ap.add_argument("--sub-steps", type=int, default=30)
+    ap.add_argument("--sub-warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--sets", type=int, default=3)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run 5 plain device copies of 1 GiB (counter calibration) and exit")
     args = ap.parse_args()
@@ -149,84 +335,35 @@ def main():
         return
 
     import torch
-
-    from hierarchical_tiling_amd import htgemm as H
     dev = torch.device("cuda:0")
+    threads = max(1, min(16, len(os.sched_getaffinity(0))))
+    sampler = ClockSampler()
+    main_res, host0 = measure(args.workload, args.steps, args.warmup, dev, clock_sampler=sampler)
+    torch.cuda.empty_cache()
+    subs = []
+    if not args.no_sub:
+        for name in SUB_WORKLOADS:
+            if name == args.workload:
+                continue
+            r, _ = measure(name, args.sub_steps, args.sub_warmup, dev)
+            subs.append(r)
+            torch.cuda.empty_cache()
     name = args.workload
-    M, N, K, dt, ao, bo, dist, std, alpha, beta, has_c, bias, act, sa, sb = WORKLOADS[name]
-    host, sets, D = build_inputs(name, args.sets, dev)
-    A0, B0, C0, _ = host[0]
-    desc = H.make_desc(M, N, K, dt, A0.strides, B0.strides, (N, 1),
-                       c_strides=C0.strides if C0 is not None else None, has_bias=bias, act=act,
-                       force_config=args.force_config)
-    g = H.Gemm(desc)
-    info = g.info
-    stream = torch.cuda.current_stream()
-
-    def step(i):
-        a, b, c, bv = sets[i % len(sets)]
-        g.run(a, b, c, D, bv, alpha=alpha, beta=beta, scale_a=sa, scale_b=sb, stream=stream)
-
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    # timed region: K launches back to back on the launch stream, one pair of HIP events around
-    # them (per-launch events would add their own gaps to short kernels)
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    t_start.record(stream)
-    for i in range(args.steps):
-        step(i)
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms = float(wall * 1e3 / args.steps)
-    avg_launch_ms = float(t_start.elapsed_time(t_end)) / args.steps
-    # spread of single launches, in a separate pass (not part of the value)
-    n_pct = min(args.steps, 20)
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(n_pct)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(n_pct)]
-    for i in range(n_pct):
-        starts[i].record(stream)
-        step(i)
-        ends[i].record(stream)
-    torch.cuda.synchronize()
-    per = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])  # ms per launch
-    flops = 2.0 * M * N * K
-    tflops = flops / (ms * 1e-3) / 1e12
-    achieved = flops / (avg_launch_ms * 1e-3) / 1e12
-    nbytes = algorithmic_bytes(M, N, K, dt, has_c, bias)
-    memory_bound = name == "e4m3_skinny"
-    if memory_bound:
-        ach = nbytes / (avg_launch_ms * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None}
-    else:
-        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_TFLOPS[dt],
-                "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS[dt], 4), "traffic": None}
-    from hierarchical_tiling_amd import counters
-    traffic, source = counters.traffic_for(info.name.decode(), name, os.path.join(ROOT, "profiles"))
-    roof["traffic"] = traffic
-    roof.update({"traffic_source": source, "kernel": info.name.decode(),
-                 "launch_ms_mean": round(avg_launch_ms, 4),
-                 "single_launch_ms_p10": round(float(np.percentile(per, 10)), 4),
-                 "single_launch_ms_p50": round(float(np.percentile(per, 50)), 4),
-                 "single_launch_ms_p90": round(float(np.percentile(per, 90)), 4),
-                 "algorithmic_bytes": nbytes, "algorithmic_flops": flops})
+    M, N, K, dt = WORKLOADS[name][:4]
     out = {
-        "metric": METRIC, "value": round(tflops, 1), "unit": "TFLOP/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "metric": METRIC, "value": main_res["tflops"], "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": main_res["ms_per_step"],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dt,
         "data": "synthetic (seeded numpy PCG64 draws rounded to the operand type)",
-        "config": {"workload": DESCRIBE[name], "M": M, "N": N, "K": K, "tile": [info.bm, info.bn, info.bk],
-                   "grid": int(info.grid)},
-        "roofline": roof,
+        "config": {"workload": DESCRIBE[name], "M": M, "N": N, "K": K, "tile": main_res["tile"],
+                   "grid": main_res["grid"], "input_sets": SETS[name]},
+        "roofline": main_res["roofline"],
+        "sclk_mhz_during_sustained_run": main_res.get("sclk_mhz_during_sustained_run"),
+        "sub_results": subs,
+        "run": run_metadata(threads),
     }
     if not args.no_cpu_baseline:
-        threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or min(16, len(os.sched_getaffinity(0)))
-        out["cpu_baseline"] = cpu_baseline(name, host[0], threads)
+        out["cpu_baseline"] = cpu_baseline(name, host0, threads)
     print(json.dumps(out), flush=True)
 
 

@@ -87,10 +87,13 @@ bool entry_fits(const KernelEntry& e, const gemm_handle_s& h, bool vec_a, bool v
       (e.skinny || int64_t(e.bm) * e.bn * dtype_size(d.d_type) > e.lds_bytes))
     return false;
   if (e.vec) {
-    // the 16-byte K-major loaders address one tile with 31-bit buffer offsets
+    // the 16-byte K-major loaders address one tile with 31-bit buffer offsets, and so do the
+    // MN-major loaders that keep 2-byte tiles as rows of k, over all of K
     const int64_t sz = dtype_size(e.dtype), lim = int64_t(1) << 31;
     if (h.a.kmajor && (int64_t(e.bm) * h.a.ld + d.K) * sz >= lim) return false;
     if (h.b.kmajor && (int64_t(e.bn) * h.b.ld + d.K) * sz >= lim) return false;
+    if (e.mn_rows && !h.a.kmajor && (d.K * h.a.ld + e.bm) * sz >= lim - 64) return false;
+    if (e.mn_rows && !h.b.kmajor && (d.K * h.b.ld + e.bn) * sz >= lim - 64) return false;
   }
   if (e.realign) {
     // realigned loaders: 31-bit offsets over a tile's rows (K-major) or over all of K (M/N-major)
@@ -288,9 +291,23 @@ template <int CH> bool check_swizzle_now() {
   return true;
 }
 
+// The MN-major tiles' slots against two Swizzle functors of the helper.
+template <int CHR> bool check_mn_swizzle_now() {
+  for (int k = 0; k < 256; ++k)
+    for (int c = 0; c < CHR; ++c) {
+      const int o = 16 * (k % 16) + (c % 16);
+      const int64_t sw = ht_swizzle(ht_swizzle(o, 2, 2, 2), 1, 1, 6);
+      const int slot = mn_slot<CHR>(k, c);
+      if (slot != k * CHR + (c & ~15) + (int)(sw % 16)) return false;
+      if (slot / CHR != k) return false;
+    }
+  return true;
+}
+
 // 0: not checked yet, 1: agrees, 2: disagrees (the result is the same every time)
 std::atomic<int> g_atom_state[kNumAtomMaps];
 std::atomic<int> g_swizzle_state[2];
+std::atomic<int> g_mn_swizzle_state[2];
 
 bool cached(std::atomic<int>& st, bool (*fn)()) {
   int v = st.load(std::memory_order_acquire);
@@ -317,6 +334,11 @@ bool atom_ok(int dtype, int mi) {
 // The lane maps and LDS swizzle of table entry e agree with the layout helper.
 bool entry_maps_ok(const KernelEntry& e) {
   if (!atom_ok(e.dtype, e.mi)) return false;
+  if (e.mn_rows) {  // an MN-major operand tile with rows of k (16 or 32 chunks)
+    if (!cached(g_mn_swizzle_state[0], &check_mn_swizzle_now<16>) ||
+        !cached(g_mn_swizzle_state[1], &check_mn_swizzle_now<32>))
+      return false;
+  }
   if (e.lds_row_chunks == 8) return cached(g_swizzle_state[1], &check_swizzle_now<8>);
   if (e.lds_row_chunks == 4) return cached(g_swizzle_state[0], &check_swizzle_now<4>);
   return e.lds_row_chunks == 0;

@@ -99,4 +99,19 @@ template <int CH> __host__ __device__ constexpr int swizzled_slot(int row, int c
   return swizzle(row * CH + chunk, RowSwizzle<CH>::B, RowSwizzle<CH>::M, RowSwizzle<CH>::S);
 }
 
+// MN-major operand tiles (A stored M-contiguous, B N-contiguous): one LDS row per k holding the
+// tile's R elements as CHR = R * esize / 16 >= 16 chunks, so that rows are copied untransposed
+// and the MFMA fragments are assembled by transposing LDS reads (ds_read_b64_tr_b16: within
+// each 16-lane group, lane i receives element i % 4 of the 8 bytes read by lanes 4j + i / 4,
+// j = 0..3, so 16 lanes that address a 4 (k) x 16 (m or n) block receive 4 consecutive k of one
+// column each).  Chunk c of row k sits at slot c ^ mn_key(k).  On the 16-chunk view
+// o = 16 (k mod 16) + (c mod 16) this is Swizzle<2,2,2> followed by Swizzle<1,1,6>.  The 32
+// lanes that one 8-byte read phase serves then touch 16 different 16-byte bank slots: rows
+// k..k+3 (and k+8..k+11 for the 16 x 16 atom) over 2 or 4 neighbouring chunks.
+__host__ __device__ constexpr int mn_key(int k) { return 4 * (k & 3) + 2 * ((k >> 3) & 1); }
+template <int CHR> __host__ __device__ constexpr int mn_slot(int k, int c) {
+  static_assert(CHR >= 16 && CHR % 16 == 0, "rows of at least 256 bytes");
+  return k * CHR + (c ^ mn_key(k));
+}
+
 }  // namespace htk

@@ -65,6 +65,7 @@ struct KernelEntry {
   int rank_one_round; // rank when all workgroups fit on the CUs at once (one tile per CU)
   int mi;             // MFMA atom: MI x MI output block (its layouts are in atom_maps.h)
   int lds_row_chunks; // 16-byte chunks per swizzled LDS row of the operand tiles (4 or 8)
+  int mn_rows;        // 1: an MN-major operand is kept as rows of k and read by transposing reads
 };
 
 const KernelEntry* table();

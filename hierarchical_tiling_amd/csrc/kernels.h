@@ -41,6 +41,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
 #include <utility>
 
 #include "atom_maps.h"
@@ -836,6 +837,123 @@ struct LoadMNMajorMis {
   }
 };
 
+// ------------------------------------------------------------------------------------------
+// MN-major 2-byte operands kept as rows of k.  The tile's BKE rows (one per k) of R >= 128
+// elements are copied untransposed into LDS (slot mn_slot, atom_maps.h) and the MFMA fragments
+// are assembled by transposing LDS reads (read_rows_frag), so no VALU transpose is needed.
+// Thread q of a copy owns chunks (k, c) = (q / CHR, q % CHR) + (NT / CHR) rows per step: 16
+// consecutive lanes read 256 contiguous bytes of one row and write 16 distinct bank slots.
+// Columns past the operand's last one are not cleared: they only reach outputs past N (or M),
+// which are never stored; reads past the operand's end return zero (buffer range check).
+// ------------------------------------------------------------------------------------------
+template <int DT, int R, int BKE, int NT>
+struct LoadMNRowsVec {
+  static_assert(Ty<DT>::SZ == 2, "2-byte elements");
+  static constexpr int SZ = 2, VE = 8, CHR = R * SZ / 16, STEP = NT / CHR;
+  static constexpr int N = BKE * CHR / NT;
+  static_assert(BKE * CHR % NT == 0 && NT % CHR == 0, "tile chunks must divide over the threads");
+  u32x4 r[N];
+  const char* tile;
+  int64_t ld, span, K;
+  uint32_t voff;  // this thread's first chunk: row tid / CHR, chunk tid % CHR
+  int k1;         // its first row
+  __device__ __forceinline__ void init(const void* base, int64_t ld_, int64_t row0, int64_t rows,
+                                       int64_t K_, int tid) {
+    tile = (const char*)base + row0 * SZ;
+    ld = ld_;
+    K = K_;
+    span = ((K_ - 1) * ld_ + (rows - row0)) * SZ;  // bytes from the tile start to the last element
+    k1 = tid / CHR;
+    voff = (uint32_t)((k1 * ld_ + (tid % CHR) * VE) * SZ);
+  }
+  template <bool PRED>
+  __device__ __forceinline__ void load(int64_t k0) {
+    const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(tile, span);
+    const uint32_t row_step = (uint32_t)(STEP * ld * SZ);
+    const uint32_t kb = (uint32_t)(k0 * ld * SZ);
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const bool ok = !PRED || k0 + k1 + i * STEP < K;
+      r[i] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, ok ? voff + kb + i * row_step : kOobOffset, 0, 0);
+    }
+  }
+  __device__ __forceinline__ void store(u32x4* lds, int tid) const {
+#pragma unroll
+    for (int i = 0; i < N; ++i) lds[mn_slot<CHR>(tid / CHR + i * STEP, tid % CHR)] = r[i];
+  }
+};
+
+template <int DT, int R, int BKE, int NT>
+struct LoadMNRowsMis {
+  static_assert(Ty<DT>::SZ == 2, "2-byte elements");
+  static constexpr int SZ = 2, VE = 8, CHR = R * SZ / 16, STEP = NT / CHR;
+  static constexpr int N = BKE * CHR / NT;
+  static_assert(BKE * CHR % NT == 0 && NT % CHR == 0, "tile chunks must divide over the threads");
+  Raw16 w[N];
+  const char* rb;      // the tile's first byte rounded down to 4 bytes (uniform)
+  int64_t ext, K, ld;
+  uint32_t voff;       // this thread's first chunk, from rb
+  uint32_t shift;      // 2 when its chunks start 2 bytes past a dword (the same for all of them:
+                       // STEP rows apart is a whole number of dwords, STEP being even)
+  int k1;
+  __device__ __forceinline__ void init(const void* base, int64_t ld_, int64_t row0, int64_t rows,
+                                       int64_t K_, int tid) {
+    static_assert(STEP % 2 == 0, "even row steps keep the dword phase");
+    const char* tile = (const char*)base + row0 * SZ;
+    rb = (const char*)((uintptr_t)tile & ~uintptr_t(3));
+    const uint32_t delta = (uint32_t)(tile - rb);
+    ld = ld_;
+    K = K_;
+    ext = (delta + ((K_ - 1) * ld_ + (rows - row0)) * SZ + 3) & ~int64_t(3);
+    k1 = tid / CHR;
+    voff = delta + (uint32_t)((k1 * ld_ + (tid % CHR) * VE) * SZ);
+    shift = voff & 2u;
+  }
+  template <bool PRED>
+  __device__ __forceinline__ void load(int64_t k0) {
+    const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(rb, ext);
+    const uint32_t row_step = (uint32_t)(STEP * ld * SZ);
+    const uint32_t kb = (uint32_t)(k0 * ld * SZ);
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const bool ok = !PRED || k0 + k1 + i * STEP < K;
+      w[i] = raw16(rsrc, ok ? ((voff + kb + i * row_step) & ~3u) : kOobOffset);
+    }
+  }
+  __device__ __forceinline__ void store(u32x4* lds, int tid) const {
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+      lds[mn_slot<CHR>(tid / CHR + i * STEP, tid % CHR)] = realign16(w[i], shift, 0xffu);
+  }
+};
+
+// One MFMA operand fragment from a rows-of-k tile: lane l receives k = kb .. kb + 7 of column
+// col0 + frow, frow being its row / column in the atom's operand layout (frag_row), through two
+// transposing 8-byte reads.  Each read gives every 16-lane group a 4 (k) x 16 (column) block: the
+// lane at place s of its group addresses row kb + 4h + s / 4 at column (the group's first
+// column) + 4 (s % 4), and receives that block's column s; the layouts put the lanes of a group
+// on 16 consecutive columns, frow = (frow & ~15) + s.
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16_t;
+typedef __attribute__((address_space(3))) char lds_char_t;
+template <int CHR>
+__device__ __forceinline__ u32x4 read_rows_frag(const u32x4* tile, int kb, int col0, int frow, int lane) {
+  const int s = lane & 15;
+  const int col = col0 + (frow & ~15) + 4 * (s & 3);
+  u32x4 out;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int k = kb + 4 * h + (s >> 2);
+    const int byte = mn_slot<CHR>(k, col >> 3) * 16 + (col & 4) * 2;
+    const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_v4i16_t*)((lds_char_t*)(tile) + byte));
+    const u32x4 w = __builtin_bit_cast(u32x4, __builtin_shufflevector(v, v, 0, 1, 2, 3, 0, 1, 2, 3));
+    out[2 * h] = w[0];
+    out[2 * h + 1] = w[1];
+  }
+  return out;
+}
+
 // VEC: 0 element loads (any alignment), 1 16-byte loads (aligned rows), 2 realigned 16-byte
 // loads (2-byte types, any element alignment)
 template <int DT, bool KMAJ, int VEC, int R, int BKE, int NT>
@@ -846,9 +964,14 @@ template <int DT, int R, int BKE, int NT>
 struct PickLoader<DT, true, 1, R, BKE, NT> {
   typedef LoadKMajorVec<DT, R, BKE, NT> type;
 };
+// MN-major 2-byte operands of at least 128 rows are kept as rows of k (transposing reads)
+template <int DT, bool KMAJ, int VEC, int R> struct RowsLayout {
+  static constexpr bool value = !KMAJ && VEC != 0 && Ty<DT>::SZ == 2 && R >= 128;
+};
 template <int DT, int R, int BKE, int NT>
 struct PickLoader<DT, false, 1, R, BKE, NT> {
-  typedef LoadMNMajorVec<DT, R, BKE, NT> type;
+  typedef typename std::conditional<RowsLayout<DT, false, 1, R>::value, LoadMNRowsVec<DT, R, BKE, NT>,
+                                    LoadMNMajorVec<DT, R, BKE, NT>>::type type;
 };
 template <int DT, int R, int BKE, int NT>
 struct PickLoader<DT, true, 2, R, BKE, NT> {
@@ -856,7 +979,8 @@ struct PickLoader<DT, true, 2, R, BKE, NT> {
 };
 template <int DT, int R, int BKE, int NT>
 struct PickLoader<DT, false, 2, R, BKE, NT> {
-  typedef LoadMNMajorMis<DT, R, BKE, NT> type;
+  typedef typename std::conditional<RowsLayout<DT, false, 2, R>::value, LoadMNRowsMis<DT, R, BKE, NT>,
+                                    LoadMNMajorMis<DT, R, BKE, NT>>::type type;
 };
 
 // One element of C through a range-checked buffer load: `off` is its byte offset from C's base,
@@ -1072,13 +1196,26 @@ __global__ __launch_bounds__(WM * WN * 64, BM * BN <= 128 * 128 && (AK || BKM) ?
   // fragment addressing: lane row within an atom, and lane group along k
   const int frow = frag_row<DT, MI>(lane), fgrp = frag_chunk<DT, MI>(lane);
   u32x4 fa[2][RM][At::UNITS], fb[2][RN][At::UNITS];
+  // an MN-major operand tile kept as rows of k is read with transposing reads (the chunk c of
+  // the K-major layout is the k run 8c .. 8c + 7)
+  constexpr bool ROWS_A = RowsLayout<DT, AK, VEC, BM>::value, ROWS_B = RowsLayout<DT, BKM, VEC, BN>::value;
   auto read_frags = [&](auto buf, const u32x4* stage, auto sub) {
     const u32x4* As = stage;
     const u32x4* Bs = stage + BM * CH;
     static_for<At::UNITS>([&](auto x) {
       const int c = fgrp + At::G * (sub * At::UNITS + x);
-      static_for<RM>([&](auto i) { fa[buf][i][x] = As[lds_slot<CH>(wm * WTM + i * MI + frow, c)]; });
-      static_for<RN>([&](auto j) { fb[buf][j][x] = Bs[lds_slot<CH>(wn * WTN + j * MI + frow, c)]; });
+      static_for<RM>([&](auto i) {
+        if constexpr (ROWS_A)
+          fa[buf][i][x] = read_rows_frag<BM * SZ / 16>(As, c * (16 / SZ), wm * WTM + i * MI, frow, lane);
+        else
+          fa[buf][i][x] = As[lds_slot<CH>(wm * WTM + i * MI + frow, c)];
+      });
+      static_for<RN>([&](auto j) {
+        if constexpr (ROWS_B)
+          fb[buf][j][x] = read_rows_frag<BN * SZ / 16>(Bs, c * (16 / SZ), wn * WTN + j * MI, frow, lane);
+        else
+          fb[buf][j][x] = Bs[lds_slot<CH>(wn * WTN + j * MI + frow, c)];
+      });
     });
   };
   auto load_tile = [&](int t) {
@@ -1384,7 +1521,7 @@ static hipError_t launch_dma(const KParams& p, hipStream_t s, dim3 grid) {
 // Summation order per output is the same as the two-stage DMA kernel's (k-tiles in order,
 // substeps in order), so both produce the same bits.
 // ------------------------------------------------------------------------------------------
-template <int DT, int WM, int WN, int MI, int NB>
+template <int DT, int WM, int WN, int MI, int NB, bool BKM>
 __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_ring(const KParams p_) {
   KParams p;
   int pid, nwg;
@@ -1424,9 +1561,12 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_ring(const KParams p_) {
   const KRange kr = k_range(p);
   const int64_t K = uniform_i64(kr.len);
   const char* a_tile = uniform_ptr((const char*)p.A + (m0 * p.lda + kr.begin) * SZ);
-  const char* b_tile = uniform_ptr((const char*)p.B + (n0 * p.ldb + kr.begin) * SZ);
+  // B K-major: the tile's first column at its first k; B N-major (row-major): its first k row
+  // at its first column
+  const char* b_tile = uniform_ptr((const char*)p.B + (BKM ? n0 * p.ldb + kr.begin : kr.begin * p.ldb + n0) * SZ);
   const int64_t a_span = uniform_i64(((p.M - m0 - 1) * p.lda + K) * SZ);
-  const int64_t b_span = uniform_i64(((min((int64_t)BN, p.N - n0) - 1) * p.ldb + K) * SZ);
+  const int64_t b_span = uniform_i64(BKM ? ((min((int64_t)BN, p.N - n0) - 1) * p.ldb + K) * SZ
+                                         : ((K - 1) * p.ldb + (p.N - n0)) * SZ);
   // Lane l of DMA block blk fills slot l of a kilobyte: row blk * RPB + l / CH, slot l % CH,
   // which holds logical chunk (l % CH) ^ key(row).  A wave's blocks are NW apart, so its rows
   // differ by multiples of RPB * NW; the key takes row bits 1..3 (2..3 for 64-byte rows), so
@@ -1436,7 +1576,16 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_ring(const KParams p_) {
   const int row0 = wave * RPB + lane / CH;
   const int kc = ((lane % CH) ^ row_key<CH>(row0)) * VE;  // this lane's first k of its chunk
   const uint32_t a_off0 = (uint32_t)(row0 * p.lda * SZ + kc * SZ);
-  const uint32_t b_off0 = (uint32_t)(row0 * p.ldb * SZ + kc * SZ);
+  // B N-major: a k-tile is BKE rows of BN elements (CHR chunks, slot mn_slot); lane l of DMA
+  // block blk fills row blk * 2 + l / CHR, slot l % CHR, which holds logical chunk
+  // (l % CHR) ^ mn_key(row).  A wave's blocks are NW apart, i.e. rows 2 NW apart, and mn_key
+  // takes row bits 0..3, so with 2 NW a multiple of 16 every block has the same chunk per lane.
+  constexpr int CHR = BN * SZ / 16, RPBR = 64 / CHR;
+  static_assert(BKM || (RPBR * NW) % 16 == 0, "one chunk per lane across a wave's B blocks");
+  static_assert(BKM || BKE / RPBR == BN / RPB, "a B unit takes as many DMA blocks either way");
+  const int brow0 = wave * RPBR + lane / CHR;
+  const uint32_t b_off0 = BKM ? (uint32_t)(row0 * p.ldb * SZ + kc * SZ)
+                              : (uint32_t)((brow0 * p.ldb + ((lane % CHR) ^ mn_key(brow0)) * VE) * SZ);
   const int nk = (int)((K + BKE - 1) / BKE);
 
   // Unit OP (0: A, 1: B) of k-tile t into `slot`.  Units past the end of K are all out of range
@@ -1446,20 +1595,36 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_ring(const KParams p_) {
     // elements of this k-tile inside K (at most BKE; zero or less past the end): the per-lane
     // tail check is one 32-bit compare against this uniform value
     const int rem = (int)min(K - k0, (int64_t)BKE);
-    const __amdgpu_buffer_rsrc_t r = OP == 0 ? make_rsrc(a_tile, a_span) : make_rsrc(b_tile, b_span);
-    const uint32_t step = (uint32_t)((OP == 0 ? p.lda : p.ldb) * (RPB * NW * SZ));
-    // The base passes through an empty asm so that the per-block sums are formed here, at the
-    // issue, and not hoisted out of the k-loop as DU more live registers per operand.
-    uint32_t off0 = OP == 0 ? a_off0 : b_off0;
-    asm volatile("" : "+v"(off0));
-    const bool in_k = kc < rem;
     u32x4* st = lds + slot * SLOT;
-    static_for<DU>([&](auto i) {
-      const int blk = wave + NW * i;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(st + blk * 64), 16,
-                                               in_k ? off0 + (uint32_t)i * step : kOobOffset,
-                                               (int)(k0 * SZ), 0, 0);
-    });
+    if constexpr (OP == 1 && !BKM) {
+      // rows of k: the k advance moves the descriptor's base, so the range check (on the VGPR
+      // offset) covers every row and column read; rows past K read zero
+      const int64_t adv = k0 * p.ldb * SZ;
+      const __amdgpu_buffer_rsrc_t r = make_rsrc(b_tile + adv, b_span - adv);
+      const uint32_t step = (uint32_t)(p.ldb * (RPBR * NW * SZ));
+      uint32_t off0 = b_off0;
+      asm volatile("" : "+v"(off0));
+      static_for<DU>([&](auto i) {
+        const int blk = wave + NW * i;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(st + blk * 64), 16,
+                                                 brow0 + RPBR * NW * i < rem ? off0 + (uint32_t)i * step : kOobOffset,
+                                                 0, 0, 0);
+      });
+    } else {
+      const __amdgpu_buffer_rsrc_t r = OP == 0 ? make_rsrc(a_tile, a_span) : make_rsrc(b_tile, b_span);
+      const uint32_t step = (uint32_t)((OP == 0 ? p.lda : p.ldb) * (RPB * NW * SZ));
+      // The base passes through an empty asm so that the per-block sums are formed here, at the
+      // issue, and not hoisted out of the k-loop as DU more live registers per operand.
+      uint32_t off0 = OP == 0 ? a_off0 : b_off0;
+      asm volatile("" : "+v"(off0));
+      const bool in_k = kc < rem;
+      static_for<DU>([&](auto i) {
+        const int blk = wave + NW * i;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(st + blk * 64), 16,
+                                                 in_k ? off0 + (uint32_t)i * step : kOobOffset,
+                                                 (int)(k0 * SZ), 0, 0);
+      });
+    }
   };
 
   const int frow = frag_row<DT, MI>(lane), fgrp = frag_chunk<DT, MI>(lane);
@@ -1473,9 +1638,16 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_ring(const KParams p_) {
   auto read_b = [&](const u32x4* sb, auto sub) {
     static_for<At::UNITS>([&](auto x) {
       const int c = fgrp + At::G * (sub * At::UNITS + x);
-      static_for<RN>([&](auto j) { fb[sub][j][x] = sb[dslot<CH>(wn * WTN + j * MI + frow, c)]; });
+      static_for<RN>([&](auto j) {
+        if constexpr (BKM)
+          fb[sub][j][x] = sb[dslot<CH>(wn * WTN + j * MI + frow, c)];
+        else
+          fb[sub][j][x] = read_rows_frag<CHR>(sb, c * VE, wn * WTN + j * MI, frow, lane);
+      });
     });
   };
+  // LDS read instructions per B fragment (two transposing reads from rows of k)
+  constexpr int RB = BKM ? 1 : 2;
   auto mma_rows = [&](auto buf, auto sub, auto i0, auto i1) {
     static_for<At::PER_UNIT>([&](auto u) {
       static_for<i1 - i0>([&](auto ii) {
@@ -1531,7 +1703,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_ring(const KParams p_) {
         mma_rows(std::integral_constant<int, buf>{}, s, I0{}, std::integral_constant<int, RM>{});
         // the first substep also carries the B reads of the rest of the k-tile
         interleave(std::integral_constant<int, nvm>{},
-                   std::integral_constant<int, RM * At::UNITS + (s == 0 ? (S - 1) * RN * At::UNITS : 0)>{},
+                   std::integral_constant<int, RM * At::UNITS + (s == 0 ? (S - 1) * RN * At::UNITS * RB : 0)>{},
                    std::integral_constant<int, RM * RN * At::PER_UNIT>{});
         if constexpr (s + 1 == MID && NB == 2) {
           // this wave's reads of B(t) are complete (lgkmcnt 0); after the barrier no wave
@@ -1564,7 +1736,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_ring(const KParams p_) {
         mma_rows(std::integral_constant<int, buf>{}, s, std::integral_constant<int, RM / 2>{},
                  std::integral_constant<int, RM>{});
         interleave(std::integral_constant<int, NB == 1 ? 2 * DU : 0>{},
-                   std::integral_constant<int, (RM + RN) * At::UNITS>{},
+                   std::integral_constant<int, (RM + RN * RB) * At::UNITS>{},
                    std::integral_constant<int, RM / 2 * RN * At::PER_UNIT>{});
       }
     };
@@ -1612,9 +1784,9 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_ring(const KParams p_) {
   }
 }
 
-template <int DT, int WM, int WN, int MI, int NB>
+template <int DT, int WM, int WN, int MI, int NB, bool BKM>
 static hipError_t launch_ring(const KParams& p, hipStream_t s, dim3 grid) {
-  hipLaunchKernelGGL((gemm_ring<DT, WM, WN, MI, NB>), grid, dim3(WM * WN * 64), 0, s, p);
+  hipLaunchKernelGGL((gemm_ring<DT, WM, WN, MI, NB, BKM>), grid, dim3(WM * WN * 64), 0, s, p);
   return hipGetLastError();
 }
 
@@ -1899,26 +2071,31 @@ static hipError_t launch_tiled(const KParams& p, hipStream_t s, dim3 grid) {
 #define HT_TILED(NAME, DT, AK, BKM, VEC, BM, BN, BKE, WM, WN, MI)                                 \
   {NAME, DT, AK, BKM, (VEC) == 1, 0, BM, BN, BKE, WM * WN, 2, 2 * (BM + BN) * BKE * Ty<DT>::SZ, 64, \
    (VEC) == 2 ? 1 : 0, &launch_tiled<DT, AK, BKM, VEC, BM, BN, BKE, WM, WN, MI>, (VEC) == 2, \
-   (VEC) == 2 ? 1 : 0, MI, BKE * Ty<DT>::SZ / 16}
+   (VEC) == 2 ? 1 : 0, MI, BKE * Ty<DT>::SZ / 16,                                               \
+   RowsLayout<DT, AK, VEC, BM>::value || RowsLayout<DT, BKM, VEC, BN>::value}
 
 #define HT_DMA(NAME, DT, BM, BN, WM, WN, MI, ST, OCC, CH, RANK)                                \
   {NAME, DT, 1, 1, 1, 0, BM, BN, CH * 16 / Ty<DT>::SZ, WM * WN, ST, ST * (BM + BN) * CH * 16, 1, \
-   RANK, &launch_dma<DT, BM, BN, WM, WN, MI, ST, OCC, CH>, 0, RANK, MI, CH}
+   RANK, &launch_dma<DT, BM, BN, WM, WN, MI, ST, OCC, CH>, 0, RANK, MI, CH, 0}
 
-// Split-ring entries: 256 x 256 tiles, 128-byte rows, 5 units of 32 KiB.
+// Split-ring entries: 256 x 256 tiles, 128-byte rows, 5 units of 32 KiB.  The _BN form takes a
+// row-major (N-contiguous) B kept in LDS as rows of k.
 #define HT_RING(NAME, DT, WM, WN, MI, NB, RANK, RANK1)                                               \
   {NAME, DT, 1, 1, 1, 0, 256, 256, 128 / Ty<DT>::SZ, WM * WN, 5, 5 * 256 * 128, 64, RANK,         \
-   &launch_ring<DT, WM, WN, MI, NB>, 0, RANK1, MI, 8}
+   &launch_ring<DT, WM, WN, MI, NB, true>, 0, RANK1, MI, 8, 0}
+#define HT_RING_BN(NAME, DT, WM, WN, MI, NB, RANK, RANK1)                                            \
+  {NAME, DT, 1, 0, 1, 0, 256, 256, 128 / Ty<DT>::SZ, WM * WN, 5, 5 * 256 * 128, 64, RANK,         \
+   &launch_ring<DT, WM, WN, MI, NB, false>, 0, RANK1, MI, 8, 1}
 
 // Streaming skinny entries: bm = 16 rows, bn = 16*NBW columns, bk = one 128-byte block of K.
 #define HT_SKINNY_DMA(NAME, DT, WK, NBW, R, OCC)                                                  \
   {NAME, DT, 1, 1, 1, 1, 16, NBW * 16, 128 / Ty<DT>::SZ, WK, R, WK * R * (NBW + 1) * 16 * 128, 1, 0, \
-   &launch_skinny_dma<DT, WK, NBW, R, OCC>, 0, 0, 16, 8}
+   &launch_skinny_dma<DT, WK, NBW, R, OCC>, 0, 0, 16, 8, 0}
 
 // Skinny entries: bm = 16 rows, bn = WN*NBW*16 columns per workgroup, bk = one MFMA k-step (no
 // LDS operand tiles).
 #define HT_SKINNY(NAME, DT, WK, WN, NBW, U, OCC)                                                 \
   {NAME, DT, 1, 1, 1, 1, 16, WN * NBW * 16, 4 * Atom<DT, 16>::UNITS * 16 / Ty<DT>::SZ, WK * WN, \
-   1, WK * WN * NBW * 16 * 16 * 4, 1, 0, &launch_skinny<DT, WK, WN, NBW, U, OCC>, 0, 0, 16, 0}
+   1, WK * WN * NBW * 16 * 16 * 4, 1, 0, &launch_skinny<DT, WK, WN, NBW, U, OCC>, 0, 0, 16, 0, 0}
 
 }  // namespace htk

@@ -77,6 +77,11 @@ def place(bits_rowmajor: np.ndarray, rows: int, cols: int, dtype: str, order: st
           ld: int | None = None, fill: int = 0) -> HostMatrix:
     """Lay out logical row-major bits in the requested storage order."""
     strides, n = layout_strides(rows, cols, order, ld)
+    if rows and cols and ld is None:
+        # dense layouts: the logical bits themselves, or their transpose
+        logical = np.ascontiguousarray(bits_rowmajor, dtype=STORAGE[dtype]).reshape(rows, cols)
+        storage = logical.ravel() if order == "row" else np.ascontiguousarray(logical.T).ravel()
+        return HostMatrix(storage.copy(), dtype, (rows, cols), strides)
     storage = np.full(max(n, 1) if rows and cols else 0, fill, dtype=STORAGE[dtype])
     if rows and cols:
         logical = bits_rowmajor.reshape(rows, cols)
