@@ -35,6 +35,7 @@ SOURCES = [
     ("table.cpp", HIP),
     ("reduce.hip", HIP),
     ("probe.hip", HIP),
+    ("repack.hip", HIP),
     ("api.cpp", HIP),
     ("layout.cpp", ["g++"] + COMMON),
 ]

@@ -49,6 +49,13 @@ struct gemm_handle_s {
   int64_t kps_cfg, kps_fb;     // K elements per slice
   int tail_tiles, tail_split;  // split tail of the cfg entry (tail_split 1: none)
   int64_t tail_kps;            // K elements per slice of a tail tile
+  // Repack plan: A and B are read through K-major, 16-byte aligned copies of K padded to kp
+  // (zeros past K) at the start of the workspace (A' then B', each rounded to 256 bytes), and
+  // cfg is the entry chosen for that aligned problem.  An operand that is already K-major with
+  // a 16-byte leading dimension, K == kp and a 16-byte aligned pointer is used in place.
+  int repack;
+  int64_t kp;
+  size_t repack_bytes_a, repack_bytes_b;
 };
 
 namespace {
@@ -344,6 +351,27 @@ bool entry_maps_ok(const KernelEntry& e) {
   return e.lds_row_chunks == 0;
 }
 
+// Whether to run a product whose operands the 16-byte loaders cannot read (a leading dimension
+// or base off 16 bytes, or an fp8 operand that is not K-contiguous) on aligned K-major copies:
+// one extra pass over A and B (HBM-bound) against running every k-tile with realigned or
+// element-wise register-staged loads, which keep only one k-tile of loads in flight.  Measured
+// on MI355X, odd leading dimensions and row-major B (copies + chosen kernel vs the best direct
+// entry):
+//   f16  4099 x 3071 x 2053   110 us vs 129 us (realigned 128 x 128)
+//   f16  2051 x 1533 x 1027   41.5 us vs 33.1 us
+//   f16  1503 x 1301 x 1101   28.7 us vs 32.1 us
+//   e4m3 2051 x 1533 x 1027   34.7 us vs 122.6 us (element loads)
+//   e4m3 3001 x 2999 x 2049   81.1 us vs 533 us
+// 2-byte types have realigned loaders and take the copies from 2^35 FLOP; fp8 and fp32, which
+// only have element-wise loaders for such operands, from 2^31.  Batches and groups keep the
+// direct path.
+bool repack_pays(const gemm_desc& d, bool vec_both) {
+  if (vec_both || d.ragged_m || d.batch > 1) return false;
+  if (d.M < 128 || d.N < 128 || d.K < 64) return false;
+  const double flop = 2.0 * (double)d.M * (double)d.N * (double)d.K;
+  return flop >= (dtype_size(d.a_type) == 2 ? 34359738368.0 : 2147483648.0);
+}
+
 int check_arch() {
   const char* fake = std::getenv("HTGEMM_FAKE_ARCH");
   if (fake && *fake) return std::strncmp(fake, "gfx950", 6) == 0 ? GEMM_OK : GEMM_ERR_ARCH;
@@ -422,6 +450,37 @@ int gemm_create(const gemm_desc* desc, gemm_t* out) {
   const int split_req = L > 1 || d.ragged_m || d.has_row_sumsq || d.has_col_sum ? 1 : d.split_k;
   h.fallback = choose(h, va, vb, false, split_req);
   if (h.fallback < 0) return GEMM_ERR_NO_CONFIG;
+  if (d.force_config < 0 && repack_pays(d, va && vb)) {
+    // the product runs on aligned K-major copies of A and B: choose for that problem
+    gemm_handle_s v = h;
+    v.kp = (d.K + 16 / isz - 1) / (16 / isz) * (16 / isz);
+    v.d.K = v.kp;
+    v.d.a_stride_m = v.kp;
+    v.d.a_stride_k = 1;
+    v.d.b_stride_k = 1;
+    v.d.b_stride_n = v.kp;
+    v.a = Operand{true, v.kp};
+    v.b = Operand{true, v.kp};
+    const int inner = choose(v, true, true, true, split_req);
+    if (inner >= 0 && table()[inner].vec) {
+      h.repack = 1;
+      h.kp = v.kp;
+      h.cfg = h.fallback = inner;
+      h.repack_bytes_a = ((size_t)d.M * v.kp * isz + 255) / 256 * 256;
+      h.repack_bytes_b = ((size_t)d.N * v.kp * isz + 255) / 256 * 256;
+      if (!entry_maps_ok(table()[inner])) return GEMM_ERR_LANE_MAP;
+      h.group_m = 4;
+      plan_split(table()[inner], v.d, split_req, &h.split_cfg, &h.kps_cfg);
+      h.split_fb = h.split_cfg;
+      h.kps_fb = h.kps_cfg;
+      plan_tail(table()[inner], v.d, split_req, h.split_cfg, &h.tail_tiles, &h.tail_split, &h.tail_kps);
+      gemm_handle_s* p = new (std::nothrow) gemm_handle_s(h);
+      if (!p) return GEMM_ERR_INVALID_ARG;
+      p->magic = kMagic;
+      *out = p;
+      return GEMM_OK;
+    }
+  }
   if (d.force_config >= 0) {
     if (d.force_config >= table_size() || !entry_fits(table()[d.force_config], h, va, vb))
       return GEMM_ERR_NO_CONFIG;
@@ -466,11 +525,27 @@ size_t reduction_bytes(const gemm_handle_s& h, size_t* col_off) {
 }
 }  // namespace
 
+namespace {
+size_t inner_workspace(const gemm_handle_s& h);
+}  // namespace
+
 extern "C" {
 
 int gemm_workspace_size(gemm_t h, size_t* bytes) {
   if (!h || h->magic != kMagic) return GEMM_ERR_BAD_HANDLE;
   if (!bytes) return GEMM_ERR_INVALID_ARG;
+  *bytes = h->repack_bytes_a + h->repack_bytes_b + inner_workspace(*h);
+  return GEMM_OK;
+}
+
+}  // extern "C"
+
+namespace {
+// Workspace of the kernels proper (split-K planes, split-tail partials or reduction partials).
+size_t inner_workspace(const gemm_handle_s& hh) {
+  const gemm_handle_s* h = &hh;
+  size_t v = 0;
+  size_t* bytes = &v;
   const int s = std::max(h->split_cfg, h->split_fb);
   *bytes = s > 1 ? (size_t)s * (size_t)h->d.M * (size_t)h->d.N * sizeof(float) : 0;
   if (h->tail_split > 1) {
@@ -479,8 +554,11 @@ int gemm_workspace_size(gemm_t h, size_t* bytes) {
                                   (size_t)e.bn * sizeof(float));
   }
   if (h->d.has_row_sumsq || h->d.has_col_sum) *bytes = reduction_bytes(*h, nullptr);
-  return GEMM_OK;
+  return v;
 }
+}  // namespace
+
+extern "C" {
 
 int gemm_get_info(gemm_t h, gemm_info* info) {
   if (!h || h->magic != kMagic) return GEMM_ERR_BAD_HANDLE;
@@ -502,6 +580,7 @@ int gemm_get_info(gemm_t h, gemm_info* info) {
   std::strncpy(info->name, e.name, sizeof(info->name) - 1);
   info->tail_tiles = h->tail_split > 1 ? h->tail_tiles : 0;
   info->tail_split = h->tail_split;
+  info->repack = h->repack;
   return GEMM_OK;
 }
 
@@ -534,8 +613,38 @@ int run_impl(gemm_t h, const void* A, const void* B, const void* C, void* D, con
       (read_c && !aligned(C, out_sz)) || (d.has_bias && !aligned(bias, out_sz)))
     return GEMM_ERR_MISALIGNED;
 
+  // The operands the kernels read: A and B themselves, or (repack plan) their aligned K-major
+  // copies in the workspace, written by one copy kernel each on `stream` before the product.
+  const void* Ae = A;
+  const void* Be = B;
+  int64_t lda = h->a.ld, ldb = h->b.ld, Ke = d.K;
+  if (h->repack) {
+    if (!workspace || !aligned(workspace, 16)) return GEMM_ERR_INVALID_ARG;
+    char* ws = static_cast<char*>(workspace);
+    const bool a_direct = h->a.kmajor && (h->a.ld * (int64_t)in_sz) % 16 == 0 && h->a.ld >= d.K &&
+                          h->kp == d.K && aligned(A, 16);
+    const bool b_direct = h->b.kmajor && (h->b.ld * (int64_t)in_sz) % 16 == 0 && h->b.ld >= d.K &&
+                          h->kp == d.K && aligned(B, 16);
+    hipError_t err = hipSuccess;
+    if (!a_direct) {
+      err = launch_repack(A, ws, d.M, d.K, h->kp, d.a_stride_m, d.a_stride_k, (int)in_sz,
+                          (hipStream_t)stream);
+      Ae = ws;
+      lda = h->kp;
+    }
+    if (err == hipSuccess && !b_direct) {
+      err = launch_repack(B, ws + h->repack_bytes_a, d.N, d.K, h->kp, d.b_stride_n, d.b_stride_k,
+                          (int)in_sz, (hipStream_t)stream);
+      Be = ws + h->repack_bytes_a;
+      ldb = h->kp;
+    }
+    if (err != hipSuccess) return GEMM_ERR_LAUNCH;
+    Ke = h->kp;
+    workspace = ws + h->repack_bytes_a + h->repack_bytes_b;
+  }
+
   int idx = h->cfg;
-  if (table()[idx].vec && (!aligned(A, 16) || !aligned(B, 16))) idx = h->fallback;
+  if (table()[idx].vec && (!aligned(Ae, 16) || !aligned(Be, 16))) idx = h->fallback;
   const KernelEntry& e = table()[idx];
   const int split = idx == h->cfg ? h->split_cfg : h->split_fb;
   const int64_t kps = idx == h->cfg ? h->kps_cfg : h->kps_fb;
@@ -545,16 +654,16 @@ int run_impl(gemm_t h, const void* A, const void* B, const void* C, void* D, con
 
   KParams p;
   std::memset(&p, 0, sizeof(p));
-  p.A = A;
-  p.B = B;
+  p.A = Ae;
+  p.B = Be;
   p.C = read_c ? C : nullptr;
   p.D = D;
   p.bias = d.has_bias ? bias : nullptr;
   p.M = d.M;
   p.N = d.N;
-  p.K = d.K;
-  p.lda = h->a.ld;
-  p.ldb = h->b.ld;
+  p.K = Ke;
+  p.lda = lda;
+  p.ldb = ldb;
   p.c_sm = d.c_stride_m;
   p.c_sn = d.c_stride_n;
   p.d_sm = d.d_stride_m;

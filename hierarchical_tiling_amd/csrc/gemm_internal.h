@@ -83,6 +83,11 @@ hipError_t launch_row_sumsq_reduce(const float* ws, float* out, int64_t M, int t
 // The same fixed-order sum for the column sums: out[n] = sum over t < planes of ws[t * N + n].
 // (The row reduction is this with N = M and planes = tiles_n.)
 
+// Copy of an operand into a K-major, 16-byte aligned, zero-padded buffer: dst[r * Kp + k] =
+// src(r, k) (element offset r * s_row + k * s_k) for k < K, 0 for K <= k < Kp (repack.hip).
+hipError_t launch_repack(const void* src, void* dst, int64_t rows, int64_t K, int64_t Kp,
+                         int64_t s_row, int64_t s_k, int esize, hipStream_t s);
+
 // Output type of a given operand type (htgemm.h type table).
 constexpr int out_dtype(int dt) { return dt == DT_F8 ? DT_BF16 : dt; }
 constexpr int dtype_size(int dt) { return dt == DT_F32 ? 4 : (dt == DT_F8 ? 1 : 2); }

@@ -74,7 +74,8 @@ class gemm_info(ctypes.Structure):
                 ("waves", ctypes.c_int32), ("stages", ctypes.c_int32),
                 ("lds_bytes", ctypes.c_int32), ("split_k", ctypes.c_int32),
                 ("grid", ctypes.c_int64), ("name", ctypes.c_char * 96),
-                ("tail_tiles", ctypes.c_int32), ("tail_split", ctypes.c_int32)]
+                ("tail_tiles", ctypes.c_int32), ("tail_split", ctypes.c_int32),
+                ("repack", ctypes.c_int32)]
 
 
 class ht_tile_stats(ctypes.Structure):

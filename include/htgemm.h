@@ -151,7 +151,12 @@ int gemm_create(const gemm_desc* desc, gemm_t* out);
 
 /* Bytes of device workspace gemm_run needs for this handle: 0 unless the problem is split along
  * K ("CUTLASS", Part III: split-K for outputs with too few tiles to fill the GPU), in which case
- * it is split_k * M * N * 4 (one fp32 plane of partial sums per slice).  A split tail (the
+ * it is split_k * M * N * 4 (one fp32 plane of partial sums per slice).  A large product whose A
+ * or B the 16-byte loaders cannot read (a leading dimension off 16 bytes, K not a multiple of
+ * 16 bytes' worth of elements, or an fp8 operand that is not K-contiguous) runs on K-major,
+ * aligned copies of both (gemm_info.repack): the workspace then starts with M * Kp and N * Kp
+ * elements (each rounded up to 256 bytes), Kp being K rounded up to 16 bytes' worth, and
+ * gemm_run writes them with one copy kernel per operand on the stream before the product.  A split tail (the
  * Stream-K idea, same Part: the tiles of a last round that would leave most CUs idle are each
  * split along K) needs tail_split * tail_tiles * bm * bn * 4 (gemm_info).  With has_row_sumsq it
  * is the number of N tiles * M * 4, and has_col_sum adds (M tiles * row groups) * N * 4.  The caller owns the
@@ -254,6 +259,7 @@ typedef struct gemm_info {
   char name[96];          /* kernel name                                                        */
   int32_t tail_tiles;     /* tiles of an incomplete last round run split along K (0: none)      */
   int32_t tail_split;     /* K slices of each such tile (1: none)                               */
+  int32_t repack;         /* 1: A and B are read through aligned K-major copies in the workspace */
 } gemm_info;
 
 int gemm_get_info(gemm_t h, gemm_info* info);

@@ -125,9 +125,23 @@ def test_tile_table_choices(fake_gfx950):
     big = _info(desc(M=8192, N=8192, K=8192, a_strides=(8192, 1), b_strides=(1, 8192), d_strides=(8192, 1)))
     assert (big.bm, big.bn) == (256, 256) and big.name.startswith(b"bf16_ak_bk")
     assert big.grid == 32 * 32
-    # ragged fp16 with odd leading dimensions (2-byte aligned rows): the realigning loader
-    rag = _info(H.make_desc(4099, 3071, 2053, "f16", (2053, 1), (3071, 1), (3071, 1), c_strides=(3071, 1)))
-    assert b"realign" in rag.name and rag.config == rag.fallback
+    # ragged fp16 with odd leading dimensions (2-byte aligned rows): a small product takes the
+    # realigning loader; a large one runs on aligned K-major copies of A and B (K padded to 2056)
+    # made in the workspace, with the split ring
+    small_rag = _info(H.make_desc(2051, 1533, 1027, "f16", (1027, 1), (1533, 1), (1533, 1)))
+    assert b"realign" in small_rag.name and not small_rag.repack
+    # fp8 has no realigning loader: copies from 2^31 FLOP (row-major B here)
+    r8 = _info(H.make_desc(2051, 1533, 1027, "e4m3", (1027, 1), (1533, 1), (1533, 1)))
+    assert r8.repack and r8.name.startswith(b"e4m3_ak_bk_")
+    d_rag = H.make_desc(4099, 3071, 2053, "f16", (2053, 1), (3071, 1), (3071, 1), c_strides=(3071, 1))
+    rag = _info(d_rag)
+    assert rag.repack and rag.name.startswith(b"f16_ak_bk_") and rag.config == rag.fallback
+    h = H.gemm_create(d_rag)
+    try:
+        copies = ((4099 * 2056 * 2 + 255) // 256 + (3071 * 2056 * 2 + 255) // 256) * 256
+        assert H.gemm_workspace_size(h) == copies      # the ring here needs no split workspace
+    finally:
+        H.gemm_destroy(h)
     # fp8 and fp32 have no realigning loader: element loads
     rag8 = _info(H.make_desc(301, 257, 203, "e4m3", (203, 1), (1, 203), (257, 1)))
     assert b"narrow" in rag8.name
@@ -367,7 +381,8 @@ def test_kernel_choice_by_rounds(fake_gfx950, shape, kernel, split, tail):
     # odd leading dimensions: realigned loaders; 128x128 from 129 workgroups
     ("f16", (1001, 999, 1003), ("row", "row"), "_64x64x64_w2x2_m16_realign"),
     ("f16", (2051, 1533, 1027), ("row", "row"), "_128x128x64_w2x2_m32_realign"),
-    ("f16", (4099, 3071, 2053), ("row", "row"), "_128x128x64_w2x2_m32_realign"),
+    # from 2^35 FLOP a 2-byte product runs on aligned K-major copies (gemm_info.repack)
+    ("f16", (4099, 3071, 2053), ("row", "row"), "_ak_bk_256x256x64_w2x4_m16_ring"),
     ("bf16", (255, 257, 251), ("row", "row"), "_64x64x64_w2x2_m16_realign"),         # rank breaks the tie
 ])
 def test_kernel_choice_small_and_realigned(fake_gfx950, dtype, shape, orders, kernel):
