@@ -16,7 +16,6 @@ from __future__ import annotations
 import argparse
 import json
 import os
-import subprocess
 import sys
 import threading
 import time
@@ -250,12 +249,20 @@ def run_metadata(threads):
         meta["rocm"] = open("/opt/rocm/.info/version").read().strip()
     except OSError:
         meta["rocm"] = None
+    # the compiler that built the library (recorded by the build; no child process here, which
+    # under a profiler's preload would start a second GPU client)
     try:
-        out = subprocess.run(["/opt/rocm/bin/hipcc", "--version"], capture_output=True, text=True,
-                             timeout=30).stdout.splitlines()
-        meta["hipcc"] = next((line for line in out if line.startswith("HIP version")), None)
+        with open(os.path.join(ROOT, "hierarchical_tiling_amd", "libhtgemm.so.buildinfo")) as f:
+            meta.update(json.loads(f.read()))
     except Exception:
         meta["hipcc"] = None
+    try:
+        import ctypes
+        v = ctypes.c_int()
+        ctypes.CDLL("libamdhip64.so").hipRuntimeGetVersion(ctypes.byref(v))
+        meta["hip_runtime_version"] = v.value
+    except Exception:
+        meta["hip_runtime_version"] = None
     try:
         meta["cpu_model"] = next(line.split(":", 1)[1].strip() for line in open("/proc/cpuinfo")
                                  if line.startswith("model name"))
@@ -324,6 +331,8 @@ def main():
     ap.add_argument("--sub-steps", type=int, default=30)
     ap.add_argument("--sub-warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-clock", action="store_true",
+                    help="skip the one-second sustained run that samples the shader clock")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run 5 plain device copies of 1 GiB (counter calibration) and exit")
     args = ap.parse_args()
@@ -337,7 +346,7 @@ def main():
     import torch
     dev = torch.device("cuda:0")
     threads = max(1, min(16, len(os.sched_getaffinity(0))))
-    sampler = ClockSampler()
+    sampler = None if args.no_clock else ClockSampler()
     main_res, host0 = measure(args.workload, args.steps, args.warmup, dev, clock_sampler=sampler)
     torch.cuda.empty_cache()
     subs = []

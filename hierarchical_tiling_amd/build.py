@@ -8,6 +8,7 @@ binding loads it in-tree.
 from __future__ import annotations
 
 import concurrent.futures as cf
+import json
 import os
 import subprocess
 import sys
@@ -71,6 +72,12 @@ def build(verbose: bool = True, incremental: bool = False) -> str:
     if res.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(link)}\n{res.stdout}\n{res.stderr}")
     os.replace(tmp, OUT)
+    # the compiler that built the library, for the benchmark's run record
+    ver = subprocess.run([HIPCC, "--version"], capture_output=True, text=True).stdout.splitlines()
+    with open(OUT + ".buildinfo", "w") as f:
+        f.write(json.dumps({"hipcc": next((v for v in ver if v.startswith("HIP version")), None),
+                            "clang": next((v for v in ver if "clang version" in v), None),
+                            "offload_arch": ARCH}) + "\n")
     if verbose:
         print(f"built {OUT}")
     return OUT

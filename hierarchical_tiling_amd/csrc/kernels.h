@@ -1318,20 +1318,6 @@ __device__ __forceinline__ void barrier_nofence() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-// A read of the shader timer through the scalar memory path, waited for at once; the result is
-// unused.  Issued right after the end-of-k-tile barrier of the split-ring kernel it raises
-// whole-kernel throughput by 6-9% on 8192^3 bf16 (measured on several machines): the cycles per
-// k-tile stay the same while the shader clock under the power limit runs about 5% higher.  A
-// scalar ALU read, s_sleep, s_nop or the same read before the barrier do not do this; the
-// mechanism was not established.  The wait sits in the same asm statement: the timer value is
-// written to its SGPRs asynchronously, and the compiler, which does not see that write, could
-// otherwise hand those registers to another value first.  Outstanding LDS reads are zero at that
-// point, so the wait covers the timer read alone.
-__device__ __forceinline__ void smem_timer_read() {
-  uint64_t t;
-  asm volatile("s_memtime %0\n\ts_waitcnt lgkmcnt(0)" : "=s"(t));
-}
-
 // Values that are the same in every lane, passed through readfirstlane so the compiler keeps
 // them in scalar registers (buffer descriptors must be scalar; a value it cannot prove uniform
 // gets a readfirstlane loop around every use).
@@ -1720,7 +1706,6 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_ring(const KParams p_) {
         // per k-tile: once at most A(t+2), issued after B(t+1), is)
         if constexpr (NB == 2) wait_counts<2 * DU, true>(); else wait_counts<DU, true>();
         barrier_nofence();
-        smem_timer_read();
         // (after the last k-tile these read zero-filled slots; the values are never used).  B
         // first: the next substep's first MFMAs need A fragment 0 and every B fragment
         const int na = sa_i == 2 ? 0 : sa_i + 1;
@@ -1817,7 +1802,9 @@ __global__ __launch_bounds__(WK * WN * 64, OCC) void gemm_skinny(const KParams p
   constexpr int BN = WN * NBW * 16;           // columns per workgroup
   static_assert(At::PER_UNIT == 1, "one MFMA per k-step");
 
-  __shared__ float part[WK][BN / 16][16][16];  // partial sums of each K slice
+  // partial sums of each K slice; rows padded to 17 floats so that the four 16-lane groups of a
+  // store, which write rows 4 apart, fall on different banks
+  __shared__ float part[WK][BN / 16][16][17];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wk = wave % WK, wn = wave / WK;
@@ -2027,11 +2014,13 @@ __global__ __launch_bounds__(WK * 64, OCC) void gemm_skinny_dma(const KParams p_
 
   // partial sums -> LDS (reusing the ring); reduction over the WK slices; epilogue
   __syncthreads();
-  float* part = reinterpret_cast<float*>(&ring[0][0][0]);  // [WK][NBW][16][16]
-  static_assert(sizeof(ring) >= sizeof(float) * WK * NBW * 256, "reduction buffer");
+  // [WK][NBW][16][17]: rows padded to 17 floats so that the four 16-lane groups of a store, which
+  // write rows 4 apart, fall on different banks
+  float* part = reinterpret_cast<float*>(&ring[0][0][0]);
+  static_assert(sizeof(ring) >= sizeof(float) * WK * NBW * 16 * 17, "reduction buffer");
   static_for<NBW>([&](auto b) {
     static_for<4>([&](auto r) {
-      part[((wave * NBW + b) * 16 + acc_row<DT, 16>(lane, r)) * 16 + acc_col<DT, 16>(lane, r)] = acc[b][(int)r];
+      part[((wave * NBW + b) * 16 + acc_row<DT, 16>(lane, r)) * 17 + acc_col<DT, 16>(lane, r)] = acc[b][(int)r];
     });
   });
   __syncthreads();
@@ -2043,7 +2032,7 @@ __global__ __launch_bounds__(WK * 64, OCC) void gemm_skinny_dma(const KParams p_
     if (row >= p.M || col >= p.N) continue;
     float sum = 0.f;
 #pragma unroll
-    for (int w = 0; w < WK; ++w) sum += part[((w * NBW + c / 16) * 16 + row) * 16 + c % 16];
+    for (int w = 0; w < WK; ++w) sum += part[((w * NBW + c / 16) * 16 + row) * 17 + c % 16];
     O::store(p.D, row * p.d_sm + col * p.d_sn, finish_elem<ODT>(p, row, col, sum));
   }
 }
