@@ -527,6 +527,11 @@ size_t reduction_bytes(const gemm_handle_s& h, size_t* col_off) {
 
 namespace {
 size_t inner_workspace(const gemm_handle_s& h);
+// grouped launches: G + 1 effective offsets (int32, padded to 256 bytes), then G + 1 first tiles
+size_t group_lo_bytes(int64_t G) { return ((size_t)(G + 1) * 4 + 255) / 256 * 256; }
+size_t group_table_bytes(const gemm_handle_s& h) {
+  return h.d.ragged_m ? group_lo_bytes(h.d.batch) + (size_t)(h.d.batch + 1) * 8 : 0;
+}
 }  // namespace
 
 extern "C" {
@@ -534,7 +539,7 @@ extern "C" {
 int gemm_workspace_size(gemm_t h, size_t* bytes) {
   if (!h || h->magic != kMagic) return GEMM_ERR_BAD_HANDLE;
   if (!bytes) return GEMM_ERR_INVALID_ARG;
-  *bytes = h->repack_bytes_a + h->repack_bytes_b + inner_workspace(*h);
+  *bytes = h->repack_bytes_a + h->repack_bytes_b + inner_workspace(*h) + group_table_bytes(*h);
   return GEMM_OK;
 }
 
@@ -702,7 +707,16 @@ int run_impl(gemm_t h, const void* A, const void* B, const void* C, void* D, con
   unsigned gz = (unsigned)p.batch;
   if (offsets) {
     // grouped: every group's tiles in one x range, sized for the most tiles any split of the M
-    // rows into `batch` groups can need (each group adds at most one partial tile row)
+    // rows into `batch` groups can need (each group adds at most one partial tile row); the
+    // groups' tile table is built on the stream first, in the workspace
+    if (!workspace || !aligned(workspace, 16)) return GEMM_ERR_INVALID_ARG;
+    int32_t* glo = static_cast<int32_t*>(workspace);
+    int64_t* gbase = reinterpret_cast<int64_t*>(static_cast<char*>(workspace) + group_lo_bytes(d.batch));
+    if (launch_group_scan(offsets, (int)d.batch, d.M, e.bm, p.tiles_n, glo, gbase,
+                          (hipStream_t)stream) != hipSuccess)
+      return GEMM_ERR_LAUNCH;
+    p.group_lo = glo;
+    p.group_base = gbase;
     p.offsets = offsets;
     p.a_row_bytes = h->a.ld * (int64_t)in_sz;
     p.c_row_bytes = d.c_stride_m * (int64_t)out_sz;

@@ -33,6 +33,8 @@ struct KParams {
   int64_t c_span;          // bytes from C's base to the end of its last element when below
                            // 2^31 - 64 (range-checked buffer loads), else 0
   const int32_t* offsets;  // grouped launch: batch + 1 row offsets (device); nullptr otherwise
+  const int32_t* group_lo;    // grouped: batch + 1 effective row offsets (gemm_group_scan)
+  const int64_t* group_base;  // grouped: batch + 1 first tile indices of the groups
   int64_t a_row_bytes, c_row_bytes, d_row_bytes;  // bytes between consecutive rows (grouped)
   float* rsq_ws;           // row sums of squares: one partial per (tile column, row), or nullptr
   float* csum_ws;          // column sums: one partial per (tile row, row group, column), or nullptr
@@ -87,6 +89,13 @@ hipError_t launch_row_sumsq_reduce(const float* ws, float* out, int64_t M, int t
 // src(r, k) (element offset r * s_row + k * s_k) for k < K, 0 for K <= k < Kp (repack.hip).
 hipError_t launch_repack(const void* src, void* dst, int64_t rows, int64_t K, int64_t Kp,
                          int64_t s_row, int64_t s_k, int esize, hipStream_t s);
+
+// Grouped launches: from the caller's G + 1 device row offsets, the effective offsets lo[0..G]
+// (clamped into [0, M] and made non-decreasing) and the first tile of each group base[0..G]
+// (base[G] = all tiles), groups of ceil((lo[e+1] - lo[e]) / bm) * tiles_n tiles in order.  One
+// workgroup; the tile kernels then find their group by binary search.
+hipError_t launch_group_scan(const int32_t* offsets, int G, int64_t M, int bm, int tiles_n,
+                             int32_t* lo, int64_t* base, hipStream_t s);
 
 // Output type of a given operand type (htgemm.h type table).
 constexpr int out_dtype(int dt) { return dt == DT_F8 ? DT_BF16 : dt; }

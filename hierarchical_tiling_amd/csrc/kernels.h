@@ -340,43 +340,40 @@ __device__ __forceinline__ KParams reload_args() {
 // blockIdx.x of gridDim.x.  A grouped launch with ragged M (mixture-of-experts: "CUTLASS",
 // Part V, a grouped GEMM in which each expert is one problem of a batch of differently shaped
 // problems) shares A's, C's and D's row space among the groups: group e owns rows
-// [offsets[e], offsets[e+1]) and multiplies them by its own B, and the grid enumerates the tiles
-// of every group in order.  Offsets are clamped into [0, M] and made non-decreasing, so no
-// offset array can send a workgroup outside the operands.  Returns false for a workgroup past
-// the last group's tiles (the grid is sized for the most tiles any split of M can need); such a
-// workgroup exits before its first barrier.
+// [lo[e], lo[e+1]) and multiplies them by its own B, and the grid enumerates the tiles of every
+// group in order.  lo (the caller's offsets clamped into [0, M] and made non-decreasing) and the
+// groups' first tiles come from gemm_group_scan; a workgroup finds its group by binary search.
+// Returns false for a workgroup past the last group's tiles (the grid is sized for the most
+// tiles any split of M can need); such a workgroup exits before its first barrier.
 template <int BM>
 __device__ __forceinline__ bool problem_view(const KParams& in, KParams& p, int& pid, int& nwg) {
   p = batch_view(in);
   pid = blockIdx.x;
   nwg = gridDim.x;
   if (!in.offsets) return true;
-  const int M = (int)in.M;
-  int64_t base = 0;
-  int lo = 0;
-  for (int e = 0; e < in.batch; ++e) {
-    lo = min(max(in.offsets[e], lo), M);
-    const int hi = min(max(in.offsets[e + 1], lo), M);
-    const int tm = (hi - lo + BM - 1) / BM;
-    const int64_t nt = (int64_t)tm * in.tiles_n;
-    if ((int64_t)blockIdx.x < base + nt) {
-      p.A = (const char*)in.A + lo * in.a_row_bytes;
-      p.B = (const char*)in.B + e * in.b_bstride;
-      if (in.has_c) {
-        p.C = (const char*)in.C + lo * in.c_row_bytes;
-        if (in.c_span > 0) p.c_span = in.c_span - lo * in.c_row_bytes;
-      }
-      p.D = (char*)in.D + lo * in.d_row_bytes;
-      if (in.has_row_scale) p.row_scale = in.row_scale + lo;
-      p.M = hi - lo;
-      p.tiles_m = tm;
-      pid = (int)((int64_t)blockIdx.x - base);
-      nwg = (int)nt;
-      return true;
-    }
-    base += nt;
+  const int64_t x = blockIdx.x;
+  const int G = in.batch;
+  if (x >= in.group_base[G]) return false;
+  int e = 0, hi_e = G;  // group_base[e] <= x < group_base[hi_e]
+  while (hi_e - e > 1) {
+    const int mid = (e + hi_e) >> 1;
+    if (in.group_base[mid] <= x) e = mid; else hi_e = mid;
   }
-  return false;
+  const int lo = in.group_lo[e], hi = in.group_lo[e + 1];
+  const int tm = (hi - lo + BM - 1) / BM;
+  p.A = (const char*)in.A + lo * in.a_row_bytes;
+  p.B = (const char*)in.B + e * in.b_bstride;
+  if (in.has_c) {
+    p.C = (const char*)in.C + lo * in.c_row_bytes;
+    if (in.c_span > 0) p.c_span = in.c_span - lo * in.c_row_bytes;
+  }
+  p.D = (char*)in.D + lo * in.d_row_bytes;
+  if (in.has_row_scale) p.row_scale = in.row_scale + lo;
+  p.M = hi - lo;
+  p.tiles_m = tm;
+  pid = (int)(x - in.group_base[e]);
+  nwg = tm * in.tiles_n;
+  return true;
 }
 
 // Epilogue of one output element (row, col) from its fp32 sum, for the kernels that finish

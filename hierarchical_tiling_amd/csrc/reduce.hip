@@ -48,4 +48,58 @@ hipError_t launch_row_sumsq_reduce(const float* ws, float* out, int64_t M, int t
   return hipGetLastError();
 }
 
+// Grouped tile table: two block-wide scans over the G + 1 offsets (a running maximum, then a
+// sum of tile counts), each thread taking a contiguous run of entries.
+__global__ __launch_bounds__(1024) void gemm_group_scan(const int32_t* off, int G, int M, int bm,
+                                                       int tiles_n, int32_t* lo, int64_t* base) {
+  __shared__ int smax[1024];
+  __shared__ int64_t ssum[1024];
+  const int t = threadIdx.x;
+  const int per = (G + 1 + 1023) / 1024;
+  const int b = min(t * per, G + 1), e = min(b + per, G + 1);
+  int m = 0;
+  for (int i = b; i < e; ++i) m = max(m, off[i]);
+  smax[t] = m;
+  __syncthreads();
+  for (int d = 1; d < 1024; d <<= 1) {   // inclusive scan of the chunk maxima
+    const int v = t >= d ? smax[t - d] : 0;
+    __syncthreads();
+    smax[t] = max(smax[t], v);
+    __syncthreads();
+  }
+  int run = t > 0 ? smax[t - 1] : 0;      // running maximum before this chunk
+  int prev = min(run, M);                 // effective offset of the entry before this chunk
+  int64_t sum = 0;                        // tiles of the groups that end in this chunk
+  for (int i = b; i < e; ++i) {
+    run = max(run, off[i]);
+    const int eff = min(run, M);
+    lo[i] = eff;
+    if (i > 0) sum += (int64_t)((eff - prev + bm - 1) / bm) * tiles_n;
+    prev = eff;
+  }
+  ssum[t] = sum;
+  __syncthreads();
+  for (int d = 1; d < 1024; d <<= 1) {   // inclusive scan of the chunk sums
+    const int64_t v = t >= d ? ssum[t - d] : 0;
+    __syncthreads();
+    ssum[t] += v;
+    __syncthreads();
+  }
+  int64_t acc = t > 0 ? ssum[t - 1] : 0;
+  prev = b > 0 ? min(smax[t > 0 ? t - 1 : 0], M) : 0;
+  for (int i = b; i < e; ++i) {
+    const int eff = lo[i];
+    if (i > 0) acc += (int64_t)((eff - prev + bm - 1) / bm) * tiles_n;
+    base[i] = acc;
+    prev = eff;
+  }
+}
+
+hipError_t launch_group_scan(const int32_t* offsets, int G, int64_t M, int bm, int tiles_n,
+                             int32_t* lo, int64_t* base, hipStream_t s) {
+  hipLaunchKernelGGL(gemm_group_scan, dim3(1), dim3(1024), 0, s, offsets, G, (int)M, bm, tiles_n,
+                     lo, base);
+  return hipGetLastError();
+}
+
 }  // namespace htk

@@ -184,9 +184,10 @@ def gemm_run_ex(h, A, B, C, D, bias, row_scale, col_scale, alpha, beta, scale_a=
 
 
 def gemm_run_grouped(h, A, B, C, D, bias, row_scale, col_scale, offsets, alpha, beta,
-                     scale_a=1.0, scale_b=1.0, stream=None):
-    """Grouped ragged-M run: `offsets` is the device address of batch + 1 int32 row offsets."""
-    a = gemm_args(A, B, C, D, bias, row_scale, col_scale, alpha, beta, scale_a, scale_b, None)
+                     scale_a=1.0, scale_b=1.0, stream=None, workspace=None):
+    """Grouped ragged-M run: `offsets` is the device address of batch + 1 int32 row offsets;
+    `workspace` the device address of gemm_workspace_size bytes (the groups' tile table)."""
+    a = gemm_args(A, B, C, D, bias, row_scale, col_scale, alpha, beta, scale_a, scale_b, workspace)
     _check(lib().gemm_run_grouped(h, ctypes.byref(a), offsets, stream), "gemm_run_grouped")
 
 

@@ -7,8 +7,8 @@ same input (the GPU library and the CPU oracle) receives the bits produced here.
 Recipe (the pages measure on no dataset; every input is synthetic):
 * values are drawn in float64 from numpy's PCG64 generator seeded with the given seed, in
   logical row-major order, so the same seed gives the same logical matrix in any storage order;
-* they are rounded to float32, then to the operand type with round-to-nearest-even by torch's CPU
-  cast (float8 is OCP e4m3 "fn");
+* they are rounded once from float64 to the operand type, to nearest with ties to even (float8 is
+  OCP e4m3 "fn", saturating at +-448);
 * storage is a flat array; element (r, c) sits at r * strides[0] + c * strides[1].
 """
 from __future__ import annotations
@@ -39,9 +39,34 @@ def draw(seed: int, count: int, dist: str = "normal", *, std: float = 1.0, lo: f
     raise ValueError(f"unknown distribution {dist!r}")
 
 
+# (stored mantissa bits, smallest normal exponent, largest finite value) of the narrow types
+_FORMAT = {"bf16": (7, -126, (2.0 - 2.0 ** -7) * 2.0 ** 127), "e4m3": (3, -6, 448.0)}
+
+
 def quantize(values: np.ndarray, dtype: str) -> np.ndarray:
-    """Round float64 values to `dtype`; returns the stored bits as a numpy array."""
-    t = torch.from_numpy(np.ascontiguousarray(values, dtype=np.float64).astype(np.float32))
+    """Round float64 values once to `dtype`, to nearest with ties to even; returns the stored
+    bits.  f32 and f16 use numpy's direct conversions from double.  bf16 and e4m3 round at the
+    value's quantum 2^(max(e, emin) - mbits) (e its binary exponent) with numpy's rint, which ties
+    to even; the result is then exact in float32 and in the type, so the final casts are exact.
+    bf16 overflows to infinity; e4m3 ("fn", no infinities) saturates to +-448."""
+    v = np.ascontiguousarray(values, dtype=np.float64)
+    if dtype == "f32":
+        return v.astype(np.float32).view(np.uint32).copy()
+    if dtype == "f16":
+        with np.errstate(over="ignore"):           # beyond 65504: infinity, as IEEE rounding gives
+            return v.astype(np.float16).view(np.uint16).copy()
+    mbits, emin, vmax = _FORMAT[dtype]
+    with np.errstate(over="ignore", invalid="ignore"):
+        _, ex = np.frexp(v)                        # v = f * 2^ex, 0.5 <= |f| < 1
+        e = np.maximum(ex - 1, emin)
+        q = np.ldexp(1.0, e - mbits)               # the quantum at v's exponent
+        r = np.rint(v / q) * q                     # exact scalings; rint ties to even
+        if dtype == "bf16":
+            r = np.where(np.abs(r) > vmax, np.copysign(np.inf, v), r)
+        else:
+            r = np.clip(r, -vmax, vmax)
+        r = np.where(np.isnan(v), np.nan, r)
+    t = torch.from_numpy(r.astype(np.float32))     # exact: r has at most mbits + 1 bits
     bits = t.to(_TORCH[dtype]).view(_TORCH_BITS[dtype]).numpy()
     return bits.view(STORAGE[dtype]).copy()
 

@@ -220,10 +220,13 @@ int gemm_run_ex(gemm_t h, const gemm_args* args, void* stream);
  * B_e = B + e * b_stride_l, with shared N, K, bias, col_scale, alpha and beta.  `offsets` is a
  * device array of G + 1 int32 values, 4-byte aligned, non-decreasing from 0 to M; it is read
  * on the device, so routing decided on the GPU needs no host round trip.  Out-of-range or
- * decreasing offsets are clamped into [0, M] and made non-decreasing, so they cannot send the
- * kernel outside the operands, but the rows they drop are not written.  The other pointers and
- * scalars are those of gemm_run_ex.  gemm_run and gemm_run_ex refuse a ragged handle, and this
- * entry point refuses any other (GEMM_ERR_INVALID_ARG). */
+ * decreasing offsets are clamped into [0, M] and made non-decreasing (offset e becomes
+ * min(M, max(0, offsets[0..e]))), so they cannot send the kernel outside the operands, but the
+ * rows they drop are not written.  args->workspace must hold gemm_workspace_size bytes: a first
+ * kernel on `stream` writes there each group's clamped rows and first tile (a prefix over the
+ * groups), and each workgroup of the product finds its group by binary search.  The other
+ * pointers and scalars are those of gemm_run_ex.  gemm_run and gemm_run_ex refuse a ragged
+ * handle, and this entry point refuses any other (GEMM_ERR_INVALID_ARG). */
 int gemm_run_grouped(gemm_t h, const gemm_args* args, const int32_t* offsets, void* stream);
 
 /* For callers that cannot allocate device memory (code under HIP graph capture, tight serving

@@ -223,16 +223,31 @@ GROUP_CASES = {
                            scale_b=0.25),
     "f32_moe_c": dict(sizes=[33, 31], N=40, K=50, dtype="f32", dist="uniform", has_c=True,
                       beta=-1.0, alpha=2.0),
+    # 3000 groups of 0..7 rows: several offsets per thread of the scan that builds the tile table
+    "bf16_3000_groups": dict(sizes=[int(v) for v in np.random.default_rng(5).integers(0, 8, 3000)],
+                             N=64, K=64, dtype="bf16", bias=True),
+    # offsets out of range and decreasing: clamped into [0, M] and made non-decreasing, so the
+    # groups are rows [0, 50), [50, 50), [50, 180), [180, 180), [180, 180); no row is left out
+    "bf16_clamped_offsets": dict(raw_offsets=[-5, 50, 30, 200, 150, 400], M=180, N=72, K=64,
+                                 dtype="bf16"),
 }
 
 
 @pytest.mark.parametrize("name", list(GROUP_CASES))
 def test_grouped_ragged_m_matches_oracle_per_group(name):
     kw = dict(GROUP_CASES[name])
-    sizes = kw.pop("sizes")
+    if "raw_offsets" in kw:
+        offsets = np.array(kw.pop("raw_offsets"), dtype=np.int32)
+        M = kw.pop("M")
+        G = offsets.size - 1
+    else:
+        sizes = kw.pop("sizes")
+        G, M = len(sizes), int(sum(sizes))
+        offsets = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    # the offsets as the library reads them: clamped into [0, M], made non-decreasing
+    eff = np.minimum(np.maximum.accumulate(np.maximum(offsets, 0)), M)
     force = kw.pop("force", None)
     b_order = kw.pop("b_order", "col")
-    G, M = len(sizes), int(sum(sizes))
     seed = 200 + list(GROUP_CASES).index(name) * 10
     p = Prepared(Case(M=M, seed=seed, b_order=b_order, **kw))   # A, C, D, bias, scale vectors
     c = p.case
@@ -241,7 +256,6 @@ def test_grouped_ragged_m_matches_oracle_per_group(name):
     Bs = [inputs.matrix(seed + 5 + e, c.K, c.N, c.dtype, c.dist, order=b_order, **bkw)
           for e in range(G)]
     b_flat, sb = _stack(Bs, 0, 16)
-    offsets = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
     ot = OUT_T[c.dtype]
     tail = 37                                                     # sentinel after D
     d_rows = M * p.d_strides[0]
@@ -259,33 +273,44 @@ def test_grouped_ragged_m_matches_oracle_per_group(name):
     assert b"skinny" not in info.name and info.split_k == 1
     assert info.grid == (-(-M // info.bm) + G) * -(-c.N // info.bn)
     a_ptr = p.dA[0].data_ptr()
+    # the groups' tile table lives in the workspace, which starts as garbage
+    assert g.workspace_bytes >= (G + 1) * 12
+    ws = torch.full((g.workspace_bytes // 4,), -1, dtype=torch.int32, device="cuda")
     H.gemm_run_grouped(g.handle, a_ptr, dB.data_ptr(), p.dC.data_ptr() if p.dC is not None else None,
                        dD.data_ptr(), p.dbias.data_ptr() if p.dbias is not None else None,
                        p.drs.data_ptr() if p.drs is not None else None,
                        p.dcs.data_ptr() if p.dcs is not None else None, doff.data_ptr(),
                        c.alpha, c.beta, c.scale_a, c.scale_b,
-                       torch.cuda.current_stream().cuda_stream)
+                       torch.cuda.current_stream().cuda_stream, ws.data_ptr())
     torch.cuda.synchronize()
     d_all = dD.cpu().numpy().view(inputs.STORAGE[ot])
     assert (d_all[d_rows:] == sentinel).all(), "a group wrote past D"
     vals = oracle.decode(ot, d_all[:d_rows])
     ld_a, ld_d = p.A.strides[0], p.d_strides[0]
+    covered = np.zeros(M, dtype=bool)
     for e in range(G):
-        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        lo, hi = int(eff[e]), int(eff[e + 1])
         if hi == lo:
             continue
+        covered[lo:hi] = True
         A_e = oracle.Operand(p.A.storage[lo * ld_a:], c.dtype, (hi - lo, c.K), p.A.strides)
         C_e = (oracle.Operand(p.C.storage[lo * p.C.strides[0]:], ot, (hi - lo, c.N), p.C.strides)
                if p.C is not None else None)
         want = oracle.gemm(A_e, op(Bs[e]), C_e, op(p.bias) if p.bias is not None else None,
                            alpha=c.alpha, beta=c.beta, scale_a=c.scale_a, scale_b=c.scale_b,
                            act=c.act, row_scale=p.rs[lo:hi] if p.rs is not None else None,
-                           col_scale=p.cs)
+                           col_scale=p.cs, threads=1)
         r = np.arange(lo, hi)[:, None] * ld_d + np.arange(c.N)[None, :] * p.d_strides[1]
         got = vals[r]
         err = error(c.dtype, got, want)
-        print(f"{name}[{e}] rows {lo}:{hi}: {info.name.decode()} err={err:.3e}")
-        assert err <= TOL[c.dtype], (name, e, err)
+        if G <= 16:
+            print(f"{name}[{e}] rows {lo}:{hi}: {info.name.decode()} err={err:.3e}")
+        assert err <= TOL[c.dtype], (name, e, lo, hi, err)
+    # rows outside every group are not written
+    rows_out = np.flatnonzero(~covered)
+    if rows_out.size:
+        r = rows_out[:, None] * ld_d + np.arange(c.N)[None, :] * p.d_strides[1]
+        assert (d_all[r] == sentinel).all()
 
 
 # ---- fused reductions: row sums of squares (the next layer's norm) and column sums ------------
