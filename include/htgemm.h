@@ -158,7 +158,8 @@ int gemm_create(const gemm_desc* desc, gemm_t* out);
  * elements (each rounded up to 256 bytes), Kp being K rounded up to 16 bytes' worth, and
  * gemm_run writes them with one copy kernel per operand on the stream before the product.  A split tail (the
  * Stream-K idea, same Part: the tiles of a last round that would leave most CUs idle are each
- * split along K) needs tail_split * tail_tiles * bm * bn * 4 (gemm_info).  With has_row_sumsq it
+ * split along K) needs tail_split * tail_tiles * bm * bn * 4 (gemm_info).  A grouped handle
+ * (ragged_m) needs (G + 1) * 4 bytes rounded up to 256, plus (G + 1) * 8.  With has_row_sumsq it
  * is the number of N tiles * M * 4, and has_col_sum adds (M tiles * row groups) * N * 4.  The caller owns the
  * workspace; its contents after a run are unspecified, and two runs in flight at once need two
  * workspaces. */
