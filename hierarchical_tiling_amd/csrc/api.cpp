@@ -202,6 +202,28 @@ int choose(const gemm_handle_s& h, bool vec_a, bool vec_b, bool want_vec, int sp
   int64_t best_area = -1;
   int best_small = -1, best_small_rank = 0;
   int64_t best_small_wg = -1, best_small_area = -1;
+  // a batch runs every problem's tiles in one launch (a grouped launch's M already spans all of
+  // its groups)
+  const int64_t problems = h.d.batch > 1 && !h.d.ragged_m ? h.d.batch : 1;
+  auto fills = [&](const KernelEntry& e, int64_t wg) {
+    const int64_t area = int64_t(e.bm) * e.bn;
+    return wg >= 256 || (wg > 128 && (one_per_cu(e) || (e.realign && area >= 128 * 128)));
+  };
+  // Does an entry with a tile of at least 128 x 128 fill the GPU without splitting K?  Then a
+  // split whose slices keep fewer than 24 k-tiles does not count as filling it: each slice pays
+  // the pipeline fill, an fp32 partial plane and its share of the sum kernel.  Measured on
+  // MI355X, bf16 2048^2 x 4096: ring x 4 slices of 16 k-tiles 0.055 ms, unsplit 128 x 128
+  // (256 tiles) 0.048 ms (another box: 57.1 vs 55.6-57.3 us, a tie).  With fewer tiles no such
+  // entry fills the GPU and the split stays (1536^2 x 8192: ring x 7 slices of 19 k-tiles
+  // 62-67 us, 128 x 128 tiles 88-94 us).
+  bool unsplit_fills = false;
+  for (int i = 0; i < table_size() && split_req == 0; ++i) {
+    const KernelEntry& e = t[i];
+    if ((e.vec != 0) != want_vec || e.skinny || int64_t(e.bm) * e.bn < 128 * 128 ||
+        !entry_fits(e, h, vec_a, vec_b))
+      continue;
+    if (fills(e, cdiv(h.d.M, e.bm) * cdiv(h.d.N, e.bn) * problems)) unsplit_fills = true;
+  }
   for (int i = 0; i < table_size(); ++i) {
     const KernelEntry& e = t[i];
     if ((e.vec != 0) != want_vec || e.skinny) continue;
@@ -210,12 +232,10 @@ int choose(const gemm_handle_s& h, bool vec_a, bool vec_b, bool want_vec, int sp
     int slices;
     int64_t kps;
     plan_split(e, h.d, split_req, &slices, &kps);
-    // a batch runs every problem's tiles in one launch (a grouped launch's M already spans
-    // all of its groups)
-    const int64_t problems = h.d.batch > 1 && !h.d.ragged_m ? h.d.batch : 1;
     const int64_t wg = cdiv(h.d.M, e.bm) * cdiv(h.d.N, e.bn) * slices * problems;
     const int64_t area = int64_t(e.bm) * e.bn;
     const int rank = wg <= 256 ? e.rank_one_round : e.rank;
+    const bool shallow_split = unsplit_fills && slices > 1 && kps / e.bk < 24;
     // An entry fills the GPU with 256 workgroups or more.  A kernel that runs one per CU, or a
     // 128 x 128 tile with the realigned loaders (whose smaller tile is much less efficient),
     // also fills it with more than 128: a tile of half the area then needs two per CU somewhere
@@ -225,8 +245,8 @@ int choose(const gemm_handle_s& h, bool vec_a, bool vec_b, bool want_vec, int sp
     // realigned (204 workgroups) 47 us vs 64x64 (792) 65 us.  With exactly 128 ring tiles
     // (2048 x 4096 x 2048) the 256x128 kernel is faster; for the 16-byte loaders 64x64 tiles
     // were as fast or faster than 144-192 workgroups of 128x128 (f32 1536^3 111 vs 134 us).
-    const bool fills = wg >= 256 || (wg > 128 && (one_per_cu(e) || (e.realign && area >= 128 * 128)));
-    if (fills && (area > best_area || (area == best_area && rank > best_rank))) {
+    const bool fill = fills(e, wg) && !shallow_split;
+    if (fill && (area > best_area || (area == best_area && rank > best_rank))) {
       best = i;
       best_area = area;
       best_rank = rank;

@@ -357,7 +357,9 @@ def test_col_sum_fields(fake_gfx950):
     ((3328, 3328, 4096), "m16_ring", 1, (0, 1)),       # 169: no split, 2 slices would be 338
     ((2816, 2816, 4096), "m16_ring", 2, (0, 1)),       # 121 tiles x 2 = 242
     ((1536, 1536, 8192), "m16_ring", 7, (0, 1)),       # 36 x 7 = 252; 8 would start a round
-    ((2048, 2048, 4096), "m16_ring", 4, (0, 1)),
+    # 4 ring slices would keep 16 k-tiles each while 128 x 128 tiles fill the GPU unsplit:
+    # 0.048 against 0.055 ms on one MI355X, a tie on another
+    ((2048, 2048, 4096), "128x128x64", 1, (0, 1)),
     ((2048, 4096, 2048), "256x128x32", 1, (0, 1)),     # exactly 128 ring tiles: half-size tile
     ((2048, 2048, 2048), "128x128x64", 1, (0, 1)),
     ((512, 512, 16384), "128x128x64", 16, (0, 1)),
@@ -420,3 +422,11 @@ def test_noalloc_scratch_limit_and_arguments(fake_gfx950):
         H.gemm_destroy(big)
     assert H.lib().gemm_run_noalloc(None, None, None) == 7   # GEMM_ERR_BAD_HANDLE
     assert H.gemm_status_string(H.GEMM_ERR_SCRATCH_LIMIT).startswith("the problem needs more")
+
+
+def test_kernel_choice_for_the_misjudged_fp8_product(fake_gfx950):
+    """e4m3 3001 x 2999 x 2049 with odd leading dimensions: element-wise loads took 533 us
+    (64 x 64) and 628 us (128 x 128) on MI355X; the library now copies A and B to aligned K-major
+    buffers and runs the split ring on them (81 us)."""
+    info = _info(H.make_desc(3001, 2999, 2049, "e4m3", (2049, 1), (1, 2049), (2999, 1)))
+    assert info.repack == 1 and info.name == b"e4m3_ak_bk_256x256x128_w2x4_m32_ring"
