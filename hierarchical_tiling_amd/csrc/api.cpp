@@ -88,7 +88,7 @@ bool entry_fits(const KernelEntry& e, const gemm_handle_s& h, bool vec_a, bool v
   if ((e.a_kmajor != 0) != h.a.kmajor || (e.b_kmajor != 0) != h.b.kmajor) return false;
   if (e.vec && !(vec_a && vec_b)) return false;
   if (e.skinny && d.M > e.bm) return false;  // the streaming kernel holds all M rows in one tile
-  if (e.skinny && d.ragged_m) return false;  // grouped launches use the tile kernels only
+  if (e.skinny && (d.ragged_m || d.grouped)) return false;  // grouped launches use tile kernels
   // the row reduction reads the output tile repacked in LDS: tile kernels whose LDS holds it
   if ((d.has_row_sumsq || d.has_col_sum) &&
       (e.skinny || int64_t(e.bm) * e.bn * dtype_size(d.d_type) > e.lds_bytes))
@@ -195,7 +195,7 @@ void plan_tail(const KernelEntry& e, const gemm_desc& d, int split_req, int spli
 int choose(const gemm_handle_s& h, bool vec_a, bool vec_b, bool want_vec, int split_req) {
   const KernelEntry* t = table();
   const bool need_split = split_req > 1;
-  for (int i = 0; i < table_size() && !need_split && !h.d.ragged_m && !h.d.has_row_sumsq &&
+  for (int i = 0; i < table_size() && !need_split && !h.d.ragged_m && !h.d.grouped && !h.d.has_row_sumsq &&
                   !h.d.has_col_sum; ++i)
     if (t[i].skinny && (t[i].vec != 0) == want_vec && entry_fits(t[i], h, vec_a, vec_b)) return i;
   int best = -1, best_rank = 0;
@@ -386,7 +386,7 @@ bool entry_maps_ok(const KernelEntry& e) {
 // only have element-wise loaders for such operands, from 2^31.  Batches and groups keep the
 // direct path.
 bool repack_pays(const gemm_desc& d, bool vec_both) {
-  if (vec_both || d.ragged_m || d.batch > 1) return false;
+  if (vec_both || d.ragged_m || d.grouped || d.batch > 1) return false;
   if (d.M < 128 || d.N < 128 || d.K < 64) return false;
   const double flop = 2.0 * (double)d.M * (double)d.N * (double)d.K;
   return flop >= (dtype_size(d.a_type) == 2 ? 34359738368.0 : 2147483648.0);
@@ -423,6 +423,7 @@ int gemm_create(const gemm_desc* desc, gemm_t* out) {
   if (d.batch < 0 || d.batch > 65535) return GEMM_ERR_INVALID_ARG;
   const int64_t L = d.batch > 1 ? d.batch : 1;
   if (d.ragged_m != 0 && d.ragged_m != 1) return GEMM_ERR_INVALID_ARG;
+  if (d.grouped != 0 && d.grouped != 1) return GEMM_ERR_INVALID_ARG;
   if (d.has_row_sumsq != 0 && d.has_row_sumsq != 1) return GEMM_ERR_INVALID_ARG;
   if (d.has_col_sum != 0 && d.has_col_sum != 1) return GEMM_ERR_INVALID_ARG;
   // the reductions cover one problem and are not split along K
@@ -434,7 +435,16 @@ int gemm_create(const gemm_desc* desc, gemm_t* out) {
     // batch field is the group count G (offsets holds G + 1 values), so it must be at least 1.
     if (d.batch < 1) return GEMM_ERR_INVALID_ARG;
     if (d.b_stride_l < 0) return GEMM_ERR_LAYOUT;
-    if (d.split_k > 1) return GEMM_ERR_INVALID_ARG;
+    if (d.split_k > 1 || d.grouped) return GEMM_ERR_INVALID_ARG;
+  } else if (d.grouped) {
+    // independent problems: shapes, pointers and leading dimensions come with each run; the
+    // descriptor fixes types, layouts and epilogue.  One launch, no split, no per-row or
+    // per-column vectors (their lengths would differ per problem).
+    if (d.batch < 1 || d.split_k > 1) return GEMM_ERR_INVALID_ARG;
+    if (d.has_row_scale || d.has_col_scale || d.has_row_sumsq || d.has_col_sum)
+      return GEMM_ERR_INVALID_ARG;
+    if (d.d_stride_n != 1 && d.d_stride_m != 1) return GEMM_ERR_LAYOUT;
+    if (d.has_c && d.c_stride_n != 1 && d.c_stride_m != 1) return GEMM_ERR_LAYOUT;
   } else if (L > 1) {
     if (d.a_stride_l < 0 || d.b_stride_l < 0 || d.c_stride_l < 0 || d.d_stride_l < 0)
       return GEMM_ERR_LAYOUT;
@@ -463,11 +473,13 @@ int gemm_create(const gemm_desc* desc, gemm_t* out) {
   // the 16-byte loaders need every problem's operand base 16-byte aligned
   const int64_t isz = dtype_size(d.a_type);
   const bool va = vec_ok(h.a, d.M, d.K, d.a_type) &&
-                  (L == 1 || d.ragged_m || (d.a_stride_l * isz) % 16 == 0);
-  const bool vb = vec_ok(h.b, d.N, d.K, d.b_type) && (L == 1 || (d.b_stride_l * isz) % 16 == 0);
+                  (L == 1 || d.ragged_m || d.grouped || (d.a_stride_l * isz) % 16 == 0);
+  const bool vb = vec_ok(h.b, d.N, d.K, d.b_type) &&
+                  (L == 1 || d.grouped || (d.b_stride_l * isz) % 16 == 0);
   const bool need_split = d.split_k > 1;
   // no split of a batch, a group or a product with a row reduction
-  const int split_req = L > 1 || d.ragged_m || d.has_row_sumsq || d.has_col_sum ? 1 : d.split_k;
+  const int split_req = L > 1 || d.ragged_m || d.grouped || d.has_row_sumsq || d.has_col_sum
+                            ? 1 : d.split_k;
   h.fallback = choose(h, va, vb, false, split_req);
   if (h.fallback < 0) return GEMM_ERR_NO_CONFIG;
   if (d.force_config < 0 && repack_pays(d, va && vb)) {
@@ -549,7 +561,12 @@ namespace {
 size_t inner_workspace(const gemm_handle_s& h);
 // grouped launches: G + 1 effective offsets (int32, padded to 256 bytes), then G + 1 first tiles
 size_t group_lo_bytes(int64_t G) { return ((size_t)(G + 1) * 4 + 255) / 256 * 256; }
+// independent problems: the problem table (padded to 256 bytes), then their G + 1 first tiles
+size_t problem_table_bytes(int64_t G) {
+  return ((size_t)G * sizeof(GroupProblem) + 255) / 256 * 256;
+}
 size_t group_table_bytes(const gemm_handle_s& h) {
+  if (h.d.grouped) return problem_table_bytes(h.d.batch) + (size_t)(h.d.batch + 1) * 8;
   return h.d.ragged_m ? group_lo_bytes(h.d.batch) + (size_t)(h.d.batch + 1) * 8 : 0;
 }
 }  // namespace
@@ -618,6 +635,7 @@ int run_impl(gemm_t h, const void* A, const void* B, const void* C, void* D, con
              float scale_a, float scale_b, void* workspace, const int32_t* offsets,
              float* row_sumsq, float* col_sum, void* stream) {
   const gemm_desc& d = h->d;
+  if (d.grouped) return GEMM_ERR_INVALID_ARG;  // independent problems run through gemm_run_problems
   if ((d.has_row_sumsq != 0) != (row_sumsq != nullptr)) return GEMM_ERR_INVALID_ARG;
   if ((d.has_col_sum != 0) != (col_sum != nullptr)) return GEMM_ERR_INVALID_ARG;
   if ((row_sumsq && !aligned(row_sumsq, 4)) || (col_sum && !aligned(col_sum, 4)))
@@ -800,6 +818,117 @@ int gemm_run_grouped(gemm_t h, const gemm_args* a, const int32_t* offsets, void*
   return run_impl(h, a->A, a->B, a->C, a->D, a->bias, a->row_scale, a->col_scale, a->alpha,
                   a->beta, a->scale_a, a->scale_b, a->workspace, offsets, a->row_sumsq, a->col_sum,
                   stream);
+}
+
+int gemm_run_problems(gemm_t h, const gemm_problem* probs, int64_t count, const gemm_args* a,
+                      void* stream) {
+  if (!h || h->magic != kMagic) return GEMM_ERR_BAD_HANDLE;
+  const gemm_desc& d = h->d;
+  if (!d.grouped || !a) return GEMM_ERR_INVALID_ARG;
+  if (count < 0 || count > d.batch || (count > 0 && !probs)) return GEMM_ERR_INVALID_ARG;
+  // the per-problem pointers come with the problems; per-row and per-column vectors are refused
+  if (a->A || a->B || a->C || a->D || a->bias || a->row_scale || a->col_scale || a->row_sumsq ||
+      a->col_sum)
+    return GEMM_ERR_INVALID_ARG;
+  if (!d.has_c && a->beta != 0.0f) return GEMM_ERR_INVALID_ARG;
+  const bool read_c = d.has_c && a->beta != 0.0f;
+  const size_t in_sz = dtype_size(d.a_type), out_sz = dtype_size(d.d_type);
+  const KernelEntry& vec_e = table()[h->cfg];
+  const KernelEntry& fb_e = table()[h->fallback];
+  // Is problem q within the reach of entry e (the 31-bit tile offsets of its loaders)?
+  auto fits = [&](const KernelEntry& e, const gemm_problem& q) {
+    gemm_handle_s t = *h;
+    t.d.M = q.M;
+    t.d.N = q.N;
+    t.d.K = q.K;
+    t.a.ld = q.lda;
+    t.b.ld = q.ldb;
+    return entry_fits(e, t, true, true);
+  };
+  // arguments of every problem first: an error launches nothing
+  bool use_vec = vec_e.vec != 0;
+  for (int64_t i = 0; i < count; ++i) {
+    const gemm_problem& q = probs[i];
+    if (q.M < 0 || q.N < 0 || q.K < 0) return GEMM_ERR_INVALID_ARG;
+    if (q.M > INT32_MAX / 2 || q.N > INT32_MAX / 2 || q.K > INT32_MAX / 2) return GEMM_ERR_INVALID_ARG;
+    if (q.lda < 0 || q.ldb < 0 || q.ldc < 0 || q.ldd < 0) return GEMM_ERR_LAYOUT;
+    if (q.M == 0 || q.N == 0) continue;
+    if (!q.D || (q.K > 0 && (!q.A || !q.B)) || (read_c && !q.C) || (d.has_bias && !q.bias))
+      return GEMM_ERR_INVALID_ARG;
+    if (!aligned(q.A, in_sz) || !aligned(q.B, in_sz) || !aligned(q.D, out_sz) ||
+        (read_c && !aligned(q.C, out_sz)) || (d.has_bias && !aligned(q.bias, out_sz)))
+      return GEMM_ERR_MISALIGNED;
+    if (use_vec)
+      use_vec = vec_ok(Operand{h->a.kmajor, q.lda}, q.M, q.K, d.a_type) &&
+                vec_ok(Operand{h->b.kmajor, q.ldb}, q.N, q.K, d.b_type) && aligned(q.A, 16) &&
+                aligned(q.B, 16) && fits(vec_e, q);
+  }
+  const KernelEntry& e = use_vec ? vec_e : fb_e;
+  if (!use_vec)
+    for (int64_t i = 0; i < count; ++i)
+      if (probs[i].M > 0 && probs[i].N > 0 && !fits(fb_e, probs[i])) return GEMM_ERR_NO_CONFIG;
+  // the problem table and the problems' first tiles, built here and copied into the workspace
+  const size_t rec_bytes = problem_table_bytes(count);
+  const size_t bytes = rec_bytes + (size_t)(count + 1) * 8;
+  std::vector<uint64_t> host((bytes + 7) / 8, 0);
+  GroupProblem* rec = reinterpret_cast<GroupProblem*>(host.data());
+  int64_t* base = reinterpret_cast<int64_t*>(reinterpret_cast<char*>(host.data()) + rec_bytes);
+  int64_t total = 0;
+  for (int64_t i = 0; i < count; ++i) {
+    const gemm_problem& q = probs[i];
+    GroupProblem& r = rec[i];
+    r.A = q.A;
+    r.B = q.B;
+    r.C = read_c ? q.C : nullptr;
+    r.D = q.D;
+    r.bias = d.has_bias ? q.bias : nullptr;
+    r.M = q.M;
+    r.N = q.N;
+    r.K = q.K;
+    r.lda = q.lda;
+    r.ldb = q.ldb;
+    r.ldc = q.ldc;
+    r.ldd = q.ldd;
+    const bool empty = q.M == 0 || q.N == 0;
+    r.tiles_m = empty ? 0 : (int32_t)cdiv(q.M, e.bm);
+    r.tiles_n = empty ? 0 : (int32_t)cdiv(q.N, e.bn);
+    if (read_c && !empty) {
+      const int64_t csm = d.c_stride_n == 1 ? q.ldc : d.c_stride_m;
+      const int64_t csn = d.c_stride_n == 1 ? 1 : q.ldc;
+      const int64_t span = ((q.M - 1) * csm + (q.N - 1) * csn + 1) * (int64_t)out_sz;
+      r.c_span = span < (int64_t(1) << 31) - 64 ? span : 0;
+    }
+    base[i] = total;
+    total += int64_t(r.tiles_m) * r.tiles_n;
+  }
+  base[count] = total;
+  if (total > INT32_MAX) return GEMM_ERR_INVALID_ARG;
+  if (total == 0) return GEMM_OK;
+  void* ws = a->workspace;
+  if (!ws || !aligned(ws, 16)) return GEMM_ERR_INVALID_ARG;
+  if (hipMemcpyAsync(ws, host.data(), bytes, hipMemcpyHostToDevice, (hipStream_t)stream) != hipSuccess)
+    return GEMM_ERR_HIP;
+
+  KParams p;
+  std::memset(&p, 0, sizeof(p));
+  p.c_sm = d.c_stride_m;
+  p.c_sn = d.has_c ? (d.c_stride_n == 1 ? 1 : d.c_stride_n) : 1;
+  p.d_sm = d.d_stride_m;
+  p.d_sn = d.d_stride_n == 1 ? 1 : d.d_stride_n;
+  p.alpha = a->alpha * a->scale_a * a->scale_b;
+  p.beta = a->beta;
+  p.has_c = read_c ? 1 : 0;
+  p.has_bias = d.has_bias;
+  p.act = d.act;
+  p.tile_bm = e.bm;
+  p.tile_bn = e.bn;
+  p.group_m = h->group_m;
+  p.split_k = 1;
+  p.batch = (int)count;
+  p.problems = reinterpret_cast<const GroupProblem*>(ws);
+  p.group_base = reinterpret_cast<const int64_t*>(static_cast<char*>(ws) + rec_bytes);
+  const hipError_t err = e.launch(p, (hipStream_t)stream, dim3((unsigned)total, 1, 1));
+  return err == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
 }
 
 }  // extern "C"

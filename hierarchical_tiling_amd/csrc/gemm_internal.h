@@ -9,6 +9,22 @@ namespace htk {
 // Operand element types; the numbering matches gemm_dtype in htgemm.h.
 enum : int { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2, DT_F8 = 3 };
 
+// One problem of a grouped launch of independent problems, as the device reads it (the host
+// builds the table in the workspace).  lda / ldb are the non-unit strides of A and B; ldc / ldd
+// replace the stride of C / D that is not the unit one; c_span as in KParams.
+struct GroupProblem {
+  const void* A;
+  const void* B;
+  const void* C;
+  void* D;
+  const void* bias;
+  int64_t M, N, K;
+  int64_t lda, ldb, ldc, ldd;
+  int64_t c_span;
+  int32_t tiles_m, tiles_n;
+};
+static_assert(sizeof(GroupProblem) == 112, "the table entry size the header documents");
+
 // Arguments of one launch.  The operand of A or B with unit stride is implied by the kernel
 // variant; lda / ldb is the other stride.  alpha already includes scale_a * scale_b.
 struct KParams {
@@ -44,6 +60,9 @@ struct KParams {
   // workgroups); with tail_tiles > 0 its fp32 partials go to a compact workspace of
   // split_k x tail_tiles tiles of tile_bm x tile_bn (plane blockIdx.y, slot blockIdx.x).
   int tile_base, tail_tiles, tile_bm, tile_bn;
+  // Grouped launch of independent problems: `batch` entries, and their first tiles in
+  // group_base (batch + 1 values); nullptr otherwise.
+  const GroupProblem* problems;
 };
 
 typedef hipError_t (*launch_fn)(const KParams&, hipStream_t, dim3 grid);

@@ -315,7 +315,7 @@ __device__ __forceinline__ float activate(int act, float v) {
 // (shape, strides, alpha, beta, bias and the scale vectors) is shared.
 __device__ __forceinline__ KParams batch_view(const KParams& p) {
   KParams q = p;
-  if (p.batch > 1 && !p.offsets) {
+  if (p.batch > 1 && !p.offsets && !p.problems) {
     const int64_t z = blockIdx.z;
     q.A = (const char*)p.A + z * p.a_bstride;
     q.B = (const char*)p.B + z * p.b_bstride;
@@ -345,20 +345,53 @@ __device__ __forceinline__ KParams reload_args() {
 // groups' first tiles come from gemm_group_scan; a workgroup finds its group by binary search.
 // Returns false for a workgroup past the last group's tiles (the grid is sized for the most
 // tiles any split of M can need); such a workgroup exits before its first barrier.
+//
+// A grouped launch of independent problems ("CUTLASS", Part III: many problems of irregular
+// shapes in one launch) takes every operand, shape and leading dimension from the problem's
+// table entry; the strides' directions, the types and the epilogue stay those of the launch.
+__device__ __forceinline__ int find_group(const int64_t* base, int G, int64_t x) {
+  int e = 0, hi_e = G;  // base[e] <= x < base[hi_e]
+  while (hi_e - e > 1) {
+    const int mid = (e + hi_e) >> 1;
+    if (base[mid] <= x) e = mid; else hi_e = mid;
+  }
+  return e;
+}
 template <int BM>
 __device__ __forceinline__ bool problem_view(const KParams& in, KParams& p, int& pid, int& nwg) {
   p = batch_view(in);
   pid = blockIdx.x;
   nwg = gridDim.x;
+  if (in.problems) {
+    const int64_t x = blockIdx.x;
+    if (x >= in.group_base[in.batch]) return false;
+    const int e = find_group(in.group_base, in.batch, x);
+    const GroupProblem& q = in.problems[e];
+    p.A = q.A;
+    p.B = q.B;
+    p.C = in.has_c ? q.C : nullptr;
+    p.D = q.D;
+    p.bias = q.bias;
+    p.M = q.M;
+    p.N = q.N;
+    p.K = q.K;
+    p.k_per_split = (int)q.K;
+    p.lda = q.lda;
+    p.ldb = q.ldb;
+    if (in.c_sn == 1) p.c_sm = q.ldc; else p.c_sn = q.ldc;
+    if (in.d_sn == 1) p.d_sm = q.ldd; else p.d_sn = q.ldd;
+    p.c_span = q.c_span;
+    p.tiles_m = q.tiles_m;
+    p.tiles_n = q.tiles_n;
+    pid = (int)(x - in.group_base[e]);
+    nwg = q.tiles_m * q.tiles_n;
+    return true;
+  }
   if (!in.offsets) return true;
   const int64_t x = blockIdx.x;
   const int G = in.batch;
   if (x >= in.group_base[G]) return false;
-  int e = 0, hi_e = G;  // group_base[e] <= x < group_base[hi_e]
-  while (hi_e - e > 1) {
-    const int mid = (e + hi_e) >> 1;
-    if (in.group_base[mid] <= x) e = mid; else hi_e = mid;
-  }
+  const int e = find_group(in.group_base, G, x);
   const int lo = in.group_lo[e], hi = in.group_lo[e + 1];
   const int tm = (hi - lo + BM - 1) / BM;
   p.A = (const char*)in.A + lo * in.a_row_bytes;

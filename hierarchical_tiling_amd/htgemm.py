@@ -55,7 +55,15 @@ class gemm_desc(ctypes.Structure):
                 ("a_stride_l", ctypes.c_int64), ("b_stride_l", ctypes.c_int64),
                 ("c_stride_l", ctypes.c_int64), ("d_stride_l", ctypes.c_int64),
                 ("ragged_m", ctypes.c_int32), ("has_row_sumsq", ctypes.c_int32),
-                ("has_col_sum", ctypes.c_int32)]
+                ("has_col_sum", ctypes.c_int32), ("grouped", ctypes.c_int32)]
+
+
+class gemm_problem(ctypes.Structure):
+    _fields_ = [("M", ctypes.c_int64), ("N", ctypes.c_int64), ("K", ctypes.c_int64),
+                ("A", ctypes.c_void_p), ("B", ctypes.c_void_p), ("C", ctypes.c_void_p),
+                ("D", ctypes.c_void_p), ("bias", ctypes.c_void_p),
+                ("lda", ctypes.c_int64), ("ldb", ctypes.c_int64), ("ldc", ctypes.c_int64),
+                ("ldd", ctypes.c_int64)]
 
 
 class gemm_args(ctypes.Structure):
@@ -106,6 +114,8 @@ def lib():
         "gemm_run_ex": ([vp, ctypes.POINTER(gemm_args), vp], i32),
         "gemm_run_grouped": ([vp, ctypes.POINTER(gemm_args), vp, vp], i32),
         "gemm_run_noalloc": ([vp, ctypes.POINTER(gemm_args), vp], i32),
+        "gemm_run_problems": ([vp, ctypes.POINTER(gemm_problem), i64, ctypes.POINTER(gemm_args), vp],
+                              i32),
         "gemm_destroy": ([vp], i32),
         "gemm_status_string": ([i32], cp),
         "gemm_get_info": ([vp, ctypes.POINTER(gemm_info)], i32),
@@ -137,7 +147,7 @@ def lib():
 
 
 EXPORTED = ["gemm_create", "gemm_workspace_size", "gemm_run", "gemm_run_ex", "gemm_run_grouped",
-            "gemm_run_noalloc",
+            "gemm_run_noalloc", "gemm_run_problems",
             "gemm_destroy",
             "gemm_status_string",
             "gemm_get_info", "gemm_num_configs", "gemm_config_name", "gemm_atom_layouts",
@@ -199,6 +209,24 @@ def gemm_run_noalloc(h, A, B, C, D, bias, row_scale, col_scale, alpha, beta, sca
     _check(lib().gemm_run_noalloc(h, ctypes.byref(a), stream), "gemm_run_noalloc")
 
 
+def gemm_run_problems(h, problems, alpha, beta, scale_a=1.0, scale_b=1.0, stream=None,
+                      workspace=None):
+    """Grouped run of independent problems: `problems` is a sequence of dicts (or gemm_problem)
+    with M, N, K, A, B, C, D, bias (device addresses or None) and lda, ldb, ldc, ldd."""
+    n = len(problems)
+    arr = (gemm_problem * max(n, 1))()
+    for i, q in enumerate(problems):
+        if isinstance(q, gemm_problem):
+            arr[i] = q
+        else:
+            arr[i] = gemm_problem(q["M"], q["N"], q["K"], q.get("A"), q.get("B"), q.get("C"),
+                                  q.get("D"), q.get("bias"), q.get("lda", 0), q.get("ldb", 0),
+                                  q.get("ldc", 0), q.get("ldd", 0))
+    a = gemm_args(None, None, None, None, None, None, None, alpha, beta, scale_a, scale_b,
+                  workspace, None, None)
+    _check(lib().gemm_run_problems(h, arr, n, ctypes.byref(a), stream), "gemm_run_problems")
+
+
 def gemm_destroy(h):
     _check(lib().gemm_destroy(h), "gemm_destroy")
 
@@ -240,7 +268,7 @@ def gemm_probe_atom(dtype: str, mi: int, out, stream=None):
 def make_desc(M, N, K, dtype, a_strides, b_strides, d_strides, c_strides=None, has_bias=False,
               act="none", force_config=-1, split_k=0, row_scale=False, col_scale=False, batch=1,
               batch_strides=(0, 0, 0, 0), ragged_m=False, row_sumsq=False,
-              col_sum=False) -> gemm_desc:
+              col_sum=False, grouped=False) -> gemm_desc:
     """a_strides = (stride_m, stride_k); b_strides = (stride_k, stride_n); c/d = (m, n);
     batch_strides = element offsets between consecutive problems of A, B, C, D."""
     out_t = "bf16" if dtype == "e4m3" else dtype
@@ -264,6 +292,7 @@ def make_desc(M, N, K, dtype, a_strides, b_strides, d_strides, c_strides=None, h
     d.ragged_m = 1 if ragged_m else 0
     d.has_row_sumsq = 1 if row_sumsq else 0
     d.has_col_sum = 1 if col_sum else 0
+    d.grouped = 1 if grouped else 0
     return d
 
 

@@ -33,6 +33,7 @@
  *   gemm_run            enqueues the kernel on the caller's HIP stream; asynchronous.
  *   gemm_run_ex         the same with the arguments in a struct, including the scale vectors.
  *   gemm_run_grouped    a grouped GEMM whose groups split M by device offsets.
+ *   gemm_run_problems   a grouped GEMM of independent problems of any shapes.
  *   gemm_destroy        frees the handle.
  *
  * Ownership: the caller owns every device buffer (A, B, C, D, bias, row_scale, col_scale,
@@ -138,6 +139,13 @@ typedef struct gemm_desc {
                               /* of the stored (rounded) D; one problem, no split (see gemm_args) */
   int32_t has_col_sum;        /* 1: gemm_run_ex also writes col_sum[n] = sum over m of D(m,n) of  */
                               /* the stored D; the same conditions                               */
+  int32_t grouped;            /* 1: grouped GEMM of independent problems, run by               */
+                              /* gemm_run_problems: up to `batch` (>= 1) problems per call, each */
+                              /* with its own M, N, K, pointers and leading dimensions; M, N, K  */
+                              /* above describe a typical problem (the kernel is chosen for      */
+                              /* `batch` problems of that shape) and the strides give each       */
+                              /* operand's unit-stride direction; ragged_m, split_k > 1, scale   */
+                              /* vectors and the reductions are refused                          */
 } gemm_desc;
 
 typedef struct gemm_handle_s* gemm_t;
@@ -159,7 +167,8 @@ int gemm_create(const gemm_desc* desc, gemm_t* out);
  * gemm_run writes them with one copy kernel per operand on the stream before the product.  A split tail (the
  * Stream-K idea, same Part: the tiles of a last round that would leave most CUs idle are each
  * split along K) needs tail_split * tail_tiles * bm * bn * 4 (gemm_info).  A grouped handle
- * (ragged_m) needs (G + 1) * 4 bytes rounded up to 256, plus (G + 1) * 8.  With has_row_sumsq it
+ * (ragged_m) needs (G + 1) * 4 bytes rounded up to 256, plus (G + 1) * 8; a handle of independent
+ * problems (grouped) needs 112 * batch bytes rounded up to 256, plus (batch + 1) * 8.  With has_row_sumsq it
  * is the number of N tiles * M * 4, and has_col_sum adds (M tiles * row groups) * N * 4.  The caller owns the
  * workspace; its contents after a run are unspecified, and two runs in flight at once need two
  * workspaces. */
@@ -229,6 +238,40 @@ int gemm_run_ex(gemm_t h, const gemm_args* args, void* stream);
  * pointers and scalars are those of gemm_run_ex.  gemm_run and gemm_run_ex refuse a ragged
  * handle, and this entry point refuses any other (GEMM_ERR_INVALID_ARG). */
 int gemm_run_grouped(gemm_t h, const gemm_args* args, const int32_t* offsets, void* stream);
+
+/* One problem of a grouped call (gemm_run_problems).  Shapes and pointers as in gemm_run; each
+ * leading dimension replaces the descriptor's stride along that operand's other direction
+ * (lda: a_stride_m for a K-major A, a_stride_k for an M-major one; ldb likewise; ldc and ldd:
+ * the row stride of a row-major C or D (descriptor stride along n == 1), else the column
+ * stride).  C is read only when beta != 0; bias (N values) only when the handle has has_bias. */
+typedef struct gemm_problem {
+  int64_t M, N, K;
+  const void* A;
+  const void* B;
+  const void* C;
+  void* D;
+  const void* bias;
+  int64_t lda, ldb, ldc, ldd;
+} gemm_problem;
+
+/* Grouped GEMM of independent problems ("CUTLASS", Part III: a grouped GEMM runs many problems
+ * of irregular shapes in one launch; "CUTLASS, CuTe, and CUDA Tile", "Assembling a CUTLASS
+ * kernel": the problem shape [M, N, K, L] with a problem per L index).  For a handle created
+ * with grouped == 1: problem i computes D_i = act(alpha*scale_a*scale_b*(A_i @ B_i) + beta*C_i
+ * + bias_i) for i < count (0 <= count <= the handle's batch), all with the handle's types,
+ * layouts and epilogue and the scalars of `args` (whose A, B, C, D, bias, scale-vector and
+ * reduction pointers must be NULL).  `problems` is a host array read during the call: it is
+ * checked, the tile count of every problem is taken, and a table of the problems and of their
+ * first tiles is copied into args->workspace (gemm_workspace_size bytes, 16-byte aligned) with
+ * hipMemcpyAsync on `stream` -- from pageable memory that copy completes before the call returns
+ * -- and one launch then runs the tiles of every problem, each workgroup finding its problem by
+ * binary search.  The 16-byte kernel runs when every problem's A and B meet its alignment,
+ * otherwise the narrow-load kernel runs them all.  Errors: those of gemm_run for any problem
+ * (the call launches nothing then), GEMM_ERR_INVALID_ARG for a handle that is not grouped or a
+ * count above its batch, GEMM_ERR_NO_CONFIG when a problem's operands exceed the chosen
+ * kernels' 31-bit tile offsets. */
+int gemm_run_problems(gemm_t h, const gemm_problem* problems, int64_t count, const gemm_args* args,
+                      void* stream);
 
 /* For callers that cannot allocate device memory (code under HIP graph capture, tight serving
  * loops, harnesses that forbid allocation): gemm_run_ex with the workspace taken from a static

@@ -296,6 +296,71 @@ def test_grouped_ragged_m_fields(fake_gfx950):
         H.gemm_destroy(h)
 
 
+def test_grouped_problems_fields(fake_gfx950):
+    """Grouped GEMM of independent problems ("CUTLASS", Part III: many problems of irregular
+    shapes in one launch): the descriptor fixes types, layouts and epilogue; the run's host
+    checks refuse bad problems before anything reaches the device."""
+    G = 5
+    base = dict(M=512, N=512, K=256, a_strides=(256, 1), b_strides=(1, 256), d_strides=(512, 1),
+                batch=G, grouped=True)
+    info = _info(desc(**base))
+    assert info.split_k == 1 and b"skinny" not in info.name
+    h = H.gemm_create(desc(**base))
+    try:
+        # the problem table (112 bytes a problem, padded to 256) and G + 1 first tiles
+        assert H.gemm_workspace_size(h) == (112 * G + 255) // 256 * 256 + (G + 1) * 8
+        lib = H.lib()
+        args = H.gemm_args(None, None, None, None, None, None, None, 1.0, 0.0, 1.0, 1.0, 4096)
+        good = dict(M=64, N=64, K=64, A=256, B=256, D=256, lda=64, ldb=64, ldd=64)
+
+        def rc(problems, a=args, count=None, handle=h):
+            arr = (H.gemm_problem * max(len(problems), 1))()
+            for i, q in enumerate(problems):
+                arr[i] = H.gemm_problem(q["M"], q["N"], q["K"], q.get("A"), q.get("B"),
+                                        q.get("C"), q.get("D"), q.get("bias"), q.get("lda", 0),
+                                        q.get("ldb", 0), q.get("ldc", 0), q.get("ldd", 0))
+            n = len(problems) if count is None else count
+            return lib.gemm_run_problems(handle, arr, n, ctypes.byref(a), None)
+
+        # nothing to do: no problems, or only empty ones (no device call is made)
+        assert rc([]) == 0
+        assert rc([dict(good, M=0), dict(good, N=0, D=None)]) == 0
+        assert rc([good] * (G + 1)) == H.GEMM_ERR_INVALID_ARG           # more than batch
+        assert rc([good], count=-1) == H.GEMM_ERR_INVALID_ARG
+        assert rc([dict(good, M=-1)]) == H.GEMM_ERR_INVALID_ARG
+        assert rc([dict(good, ldb=-64)]) == H.GEMM_ERR_LAYOUT
+        assert rc([dict(good, D=None)]) == H.GEMM_ERR_INVALID_ARG
+        assert rc([dict(good, A=None)]) == H.GEMM_ERR_INVALID_ARG
+        assert rc([good, dict(good, D=257)]) == H.GEMM_ERR_MISALIGNED   # odd address, 2-byte D
+        # per-operand pointers belong to the problems, not to the arguments
+        for field in ("A", "B", "D"):
+            bad = H.gemm_args(None, None, None, None, None, None, None, 1.0, 0.0, 1.0, 1.0, 4096)
+            setattr(bad, field, 256)
+            assert rc([good], a=bad) == H.GEMM_ERR_INVALID_ARG
+        beta = H.gemm_args(None, None, None, None, None, None, None, 1.0, 0.5, 1.0, 1.0, 4096)
+        assert rc([good], a=beta) == H.GEMM_ERR_INVALID_ARG             # beta without C
+        # the other entry points refuse a grouped handle, and this one any other handle
+        assert lib.gemm_run(h, 256, 256, None, 256, None, 1.0, 0.0, 1.0, 1.0, None, None) == 1
+        plain = H.gemm_create(desc())
+        try:
+            assert rc([good], handle=plain) == H.GEMM_ERR_INVALID_ARG
+        finally:
+            H.gemm_destroy(plain)
+    finally:
+        H.gemm_destroy(h)
+    for bad, status in ((dict(batch=0), H.GEMM_ERR_INVALID_ARG),
+                        (dict(split_k=2), H.GEMM_ERR_INVALID_ARG),
+                        (dict(ragged_m=True), H.GEMM_ERR_INVALID_ARG),
+                        (dict(row_scale=True), H.GEMM_ERR_INVALID_ARG),
+                        (dict(d_strides=(1024, 2)), H.GEMM_ERR_LAYOUT)):
+        assert status_of(desc(**dict(base, **bad))) == status, bad
+    d = desc(**base)
+    d.grouped = 3
+    assert status_of(d) == H.GEMM_ERR_INVALID_ARG
+    # a column-major D is accepted (ldd then replaces the column stride)
+    assert status_of(desc(**dict(base, d_strides=(1, 512)))) == 0
+
+
 def test_row_sumsq_fields(fake_gfx950):
     """The fused row reduction ("CUTLASS", Part IV Stage 5: a reduction for the next layer's
     norm): one problem, no split, no skinny kernel, a workspace of one fp32 partial per tile
