@@ -30,6 +30,10 @@ namespace {
 constexpr uint32_t kMagic = 0x47454d4du;   // live handle
 constexpr uint32_t kDead = 0xdeadbeefu;    // destroyed handle
 constexpr int64_t kLdsBudget = 160 * 1024;  // LDS per CU on gfx950
+constexpr int kCUs = 256;                   // compute units of an MI355X: one round of a
+                                            // one-workgroup-per-CU kernel, and the Stream-K
+                                            // launch's persistent workgroups
+static_assert(kCUs % 8 == 0, "Stream-K shares are dealt over the 8 XCDs");
 
 struct Operand {
   bool kmajor;  // unit stride along K
@@ -49,6 +53,7 @@ struct gemm_handle_s {
   int64_t kps_cfg, kps_fb;     // K elements per slice
   int tail_tiles, tail_split;  // split tail of the cfg entry (tail_split 1: none)
   int64_t tail_kps;            // K elements per slice of a tail tile
+  int sk_tiles;                // Stream-K tiles of the cfg entry (0: none)
   // Repack plan: A and B are read through K-major, 16-byte aligned copies of K padded to kp
   // (zeros past K) at the start of the workspace (A' then B', each rounded to 256 bytes), and
   // cfg is the entry chosen for that aligned problem.  An operand that is already K-major with
@@ -158,7 +163,9 @@ void plan_split(const KernelEntry& e, const gemm_desc& d, int req, int* S, int64
 // the last is at most half full, the R = tiles mod 256 tiles of that round are split along K into
 // S slices each, about R * S <= 256 workgroups, written as compact fp32 partials and summed in
 // fixed order by a second kernel; the other tiles run whole.  Only when the library decides the
-// split (split_k = 0, one plain product) and no whole-problem split is planned.
+// split (split_k = 0, one plain product), no whole-problem split is planned and Stream-K is
+// not (it takes this case for the kernels that have a Stream-K form; with decomposition 1 the
+// split tail stays).
 void plan_tail(const KernelEntry& e, const gemm_desc& d, int split_req, int split_whole, int* R,
                int* S, int64_t* kps) {
   *R = 0;
@@ -182,6 +189,36 @@ void plan_tail(const KernelEntry& e, const gemm_desc& d, int split_req, int spli
   *R = (int)rem;
   *S = (int)slices;
   *kps = per * e.bk;
+}
+
+// Stream-K (the work-centric tile scheduler; "CUTLASS", Part IV Stage 2 and its Stream-K
+// reference, Osama et al. 2023): kCUs persistent workgroups share the k-tile iterations of the
+// last tiles equally, so no CU idles in a last round that the tiles fill only partly.  As in
+// that paper's data-parallel hybrid, only the tiles of the last partial round run Stream-K (each
+// workgroup then takes less than one tile of work); the others run whole, a tile per workgroup.
+// With at most kCUs tiles all of them run Stream-K (with whole rounds only, forced, the last
+// round: whole tiles on persistent workgroups).  decomposition 2 forces the plan.  0 applies it
+// where it was measured to pay on MI355X: a last round at most half full after whole rounds,
+// with at least 64 k-tiles per tile, where it replaces the split tail (bf16 ring: 6144^2 x 8192
+// 495 us against 562 us split tail and 541-554 us data-parallel; 7168^2 x 8192 675 / 746 /
+// 732-742; 4352^2 x 8192 297 / 311 / 348-356; 4864 x 4096 x 4096 180 / 185 / 188-197).  With
+// a fuller last round, or with every tile in one round, the shares are larger than half a tile
+// and Stream-K lost (5376^2 x 4096: 280 us against 199-212 data-parallel; 3840^2 x 8192, 225
+// tiles: 336 against 190-209): a workgroup's share starts at a k offset of its own, so the
+// workgroups that share A and B panels no longer read them together and most reads miss L2.
+void plan_sk(const KernelEntry& e, const gemm_desc& d, int split_req, int split_whole,
+             int* sk_tiles) {
+  *sk_tiles = 0;
+  if (!e.launch_sk || d.decomposition == 1 || split_whole > 1) return;
+  if (d.batch > 1 || d.ragged_m || d.grouped || d.has_row_sumsq || d.has_col_sum) return;
+  const int64_t tiles = cdiv(d.M, e.bm) * cdiv(d.N, e.bn);
+  const int64_t nkt = cdiv(d.K, e.bk);
+  if (tiles == 0 || nkt == 0) return;
+  const int64_t rem = tiles % kCUs;
+  if (d.decomposition == 0) {
+    if (split_req != 0 || tiles <= kCUs || rem == 0 || rem > kCUs / 2 || nkt < 64) return;
+  }
+  *sk_tiles = (int)(tiles <= kCUs ? tiles : (rem == 0 ? kCUs : rem));
 }
 
 // Heuristic choice among fitting entries.  A product with M <= 16 is bound by streaming B and
@@ -424,6 +461,10 @@ int gemm_create(const gemm_desc* desc, gemm_t* out) {
   const int64_t L = d.batch > 1 ? d.batch : 1;
   if (d.ragged_m != 0 && d.ragged_m != 1) return GEMM_ERR_INVALID_ARG;
   if (d.grouped != 0 && d.grouped != 1) return GEMM_ERR_INVALID_ARG;
+  if (d.decomposition < 0 || d.decomposition > 2) return GEMM_ERR_INVALID_ARG;
+  if (d.decomposition == 2 && (d.split_k > 1 || d.batch > 1 || d.ragged_m || d.grouped ||
+                               d.has_row_sumsq || d.has_col_sum))
+    return GEMM_ERR_INVALID_ARG;
   if (d.has_row_sumsq != 0 && d.has_row_sumsq != 1) return GEMM_ERR_INVALID_ARG;
   if (d.has_col_sum != 0 && d.has_col_sum != 1) return GEMM_ERR_INVALID_ARG;
   // the reductions cover one problem and are not split along K
@@ -478,7 +519,9 @@ int gemm_create(const gemm_desc* desc, gemm_t* out) {
                   (L == 1 || d.grouped || (d.b_stride_l * isz) % 16 == 0);
   const bool need_split = d.split_k > 1;
   // no split of a batch, a group or a product with a row reduction
-  const int split_req = L > 1 || d.ragged_m || d.grouped || d.has_row_sumsq || d.has_col_sum
+  // (and Stream-K, when forced, in place of any split)
+  const int split_req = L > 1 || d.ragged_m || d.grouped || d.has_row_sumsq || d.has_col_sum ||
+                                d.decomposition == 2
                             ? 1 : d.split_k;
   h.fallback = choose(h, va, vb, false, split_req);
   if (h.fallback < 0) return GEMM_ERR_NO_CONFIG;
@@ -505,7 +548,9 @@ int gemm_create(const gemm_desc* desc, gemm_t* out) {
       plan_split(table()[inner], v.d, split_req, &h.split_cfg, &h.kps_cfg);
       h.split_fb = h.split_cfg;
       h.kps_fb = h.kps_cfg;
-      plan_tail(table()[inner], v.d, split_req, h.split_cfg, &h.tail_tiles, &h.tail_split, &h.tail_kps);
+      plan_sk(table()[inner], v.d, split_req, h.split_cfg, &h.sk_tiles);
+      plan_tail(table()[inner], v.d, h.sk_tiles > 0 ? 1 : split_req, h.split_cfg, &h.tail_tiles,
+                &h.tail_split, &h.tail_kps);
       gemm_handle_s* p = new (std::nothrow) gemm_handle_s(h);
       if (!p) return GEMM_ERR_INVALID_ARG;
       p->magic = kMagic;
@@ -527,7 +572,10 @@ int gemm_create(const gemm_desc* desc, gemm_t* out) {
   h.group_m = 4;
   plan_split(table()[h.cfg], d, split_req, &h.split_cfg, &h.kps_cfg);
   plan_split(table()[h.fallback], d, split_req, &h.split_fb, &h.kps_fb);
-  plan_tail(table()[h.cfg], d, split_req, h.split_cfg, &h.tail_tiles, &h.tail_split, &h.tail_kps);
+  // Stream-K where it pays, else the split tail where that does
+  plan_sk(table()[h.cfg], d, split_req, h.split_cfg, &h.sk_tiles);
+  plan_tail(table()[h.cfg], d, h.sk_tiles > 0 ? 1 : split_req, h.split_cfg, &h.tail_tiles,
+            &h.tail_split, &h.tail_kps);
 
   gemm_handle_s* p = new (std::nothrow) gemm_handle_s(h);
   if (!p) return GEMM_ERR_INVALID_ARG;
@@ -595,6 +643,10 @@ size_t inner_workspace(const gemm_handle_s& hh) {
     *bytes = std::max(*bytes, (size_t)h->tail_split * (size_t)h->tail_tiles * (size_t)e.bm *
                                   (size_t)e.bn * sizeof(float));
   }
+  if (h->sk_tiles > 0) {
+    const KernelEntry& e = table()[h->cfg];
+    *bytes = std::max(*bytes, (size_t)2 * kCUs * (size_t)e.bm * (size_t)e.bn * sizeof(float));
+  }
   if (h->d.has_row_sumsq || h->d.has_col_sum) *bytes = reduction_bytes(*h, nullptr);
   return v;
 }
@@ -623,6 +675,8 @@ int gemm_get_info(gemm_t h, gemm_info* info) {
   info->tail_tiles = h->tail_split > 1 ? h->tail_tiles : 0;
   info->tail_split = h->tail_split;
   info->repack = h->repack;
+  info->sk_tiles = h->sk_tiles;
+  info->sk_wgs = h->sk_tiles > 0 ? kCUs : 0;
   return GEMM_OK;
 }
 
@@ -692,7 +746,8 @@ int run_impl(gemm_t h, const void* A, const void* B, const void* C, void* D, con
   const int split = idx == h->cfg ? h->split_cfg : h->split_fb;
   const int64_t kps = idx == h->cfg ? h->kps_cfg : h->kps_fb;
   const bool tail = idx == h->cfg && h->tail_split > 1;
-  if ((split > 1 || tail || row_sumsq || col_sum) && (!workspace || !aligned(workspace, 16)))
+  const bool sk = idx == h->cfg && h->sk_tiles > 0;
+  if ((split > 1 || tail || sk || row_sumsq || col_sum) && (!workspace || !aligned(workspace, 16)))
     return GEMM_ERR_INVALID_ARG;
 
   KParams p;
@@ -763,6 +818,22 @@ int run_impl(gemm_t h, const void* A, const void* B, const void* C, void* D, con
     gz = 1;
   }
   if (grid <= 0 || grid > INT32_MAX) return GEMM_ERR_INVALID_ARG;
+  if (sk) {
+    // the tiles before the Stream-K part whole (tile order 0 .. grid - sk_tiles - 1), then the
+    // persistent workgroups over the rest, then the sum of the shared tiles' pieces
+    const int64_t whole = grid - h->sk_tiles;
+    hipError_t err = whole > 0 ? e.launch(p, (hipStream_t)stream, dim3((unsigned)whole, 1, 1))
+                               : hipSuccess;
+    KParams q = p;
+    q.tile_base = (int)whole;
+    q.sk_tiles = h->sk_tiles;
+    q.sk_nkt = (int)cdiv(Ke, e.bk);
+    q.sk_wgs = kCUs;  // a multiple of 8 (the kernel spreads shares over the 8 XCDs)
+    q.workspace = static_cast<float*>(workspace);
+    if (err == hipSuccess) err = e.launch_sk(q, (hipStream_t)stream, dim3((unsigned)kCUs, 1, 1));
+    if (err == hipSuccess) err = launch_sk_fixup(q, d.d_type, (hipStream_t)stream);
+    return err == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
+  }
   if (tail) {
     // whole tiles first (tile order 0 .. grid - R - 1), then the R tail tiles split along K,
     // then their fixed-order sum and epilogue

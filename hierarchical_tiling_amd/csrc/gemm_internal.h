@@ -63,6 +63,10 @@ struct KParams {
   // Grouped launch of independent problems: `batch` entries, and their first tiles in
   // group_base (batch + 1 values); nullptr otherwise.
   const GroupProblem* problems;
+  // Stream-K launch (sk_wgs > 0): sk_wgs persistent workgroups share the sk_tiles * sk_nkt
+  // k-tile iterations of the tiles from tile order tile_base on; pieces of shared tiles go to
+  // compact BM x BN slots of the workspace (2 per workgroup).
+  int sk_tiles, sk_nkt, sk_wgs;
 };
 
 typedef hipError_t (*launch_fn)(const KParams&, hipStream_t, dim3 grid);
@@ -87,6 +91,7 @@ struct KernelEntry {
   int mi;             // MFMA atom: MI x MI output block (its layouts are in atom_maps.h)
   int lds_row_chunks; // 16-byte chunks per swizzled LDS row of the operand tiles (4 or 8)
   int mn_rows;        // 1: an MN-major operand is kept as rows of k and read by transposing reads
+  launch_fn launch_sk;  // the kernel's Stream-K form (persistent workgroups), or nullptr
 };
 
 const KernelEntry* table();
@@ -98,6 +103,9 @@ hipError_t launch_splitk_reduce(const KParams& p, int out_type, hipStream_t s);
 // Second kernel of a split tail: for each of the p.tail_tiles tiles, D = act(alpha * sum of its
 // split_k compact fp32 partials + beta * C + bias) over that tile.
 hipError_t launch_tail_reduce(const KParams& p, int out_type, hipStream_t s);
+// Second kernel of a Stream-K launch: each of the p.sk_tiles tiles that several workgroups
+// shared gets D = act(alpha * (sum of its pieces in K order) + beta * C + bias).
+hipError_t launch_sk_fixup(const KParams& p, int out_type, hipStream_t s);
 // Sums the per-tile-column partials of the row sums of squares in fixed order: out[m] =
 // sum over t < tiles_n of ws[t * M + m].
 hipError_t launch_row_sumsq_reduce(const float* ws, float* out, int64_t M, int tiles_n, hipStream_t s);

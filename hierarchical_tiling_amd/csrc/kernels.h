@@ -258,10 +258,8 @@ template <int DT, int MI> __device__ __forceinline__ int frag_chunk(int l) {
 // are walked GROUP_M tile rows at a time so concurrently resident neighbours share A and B.
 // A split-tail launch covers the tile order from p.tile_base on.
 // ------------------------------------------------------------------------------------------
-__device__ __forceinline__ void tile_of(const KParams& p, int pid, int nwg, int& tm, int& tn) {
-  const int per = nwg >> 3, extra = nwg & 7;
-  const int xcd = pid & 7, local = pid >> 3;
-  const int t = xcd * per + min(xcd, extra) + local + p.tile_base;
+// Tile t of the tile order: GROUP_M tile rows at a time, column by column within a group.
+__device__ __forceinline__ void tile_walk(const KParams& p, int t, int& tm, int& tn) {
   const int width = p.group_m * p.tiles_n;
   const int group = t / width;
   const int first = group * p.group_m;
@@ -269,6 +267,11 @@ __device__ __forceinline__ void tile_of(const KParams& p, int pid, int nwg, int&
   const int within = t - group * width;
   tm = first + within % gsz;
   tn = within / gsz;
+}
+__device__ __forceinline__ void tile_of(const KParams& p, int pid, int nwg, int& tm, int& tn) {
+  const int per = nwg >> 3, extra = nwg & 7;
+  const int xcd = pid & 7, local = pid >> 3;
+  tile_walk(p, xcd * per + min(xcd, extra) + local + p.tile_base, tm, tn);
 }
 
 // ReLU that keeps NaN (max(0, NaN) is NaN, as in the oracle's definition).
@@ -446,13 +449,15 @@ __device__ __forceinline__ const void* advance_k(const void* base, int64_t ld, i
 // raw fp32 partial sums of this workgroup's tile into plane blockIdx.y of the workspace
 template <int DT, int MI, int BM, int BN, int WTM, int WTN, int RM, int RN, class AccT>
 __device__ __forceinline__ void store_partial(const KParams& p, const AccT (&acc)[RM][RN],
-                                              int64_t m0, int64_t n0, int wm, int wn, int lane) {
+                                              int64_t m0, int64_t n0, int wm, int wn, int lane,
+                                              int slot = -1) {
   typedef Atom<DT, MI> At;
   // whole-problem split: plane blockIdx.y of M x N; split tail: the compact BM x BN slot of
-  // tail workgroup blockIdx.x in plane blockIdx.y
-  const bool tail = p.tail_tiles > 0;
-  float* w = tail ? p.workspace + ((int64_t)blockIdx.y * p.tail_tiles + blockIdx.x) * (BM * BN)
-                  : p.workspace + (int64_t)blockIdx.y * p.M * p.N;
+  // tail workgroup blockIdx.x in plane blockIdx.y; Stream-K: compact slot `slot`
+  const bool tail = slot >= 0 || p.tail_tiles > 0;
+  float* w = slot >= 0 ? p.workspace + (int64_t)slot * (BM * BN)
+             : tail ? p.workspace + ((int64_t)blockIdx.y * p.tail_tiles + blockIdx.x) * (BM * BN)
+                    : p.workspace + (int64_t)blockIdx.y * p.M * p.N;
   static_for<RM>([&](auto i) {
     static_for<RN>([&](auto j) {
       static_for<At::NACC>([&](auto r) {
@@ -489,11 +494,59 @@ __global__ __launch_bounds__(256) void gemm_tail_reduce(const KParams p) {
   const int64_t m0 = (int64_t)tm * p.tile_bm, n0 = (int64_t)tn * p.tile_bn;
   const int64_t area = (int64_t)p.tile_bm * p.tile_bn, plane = area * p.tail_tiles;
   const float* w = p.workspace + (int64_t)blockIdx.x * area;
-  for (int64_t e = (int64_t)blockIdx.y * 256 + threadIdx.x; e < area; e += (int64_t)gridDim.y * 256) {
-    const int64_t row = m0 + e / p.tile_bn, col = n0 + e % p.tile_bn;
+  const int bn = p.tile_bn;
+  for (int e = blockIdx.y * 256 + threadIdx.x; e < (int)area; e += gridDim.y * 256) {
+    const int64_t row = m0 + e / bn, col = n0 + e % bn;
     if (row >= p.M || col >= p.N) continue;
     float sum = 0.f;
     for (int s = 0; s < p.split_k; ++s) sum += w[s * plane + e];
+    O::store(p.D, row * p.d_sm + col * p.d_sn, finish_elem<ODT>(p, row, col, sum));
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// Stream-K ("CUTLASS", Part IV Stage 2: a tile scheduler that splits K across blocks so every
+// processor gets an equal share of the work, then reduces the partial sums; Stream-K, Osama et
+// al. 2023, cited there): P persistent workgroups share the I = tiles * nkt k-tile iterations of
+// the Stream-K tiles; workgroup w takes iterations [I w / P, I (w+1) / P), walking them tile by
+// tile.  A tile whose iterations one workgroup covers whole is finished by it; the pieces of a
+// tile shared by several workgroups go to slots of the workspace (slot 2w for the first tile of
+// workgroup w, 2w + 1 for its last) and a second pass adds them in workgroup (so K) order and
+// applies the epilogue -- the pages' separate-reduction form of the second phase.
+// ------------------------------------------------------------------------------------------
+__host__ __device__ __forceinline__ int64_t sk_start(int64_t I, int P, int64_t w) { return I * w / P; }
+// the workgroup whose range holds iteration i: the largest w with sk_start(w) <= i
+__host__ __device__ __forceinline__ int sk_owner(int64_t I, int P, int64_t i) {
+  const int64_t w = ((i + 1) * P + I - 1) / I - 1;
+  return (int)(w < 0 ? 0 : (w >= P ? P - 1 : w));
+}
+template <int ODT>
+__global__ __launch_bounds__(256) void gemm_sk_fixup(const KParams p) {
+  typedef Out<ODT> O;
+  const int64_t t = blockIdx.x, nkt = p.sk_nkt, I = (int64_t)p.sk_tiles * nkt;
+  const int P = p.sk_wgs;
+  const int wlo = sk_owner(I, P, t * nkt), whi = sk_owner(I, P, (t + 1) * nkt - 1);
+  if (wlo == whi) return;  // finished by its one workgroup
+  int tm, tn;
+  tile_walk(p, (int)(p.tile_base + t), tm, tn);
+  const int64_t m0 = (int64_t)tm * p.tile_bm, n0 = (int64_t)tn * p.tile_bn;
+  const int64_t area = (int64_t)p.tile_bm * p.tile_bn;
+  // the tile's pieces in workgroup order: one thread per workgroup finds its slot (-1: an empty
+  // range, which holds no piece); at most P workgroups share a tile
+  __shared__ int slots[256];
+  const int n = whi - wlo + 1;
+  for (int i = threadIdx.x; i < n; i += 256) {
+    const int64_t s0 = sk_start(I, P, wlo + i);
+    slots[i] = s0 == sk_start(I, P, wlo + i + 1) ? -1 : 2 * (wlo + i) + (s0 / nkt == t ? 0 : 1);
+  }
+  __syncthreads();
+  const int bn = p.tile_bn;
+  for (int e = blockIdx.y * 256 + threadIdx.x; e < (int)area; e += gridDim.y * 256) {
+    const int64_t row = m0 + e / bn, col = n0 + e % bn;
+    if (row >= p.M || col >= p.N) continue;
+    float sum = 0.f;
+    for (int i = 0; i < n; ++i)
+      if (slots[i] >= 0) sum += p.workspace[slots[i] * area + e];
     O::store(p.D, row * p.d_sm + col * p.d_sn, finish_elem<ODT>(p, row, col, sum));
   }
 }
@@ -1537,7 +1590,7 @@ static hipError_t launch_dma(const KParams& p, hipStream_t s, dim3 grid) {
 // Summation order per output is the same as the two-stage DMA kernel's (k-tiles in order,
 // substeps in order), so both produce the same bits.
 // ------------------------------------------------------------------------------------------
-template <int DT, int WM, int WN, int MI, int NB, bool BKM>
+template <int DT, int WM, int WN, int MI, int NB, bool BKM, bool SK>
 __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_ring(const KParams p_) {
   KParams p;
   int pid, nwg;
@@ -1564,244 +1617,277 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_ring(const KParams p_) {
 
   __shared__ u32x4 lds[5 * SLOT];  // slots 0..2: A ring; 3..4: B ring
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  int tm, tn;
-  tile_of(p, pid, nwg, tm, tn);
-  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
-  const int wm = wave % WM, wn = wave / WM;
+  // Output tile (tm, tn) over the K range kr: the whole product's K, this workgroup's slice of
+  // a split, or (slot >= 0) a Stream-K piece of the tile, stored raw to that workspace slot.
+  auto run_tile = [&](int tm, int tn, const KRange kr, int slot) {
+    // The thread index passes through an empty asm here, so that nothing derived from it is
+    // hoisted out of a Stream-K workgroup's loop over tiles and held in registers across every
+    // tile's main loop.
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave % WM, wn = wave / WM;
+    const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
 
-  acc_t acc[RM][RN];
-  static_for<RM>([&](auto i) { static_for<RN>([&](auto j) { acc[i][j] = acc_t{}; }); });
+    acc_t acc[RM][RN];
+    static_for<RM>([&](auto i) { static_for<RN>([&](auto j) { acc[i][j] = acc_t{}; }); });
 
-  // this workgroup's K slice (all of K unless the product is split along K)
-  const KRange kr = k_range(p);
-  const int64_t K = uniform_i64(kr.len);
-  const char* a_tile = uniform_ptr((const char*)p.A + (m0 * p.lda + kr.begin) * SZ);
-  // B K-major: the tile's first column at its first k; B N-major (row-major): its first k row
-  // at its first column
-  const char* b_tile = uniform_ptr((const char*)p.B + (BKM ? n0 * p.ldb + kr.begin : kr.begin * p.ldb + n0) * SZ);
-  const int64_t a_span = uniform_i64(((p.M - m0 - 1) * p.lda + K) * SZ);
-  const int64_t b_span = uniform_i64(BKM ? ((min((int64_t)BN, p.N - n0) - 1) * p.ldb + K) * SZ
-                                         : ((K - 1) * p.ldb + (p.N - n0)) * SZ);
-  // Lane l of DMA block blk fills slot l of a kilobyte: row blk * RPB + l / CH, slot l % CH,
-  // which holds logical chunk (l % CH) ^ key(row).  A wave's blocks are NW apart, so its rows
-  // differ by multiples of RPB * NW; the key takes row bits 1..3 (2..3 for 64-byte rows), so
-  // with RPB * NW a multiple of 16 every block of the wave has the same chunk per lane, and the
-  // source offsets differ only by a uniform row stride.
-  static_assert((RPB * NW) % 16 == 0, "one chunk per lane across a wave's DMA blocks");
-  const int row0 = wave * RPB + lane / CH;
-  const int kc = ((lane % CH) ^ row_key<CH>(row0)) * VE;  // this lane's first k of its chunk
-  const uint32_t a_off0 = (uint32_t)(row0 * p.lda * SZ + kc * SZ);
-  // B N-major: a k-tile is BKE rows of BN elements (CHR chunks, slot mn_slot); lane l of DMA
-  // block blk fills row blk * 2 + l / CHR, slot l % CHR, which holds logical chunk
-  // (l % CHR) ^ mn_key(row).  A wave's blocks are NW apart, i.e. rows 2 NW apart, and mn_key
-  // takes row bits 0..3, so with 2 NW a multiple of 16 every block has the same chunk per lane.
-  constexpr int CHR = BN * SZ / 16, RPBR = 64 / CHR;
-  static_assert(BKM || (RPBR * NW) % 16 == 0, "one chunk per lane across a wave's B blocks");
-  static_assert(BKM || BKE / RPBR == BN / RPB, "a B unit takes as many DMA blocks either way");
-  const int brow0 = wave * RPBR + lane / CHR;
-  const uint32_t b_off0 = BKM ? (uint32_t)(row0 * p.ldb * SZ + kc * SZ)
-                              : (uint32_t)((brow0 * p.ldb + ((lane % CHR) ^ mn_key(brow0)) * VE) * SZ);
-  const int nk = (int)((K + BKE - 1) / BKE);
+    const int64_t K = uniform_i64(kr.len);
+    const char* a_tile = uniform_ptr((const char*)p.A + (m0 * p.lda + kr.begin) * SZ);
+    // B K-major: the tile's first column at its first k; B N-major (row-major): its first k row
+    // at its first column
+    const char* b_tile = uniform_ptr((const char*)p.B + (BKM ? n0 * p.ldb + kr.begin : kr.begin * p.ldb + n0) * SZ);
+    const int64_t a_span = uniform_i64(((p.M - m0 - 1) * p.lda + K) * SZ);
+    const int64_t b_span = uniform_i64(BKM ? ((min((int64_t)BN, p.N - n0) - 1) * p.ldb + K) * SZ
+                                           : ((K - 1) * p.ldb + (p.N - n0)) * SZ);
+    // Lane l of DMA block blk fills slot l of a kilobyte: row blk * RPB + l / CH, slot l % CH,
+    // which holds logical chunk (l % CH) ^ key(row).  A wave's blocks are NW apart, so its rows
+    // differ by multiples of RPB * NW; the key takes row bits 1..3 (2..3 for 64-byte rows), so
+    // with RPB * NW a multiple of 16 every block of the wave has the same chunk per lane, and the
+    // source offsets differ only by a uniform row stride.
+    static_assert((RPB * NW) % 16 == 0, "one chunk per lane across a wave's DMA blocks");
+    const int row0 = wave * RPB + lane / CH;
+    const int kc = ((lane % CH) ^ row_key<CH>(row0)) * VE;  // this lane's first k of its chunk
+    const uint32_t a_off0 = (uint32_t)(row0 * p.lda * SZ + kc * SZ);
+    // B N-major: a k-tile is BKE rows of BN elements (CHR chunks, slot mn_slot); lane l of DMA
+    // block blk fills row blk * 2 + l / CHR, slot l % CHR, which holds logical chunk
+    // (l % CHR) ^ mn_key(row).  A wave's blocks are NW apart, i.e. rows 2 NW apart, and mn_key
+    // takes row bits 0..3, so with 2 NW a multiple of 16 every block has the same chunk per lane.
+    constexpr int CHR = BN * SZ / 16, RPBR = 64 / CHR;
+    static_assert(BKM || (RPBR * NW) % 16 == 0, "one chunk per lane across a wave's B blocks");
+    static_assert(BKM || BKE / RPBR == BN / RPB, "a B unit takes as many DMA blocks either way");
+    const int brow0 = wave * RPBR + lane / CHR;
+    const uint32_t b_off0 = BKM ? (uint32_t)(row0 * p.ldb * SZ + kc * SZ)
+                                : (uint32_t)((brow0 * p.ldb + ((lane % CHR) ^ mn_key(brow0)) * VE) * SZ);
+    const int nk = (int)((K + BKE - 1) / BKE);
 
-  // Unit OP (0: A, 1: B) of k-tile t into `slot`.  Units past the end of K are all out of range
-  // (zeros) and are issued anyway, so the wait counts stay the same on every k-tile.
-  auto dma = [&](auto OP, int t, int slot) {
-    const int64_t k0 = (int64_t)t * BKE;
-    // elements of this k-tile inside K (at most BKE; zero or less past the end): the per-lane
-    // tail check is one 32-bit compare against this uniform value
-    const int rem = (int)min(K - k0, (int64_t)BKE);
-    u32x4* st = lds + slot * SLOT;
-    if constexpr (OP == 1 && !BKM) {
-      // rows of k: the k advance moves the descriptor's base, so the range check (on the VGPR
-      // offset) covers every row and column read; rows past K read zero
-      const int64_t adv = k0 * p.ldb * SZ;
-      const __amdgpu_buffer_rsrc_t r = make_rsrc(b_tile + adv, b_span - adv);
-      const uint32_t step = (uint32_t)(p.ldb * (RPBR * NW * SZ));
-      uint32_t off0 = b_off0;
-      asm volatile("" : "+v"(off0));
-      static_for<DU>([&](auto i) {
-        const int blk = wave + NW * i;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(st + blk * 64), 16,
-                                                 brow0 + RPBR * NW * i < rem ? off0 + (uint32_t)i * step : kOobOffset,
-                                                 0, 0, 0);
-      });
-    } else {
-      const __amdgpu_buffer_rsrc_t r = OP == 0 ? make_rsrc(a_tile, a_span) : make_rsrc(b_tile, b_span);
-      const uint32_t step = (uint32_t)((OP == 0 ? p.lda : p.ldb) * (RPB * NW * SZ));
-      // The base passes through an empty asm so that the per-block sums are formed here, at the
-      // issue, and not hoisted out of the k-loop as DU more live registers per operand.
-      uint32_t off0 = OP == 0 ? a_off0 : b_off0;
-      asm volatile("" : "+v"(off0));
-      const bool in_k = kc < rem;
-      static_for<DU>([&](auto i) {
-        const int blk = wave + NW * i;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(st + blk * 64), 16,
-                                                 in_k ? off0 + (uint32_t)i * step : kOobOffset,
-                                                 (int)(k0 * SZ), 0, 0);
-      });
-    }
-  };
-
-  const int frow = frag_row<DT, MI>(lane), fgrp = frag_chunk<DT, MI>(lane);
-  u32x4 fa[2][RM][At::UNITS], fb[S][RN][At::UNITS];
-  auto read_a = [&](auto buf, const u32x4* sa, auto sub) {
-    static_for<At::UNITS>([&](auto x) {
-      const int c = fgrp + At::G * (sub * At::UNITS + x);
-      static_for<RM>([&](auto i) { fa[buf][i][x] = sa[dslot<CH>(wm * WTM + i * MI + frow, c)]; });
-    });
-  };
-  auto read_b = [&](const u32x4* sb, auto sub) {
-    static_for<At::UNITS>([&](auto x) {
-      const int c = fgrp + At::G * (sub * At::UNITS + x);
-      static_for<RN>([&](auto j) {
-        if constexpr (BKM)
-          fb[sub][j][x] = sb[dslot<CH>(wn * WTN + j * MI + frow, c)];
-        else
-          fb[sub][j][x] = read_rows_frag<CHR>(sb, c * VE, wn * WTN + j * MI, frow, lane);
-      });
-    });
-  };
-  // LDS read instructions per B fragment (two transposing reads from rows of k)
-  constexpr int RB = BKM ? 1 : 2;
-  auto mma_rows = [&](auto buf, auto sub, auto i0, auto i1) {
-    static_for<At::PER_UNIT>([&](auto u) {
-      static_for<i1 - i0>([&](auto ii) {
-        static_for<RN>([&](auto j) { At::mma(acc[i0 + ii][j], fa[buf][i0 + ii], fb[sub][j], u); });
-      });
-    });
-  };
-  constexpr std::integral_constant<int, 0> OPA{};
-  constexpr std::integral_constant<int, 1> OPB{};
-  typedef std::integral_constant<int, 0> I0;
-  // Scheduling hint for one region: spread its NVM DMA instructions and NDS LDS reads (the next
-  // substep's fragments) evenly among its NMF MFMAs, then fence the region.  Left alone, the
-  // scheduler issues each read just before the MFMA that needs it (every MFMA then waits for an
-  // LDS round trip), bunches the DMA issue, and moves MFMAs across the barriers, which with one
-  // or two waves per SIMD leaves the matrix pipe idle at every barrier.
-  auto interleave = [&](auto NVM, auto NDS, auto NMF) {
-    constexpr int nvm = NVM, nds = NDS, nmf = NMF;
-    constexpr int ng = nvm > nds ? nvm : nds;
-    if constexpr (ng > 0) {
-      constexpr int per = (nmf + ng - 1) / ng;
-      static_for<ng>([&](auto g) {
-        if constexpr (g < nvm) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);  // one DMA
-        if constexpr (g < nds) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
-        __builtin_amdgcn_sched_group_barrier(0x008, per, 0);                        // MFMAs
-      });
-    }
-    __builtin_amdgcn_sched_barrier(0);
-  };
-  typedef std::integral_constant<int, 0> Z;
-
-  if (nk > 0) {
-    dma(OPA, 0, 0);
-    dma(OPB, 0, 3);
-    dma(OPA, 1, 1);
-    dma(OPB, 1, 4);
-    wait_counts<2 * DU, true>();
-    barrier_nofence();
-    if constexpr (NB == 1) dma(OPA, 2, 2);  // the third A slot is free from the start
-    read_a(I0{}, lds, I0{});
-    read_b(lds + 3 * SLOT, I0{});
-    // Substep s of k-tile t, whose A unit sits in slot sa_i.
-    auto substep = [&](int t, int sa_i, auto s) {
-      constexpr int buf = s & 1;
-      const int sb_i = 3 + (t & 1);
-      const u32x4* sa = lds + sa_i * SLOT;
-      // With two barriers per k-tile, A(t+2) is issued in substep 0, into the slot A(t-1)
-      // released, and B(t+2) in substep MID, after the barrier that released B(t)'s slot.
-      constexpr int nvm = NB == 2 ? (s == 0 ? DU : 0) + (s == MID ? DU : 0) : 0;
-      if constexpr (NB == 2 && s == 0) dma(OPA, t + 2, sa_i == 0 ? 2 : sa_i - 1);
-      if constexpr (NB == 2 && s == MID) dma(OPB, t + 2, sb_i);
-      if constexpr (s + 1 < S) {
-        read_a(std::integral_constant<int, buf ^ 1>{}, sa, std::integral_constant<int, s + 1>{});
-        mma_rows(std::integral_constant<int, buf>{}, s, I0{}, std::integral_constant<int, RM>{});
-        // the first substep also carries the B reads of the rest of the k-tile
-        interleave(std::integral_constant<int, nvm>{},
-                   std::integral_constant<int, RM * At::UNITS + (s == 0 ? (S - 1) * RN * At::UNITS * RB : 0)>{},
-                   std::integral_constant<int, RM * RN * At::PER_UNIT>{});
-        if constexpr (s + 1 == MID && NB == 2) {
-          // this wave's reads of B(t) are complete (lgkmcnt 0); after the barrier no wave
-          // reads B(t), and B(t+2) may take its slot
-          wait_counts<63, true>();
-          barrier_nofence();
-        }
+    // Unit OP (0: A, 1: B) of k-tile t into `slot`.  Units past the end of K are all out of range
+    // (zeros) and are issued anyway, so the wait counts stay the same on every k-tile.
+    auto dma = [&](auto OP, int t, int slot) {
+      const int64_t k0 = (int64_t)t * BKE;
+      // elements of this k-tile inside K (at most BKE; zero or less past the end): the per-lane
+      // tail check is one 32-bit compare against this uniform value
+      const int rem = (int)min(K - k0, (int64_t)BKE);
+      u32x4* st = lds + slot * SLOT;
+      if constexpr (OP == 1 && !BKM) {
+        // rows of k: the k advance moves the descriptor's base, so the range check (on the VGPR
+        // offset) covers every row and column read; rows past K read zero
+        const int64_t adv = k0 * p.ldb * SZ;
+        const __amdgpu_buffer_rsrc_t r = make_rsrc(b_tile + adv, b_span - adv);
+        const uint32_t step = (uint32_t)(p.ldb * (RPBR * NW * SZ));
+        uint32_t off0 = b_off0;
+        asm volatile("" : "+v"(off0));
+        static_for<DU>([&](auto i) {
+          const int blk = wave + NW * i;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(st + blk * 64), 16,
+                                                   brow0 + RPBR * NW * i < rem ? off0 + (uint32_t)i * step : kOobOffset,
+                                                   0, 0, 0);
+        });
       } else {
-        mma_rows(std::integral_constant<int, buf>{}, s, I0{}, std::integral_constant<int, RM / 2>{});
-        // these MFMAs stay before the barrier
-        interleave(std::integral_constant<int, nvm>{}, Z{},
-                   std::integral_constant<int, RM / 2 * RN * At::PER_UNIT>{});
-        // A(t+1) and B(t+1) have landed once at most A(t+2), B(t+2) are in flight (one barrier
-        // per k-tile: once at most A(t+2), issued after B(t+1), is)
-        if constexpr (NB == 2) wait_counts<2 * DU, true>(); else wait_counts<DU, true>();
-        barrier_nofence();
-        // (after the last k-tile these read zero-filled slots; the values are never used).  B
-        // first: the next substep's first MFMAs need A fragment 0 and every B fragment
-        const int na = sa_i == 2 ? 0 : sa_i + 1;
-        read_b(lds + (3 + ((t + 1) & 1)) * SLOT, I0{});
-        read_a(std::integral_constant<int, buf ^ 1>{}, lds + na * SLOT, I0{});
-        if constexpr (NB == 1) {
-          // every wave is past k-tile t: B(t+2) and A(t+3) take the slots of B(t) and A(t).
-          // Issued after the reads above, so the compiler cannot move those reads across the
-          // loop's back edge (the DMA may alias them).
-          dma(OPB, t + 2, sb_i);
-          dma(OPA, t + 3, sa_i);
+        const __amdgpu_buffer_rsrc_t r = OP == 0 ? make_rsrc(a_tile, a_span) : make_rsrc(b_tile, b_span);
+        const uint32_t step = (uint32_t)((OP == 0 ? p.lda : p.ldb) * (RPB * NW * SZ));
+        // The base passes through an empty asm so that the per-block sums are formed here, at the
+        // issue, and not hoisted out of the k-loop as DU more live registers per operand.
+        uint32_t off0 = OP == 0 ? a_off0 : b_off0;
+        asm volatile("" : "+v"(off0));
+        const bool in_k = kc < rem;
+        static_for<DU>([&](auto i) {
+          const int blk = wave + NW * i;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(st + blk * 64), 16,
+                                                   in_k ? off0 + (uint32_t)i * step : kOobOffset,
+                                                   (int)(k0 * SZ), 0, 0);
+        });
+      }
+    };
+
+    const int frow = frag_row<DT, MI>(lane), fgrp = frag_chunk<DT, MI>(lane);
+    u32x4 fa[2][RM][At::UNITS], fb[S][RN][At::UNITS];
+    auto read_a = [&](auto buf, const u32x4* sa, auto sub) {
+      static_for<At::UNITS>([&](auto x) {
+        const int c = fgrp + At::G * (sub * At::UNITS + x);
+        static_for<RM>([&](auto i) { fa[buf][i][x] = sa[dslot<CH>(wm * WTM + i * MI + frow, c)]; });
+      });
+    };
+    auto read_b = [&](const u32x4* sb, auto sub) {
+      static_for<At::UNITS>([&](auto x) {
+        const int c = fgrp + At::G * (sub * At::UNITS + x);
+        static_for<RN>([&](auto j) {
+          if constexpr (BKM)
+            fb[sub][j][x] = sb[dslot<CH>(wn * WTN + j * MI + frow, c)];
+          else
+            fb[sub][j][x] = read_rows_frag<CHR>(sb, c * VE, wn * WTN + j * MI, frow, lane);
+        });
+      });
+    };
+    // LDS read instructions per B fragment (two transposing reads from rows of k)
+    constexpr int RB = BKM ? 1 : 2;
+    auto mma_rows = [&](auto buf, auto sub, auto i0, auto i1) {
+      static_for<At::PER_UNIT>([&](auto u) {
+        static_for<i1 - i0>([&](auto ii) {
+          static_for<RN>([&](auto j) { At::mma(acc[i0 + ii][j], fa[buf][i0 + ii], fb[sub][j], u); });
+        });
+      });
+    };
+    constexpr std::integral_constant<int, 0> OPA{};
+    constexpr std::integral_constant<int, 1> OPB{};
+    typedef std::integral_constant<int, 0> I0;
+    // Scheduling hint for one region: spread its NVM DMA instructions and NDS LDS reads (the next
+    // substep's fragments) evenly among its NMF MFMAs, then fence the region.  Left alone, the
+    // scheduler issues each read just before the MFMA that needs it (every MFMA then waits for an
+    // LDS round trip), bunches the DMA issue, and moves MFMAs across the barriers, which with one
+    // or two waves per SIMD leaves the matrix pipe idle at every barrier.
+    auto interleave = [&](auto NVM, auto NDS, auto NMF) {
+      constexpr int nvm = NVM, nds = NDS, nmf = NMF;
+      constexpr int ng = nvm > nds ? nvm : nds;
+      if constexpr (ng > 0) {
+        constexpr int per = (nmf + ng - 1) / ng;
+        static_for<ng>([&](auto g) {
+          if constexpr (g < nvm) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);  // one DMA
+          if constexpr (g < nds) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+          __builtin_amdgcn_sched_group_barrier(0x008, per, 0);                        // MFMAs
+        });
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    typedef std::integral_constant<int, 0> Z;
+
+    if (nk > 0) {
+      dma(OPA, 0, 0);
+      dma(OPB, 0, 3);
+      dma(OPA, 1, 1);
+      dma(OPB, 1, 4);
+      wait_counts<2 * DU, true>();
+      barrier_nofence();
+      if constexpr (NB == 1) dma(OPA, 2, 2);  // the third A slot is free from the start
+      read_a(I0{}, lds, I0{});
+      read_b(lds + 3 * SLOT, I0{});
+      // Substep s of k-tile t, whose A unit sits in slot sa_i.
+      auto substep = [&](int t, int sa_i, auto s) {
+        constexpr int buf = s & 1;
+        const int sb_i = 3 + (t & 1);
+        const u32x4* sa = lds + sa_i * SLOT;
+        // With two barriers per k-tile, A(t+2) is issued in substep 0, into the slot A(t-1)
+        // released, and B(t+2) in substep MID, after the barrier that released B(t)'s slot.
+        constexpr int nvm = NB == 2 ? (s == 0 ? DU : 0) + (s == MID ? DU : 0) : 0;
+        if constexpr (NB == 2 && s == 0) dma(OPA, t + 2, sa_i == 0 ? 2 : sa_i - 1);
+        if constexpr (NB == 2 && s == MID) dma(OPB, t + 2, sb_i);
+        if constexpr (s + 1 < S) {
+          read_a(std::integral_constant<int, buf ^ 1>{}, sa, std::integral_constant<int, s + 1>{});
+          mma_rows(std::integral_constant<int, buf>{}, s, I0{}, std::integral_constant<int, RM>{});
+          // the first substep also carries the B reads of the rest of the k-tile
+          interleave(std::integral_constant<int, nvm>{},
+                     std::integral_constant<int, RM * At::UNITS + (s == 0 ? (S - 1) * RN * At::UNITS * RB : 0)>{},
+                     std::integral_constant<int, RM * RN * At::PER_UNIT>{});
+          if constexpr (s + 1 == MID && NB == 2) {
+            // this wave's reads of B(t) are complete (lgkmcnt 0); after the barrier no wave
+            // reads B(t), and B(t+2) may take its slot
+            wait_counts<63, true>();
+            barrier_nofence();
+          }
+        } else {
+          mma_rows(std::integral_constant<int, buf>{}, s, I0{}, std::integral_constant<int, RM / 2>{});
+          // these MFMAs stay before the barrier
+          interleave(std::integral_constant<int, nvm>{}, Z{},
+                     std::integral_constant<int, RM / 2 * RN * At::PER_UNIT>{});
+          // A(t+1) and B(t+1) have landed once at most A(t+2), B(t+2) are in flight (one barrier
+          // per k-tile: once at most A(t+2), issued after B(t+1), is)
+          if constexpr (NB == 2) wait_counts<2 * DU, true>(); else wait_counts<DU, true>();
+          barrier_nofence();
+          // (after the last k-tile these read zero-filled slots; the values are never used).  B
+          // first: the next substep's first MFMAs need A fragment 0 and every B fragment
+          const int na = sa_i == 2 ? 0 : sa_i + 1;
+          read_b(lds + (3 + ((t + 1) & 1)) * SLOT, I0{});
+          read_a(std::integral_constant<int, buf ^ 1>{}, lds + na * SLOT, I0{});
+          if constexpr (NB == 1) {
+            // every wave is past k-tile t: B(t+2) and A(t+3) take the slots of B(t) and A(t).
+            // Issued after the reads above, so the compiler cannot move those reads across the
+            // loop's back edge (the DMA may alias them).
+            dma(OPB, t + 2, sb_i);
+            dma(OPA, t + 3, sa_i);
+          }
+          mma_rows(std::integral_constant<int, buf>{}, s, std::integral_constant<int, RM / 2>{},
+                   std::integral_constant<int, RM>{});
+          interleave(std::integral_constant<int, NB == 1 ? 2 * DU : 0>{},
+                     std::integral_constant<int, (RM + RN * RB) * At::UNITS>{},
+                     std::integral_constant<int, RM / 2 * RN * At::PER_UNIT>{});
         }
-        mma_rows(std::integral_constant<int, buf>{}, s, std::integral_constant<int, RM / 2>{},
-                 std::integral_constant<int, RM>{});
-        interleave(std::integral_constant<int, NB == 1 ? 2 * DU : 0>{},
-                   std::integral_constant<int, (RM + RN * RB) * At::UNITS>{},
-                   std::integral_constant<int, RM / 2 * RN * At::PER_UNIT>{});
+      };
+      // First half of k-tile t: read the rest of the k-tile's B fragments, substeps 0 .. MID-1
+      // (ending with the barrier that releases B(t)).
+      auto tile_front = [&](int t, int sa_i) {
+        const u32x4* sb = lds + (3 + (t & 1)) * SLOT;
+        static_for<S - 1>([&](auto s) { read_b(sb, std::integral_constant<int, s + 1>{}); });
+        static_for<MID>([&](auto s) { substep(t, sa_i, s); });
+      };
+      auto tile_back = [&](int t, int sa_i) {
+        static_for<S - MID>([&](auto s) { substep(t, sa_i, std::integral_constant<int, MID + s>{}); });
+      };
+      // The loop turns at the B-release barrier in the middle of a k-tile.  Turning at the k-tile
+      // boundary instead lets the compiler merge the next k-tile's first fragment reads with the
+      // prologue's and sink them to the loop head, right before the MFMAs that consume them, so
+      // every k-tile would start with an exposed LDS round trip on all waves at once; nothing
+      // can be moved across the barrier and DMA that end each half here.
+      int sa_i = 0;  // slot of A(t) in the A ring
+      if constexpr (NB == 2) {
+        tile_front(0, 0);
+        for (int t = 0; t + 1 < nk; ++t) {
+          tile_back(t, sa_i);
+          sa_i = sa_i == 2 ? 0 : sa_i + 1;
+          tile_front(t + 1, sa_i);
+        }
+        tile_back(nk - 1, sa_i);
+      } else {
+        for (int t = 0; t < nk; ++t) {
+          tile_front(t, sa_i);
+          tile_back(t, sa_i);
+          sa_i = sa_i == 2 ? 0 : sa_i + 1;
+        }
       }
-    };
-    // First half of k-tile t: read the rest of the k-tile's B fragments, substeps 0 .. MID-1
-    // (ending with the barrier that releases B(t)).
-    auto tile_front = [&](int t, int sa_i) {
-      const u32x4* sb = lds + (3 + (t & 1)) * SLOT;
-      static_for<S - 1>([&](auto s) { read_b(sb, std::integral_constant<int, s + 1>{}); });
-      static_for<MID>([&](auto s) { substep(t, sa_i, s); });
-    };
-    auto tile_back = [&](int t, int sa_i) {
-      static_for<S - MID>([&](auto s) { substep(t, sa_i, std::integral_constant<int, MID + s>{}); });
-    };
-    // The loop turns at the B-release barrier in the middle of a k-tile.  Turning at the k-tile
-    // boundary instead lets the compiler merge the next k-tile's first fragment reads with the
-    // prologue's and sink them to the loop head, right before the MFMAs that consume them, so
-    // every k-tile would start with an exposed LDS round trip on all waves at once; nothing
-    // can be moved across the barrier and DMA that end each half here.
-    int sa_i = 0;  // slot of A(t) in the A ring
-    if constexpr (NB == 2) {
-      tile_front(0, 0);
-      for (int t = 0; t + 1 < nk; ++t) {
-        tile_back(t, sa_i);
-        sa_i = sa_i == 2 ? 0 : sa_i + 1;
-        tile_front(t + 1, sa_i);
-      }
-      tile_back(nk - 1, sa_i);
-    } else {
-      for (int t = 0; t < nk; ++t) {
-        tile_front(t, sa_i);
-        tile_back(t, sa_i);
-        sa_i = sa_i == 2 ? 0 : sa_i + 1;
-      }
+      wait_counts<0, true>();  // the zero-filled units issued past the end are still in flight
+      barrier_nofence();
     }
-    wait_counts<0, true>();  // the zero-filled units issued past the end are still in flight
-    barrier_nofence();
-  }
-  KParams pe;
-  problem_view<256>(reload_args(), pe, pid, nwg);
-  if (pe.split_k > 1) {
-    store_partial<DT, MI, BM, BN, WTM, WTN>(pe, acc, m0, n0, wm, wn, lane);
+    KParams pe;
+    int pid_e, nwg_e;
+    problem_view<256>(reload_args(), pe, pid_e, nwg_e);
+    if (SK && slot >= 0) {
+      store_partial<DT, MI, BM, BN, WTM, WTN>(pe, acc, m0, n0, wm, wn, lane, slot);
+    } else if (pe.split_k > 1) {
+      store_partial<DT, MI, BM, BN, WTM, WTN>(pe, acc, m0, n0, wm, wn, lane);
+    } else {
+      epilogue<DT, MI, BM, BN, WTM, WTN, RM, RN, NT, sizeof(lds)>(pe, acc, lds, m0, n0, wm, wn, lane,
+                                                                  tid, nk == 0);
+    }
+  };
+
+  if constexpr (!SK) {
+    int tm, tn;
+    tile_of(p, pid, nwg, tm, tn);
+    run_tile(tm, tn, k_range(p), -1);
   } else {
-    epilogue<DT, MI, BM, BN, WTM, WTN, RM, RN, NT, sizeof(lds)>(pe, acc, lds, m0, n0, wm, wn, lane,
-                                                                tid, nk == 0);
+    // Stream-K: this workgroup's contiguous share of the k-tile iterations, tile by tile.  Its
+    // place v in the sharing order puts the workgroups of one XCD (dispatch deals consecutive
+    // ids to the 8 XCDs in turn) on consecutive shares, so neighbouring tiles, which share A
+    // and B panels, are worked on under one L2.
+    const int v = (pid & 7) * (p.sk_wgs >> 3) + (pid >> 3);
+    const int64_t nkt = p.sk_nkt, I = (int64_t)p.sk_tiles * nkt;
+    int64_t it = sk_start(I, p.sk_wgs, v);
+    const int64_t end = sk_start(I, p.sk_wgs, v + 1);
+    const int64_t first = it / nkt;
+    while (it < end) {
+      const int64_t t = it / nkt, kb = it - t * nkt, ke = min(nkt, kb + (end - it));
+      int tm, tn;
+      tile_walk(p, (int)(p.tile_base + t), tm, tn);
+      const KRange kr{kb * BKE, min(p.K, ke * BKE) - kb * BKE};
+      run_tile(tm, tn, kr, kb == 0 && ke == nkt ? -1 : (int)(2 * v + (t == first ? 0 : 1)));
+      it += ke - kb;
+      __syncthreads();  // no wave still reads this tile's LDS when the next tile's copies land
+    }
   }
 }
 
-template <int DT, int WM, int WN, int MI, int NB, bool BKM>
+template <int DT, int WM, int WN, int MI, int NB, bool BKM, bool SK>
 static hipError_t launch_ring(const KParams& p, hipStream_t s, dim3 grid) {
-  hipLaunchKernelGGL((gemm_ring<DT, WM, WN, MI, NB, BKM>), grid, dim3(WM * WN * 64), 0, s, p);
+  hipLaunchKernelGGL((gemm_ring<DT, WM, WN, MI, NB, BKM, SK>), grid, dim3(WM * WN * 64), 0, s, p);
   return hipGetLastError();
 }
 
@@ -2101,10 +2187,20 @@ static hipError_t launch_tiled(const KParams& p, hipStream_t s, dim3 grid) {
 // row-major (N-contiguous) B kept in LDS as rows of k.
 #define HT_RING(NAME, DT, WM, WN, MI, NB, RANK, RANK1)                                               \
   {NAME, DT, 1, 1, 1, 0, 256, 256, 128 / Ty<DT>::SZ, WM * WN, 5, 5 * 256 * 128, 64, RANK,         \
-   &launch_ring<DT, WM, WN, MI, NB, true>, 0, RANK1, MI, 8, 0}
+   &launch_ring<DT, WM, WN, MI, NB, true, false>, 0, RANK1, MI, 8, 0, nullptr}
 #define HT_RING_BN(NAME, DT, WM, WN, MI, NB, RANK, RANK1)                                            \
   {NAME, DT, 1, 0, 1, 0, 256, 256, 128 / Ty<DT>::SZ, WM * WN, 5, 5 * 256 * 128, 64, RANK,         \
-   &launch_ring<DT, WM, WN, MI, NB, false>, 0, RANK1, MI, 8, 1}
+   &launch_ring<DT, WM, WN, MI, NB, false, false>, 0, RANK1, MI, 8, 1, nullptr}
+// The same entries with the Stream-K form of the kernel as well.  (The fp8 ring has none: its
+// 256 registers are full, and the form's loop over tiles spilled and ran at half speed.)
+#define HT_RING_SK(NAME, DT, WM, WN, MI, NB, RANK, RANK1)                                            \
+  {NAME, DT, 1, 1, 1, 0, 256, 256, 128 / Ty<DT>::SZ, WM * WN, 5, 5 * 256 * 128, 64, RANK,         \
+   &launch_ring<DT, WM, WN, MI, NB, true, false>, 0, RANK1, MI, 8, 0,                            \
+   &launch_ring<DT, WM, WN, MI, NB, true, true>}
+#define HT_RING_BN_SK(NAME, DT, WM, WN, MI, NB, RANK, RANK1)                                         \
+  {NAME, DT, 1, 0, 1, 0, 256, 256, 128 / Ty<DT>::SZ, WM * WN, 5, 5 * 256 * 128, 64, RANK,         \
+   &launch_ring<DT, WM, WN, MI, NB, false, false>, 0, RANK1, MI, 8, 1,                           \
+   &launch_ring<DT, WM, WN, MI, NB, false, true>}
 
 // Streaming skinny entries: bm = 16 rows, bn = 16*NBW columns, bk = one 128-byte block of K.
 #define HT_SKINNY_DMA(NAME, DT, WK, NBW, R, OCC)                                                  \

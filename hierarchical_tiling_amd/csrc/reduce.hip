@@ -30,6 +30,19 @@ hipError_t launch_tail_reduce(const KParams& p, int out_type, hipStream_t s) {
   return hipGetLastError();
 }
 
+hipError_t launch_sk_fixup(const KParams& p, int out_type, hipStream_t s) {
+  if (p.sk_tiles <= 0) return hipSuccess;
+  const int64_t area = (int64_t)p.tile_bm * p.tile_bn;
+  const dim3 grid((unsigned)p.sk_tiles, (unsigned)min((area + 255) / 256, (int64_t)32));
+  switch (out_type) {
+    case DT_F32: hipLaunchKernelGGL(gemm_sk_fixup<DT_F32>, grid, dim3(256), 0, s, p); break;
+    case DT_F16: hipLaunchKernelGGL(gemm_sk_fixup<DT_F16>, grid, dim3(256), 0, s, p); break;
+    case DT_BF16: hipLaunchKernelGGL(gemm_sk_fixup<DT_BF16>, grid, dim3(256), 0, s, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 // out[m] = sum of the tiles_n partials of row m, in plane order.
 __global__ __launch_bounds__(256) void gemm_row_sumsq_reduce(const float* ws, float* out,
                                                                int64_t M, int tiles_n) {

@@ -16,9 +16,9 @@ static const KernelEntry g_bf16_dma[] = {
     HT_DMA("bf16_ak_bk_256x256x32_w4x2_m32_dma5", DT_BF16, 256, 256, 4, 2, 32, 5, 1, 4, 4),
     HT_DMA("bf16_ak_bk_256x256x64_w2x4_m32_dma2", DT_BF16, 256, 256, 2, 4, 32, 2, 1, 8, 5),
     HT_RING("bf16_ak_bk_256x256x64_w2x4_m32_ring", DT_BF16, 2, 4, 32, 2, 6, 6),
-    HT_RING("bf16_ak_bk_256x256x64_w2x4_m16_ring", DT_BF16, 2, 4, 16, 2, 7, 7),
+    HT_RING_SK("bf16_ak_bk_256x256x64_w2x4_m16_ring", DT_BF16, 2, 4, 16, 2, 7, 7),
     HT_RING("bf16_ak_bk_256x256x64_w2x4_m16_ring1", DT_BF16, 2, 4, 16, 1, 0, 0),
-    HT_RING_BN("bf16_ak_bn_256x256x64_w2x4_m16_ring", DT_BF16, 2, 4, 16, 2, 7, 7),
+    HT_RING_BN_SK("bf16_ak_bn_256x256x64_w2x4_m16_ring", DT_BF16, 2, 4, 16, 2, 7, 7),
     HT_SKINNY_DMA("bf16_ak_bk_16x32_w4_skinny_dma", DT_BF16, 4, 2, 3, 2),
     HT_SKINNY("bf16_ak_bk_16x32_w8_skinny", DT_BF16, 8, 1, 2, 2, 4),
 };

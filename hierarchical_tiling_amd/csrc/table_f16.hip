@@ -36,8 +36,8 @@ static const KernelEntry g_f16[] = {
     HT_DMA("f16_ak_bk_256x256x64_w2x2_m32_dma2", DT_F16, 256, 256, 2, 2, 32, 2, 1, 8, 3),
     HT_DMA("f16_ak_bk_256x256x64_w2x4_m32_dma2", DT_F16, 256, 256, 2, 4, 32, 2, 1, 8, 5),
     HT_RING("f16_ak_bk_256x256x64_w2x4_m32_ring", DT_F16, 2, 4, 32, 2, 6, 6),
-    HT_RING("f16_ak_bk_256x256x64_w2x4_m16_ring", DT_F16, 2, 4, 16, 2, 7, 7),
-    HT_RING_BN("f16_ak_bn_256x256x64_w2x4_m16_ring", DT_F16, 2, 4, 16, 2, 7, 7),
+    HT_RING_SK("f16_ak_bk_256x256x64_w2x4_m16_ring", DT_F16, 2, 4, 16, 2, 7, 7),
+    HT_RING_BN_SK("f16_ak_bn_256x256x64_w2x4_m16_ring", DT_F16, 2, 4, 16, 2, 7, 7),
     HT_SKINNY_DMA("f16_ak_bk_16x32_w4_skinny_dma", DT_F16, 4, 2, 3, 2),
     HT_SKINNY("f16_ak_bk_16x32_w8_skinny", DT_F16, 8, 1, 2, 2, 4),
 };

@@ -55,7 +55,8 @@ class gemm_desc(ctypes.Structure):
                 ("a_stride_l", ctypes.c_int64), ("b_stride_l", ctypes.c_int64),
                 ("c_stride_l", ctypes.c_int64), ("d_stride_l", ctypes.c_int64),
                 ("ragged_m", ctypes.c_int32), ("has_row_sumsq", ctypes.c_int32),
-                ("has_col_sum", ctypes.c_int32), ("grouped", ctypes.c_int32)]
+                ("has_col_sum", ctypes.c_int32), ("grouped", ctypes.c_int32),
+                ("decomposition", ctypes.c_int32)]
 
 
 class gemm_problem(ctypes.Structure):
@@ -83,7 +84,8 @@ class gemm_info(ctypes.Structure):
                 ("lds_bytes", ctypes.c_int32), ("split_k", ctypes.c_int32),
                 ("grid", ctypes.c_int64), ("name", ctypes.c_char * 96),
                 ("tail_tiles", ctypes.c_int32), ("tail_split", ctypes.c_int32),
-                ("repack", ctypes.c_int32)]
+                ("repack", ctypes.c_int32), ("sk_tiles", ctypes.c_int32),
+                ("sk_wgs", ctypes.c_int32)]
 
 
 class ht_tile_stats(ctypes.Structure):
@@ -268,7 +270,7 @@ def gemm_probe_atom(dtype: str, mi: int, out, stream=None):
 def make_desc(M, N, K, dtype, a_strides, b_strides, d_strides, c_strides=None, has_bias=False,
               act="none", force_config=-1, split_k=0, row_scale=False, col_scale=False, batch=1,
               batch_strides=(0, 0, 0, 0), ragged_m=False, row_sumsq=False,
-              col_sum=False, grouped=False) -> gemm_desc:
+              col_sum=False, grouped=False, decomposition=0) -> gemm_desc:
     """a_strides = (stride_m, stride_k); b_strides = (stride_k, stride_n); c/d = (m, n);
     batch_strides = element offsets between consecutive problems of A, B, C, D."""
     out_t = "bf16" if dtype == "e4m3" else dtype
@@ -293,6 +295,7 @@ def make_desc(M, N, K, dtype, a_strides, b_strides, d_strides, c_strides=None, h
     d.has_row_sumsq = 1 if row_sumsq else 0
     d.has_col_sum = 1 if col_sum else 0
     d.grouped = 1 if grouped else 0
+    d.decomposition = decomposition
     return d
 
 

@@ -146,6 +146,12 @@ typedef struct gemm_desc {
                               /* `batch` problems of that shape) and the strides give each       */
                               /* operand's unit-stride direction; ragged_m, split_k > 1, scale   */
                               /* vectors and the reductions are refused                          */
+  int32_t decomposition;      /* how output tiles are spread over the CUs: 0 = the library       */
+                              /* decides, 1 = no Stream-K (a tile per workgroup, K slices as     */
+                              /* split_k says), 2 = Stream-K, and no other split, wherever the   */
+                              /* chosen kernel has a Stream-K form (gemm_info.sk_tiles > 0 then);*/
+                              /* 2 is refused with split_k > 1, a batch, a grouped handle or a   */
+                              /* reduction                                                       */
 } gemm_desc;
 
 typedef struct gemm_handle_s* gemm_t;
@@ -166,7 +172,10 @@ int gemm_create(const gemm_desc* desc, gemm_t* out);
  * elements (each rounded up to 256 bytes), Kp being K rounded up to 16 bytes' worth, and
  * gemm_run writes them with one copy kernel per operand on the stream before the product.  A split tail (the
  * Stream-K idea, same Part: the tiles of a last round that would leave most CUs idle are each
- * split along K) needs tail_split * tail_tiles * bm * bn * 4 (gemm_info).  A grouped handle
+ * split along K) needs tail_split * tail_tiles * bm * bn * 4 (gemm_info).  Stream-K (gemm_info.sk_tiles
+ * > 0: the last tiles of the tile order shared out as equal runs of k-tiles among sk_wgs
+ * persistent workgroups, "CUTLASS", Part IV Stage 2) needs 2 * sk_wgs * bm * bn * 4 for the
+ * pieces of the tiles they share.  A grouped handle
  * (ragged_m) needs (G + 1) * 4 bytes rounded up to 256, plus (G + 1) * 8; a handle of independent
  * problems (grouped) needs 112 * batch bytes rounded up to 256, plus (batch + 1) * 8.  With has_row_sumsq it
  * is the number of N tiles * M * 4, and has_col_sum adds (M tiles * row groups) * N * 4.  The caller owns the
@@ -185,7 +194,9 @@ int gemm_workspace_size(gemm_t h, size_t* bytes);
  * gemm_workspace_size() bytes, 16-byte aligned (GEMM_ERR_INVALID_ARG if it is needed and missing;
  * ignored when that size is 0).  A split run is two kernels on `stream`: the K slices, then their
  * fixed-order sum and the epilogue; a split-tail run is three: the whole tiles, the tail tiles'
- * K slices, then their fixed-order sum and epilogue.  Returns after the launches are queued; launch failures
+ * K slices, then their fixed-order sum and epilogue; a Stream-K run is three: the whole tiles
+ * before the Stream-K part, the persistent workgroups, then the sum of the shared tiles' pieces
+ * in K order with the epilogue.  Returns after the launches are queued; launch failures
  * return GEMM_ERR_LAUNCH. */
 int gemm_run(gemm_t h, const void* A, const void* B, const void* C, void* D, const void* bias,
              float alpha, float beta, float scale_a, float scale_b, void* workspace,
@@ -307,6 +318,8 @@ typedef struct gemm_info {
   int32_t tail_tiles;     /* tiles of an incomplete last round run split along K (0: none)      */
   int32_t tail_split;     /* K slices of each such tile (1: none)                               */
   int32_t repack;         /* 1: A and B are read through aligned K-major copies in the workspace */
+  int32_t sk_tiles;       /* tiles run Stream-K (the last ones of the tile order; 0: none)      */
+  int32_t sk_wgs;         /* persistent workgroups of the Stream-K launch                       */
 } gemm_info;
 
 int gemm_get_info(gemm_t h, gemm_info* info);

@@ -52,6 +52,7 @@ class Case:
     scale_dist: str = "uniform"  # "uniform": U[0.25, 2] rows, U[-2, 2] columns; "pow2": 2^[-3..3]
     row_sumsq: bool = False     # also compute the row sums of squares of D (gemm_run_ex)
     col_sum: bool = False       # also compute the column sums of D (gemm_run_ex)
+    decomposition: int = 0      # 0: the library decides; 1: no Stream-K; 2: Stream-K
 
 
 def op(m):
@@ -114,7 +115,7 @@ class Prepared:
                            c_strides=self.C.strides if self.C is not None else None,
                            has_bias=c.bias, act=c.act, force_config=c.force, split_k=c.split_k,
                            row_scale=c.row_scale, col_scale=c.col_scale, row_sumsq=c.row_sumsq,
-                           col_sum=c.col_sum)
+                           col_sum=c.col_sum, decomposition=c.decomposition)
 
     def run(self, g: H.Gemm | None = None, out=None):
         c = self.case

@@ -361,6 +361,48 @@ def test_grouped_problems_fields(fake_gfx950):
     assert status_of(desc(**dict(base, d_strides=(1, 512)))) == 0
 
 
+def test_stream_k_plan(fake_gfx950):
+    """Stream-K ("CUTLASS", Part IV Stage 2): the tiles of a last partial round of a
+    one-workgroup-per-CU kernel run as 256 persistent workgroups; the library applies it where
+    it was measured to pay (a last round at most half full, at least 64 k-tiles) in place of
+    the split tail."""
+    def info(M, N, K, **kw):
+        g = H.Gemm(H.make_desc(M, N, K, "bf16", (K, 1), (1, K), (N, 1), **kw))
+        return g.info, g.workspace_bytes
+    ws_sk = 2 * 256 * 256 * 256 * 4
+    i, ws = info(4352, 4352, 4096)          # 289 tiles: 33 in the last round, 64 k-tiles
+    assert "_ring" in i.name.decode() and (i.sk_tiles, i.sk_wgs) == (33, 256) and ws == ws_sk
+    assert (i.tail_tiles, i.tail_split) == (0, 1)
+    assert info(6144, 6144, 8192)[0].sk_tiles == 64
+    for shape in ((8192, 8192, 8192),       # whole rounds
+                  (5120, 5120, 8192),       # 144 left: more than half a round
+                  (3840, 3840, 8192),       # one round
+                  (6144, 6144, 2048)):      # 32 k-tiles: too shallow
+        i, _ = info(*shape)
+        assert i.sk_tiles == 0, shape
+    # no Stream-K when asked for none (the split tail then), or with a fixed split
+    i, _ = info(4352, 4352, 4096, decomposition=1)
+    assert i.sk_tiles == 0 and i.tail_split > 1
+    assert info(4352, 4352, 4096, split_k=1)[0].sk_tiles == 0
+    # forced: every tile when they fit in one round, else the last partial round (the last
+    # round with whole rounds only)
+    ring = [H.gemm_config_name(j) for j in range(H.gemm_num_configs())].index(
+        "bf16_ak_bk_256x256x64_w2x4_m16_ring")
+    assert info(1000, 1300, 64, force_config=ring, decomposition=2)[0].sk_tiles == 24
+    assert info(5120, 5120, 8192, force_config=ring, decomposition=2)[0].sk_tiles == 144
+    i, ws = info(8192, 8192, 8192, force_config=ring, decomposition=2)
+    assert i.sk_tiles == 256 and ws == ws_sk
+    # a kernel without a Stream-K form (an fp32 tile kernel, the fp8 ring) runs data-parallel
+    g = H.Gemm(H.make_desc(512, 512, 512, "f32", (512, 1), (1, 512), (512, 1), decomposition=2))
+    assert g.info.sk_tiles == 0 and g.workspace_bytes == 0
+    g = H.Gemm(H.make_desc(4352, 4352, 8192, "e4m3", (8192, 1), (1, 8192), (4352, 1)))
+    assert "_ring" in g.info.name.decode() and g.info.sk_tiles == 0 and g.info.tail_split > 1
+    for bad in (dict(decomposition=3), dict(decomposition=-1), dict(decomposition=2, split_k=2),
+                dict(decomposition=2, batch=2, batch_strides=(8192 * 8192, 8192 * 8192, 0,
+                                                              8192 * 8192))):
+        assert status_of(desc(**bad)) == H.GEMM_ERR_INVALID_ARG, bad
+
+
 def test_row_sumsq_fields(fake_gfx950):
     """The fused row reduction ("CUTLASS", Part IV Stage 5: a reduction for the next layer's
     norm): one problem, no split, no skinny kernel, a workspace of one fp32 partial per tile
@@ -415,28 +457,28 @@ def test_col_sum_fields(fake_gfx950):
 
 # Kernel choice for mid-size and large bf16 products (A row-major, B column-major).  One-round
 # rules measured on MI355X: a one-workgroup-per-CU tile is used when its single round is over
-# half full; automatic K slices stay within one round; leftover tiles of an incomplete last round
-# are split along K (split tail).
-@pytest.mark.parametrize("shape,kernel,split,tail", [
-    ((3072, 3072, 3072), "m16_ring", 1, (0, 1)),       # 144 ring tiles
-    ((3328, 3328, 4096), "m16_ring", 1, (0, 1)),       # 169: no split, 2 slices would be 338
-    ((2816, 2816, 4096), "m16_ring", 2, (0, 1)),       # 121 tiles x 2 = 242
-    ((1536, 1536, 8192), "m16_ring", 7, (0, 1)),       # 36 x 7 = 252; 8 would start a round
+# half full; automatic K slices stay within one round; the leftover tiles of an incomplete last
+# round run Stream-K on the ring (the split tail when Stream-K is turned off).
+@pytest.mark.parametrize("shape,kernel,split,tail,sk", [
+    ((3072, 3072, 3072), "m16_ring", 1, (0, 1), 0),       # 144 ring tiles
+    ((3328, 3328, 4096), "m16_ring", 1, (0, 1), 0),       # 169: no split, 2 slices would be 338
+    ((2816, 2816, 4096), "m16_ring", 2, (0, 1), 0),       # 121 tiles x 2 = 242
+    ((1536, 1536, 8192), "m16_ring", 7, (0, 1), 0),       # 36 x 7 = 252; 8 would start a round
     # 4 ring slices would keep 16 k-tiles each while 128 x 128 tiles fill the GPU unsplit:
     # 0.048 against 0.055 ms on one MI355X, a tie on another
-    ((2048, 2048, 4096), "128x128x64", 1, (0, 1)),
-    ((2048, 4096, 2048), "256x128x32", 1, (0, 1)),     # exactly 128 ring tiles: half-size tile
-    ((2048, 2048, 2048), "128x128x64", 1, (0, 1)),
-    ((512, 512, 16384), "128x128x64", 16, (0, 1)),
-    ((8192, 8192, 8192), "m16_ring", 1, (0, 1)),
-    ((4352, 4352, 4096), "m16_ring", 1, (33, 7)),
+    ((2048, 2048, 4096), "128x128x64", 1, (0, 1), 0),
+    ((2048, 4096, 2048), "256x128x32", 1, (0, 1), 0),     # exactly 128 ring tiles: half-size tile
+    ((2048, 2048, 2048), "128x128x64", 1, (0, 1), 0),
+    ((512, 512, 16384), "128x128x64", 16, (0, 1), 0),
+    ((8192, 8192, 8192), "m16_ring", 1, (0, 1), 0),
+    ((4352, 4352, 4096), "m16_ring", 1, (0, 1), 33),
 ])
-def test_kernel_choice_by_rounds(fake_gfx950, shape, kernel, split, tail):
+def test_kernel_choice_by_rounds(fake_gfx950, shape, kernel, split, tail, sk):
     M, N, K = shape
     info = _info(desc(M=M, N=N, K=K, a_strides=(K, 1), b_strides=(1, K), d_strides=(N, 1)))
     name = info.name.decode()
     assert kernel in name and not name.endswith("ring1"), name
-    assert (info.split_k, info.tail_tiles, info.tail_split) == (split,) + tail, name
+    assert (info.split_k, info.tail_tiles, info.tail_split, info.sk_tiles) == (split,) + tail + (sk,), name
 
 
 @pytest.mark.parametrize("dtype,shape,orders,kernel", [

@@ -1,6 +1,7 @@
 """Split tail: when the tiles of a one-workgroup-per-CU kernel leave the last round of 256 at most
 half full, the library splits each tile of that round along K and sums the slices in a second
-kernel (the data-parallel plus split-K hybrid of Stream-K scheduling).  Checks the plan, exact
+kernel (the data-parallel plus split-K hybrid of Stream-K scheduling; the library takes Stream-K
+itself for these shapes on kernels with a Stream-K form, so the tests ask for decomposition 1).  Checks the plan, exact
 results on dyadic inputs (bit-identical to the unsplit run and to the oracle), and tolerance on
 ordinary inputs for each operand type.
 """
@@ -17,7 +18,9 @@ pytestmark = pytest.mark.gpu
 
 
 def plan(M, N, K, dtype="bf16", split_k=0):
-    g = H.Gemm(H.make_desc(M, N, K, dtype, (K, 1), (1, K), (N, 1), split_k=split_k))
+    # decomposition 1: no Stream-K, which otherwise takes these last rounds on the ring kernels
+    g = H.Gemm(H.make_desc(M, N, K, dtype, (K, 1), (1, K), (N, 1), split_k=split_k,
+                           decomposition=1))
     return g.info, g.workspace_bytes
 
 
@@ -45,7 +48,7 @@ def test_plan(shape, dtype, want):
 
 def test_dyadic_exact_and_identical_to_unsplit():
     c = Case(4352, 4352, 4096, "bf16", "row", "col", dist="dyadic", alpha=2.0, beta=0.5,
-             has_c=True, bias=True, seed=77)
+             has_c=True, bias=True, seed=77, decomposition=1)
     p = Prepared(c)
     g, out = p.run()
     assert (g.info.tail_tiles, g.info.tail_split) == (33, 7)
@@ -61,9 +64,11 @@ def test_dyadic_exact_and_identical_to_unsplit():
 
 
 @pytest.mark.parametrize("case", [
-    Case(4352, 4352, 4096, "bf16", "row", "col", bias=True, act="gelu", seed=78),
-    Case(4864, 4096, 4096, "f16", "row", "col", has_c=True, beta=-0.5, alpha=0.75, seed=79),
-    Case(4352, 4352, 8192, "e4m3", "row", "col", std=1.0, scale_a=0.05, scale_b=0.05, seed=80),
+    Case(4352, 4352, 4096, "bf16", "row", "col", bias=True, act="gelu", seed=78, decomposition=1),
+    Case(4864, 4096, 4096, "f16", "row", "col", has_c=True, beta=-0.5, alpha=0.75, seed=79,
+         decomposition=1),
+    Case(4352, 4352, 8192, "e4m3", "row", "col", std=1.0, scale_a=0.05, scale_b=0.05, seed=80,
+         decomposition=1),
 ], ids=["bf16_gelu", "f16_c", "e4m3"])
 def test_sampled_parity(case):
     p = Prepared(case)
