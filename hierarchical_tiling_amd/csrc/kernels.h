@@ -1084,6 +1084,14 @@ __device__ __forceinline__ float load_c(__amdgpu_buffer_rsrc_t r, uint32_t off) 
 // output type.  Phase 2: the rounded tile goes through LDS so the store to D is 16-byte
 // row-contiguous chunks instead of the MFMA's column-wise lane layout.  The caller guarantees
 // that no wave still reads the LDS operand stages and no DMA into them is in flight.
+//
+// Rows of a row-major D whose 16-byte grid does not start at the tile's first column (a leading
+// dimension or base off 16 bytes) are placed in LDS shifted by that misalignment, so that chunk
+// j of an LDS row holds the outputs of D's aligned chunk j: the store is still one 16-byte store
+// per chunk, with element stores only for the partial chunks at the two ends of a row.  A
+// row-major C is staged the same way before phase 1 -- 16-byte chunks in D's grid, through
+// realigned loads where C's own alignment differs -- and each lane reads its C values from the
+// LDS position its result then overwrites.
 // ------------------------------------------------------------------------------------------
 template <int DT, int MI, int BM, int BN, int WTM, int WTN, int RM, int RN, int NT,
           size_t LDS_BYTES, class AccT>
@@ -1095,19 +1103,106 @@ __device__ __forceinline__ void epilogue(const KParams& p, AccT (&acc)[RM][RN], 
   typedef Out<ODT> O;
   typedef typename OutBits<ODT>::T OT;
   constexpr int OSZ = (int)sizeof(OT);
-  // Rows of the LDS tile are PITCH outputs apart.  With the 16x16 atom one store instruction
-  // writes rows r and r + 4 from the two quarter-waves of each half-wave; 16 bytes of padding per
-  // row put those rows on different banks (with BN * OSZ a multiple of 256 bytes they would
-  // share them).  The padding is used only where the padded tile still fits.
+  // Rows of the LDS tile are PITCH outputs apart.  One store instruction writes rows r and r + 4
+  // (16x16 atom: the two quarter-waves of each half-wave; 32x32: the two half-waves); 16 bytes
+  // of padding per row put those rows on different banks (with BN * OSZ a multiple of 256 bytes
+  // they would share them) and leave room for a row shifted by up to one chunk (below).  The
+  // padding is used only where the padded tile still fits.
   constexpr int PAD = 16 / OSZ;
-  constexpr int PITCH = MI == 16 && (size_t)BM * (BN + PAD) * OSZ <= LDS_BYTES ? BN + PAD : BN;
+  constexpr bool SHIFT = (size_t)BM * (BN + PAD) * OSZ <= LDS_BYTES;  // room for shifted rows
+  constexpr int PITCH = SHIFT ? BN + PAD : BN;
   constexpr bool REPACK = (size_t)BM * PITCH * OSZ <= LDS_BYTES;
+  constexpr int VO = 16 / OSZ;            // outputs per 16-byte chunk
+  constexpr int CPR = BN / VO;            // chunks per tile row (aligned rows)
   const bool has_c = p.has_c != 0, has_bias = p.has_bias != 0;
   const bool has_rs = p.has_row_scale != 0, has_cs = p.has_col_scale != 0;
   const int act = p.act;
   const float alpha = p.alpha, beta = p.beta;
   OT* tile = reinterpret_cast<OT*>(lds);  // BM x BN, row-major, rows PITCH apart (REPACK only)
   if (REPACK && no_mainloop) __syncthreads();
+  // Shifted rows: output (row, n0 + c) at LDS position c + mis(row), mis(row) = the element
+  // offset of D(row, n0) past a 16-byte boundary (0 for aligned rows).  Not with the fused
+  // reductions, which read the tile unshifted.
+  const bool d_rows = SHIFT && REPACK && p.d_sn == 1 && !p.rsq_ws && !p.csum_ws;
+  const bool vec_ok = p.d_sn == 1 && (p.d_sm * OSZ) % 16 == 0 &&
+                      (reinterpret_cast<uintptr_t>(p.D) % 16) == 0;
+  const bool shifted = d_rows && !vec_ok;  // aligned rows have mis = 0 throughout
+  const uint32_t d_el0 = (uint32_t)(reinterpret_cast<uintptr_t>(p.D) / OSZ) + (uint32_t)n0;
+  auto mis_raw = [&](int64_t row) -> int {
+    return (int)((d_el0 + (uint32_t)row * (uint32_t)p.d_sm) & (uint32_t)(VO - 1));
+  };
+  auto mis_of = [&](int64_t row) -> int { return shifted ? mis_raw(row) : 0; };
+  // The chunks of D's 16-byte grid that a tile row touches: chunk j covers columns
+  // col0 = n0 - mis + j * VO onward, of which [lo, hi) belong to the tile and the problem.
+  constexpr int CPRS = CPR + 1;
+  auto chunk_of = [&](int lr, int j, int64_t& col0, int64_t& lo, int64_t& hi) {
+    col0 = n0 - mis_of(m0 + lr) + (int64_t)j * VO;
+    lo = max(col0, n0);
+    hi = min(col0 + VO, min(n0 + BN, p.N));
+  };
+  // Row-major C staged into the LDS tile at the output positions (buffer loads: C below 2^31
+  // bytes).  The descriptor starts at C rounded down to 4 bytes; `cdelta` is the difference.
+  const bool c_lds = d_rows && has_c && p.c_sn == 1 && p.c_span > 0;
+  if (c_lds) {
+    const char* cb = reinterpret_cast<const char*>(reinterpret_cast<uintptr_t>(p.C) & ~uintptr_t(3));
+    const uint32_t cdelta = (uint32_t)(reinterpret_cast<const char*>(p.C) - cb);
+    const __amdgpu_buffer_rsrc_t cr = make_rsrc(cb, (cdelta + p.c_span + 3) & ~int64_t(3));
+    // Whole chunks: branch-free loads (out-of-range offsets read zero), a batch of them issued
+    // back to back before their LDS writes, so a batch waits for memory once.
+    constexpr int ITER = (BM * CPRS + NT - 1) / NT;
+    constexpr int BATCH = ITER < 9 ? ITER : 9;
+#pragma unroll
+    for (int it0 = 0; it0 < ITER; it0 += BATCH) {
+      Raw16 w[BATCH];
+      uint32_t sh[BATCH];
+      int pos[BATCH];
+      static_for<BATCH>([&](auto b) {
+        const int q = tid + (it0 + b) * NT;
+        const int lr = q / CPRS, j = q - lr * CPRS;
+        int64_t col0, lo, hi;
+        chunk_of(lr, j, col0, lo, hi);
+        const bool whole = q < BM * CPRS && m0 + lr < p.M && lo == col0 && hi == col0 + VO;
+        const uint32_t off = cdelta + (uint32_t)(((m0 + lr) * p.c_sm + col0) * OSZ);
+        if constexpr (OSZ == 2) {
+          w[b] = raw16(cr, whole ? (off & ~3u) : kOobOffset);
+        } else {
+          w[b].q = __builtin_amdgcn_raw_buffer_load_b128(cr, whole ? off : kOobOffset, 0, 0);
+          w[b].x = 0;
+        }
+        sh[b] = off & 2u;
+        pos[b] = whole ? lr * PITCH + j * VO : -1;
+      });
+      static_for<BATCH>([&](auto b) {
+        if (pos[b] >= 0)
+          *reinterpret_cast<u32x4*>(&tile[pos[b]]) = OSZ == 2 ? realign16(w[b], sh[b], 0xffu) : w[b].q;
+      });
+    }
+    // The partial chunks at the two ends of a row (the first when the row is shifted, the one
+    // holding the row's last column when it does not end a chunk): element loads.
+    for (int q = tid; q < BM * 2; q += NT) {
+      const int lr = q >> 1;
+      const int64_t row = m0 + lr;
+      const int64_t end = min(n0 + BN, p.N);
+      if (row >= p.M || end <= n0) continue;
+      const int jl = (int)((end - 1 - (n0 - mis_of(row))) / VO);
+      if ((q & 1) && jl == 0) continue;  // a single chunk: the even thread takes it
+      const int j = (q & 1) ? jl : 0;
+      int64_t col0, lo, hi;
+      chunk_of(lr, j, col0, lo, hi);
+      if (lo >= hi || (lo == col0 && hi == col0 + VO)) continue;
+      OT e[VO];
+#pragma unroll
+      for (int x = 0; x < VO; ++x) {
+        const int64_t col = col0 + x;
+        const uint32_t off = col >= lo && col < hi ? cdelta + (uint32_t)((row * p.c_sm + col) * OSZ)
+                                                   : kOobOffset;
+        if constexpr (OSZ == 2) e[x] = (OT)__builtin_amdgcn_raw_buffer_load_b16(cr, off, 0, 0);
+        else e[x] = (OT)__builtin_amdgcn_raw_buffer_load_b32(cr, off, 0, 0);
+      }
+      *reinterpret_cast<u32x4*>(&tile[lr * PITCH + j * VO]) = *reinterpret_cast<const u32x4*>(e);
+    }
+    __syncthreads();
+  }
   // The stages run one row block of atoms (acc[i][*]) at a time, so only that block's values
   // are live in VGPRs; within a block each stage is one straight-line pass entered on a uniform
   // condition, so the common case (no C) carries no per-element branches:
@@ -1131,7 +1226,18 @@ __device__ __forceinline__ void epilogue(const KParams& p, AccT (&acc)[RM][RN], 
       });
     }
     if (has_cs) each([&](auto j, auto r) { acc[i][j][(int)r] *= cs_v[j]; });
-    if (has_c && p.c_span > 0) {
+    if (c_lds) {
+      // (two forms, so that aligned rows carry no per-element shift arithmetic)
+      auto get_c = [&](auto SH) {
+        each([&](auto j, auto r) {
+          const int lc = wn * WTN + j * MI + acol;
+          const int lr = wm * WTM + i * MI + acc_row<DT, MI>(lane, r);
+          const int pos = lr * PITCH + lc + (SH ? mis_raw(m0 + lr) : 0);
+          acc[i][j][(int)r] += beta * O::from_bits((u32)tile[pos]);
+        });
+      };
+      if (shifted) get_c(std::true_type{}); else get_c(std::false_type{});
+    } else if (has_c && p.c_span > 0) {
       const __amdgpu_buffer_rsrc_t cr = make_rsrc((const char*)p.C, p.c_span);
       each([&](auto j, auto r) {
         const int64_t col = n0 + wn * WTN + j * MI + acol;
@@ -1152,44 +1258,67 @@ __device__ __forceinline__ void epilogue(const KParams& p, AccT (&acc)[RM][RN], 
     if (act == 2) each([&](auto j, auto r) { acc[i][j][(int)r] = gelu(acc[i][j][(int)r]); });
     else if (act == 1) each([&](auto j, auto r) { acc[i][j][(int)r] = relu(acc[i][j][(int)r]); });
     else if (act == 3) each([&](auto j, auto r) { acc[i][j][(int)r] = silu(acc[i][j][(int)r]); });
-    static_for<RN>([&](auto j) {
-      const int lc = wn * WTN + j * MI + acol;
-      const int64_t col = n0 + lc;
-      static_for<At::NACC>([&](auto r) {
-        const int lr = wm * WTM + i * MI + acc_row<DT, MI>(lane, r);
-        const float v = acc[i][j][(int)r];
-        if constexpr (REPACK) {
-          tile[lr * PITCH + lc] = to_bits(v, std::integral_constant<int, ODT>{});
-        } else {
-          const int64_t row = m0 + lr;
-          if (col < p.N && row < p.M) O::store(p.D, row * p.d_sm + col * p.d_sn, v);
-        }
+    auto put = [&](auto SH) {
+      static_for<RN>([&](auto j) {
+        const int lc = wn * WTN + j * MI + acol;
+        const int64_t col = n0 + lc;
+        static_for<At::NACC>([&](auto r) {
+          const int lr = wm * WTM + i * MI + acc_row<DT, MI>(lane, r);
+          const float v = acc[i][j][(int)r];
+          if constexpr (REPACK) {
+            const int pos = lr * PITCH + lc + (SH ? mis_raw(m0 + lr) : 0);
+            tile[pos] = to_bits(v, std::integral_constant<int, ODT>{});
+          } else {
+            const int64_t row = m0 + lr;
+            if (col < p.N && row < p.M) O::store(p.D, row * p.d_sm + col * p.d_sn, v);
+          }
+        });
       });
-    });
+    };
+    if (shifted) put(std::true_type{}); else put(std::false_type{});
   });
   if constexpr (REPACK) {
     __syncthreads();
-    constexpr int VO = 16 / OSZ;            // outputs per 16-byte chunk
-    constexpr int CPR = BN / VO;            // chunks per tile row
     constexpr int NCH = BM * CPR;
     static_assert(NCH % NT == 0, "output chunks must divide over the threads");
-    const bool vec_ok = p.d_sn == 1 && (p.d_sm * OSZ) % 16 == 0 &&
-                        (reinterpret_cast<uintptr_t>(p.D) % 16) == 0;
     OT* dst = reinterpret_cast<OT*>(p.D);
+    if (shifted) {
+      // shifted rows: one aligned 16-byte store per whole chunk of D's grid
+      constexpr int ITER = (BM * CPRS + NT - 1) / NT;
 #pragma unroll
-    for (int it = 0; it < NCH / NT; ++it) {
-      const int q = tid + it * NT;
-      const int lr = q / CPR, lc = (q % CPR) * VO;
-      const int64_t row = m0 + lr, col = n0 + lc;
-      if (row >= p.M) continue;
-      const u32x4 val = *reinterpret_cast<const u32x4*>(&tile[lr * PITCH + lc]);
-      if (vec_ok && col + VO <= p.N) {
-        *reinterpret_cast<u32x4*>(dst + row * p.d_sm + col) = val;
-      } else {
-        const OT* e = reinterpret_cast<const OT*>(&val);
+      for (int it = 0; it < ITER; ++it) {
+        const int q = tid + it * NT;
+        const int lr = q / CPRS, j = q - lr * CPRS;
+        const int64_t row = m0 + lr;
+        int64_t col0, lo, hi;
+        chunk_of(lr, j, col0, lo, hi);
+        if (q >= BM * CPRS || row >= p.M || lo >= hi) continue;
+        const u32x4 val = *reinterpret_cast<const u32x4*>(&tile[lr * PITCH + j * VO]);
+        if (lo == col0 && hi == col0 + VO) {
+          *reinterpret_cast<u32x4*>(dst + row * p.d_sm + col0) = val;
+        } else {
+          const OT* e = reinterpret_cast<const OT*>(&val);
 #pragma unroll
-        for (int x = 0; x < VO; ++x)
-          if (col + x < p.N) dst[row * p.d_sm + (col + x) * p.d_sn] = e[x];
+          for (int x = 0; x < VO; ++x)
+            if (col0 + x >= lo && col0 + x < hi) dst[row * p.d_sm + col0 + x] = e[x];
+        }
+      }
+    } else {
+#pragma unroll
+      for (int it = 0; it < NCH / NT; ++it) {
+        const int q = tid + it * NT;
+        const int lr = q / CPR, lc = (q % CPR) * VO;
+        const int64_t row = m0 + lr, col = n0 + lc;
+        if (row >= p.M) continue;
+        const u32x4 val = *reinterpret_cast<const u32x4*>(&tile[lr * PITCH + lc]);
+        if (vec_ok && col + VO <= p.N) {
+          *reinterpret_cast<u32x4*>(dst + row * p.d_sm + col) = val;
+        } else {
+          const OT* e = reinterpret_cast<const OT*>(&val);
+#pragma unroll
+          for (int x = 0; x < VO; ++x)
+            if (col + x < p.N) dst[row * p.d_sm + (col + x) * p.d_sn] = e[x];
+        }
       }
     }
     if (p.rsq_ws) {
