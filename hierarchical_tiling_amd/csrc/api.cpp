@@ -722,20 +722,20 @@ int run_impl(gemm_t h, const void* A, const void* B, const void* C, void* D, con
                           h->kp == d.K && aligned(A, 16);
     const bool b_direct = h->b.kmajor && (h->b.ld * (int64_t)in_sz) % 16 == 0 && h->b.ld >= d.K &&
                           h->kp == d.K && aligned(B, 16);
-    hipError_t err = hipSuccess;
+    // both copies in one launch where the pair kernel can take them
+    const hipError_t err = launch_repack_pair(
+        a_direct ? nullptr : A, ws, d.M, d.a_stride_m, d.a_stride_k, b_direct ? nullptr : B,
+        ws + h->repack_bytes_a, d.N, d.b_stride_n, d.b_stride_k, d.K, h->kp, (int)in_sz,
+        (hipStream_t)stream);
+    if (err != hipSuccess) return GEMM_ERR_LAUNCH;
     if (!a_direct) {
-      err = launch_repack(A, ws, d.M, d.K, h->kp, d.a_stride_m, d.a_stride_k, (int)in_sz,
-                          (hipStream_t)stream);
       Ae = ws;
       lda = h->kp;
     }
-    if (err == hipSuccess && !b_direct) {
-      err = launch_repack(B, ws + h->repack_bytes_a, d.N, d.K, h->kp, d.b_stride_n, d.b_stride_k,
-                          (int)in_sz, (hipStream_t)stream);
+    if (!b_direct) {
       Be = ws + h->repack_bytes_a;
       ldb = h->kp;
     }
-    if (err != hipSuccess) return GEMM_ERR_LAUNCH;
     Ke = h->kp;
     workspace = ws + h->repack_bytes_a + h->repack_bytes_b;
   }

@@ -116,6 +116,12 @@ hipError_t launch_row_sumsq_reduce(const float* ws, float* out, int64_t M, int t
 // src(r, k) (element offset r * s_row + k * s_k) for k < K, 0 for K <= k < Kp (repack.hip).
 hipError_t launch_repack(const void* src, void* dst, int64_t rows, int64_t K, int64_t Kp,
                          int64_t s_row, int64_t s_k, int esize, hipStream_t s);
+// The copies of both operands of a product (a NULL source skips that operand), in one launch
+// when both are 2-byte copies the pair kernel takes, else one launch_repack each.
+hipError_t launch_repack_pair(const void* a_src, void* a_dst, int64_t a_rows, int64_t a_srow,
+                              int64_t a_sk, const void* b_src, void* b_dst, int64_t b_rows,
+                              int64_t b_srow, int64_t b_sk, int64_t K, int64_t Kp, int esize,
+                              hipStream_t s);
 
 // Grouped launches: from the caller's G + 1 device row offsets, the effective offsets lo[0..G]
 // (clamped into [0, M] and made non-decreasing) and the first tile of each group base[0..G]

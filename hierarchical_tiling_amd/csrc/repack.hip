@@ -55,9 +55,9 @@ __global__ __launch_bounds__(256) void gemm_repack_kernel(const RepackParams p) 
 // 2-byte elements, K-contiguous source at any element alignment: each thread writes one 16-byte
 // chunk of dst from the realigned 16 bytes (plus the next dword) of the source row, elements at
 // k >= K cleared; no LDS.  The descriptor spans the whole source rounded up to a dword.
-__global__ __launch_bounds__(256) void gemm_repack_rows16(const RepackParams p) {
+__device__ __forceinline__ void repack_rows16(const RepackParams& p, int64_t bx) {
   const int64_t cpr = p.Kp / 8;                              // chunks per dst row
-  const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t q = bx * 256 + threadIdx.x;
   if (q >= p.rows * cpr) return;
   const int64_t r = q / cpr, c = q - r * cpr;
   const char* base = (const char*)((uintptr_t)p.src & ~uintptr_t(3));
@@ -70,14 +70,18 @@ __global__ __launch_bounds__(256) void gemm_repack_rows16(const RepackParams p) 
   const Raw16 w = raw16(rsrc, emask ? (off & ~3u) : kOobOffset);
   *(u32x4*)((char*)p.dst + (r * p.Kp + k) * 2) = realign16(w, off & 2u, emask);
 }
+__global__ __launch_bounds__(256) void gemm_repack_rows16(const RepackParams p) {
+  repack_rows16(p, blockIdx.x);
+}
 
 // 2-byte elements, row-contiguous source (element (r, k) at r + k * s_k) at any alignment: a
 // 64 (k) x 64 (r) tile is read as realigned 16-byte chunks of 8 consecutive r at one k, written
 // into LDS transposed (element by element), and stored as 16-byte chunks of dst rows.
-__global__ __launch_bounds__(256) void gemm_repack_cols16(const RepackParams p) {
-  constexpr int TILE = 64, PITCH = TILE + 2;  // LDS row = one r, TILE k values
-  __shared__ uint16_t tile[TILE][PITCH];
-  const int64_t r0 = (int64_t)blockIdx.y * TILE, k0 = (int64_t)blockIdx.x * TILE;
+constexpr int kColsTile = 64, kColsPitch = kColsTile + 2;  // LDS row = one r, 64 k values
+__device__ __forceinline__ void repack_cols16(const RepackParams& p, int64_t bx, int64_t by,
+                                              uint16_t (*tile)[kColsPitch]) {
+  constexpr int TILE = kColsTile;
+  const int64_t r0 = by * TILE, k0 = bx * TILE;
   const char* base = (const char*)((uintptr_t)p.src & ~uintptr_t(3));
   const uint32_t delta = (uint32_t)((const char*)p.src - base);
   const int64_t ext = (delta + ((p.K - 1) * p.s_k + p.rows) * 2 + 3) & ~int64_t(3);
@@ -108,6 +112,68 @@ __global__ __launch_bounds__(256) void gemm_repack_cols16(const RepackParams p) 
     for (int d = 0; d < 4; ++d) v[d] = (u32)tile[r][c * 8 + 2 * d] | ((u32)tile[r][c * 8 + 2 * d + 1] << 16);
     *(u32x4*)((char*)p.dst + (gr * p.Kp + gk) * 2) = v;
   }
+}
+__global__ __launch_bounds__(256) void gemm_repack_cols16(const RepackParams p) {
+  __shared__ uint16_t tile[kColsTile][kColsPitch];
+  repack_cols16(p, blockIdx.x, blockIdx.y, tile);
+}
+
+// Both operands of a product in one launch (2-byte elements, each source K- or row-contiguous):
+// workgroups [0, na) copy the first operand, the rest the second, so the two copies share the
+// GPU instead of running one after the other.  kind 0: realigned row copy (K-contiguous source),
+// 1: LDS transpose (row-contiguous source).
+struct RepackJob {
+  RepackParams p;
+  int kind;
+  int64_t gx;      // workgroups along K (transposes: the grid's x extent)
+  int64_t blocks;  // workgroups of this job
+};
+__global__ __launch_bounds__(256) void gemm_repack_pair16(const RepackJob a, const RepackJob b) {
+  __shared__ uint16_t tile[kColsTile][kColsPitch];
+  const int64_t x = blockIdx.x;
+  const bool first = x < a.blocks;
+  const RepackJob& j = first ? a : b;
+  const int64_t l = first ? x : x - a.blocks;
+  if (j.kind == 0) repack_rows16(j.p, l);
+  else repack_cols16(j.p, l % j.gx, l / j.gx, tile);
+}
+
+namespace {
+// The pair kernel's job for one operand, or kind -1 when it needs the generic copy.
+RepackJob job16(const void* src, void* dst, int64_t rows, int64_t K, int64_t Kp, int64_t s_row,
+                int64_t s_k) {
+  RepackJob j{{src, dst, rows, K, Kp, s_row, s_k}, -1, 0, 0};
+  const bool kc = s_k == 1;
+  const int64_t span = kc ? (rows - 1) * s_row + K : (K - 1) * s_k + rows;
+  if (rows <= 0 || Kp <= 0 || span * 2 >= (int64_t(1) << 31) - 64) return j;
+  if (kc) {
+    j.kind = 0;
+    j.blocks = (rows * (Kp / 8) + 255) / 256;
+  } else if (s_row == 1) {
+    j.kind = 1;
+    j.gx = (Kp + 63) / 64;
+    j.blocks = j.gx * ((rows + 63) / 64);
+  }
+  return j;
+}
+}  // namespace
+
+hipError_t launch_repack_pair(const void* a_src, void* a_dst, int64_t a_rows, int64_t a_srow,
+                              int64_t a_sk, const void* b_src, void* b_dst, int64_t b_rows,
+                              int64_t b_srow, int64_t b_sk, int64_t K, int64_t Kp, int esize,
+                              hipStream_t s) {
+  if (esize == 2) {
+    const RepackJob a = a_src ? job16(a_src, a_dst, a_rows, K, Kp, a_srow, a_sk) : RepackJob{{}, 0, 1, 0};
+    const RepackJob b = b_src ? job16(b_src, b_dst, b_rows, K, Kp, b_srow, b_sk) : RepackJob{{}, 0, 1, 0};
+    if (a.kind >= 0 && b.kind >= 0 && a.blocks + b.blocks > 0) {
+      hipLaunchKernelGGL(gemm_repack_pair16, dim3((unsigned)(a.blocks + b.blocks)), dim3(256), 0, s, a, b);
+      return hipGetLastError();
+    }
+  }
+  hipError_t err = hipSuccess;
+  if (a_src) err = launch_repack(a_src, a_dst, a_rows, K, Kp, a_srow, a_sk, esize, s);
+  if (err == hipSuccess && b_src) err = launch_repack(b_src, b_dst, b_rows, K, Kp, b_srow, b_sk, esize, s);
+  return err;
 }
 
 hipError_t launch_repack(const void* src, void* dst, int64_t rows, int64_t K, int64_t Kp,
