@@ -119,3 +119,31 @@ def test_heuristic_stream_k_other_types(case):
     print(f"{case.dtype} {case.M}x{case.N}x{case.K}: {info.name.decode()} sk {info.sk_tiles}: "
           f"{what} err={err:.3e}")
     assert err <= TOL[case.dtype], err
+
+
+def test_stream_k_with_scale_vectors():
+    # both scale vectors and SiLU through the Stream-K pieces and the fix-up's epilogue
+    c = Case(1000, 1300, 1000, "bf16", bias=True, act="silu", row_scale=True, col_scale=True,
+             seed=312, force=_index(RING["bf16"]), decomposition=2)
+    p = Prepared(c)
+    g, out = p.run()
+    assert g.info.sk_tiles == 24
+    got, _ = p.decode_out(out)
+    err = error("bf16", got, p.oracle_full())
+    print(f"Stream-K with scale vectors: err={err:.3e}")
+    assert err <= TOL["bf16"], err
+
+
+def test_stream_k_on_repacked_operands():
+    # odd leading dimensions and K: aligned copies of A and B, then Stream-K over the last round
+    # of 18 x 18 = 324 ring tiles (68 left) of 65 k-tiles
+    c = Case(4353, 4353, 4097, "f16", b_order="row", has_c=True, beta=0.5, seed=313)
+    p = Prepared(c)
+    g, out = p.run()
+    info = g.info
+    assert info.repack == 1 and info.sk_tiles == 68, (info.repack, info.sk_tiles)
+    got, _ = p.decode_out(out)
+    have, want, what = p.oracle_sample(got, seed=13)
+    err = error("f16", have, want)
+    print(f"f16 4353^2 x 4097 repack + Stream-K: {what} err={err:.3e}")
+    assert err <= TOL["f16"], err
