@@ -216,6 +216,45 @@ def test_in_place_d_equals_c():
     assert error("bf16", got, want) <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("force,dtype", [("bf16_ak_bk_256x256x64_w2x4_m16_ring", "bf16"),
+                                         ("f16_ak_bk_64x64x64_w2x2_m16_vec", "f16"),
+                                         ("f32_ak_bk_64x64x32_w2x2_m16_vec", "f32")])
+def test_c_and_d_bases_off_16_bytes(force, dtype):
+    # C and D start 3 and 1 elements past a 16-byte boundary with padded leading dimensions that
+    # keep every row off the grid as well: C is staged and D stored in D's own 16-byte grid
+    names = [H.gemm_config_name(i) for i in range(H.gemm_num_configs())]
+    M, N, K = 300, 520, 256
+    c = Case(M, N, K, dtype, has_c=True, beta=-0.75, alpha=1.25, bias=True, c_ld=N + 5,
+             dist="uniform" if dtype == "f32" else "normal", seed=17, force=names.index(force))
+    p = Prepared(c)
+    want = p.oracle_full()
+    ot = OUT_T[dtype]
+    es = {"f32": 4, "f16": 2, "bf16": 2}[ot]
+    d_ld = N + 3
+    c_host = p.C.storage
+    c_buf = torch.zeros((c_host.size + 8) * es, dtype=torch.uint8, device="cuda")
+    c_buf[3 * es:3 * es + c_host.size * es] = torch.from_numpy(c_host.view(np.uint8)).to("cuda")
+    sentinel = oracle.encode_rne(ot, np.array([np.nan]))[0]
+    d_host = np.full(M * d_ld + 16, sentinel, dtype=c_host.dtype)
+    d_buf = torch.from_numpy(d_host.view(np.uint8)).to("cuda")
+    desc = p.desc()
+    desc.d_stride_m, desc.d_stride_n = d_ld, 1
+    g = H.Gemm(desc)
+    assert g.info.name.decode() == force
+    g.run(p.dA[0].data_ptr(), p.dB, c_buf.data_ptr() + 3 * es, d_buf.data_ptr() + es, p.dbias,
+          alpha=c.alpha, beta=c.beta)
+    torch.cuda.synchronize()
+    bits = d_buf.cpu().numpy().view(c_host.dtype)[1:]
+    r = np.arange(M)[:, None] * d_ld + np.arange(N)[None, :]
+    inside = np.zeros(bits.size, dtype=bool)
+    inside[r.ravel()] = True
+    assert (bits[~inside] == sentinel).all(), "a write outside D's rows"
+    got = oracle.decode(ot, bits[r])
+    err = error(dtype, got, want)
+    print(f"{force}: err={err:.3e}")
+    assert err <= TOL[dtype], err
+
+
 def test_repeated_runs_are_bitwise_identical():
     c = Case(1024, 768, 512, "bf16", bias=True, act="gelu", seed=16)
     p = Prepared(c)
