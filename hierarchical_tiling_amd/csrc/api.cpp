@@ -1040,6 +1040,8 @@ extern "C" {
 int gemm_run_noalloc(gemm_t h, const gemm_args* a, void* stream) {
   if (!h || h->magic != kMagic) return GEMM_ERR_BAD_HANDLE;
   if (!a || a->workspace) return GEMM_ERR_INVALID_ARG;  // the library supplies the scratch
+  // grouped handles run through their own entry points
+  if (h->d.ragged_m || h->d.grouped) return GEMM_ERR_INVALID_ARG;
   size_t need = 0;
   int rc = gemm_workspace_size(h, &need);
   if (rc) return rc;
@@ -1049,7 +1051,6 @@ int gemm_run_noalloc(gemm_t h, const gemm_args* a, void* stream) {
     rc = scratch_address(&ws);
     if (rc) return rc;
   }
-  if (h->d.ragged_m) return GEMM_ERR_INVALID_ARG;  // grouped handles run through gemm_run_grouped
   return run_impl(h, a->A, a->B, a->C, a->D, a->bias, a->row_scale, a->col_scale, a->alpha,
                   a->beta, a->scale_a, a->scale_b, ws, nullptr, a->row_sumsq, a->col_sum, stream);
 }

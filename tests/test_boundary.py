@@ -341,6 +341,9 @@ def test_grouped_problems_fields(fake_gfx950):
         assert rc([good], a=beta) == H.GEMM_ERR_INVALID_ARG             # beta without C
         # the other entry points refuse a grouped handle, and this one any other handle
         assert lib.gemm_run(h, 256, 256, None, 256, None, 1.0, 0.0, 1.0, 1.0, None, None) == 1
+        plain_args = H.gemm_args(256, 256, None, 256, None, None, None, 1.0, 0.0, 1.0, 1.0, None)
+        assert lib.gemm_run_ex(h, ctypes.byref(plain_args), None) == 1
+        assert lib.gemm_run_noalloc(h, ctypes.byref(plain_args), None) == 1
         plain = H.gemm_create(desc())
         try:
             assert rc([good], handle=plain) == H.GEMM_ERR_INVALID_ARG

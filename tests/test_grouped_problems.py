@@ -191,3 +191,39 @@ def test_grouped_problems_run_twice_with_fewer_problems():
             got = oracle.decode("f16", outs[i].cpu().numpy().view(np.uint16)).reshape(M, N)
             want = oracle.gemm(op(A), op(B), None, None, threads=THREADS)
             assert error(dt, got, want) <= TOL[dt], (count, i)
+
+
+def test_grouped_problems_many_small():
+    """1,500 problems of 0..40 rows and columns: the binary search over the problems' first tiles
+    and the table copy at a size where most workgroups belong to problems deep in the table."""
+    rng = np.random.default_rng(77)
+    G = 1500
+    shapes = [(int(m), int(n), 32) for m, n in zip(rng.integers(0, 41, G), rng.integers(0, 41, G))]
+    dt, ot = "bf16", "bf16"
+    A_all = inputs.matrix(7000, sum(m for m, _, _ in shapes) + 1, 32, dt, "dyadic", order="row")
+    B_all = inputs.matrix(7001, 32, 40 * G, dt, "dyadic", order="col")
+    dA, dB = inputs.to_device(A_all), inputs.to_device(B_all)
+    D = torch.zeros(sum(m * n for m, n, _ in shapes) + 8, dtype=torch.int16, device="cuda")
+    probs, where, r0, d0 = [], [], 0, 0
+    for e, (m, n, k) in enumerate(shapes):
+        probs.append(dict(M=m, N=n, K=k, A=dA.data_ptr() + r0 * 32 * 2,
+                          B=dB.data_ptr() + e * 40 * 32 * 2, D=D.data_ptr() + d0 * 2,
+                          lda=32, ldb=32, ldd=max(n, 1)))
+        where.append((r0, e * 40, d0))
+        r0 += m
+        d0 += m * n
+    g = H.Gemm(H.make_desc(32, 32, 32, dt, (32, 1), (1, 32), (32, 1), batch=G, grouped=True))
+    ws = torch.empty(g.workspace_bytes, dtype=torch.uint8, device="cuda")
+    H.gemm_run_problems(g.handle, probs, 1.0, 0.0, workspace=ws.data_ptr())
+    torch.cuda.synchronize()
+    bits = D.cpu().numpy().view(np.uint16)
+    bad = 0
+    for (m, n, k), (ra, cb, dd) in zip(shapes, where):
+        if m == 0 or n == 0:
+            continue
+        A_e = oracle.Operand(A_all.storage[ra * 32:], dt, (m, 32), (32, 1))
+        B_e = oracle.Operand(B_all.storage[cb * 32:], dt, (32, n), (1, 32))
+        want = oracle.gemm(A_e, B_e, None, None, threads=1)
+        # dyadic inputs: every sum is exact, so the stored bits are unique
+        bad += int((bits[dd:dd + m * n] != oracle.encode_rne(ot, want).ravel()).sum())
+    assert bad == 0
