@@ -337,7 +337,7 @@ def main():
                     help="only run 5 plain device copies of 1 GiB (counter calibration) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        print(json.dumps({"error": "the library runs on one GPU; --gpus must be 1"}))
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()

@@ -13,10 +13,10 @@ from hierarchical_tiling_amd import htgemm as H
 from hierarchical_tiling_amd import inputs
 
 OUT_T = {"f32": "f32", "f16": "f16", "bf16": "bf16", "e4m3": "bf16"}
-# host threads for the oracle: every core this process may use, at most 16 (a GPU machine gives a
-# one-GPU job 16 CPU threads whatever the machine's core count)
+# host threads for the oracle: every core this process may use, at most 16 (the host threads that
+# go with one GPU on an 8-GPU MI355X machine, whatever its core count)
 THREADS = max(1, min(16, len(os.sched_getaffinity(0))))
-# spec tolerances: fp32 relative Frobenius; 16-bit max-abs-relative; fp8 max-abs-relative
+# tolerances: fp32 relative Frobenius; 16-bit max-abs-relative; fp8 max-abs-relative
 TOL = {"f32": 1e-5, "f16": 1e-2, "bf16": 1e-2, "e4m3": 3e-2}
 
 
@@ -222,7 +222,7 @@ def _gather(m, rows, cols):
 
 
 def error(dtype, got, want):
-    """The benchmark spec's metric for `dtype`: relative Frobenius (fp32) or max-abs-relative."""
+    """The error metric for `dtype`: relative Frobenius (fp32) or max-abs-relative."""
     got = np.asarray(got, dtype=np.float64)
     want = np.asarray(want, dtype=np.float64)
     if dtype == "f32":

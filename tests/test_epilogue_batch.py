@@ -6,7 +6,7 @@
 * A batch of L problems of one shape in one call ("CUTLASS, CuTe, and CUDA Tile", "Assembling a
   CUTLASS kernel": the problem shape [M, N, K, L]).
 
-Tolerances are the spec ones (see test_gemm_parity); dyadic inputs with power-of-two scales
+Tolerances as in test_gemm_parity; dyadic inputs with power-of-two scales
 must match the oracle bit for bit.
 """
 import numpy as np

@@ -1,6 +1,6 @@
 """GPU parity: the HIP library (through its C ABI) against the CPU oracle on the same seeded bits.
 
-Tolerances are the spec ones: fp32 relative Frobenius <= 1e-5; bf16/fp16 max-abs-relative
+Tolerances: fp32 relative Frobenius <= 1e-5; bf16/fp16 max-abs-relative
 <= 1e-2; fp8 <= 3e-2 (max-abs-relative = max|D - O| / max|O|, with O the unrounded double
 oracle).  Dyadic inputs (multiples of 1/4, exact in every operand type) make every fp32 partial
 sum exact, so there the rounded result must match the oracle bit for bit in any summation order.
