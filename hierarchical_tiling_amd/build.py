@@ -34,6 +34,7 @@ SOURCES = [
     ("table_e4m3.hip", HIP),
     ("table_f32.hip", HIP),
     ("table.cpp", HIP),
+    ("cost_table.cpp", HIP),
     ("reduce.hip", HIP),
     ("probe.hip", HIP),
     ("repack.hip", HIP),

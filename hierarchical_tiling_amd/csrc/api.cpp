@@ -11,8 +11,10 @@
 
 #include <algorithm>
 #include <atomic>
+#include <cmath>
 #include <cstdlib>
 #include <cstring>
+#include <limits>
 #include <mutex>
 #include <new>
 #include <utility>
@@ -54,6 +56,7 @@ struct gemm_handle_s {
   int tail_tiles, tail_split;  // split tail of the cfg entry (tail_split 1: none)
   int64_t tail_kps;            // K elements per slice of a tail tile
   int sk_tiles;                // Stream-K tiles of the cfg entry (0: none)
+  double predicted_us;         // the cost model's time of one run (0: no measured costs)
   // Repack plan: A and B are read through K-major, 16-byte aligned copies of K padded to kp
   // (zeros past K) at the start of the workspace (A' then B', each rounded to 256 bytes), and
   // cfg is the entry chosen for that aligned problem.  An operand that is already K-major with
@@ -129,32 +132,92 @@ int col_sum_row_groups(const KernelEntry& e) {
   return e.waves >= cg ? e.waves / cg : 1;
 }
 
-// Split along K for entry e: S slices of whole k-tiles ("CUTLASS", Part III: split-K restores
-// occupancy when the output has too few tiles).  req > 1 forces S (at most one slice per
-// k-tile); req == 1 never splits; req == 0 (automatic) splits an output of fewer than 256 tiles
-// when K is long (at least 64 k-tiles) into enough slices for about 256 workgroups, at most 16,
-// each slice keeping at least 8 k-tiles.
+// ---- cost model ----------------------------------------------------------------------------
+// The kernel choice and the split plan predict run times from each entry's measured costs
+// (EntryCost; "CUTLASS", stanleyjacob.dev, Part IX: the best tile depends on the problem, so the
+// library is measured rather than guessed).  launch_us is a launch of wg workgroups of kt k-tiles
+// each.  Whole loads n (n workgroups on every CU) take the measured time; a load above 8 adds
+// whole groups of 8; a partly filled last round costs the step to the next whole load, scaled as
+// a round with that fraction of the CUs busy (piecewise linear over the loads 1/4, 1/2, 3/4, 1).
+double launch_us(const EntryCost& c, int64_t wg, int64_t kt) {
+  if (wg <= 0 || kt <= 0) return 0.0;
+  static constexpr double kPart[kCostLoadOne + 1] = {0.25, 0.5, 0.75, 1.0};
+  auto at = [&](int i) { return double(c.f[i]) + double(kt) * double(c.c[i]); };
+  auto whole = [&](int64_t n) {
+    if (n <= 0) return 0.0;
+    const int64_t g = (n - 1) / 8;
+    return double(g) * at(kCostLoads - 1) + at(int(n - 8 * g) + kCostLoadOne - 1);
+  };
+  auto part = [&](double w) {
+    double t = at(0);
+    if (w > kPart[0]) {
+      int i = 1;
+      while (kPart[i] < w) ++i;
+      t = at(i - 1) + (w - kPart[i - 1]) / (kPart[i] - kPart[i - 1]) * (at(i) - at(i - 1));
+    }
+    return t / at(kCostLoadOne);
+  };
+  const int64_t n = cdiv(wg, kCUs);
+  const double w = double(wg - (n - 1) * kCUs) / kCUs;
+  const double lo = whole(n - 1), hi = whole(n);
+  return lo + (hi - lo) * part(w);
+}
+
+// The sum kernel of a split: partial_bytes of fp32 partials (written by the first kernel and read
+// by the second) and out_bytes of output.
+double reduce_us(double partial_bytes, double out_bytes) {
+  return kSplitFixedUs + kSplitUsPerByte * (2.0 * partial_bytes + out_bytes);
+}
+
+// Output tiles of entry e over d: all problems of a batch, or a grouped launch's tiles (each group
+// may start a tile row of its own).
+int64_t tiles_of(const KernelEntry& e, const gemm_desc& d) {
+  const int64_t groups = d.batch > 1 ? d.batch : 1;
+  if (d.ragged_m) return (cdiv(d.M, e.bm) + groups) * cdiv(d.N, e.bn);
+  return cdiv(d.M, e.bm) * cdiv(d.N, e.bn) * (d.grouped ? 1 : groups);
+}
+
 // An entry whose LDS leaves no room for a second workgroup runs one per CU: 256 make a round.
 bool one_per_cu(const KernelEntry& e) { return 2 * int64_t(e.lds_bytes) > kLdsBudget; }
 
+// Split along K for entry e: S slices of whole k-tiles ("CUTLASS", Part III: split-K restores
+// occupancy when the output has too few tiles).  req > 1 forces S (at most one slice per
+// k-tile); req == 1 never splits; req == 0 (automatic) considers splitting an output of fewer
+// than 256 tiles into at most 16 slices and takes the count with the least predicted time: the
+// launch of tiles x S workgroups plus the sum kernel.  With the measured costs the choice keeps
+// what was found by hand on MI355X: bf16 1536^2 x 8192 runs on the ring in 7 slices (252
+// workgroups; 8 would start a second round), and bf16 2048^2 x 4096 unsplit on 128 x 128 tiles
+// (0.048 ms, against 0.055 ms in 4 ring slices).  An entry without measured costs is not split
+// unless forced.
 void plan_split(const KernelEntry& e, const gemm_desc& d, int req, int* S, int64_t* kps) {
   *S = 1;
   *kps = d.K;
   if (req == 1 || e.max_split_k <= 1 || d.K == 0) return;
   const int64_t tiles = cdiv(d.M, e.bm) * cdiv(d.N, e.bn);
   const int64_t nkt = cdiv(d.K, e.bk);
-  int64_t s = req;
-  if (req == 0) {
-    if (tiles >= 256 || nkt < 64) return;
-    // slices that fill one round: for one workgroup per CU no more than 256 / tiles (one more
-    // would start a second round: 1536^2 x 8192 ring, 8 slices 0.082 ms, 7 slices 0.060 ms)
-    s = std::min<int64_t>({one_per_cu(e) ? 256 / tiles : cdiv(256, tiles), nkt / 8, 16});
+  if (req > 1) {
+    const int64_t s = std::min<int64_t>({(int64_t)req, nkt, (int64_t)e.max_split_k});
+    if (s <= 1) return;
+    const int64_t per = cdiv(nkt, s);  // k-tiles per slice
+    *kps = per * e.bk;
+    *S = (int)cdiv(nkt, per);           // no empty slice
+    return;
   }
-  s = std::min<int64_t>({s, nkt, (int64_t)e.max_split_k});
-  if (s <= 1) return;
-  const int64_t per = cdiv(nkt, s);  // k-tiles per slice
-  *kps = per * e.bk;
-  *S = (int)cdiv(nkt, per);           // no empty slice
+  if (tiles >= kCUs || !e.cost) return;
+  const double out_bytes = double(d.M) * double(d.N) * dtype_size(d.d_type);
+  double best = launch_us(*e.cost, tiles, nkt);
+  const int64_t smax = std::min<int64_t>({nkt, (int64_t)e.max_split_k, 16});
+  for (int64_t s = 2; s <= smax; ++s) {
+    const int64_t per = cdiv(nkt, s);
+    if (cdiv(nkt, per) != s) continue;  // the same slices as a smaller count
+    const double t = launch_us(*e.cost, tiles * s, per) +
+                     reduce_us(4.0 * double(s) * double(d.M) * double(d.N), out_bytes);
+    if (t < best) {
+      best = t;
+      *S = (int)s;
+      *kps = per * e.bk;
+    }
+  }
 }
 
 // Split tail (the data-parallel plus split-K hybrid of Stream-K scheduling; "CUTLASS", Part III:
@@ -221,83 +284,119 @@ void plan_sk(const KernelEntry& e, const gemm_desc& d, int split_req, int split_
   *sk_tiles = (int)(tiles <= kCUs ? tiles : (rem == 0 ? kCUs : rem));
 }
 
-// Heuristic choice among fitting entries.  A product with M <= 16 is bound by streaming B and
-// takes the skinny kernel when one fits.  Otherwise each entry is counted with the split-K plan
-// it would get (plan_split) and the choice is the largest tile whose workgroups (tiles x slices)
-// still fill the GPU (at least 256, or over 128 for a one-per-CU or realigned 128 x 128 tile), ties
-// broken by the measured rank -- the entry's one-round rank when all its workgroups run at once
-// (at most 256), else its rank -- or, when no tile fills it, the entry with the most
-// workgroups (ties: larger tile, then rank).  A forced split (split_req > 1) admits only entries
-// that can split.
-int choose(const gemm_handle_s& h, bool vec_a, bool vec_b, bool want_vec, int split_req) {
+// An entry's plan for a problem: its split, Stream-K tiles or split tail, and the predicted time
+// of a run (infinite for an entry without measured costs).
+struct Plan {
+  int S = 1;                    // K slices of the whole problem
+  int64_t kps = 0;              // K elements per slice
+  int sk_tiles = 0;             // tiles run Stream-K
+  int tail_R = 0, tail_S = 1;   // split tail: tiles, and slices of each
+  int64_t tail_kps = 0;
+  double us = 0.0;
+};
+
+Plan make_plan(const KernelEntry& e, const gemm_desc& d, int split_req) {
+  Plan p;
+  plan_split(e, d, split_req, &p.S, &p.kps);
+  plan_sk(e, d, split_req, p.S, &p.sk_tiles);
+  plan_tail(e, d, p.sk_tiles > 0 ? 1 : split_req, p.S, &p.tail_R, &p.tail_S, &p.tail_kps);
+  if (!e.cost) {
+    p.us = std::numeric_limits<double>::infinity();
+    return p;
+  }
+  const EntryCost& c = *e.cost;
+  const int64_t tiles = tiles_of(e, d);
+  const int64_t nkt = cdiv(d.K, e.bk);
+  const double tile_out = double(e.bm) * e.bn, osz = dtype_size(d.d_type);
+  // edges: a partial last k-tile in every tile, partial last tile rows or columns, and D rows
+  // that the epilogue cannot store as whole aligned 16-byte chunks (with a base 16-byte aligned)
+  double edges = 0.0;
+  if (d.K % e.bk != 0) edges += double(c.edge_k) * double(cdiv(tiles, kCUs));
+  if (d.M % e.bm != 0 || d.N % e.bn != 0) edges += c.edge_mn;
+  if (d.d_stride_n != 1 || (d.d_stride_m * int64_t(osz)) % 16 != 0)
+    edges += double(c.edge_d) * double(cdiv(tiles, kCUs));
+  if (p.sk_tiles > 0) {
+    // whole tiles, then 256 workgroups sharing the k-tiles of the others, then the fix-up
+    p.us = launch_us(c, tiles - p.sk_tiles, nkt) + kSkFixedUs +
+           kSkShareFactor * launch_us(c, kCUs, cdiv(int64_t(p.sk_tiles) * nkt, kCUs));
+  } else if (p.tail_S > 1) {
+    const double parts = double(p.tail_R) * p.tail_S;
+    p.us = launch_us(c, tiles - p.tail_R, nkt) +
+           launch_us(c, int64_t(p.tail_R) * p.tail_S, cdiv(p.tail_kps, e.bk)) +
+           reduce_us(4.0 * parts * tile_out, osz * p.tail_R * tile_out);
+  } else {
+    p.us = launch_us(c, tiles * p.S, cdiv(p.kps, e.bk));
+    if (p.S > 1)
+      p.us += reduce_us(4.0 * p.S * double(d.M) * double(d.N), osz * double(d.M) * double(d.N));
+  }
+  p.us += edges;
+  return p;
+}
+
+// Sustained cost of an entry: its time per k-tile with four workgroups on every CU, per
+// multiply-add of a k-tile (the steadiest of its measurements: long launches at full load).
+double sustained_cost(const KernelEntry& e) {
+  return double(e.cost->c[kCostLoadOne + 3]) / (double(e.bm) * e.bn * e.bk);
+}
+
+// Predictions closer than this fraction count as a tie: on 66 measured shapes, times of the same
+// kernel and plan differed by up to ~5 % between runs, and the model's predictions for the leading
+// entries were within a few percent of their measured times.
+constexpr double kTie = 0.03;
+
+// Kernel choice.  A product with M <= 16 is bound by streaming B and takes the skinny kernel when
+// one fits.  Otherwise the choice is the fitting entry of the family (16-byte loaders or not) with
+// the least predicted time under the plan it would get (make_plan); among entries predicted within
+// kTie of that least time, the one with the least sustained cost (then the earlier entry) wins.
+// An entry without measured costs is chosen only when nothing else fits.  A forced split
+// (split_req > 1) admits only entries that can split.  *us receives the chosen plan's predicted
+// time.
+int choose(const gemm_handle_s& h, bool vec_a, bool vec_b, bool want_vec, int split_req,
+           double* us = nullptr) {
   const KernelEntry* t = table();
   const bool need_split = split_req > 1;
+  if (us) *us = 0.0;
   for (int i = 0; i < table_size() && !need_split && !h.d.ragged_m && !h.d.grouped && !h.d.has_row_sumsq &&
                   !h.d.has_col_sum; ++i)
     if (t[i].skinny && (t[i].vec != 0) == want_vec && entry_fits(t[i], h, vec_a, vec_b)) return i;
-  int best = -1, best_rank = 0;
-  int64_t best_area = -1;
-  int best_small = -1, best_small_rank = 0;
-  int64_t best_small_wg = -1, best_small_area = -1;
-  // a batch runs every problem's tiles in one launch (a grouped launch's M already spans all of
-  // its groups)
-  const int64_t problems = h.d.batch > 1 && !h.d.ragged_m ? h.d.batch : 1;
-  auto fills = [&](const KernelEntry& e, int64_t wg) {
-    const int64_t area = int64_t(e.bm) * e.bn;
-    return wg >= 256 || (wg > 128 && (one_per_cu(e) || (e.realign && area >= 128 * 128)));
-  };
-  // Does an entry with a tile of at least 128 x 128 fill the GPU without splitting K?  Then a
-  // split whose slices keep fewer than 24 k-tiles does not count as filling it: each slice pays
-  // the pipeline fill, an fp32 partial plane and its share of the sum kernel.  Measured on
-  // MI355X, bf16 2048^2 x 4096: ring x 4 slices of 16 k-tiles 0.055 ms, unsplit 128 x 128
-  // (256 tiles) 0.048 ms (another box: 57.1 vs 55.6-57.3 us, a tie).  With fewer tiles no such
-  // entry fills the GPU and the split stays (1536^2 x 8192: ring x 7 slices of 19 k-tiles
-  // 62-67 us, 128 x 128 tiles 88-94 us).
-  bool unsplit_fills = false;
-  for (int i = 0; i < table_size() && split_req == 0; ++i) {
-    const KernelEntry& e = t[i];
-    if ((e.vec != 0) != want_vec || e.skinny || int64_t(e.bm) * e.bn < 128 * 128 ||
-        !entry_fits(e, h, vec_a, vec_b))
-      continue;
-    if (fills(e, cdiv(h.d.M, e.bm) * cdiv(h.d.N, e.bn) * problems)) unsplit_fills = true;
-  }
+  std::vector<std::pair<int, double>> cand;  // fitting entries and their predicted times
+  double least = std::numeric_limits<double>::infinity();
   for (int i = 0; i < table_size(); ++i) {
     const KernelEntry& e = t[i];
     if ((e.vec != 0) != want_vec || e.skinny) continue;
     if (need_split && e.max_split_k <= 1) continue;
     if (!entry_fits(e, h, vec_a, vec_b)) continue;
-    int slices;
-    int64_t kps;
-    plan_split(e, h.d, split_req, &slices, &kps);
-    const int64_t wg = cdiv(h.d.M, e.bm) * cdiv(h.d.N, e.bn) * slices * problems;
-    const int64_t area = int64_t(e.bm) * e.bn;
-    const int rank = wg <= 256 ? e.rank_one_round : e.rank;
-    const bool shallow_split = unsplit_fills && slices > 1 && kps / e.bk < 24;
-    // An entry fills the GPU with 256 workgroups or more.  A kernel that runs one per CU, or a
-    // 128 x 128 tile with the realigned loaders (whose smaller tile is much less efficient),
-    // also fills it with more than 128: a tile of half the area then needs two per CU somewhere
-    // (a quarter, three or more), so no CU does much less work with it, and the larger tile's
-    // higher efficiency decides.  MI355X: bf16 3072^3 ring 0.068 ms vs 256x128 0.093 ms;
-    // 3328^2 x 4096 0.093 vs 0.130; fp16 2051 x 1533 x 1027 with odd leading dims, 128x128
-    // realigned (204 workgroups) 47 us vs 64x64 (792) 65 us.  With exactly 128 ring tiles
-    // (2048 x 4096 x 2048) the 256x128 kernel is faster; for the 16-byte loaders 64x64 tiles
-    // were as fast or faster than 144-192 workgroups of 128x128 (f32 1536^3 111 vs 134 us).
-    const bool fill = fills(e, wg) && !shallow_split;
-    if (fill && (area > best_area || (area == best_area && rank > best_rank))) {
-      best = i;
-      best_area = area;
-      best_rank = rank;
-    }
-    if (wg > best_small_wg ||
-        (wg == best_small_wg && (area > best_small_area ||
-                                 (area == best_small_area && rank > best_small_rank)))) {
-      best_small = i;
-      best_small_wg = wg;
-      best_small_area = area;
-      best_small_rank = rank;
-    }
+    const double u = make_plan(e, h.d, split_req).us;
+    cand.emplace_back(i, u);
+    least = std::min(least, u);
   }
-  return best >= 0 ? best : best_small;
+  if (cand.empty()) return -1;
+  int best = -1;
+  double best_us = 0.0;
+  if (std::isfinite(least)) {
+    for (const auto& c : cand) {
+      if (c.second > least * (1.0 + kTie)) continue;
+      if (best < 0 || sustained_cost(t[c.first]) < sustained_cost(t[best])) {
+        best = c.first;
+        best_us = c.second;
+      }
+    }
+  } else {
+    best = cand.front().first;  // no fitting entry has measured costs
+    best_us = cand.front().second;
+  }
+  if (us) *us = std::isfinite(best_us) ? best_us : 0.0;
+  return best;
+}
+
+void set_plan(gemm_handle_s* h, const Plan& p) {
+  h->split_cfg = p.S;
+  h->kps_cfg = p.kps;
+  h->sk_tiles = p.sk_tiles;
+  h->tail_tiles = p.tail_R;
+  h->tail_split = p.tail_S;
+  h->tail_kps = p.tail_kps;
+  h->predicted_us = std::isfinite(p.us) ? p.us : 0.0;
 }
 
 // ---- lane maps checked with the layout helper ---------------------------------------------
@@ -408,25 +507,18 @@ bool entry_maps_ok(const KernelEntry& e) {
   return e.lds_row_chunks == 0;
 }
 
-// Whether to run a product whose operands the 16-byte loaders cannot read (a leading dimension
-// or base off 16 bytes, or an fp8 operand that is not K-contiguous) on aligned K-major copies:
+// Whether a product whose operands the 16-byte loaders cannot read (a leading dimension or base
+// off 16 bytes, or an fp8 operand that is not K-contiguous) may run on aligned K-major copies:
 // one extra pass over A and B (HBM-bound) against running every k-tile with realigned or
-// element-wise register-staged loads, which keep only one k-tile of loads in flight.  Measured
-// on MI355X, odd leading dimensions and row-major B (copies + chosen kernel vs the best direct
-// entry):
-//   f16  4099 x 3071 x 2053   110 us vs 129 us (realigned 128 x 128)
-//   f16  2051 x 1533 x 1027   41.5 us vs 33.1 us
-//   f16  1503 x 1301 x 1101   28.7 us vs 32.1 us
-//   e4m3 2051 x 1533 x 1027   34.7 us vs 122.6 us (element loads)
-//   e4m3 3001 x 2999 x 2049   81.1 us vs 533 us
-// 2-byte types have realigned loaders and take the copies from 2^35 FLOP; fp8 and fp32, which
-// only have element-wise loaders for such operands, from 2^31.  Batches and groups keep the
-// direct path.
-bool repack_pays(const gemm_desc& d, bool vec_both) {
+// element-wise register-staged loads, which keep only one k-tile of loads in flight.  The cost
+// model decides between the two (the copies plus the kernel chosen for them against the best
+// direct entry).  Measured on MI355X before the model decided: e4m3 3001 x 2999 x 2049 with odd
+// leading dimensions, 81 us on copies against 533 us with element loads; f16 4099 x 3071 x 2053,
+// 110 us against 129 us on realigned loads.  Batches and groups keep the direct path, and so
+// do products too small to be worth a pass.
+bool repack_allowed(const gemm_desc& d, bool vec_both) {
   if (vec_both || d.ragged_m || d.grouped || d.batch > 1) return false;
-  if (d.M < 128 || d.N < 128 || d.K < 64) return false;
-  const double flop = 2.0 * (double)d.M * (double)d.N * (double)d.K;
-  return flop >= (dtype_size(d.a_type) == 2 ? 34359738368.0 : 2147483648.0);
+  return d.M >= 128 && d.N >= 128 && d.K >= 64;
 }
 
 int check_arch() {
@@ -523,9 +615,10 @@ int gemm_create(const gemm_desc* desc, gemm_t* out) {
   const int split_req = L > 1 || d.ragged_m || d.grouped || d.has_row_sumsq || d.has_col_sum ||
                                 d.decomposition == 2
                             ? 1 : d.split_k;
-  h.fallback = choose(h, va, vb, false, split_req);
+  double fallback_us = 0.0;
+  h.fallback = choose(h, va, vb, false, split_req, &fallback_us);
   if (h.fallback < 0) return GEMM_ERR_NO_CONFIG;
-  if (d.force_config < 0 && repack_pays(d, va && vb)) {
+  if (d.force_config < 0 && repack_allowed(d, va && vb)) {
     // the product runs on aligned K-major copies of A and B: choose for that problem
     gemm_handle_s v = h;
     v.kp = (d.K + 16 / isz - 1) / (16 / isz) * (16 / isz);
@@ -536,8 +629,12 @@ int gemm_create(const gemm_desc* desc, gemm_t* out) {
     v.d.b_stride_n = v.kp;
     v.a = Operand{true, v.kp};
     v.b = Operand{true, v.kp};
-    const int inner = choose(v, true, true, true, split_req);
-    if (inner >= 0 && table()[inner].vec) {
+    double inner_us = 0.0;
+    const int inner = choose(v, true, true, true, split_req, &inner_us);
+    // the copies read and write A and B once
+    const double copy_us = kRepackFixedUs + kRepackUsPerByte * 2.0 * double(d.M + d.N) *
+                                                double(v.kp) * double(isz);
+    if (inner >= 0 && table()[inner].vec && copy_us + inner_us < fallback_us) {
       h.repack = 1;
       h.kp = v.kp;
       h.cfg = h.fallback = inner;
@@ -545,12 +642,10 @@ int gemm_create(const gemm_desc* desc, gemm_t* out) {
       h.repack_bytes_b = ((size_t)d.N * v.kp * isz + 255) / 256 * 256;
       if (!entry_maps_ok(table()[inner])) return GEMM_ERR_LANE_MAP;
       h.group_m = 4;
-      plan_split(table()[inner], v.d, split_req, &h.split_cfg, &h.kps_cfg);
+      set_plan(&h, make_plan(table()[inner], v.d, split_req));
+      h.predicted_us += copy_us;
       h.split_fb = h.split_cfg;
       h.kps_fb = h.kps_cfg;
-      plan_sk(table()[inner], v.d, split_req, h.split_cfg, &h.sk_tiles);
-      plan_tail(table()[inner], v.d, h.sk_tiles > 0 ? 1 : split_req, h.split_cfg, &h.tail_tiles,
-                &h.tail_split, &h.tail_kps);
       gemm_handle_s* p = new (std::nothrow) gemm_handle_s(h);
       if (!p) return GEMM_ERR_INVALID_ARG;
       p->magic = kMagic;
@@ -570,12 +665,9 @@ int gemm_create(const gemm_desc* desc, gemm_t* out) {
   // the chosen kernels' thread-to-data maps, checked once per atom against the layout helper
   if (!entry_maps_ok(table()[h.cfg]) || !entry_maps_ok(table()[h.fallback])) return GEMM_ERR_LANE_MAP;
   h.group_m = 4;
-  plan_split(table()[h.cfg], d, split_req, &h.split_cfg, &h.kps_cfg);
+  // split, Stream-K or split tail, as the plan for the chosen entry has it
+  set_plan(&h, make_plan(table()[h.cfg], d, split_req));
   plan_split(table()[h.fallback], d, split_req, &h.split_fb, &h.kps_fb);
-  // Stream-K where it pays, else the split tail where that does
-  plan_sk(table()[h.cfg], d, split_req, h.split_cfg, &h.sk_tiles);
-  plan_tail(table()[h.cfg], d, h.sk_tiles > 0 ? 1 : split_req, h.split_cfg, &h.tail_tiles,
-            &h.tail_split, &h.tail_kps);
 
   gemm_handle_s* p = new (std::nothrow) gemm_handle_s(h);
   if (!p) return GEMM_ERR_INVALID_ARG;
@@ -677,6 +769,7 @@ int gemm_get_info(gemm_t h, gemm_info* info) {
   info->repack = h->repack;
   info->sk_tiles = h->sk_tiles;
   info->sk_wgs = h->sk_tiles > 0 ? kCUs : 0;
+  info->predicted_us = h->predicted_us;
   return GEMM_OK;
 }
 

@@ -84,18 +84,42 @@ struct KernelEntry {
   int stages;         // LDS stages
   int lds_bytes;      // LDS per workgroup
   int max_split_k;    // largest split along K the kernel supports (1: none)
-  int rank;           // preference among entries with the same tile area (measured; higher wins)
   launch_fn launch;
   int realign;        // 1: realigned 16-byte loads of 2-byte elements (31-bit tile offsets)
-  int rank_one_round; // rank when all workgroups fit on the CUs at once (one tile per CU)
   int mi;             // MFMA atom: MI x MI output block (its layouts are in atom_maps.h)
   int lds_row_chunks; // 16-byte chunks per swizzled LDS row of the operand tiles (4 or 8)
   int mn_rows;        // 1: an MN-major operand is kept as rows of k and read by transposing reads
   launch_fn launch_sk;  // the kernel's Stream-K form (persistent workgroups), or nullptr
+  const struct EntryCost* cost;  // measured costs (set from the cost table by name), or nullptr:
+                                 // then the entry runs only when forced
 };
 
 const KernelEntry* table();
 int table_size();
+
+// Measured cost of one entry on MI355X (cost_table.cpp, written by calibrate.py).  Index i =
+// 0..10 stands for the load 1/4, 1/2, 3/4, 1, 2, ..., 8 (workgroups per compute unit): a launch
+// of 256 * load workgroups of kt k-tiles each took f[i] + kt * c[i] microseconds.
+constexpr int kCostLoads = 11;
+constexpr int kCostLoadOne = 3;  // index of the load 1
+struct EntryCost {
+  const char* name;
+  float f[kCostLoads];
+  float c[kCostLoads];
+  float edge_k;   // extra time of a partial last k-tile, per workgroup on the busiest CU
+  float edge_mn;  // extra time of partial last tile rows or columns, once per launch
+  float edge_d;   // extra time of D rows off 16 bytes, per workgroup on the busiest CU
+};
+extern const EntryCost kEntryCosts[];
+extern const int kEntryCostCount;
+// split-K second kernel and partial stores: kSplitFixedUs + kSplitUsPerByte * (partial bytes,
+// written and read, plus output bytes)
+extern const double kSplitFixedUs, kSplitUsPerByte;
+// copies into aligned K-major buffers: kRepackFixedUs + kRepackUsPerByte * (bytes read and written)
+extern const double kRepackFixedUs, kRepackUsPerByte;
+// Stream-K launch and fix-up beyond the whole tiles: kSkFixedUs + kSkShareFactor * (the entry's
+// time for 256 workgroups of one share of k-tiles)
+extern const double kSkFixedUs, kSkShareFactor;
 
 // Second kernel of a split-K run: D = act(alpha * sum of the split_k fp32 planes in
 // p.workspace + beta * C + bias), with out_type the type of C, D and bias.

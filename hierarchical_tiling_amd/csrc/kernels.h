@@ -2301,45 +2301,44 @@ static hipError_t launch_tiled(const KParams& p, hipStream_t s, dim3 grid) {
 }
 
 // VEC 2 (realigned 2-byte loads) entries need no 16-byte alignment, so they count as element-
-// aligned (vec 0) kernels that outrank the element-wise ones (rank 1)
+// aligned (vec 0) kernels
 #define HT_TILED(NAME, DT, AK, BKM, VEC, BM, BN, BKE, WM, WN, MI)                                 \
   {NAME, DT, AK, BKM, (VEC) == 1, 0, BM, BN, BKE, WM * WN, 2, 2 * (BM + BN) * BKE * Ty<DT>::SZ, 64, \
-   (VEC) == 2 ? 1 : 0, &launch_tiled<DT, AK, BKM, VEC, BM, BN, BKE, WM, WN, MI>, (VEC) == 2, \
-   (VEC) == 2 ? 1 : 0, MI, BKE * Ty<DT>::SZ / 16,                                               \
+   &launch_tiled<DT, AK, BKM, VEC, BM, BN, BKE, WM, WN, MI>, (VEC) == 2, MI, BKE * Ty<DT>::SZ / 16, \
    RowsLayout<DT, AK, VEC, BM>::value || RowsLayout<DT, BKM, VEC, BN>::value}
 
-#define HT_DMA(NAME, DT, BM, BN, WM, WN, MI, ST, OCC, CH, RANK)                                \
+#define HT_DMA(NAME, DT, BM, BN, WM, WN, MI, ST, OCC, CH)                                      \
   {NAME, DT, 1, 1, 1, 0, BM, BN, CH * 16 / Ty<DT>::SZ, WM * WN, ST, ST * (BM + BN) * CH * 16, 1, \
-   RANK, &launch_dma<DT, BM, BN, WM, WN, MI, ST, OCC, CH>, 0, RANK, MI, CH, 0}
+   &launch_dma<DT, BM, BN, WM, WN, MI, ST, OCC, CH>, 0, MI, CH, 0}
 
 // Split-ring entries: 256 x 256 tiles, 128-byte rows, 5 units of 32 KiB.  The _BN form takes a
 // row-major (N-contiguous) B kept in LDS as rows of k.
-#define HT_RING(NAME, DT, WM, WN, MI, NB, RANK, RANK1)                                               \
-  {NAME, DT, 1, 1, 1, 0, 256, 256, 128 / Ty<DT>::SZ, WM * WN, 5, 5 * 256 * 128, 64, RANK,         \
-   &launch_ring<DT, WM, WN, MI, NB, true, false>, 0, RANK1, MI, 8, 0, nullptr}
-#define HT_RING_BN(NAME, DT, WM, WN, MI, NB, RANK, RANK1)                                            \
-  {NAME, DT, 1, 0, 1, 0, 256, 256, 128 / Ty<DT>::SZ, WM * WN, 5, 5 * 256 * 128, 64, RANK,         \
-   &launch_ring<DT, WM, WN, MI, NB, false, false>, 0, RANK1, MI, 8, 1, nullptr}
+#define HT_RING(NAME, DT, WM, WN, MI, NB)                                                          \
+  {NAME, DT, 1, 1, 1, 0, 256, 256, 128 / Ty<DT>::SZ, WM * WN, 5, 5 * 256 * 128, 64,               \
+   &launch_ring<DT, WM, WN, MI, NB, true, false>, 0, MI, 8, 0, nullptr}
+#define HT_RING_BN(NAME, DT, WM, WN, MI, NB)                                                       \
+  {NAME, DT, 1, 0, 1, 0, 256, 256, 128 / Ty<DT>::SZ, WM * WN, 5, 5 * 256 * 128, 64,               \
+   &launch_ring<DT, WM, WN, MI, NB, false, false>, 0, MI, 8, 1, nullptr}
 // The same entries with the Stream-K form of the kernel as well.  (The fp8 ring has none: its
 // 256 registers are full, and the form's loop over tiles spilled and ran at half speed.)
-#define HT_RING_SK(NAME, DT, WM, WN, MI, NB, RANK, RANK1)                                            \
-  {NAME, DT, 1, 1, 1, 0, 256, 256, 128 / Ty<DT>::SZ, WM * WN, 5, 5 * 256 * 128, 64, RANK,         \
-   &launch_ring<DT, WM, WN, MI, NB, true, false>, 0, RANK1, MI, 8, 0,                            \
+#define HT_RING_SK(NAME, DT, WM, WN, MI, NB)                                                       \
+  {NAME, DT, 1, 1, 1, 0, 256, 256, 128 / Ty<DT>::SZ, WM * WN, 5, 5 * 256 * 128, 64,               \
+   &launch_ring<DT, WM, WN, MI, NB, true, false>, 0, MI, 8, 0,                                    \
    &launch_ring<DT, WM, WN, MI, NB, true, true>}
-#define HT_RING_BN_SK(NAME, DT, WM, WN, MI, NB, RANK, RANK1)                                         \
-  {NAME, DT, 1, 0, 1, 0, 256, 256, 128 / Ty<DT>::SZ, WM * WN, 5, 5 * 256 * 128, 64, RANK,         \
-   &launch_ring<DT, WM, WN, MI, NB, false, false>, 0, RANK1, MI, 8, 1,                           \
+#define HT_RING_BN_SK(NAME, DT, WM, WN, MI, NB)                                                    \
+  {NAME, DT, 1, 0, 1, 0, 256, 256, 128 / Ty<DT>::SZ, WM * WN, 5, 5 * 256 * 128, 64,               \
+   &launch_ring<DT, WM, WN, MI, NB, false, false>, 0, MI, 8, 1,                                   \
    &launch_ring<DT, WM, WN, MI, NB, false, true>}
 
 // Streaming skinny entries: bm = 16 rows, bn = 16*NBW columns, bk = one 128-byte block of K.
 #define HT_SKINNY_DMA(NAME, DT, WK, NBW, R, OCC)                                                  \
-  {NAME, DT, 1, 1, 1, 1, 16, NBW * 16, 128 / Ty<DT>::SZ, WK, R, WK * R * (NBW + 1) * 16 * 128, 1, 0, \
-   &launch_skinny_dma<DT, WK, NBW, R, OCC>, 0, 0, 16, 8, 0}
+  {NAME, DT, 1, 1, 1, 1, 16, NBW * 16, 128 / Ty<DT>::SZ, WK, R, WK * R * (NBW + 1) * 16 * 128, 1, \
+   &launch_skinny_dma<DT, WK, NBW, R, OCC>, 0, 16, 8, 0}
 
 // Skinny entries: bm = 16 rows, bn = WN*NBW*16 columns per workgroup, bk = one MFMA k-step (no
 // LDS operand tiles).
 #define HT_SKINNY(NAME, DT, WK, WN, NBW, U, OCC)                                                 \
   {NAME, DT, 1, 1, 1, 1, 16, WN * NBW * 16, 4 * Atom<DT, 16>::UNITS * 16 / Ty<DT>::SZ, WK * WN, \
-   1, WK * WN * NBW * 16 * 16 * 4, 1, 0, &launch_skinny<DT, WK, WN, NBW, U, OCC>, 0, 0, 16, 0, 0}
+   1, WK * WN * NBW * 16 * 16 * 4, 1, &launch_skinny<DT, WK, WN, NBW, U, OCC>, 0, 16, 0, 0}
 
 }  // namespace htk

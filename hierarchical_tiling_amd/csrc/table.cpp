@@ -1,6 +1,8 @@
-// table.cpp -- the tile table: the per-type entry lists of table_*.hip, concatenated once.
+// table.cpp -- the tile table: the per-type entry lists of table_*.hip, concatenated once, each
+// entry joined to its measured costs (cost_table.cpp).
 // Entry indices (gemm_desc.force_config, gemm_config_name) refer to this order.
 #include <cstdlib>
+#include <cstring>
 
 #include "gemm_internal.h"
 
@@ -32,6 +34,12 @@ struct Combined {
     append(table_f16);
     append(table_f32);
     append(table_e4m3);
+    // each entry's measured costs, matched by name
+    for (int i = 0; i < n; ++i) {
+      e[i].cost = nullptr;
+      for (int j = 0; j < kEntryCostCount; ++j)
+        if (std::strcmp(kEntryCosts[j].name, e[i].name) == 0) e[i].cost = &kEntryCosts[j];
+    }
   }
 };
 

@@ -5,20 +5,20 @@
 namespace htk {
 
 static const KernelEntry g_bf16_dma[] = {
-    HT_DMA("bf16_ak_bk_256x256x32_w2x2_m32_dma4", DT_BF16, 256, 256, 2, 2, 32, 4, 1, 4, 2),
-    HT_DMA("bf16_ak_bk_256x256x32_w2x2_m32_dma5", DT_BF16, 256, 256, 2, 2, 32, 5, 1, 4, 3),
-    HT_DMA("bf16_ak_bk_256x128x32_w2x2_m32_dma3_o2", DT_BF16, 256, 128, 2, 2, 32, 3, 2, 4, 1),
-    HT_DMA("bf16_ak_bk_128x256x32_w2x2_m32_dma3_o2", DT_BF16, 128, 256, 2, 2, 32, 3, 2, 4, 1),
-    HT_DMA("bf16_ak_bk_256x128x32_w4x1_m32_dma3_o2", DT_BF16, 256, 128, 4, 1, 32, 3, 2, 4, 1),
-    HT_DMA("bf16_ak_bk_256x256x64_w2x2_m32_dma2", DT_BF16, 256, 256, 2, 2, 32, 2, 1, 8, 2),
-    HT_DMA("bf16_ak_bk_256x128x64_w2x2_m32_dma3", DT_BF16, 256, 128, 2, 2, 32, 3, 1, 8, 1),
-    HT_DMA("bf16_ak_bk_256x256x32_w2x4_m32_dma5", DT_BF16, 256, 256, 2, 4, 32, 5, 1, 4, 4),
-    HT_DMA("bf16_ak_bk_256x256x32_w4x2_m32_dma5", DT_BF16, 256, 256, 4, 2, 32, 5, 1, 4, 4),
-    HT_DMA("bf16_ak_bk_256x256x64_w2x4_m32_dma2", DT_BF16, 256, 256, 2, 4, 32, 2, 1, 8, 5),
-    HT_RING("bf16_ak_bk_256x256x64_w2x4_m32_ring", DT_BF16, 2, 4, 32, 2, 6, 6),
-    HT_RING_SK("bf16_ak_bk_256x256x64_w2x4_m16_ring", DT_BF16, 2, 4, 16, 2, 7, 7),
-    HT_RING("bf16_ak_bk_256x256x64_w2x4_m16_ring1", DT_BF16, 2, 4, 16, 1, 0, 0),
-    HT_RING_BN_SK("bf16_ak_bn_256x256x64_w2x4_m16_ring", DT_BF16, 2, 4, 16, 2, 7, 7),
+    HT_DMA("bf16_ak_bk_256x256x32_w2x2_m32_dma4", DT_BF16, 256, 256, 2, 2, 32, 4, 1, 4),
+    HT_DMA("bf16_ak_bk_256x256x32_w2x2_m32_dma5", DT_BF16, 256, 256, 2, 2, 32, 5, 1, 4),
+    HT_DMA("bf16_ak_bk_256x128x32_w2x2_m32_dma3_o2", DT_BF16, 256, 128, 2, 2, 32, 3, 2, 4),
+    HT_DMA("bf16_ak_bk_128x256x32_w2x2_m32_dma3_o2", DT_BF16, 128, 256, 2, 2, 32, 3, 2, 4),
+    HT_DMA("bf16_ak_bk_256x128x32_w4x1_m32_dma3_o2", DT_BF16, 256, 128, 4, 1, 32, 3, 2, 4),
+    HT_DMA("bf16_ak_bk_256x256x64_w2x2_m32_dma2", DT_BF16, 256, 256, 2, 2, 32, 2, 1, 8),
+    HT_DMA("bf16_ak_bk_256x128x64_w2x2_m32_dma3", DT_BF16, 256, 128, 2, 2, 32, 3, 1, 8),
+    HT_DMA("bf16_ak_bk_256x256x32_w2x4_m32_dma5", DT_BF16, 256, 256, 2, 4, 32, 5, 1, 4),
+    HT_DMA("bf16_ak_bk_256x256x32_w4x2_m32_dma5", DT_BF16, 256, 256, 4, 2, 32, 5, 1, 4),
+    HT_DMA("bf16_ak_bk_256x256x64_w2x4_m32_dma2", DT_BF16, 256, 256, 2, 4, 32, 2, 1, 8),
+    HT_RING("bf16_ak_bk_256x256x64_w2x4_m32_ring", DT_BF16, 2, 4, 32, 2),
+    HT_RING_SK("bf16_ak_bk_256x256x64_w2x4_m16_ring", DT_BF16, 2, 4, 16, 2),
+    HT_RING("bf16_ak_bk_256x256x64_w2x4_m16_ring1", DT_BF16, 2, 4, 16, 1),
+    HT_RING_BN_SK("bf16_ak_bn_256x256x64_w2x4_m16_ring", DT_BF16, 2, 4, 16, 2),
     HT_SKINNY_DMA("bf16_ak_bk_16x32_w4_skinny_dma", DT_BF16, 4, 2, 3, 2),
     HT_SKINNY("bf16_ak_bk_16x32_w8_skinny", DT_BF16, 8, 1, 2, 2, 4),
 };

@@ -16,10 +16,10 @@ static const KernelEntry g_e4m3[] = {
     HT_TILED("e4m3_ak_bn_64x64x128_w2x2_m16_narrow", DT_F8, 1, 0, 0, 64, 64, 128, 2, 2, 16),
     HT_TILED("e4m3_am_bk_64x64x128_w2x2_m16_narrow", DT_F8, 0, 1, 0, 64, 64, 128, 2, 2, 16),
     HT_TILED("e4m3_am_bn_64x64x128_w2x2_m16_narrow", DT_F8, 0, 0, 0, 64, 64, 128, 2, 2, 16),
-    HT_DMA("e4m3_ak_bk_256x256x64_w2x2_m32_dma4", DT_F8, 256, 256, 2, 2, 32, 4, 1, 4, 2),
-    HT_DMA("e4m3_ak_bk_256x256x128_w2x2_m32_dma2", DT_F8, 256, 256, 2, 2, 32, 2, 1, 8, 3),
-    HT_RING("e4m3_ak_bk_256x256x128_w2x4_m32_ring", DT_F8, 2, 4, 32, 2, 6, 6),
-    HT_RING("e4m3_ak_bk_256x256x128_w2x4_m32_ring1", DT_F8, 2, 4, 32, 1, 0, 0),
+    HT_DMA("e4m3_ak_bk_256x256x64_w2x2_m32_dma4", DT_F8, 256, 256, 2, 2, 32, 4, 1, 4),
+    HT_DMA("e4m3_ak_bk_256x256x128_w2x2_m32_dma2", DT_F8, 256, 256, 2, 2, 32, 2, 1, 8),
+    HT_RING("e4m3_ak_bk_256x256x128_w2x4_m32_ring", DT_F8, 2, 4, 32, 2),
+    HT_RING("e4m3_ak_bk_256x256x128_w2x4_m32_ring1", DT_F8, 2, 4, 32, 1),
     HT_SKINNY_DMA("e4m3_ak_bk_16x32_w4_skinny_dma", DT_F8, 4, 2, 3, 2),
     HT_SKINNY("e4m3_ak_bk_16x32_w4_skinny", DT_F8, 4, 1, 2, 2, 2),
 };

@@ -85,7 +85,7 @@ class gemm_info(ctypes.Structure):
                 ("grid", ctypes.c_int64), ("name", ctypes.c_char * 96),
                 ("tail_tiles", ctypes.c_int32), ("tail_split", ctypes.c_int32),
                 ("repack", ctypes.c_int32), ("sk_tiles", ctypes.c_int32),
-                ("sk_wgs", ctypes.c_int32)]
+                ("sk_wgs", ctypes.c_int32), ("predicted_us", ctypes.c_double)]
 
 
 class ht_tile_stats(ctypes.Structure):

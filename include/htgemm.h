@@ -320,6 +320,8 @@ typedef struct gemm_info {
   int32_t repack;         /* 1: A and B are read through aligned K-major copies in the workspace */
   int32_t sk_tiles;       /* tiles run Stream-K (the last ones of the tile order; 0: none)      */
   int32_t sk_wgs;         /* persistent workgroups of the Stream-K launch                       */
+  double predicted_us;    /* the cost model's time of one run, in microseconds (0: the entry has
+                             no measured costs); the choice took the least of these             */
 } gemm_info;
 
 int gemm_get_info(gemm_t h, gemm_info* info);

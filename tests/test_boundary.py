@@ -125,12 +125,12 @@ def test_tile_table_choices(fake_gfx950):
     big = _info(desc(M=8192, N=8192, K=8192, a_strides=(8192, 1), b_strides=(1, 8192), d_strides=(8192, 1)))
     assert (big.bm, big.bn) == (256, 256) and big.name.startswith(b"bf16_ak_bk")
     assert big.grid == 32 * 32
-    # ragged fp16 with odd leading dimensions (2-byte aligned rows): a small product takes the
+    # ragged fp16 with odd leading dimensions (2-byte aligned rows): this product takes the
     # realigning loader; a large one runs on aligned K-major copies of A and B (K padded to 2056)
     # made in the workspace, with the split ring
     small_rag = _info(H.make_desc(2051, 1533, 1027, "f16", (1027, 1), (1533, 1), (1533, 1)))
     assert b"realign" in small_rag.name and not small_rag.repack
-    # fp8 has no realigning loader: copies from 2^31 FLOP (row-major B here)
+    # fp8 has no realigning loader: copies (row-major B here)
     r8 = _info(H.make_desc(2051, 1533, 1027, "e4m3", (1027, 1), (1533, 1), (1533, 1)))
     assert r8.repack and r8.name.startswith(b"e4m3_ak_bk_")
     d_rag = H.make_desc(4099, 3071, 2053, "f16", (2053, 1), (3071, 1), (3071, 1), c_strides=(3071, 1))
@@ -142,9 +142,12 @@ def test_tile_table_choices(fake_gfx950):
         assert H.gemm_workspace_size(h) == copies      # the ring here needs no split workspace
     finally:
         H.gemm_destroy(h)
-    # fp8 and fp32 have no realigning loader: element loads
+    # fp8 has no realigning loader: element loads, or copies where the model predicts them faster
+    # (e4m3 301 x 257 x 203: 13.4 us on copies against 14.9 us with element loads)
     rag8 = _info(H.make_desc(301, 257, 203, "e4m3", (203, 1), (1, 203), (257, 1)))
-    assert b"narrow" in rag8.name
+    assert rag8.repack and b"_vec" in rag8.name
+    small8 = _info(H.make_desc(120, 257, 203, "e4m3", (203, 1), (1, 203), (257, 1)))
+    assert b"narrow" in small8.name and not small8.repack   # below 128 rows: no copies
     # M <= 16 with 16-byte-aligned K-major operands: the streaming (skinny) kernel, one
     # workgroup per 32 output columns
     sk = _info(H.make_desc(16, 16384, 8192, "e4m3", (8192, 1), (1, 8192), (16384, 1)))
@@ -366,31 +369,37 @@ def test_grouped_problems_fields(fake_gfx950):
 
 def test_stream_k_plan(fake_gfx950):
     """Stream-K ("CUTLASS", Part IV Stage 2): the tiles of a last partial round of a
-    one-workgroup-per-CU kernel run as 256 persistent workgroups; the library applies it where
-    it was measured to pay (a last round at most half full, at least 64 k-tiles) in place of
-    the split tail."""
+    one-workgroup-per-CU kernel run as 256 persistent workgroups; the library plans it where it
+    was measured to pay (a last round at most half full, at least 64 k-tiles) in place of the
+    split tail, for the entries that have a Stream-K form."""
+    ring = [H.gemm_config_name(j) for j in range(H.gemm_num_configs())].index(
+        "bf16_ak_bk_256x256x64_w2x4_m16_ring")
+
     def info(M, N, K, **kw):
         g = H.Gemm(H.make_desc(M, N, K, "bf16", (K, 1), (1, K), (N, 1), **kw))
         return g.info, g.workspace_bytes
     ws_sk = 2 * 256 * 256 * 256 * 4
-    i, ws = info(4352, 4352, 4096)          # 289 tiles: 33 in the last round, 64 k-tiles
-    assert "_ring" in i.name.decode() and (i.sk_tiles, i.sk_wgs) == (33, 256) and ws == ws_sk
+    # the ring that has a Stream-K form, with the library deciding the decomposition
+    i, ws = info(4352, 4352, 4096, force_config=ring)   # 289 tiles: 33 in the last round
+    assert (i.sk_tiles, i.sk_wgs) == (33, 256) and ws == ws_sk
     assert (i.tail_tiles, i.tail_split) == (0, 1)
-    assert info(6144, 6144, 8192)[0].sk_tiles == 64
+    assert info(6144, 6144, 8192, force_config=ring)[0].sk_tiles == 64
     for shape in ((8192, 8192, 8192),       # whole rounds
                   (5120, 5120, 8192),       # 144 left: more than half a round
                   (3840, 3840, 8192),       # one round
                   (6144, 6144, 2048)):      # 32 k-tiles: too shallow
-        i, _ = info(*shape)
+        i, _ = info(*shape, force_config=ring)
         assert i.sk_tiles == 0, shape
     # no Stream-K when asked for none (the split tail then), or with a fixed split
-    i, _ = info(4352, 4352, 4096, decomposition=1)
+    i, _ = info(4352, 4352, 4096, force_config=ring, decomposition=1)
     assert i.sk_tiles == 0 and i.tail_split > 1
-    assert info(4352, 4352, 4096, split_k=1)[0].sk_tiles == 0
+    assert info(4352, 4352, 4096, force_config=ring, split_k=1)[0].sk_tiles == 0
+    # the automatic choice compares the plans: here an entry with the split tail is predicted
+    # (and was measured) faster than the ring with Stream-K
+    i, _ = info(4352, 4352, 4096)
+    assert "_ring" in i.name.decode() and i.sk_tiles == 0 and i.tail_split > 1
     # forced: every tile when they fit in one round, else the last partial round (the last
     # round with whole rounds only)
-    ring = [H.gemm_config_name(j) for j in range(H.gemm_num_configs())].index(
-        "bf16_ak_bk_256x256x64_w2x4_m16_ring")
     assert info(1000, 1300, 64, force_config=ring, decomposition=2)[0].sk_tiles == 24
     assert info(5120, 5120, 8192, force_config=ring, decomposition=2)[0].sk_tiles == 144
     i, ws = info(8192, 8192, 8192, force_config=ring, decomposition=2)
@@ -458,63 +467,77 @@ def test_col_sum_fields(fake_gfx950):
     assert status_of(d) == H.GEMM_ERR_INVALID_ARG
 
 
-# Kernel choice for mid-size and large bf16 products (A row-major, B column-major).  One-round
-# rules measured on MI355X: a one-workgroup-per-CU tile is used when its single round is over
-# half full; automatic K slices stay within one round; the leftover tiles of an incomplete last
-# round run Stream-K on the ring (the split tail when Stream-K is turned off).
-@pytest.mark.parametrize("shape,kernel,split,tail,sk", [
-    ((3072, 3072, 3072), "m16_ring", 1, (0, 1), 0),       # 144 ring tiles
-    ((3328, 3328, 4096), "m16_ring", 1, (0, 1), 0),       # 169: no split, 2 slices would be 338
-    ((2816, 2816, 4096), "m16_ring", 2, (0, 1), 0),       # 121 tiles x 2 = 242
-    ((1536, 1536, 8192), "m16_ring", 7, (0, 1), 0),       # 36 x 7 = 252; 8 would start a round
-    # 4 ring slices would keep 16 k-tiles each while 128 x 128 tiles fill the GPU unsplit:
-    # 0.048 against 0.055 ms on one MI355X, a tie on another
-    ((2048, 2048, 4096), "128x128x64", 1, (0, 1), 0),
-    ((2048, 4096, 2048), "256x128x32", 1, (0, 1), 0),     # exactly 128 ring tiles: half-size tile
-    ((2048, 2048, 2048), "128x128x64", 1, (0, 1), 0),
-    ((512, 512, 16384), "128x128x64", 16, (0, 1), 0),
-    ((8192, 8192, 8192), "m16_ring", 1, (0, 1), 0),
-    ((4352, 4352, 4096), "m16_ring", 1, (0, 1), 33),
+# Kernel choice for mid-size and large bf16 products (A row-major, B column-major), from the cost
+# model (the fitting entry with the least predicted time).  Each expectation below was measured on
+# MI355X against the rule-based choice the model replaced (microseconds, one box):
+#   3072^3         256 x 256 DMA entry 67, the ring 70
+#   2816^2 x 4096  256 x 128 tiles, unsplit 75; the ring in 2 slices 76
+#   1536^2 x 8192  the ring in 7 slices (252 workgroups; 8 would start a second round)
+#   2048^2 x 4096  128 x 128 tiles unsplit 50-53; 4 ring slices of 16 k-tiles 55
+#   2048 x 4096 x 2048  half-size (128 x 256 or 256 x 128) tiles 42-44, the ring 51
+#   4352^2 x 4096  a ring with the split tail 167-169; the ring with Stream-K 184
+@pytest.mark.parametrize("shape,tile,split,tail,sk", [
+    ((3072, 3072, 3072), (256, 256), 1, (0, 1), 0),
+    ((3328, 3328, 4096), (256, 256), 1, (0, 1), 0),
+    ((2816, 2816, 4096), (256, 128), 1, (0, 1), 0),
+    ((1536, 1536, 8192), (256, 256), 7, (0, 1), 0),
+    ((2048, 2048, 4096), (128, 128), 1, (0, 1), 0),
+    ((2048, 4096, 2048), (256, 128), 1, (0, 1), 0),
+    ((2048, 2048, 2048), (128, 128), 1, (0, 1), 0),
+    ((512, 512, 16384), (128, 128), 16, (0, 1), 0),
+    ((8192, 8192, 8192), (256, 256), 1, (0, 1), 0),
+    ((4352, 4352, 4096), (256, 256), 1, (33, 7), 0),
 ])
-def test_kernel_choice_by_rounds(fake_gfx950, shape, kernel, split, tail, sk):
+def test_kernel_choice_by_rounds(fake_gfx950, shape, tile, split, tail, sk):
     M, N, K = shape
     info = _info(desc(M=M, N=N, K=K, a_strides=(K, 1), b_strides=(1, K), d_strides=(N, 1)))
     name = info.name.decode()
-    assert kernel in name and not name.endswith("ring1"), name
+    assert (info.bm * info.bn == tile[0] * tile[1] and info.bm >= 128), name
     assert (info.split_k, info.tail_tiles, info.tail_split, info.sk_tiles) == (split,) + tail + (sk,), name
+    assert info.predicted_us > 0
 
 
-@pytest.mark.parametrize("dtype,shape,orders,kernel", [
-    ("bf16", (1024, 1024, 1024), ("row", "col"), "_64x64x64_w2x2_m16_vec"),         # 256 small tiles
-    ("e4m3", (1024, 1024, 1024), ("row", "col"), "_64x64x128_w2x2_m16_vec"),
-    ("f32", (256, 256, 256), ("row", "row"), "_64x64x32_w2x2_m16_vec"),
-    ("bf16", (1536, 1536, 1024), ("row", "col"), "_64x64x64_w2x2_m16_vec"),          # 144 of 128x128
-    ("bf16", (2048, 2048, 2048), ("row", "col"), "_128x128x64_w2x2_m32_vec"),
-    # odd leading dimensions: realigned loaders; 128x128 from 129 workgroups
-    ("f16", (1001, 999, 1003), ("row", "row"), "_64x64x64_w2x2_m16_realign"),
-    ("f16", (2051, 1533, 1027), ("row", "row"), "_128x128x64_w2x2_m32_realign"),
-    # from 2^35 FLOP a 2-byte product runs on aligned K-major copies (gemm_info.repack)
-    ("f16", (4099, 3071, 2053), ("row", "row"), "_ak_bk_256x256x64_w2x4_m16_ring"),
-    ("bf16", (255, 257, 251), ("row", "row"), "_64x64x64_w2x2_m16_realign"),         # rank breaks the tie
+def test_headline_product_runs_on_the_ring(fake_gfx950):
+    """bf16 8192^3 (A row-major, B column- or row-major): the split ring with 16 x 16 atoms, whole
+    rounds, no split."""
+    for b in ((1, 8192), (8192, 1)):
+        info = _info(desc(M=8192, N=8192, K=8192, a_strides=(8192, 1), b_strides=b,
+                          d_strides=(8192, 1), has_bias=True, act="gelu"))
+        assert info.name.decode().endswith("_w2x4_m16_ring"), info.name
+        assert (info.split_k, info.sk_tiles, info.tail_tiles, info.repack) == (1, 0, 0, 0)
+
+
+@pytest.mark.parametrize("dtype,shape,orders,kernel,repack", [
+    ("bf16", (1024, 1024, 1024), ("row", "col"), "_64x64x64_w2x2_m16_vec", 0),     # 256 small tiles
+    ("e4m3", (1024, 1024, 1024), ("row", "col"), "_64x64x128_w2x2_m16_vec", 0),
+    ("bf16", (1536, 1536, 1024), ("row", "col"), "_64x64x64_w2x2_m16_vec", 0),      # 144 of 128x128
+    ("bf16", (2048, 2048, 2048), ("row", "col"), "_128x128x64_w2x2_m32_vec", 0),
+    # odd leading dimensions: realigned loaders, or aligned K-major copies where the model
+    # predicts them faster (f16 1001^3-ish: 16.7 us on copies against 23-25 us realigned)
+    ("f16", (1001, 999, 1003), ("row", "row"), "_64x64x64_w2x2_m16_vec", 1),
+    ("f16", (2051, 1533, 1027), ("row", "row"), "_128x128x64_w2x2_m32_realign", 0),
+    ("f16", (4099, 3071, 2053), ("row", "row"), "_ak_bk_256x256x64_w2x4_m16_ring", 1),
 ])
-def test_kernel_choice_small_and_realigned(fake_gfx950, dtype, shape, orders, kernel):
+def test_kernel_choice_small_and_realigned(fake_gfx950, dtype, shape, orders, kernel, repack):
     M, N, K = shape
     a = (K, 1) if orders[0] == "row" else (1, M)
     b = (N, 1) if orders[1] == "row" else (1, K)
     info = _info(desc(M=M, N=N, K=K, dtype=dtype, a_strides=a, b_strides=b, d_strides=(N, 1)))
     assert info.name.decode().endswith(kernel), info.name.decode()
+    assert info.repack == repack
 
 
-@pytest.mark.parametrize("L,shape,kernel", [
-    (16, (1024, 1024, 512), "_m16_ring"),          # 16 tiles x 16 problems fill one ring round
-    (64, (256, 256, 1024), "_128x128x64_w2x2_m32_vec"),
-    (1, (1024, 1024, 1024), "_64x64x64_w2x2_m16_vec"),
+@pytest.mark.parametrize("L,shape,tile", [
+    (16, (1024, 1024, 512), (256, 256)),          # 16 tiles x 16 problems fill one round
+    (64, (256, 256, 1024), (128, 128)),
+    (1, (1024, 1024, 1024), (64, 64)),
 ])
-def test_kernel_choice_counts_batch_problems(fake_gfx950, L, shape, kernel):
+def test_kernel_choice_counts_batch_problems(fake_gfx950, L, shape, tile):
     M, N, K = shape
     d = desc(M=M, N=N, K=K, a_strides=(K, 1), b_strides=(1, K), d_strides=(N, 1), batch=L,
              batch_strides=(M * K, N * K, 0, M * N))
-    assert _info(d).name.decode().endswith(kernel)
+    info = _info(d)
+    assert (info.bm, info.bn) == tile, info.name
 
 
 def test_noalloc_scratch_limit_and_arguments(fake_gfx950):

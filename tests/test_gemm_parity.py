@@ -174,12 +174,13 @@ def test_beta_zero_ignores_nan_c():
 def test_misaligned_pointer_uses_fallback_path_with_same_result():
     # A's base 2 bytes off 16: the library takes its element-aligned fallback entry, whose
     # result is within tolerance of the oracle
-    base = Case(264, 264, 128, "bf16", seed=13)
+    # (no split along K in any of the runs, so that all of them sum in the same order)
+    base = Case(264, 264, 128, "bf16", seed=13, split_k=1)
     p0 = Prepared(base)
     g0, out0 = p0.run()
     vec_name = g0.info.name.decode()
     assert vec_name.endswith("_vec")
-    shifted = Case(264, 264, 128, "bf16", seed=13, a_offset=1)
+    shifted = Case(264, 264, 128, "bf16", seed=13, a_offset=1, split_k=1)
     p1 = Prepared(shifted)
     _, out1 = p1.run()
     assert error("bf16", p1.decode_out(out1)[0], p1.oracle_full()) <= TOL["bf16"]
@@ -188,7 +189,7 @@ def test_misaligned_pointer_uses_fallback_path_with_same_result():
     # three results agree bit for bit
     names = table()
     for kind in ("realign", "narrow"):
-        p2 = Prepared(Case(264, 264, 128, "bf16", seed=13, a_offset=1,
+        p2 = Prepared(Case(264, 264, 128, "bf16", seed=13, a_offset=1, split_k=1,
                            force=names.index(vec_name.replace("_vec", "_" + kind))))
         g2, out2 = p2.run()
         assert g2.info.name.decode().endswith(kind)
@@ -362,7 +363,8 @@ def test_split_k_automatic_on_few_tiles_and_long_k():
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 def test_realigned_loads_equal_element_loads(dtype, layout):
     # odd leading dimensions and a base 2 bytes off a dword: the realigning 16-byte loader and the
-    # element-wise loader feed the same tile kernel, so the outputs agree bit for bit
+    # element-wise loader feed the same tile kernel (unsplit, as the cost model may plan a split
+    # for one loader and not the other), so the outputs agree bit for bit
     a_order, b_order = layout.split("-")
     names = [H.gemm_config_name(i) for i in range(H.gemm_num_configs())]
     a = "ak" if a_order == "row" else "am"
@@ -371,7 +373,7 @@ def test_realigned_loads_equal_element_loads(dtype, layout):
     for kind in ("realign", "narrow"):
         c = Case(M=259, N=197, K=301, dtype=dtype, a_order=a_order, b_order=b_order, seed=51,
                  a_ld=261 if a_order == "col" else 303, b_ld=199 if b_order == "row" else 301,
-                 has_c=True, beta=0.5, bias=True, act="gelu", a_offset=1,
+                 has_c=True, beta=0.5, bias=True, act="gelu", a_offset=1, split_k=1,
                  force=names.index(f"{dtype}_{a}_{b}_128x128x64_w2x2_m32_{kind}"))
         p = Prepared(c)
         g, out = p.run()

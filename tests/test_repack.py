@@ -10,10 +10,11 @@ from tests.gemm_util import OUT_T, TOL, Case, Prepared, error
 
 pytestmark = pytest.mark.gpu
 
-# 2-byte types take the copies from 2^35 FLOP, fp8 and fp32 from 2^31
+# The cost model decides whether to copy (copies plus the kernel chosen for them against the best
+# direct entry); each case here is one it runs on copies.
 CASES = {
     # fp16, odd leading dimensions in every operand, B row-major, C and GELU
-    "f16_row_row_odd": Case(2603, 2601, 2599, "f16", "row", "row", dist="uniform", alpha=0.75,
+    "f16_row_row_odd": Case(3003, 3001, 2999, "f16", "row", "row", dist="uniform", alpha=0.75,
                             beta=-1.25, has_c=True, act="gelu", seed=71),
     # bf16, column-major A with a padded odd leading dimension, column-major B, bias
     "bf16_col_col_odd": Case(2611, 2603, 2561, "bf16", "col", "col", a_ld=2613, b_ld=2563,
@@ -56,7 +57,7 @@ def test_repacked_products_match_oracle(name):
 
 
 def test_repacked_dyadic_is_bit_exact():
-    c = Case(2603, 2601, 2599, "f16", "row", "row", dist="dyadic", alpha=0.75, beta=-1.25,
+    c = Case(3003, 3001, 2999, "f16", "row", "row", dist="dyadic", alpha=0.75, beta=-1.25,
              has_c=True, bias=True, seed=77)
     p = Prepared(c)
     g, out = p.run()

@@ -17,10 +17,16 @@ from tests.gemm_util import OUT_T, TOL, Case, Prepared, error, sample_indices
 pytestmark = pytest.mark.gpu
 
 
+RING = {"bf16": "bf16_ak_bk_256x256x64_w2x4_m16_ring", "f16": "f16_ak_bk_256x256x64_w2x4_m16_ring",
+        "e4m3": "e4m3_ak_bk_256x256x128_w2x4_m32_ring"}
+
+
 def plan(M, N, K, dtype="bf16", split_k=0):
-    # decomposition 1: no Stream-K, which otherwise takes these last rounds on the ring kernels
+    # the ring entry of the type, planned by the library; decomposition 1: no Stream-K, which
+    # the plan otherwise takes for these last rounds on the rings that have a Stream-K form
+    ring = [H.gemm_config_name(i) for i in range(H.gemm_num_configs())].index(RING[dtype])
     g = H.Gemm(H.make_desc(M, N, K, dtype, (K, 1), (1, K), (N, 1), split_k=split_k,
-                           decomposition=1))
+                           decomposition=1, force_config=ring))
     return g.info, g.workspace_bytes
 
 

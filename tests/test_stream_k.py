@@ -89,8 +89,9 @@ def test_dyadic_stream_k_bits_equal_data_parallel(shape):
 
 
 def test_heuristic_stream_k_at_a_real_shape():
-    # 17 x 17 = 289 tiles: a last round of 33, 64 k-tiles; GELU and bias
-    c = Case(4352, 4352, 4096, "bf16", bias=True, act="gelu", seed=308)
+    # 17 x 17 = 289 tiles: a last round of 33, 64 k-tiles; GELU and bias; the ring entry, with
+    # the library planning the decomposition
+    c = Case(4352, 4352, 4096, "bf16", bias=True, act="gelu", seed=308, force=_index(RING["bf16"]))
     p = Prepared(c)
     g, out = p.run()
     info = g.info
@@ -104,8 +105,10 @@ def test_heuristic_stream_k_at_a_real_shape():
 
 
 @pytest.mark.parametrize("case", [
-    Case(4864, 4096, 4096, "f16", has_c=True, beta=-0.5, alpha=0.75, seed=309),
-    Case(4352, 4352, 4096, "f16", b_order="row", bias=True, act="gelu", seed=310),
+    Case(4864, 4096, 4096, "f16", has_c=True, beta=-0.5, alpha=0.75, seed=309,
+         force=_index(RING["f16"])),
+    Case(4352, 4352, 4096, "f16", b_order="row", bias=True, act="gelu", seed=310,
+         force=_index(RING["f16_bn"])),
     Case(4352, 4352, 4096, "bf16", b_order="row", bias=True, seed=311),
 ], ids=["f16_c", "f16_rowB", "bf16_rowB"])
 def test_heuristic_stream_k_other_types(case):
@@ -136,14 +139,14 @@ def test_stream_k_with_scale_vectors():
 
 def test_stream_k_on_repacked_operands():
     # odd leading dimensions and K: aligned copies of A and B, then Stream-K over the last round
-    # of 18 x 18 = 324 ring tiles (68 left) of 65 k-tiles
-    c = Case(4353, 4353, 4097, "f16", b_order="row", has_c=True, beta=0.5, seed=313)
+    # of 25 x 25 = 625 ring tiles (113 left) of 129 k-tiles
+    c = Case(6145, 6145, 8193, "f16", b_order="row", has_c=True, beta=0.5, seed=313)
     p = Prepared(c)
     g, out = p.run()
     info = g.info
-    assert info.repack == 1 and info.sk_tiles == 68, (info.repack, info.sk_tiles)
+    assert info.repack == 1 and info.sk_tiles == 113, (info.repack, info.sk_tiles)
     got, _ = p.decode_out(out)
     have, want, what = p.oracle_sample(got, seed=13)
     err = error("f16", have, want)
-    print(f"f16 4353^2 x 4097 repack + Stream-K: {what} err={err:.3e}")
+    print(f"f16 6145^2 x 8193 repack + Stream-K: {what} err={err:.3e}")
     assert err <= TOL["f16"], err
