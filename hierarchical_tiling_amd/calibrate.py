@@ -1,6 +1,7 @@
 """Measures the tile table's cost model on the GPU and writes it as C++ source.
 
-    python -m hierarchical_tiling_amd.calibrate --out FILE [--only REGEX] [--reps R]
+    python -m hierarchical_tiling_amd.calibrate --out FILE [--only REGEX] [--reps R] [--passes P]
+    python -m hierarchical_tiling_amd.calibrate --check --out FILE
 
 The library chooses a kernel by predicting each fitting entry's time on the problem ("CUTLASS",
 stanleyjacob.dev, Part IX: the best tile depends on the shape, so the library measures its
@@ -23,7 +24,8 @@ written) from products that the library runs on such copies, and Stream-K launch
 the entry's time for 256 workgroups of one share) against the prediction for their whole tiles.
 
 The output is the source of the library's cost table (csrc/cost_table.cpp); rebuild after
-replacing it.
+replacing it.  With --check the script instead times the library's automatic choice against every
+fitting entry on a fixed set of products and reports how far the choice is from the best.
 """
 from __future__ import annotations
 
@@ -378,9 +380,72 @@ def emit(costs, edges, split, repack, sk, device, out):
         fh.write("\n".join(lines))
 
 
+def check_shapes():
+    """(dtype, M, N, K, A K-major, B K-major, odd leading dimensions) of the choice check: the
+    benchmark's products, square and skinny ones, odd leading dimensions, and seeded random ones."""
+    import random
+    S = [("bf16", 8192, 8192, 8192, True, True, False), ("bf16", 8192, 8192, 8192, True, False, False),
+         ("bf16", 4096, 4096, 4096, True, True, False), ("e4m3", 8192, 8192, 8192, True, True, False),
+         ("f16", 4099, 3071, 2053, True, False, True), ("f32", 256, 256, 256, True, False, False)]
+    for M, N, K in [(3072, 3072, 3072), (2816, 2816, 4096), (1536, 1536, 8192), (2048, 2048, 4096),
+                    (2048, 4096, 2048), (512, 512, 16384), (4352, 4352, 4096), (6144, 6144, 8192),
+                    (1024, 1024, 1024), (768, 768, 4096), (256, 4096, 4096)]:
+        S.append(("bf16", M, N, K, True, True, False))
+    for M, N, K in [(1001, 999, 1003), (2051, 1533, 1027), (1503, 1301, 1101)]:
+        S.append(("f16", M, N, K, True, False, True))
+    S += [("e4m3", 3001, 2999, 2049, True, True, True), ("e4m3", 2048, 2048, 8192, True, True, False),
+          ("f32", 1536, 1536, 1536, True, False, False)]
+    rng = random.Random(7)
+    for _ in range(16):
+        dt = rng.choice(["bf16", "bf16", "f16", "e4m3"])
+        M = rng.randrange(200, 6000) // 8 * 8
+        N = rng.randrange(200, 6000) // 8 * 8
+        K = rng.randrange(256, 8192) // 64 * 64
+        S.append((dt, M, N, K, True, dt == "e4m3" or rng.random() < 0.6, False))
+    return S
+
+
+def check(H, torch, pool, names, reps, out):
+    """Times the automatic choice and every fitting entry (each with the plan the library gives
+    it) on check_shapes(); prints the automatic choice's time over the best measured one and
+    their geometric mean."""
+    import math
+    lines, logsum, n = [], 0.0, 0
+    for dt, M, N, K, ak, bk, odd in check_shapes():
+        t_auto, info = run_case(H, torch, pool, -1, dt, ak, bk, odd, M, N, K, reps, split_k=0,
+                                decomposition=0)
+        best, best_name = t_auto, info.name.decode()
+        for i, name in enumerate(names):
+            d_, ak_, bk_, kind = parse_name(name)
+            if d_ != dt or ak_ != ak or bk_ != bk or kind == "skinny":
+                continue
+            try:
+                t, _ = run_case(H, torch, pool, i, dt, ak, bk, odd, M, N, K, reps, split_k=0,
+                                decomposition=0)
+            except H.GemmError:
+                continue       # the entry does not fit this product
+            if t < best:
+                best, best_name = t, name
+        logsum += math.log(t_auto / best)
+        n += 1
+        line = (f"{dt} {M}x{N}x{K} {'ak' if ak else 'am'}_{'bk' if bk else 'bn'}"
+                f"{' odd' if odd else ''}: auto {info.name.decode()} S{info.split_k}"
+                f"{' copies' if info.repack else ''} {t_auto:.1f} us (predicted "
+                f"{info.predicted_us:.1f}); best {best_name} {best:.1f} us; ratio {t_auto / best:.3f}")
+        print(line, flush=True)
+        lines.append(line)
+    summary = f"{n} products: geometric mean of automatic / best = {math.exp(logsum / n):.4f}"
+    print(summary, flush=True)
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines + [summary]) + "\n")
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--out", required=True)
+    ap.add_argument("--check", action="store_true",
+                    help="instead of measuring the table, time the automatic choice against every "
+                         "fitting entry on a set of products and write the comparison to --out")
     ap.add_argument("--only", default=None, help="regular expression over entry names")
     ap.add_argument("--reps", type=int, default=16)
     ap.add_argument("--passes", type=int, default=5)
@@ -392,6 +457,9 @@ def main(argv=None):
         sys.exit("calibration needs the GPU")
     names = [H.gemm_config_name(i) for i in range(H.gemm_num_configs())]
     pool = Pool(torch)
+    if args.check:
+        check(H, torch, pool, names, args.reps, args.out)
+        return
     import numpy as np
     chosen = [(i, n) for i, n in enumerate(names) if parse_name(n)[3] != "skinny" and
               (not args.only or re.search(args.only, n))]
