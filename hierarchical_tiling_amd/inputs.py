@@ -51,7 +51,8 @@ def quantize(values: np.ndarray, dtype: str) -> np.ndarray:
     bf16 overflows to infinity; e4m3 ("fn", no infinities) saturates to +-448."""
     v = np.ascontiguousarray(values, dtype=np.float64)
     if dtype == "f32":
-        return v.astype(np.float32).view(np.uint32).copy()
+        with np.errstate(over="ignore"):           # beyond the float32 range: infinity
+            return v.astype(np.float32).view(np.uint32).copy()
     if dtype == "f16":
         with np.errstate(over="ignore"):           # beyond 65504: infinity, as IEEE rounding gives
             return v.astype(np.float16).view(np.uint16).copy()
