@@ -33,6 +33,7 @@ SOURCES = [
     ("table_f16.hip", HIP),
     ("table_e4m3.hip", HIP),
     ("table_f32.hip", HIP),
+    ("table_pp.hip", HIP),
     ("table.cpp", HIP),
     ("cost_table.cpp", HIP),
     ("reduce.hip", HIP),
@@ -43,7 +44,7 @@ SOURCES = [
 ]
 
 
-HEADERS = [os.path.join(CSRC, "kernels.h"), os.path.join(CSRC, "gemm_internal.h"),
+HEADERS = [os.path.join(CSRC, "kernels.h"), os.path.join(CSRC, "pingpong.h"), os.path.join(CSRC, "gemm_internal.h"),
            os.path.join(CSRC, "atom_maps.h"),
            os.path.join(ROOT, "include", "htgemm.h"), os.path.join(ROOT, "include", "htlayout.h")]
 

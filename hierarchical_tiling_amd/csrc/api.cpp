@@ -371,6 +371,17 @@ int choose(const gemm_handle_s& h, bool vec_a, bool vec_b, bool want_vec, int sp
     least = std::min(least, u);
   }
   if (cand.empty()) return -1;
+  // Stream-K asked for: the entries that have a Stream-K form, where one fits
+  if (h.d.decomposition == 2) {
+    std::vector<std::pair<int, double>> sk;
+    for (const auto& c : cand)
+      if (t[c.first].launch_sk) sk.push_back(c);
+    if (!sk.empty()) {
+      cand.swap(sk);
+      least = std::numeric_limits<double>::infinity();
+      for (const auto& c : cand) least = std::min(least, c.second);
+    }
+  }
   int best = -1;
   double best_us = 0.0;
   if (std::isfinite(least)) {

@@ -13,6 +13,7 @@ const KernelEntry* table_bf16_dma(int* n);
 const KernelEntry* table_f16(int* n);
 const KernelEntry* table_f32(int* n);
 const KernelEntry* table_e4m3(int* n);
+const KernelEntry* table_pp(int* n);
 
 namespace {
 
@@ -34,6 +35,7 @@ struct Combined {
     append(table_f16);
     append(table_f32);
     append(table_e4m3);
+    append(table_pp);
     // each entry's measured costs, matched by name
     for (int i = 0; i < n; ++i) {
       e[i].cost = nullptr;

@@ -149,7 +149,9 @@ typedef struct gemm_desc {
   int32_t decomposition;      /* how output tiles are spread over the CUs: 0 = the library       */
                               /* decides, 1 = no Stream-K (a tile per workgroup, K slices as     */
                               /* split_k says), 2 = Stream-K, and no other split, wherever the   */
-                              /* chosen kernel has a Stream-K form (gemm_info.sk_tiles > 0 then);*/
+                              /* chosen kernel has a Stream-K form (gemm_info.sk_tiles > 0 then; */
+                              /* with 2 the library chooses among the kernels that have one,     */
+                              /* if any fits);                                                   */
                               /* 2 is refused with split_k > 1, a batch, a grouped handle or a   */
                               /* reduction                                                       */
 } gemm_desc;

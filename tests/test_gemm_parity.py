@@ -26,7 +26,7 @@ def case_for_entry(i, name):
     dtype = name.split("_")[0]
     a_order = "row" if "_ak_" in name else "col"
     b_order = "col" if "_bk_" in name else "row"
-    vec = name.endswith("_vec") or "_dma" in name or "_ring" in name
+    vec = name.endswith("_vec") or "_dma" in name or "_ring" in name or ("_pp" in name)
     # several tiles and a ragged tail in M and N; K spans several k-tiles with a tail
     if "_skinny" in name:
         # M below one 16-row atom, a ragged last column block, a K tail inside the last k-step,

@@ -109,7 +109,8 @@ def test_heuristic_stream_k_at_a_real_shape():
          force=_index(RING["f16"])),
     Case(4352, 4352, 4096, "f16", b_order="row", bias=True, act="gelu", seed=310,
          force=_index(RING["f16_bn"])),
-    Case(4352, 4352, 4096, "bf16", b_order="row", bias=True, seed=311),
+    Case(4352, 4352, 4096, "bf16", b_order="row", bias=True, seed=311,
+         force=_index(RING["bf16_bn"])),
 ], ids=["f16_c", "f16_rowB", "bf16_rowB"])
 def test_heuristic_stream_k_other_types(case):
     p = Prepared(case)
@@ -139,8 +140,10 @@ def test_stream_k_with_scale_vectors():
 
 def test_stream_k_on_repacked_operands():
     # odd leading dimensions and K: aligned copies of A and B, then Stream-K over the last round
-    # of 25 x 25 = 625 ring tiles (113 left) of 129 k-tiles
-    c = Case(6145, 6145, 8193, "f16", b_order="row", has_c=True, beta=0.5, seed=313)
+    # of 25 x 25 = 625 ring tiles (113 left) of 129 k-tiles (asked for: the kernel the library
+    # prefers for the copies, the ping-pong kernel, has no Stream-K form)
+    c = Case(6145, 6145, 8193, "f16", b_order="row", has_c=True, beta=0.5, seed=313,
+             decomposition=2)
     p = Prepared(c)
     g, out = p.run()
     info = g.info
