@@ -22,7 +22,7 @@ import os
 from collections import defaultdict
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-SOURCES = ("csrc/kernels.h", "csrc/gemm_internal.h", "csrc/atom_maps.h")
+SOURCES = ("csrc/kernels.h", "csrc/pingpong.h", "csrc/gemm_internal.h", "csrc/atom_maps.h")
 COPY_BYTES_DEFAULT = 1 << 30
 
 
