@@ -148,6 +148,11 @@ BATCH_CASES = {
                      has_c=True, beta=-0.5, alpha=2.0),
     "f16_rowB_silu_L3": dict(L=3, M=96, N=128, K=64, dtype="f16", b_order="row", act="silu",
                              col_scale=True),
+    # ping-pong kernel, K-major and row-major B
+    "bf16_pp_L3": dict(L=3, M=264, N=328, K=320, dtype="bf16", bias=True, act="gelu",
+                       force="bf16_ak_bk_256x256x64_w2x4_m16_pp"),
+    "f16_pp_rowB_L2": dict(L=2, M=264, N=328, K=200, dtype="f16", b_order="row", has_c=True,
+                           beta=-0.5, force="f16_ak_bn_256x256x64_w2x4_m16_pp"),
 }
 
 
@@ -214,6 +219,11 @@ GROUP_CASES = {
     "bf16_ring_moe": dict(sizes=[300, 0, 1, 517, 211], N=264, K=320, dtype="bf16", bias=True,
                           act="silu", row_scale=True, col_scale=True,
                           force="bf16_ak_bk_256x256x64_w2x4_m16_ring"),
+    # ping-pong kernel: the same group shapes
+    "bf16_pp_moe": dict(sizes=[300, 0, 1, 517, 211], N=264, K=320, dtype="bf16", bias=True,
+                        act="gelu", row_scale=True, force="bf16_ak_bk_256x256x64_w2x4_m16_pp"),
+    "e4m3_pp_moe": dict(sizes=[260, 3, 0, 250], N=520, K=384, dtype="e4m3", scale_a=0.5,
+                        scale_b=0.25, force="e4m3_ak_bk_256x256x128_w2x4_m16_pp"),
     "bf16_lib_moe_c": dict(sizes=[17, 128, 0, 95], N=200, K=128, dtype="bf16", has_c=True,
                            beta=0.5),
     # MN-major B per expert (tiled kernel), GELU
@@ -323,6 +333,10 @@ RSQ_CASES = {
     "e4m3_ring_scales": dict(M=264, N=328, K=256, dtype="e4m3", scale_a=0.5, scale_b=0.25,
                              col_scale=True, force="e4m3_ak_bk_256x256x128_w2x4_m32_ring"),
     "f32_uniform": dict(M=130, N=300, K=64, dtype="f32", dist="uniform"),
+    "bf16_pp_gelu": dict(M=300, N=600, K=320, dtype="bf16", bias=True, act="gelu",
+                         force="bf16_ak_bk_256x256x64_w2x4_m16_pp"),
+    "e4m3_pp_scales": dict(M=264, N=328, K=256, dtype="e4m3", scale_a=0.5, scale_b=0.25,
+                           col_scale=True, force="e4m3_ak_bk_256x256x128_w2x4_m16_pp"),
     # 16 rows would take the streaming skinny kernel, which has no row reduction
     "bf16_m16": dict(M=16, N=1040, K=512, dtype="bf16"),
 }
