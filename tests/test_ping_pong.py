@@ -100,3 +100,16 @@ def test_same_bits_as_the_split_ring():
         _, out2 = p2.run()
         _, bits_ring = p2.decode_out(out2)
         assert int((bits_pp != bits_ring).sum()) == 0, key
+
+
+@pytest.mark.parametrize("key", ["bf16", "e4m3", "f16_bn"])
+def test_padded_leading_dimensions(key):
+    # rows of A and B (and of C and D) longer than the product reads: the DMA's row strides and
+    # range checks use the leading dimensions, not K or N (each a multiple of 16 bytes)
+    dtype = key.split("_")[0]
+    K = DEPTHS[dtype][2] * 2
+    pad = 16 if dtype == "e4m3" else 8
+    b_ld = (520 + 3 * pad) if key.endswith("_bn") else K + 5 * pad
+    c = _case(key, 300, 520, K, a_ld=K + 3 * pad, b_ld=b_ld, c_ld=536, d_ld=544, has_c=True,
+              beta=0.25, bias=True, act="gelu", seed=660 + list(PP).index(key))
+    _check(c)
