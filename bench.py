@@ -145,8 +145,9 @@ def measure(name, steps, warmup, device, clock_sampler=None):
         ends[i].record(stream)
     torch.cuda.synchronize()
     per = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
+    kclock = kernel_clock(H, g, info, step) if clock_sampler is not None else None
     clock = None
-    if clock_sampler is not None:
+    if clock_sampler is not None and not isinstance(clock_sampler, NoSampler):
         # shader clock while the kernel runs back to back for about a second (its own pass)
         n_sus = max(1, int(1000.0 / max(launch_ms, 1e-3)))
         with clock_sampler:
@@ -178,7 +179,56 @@ def measure(name, steps, warmup, device, clock_sampler=None):
            "tflops": round(flops / (wall_ms * 1e-3) / 1e12, 1), "roofline": roof}
     if clock is not None:
         res["sclk_mhz_during_sustained_run"] = clock
+    if kclock is not None:
+        mhz = kclock["median"]
+        peak_at = roof["peak"] * mhz / MAX_SCLK_MHZ
+        kclock["peak_at_this_clock"] = round(peak_at, 1)
+        kclock["frac_at_this_clock"] = round(roof["achieved"] / peak_at, 4)
+        res["sclk_mhz_in_kernel"] = kclock
     return res, host[0]
+
+
+def kernel_clock(H, g, info, step, launches=10):
+    """The shader clock the product kernel ran at, from its own counters: the handle's clock
+    record (gemm_set_clock_record) over `launches` back-to-back launches after the timed region;
+    the last launch's per-workgroup records give (shader cycles) / (real-time ticks) x 100 MHz.
+    None where the chosen kernel does not record."""
+    import torch
+    if not info.name.decode().endswith("_pp"):
+        return None
+    n = int(info.grid)
+    rec = torch.zeros(4 * n, dtype=torch.int64, device="cuda")
+    H.gemm_set_clock_record(g.handle, rec, n)
+    for i in range(launches):
+        step(i)
+    torch.cuda.synchronize()
+    H.gemm_set_clock_record(g.handle, None, 0)
+    r = rec.cpu().numpy().astype(np.float64).reshape(n, 4)
+    ok = (r[:, 3] > r[:, 2]) & (r[:, 1] > r[:, 0])
+    if not ok.any():
+        return None
+    mhz = (r[ok, 1] - r[ok, 0]) / (r[ok, 3] - r[ok, 2]) * REALTIME_MHZ
+    return {"median": round(float(np.median(mhz)), 1), "p10": round(float(np.percentile(mhz, 10)), 1),
+            "p90": round(float(np.percentile(mhz, 90)), 1), "workgroups": int(ok.sum()),
+            "launches": launches, "method": "s_memtime / s_memrealtime per workgroup, last launch"}
+
+
+# the constant-rate counter that s_memrealtime reads, and the maximum shader clock (MI355X)
+REALTIME_MHZ = 100.0
+MAX_SCLK_MHZ = 2400.0
+
+
+class NoSampler:
+    """Stands in for ClockSampler where only the in-kernel clock is wanted."""
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        return False
+
+    def summary(self):
+        return None
 
 
 class ClockSampler:
@@ -354,7 +404,8 @@ def main():
         for name in SUB_WORKLOADS:
             if name == args.workload:
                 continue
-            r, _ = measure(name, args.sub_steps, args.sub_warmup, dev)
+            r, _ = measure(name, args.sub_steps, args.sub_warmup, dev,
+                           clock_sampler=NoSampler() if not args.no_clock else None)
             subs.append(r)
             torch.cuda.empty_cache()
     name = args.workload
@@ -368,6 +419,7 @@ def main():
                    "grid": main_res["grid"], "input_sets": SETS[name]},
         "roofline": main_res["roofline"],
         "sclk_mhz_during_sustained_run": main_res.get("sclk_mhz_during_sustained_run"),
+        "sclk_mhz_in_kernel": main_res.get("sclk_mhz_in_kernel"),
         "sub_results": subs,
         "run": run_metadata(threads),
     }

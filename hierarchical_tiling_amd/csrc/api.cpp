@@ -64,6 +64,9 @@ struct gemm_handle_s {
   int repack;
   int64_t kp;
   size_t repack_bytes_a, repack_bytes_b;
+  // clock record of the product kernel's launches (gemm_set_clock_record), or nullptr
+  unsigned long long* clock_rec;
+  int64_t clock_cap;
 };
 
 namespace {
@@ -900,6 +903,8 @@ int run_impl(gemm_t h, const void* A, const void* B, const void* C, void* D, con
     const int64_t span = ((d.M - 1) * d.c_stride_m + (d.N - 1) * d.c_stride_n + 1) * (int64_t)out_sz;
     p.c_span = span < (int64_t(1) << 31) - 64 ? span : 0;
   }
+  p.clock_rec = h->clock_rec;
+  p.clock_cap = h->clock_rec ? h->clock_cap : 0;
   int64_t grid = int64_t(p.tiles_m) * p.tiles_n;
   unsigned gz = (unsigned)p.batch;
   if (offsets) {
@@ -977,6 +982,14 @@ int gemm_run(gemm_t h, const void* A, const void* B, const void* C, void* D, con
     return GEMM_ERR_INVALID_ARG;
   return run_impl(h, A, B, C, D, bias, nullptr, nullptr, alpha, beta, scale_a, scale_b,
                   workspace, nullptr, nullptr, nullptr, stream);
+}
+
+int gemm_set_clock_record(gemm_t h, uint64_t* records, int64_t max_workgroups) {
+  if (!h || h->magic != kMagic) return GEMM_ERR_BAD_HANDLE;
+  if (records && (max_workgroups < 0 || !aligned(records, 8))) return GEMM_ERR_INVALID_ARG;
+  h->clock_rec = reinterpret_cast<unsigned long long*>(records);
+  h->clock_cap = records ? max_workgroups : 0;
+  return GEMM_OK;
 }
 
 int gemm_run_ex(gemm_t h, const gemm_args* a, void* stream) {

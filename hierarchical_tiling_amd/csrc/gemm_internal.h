@@ -67,6 +67,12 @@ struct KParams {
   // k-tile iterations of the tiles from tile order tile_base on; pieces of shared tiles go to
   // compact BM x BN slots of the workspace (2 per workgroup).
   int sk_tiles, sk_nkt, sk_wgs;
+  // Clock record (kernels that support it: the ping-pong kernel): workgroup w < clock_cap of the
+  // launch (linear id over x, y, z) writes clock_rec[4w .. 4w + 3] = the shader-clock counter at
+  // its start and end, then the constant-rate real-time counter at its start and end; nullptr
+  // otherwise.
+  unsigned long long* clock_rec;
+  int64_t clock_cap;
 };
 
 typedef hipError_t (*launch_fn)(const KParams&, hipStream_t, dim3 grid);

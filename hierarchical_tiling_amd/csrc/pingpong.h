@@ -46,6 +46,14 @@ __global__ __launch_bounds__(512, 1) void gemm_pp(const KParams p_) {
   KParams p;
   int pid, nwg;
   if (!problem_view<256>(p_, p, pid, nwg)) return;
+  // opt-in clock record of this workgroup (a uniform branch on a kernel argument)
+  const int64_t rec_id = blockIdx.x + (int64_t)gridDim.x * (blockIdx.y + (int64_t)gridDim.y * blockIdx.z);
+  const bool rec = p_.clock_rec != nullptr && rec_id < p_.clock_cap;
+  unsigned long long clk0 = 0, rt0 = 0;
+  if (rec) {
+    clk0 = __builtin_amdgcn_s_memtime();
+    rt0 = __builtin_amdgcn_s_memrealtime();
+  }
   constexpr int MI = 16;
   typedef Atom<DT, MI> At;
   typedef typename At::acc_t acc_t;
@@ -246,6 +254,16 @@ __global__ __launch_bounds__(512, 1) void gemm_pp(const KParams p_) {
   } else {
     epilogue<DT, MI, BM, BN, WTM, WTN, RM, RN, NT, sizeof(lds)>(pe, acc, lds, m0, n0, g, wq, lane,
                                                                 tid, nk == 0);
+  }
+  if (rec) {
+    const unsigned long long clk1 = __builtin_amdgcn_s_memtime(), rt1 = __builtin_amdgcn_s_memrealtime();
+    if (tid == 0) {
+      unsigned long long* r = p_.clock_rec + 4 * rec_id;
+      r[0] = clk0;
+      r[1] = clk1;
+      r[2] = rt0;
+      r[3] = rt1;
+    }
   }
 }
 

@@ -125,6 +125,7 @@ def lib():
         "gemm_config_name": ([i32, ctypes.c_char_p, sz], i32),
         "gemm_atom_layouts": ([i32, i32, ctypes.c_char_p, ctypes.c_char_p, sz], i32),
         "gemm_probe_atom": ([i32, i32, vp, vp], i32),
+        "gemm_set_clock_record": ([vp, vp, i64], i32),
         "ht_layout_eval": ([cp, ctypes.POINTER(i64), i32, ctypes.POINTER(i64)], i32),
         "ht_layout_eval_str": ([cp, cp, ctypes.POINTER(i64)], i32),
         "ht_layout_size": ([cp, ctypes.POINTER(i64)], i32),
@@ -153,7 +154,7 @@ EXPORTED = ["gemm_create", "gemm_workspace_size", "gemm_run", "gemm_run_ex", "ge
             "gemm_destroy",
             "gemm_status_string",
             "gemm_get_info", "gemm_num_configs", "gemm_config_name", "gemm_atom_layouts",
-            "gemm_probe_atom", "ht_layout_eval",
+            "gemm_probe_atom", "gemm_set_clock_record", "ht_layout_eval",
             "ht_layout_eval_str",
             "ht_layout_size", "ht_layout_table", "ht_layout_coalesce", "ht_layout_compose",
             "ht_layout_complement", "ht_layout_logical_divide", "ht_layout_zipped_divide",
@@ -259,6 +260,12 @@ def gemm_atom_layouts(dtype: str, mi: int):
     c = ctypes.create_string_buffer(256)
     _check(lib().gemm_atom_layouts(DTYPES[dtype], mi, a, c, 256), "gemm_atom_layouts")
     return a.value.decode(), c.value.decode()
+
+
+def gemm_set_clock_record(h, records, max_workgroups: int):
+    """records: a device tensor of at least 4 * max_workgroups int64 values, or None (off)."""
+    _check(lib().gemm_set_clock_record(h, _addr(records), max_workgroups if records is not None else 0),
+           "gemm_set_clock_record")
 
 
 def gemm_probe_atom(dtype: str, mi: int, out, stream=None):

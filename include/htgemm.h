@@ -34,12 +34,15 @@
  *   gemm_run_ex         the same with the arguments in a struct, including the scale vectors.
  *   gemm_run_grouped    a grouped GEMM whose groups split M by device offsets.
  *   gemm_run_problems   a grouped GEMM of independent problems of any shapes.
+ *   gemm_set_clock_record  asks the product kernel to record the clock of each launch
+ *                       (measurement).
  *   gemm_destroy        frees the handle.
  *
  * Ownership: the caller owns every device buffer (A, B, C, D, bias, row_scale, col_scale,
  * workspace) and the stream.
- * A handle holds host memory only and is immutable after gemm_create, so one handle may be run
- * concurrently on several streams.  Nothing throws across this interface; every function returns
+ * A handle holds host memory only and is immutable after gemm_create (except for the clock
+ * record that gemm_set_clock_record attaches), so one handle may be run concurrently on several
+ * streams.  Nothing throws across this interface; every function returns
  * a status code (GEMM_OK == 0) that gemm_status_string() describes.
  *
  * Element addressing: element (i, j) of an operand with strides (s0, s1) is at element offset
@@ -327,6 +330,22 @@ typedef struct gemm_info {
 } gemm_info;
 
 int gemm_get_info(gemm_t h, gemm_info* info);
+
+/* Clock record, for measurement ("CuTe DSL / CUDA Tile" post, "Build the benchmark before tuning
+ * the tile": record the conditions a number was measured under).  After this call, every launch
+ * of the handle's product kernel has each workgroup w < max_workgroups (its linear id over the
+ * launch's x, y and z) write four 64-bit values to records[4w .. 4w + 3]: the shader-clock
+ * counter (s_memtime) at the workgroup's start and at its end, then the constant-rate real-time
+ * counter (s_memrealtime; 100 MHz on MI355X) at its start and at its end, so that
+ * (records[4w+1] - records[4w]) / (records[4w+3] - records[4w+2]) x 100 MHz is the mean shader
+ * clock the workgroup ran at.  records is a device buffer of 4 * max_workgroups uint64_t, owned
+ * by the caller, 8-byte aligned; later launches overwrite it; records == NULL turns recording
+ * off.  Only the ping-pong kernel (entries whose name ends in "_pp") records; other kernels, the
+ * copy, sum and fix-up kernels leave the buffer untouched.  The cost is four scalar timer reads
+ * and one store per workgroup.  Not thread-safe against concurrent runs of the same handle.
+ * Returns GEMM_ERR_BAD_HANDLE, or GEMM_ERR_INVALID_ARG for a negative count or a misaligned
+ * buffer. */
+int gemm_set_clock_record(gemm_t h, uint64_t* records, int64_t max_workgroups);
 
 /* Number of entries in the compiled tile table, and the name of entry `idx`. */
 int gemm_num_configs(void);

@@ -569,3 +569,18 @@ def test_kernel_choice_for_the_misjudged_fp8_product(fake_gfx950):
     buffers and runs the split ring on them (81 us)."""
     info = _info(H.make_desc(3001, 2999, 2049, "e4m3", (2049, 1), (1, 2049), (2999, 1)))
     assert info.repack == 1 and info.name == b"e4m3_ak_bk_256x256x128_w2x4_m32_ring"
+
+
+def test_clock_record_arguments(fake_gfx950):
+    # host-side checks only: no device memory is touched
+    import ctypes
+    h = H.gemm_create(desc(M=512, N=512, K=256))
+    try:
+        L = H.lib()
+        assert L.gemm_set_clock_record(None, None, 0) == 7  # GEMM_ERR_BAD_HANDLE
+        assert L.gemm_set_clock_record(h, ctypes.c_void_p(0x1000), -1) == H.GEMM_ERR_INVALID_ARG
+        assert L.gemm_set_clock_record(h, ctypes.c_void_p(0x1004), 4) == H.GEMM_ERR_INVALID_ARG
+        assert L.gemm_set_clock_record(h, ctypes.c_void_p(0x1000), 4) == 0
+        assert L.gemm_set_clock_record(h, None, 0) == 0
+    finally:
+        H.gemm_destroy(h)

@@ -113,3 +113,33 @@ def test_padded_leading_dimensions(key):
     c = _case(key, 300, 520, K, a_ld=K + 3 * pad, b_ld=b_ld, c_ld=536, d_ld=544, has_c=True,
               beta=0.25, bias=True, act="gelu", seed=660 + list(PP).index(key))
     _check(c)
+
+
+def test_clock_record():
+    # the opt-in clock record: every workgroup of the launch writes its shader-clock and
+    # real-time counters at start and end; the product is unchanged, and turning the record off
+    # leaves the buffer alone
+    import torch
+    c = _case("bf16", 520, 776, 512, bias=True, act="gelu", seed=670)
+    p = Prepared(c)
+    g, out = p.run()
+    n = int(g.info.grid)
+    assert n == 3 * 4
+    rec = torch.zeros(4 * n + 4, dtype=torch.int64, device="cuda")
+    H.gemm_set_clock_record(g.handle, rec, n)
+    g2, out2 = p.run(g=g)
+    torch.cuda.synchronize()
+    r = rec.cpu().numpy().reshape(-1, 4)
+    assert (r[n] == 0).all(), "a workgroup past max_workgroups wrote"
+    r = r[:n].astype(np.float64)
+    assert (r[:, 1] > r[:, 0]).all() and (r[:, 3] > r[:, 2]).all()
+    mhz = (r[:, 1] - r[:, 0]) / (r[:, 3] - r[:, 2]) * 100.0
+    print(f"clock record: {np.median(mhz):.0f} MHz median over {n} workgroups")
+    assert ((mhz > 100) & (mhz < 3000)).all(), mhz
+    got, _ = p.decode_out(out2)
+    assert error("bf16", got, p.oracle_full()) <= TOL["bf16"]
+    H.gemm_set_clock_record(g.handle, None, 0)
+    rec.zero_()
+    p.run(g=g)
+    torch.cuda.synchronize()
+    assert int(rec.abs().sum()) == 0
