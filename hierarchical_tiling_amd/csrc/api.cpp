@@ -206,6 +206,26 @@ void plan_split(const KernelEntry& e, const gemm_desc& d, int req, int* S, int64
     *S = (int)cdiv(nkt, per);           // no empty slice
     return;
   }
+  if (e.skinny) {
+    // The streaming kernel (no measured costs; chosen by its shape) pulls B from HBM.  A grid of
+    // few column blocks with long K leaves most CUs idle, so K is cut into S slices (fp32 planes
+    // of 16 x N, summed by the split-K kernel): the largest power of two S <= 8 that keeps at
+    // least 32 blocks of K per slice and at most 512 workgroups, and only below 64 column blocks
+    // or from 256 blocks of K.  Measured on MI355X (bf16, microseconds, unsplit -> chosen):
+    // 16x16x32768 31.8 -> 11.7 (S 8), 16x256x32768 33.1 -> 12.4 (8), 16x1024x8192 11.0 -> 10.1
+    // (4), 16x2048x32768 60.5 -> 33.2 (8), 16x4096x16384 38.1 -> 36.0 (4); left unsplit:
+    // 16x4096x4096 8.3 (S 2: 11.2), 16x8192x8192 33.8 (S 2: 32.2, S 4: 38.1), e4m3 8x4096x4096
+    // 7.1 (S 2: 10.1).
+    if (tiles >= 64 && nkt < 256) return;
+    int64_t s = 1;
+    while (2 * s <= std::min<int64_t>(8, e.max_split_k) && nkt / (2 * s) >= 32 && tiles * 2 * s <= 512)
+      s *= 2;
+    if (s < 2) return;
+    const int64_t per = cdiv(nkt, s);
+    *kps = per * e.bk;
+    *S = (int)cdiv(nkt, per);
+    return;
+  }
   if (tiles >= kCUs || !e.cost) return;
   const double out_bytes = double(d.M) * double(d.N) * dtype_size(d.d_type);
   double best = launch_us(*e.cost, tiles, nkt);
@@ -359,9 +379,11 @@ int choose(const gemm_handle_s& h, bool vec_a, bool vec_b, bool want_vec, int sp
   const KernelEntry* t = table();
   const bool need_split = split_req > 1;
   if (us) *us = 0.0;
-  for (int i = 0; i < table_size() && !need_split && !h.d.ragged_m && !h.d.grouped && !h.d.has_row_sumsq &&
+  for (int i = 0; i < table_size() && !h.d.ragged_m && !h.d.grouped && !h.d.has_row_sumsq &&
                   !h.d.has_col_sum; ++i)
-    if (t[i].skinny && (t[i].vec != 0) == want_vec && entry_fits(t[i], h, vec_a, vec_b)) return i;
+    if (t[i].skinny && (t[i].vec != 0) == want_vec && (!need_split || t[i].max_split_k > 1) &&
+        entry_fits(t[i], h, vec_a, vec_b))
+      return i;
   std::vector<std::pair<int, double>> cand;  // fitting entries and their predicted times
   double least = std::numeric_limits<double>::infinity();
   for (int i = 0; i < table_size(); ++i) {

@@ -2188,17 +2188,20 @@ __global__ __launch_bounds__(WK * 64, OCC) void gemm_skinny_dma(const KParams p_
   const int64_t n0 = (int64_t)blockIdx.x * BN;
   const int lr = frag_row<DT, 16>(lane), lg = frag_chunk<DT, 16>(lane);
 
-  // K split: wave w owns blocks [w*per, min((w+1)*per, nb))
-  const int64_t nb = (p.K + BKE - 1) / BKE;
+  // This workgroup's K range: all of K, or with a split along K (too few column blocks to fill
+  // the GPU) slice blockIdx.y.  Within it, wave w owns blocks [w*per, min((w+1)*per, nb)).
+  const KRange kr = k_range(p);
+  const int64_t K = uniform_i64(kr.len);
+  const int64_t nb = (K + BKE - 1) / BKE;
   const int64_t per = (nb + WK - 1) / WK;
   const int64_t b0 = wave * per;
   const int nloc = (int)max((int64_t)0, min(b0 + per, nb) - b0);
 
-  const char* a_base = uniform_ptr((const char*)p.A);
-  const char* b_base = uniform_ptr((const char*)p.B + n0 * p.ldb * SZ);
-  const int64_t a_span = uniform_i64(((p.M - 1) * p.lda + p.K) * SZ);
-  const int64_t b_span = uniform_i64(((min((int64_t)BN, p.N - n0) - 1) * p.ldb + p.K) * SZ);
-  const int64_t kbytes = p.K * SZ;
+  const char* a_base = uniform_ptr((const char*)p.A + kr.begin * SZ);
+  const char* b_base = uniform_ptr((const char*)p.B + (n0 * p.ldb + kr.begin) * SZ);
+  const int64_t a_span = uniform_i64(((p.M - 1) * p.lda + K) * SZ);
+  const int64_t b_span = uniform_i64(((min((int64_t)BN, p.N - n0) - 1) * p.ldb + K) * SZ);
+  const int64_t kbytes = K * SZ;
   // DMA lane: LDS row 8c + lane/8 of the block, slot lane%8, holding logical chunk slot ^ key(row)
   auto key = [](int row) { return row_key<8>(row); };
 
@@ -2278,14 +2281,18 @@ __global__ __launch_bounds__(WK * 64, OCC) void gemm_skinny_dma(const KParams p_
     float sum = 0.f;
 #pragma unroll
     for (int w = 0; w < WK; ++w) sum += part[((w * NBW + c / 16) * 16 + row) * 17 + c % 16];
-    O::store(p.D, row * p.d_sm + col * p.d_sn, finish_elem<ODT>(p, row, col, sum));
+    if (p.split_k > 1)  // raw sums of this K slice to its plane; gemm_splitk_reduce finishes
+      p.workspace[(int64_t)blockIdx.y * p.M * p.N + row * p.N + col] = sum;
+    else
+      O::store(p.D, row * p.d_sm + col * p.d_sn, finish_elem<ODT>(p, row, col, sum));
   }
 }
 
 template <int DT, int WK, int NBW, int R, int OCC>
 static hipError_t launch_skinny_dma(const KParams& p, hipStream_t s, dim3) {
   constexpr int BN = NBW * 16;
-  const dim3 grid((unsigned)((p.N + BN - 1) / BN), 1, (unsigned)p.batch);
+  const dim3 grid((unsigned)((p.N + BN - 1) / BN), (unsigned)(p.split_k > 1 ? p.split_k : 1),
+                  (unsigned)p.batch);
   hipLaunchKernelGGL((gemm_skinny_dma<DT, WK, NBW, R, OCC>), grid, dim3(WK * 64), 0, s, p);
   return hipGetLastError();
 }
@@ -2330,9 +2337,10 @@ static hipError_t launch_tiled(const KParams& p, hipStream_t s, dim3 grid) {
    &launch_ring<DT, WM, WN, MI, NB, false, false>, 0, MI, 8, 1,                                   \
    &launch_ring<DT, WM, WN, MI, NB, false, true>}
 
-// Streaming skinny entries: bm = 16 rows, bn = 16*NBW columns, bk = one 128-byte block of K.
+// Streaming skinny entries: bm = 16 rows, bn = 16*NBW columns, bk = one 128-byte block of K;
+// K slices of whole blocks when the column blocks do not fill the GPU.
 #define HT_SKINNY_DMA(NAME, DT, WK, NBW, R, OCC)                                                  \
-  {NAME, DT, 1, 1, 1, 1, 16, NBW * 16, 128 / Ty<DT>::SZ, WK, R, WK * R * (NBW + 1) * 16 * 128, 1, \
+  {NAME, DT, 1, 1, 1, 1, 16, NBW * 16, 128 / Ty<DT>::SZ, WK, R, WK * R * (NBW + 1) * 16 * 128, 64, \
    &launch_skinny_dma<DT, WK, NBW, R, OCC>, 0, 16, 8, 0}
 
 // Skinny entries: bm = 16 rows, bn = WN*NBW*16 columns per workgroup, bk = one MFMA k-step (no

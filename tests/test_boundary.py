@@ -204,10 +204,11 @@ def test_split_k_plan_and_workspace(fake_gfx950):
     # split_k = 1 never splits
     assert _info(desc(M=1024, N=1024, K=65536, a_strides=(65536, 1), b_strides=(1, 65536),
                       d_strides=(1024, 1), split_k=1)).split_k == 1
-    # the streaming skinny kernel has no split: forcing one selects a tiled kernel
+    # the streaming skinny kernel takes a forced split along K; the register-staged skinny
+    # kernel has none, so forcing both is refused
     names = [H.gemm_config_name(i) for i in range(H.gemm_num_configs())]
     sk = _info(H.make_desc(16, 16384, 8192, "e4m3", (8192, 1), (1, 8192), (16384, 1), split_k=2))
-    assert b"skinny" not in sk.name and sk.split_k == 2
+    assert b"skinny_dma" in sk.name and sk.split_k == 2
     assert status_of(desc(M=16, force_config=names.index("bf16_ak_bk_16x32_w8_skinny"), split_k=2)) == 8
 
 
@@ -584,3 +585,18 @@ def test_clock_record_arguments(fake_gfx950):
         assert L.gemm_set_clock_record(h, None, 0) == 0
     finally:
         H.gemm_destroy(h)
+
+
+@pytest.mark.parametrize("shape,dtype,split", [
+    # few column blocks and long K: K slices (measured 31.8 -> 11.7, 33.1 -> 12.4,
+    # 11.0 -> 10.1, 60.5 -> 33.2 us)
+    ((16, 16, 32768), "bf16", 8), ((16, 256, 32768), "bf16", 8), ((16, 1024, 8192), "bf16", 4),
+    ((16, 2048, 32768), "bf16", 8),
+    # enough column blocks or short K: no split (measured faster unsplit)
+    ((16, 4096, 4096), "bf16", 1), ((16, 8192, 8192), "bf16", 1), ((8, 4096, 4096), "e4m3", 1),
+    ((16, 16384, 8192), "e4m3", 1),
+])
+def test_skinny_split_choice(fake_gfx950, shape, dtype, split):
+    M, N, K = shape
+    info = _info(H.make_desc(M, N, K, dtype, (K, 1), (1, K), (N, 1)))
+    assert b"skinny_dma" in info.name and info.split_k == split, (info.name, info.split_k)
