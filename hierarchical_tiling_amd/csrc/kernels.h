@@ -1092,9 +1092,26 @@ __device__ __forceinline__ float load_c(__amdgpu_buffer_rsrc_t r, uint32_t off) 
 // row-major C is staged the same way before phase 1 -- 16-byte chunks in D's grid, through
 // realigned loads where C's own alignment differs -- and each lane reads its C values from the
 // LDS position its result then overwrites.
+//
+// FORM selects a copy of the epilogue compiled for one class of launch (epilogue_form): 1 = no
+// C, no scale vectors, no fused reductions, D row-major in whole 16-byte rows; 0 = every case.
+// The epilogue runs once per tile and is unrolled over the wave tile: with every case compiled
+// in, its executed path is scattered over a long stretch of code that each tile fetches again,
+// and the specialised copy keeps it short and straight.  (A copy for a row-major C staged
+// through LDS ran out of registers in the ping-pong kernel.)
 // ------------------------------------------------------------------------------------------
+template <int DT>
+__device__ __forceinline__ int epilogue_form(const KParams& p) {
+  constexpr int OSZ = (int)sizeof(typename OutBits<out_dtype(DT)>::T);
+  return !p.has_c && !p.has_row_scale && !p.has_col_scale && !p.rsq_ws && !p.csum_ws &&
+                 p.d_sn == 1 && (p.d_sm * OSZ) % 16 == 0 &&
+                 (reinterpret_cast<uintptr_t>(p.D) % 16) == 0
+             ? 1
+             : 0;
+}
+
 template <int DT, int MI, int BM, int BN, int WTM, int WTN, int RM, int RN, int NT,
-          size_t LDS_BYTES, class AccT>
+          size_t LDS_BYTES, int FORM = 0, class AccT>
 __device__ __forceinline__ void epilogue(const KParams& p, AccT (&acc)[RM][RN], u32x4* lds,
                                               int64_t m0, int64_t n0, int wm, int wn, int lane,
                                               int tid, bool no_mainloop) {
@@ -1114,8 +1131,8 @@ __device__ __forceinline__ void epilogue(const KParams& p, AccT (&acc)[RM][RN], 
   constexpr bool REPACK = (size_t)BM * PITCH * OSZ <= LDS_BYTES;
   constexpr int VO = 16 / OSZ;            // outputs per 16-byte chunk
   constexpr int CPR = BN / VO;            // chunks per tile row (aligned rows)
-  const bool has_c = p.has_c != 0, has_bias = p.has_bias != 0;
-  const bool has_rs = p.has_row_scale != 0, has_cs = p.has_col_scale != 0;
+  const bool has_c = FORM == 0 && p.has_c != 0, has_bias = p.has_bias != 0;
+  const bool has_rs = FORM == 0 && p.has_row_scale != 0, has_cs = FORM == 0 && p.has_col_scale != 0;
   const int act = p.act;
   const float alpha = p.alpha, beta = p.beta;
   OT* tile = reinterpret_cast<OT*>(lds);  // BM x BN, row-major, rows PITCH apart (REPACK only)
@@ -1123,9 +1140,9 @@ __device__ __forceinline__ void epilogue(const KParams& p, AccT (&acc)[RM][RN], 
   // Shifted rows: output (row, n0 + c) at LDS position c + mis(row), mis(row) = the element
   // offset of D(row, n0) past a 16-byte boundary (0 for aligned rows).  Not with the fused
   // reductions, which read the tile unshifted.
-  const bool d_rows = SHIFT && REPACK && p.d_sn == 1 && !p.rsq_ws && !p.csum_ws;
-  const bool vec_ok = p.d_sn == 1 && (p.d_sm * OSZ) % 16 == 0 &&
-                      (reinterpret_cast<uintptr_t>(p.D) % 16) == 0;
+  const bool d_rows = FORM == 0 && SHIFT && REPACK && p.d_sn == 1 && !p.rsq_ws && !p.csum_ws;
+  const bool vec_ok = FORM == 1 || (p.d_sn == 1 && (p.d_sm * OSZ) % 16 == 0 &&
+                                    (reinterpret_cast<uintptr_t>(p.D) % 16) == 0);
   const bool shifted = d_rows && !vec_ok;  // aligned rows have mis = 0 throughout
   const uint32_t d_el0 = (uint32_t)(reinterpret_cast<uintptr_t>(p.D) / OSZ) + (uint32_t)n0;
   auto mis_raw = [&](int64_t row) -> int {
@@ -1321,7 +1338,7 @@ __device__ __forceinline__ void epilogue(const KParams& p, AccT (&acc)[RM][RN], 
         }
       }
     }
-    if (p.rsq_ws) {
+    if (FORM == 0 && p.rsq_ws) {
       // Row reduction for the next layer's norm ("CUTLASS", Part IV Stage 5: an epilogue visitor
       // tree can fuse a reduction): the sum of squares of this tile's stored values of each row,
       // one wave per row, lanes striding the columns, then a fixed-order butterfly.  The
@@ -1340,7 +1357,7 @@ __device__ __forceinline__ void epilogue(const KParams& p, AccT (&acc)[RM][RN], 
         if (lane == 0) p.rsq_ws[(n0 / BN) * p.M + m0 + lr] = sq;
       }
     }
-    if (p.csum_ws) {
+    if (FORM == 0 && p.csum_ws) {
       // Column sums of the stored tile: a wave takes 64 consecutive columns (one per lane, no
       // bank conflicts) and a group of rows; RG row groups give RG partials per column, written
       // to plane (tile row) * RG + (row group).

@@ -251,6 +251,9 @@ __global__ __launch_bounds__(512, 1) void gemm_pp(const KParams p_) {
   problem_view<256>(reload_args(), pe, pid_e, nwg_e);
   if (pe.split_k > 1) {
     store_partial<DT, MI, BM, BN, WTM, WTN>(pe, acc, m0, n0, g, wq, lane);
+  } else if (epilogue_form<DT>(pe) == 1) {
+    epilogue<DT, MI, BM, BN, WTM, WTN, RM, RN, NT, sizeof(lds), 1>(pe, acc, lds, m0, n0, g, wq,
+                                                                   lane, tid, nk == 0);
   } else {
     epilogue<DT, MI, BM, BN, WTM, WTN, RM, RN, NT, sizeof(lds)>(pe, acc, lds, m0, n0, g, wq, lane,
                                                                 tid, nk == 0);
