@@ -10,6 +10,7 @@ import dataclasses
 
 import numpy as np
 import pytest
+import torch
 
 import oracle
 from hierarchical_tiling_amd import htgemm as H
@@ -100,6 +101,26 @@ def test_same_bits_as_the_split_ring():
         _, out2 = p2.run()
         _, bits_ring = p2.decode_out(out2)
         assert int((bits_pp != bits_ring).sum()) == 0, key
+
+
+@pytest.mark.parametrize("key", ["bf16", "e4m3", "f16_bn"])
+def test_plain_epilogue_copy_matches_the_general_one(key):
+    # launches without C, scale vectors or fused reductions, D in whole 16-byte rows, take the
+    # epilogue copy compiled for them; a row scale of ones sends the same product through the
+    # general copy (a multiply by one is exact), which must give the same bits
+    dtype = key.split("_")[0]
+    c = _case(key, 520, 600, DEPTHS[dtype][2] * 3, bias=True, act="gelu",
+              seed=670 + list(PP).index(key))
+    p = Prepared(c)
+    _, out = p.run()
+    _, bits_plain = p.decode_out(out)
+    p2 = Prepared(dataclasses.replace(c, row_scale=True))
+    p2.rs = np.ones(c.M, dtype=np.float32)
+    p2.drs = torch.ones(c.M, dtype=torch.float32, device=p2.device)
+    _, out2 = p2.run()
+    _, bits_general = p2.decode_out(out2)
+    assert int((bits_plain != bits_general).sum()) == 0, key
+    _check(c)
 
 
 @pytest.mark.parametrize("key", ["bf16", "e4m3", "f16_bn"])
